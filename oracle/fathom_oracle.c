@@ -1,0 +1,301 @@
+/*
+ * fathom_oracle.c -- plain, slow, single-threaded CPU definition of Fathom's
+ * read path: pack (4-bit per-channel quantisation into channel-major bit
+ * planes), plan (reverse water-filling of a per-query bit budget), scan
+ * (approximate logits from the top t_c planes of each channel) and top-k.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, calls or
+ * includes this file; only the tests, the bench's CPU-baseline leg and the
+ * smoke check load it.  It shares no code, header or table with the HIP path.
+ *
+ * Sources (all on the pages about "Fathom: Per-Query Read Depth for Sparse
+ * Decoding over Offloaded KV Caches", arXiv 2609.17652):
+ *   [EXP]  the Chinese explainer (papers.ananclaw.com), sections
+ *          "核心方法" (core method: storage side / read side) and
+ *          "关键伪代码" (key pseudocode), "反向注水 vs 固定预算" (intuition).
+ *   [SUM]  the proomt.com summary, "Summary" bullet list.
+ * Points the pages leave open are resolved as listed in the design notes
+ * (readings R1..R14); each function below names the readings it relies on.
+ *
+ * Floating point: compiled with -O2 -fno-fast-math -ffp-contract=off, so every
+ * float/double operation below is one IEEE-754 round-to-nearest operation.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_BAD 1
+
+/* Words per plane row: the plane of one (kv head, channel) holds one bit per
+ * key, 32 keys per little-endian uint32 word, padded to a multiple of 2048
+ * keys (64 words).  Layout reading R1/R2. */
+int64_t orc_plane_words(int64_t n) { return 64 * ((n + 2047) / 2048); }
+
+/* ------------------------------------------------------------------------ */
+/* Pack.  [EXP] core method, storage side: K is quantised to 4 bits per
+ * channel, stored channel-major, and each channel's 4 bits are split into
+ * bit planes, plane t=0 holding the least significant bit and t=3 the most
+ * significant.  Readings:
+ *   R2  quantiser = 16 equal cells between the channel's min and max over the
+ *       n keys, code = floor((x - lo) / delta), delta = (hi - lo) / 16,
+ *       clamped to 15 (x == hi lands in the top cell);
+ *   R4  a constant channel (hi == lo) gives delta = 0 and every code 0;
+ *   R1  plane slot s = 3 - p, so the most significant plane comes first and
+ *       the first t slots of a channel are its top t planes;
+ *   R5  sigma^2 = population variance of the stored (dequantised) 4-bit
+ *       values, computed exactly from integer code sums.
+ * keys: fp32 element (token i, kv head h, channel c) at
+ *       keys[i*stride_tok + h*stride_head + c].
+ * codes  [hkv][d][n]  (uint8, may be NULL)
+ * planes [hkv][d][4][W]
+ * lo, hi, sigma2 [hkv][d]                                                    */
+int orc_pack(const float *keys, int64_t n, int hkv, int d, int64_t stride_tok,
+             int64_t stride_head, uint8_t *codes, uint32_t *planes, float *lo,
+             float *hi, float *sigma2) {
+  if (!keys || !planes || !lo || !hi || !sigma2 || n < 1 || hkv < 1 || d < 1)
+    return ORC_BAD;
+  const int64_t W = orc_plane_words(n);
+  memset(planes, 0, (size_t)hkv * d * 4 * W * sizeof(uint32_t));
+  for (int h = 0; h < hkv; ++h) {
+    for (int c = 0; c < d; ++c) {
+      const float *col = keys + (int64_t)h * stride_head + c;
+      /* channel range over all keys */
+      float mn = col[0], mx = col[0];
+      for (int64_t i = 1; i < n; ++i) {
+        float x = col[i * stride_tok];
+        if (x < mn) mn = x;
+        if (x > mx) mx = x;
+      }
+      float range = mx - mn;
+      float delta = range * 0.0625f; /* exact: scaling by 2^-4 */
+      int64_t s1 = 0, s2 = 0;
+      uint32_t *pl = planes + ((int64_t)h * d + c) * 4 * W;
+      for (int64_t i = 0; i < n; ++i) {
+        float x = col[i * stride_tok];
+        int code = 0;
+        if (delta != 0.0f) {
+          float u = x - mn;
+          float y = u / delta;
+          double fl = floor((double)y);
+          code = fl > 15.0 ? 15 : (int)fl;
+        }
+        if (codes) codes[((int64_t)h * d + c) * n + i] = (uint8_t)code;
+        s1 += code;
+        s2 += (int64_t)code * code;
+        for (int p = 0; p < 4; ++p) {
+          if ((code >> p) & 1) {
+            int slot = 3 - p;
+            pl[slot * W + i / 32] |= 1u << (i % 32);
+          }
+        }
+      }
+      /* Var(code) = (n*S2 - S1^2) / n^2, exact in int64 for n <= 2^26;
+       * Var(dequantised) = Var(code) * delta^2 (dequantisation is affine). */
+      int64_t num = n * s2 - s1 * s1;
+      double var_code = (double)num / ((double)n * (double)n);
+      double dd = (double)delta * (double)delta;
+      double var = var_code * dd;
+      lo[h * d + c] = mn;
+      hi[h * d + c] = mx;
+      sigma2[h * d + c] = (float)var;
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Plan.  [EXP] core method, read side, and the key pseudocode: each query
+ * has a budget of B bits per key; channel importance is the key-channel
+ * variance weighted by the query (R6: w_c = (q_c*q_c)*sigma_c^2 in fp32,
+ * multiply then multiply, no fused multiply-add); channels are visited in
+ * descending w (R8: equal w visits the lower channel index first) and each
+ * takes min(4, remaining budget) bits until the budget is spent (R7: the
+ * explicit fill-to-cap walk), so unimportant channels get 0 bits.
+ * R9: 0 <= B <= 4d.
+ * q [hq][d] fp32, sigma2 [hkv][d], budget [hq], plan out [hq][d] uint8.
+ * Query head h uses kv head h / (hq / hkv) (R12).                          */
+typedef struct {
+  float w;
+  int c;
+} orc_wc;
+
+static int orc_cmp_w_desc(const void *a, const void *b) {
+  const orc_wc *x = (const orc_wc *)a, *y = (const orc_wc *)b;
+  if (x->w > y->w) return -1;
+  if (x->w < y->w) return 1;
+  return (x->c < y->c) ? -1 : (x->c > y->c);
+}
+
+int orc_plan(const float *q, int hq, int hkv, int d, const float *sigma2,
+             const int32_t *budget, uint8_t *plan) {
+  if (!q || !sigma2 || !budget || !plan || hq < 1 || hkv < 1 || hq % hkv)
+    return ORC_BAD;
+  const int G = hq / hkv;
+  orc_wc *order = (orc_wc *)malloc(sizeof(orc_wc) * d);
+  if (!order) return ORC_BAD;
+  for (int h = 0; h < hq; ++h) {
+    int B = budget[h];
+    if (B < 0 || B > 4 * d) {
+      free(order);
+      return ORC_BAD;
+    }
+    const float *sg = sigma2 + (int64_t)(h / G) * d;
+    for (int c = 0; c < d; ++c) {
+      float qq = q[(int64_t)h * d + c] * q[(int64_t)h * d + c];
+      order[c].w = qq * sg[c];
+      order[c].c = c;
+    }
+    qsort(order, d, sizeof(orc_wc), orc_cmp_w_desc);
+    int remaining = B;
+    for (int j = 0; j < d; ++j) {
+      int take = remaining <= 0 ? 0 : (remaining < 4 ? remaining : 4);
+      plan[(int64_t)h * d + order[j].c] = (uint8_t)take;
+      remaining -= take;
+    }
+  }
+  free(order);
+  return ORC_OK;
+}
+
+/* Fixed-width baseline plan (the pages' 136-bit scans read the r = 32 channels
+ * with the largest |q_c| in full; R10): channels ordered by |q_c| descending,
+ * ties to the lower index, the first r get all 4 planes, the rest none. */
+int orc_plan_fixed(const float *q, int hq, int d, int r, uint8_t *plan) {
+  if (!q || !plan || hq < 1 || r < 0 || r > d) return ORC_BAD;
+  orc_wc *order = (orc_wc *)malloc(sizeof(orc_wc) * d);
+  if (!order) return ORC_BAD;
+  for (int h = 0; h < hq; ++h) {
+    for (int c = 0; c < d; ++c) {
+      order[c].w = fabsf(q[(int64_t)h * d + c]);
+      order[c].c = c;
+    }
+    qsort(order, d, sizeof(orc_wc), orc_cmp_w_desc);
+    for (int j = 0; j < d; ++j)
+      plan[(int64_t)h * d + order[j].c] = (uint8_t)(j < r ? 4 : 0);
+  }
+  free(order);
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The 4-bit code of key i in channel c of kv head h, rebuilt bit by bit from
+ * the planes (slot 3 - p holds bit p). */
+static int orc_code_from_planes(const uint32_t *planes, int64_t W, int d, int h,
+                                int c, int64_t i) {
+  const uint32_t *pl = planes + ((int64_t)h * d + c) * 4 * W;
+  int code = 0;
+  for (int p = 0; p < 4; ++p) {
+    uint32_t word = pl[(3 - p) * W + i / 32];
+    code |= (int)((word >> (i % 32)) & 1u) << p;
+  }
+  return code;
+}
+
+/* The value a query reads from the top t planes of a code: the t-bit prefix
+ * floor(code / 2^(4-t)) (0 when t = 0).  [EXP] core method: the first t
+ * planes of a channel are that channel's t-bit quantiser. */
+static int orc_prefix(int code, int t) { return t == 0 ? 0 : code >> (4 - t); }
+
+/* Scan.  [EXP] core method, read side: the query reads, per channel, only the
+ * planes its plan gives that channel, and scores every key.  Reading R11: the
+ * unread low bits sit at their midpoint, i.e. the t-bit prefix r is
+ * reconstructed at the centre of its cell of width delta*2^(4-t):
+ *     deq_t = lo + (r + 1/2) * delta * 2^(4-t)       (t = 0: lo + 8*delta),
+ *     s_i   = sum_c q_c * deq_{t_c}(code_ic)  [+ meta_scale * meta_i],
+ * evaluated in fp64 and rounded once to fp32.  meta [hkv][n] is the optional
+ * 8-bit per-key side stream of the fixed-width baseline (R10).
+ * logits [hq][ld]. */
+int orc_scan(const uint32_t *planes, const float *lo, const float *hi, int64_t n,
+             int hkv, int d, const float *q, const uint8_t *plan, int hq,
+             const uint8_t *meta, float meta_scale, float *logits, int64_t ld) {
+  if (!planes || !lo || !hi || !q || !plan || !logits || n < 0 || hkv < 1 ||
+      hq % hkv || ld < n)
+    return ORC_BAD;
+  const int G = hq / hkv;
+  const int64_t W = orc_plane_words(n);
+  for (int h = 0; h < hq; ++h) {
+    const int g = h / G;
+    for (int64_t i = 0; i < n; ++i) {
+      double s = 0.0;
+      for (int c = 0; c < d; ++c) {
+        int t = plan[(int64_t)h * d + c];
+        float l = lo[g * d + c], u = hi[g * d + c];
+        float delta = (u - l) * 0.0625f;
+        int r = orc_prefix(orc_code_from_planes(planes, W, d, g, c, i), t);
+        double cell = (double)delta * (double)(1 << (4 - t));
+        double deq = (double)l + ((double)r + 0.5) * cell;
+        s += (double)q[(int64_t)h * d + c] * deq;
+      }
+      if (meta) s += (double)meta_scale * (double)meta[(int64_t)g * n + i];
+      logits[(int64_t)h * ld + i] = (float)s;
+    }
+  }
+  return ORC_OK;
+}
+
+/* The plane reads themselves: out[h][i][c] = t_c-bit prefix of code_ic. */
+int orc_read_prefixes(const uint32_t *planes, int64_t n, int hkv, int d,
+                      const uint8_t *plan, int hq, uint8_t *out) {
+  if (!planes || !plan || !out || hkv < 1 || hq % hkv) return ORC_BAD;
+  const int G = hq / hkv;
+  const int64_t W = orc_plane_words(n);
+  for (int h = 0; h < hq; ++h)
+    for (int64_t i = 0; i < n; ++i)
+      for (int c = 0; c < d; ++c)
+        out[((int64_t)h * n + i) * d + c] = (uint8_t)orc_prefix(
+            orc_code_from_planes(planes, W, d, h / G, c, i),
+            plan[(int64_t)h * d + c]);
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Top-k.  [EXP] problem statement: every generated token scores the n keys
+ * and keeps the top k.  Reading R13: keys are ranked by (score descending,
+ * index ascending); rows shorter than k are padded with index -1 and score
+ * -inf.  Reading R12: for a GQA group of G query heads the group score of key
+ * i is the sum of the G rows' fp32 scores, added in row order in fp64 and
+ * rounded once to fp32.
+ * scores [rows][ld]; idx, vals [rows/group][k]. */
+typedef struct {
+  float s;
+  int32_t i;
+} orc_si;
+
+static int orc_cmp_score(const void *a, const void *b) {
+  const orc_si *x = (const orc_si *)a, *y = (const orc_si *)b;
+  if (x->s > y->s) return -1;
+  if (x->s < y->s) return 1;
+  return (x->i < y->i) ? -1 : (x->i > y->i);
+}
+
+int orc_topk(const float *scores, int rows, int64_t n, int64_t ld, int group,
+             int k, int32_t *idx, float *vals) {
+  if (!scores || !idx || !vals || rows < 1 || group < 1 || rows % group ||
+      k < 1 || n < 0 || ld < n || n > 2147483647)
+    return ORC_BAD;
+  orc_si *all = (orc_si *)malloc(sizeof(orc_si) * (size_t)(n > 0 ? n : 1));
+  if (!all) return ORC_BAD;
+  for (int o = 0; o < rows / group; ++o) {
+    for (int64_t i = 0; i < n; ++i) {
+      double acc = 0.0;
+      for (int r = 0; r < group; ++r)
+        acc += (double)scores[(int64_t)(o * group + r) * ld + i];
+      all[i].s = (float)acc;
+      all[i].i = (int32_t)i;
+    }
+    qsort(all, (size_t)n, sizeof(orc_si), orc_cmp_score);
+    for (int j = 0; j < k; ++j) {
+      if (j < n) {
+        idx[(int64_t)o * k + j] = all[j].i;
+        vals[(int64_t)o * k + j] = all[j].s;
+      } else {
+        idx[(int64_t)o * k + j] = -1;
+        vals[(int64_t)o * k + j] = -INFINITY;
+      }
+    }
+  }
+  free(all);
+  return ORC_OK;
+}

@@ -1,0 +1,150 @@
+"""ctypes wrapper of the CPU oracle (``fathom_oracle.c``).
+
+Test infrastructure only: the tests, the bench's CPU-baseline leg and the
+smoke check use it.  The product package never imports this module, and this
+module imports nothing from the product package.  Arguments are numpy arrays;
+fp16 keys are widened to fp32 here (exact).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fathom_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libfathom_oracle.so")
+GCC_FLAGS = ["-O2", "-std=c99", "-fno-fast-math", "-ffp-contract=off",
+             "-fPIC", "-shared", "-Wall", "-Wextra"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into ``oracle/libfathom_oracle.so``."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        L = ctypes.c_int64
+        F = ctypes.c_float
+        lib.orc_plane_words.restype = L
+        lib.orc_plane_words.argtypes = [L]
+        lib.orc_pack.argtypes = [P, L, I, I, L, L, P, P, P, P, P]
+        lib.orc_plan.argtypes = [P, I, I, I, P, P, P]
+        lib.orc_plan_fixed.argtypes = [P, I, I, I, P]
+        lib.orc_scan.argtypes = [P, P, P, L, I, I, P, P, I, P, F, P, L]
+        lib.orc_read_prefixes.argtypes = [P, L, I, I, P, I, P]
+        lib.orc_topk.argtypes = [P, I, L, L, I, I, P, P]
+        for f in ("orc_pack", "orc_plan", "orc_plan_fixed", "orc_scan",
+                  "orc_read_prefixes", "orc_topk"):
+            getattr(lib, f).restype = I
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError(f"oracle {name} rejected its arguments")
+
+
+def plane_words(n: int) -> int:
+    return int(_load().orc_plane_words(n))
+
+
+def pack(keys: np.ndarray):
+    """keys [n][hkv][d] (fp16 or fp32) -> dict(codes, planes, lo, hi, sigma2).
+
+    codes [hkv][d][n] uint8, planes [hkv][d][4][W] uint32 (slot 0 = MSB
+    plane), lo/hi/sigma2 [hkv][d] fp32.
+    """
+    k32 = np.ascontiguousarray(keys, dtype=np.float32)
+    n, hkv, d = k32.shape
+    W = plane_words(n)
+    codes = np.empty((hkv, d, n), np.uint8)
+    planes = np.empty((hkv, d, 4, W), np.uint32)
+    lo = np.empty((hkv, d), np.float32)
+    hi = np.empty((hkv, d), np.float32)
+    s2 = np.empty((hkv, d), np.float32)
+    _check(_load().orc_pack(_ptr(k32), n, hkv, d, hkv * d, d, _ptr(codes),
+                            _ptr(planes), _ptr(lo), _ptr(hi), _ptr(s2)), "pack")
+    return dict(codes=codes, planes=planes, lo=lo, hi=hi, sigma2=s2)
+
+
+def plan(q: np.ndarray, sigma2: np.ndarray, budget) -> np.ndarray:
+    """q [hq][d] fp32, sigma2 [hkv][d] fp32, budget int or [hq] -> [hq][d] u8."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    sigma2 = np.ascontiguousarray(sigma2, dtype=np.float32)
+    hq, d = q.shape
+    hkv = sigma2.shape[0]
+    b = np.ascontiguousarray(np.broadcast_to(np.asarray(budget, np.int32), (hq,)))
+    out = np.empty((hq, d), np.uint8)
+    _check(_load().orc_plan(_ptr(q), hq, hkv, d, _ptr(sigma2), _ptr(b),
+                            _ptr(out)), "plan")
+    return out
+
+
+def plan_fixed(q: np.ndarray, r: int) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    hq, d = q.shape
+    out = np.empty((hq, d), np.uint8)
+    _check(_load().orc_plan_fixed(_ptr(q), hq, d, r, _ptr(out)), "plan_fixed")
+    return out
+
+
+def scan(planes, lo, hi, n: int, q, plan_, meta=None, meta_scale: float = 0.0):
+    """-> logits [hq][n] fp32 (computed in fp64, rounded once)."""
+    planes = np.ascontiguousarray(planes, dtype=np.uint32)
+    lo = np.ascontiguousarray(lo, dtype=np.float32)
+    hi = np.ascontiguousarray(hi, dtype=np.float32)
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    plan_ = np.ascontiguousarray(plan_, dtype=np.uint8)
+    hkv, d = lo.shape
+    hq = q.shape[0]
+    if meta is not None:
+        meta = np.ascontiguousarray(meta, dtype=np.uint8)
+    out = np.empty((hq, max(n, 1)), np.float32)
+    _check(_load().orc_scan(_ptr(planes), _ptr(lo), _ptr(hi), n, hkv, d, _ptr(q),
+                            _ptr(plan_), hq, _ptr(meta), meta_scale, _ptr(out),
+                            max(n, 1)), "scan")
+    return out[:, :n]
+
+
+def read_prefixes(planes, n: int, plan_, hkv: int) -> np.ndarray:
+    planes = np.ascontiguousarray(planes, dtype=np.uint32)
+    plan_ = np.ascontiguousarray(plan_, dtype=np.uint8)
+    hq, d = plan_.shape
+    out = np.empty((hq, n, d), np.uint8)
+    _check(_load().orc_read_prefixes(_ptr(planes), n, hkv, d, _ptr(plan_), hq,
+                                     _ptr(out)), "read_prefixes")
+    return out
+
+
+def topk(scores, k: int, group: int = 1):
+    """scores [rows][n] fp32 -> (idx [rows/group][k] int32, vals fp32)."""
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    rows, n = scores.shape
+    ro = rows // group
+    idx = np.empty((ro, k), np.int32)
+    vals = np.empty((ro, k), np.float32)
+    _check(_load().orc_topk(_ptr(scores), rows, n, max(n, 1), group, k,
+                            _ptr(idx), _ptr(vals)), "topk")
+    return idx, vals

@@ -1,0 +1,465 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Nothing here touches the HIP path.  Each test checks the oracle against an
+independent fact: the plane-prefix invariant of the storage side (the top t
+planes of a channel are its t-bit quantiser), closed forms, brute force on
+tiny inputs, the pages' worked budgets (tests/golden), and library sorts.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------------------
+# helpers written for the tests (independent of the oracle's code)
+
+def top_planes_value(planes, W, h, c, i, t):
+    """Value of the first t plane slots of (h, c) at key i, read MSB first."""
+    v = 0
+    for s in range(t):
+        word = int(planes[h, c, s, i // 32])
+        v = (v << 1) | ((word >> (i % 32)) & 1)
+    return v
+
+
+def t_bit_quantizer(x, lo, hi, t):
+    """The t-bit min-max quantiser of x over [lo, hi] with 2^t equal cells,
+    cell width (hi - lo) / 2^t, in fp32 (independent of the 4-bit code)."""
+    x = np.asarray(x, np.float32)
+    lo = np.float32(lo)
+    hi = np.float32(hi)
+    width = np.float32(np.float32(hi - lo) * np.float32(2.0 ** -t))
+    if t == 0:
+        return np.zeros(x.shape, np.int64)
+    if width == 0:
+        return np.zeros(x.shape, np.int64)
+    y = np.floor((x - lo).astype(np.float32) / width)
+    return np.minimum(y, 2 ** t - 1).astype(np.int64)
+
+
+def all_finite_fp16():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = bits.view(np.float16)
+    return v[np.isfinite(v)]
+
+
+def unpack_planes_vectorised(planes, n):
+    """codes [hkv][d][n] rebuilt from planes [hkv][d][4][W] (slot 0 = MSB)."""
+    hkv, d, _, W = planes.shape
+    bits = np.unpackbits(planes.view(np.uint8).reshape(hkv, d, 4, W * 4),
+                         axis=-1, bitorder="little")[..., :n]
+    return (bits[:, :, 0] * 8 + bits[:, :, 1] * 4 + bits[:, :, 2] * 2
+            + bits[:, :, 3]).astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# pack
+
+def test_plane_prefix_invariant_exhaustive_fp16(orc):
+    """Storage side: the first t planes of a channel equal the t-bit
+    quantiser of that channel, for every finite fp16 key value."""
+    x = all_finite_fp16().astype(np.float32)
+    n = x.size
+    keys = x.reshape(n, 1, 1)
+    p = orc.pack(keys)
+    planes = p["planes"]
+    lo, hi = p["lo"][0, 0], p["hi"][0, 0]
+    assert lo == x.min() and hi == x.max()
+    codes = unpack_planes_vectorised(planes, n)[0, 0]
+    for t in range(5):
+        prefix = codes >> (4 - t) if t else np.zeros_like(codes)
+        np.testing.assert_array_equal(prefix, t_bit_quantizer(x, lo, hi, t))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_plane_prefix_invariant_random_ranges(orc, seed):
+    """Same invariant on random sub-ranges of the fp16 values and on fp32
+    samples, per channel, through the bit-by-bit top-plane reader."""
+    rng = np.random.default_rng(seed)
+    allv = all_finite_fp16().astype(np.float32)
+    n, d = 300, 5
+    cols = []
+    for c in range(d):
+        if c < 3:
+            a, b = sorted(rng.integers(0, allv.size, 2))
+            sub = np.sort(allv)[a:b + 2]
+            cols.append(rng.choice(sub, n))
+        else:
+            cols.append((rng.standard_normal(n) * rng.uniform(0.01, 50))
+                        .astype(np.float32))
+    keys = np.stack(cols, axis=1).reshape(n, 1, d).astype(np.float32)
+    p = orc.pack(keys)
+    W = p["planes"].shape[-1]
+    for c in range(d):
+        lo, hi = p["lo"][0, c], p["hi"][0, c]
+        for t in range(5):
+            ref = t_bit_quantizer(keys[:, 0, c], lo, hi, t)
+            got = [top_planes_value(p["planes"], W, 0, c, i, t) for i in range(n)]
+            np.testing.assert_array_equal(got, ref)
+
+
+def test_quantizer_properties(orc):
+    rng = np.random.default_rng(7)
+    n, hkv, d = 1000, 2, 16
+    keys = (rng.standard_normal((n, hkv, d)) *
+            rng.uniform(0.1, 4, (1, hkv, d))).astype(np.float16)
+    p = orc.pack(keys)
+    x = keys.astype(np.float64).transpose(1, 2, 0)      # [hkv][d][n]
+    codes = p["codes"].astype(np.int64)
+    assert codes.min() == 0 and codes.max() == 15
+    lo = p["lo"].astype(np.float64)[..., None]
+    hi = p["hi"].astype(np.float64)[..., None]
+    np.testing.assert_array_equal(p["lo"], x.min(-1))
+    np.testing.assert_array_equal(p["hi"], x.max(-1))
+    delta = (hi - lo) / 16
+    # min lands in cell 0, max in cell 15, codes monotone in x
+    for h in range(hkv):
+        for c in range(d):
+            order = np.argsort(x[h, c], kind="stable")
+            assert np.all(np.diff(codes[h, c][order]) >= 0)
+            assert codes[h, c][order[0]] == 0 and codes[h, c][order[-1]] == 15
+    # cell-centre reconstruction is within half a cell (plus fp32 slack)
+    deq = lo + (codes + 0.5) * delta
+    assert np.all(np.abs(x - deq) <= delta * (0.5 + 1e-5))
+    # the planes hold exactly the codes
+    np.testing.assert_array_equal(unpack_planes_vectorised(p["planes"], n), codes)
+    # padding bits of the last word are zero
+    W = p["planes"].shape[-1]
+    assert W == 64 * ((n + 2047) // 2048)
+    tail = p["planes"][..., n // 32 + 1:]
+    assert np.all(tail == 0)
+    last = p["planes"][..., n // 32]
+    assert np.all((last >> np.uint32(n % 32)) == 0)
+
+
+def test_constant_channel_and_single_key(orc):
+    n = 70
+    keys = np.zeros((n, 1, 3), np.float32)
+    keys[:, 0, 0] = 2.5                          # constant channel
+    keys[:, 0, 1] = np.linspace(-1, 1, n)
+    keys[:, 0, 2] = -7.0
+    keys[5, 0, 2] = 3.0                          # single distinct value
+    p = orc.pack(keys)
+    assert np.all(p["codes"][0, 0] == 0) and p["sigma2"][0, 0] == 0
+    assert p["lo"][0, 0] == p["hi"][0, 0] == np.float32(2.5)
+    assert p["codes"][0, 2, 5] == 15 and np.all(np.delete(p["codes"][0, 2], 5) == 0)
+    one = orc.pack(np.array([[[1.25, -3.0]]], np.float32))
+    assert np.all(one["codes"] == 0) and np.all(one["sigma2"] == 0)
+
+
+def test_sigma2_is_variance_of_dequantised_values(orc):
+    """sigma_c^2 equals a two-pass fp64 variance of lo + (code + 1/2) delta."""
+    rng = np.random.default_rng(11)
+    n, hkv, d = 3001, 2, 24
+    keys = (rng.standard_normal((n, hkv, d)) * 3).astype(np.float16)
+    p = orc.pack(keys)
+    lo = p["lo"].astype(np.float64)
+    delta = (p["hi"].astype(np.float32) - p["lo"].astype(np.float32)) * np.float32(0.0625)
+    deq = lo[..., None] + (p["codes"] + 0.5) * delta.astype(np.float64)[..., None]
+    mean = deq.mean(-1, keepdims=True)
+    var = ((deq - mean) ** 2).mean(-1)
+    np.testing.assert_allclose(p["sigma2"], var, rtol=2e-7, atol=0)
+    # and it tracks the raw key variance to within the quantisation noise
+    raw = keys.astype(np.float64).var(0)
+    assert np.all(np.abs(p["sigma2"] - raw) <= 0.2 * raw + (delta.astype(np.float64) ** 2))
+
+
+# --------------------------------------------------------------------------
+# plan
+
+def w_order(q, sigma2):
+    w = (q.astype(np.float32) * q.astype(np.float32)).astype(np.float32) * sigma2
+    return w
+
+
+def test_plan_golden_worked_examples(orc):
+    with open(os.path.join(GOLDEN, "plan_worked_examples.json")) as f:
+        cases = json.load(f)["cases"]
+    rng = np.random.default_rng(3)
+    for case in cases:
+        d, B = case["d"], case["budget"]
+        sigma2 = rng.uniform(0.5, 2.0, (1, d)).astype(np.float32)
+        q = rng.standard_normal((1, d)).astype(np.float32)
+        w = w_order(q[0], sigma2[0])
+        order = np.lexsort((np.arange(d), -w))   # w desc, index asc
+        plan = orc.plan(q, sigma2, B)[0]
+        assert list(plan[order]) == case["plan_in_w_order"], case["name"]
+
+
+@pytest.mark.parametrize("B", [0, 1, 3, 4, 17, 18, 68, 91, 92, 136, 511, 512])
+def test_plan_invariants(orc, B):
+    rng = np.random.default_rng(B)
+    hq, hkv, d = 8, 2, 128
+    q = rng.standard_normal((hq, d)).astype(np.float32)
+    sigma2 = rng.uniform(0.01, 16, (hkv, d)).astype(np.float32)
+    plan = orc.plan(q, sigma2, B).astype(np.int64)
+    assert np.all(plan.sum(1) == B)
+    assert np.all(plan <= 4)
+    assert np.all((plan > 0).sum(1) == -(-B // 4))
+    # every channel read in full outranks every channel not read at all
+    for h in range(hq):
+        w = w_order(q[h], sigma2[h // 4])
+        read, unread = w[plan[h] == 4], w[plan[h] == 0]
+        if read.size and unread.size:
+            assert read.min() >= unread.max()
+
+
+def test_plan_rejects_out_of_range_budget(orc):
+    q = np.ones((1, 8), np.float32)
+    s = np.ones((1, 8), np.float32)
+    for B in (-1, 33):
+        with pytest.raises(ValueError):
+            orc.plan(q, s, B)
+
+
+@pytest.mark.parametrize("d", [3, 4, 5, 6])
+def test_plan_greedy_is_optimal_brute_force(orc, d):
+    """The fill-to-cap walk maximises sum_c w_c t_c over all plans with
+    sum t = B and 0 <= t_c <= 4 (the importance-weighted bits read); with
+    distinct w the maximiser is unique and equals the walk."""
+    rng = np.random.default_rng(100 + d)
+    plans = np.array(list(itertools.product(range(5), repeat=d)))
+    for trial in range(6):
+        q = rng.standard_normal((1, d)).astype(np.float32)
+        sigma2 = rng.uniform(0.1, 4, (1, d)).astype(np.float32)
+        w = w_order(q[0], sigma2[0]).astype(np.float64)
+        for B in range(0, 4 * d + 1):
+            feas = plans[plans.sum(1) == B]
+            val = feas @ w
+            best = feas[val == val.max()]
+            got = orc.plan(q, sigma2, B)[0]
+            assert len(best) == 1
+            np.testing.assert_array_equal(got, best[0])
+
+
+def test_plan_ties_go_to_lower_channel(orc):
+    d = 8
+    q = np.ones((1, d), np.float32)
+    s = np.ones((1, d), np.float32)
+    assert list(orc.plan(q, s, 10)[0]) == [4, 4, 2, 0, 0, 0, 0, 0]
+    s2 = s.copy()
+    s2[0, 5] = 2.0
+    assert list(orc.plan(q, s2, 10)[0]) == [4, 2, 0, 0, 0, 4, 0, 0]
+
+
+def test_plan_focused_query_spends_budget_on_few_channels(orc):
+    """Intuition example 1: a query that depends on one or two channels puts
+    its whole budget there."""
+    d = 128
+    q = np.full((1, d), 1e-3, np.float32)
+    q[0, 17], q[0, 90] = 3.0, -2.0
+    s = np.ones((1, d), np.float32)
+    plan = orc.plan(q, s, 8)[0]
+    assert plan[17] == 4 and plan[90] == 4 and plan.sum() == 8
+
+
+def test_plan_gqa_uses_group_sigma(orc):
+    hq, hkv, d = 4, 2, 8
+    q = np.ones((hq, d), np.float32)
+    s = np.ones((hkv, d), np.float32)
+    s[0, 7] = 5.0
+    s[1, 2] = 5.0
+    plan = orc.plan(q, s, 4)
+    assert plan[0, 7] == 4 and plan[1, 7] == 4
+    assert plan[2, 2] == 4 and plan[3, 2] == 4
+
+
+def test_plan_fixed_is_top_r_abs_q_and_matches_equal_sigma(orc):
+    rng = np.random.default_rng(5)
+    hq, d = 6, 128
+    q = rng.standard_normal((hq, d)).astype(np.float32)
+    for r in (0, 1, 16, 32, 128):
+        fixed = orc.plan_fixed(q, r)
+        for h in range(hq):
+            order = np.lexsort((np.arange(d), -np.abs(q[h])))
+            exp = np.zeros(d, np.uint8)
+            exp[order[:r]] = 4
+            np.testing.assert_array_equal(fixed[h], exp)
+        same = orc.plan(q, np.ones((hq, d), np.float32), 4 * r)
+        np.testing.assert_array_equal(fixed, same)
+
+
+# --------------------------------------------------------------------------
+# scan
+
+def make_layer(seed, n=300, hkv=2, hq=4, d=16, dtype=np.float16):
+    rng = np.random.default_rng(seed)
+    sig = np.exp(rng.uniform(np.log(0.1), np.log(4), (hkv, d)))
+    keys = (rng.standard_normal((n, hkv, d)) * sig[None]).astype(dtype)
+    q = rng.standard_normal((hq, d)).astype(np.float32)
+    return keys, q
+
+
+def test_scan_full_budget_is_full_4bit_dot_product(orc):
+    keys, q = make_layer(1)
+    n, hkv, d = keys.shape
+    hq = q.shape[0]
+    p = orc.pack(keys)
+    plan = orc.plan(q, p["sigma2"], 4 * d)
+    s = orc.scan(p["planes"], p["lo"], p["hi"], n, q, plan)
+    lo = p["lo"].astype(np.float64)
+    delta = ((p["hi"] - p["lo"]) * np.float32(0.0625)).astype(np.float64)
+    G = hq // hkv
+    for h in range(hq):
+        g = h // G
+        deq = lo[g][:, None] + (p["codes"][g] + 0.5) * delta[g][:, None]  # [d][n]
+        ref = q[h].astype(np.float64) @ deq
+        np.testing.assert_array_equal(s[h], ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("B", [0, 5, 18, 46, 64])
+def test_scan_matches_t_bit_quantiser_from_raw_keys(orc, B):
+    """Per key and channel, the scan's value equals the t-bit quantiser of the
+    raw key reconstructed at its cell centre, summed against q (computed here
+    from the keys, not from the planes)."""
+    keys, q = make_layer(2 + B, n=130, hkv=1, hq=2, d=16)
+    n, hkv, d = keys.shape
+    p = orc.pack(keys)
+    plan = orc.plan(q, p["sigma2"], B)
+    s = orc.scan(p["planes"], p["lo"], p["hi"], n, q, plan)
+    x = keys.astype(np.float32)[:, 0, :]
+    for h in range(2):
+        acc = np.zeros(n)
+        for c in range(d):
+            t = int(plan[h, c])
+            lo, hi = p["lo"][0, c], p["hi"][0, c]
+            qt = t_bit_quantizer(x[:, c], lo, hi, t)
+            width = float(np.float32(np.float32(hi - lo) * np.float32(0.0625))) * 2 ** (4 - t)
+            acc += float(q[h, c]) * (float(lo) + (qt + 0.5) * width)
+        np.testing.assert_array_equal(s[h], acc.astype(np.float32))
+
+
+def test_scan_zero_budget_is_constant_midpoint(orc):
+    keys, q = make_layer(3)
+    n = keys.shape[0]
+    p = orc.pack(keys)
+    plan = orc.plan(q, p["sigma2"], 0)
+    s = orc.scan(p["planes"], p["lo"], p["hi"], n, q, plan)
+    mid = (p["lo"].astype(np.float64) + p["hi"].astype(np.float64)) / 2
+    for h in range(q.shape[0]):
+        assert np.all(s[h] == s[h, 0])
+        np.testing.assert_allclose(s[h, 0], q[h] @ mid[h // 2], rtol=1e-6)
+
+
+def test_scan_one_hot_query_ranks_by_code(orc):
+    keys, _ = make_layer(4, n=500, hkv=1, hq=1, d=16)
+    p = orc.pack(keys)
+    c = 9
+    q = np.zeros((1, 16), np.float32)
+    q[0, c] = 1.0
+    plan = orc.plan(q, p["sigma2"], 4)
+    assert plan[0, c] == 4
+    s = orc.scan(p["planes"], p["lo"], p["hi"], 500, q, plan)[0]
+    codes = p["codes"][0, c]
+    delta = np.float32(p["hi"][0, c] - p["lo"][0, c]) * np.float32(0.0625)
+    np.testing.assert_allclose(s, p["lo"][0, c] + (codes + 0.5) * float(delta),
+                               rtol=1e-6)
+    assert np.all(np.diff(s[np.argsort(codes, kind="stable")]) >= 0)
+
+
+def test_scan_ignores_unread_plane_bits(orc):
+    """Flipping any bit the plan does not read leaves every logit unchanged."""
+    keys, q = make_layer(5, n=200)
+    n, hkv, d = keys.shape
+    p = orc.pack(keys)
+    plan = orc.plan(q, p["sigma2"], 30)
+    s0 = orc.scan(p["planes"], p["lo"], p["hi"], n, q, plan)
+    G = q.shape[0] // hkv
+    depth = np.zeros((hkv, d), np.int64)   # deepest plane any head of the group reads
+    for h in range(q.shape[0]):
+        depth[h // G] = np.maximum(depth[h // G], plan[h])
+    flipped = p["planes"].copy()
+    rng = np.random.default_rng(0)
+    for g in range(hkv):
+        for c in range(d):
+            for slot in range(depth[g, c], 4):
+                flipped[g, c, slot] ^= rng.integers(0, 2 ** 32, flipped.shape[-1],
+                                                   dtype=np.uint64).astype(np.uint32)
+    s1 = orc.scan(flipped, p["lo"], p["hi"], n, q, plan)
+    np.testing.assert_array_equal(s0, s1)
+    # and flipping a read bit does change something
+    g, c = np.argwhere(depth > 0)[0]
+    flipped2 = p["planes"].copy()
+    flipped2[g, c, 0] ^= np.uint32(0xFFFFFFFF)
+    s2 = orc.scan(flipped2, p["lo"], p["hi"], n, q, plan)
+    assert np.any(s2 != s0)
+
+
+def test_scan_side_stream_adds_scaled_byte(orc):
+    keys, q = make_layer(6, n=100)
+    n, hkv, d = keys.shape
+    p = orc.pack(keys)
+    plan = orc.plan_fixed(q, 4)
+    meta = np.random.default_rng(1).integers(0, 256, (hkv, n)).astype(np.uint8)
+    s0 = orc.scan(p["planes"], p["lo"], p["hi"], n, q, plan)
+    s1 = orc.scan(p["planes"], p["lo"], p["hi"], n, q, plan, meta, 0.25)
+    G = q.shape[0] // hkv
+    for h in range(q.shape[0]):
+        np.testing.assert_allclose(s1[h], s0[h] + 0.25 * meta[h // G], rtol=1e-6,
+                                   atol=1e-6)
+
+
+def test_read_prefixes_are_shifted_codes(orc):
+    keys, q = make_layer(8, n=90)
+    n, hkv, d = keys.shape
+    p = orc.pack(keys)
+    plan = orc.plan(q, p["sigma2"], 23)
+    r = orc.read_prefixes(p["planes"], n, plan, hkv)
+    G = q.shape[0] // hkv
+    for h in range(q.shape[0]):
+        for c in range(d):
+            t = int(plan[h, c])
+            exp = p["codes"][h // G, c] >> (4 - t) if t else 0
+            np.testing.assert_array_equal(r[h, :, c], exp)
+
+
+# --------------------------------------------------------------------------
+# top-k
+
+def lexsort_topk(S, k):
+    order = np.lexsort((np.arange(S.size), -S.astype(np.float64)))
+    return order[:k]
+
+
+@pytest.mark.parametrize("n,k", [(1, 1), (7, 3), (64, 64), (500, 37), (4096, 64),
+                                 (50, 80)])
+def test_topk_matches_full_sort(orc, n, k):
+    rng = np.random.default_rng(n * 31 + k)
+    rows = 3
+    S = rng.standard_normal((rows, n)).astype(np.float32)
+    S[:, ::5] = np.round(S[:, ::5])          # plenty of exact ties
+    idx, vals = orc.topk(S, k)
+    for r in range(rows):
+        exp = lexsort_topk(S[r], k)
+        m = min(k, n)
+        np.testing.assert_array_equal(idx[r, :m], exp)
+        np.testing.assert_array_equal(vals[r, :m], S[r, exp])
+        assert np.all(idx[r, m:] == -1) and np.all(np.isneginf(vals[r, m:]))
+
+
+def test_topk_group_sum_in_fp64(orc):
+    rng = np.random.default_rng(9)
+    G, n, k = 4, 1000, 25
+    S = rng.standard_normal((2 * G, n)).astype(np.float32)
+    idx, vals = orc.topk(S, k, group=G)
+    for o in range(2):
+        tot = S[o * G:(o + 1) * G].astype(np.float64).sum(0).astype(np.float32)
+        exp = lexsort_topk(tot, k)
+        np.testing.assert_array_equal(idx[o], exp)
+        np.testing.assert_array_equal(vals[o], tot[exp])
+
+
+def test_topk_all_equal_scores_take_lowest_indices(orc):
+    S = np.full((1, 100), 2.0, np.float32)
+    S[0, 50] = -0.0
+    idx, _ = orc.topk(S, 10)
+    assert list(idx[0]) == list(range(10))
+    S2 = np.zeros((1, 10), np.float32)
+    S2[0, 3] = -0.0                 # -0 ties with +0
+    idx2, _ = orc.topk(S2, 10)
+    assert list(idx2[0]) == list(range(10))
