@@ -68,6 +68,9 @@ int orc_pack(const float *keys, int64_t n, int hkv, int d, int64_t stride_tok,
         if (x < mn) mn = x;
         if (x > mx) mx = x;
       }
+      /* R4: -0 and +0 are one key value; the stored range ends are +0. */
+      mn = mn + 0.0f;
+      mx = mx + 0.0f;
       float range = mx - mn;
       float delta = range * 0.0625f; /* exact: scaling by 2^-4 */
       int64_t s1 = 0, s2 = 0;
