@@ -1,0 +1,217 @@
+/*
+ * fathom.h -- C ABI of the MI355X (gfx950) implementation of Fathom's read
+ * path over a 4-bit, channel-major, bit-plane K cache:
+ *
+ *     fathom_pack -> fathom_plan -> fathom_scan -> fathom_topk
+ *
+ * The method is the one described on the pages about "Fathom: Per-Query Read
+ * Depth for Sparse Decoding over Offloaded KV Caches" (arXiv 2609.17652);
+ * citations below name the Chinese explainer page (papers.ananclaw.com) and
+ * its section headings.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Plain C: pointers, sizes, an opaque stream.  `stream` is a hipStream_t
+ *    (NULL = the default stream).  Every GPU call only enqueues work on that
+ *    stream; nothing synchronises inside the library.
+ *  - Ownership: the caller allocates and frees every buffer (inputs, outputs,
+ *    workspaces).  The library never allocates, frees or keeps pointers.
+ *  - Device pointers are HBM pointers unless an argument says it may also be
+ *    pinned host memory (allocated with hipHostMalloc, e.g. torch's
+ *    pin_memory); such memory is read zero-copy over the host link.
+ *  - Return value: FATHOM_OK, or an error code.  Argument errors are detected
+ *    on the host before anything is enqueued; fathom_last_error() then holds
+ *    a one-line, thread-local description.  Faults during execution surface
+ *    on the stream as HIP errors, like any kernel's.
+ *  - Shapes: d (head dimension) must be 128 (FATHOM_ERR_UNSUPPORTED
+ *    otherwise).  Query head h of a layer reads kv head h / (hq / hkv)
+ *    (grouped-query attention); hq must be a multiple of hkv.
+ *  - Inputs must be finite (no NaN/Inf keys, queries or scores); behaviour on
+ *    non-finite inputs is unspecified.
+ *  - Thread safety: calls are reentrant; two calls that write the same
+ *    buffers must be ordered by the caller (same stream or events).
+ */
+#ifndef FATHOM_H
+#define FATHOM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FATHOM_ABI_VERSION 1
+#define FATHOM_HEAD_DIM 128
+#define FATHOM_MAX_K 2048         /* largest k accepted by the top-k calls */
+#define FATHOM_MAX_SESSIONS 64    /* sessions per batched call */
+
+enum {
+  FATHOM_OK = 0,
+  FATHOM_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad budget, ...   */
+  FATHOM_ERR_UNSUPPORTED = 2, /* valid but not implemented (d != 128, ...) */
+  FATHOM_ERR_HIP = 3,         /* a HIP runtime call or launch failed        */
+  FATHOM_ERR_WORKSPACE = 4    /* workspace missing or smaller than needed   */
+};
+
+enum { FATHOM_F16 = 0, FATHOM_F32 = 1 }; /* key element types */
+
+int32_t fathom_abi_version(void);
+const char *fathom_last_error(void);
+
+/* ---- sizes -------------------------------------------------------------- */
+
+/* Words per plane row: one bit per key, 32 keys per uint32 word, padded to a
+ * whole number of 2048-key blocks: W = 64 * ceil(n / 2048). */
+int64_t fathom_plane_words(int64_t n);
+/* Bytes of the plane array of one layer: hkv * d * 4 * W * 4. */
+int64_t fathom_planes_bytes(int64_t n, int32_t hkv, int32_t d);
+/* Workspace bytes fathom_pack needs for n keys (0 on bad arguments). */
+int64_t fathom_pack_workspace_bytes(int64_t n, int32_t hkv, int32_t d);
+/* Workspace bytes fathom_topk needs for `out_rows` = rows / group output rows
+ * (independent of n).  fathom_topk_batched needs this for the sum of its
+ * sessions' output rows. */
+int64_t fathom_topk_workspace_bytes(int32_t out_rows, int32_t k);
+
+/* ---- pack (storage side) -------------------------------------------------
+ * Explainer, section 核心方法 (core method), storage side: K is quantised to
+ * 4 bits per channel and stored channel-major, each channel's 4 bits split
+ * into bit planes; the first t planes of a channel are its t-bit quantiser.
+ *
+ * keys      device, token-major: element (token i, kv head h, channel c) at
+ *           keys[i*stride_tok + h*stride_head + c] (strides in elements,
+ *           channel stride 1), dtype FATHOM_F16 or FATHOM_F32, n >= 1.
+ * planes    device (HBM) output, uint32[hkv][d][4][W]: slot s of channel c
+ *           holds bit (3 - s) of the codes, so slot 0 is the most significant
+ *           plane and the top t planes of a channel are the t*W contiguous
+ *           words starting at slot 0.  Bit j of word w belongs to key 32w + j;
+ *           padding bits (keys >= n) are 0.
+ * lo, hi    device outputs fp32[hkv][d]: the channel's minimum and maximum
+ *           over the n keys.  delta = (hi - lo) * 1/16 (fp32), code =
+ *           min(15, floor((x - lo) / delta)) with IEEE fp32 subtract and
+ *           divide; delta == 0 gives code 0.
+ * sigma2    device output fp32[hkv][d]: variance of the dequantised 4-bit
+ *           values lo + (code + 1/2) delta, computed exactly from integer code
+ *           sums: fp32((n*S2 - S1^2) / n^2 * delta^2) in fp64.
+ * ws        device workspace of at least fathom_pack_workspace_bytes bytes.
+ * Enqueues 4 kernels.  Outputs are bit-identical to the CPU definition.    */
+int32_t fathom_pack(const void *keys, int32_t dtype, int64_t n, int32_t hkv,
+                    int32_t d, int64_t stride_tok, int64_t stride_head,
+                    uint32_t *planes, float *lo, float *hi, float *sigma2,
+                    void *ws, int64_t ws_bytes, void *stream);
+
+/* ---- plan (read side) ----------------------------------------------------
+ * Explainer, sections 核心方法 (read side) and 关键伪代码: each query head
+ * spends a budget of B bits per key over channels by reverse water-filling:
+ * importance w_c = (q_c * q_c) * sigma2_c (fp32, two rounded multiplies),
+ * channels visited by w descending (equal w: lower channel first), each
+ * taking min(4, remaining budget) bits.  Channels may get 0 bits.
+ *
+ * q            device fp32[hq][d]
+ * sigma2       device fp32[hkv][d] (from fathom_pack or any non-negative
+ *              calibrated variance)
+ * budget_bits  HOST int32[hq], each in [0, 4d] (else FATHOM_ERR_INVALID_ARG)
+ * plan         device output uint8[hq][d]: t_c in 0..4, sum_c t_c = B.     */
+int32_t fathom_plan(const float *q, int32_t hq, int32_t hkv, int32_t d,
+                    const float *sigma2, const int32_t *budget_bits,
+                    uint8_t *plan, void *stream);
+
+/* Fixed-width baseline plan (the pages' 136-bit scans read r = 32 channels
+ * in full): the r channels with the largest |q_c| (ties: lower channel) get
+ * t = 4, all others 0.  0 <= r <= d.                                        */
+int32_t fathom_plan_fixed(const float *q, int32_t hq, int32_t d, int32_t r,
+                          uint8_t *plan, void *stream);
+
+/* ---- scan ----------------------------------------------------------------
+ * Explainer, section 核心方法 (read side) and problem statement: each query
+ * head reads only the top t_c planes of every channel and scores all n keys.
+ * The unread low bits are reconstructed at their midpoint:
+ *   s_i = sum_c q_c * (lo_c + (floor(code_ic / 2^(4-t_c)) + 1/2) *
+ *                       delta_c * 2^(4-t_c))   [+ meta_scale * meta[g][i]]
+ * Per kv head the planes read are the union of its query heads' plans, read
+ * once for the whole group.  Accuracy: |s - exact| <= 1e-5 * A_h with
+ * A_h = sum_c |q_c| * max(|lo_c|, |hi_c|).
+ *
+ * planes      device (HBM) or pinned host memory, layout of fathom_pack.
+ * lo, hi      device fp32[hkv][d]
+ * q           device fp32[hq][d];  plan  device uint8[hq][d] (t in 0..4)
+ * meta        NULL, or device/pinned uint8[hkv][n]: an 8-bit per-key side
+ *             stream added as meta_scale * meta (fixed-width baseline).
+ * logits      device output fp32[hq][ld_logits], ld_logits >= n; only
+ *             columns < n are written.                                      */
+int32_t fathom_scan(const uint32_t *planes, const float *lo, const float *hi,
+                    int64_t n, int32_t hkv, int32_t d, const float *q,
+                    const uint8_t *plan, int32_t hq, const uint8_t *meta,
+                    float meta_scale, float *logits, int64_t ld_logits,
+                    void *stream);
+
+/* ---- top-k ---------------------------------------------------------------
+ * Explainer, problem statement: every decode step keeps the top k of the n
+ * scored keys.  Ranking: score descending, then index ascending.  With
+ * group = G > 1 each output row o ranks the group score
+ *   S_i = fp32( ((0 + s[oG][i]) + s[oG+1][i]) + ... ) added in fp64.
+ * -0.0 ranks equal to +0.0.  Rows with n < k are padded with idx -1 and
+ * score -inf.  Results are identical to a full sort.
+ *
+ * scores  device fp32[rows][ld], ld >= n;  rows % group == 0
+ * idx     device output int32[rows/group][k];  vals  fp32[rows/group][k]
+ *         (the ranked scores, in rank order)
+ * ws      device workspace, >= fathom_topk_workspace_bytes(rows/group, k).
+ * 1 <= k <= FATHOM_MAX_K, 0 <= n < 2^31.                                    */
+int32_t fathom_topk(const float *scores, int32_t rows, int64_t n, int64_t ld,
+                    int32_t group, int32_t k, int32_t *idx, float *vals,
+                    void *ws, int64_t ws_bytes, void *stream);
+
+/* ---- many sessions in one launch ----------------------------------------
+ * Ragged multi-session decode: every session has its own K cache (planes,
+ * lo, hi of n keys), its own queries and plan; one launch scans all sessions
+ * (work spread over (session, kv head, key tile)), and one set of launches
+ * selects all sessions' top-k.  The descriptor array is HOST memory, read
+ * during the call only.  Fields not used by a call may be NULL.            */
+typedef struct {
+  const uint32_t *planes; /* device or pinned host, fathom_pack layout      */
+  const float *lo, *hi;   /* device fp32[hkv][d]                            */
+  int64_t n;              /* keys in this session (>= 0)                    */
+  const float *q;         /* device fp32[hq][d]                             */
+  const uint8_t *plan;    /* device uint8[hq][d]                            */
+  const uint8_t *meta;    /* NULL or uint8[hkv][n]                          */
+  float meta_scale;
+  float *logits;          /* device fp32[hq][ld_logits]                     */
+  int64_t ld_logits;
+  int32_t *idx;           /* device int32[hq/group][k] (top-k output)       */
+  float *vals;            /* device fp32[hq/group][k]                       */
+} fathom_session;
+
+int32_t fathom_scan_batched(const fathom_session *sessions, int32_t n_sessions,
+                            int32_t hkv, int32_t d, int32_t hq, void *stream);
+int32_t fathom_topk_batched(const fathom_session *sessions, int32_t n_sessions,
+                            int32_t hq, int32_t group, int32_t k, void *ws,
+                            int64_t ws_bytes, void *stream);
+
+/* ---- observability -------------------------------------------------------
+ * The plane reads themselves, for bit-exact checks: out[h][i][c] =
+ * floor(code_ic / 2^(4-t_hc)) (0 where t = 0).  out device uint8[hq][n][d]. */
+int32_t fathom_read_prefixes(const uint32_t *planes, int64_t n, int32_t hkv,
+                             int32_t d, const uint8_t *plan, int32_t hq,
+                             uint8_t *out, void *stream);
+
+/* Explainer, section 对工程落地的启发 (engineering notes): the bits each
+ * channel reads should be observable per query.  HOST-only: from a host copy
+ * of a plan, hist[t] = number of (head, channel) pairs read at depth t
+ * (t = 0..4), union_bits[g] = sum_c max_{h in group g} t_hc = plane bits per
+ * key that group g's scan reads.  union_bits may be NULL.                   */
+int32_t fathom_plan_stats(const uint8_t *plan_host, int32_t hq, int32_t d,
+                          int32_t group, uint32_t *hist,
+                          uint32_t *union_bits);
+
+/* Streaming-read probe used as the roofline denominator: reads `bytes` from
+ * `src` (device or pinned host, 16-byte aligned, bytes % 16 == 0) with every
+ * CU and writes one checksum word to device `out` (uint32[1]).  `blocks`
+ * = 0 picks a default grid.                                                 */
+int32_t fathom_probe_read(const void *src, int64_t bytes, uint32_t *out,
+                          int32_t blocks, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FATHOM_H */

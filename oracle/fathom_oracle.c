@@ -238,6 +238,39 @@ int orc_scan(const uint32_t *planes, const float *lo, const float *hi, int64_t n
   return ORC_OK;
 }
 
+/* The same scores at chosen keys only: out[h][j] = s_{keys[j]} of head h
+ * (for spot checks of large layers). */
+int orc_scan_at(const uint32_t *planes, const float *lo, const float *hi,
+                int64_t n, int hkv, int d, const float *q, const uint8_t *plan,
+                int hq, const uint8_t *meta, float meta_scale,
+                const int64_t *keys, int64_t nk, float *out) {
+  if (!planes || !lo || !hi || !q || !plan || !keys || !out || hkv < 1 ||
+      hq % hkv)
+    return ORC_BAD;
+  const int G = hq / hkv;
+  const int64_t W = orc_plane_words(n);
+  for (int h = 0; h < hq; ++h) {
+    const int g = h / G;
+    for (int64_t j = 0; j < nk; ++j) {
+      const int64_t i = keys[j];
+      if (i < 0 || i >= n) return ORC_BAD;
+      double s = 0.0;
+      for (int c = 0; c < d; ++c) {
+        int t = plan[(int64_t)h * d + c];
+        float l = lo[g * d + c], u = hi[g * d + c];
+        float delta = (u - l) * 0.0625f;
+        int r = orc_prefix(orc_code_from_planes(planes, W, d, g, c, i), t);
+        double cell = (double)delta * (double)(1 << (4 - t));
+        double deq = (double)l + ((double)r + 0.5) * cell;
+        s += (double)q[(int64_t)h * d + c] * deq;
+      }
+      if (meta) s += (double)meta_scale * (double)meta[(int64_t)g * n + i];
+      out[(int64_t)h * nk + j] = (float)s;
+    }
+  }
+  return ORC_OK;
+}
+
 /* The plane reads themselves: out[h][i][c] = t_c-bit prefix of code_ic. */
 int orc_read_prefixes(const uint32_t *planes, int64_t n, int hkv, int d,
                       const uint8_t *plan, int hq, uint8_t *out) {

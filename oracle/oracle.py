@@ -48,9 +48,10 @@ def _load():
         lib.orc_plan.argtypes = [P, I, I, I, P, P, P]
         lib.orc_plan_fixed.argtypes = [P, I, I, I, P]
         lib.orc_scan.argtypes = [P, P, P, L, I, I, P, P, I, P, F, P, L]
+        lib.orc_scan_at.argtypes = [P, P, P, L, I, I, P, P, I, P, F, P, L, P]
         lib.orc_read_prefixes.argtypes = [P, L, I, I, P, I, P]
         lib.orc_topk.argtypes = [P, I, L, L, I, I, P, P]
-        for f in ("orc_pack", "orc_plan", "orc_plan_fixed", "orc_scan",
+        for f in ("orc_pack", "orc_plan", "orc_plan_fixed", "orc_scan", "orc_scan_at",
                   "orc_read_prefixes", "orc_topk"):
             getattr(lib, f).restype = I
         _lib = lib
@@ -126,6 +127,25 @@ def scan(planes, lo, hi, n: int, q, plan_, meta=None, meta_scale: float = 0.0):
                             _ptr(plan_), hq, _ptr(meta), meta_scale, _ptr(out),
                             max(n, 1)), "scan")
     return out[:, :n]
+
+
+def scan_at(planes, lo, hi, n: int, q, plan_, keys, meta=None, meta_scale: float = 0.0):
+    """Scores of the chosen key indices only -> [hq][len(keys)] fp32."""
+    planes = np.ascontiguousarray(planes, dtype=np.uint32)
+    lo = np.ascontiguousarray(lo, dtype=np.float32)
+    hi = np.ascontiguousarray(hi, dtype=np.float32)
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    plan_ = np.ascontiguousarray(plan_, dtype=np.uint8)
+    keys = np.ascontiguousarray(keys, dtype=np.int64)
+    hkv, d = lo.shape
+    hq = q.shape[0]
+    if meta is not None:
+        meta = np.ascontiguousarray(meta, dtype=np.uint8)
+    out = np.empty((hq, keys.size), np.float32)
+    _check(_load().orc_scan_at(_ptr(planes), _ptr(lo), _ptr(hi), n, hkv, d, _ptr(q),
+                               _ptr(plan_), hq, _ptr(meta), meta_scale, _ptr(keys),
+                               keys.size, _ptr(out)), "scan_at")
+    return out
 
 
 def read_prefixes(planes, n: int, plan_, hkv: int) -> np.ndarray:

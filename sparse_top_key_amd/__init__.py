@@ -1,0 +1,282 @@
+"""Python binding of libfathom (Fathom's per-query bit-depth top-k key scan on
+MI355X).  Argument marshalling only: torch tensors provide device memory and
+the current HIP stream; every step of the path runs in the library's HIP
+kernels.  There is no CPU fallback: without the built library or a GPU every
+call raises.
+
+    planes, lo, hi, sigma2 = pack(keys)            # keys [n][hkv][128] fp16/fp32
+    plan_ = plan(q, sigma2, budget=92)              # q [hq][128] fp32
+    logits = scan(planes, lo, hi, n, q, plan_)      # [hq][n] fp32
+    idx, vals = topk(logits, k=2048)                # [hq][k]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfathom.so")
+
+D = 128
+MAX_K = 2048
+MAX_SESSIONS = 64
+F16, F32 = 0, 1
+_ERRORS = {1: "invalid argument", 2: "unsupported", 3: "HIP error", 4: "workspace"}
+
+_lib = None
+
+
+class FathomError(RuntimeError):
+    pass
+
+
+class _Session(ctypes.Structure):
+    _fields_ = [
+        ("planes", ctypes.c_void_p), ("lo", ctypes.c_void_p), ("hi", ctypes.c_void_p),
+        ("n", ctypes.c_int64), ("q", ctypes.c_void_p), ("plan", ctypes.c_void_p),
+        ("meta", ctypes.c_void_p), ("meta_scale", ctypes.c_float),
+        ("logits", ctypes.c_void_p), ("ld_logits", ctypes.c_int64),
+        ("idx", ctypes.c_void_p), ("vals", ctypes.c_void_p),
+    ]
+
+
+def lib():
+    """Load libfathom.so (raises if it is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FathomError(f"{LIB_PATH} is not built; run "
+                              "`python -m sparse_top_key_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        sig = {
+            "fathom_abi_version": (I32, []),
+            "fathom_last_error": (ctypes.c_char_p, []),
+            "fathom_plane_words": (I64, [I64]),
+            "fathom_planes_bytes": (I64, [I64, I32, I32]),
+            "fathom_pack_workspace_bytes": (I64, [I64, I32, I32]),
+            "fathom_topk_workspace_bytes": (I64, [I32, I32]),
+            "fathom_pack": (I32, [P, I32, I64, I32, I32, I64, I64, P, P, P, P, P, I64, P]),
+            "fathom_plan": (I32, [P, I32, I32, I32, P, P, P, P]),
+            "fathom_plan_fixed": (I32, [P, I32, I32, I32, P, P]),
+            "fathom_scan": (I32, [P, P, P, I64, I32, I32, P, P, I32, P, F, P, I64, P]),
+            "fathom_topk": (I32, [P, I32, I64, I64, I32, I32, P, P, P, I64, P]),
+            "fathom_scan_batched": (I32, [P, I32, I32, I32, I32, P]),
+            "fathom_topk_batched": (I32, [P, I32, I32, I32, I32, P, I64, P]),
+            "fathom_read_prefixes": (I32, [P, I64, I32, I32, P, I32, P, P]),
+            "fathom_plan_stats": (I32, [P, I32, I32, I32, P, P]),
+            "fathom_probe_read": (I32, [P, I64, P, I32, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _require_gpu(*ts: torch.Tensor):
+    if not torch.cuda.is_available():
+        raise FathomError("libfathom needs a ROCm GPU (none visible)")
+    for t in ts:
+        if t is not None and not (t.is_cuda or t.is_pinned()):
+            raise FathomError("tensor must be on the GPU (or pinned host memory)")
+
+
+def _check(rc: int, name: str):
+    if rc != 0:
+        msg = lib().fathom_last_error().decode()
+        raise FathomError(f"{name}: {_ERRORS.get(rc, rc)}: {msg}")
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def plane_words(n: int) -> int:
+    return int(lib().fathom_plane_words(n))
+
+
+def pack_workspace_bytes(n: int, hkv: int) -> int:
+    return int(lib().fathom_pack_workspace_bytes(n, hkv, D))
+
+
+def topk_workspace_bytes(out_rows: int, k: int) -> int:
+    return int(lib().fathom_topk_workspace_bytes(out_rows, k))
+
+
+@dataclass
+class Packed:
+    planes: torch.Tensor   # uint32 [hkv][d][4][W] (stored as int32)
+    lo: torch.Tensor       # fp32 [hkv][d]
+    hi: torch.Tensor
+    sigma2: torch.Tensor
+    n: int
+
+
+def pack(keys: torch.Tensor, planes: Optional[torch.Tensor] = None,
+         ws: Optional[torch.Tensor] = None) -> Packed:
+    """keys [n][hkv][d] (fp16/fp32, any token/head strides, channel stride 1)."""
+    _require_gpu(keys)
+    n, hkv, d = keys.shape
+    if keys.stride(2) != 1:
+        raise FathomError("pack: channel stride must be 1")
+    dt = {torch.float16: F16, torch.float32: F32}.get(keys.dtype)
+    if dt is None:
+        raise FathomError("pack: keys must be fp16 or fp32")
+    dev = keys.device
+    W = plane_words(n)
+    if planes is None:
+        planes = torch.empty((hkv, d, 4, W), dtype=torch.int32, device=dev)
+    lo = torch.empty((hkv, d), dtype=torch.float32, device=dev)
+    hi = torch.empty_like(lo)
+    s2 = torch.empty_like(lo)
+    need = pack_workspace_bytes(n, hkv) if n > 0 else 0
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib().fathom_pack(_p(keys), dt, n, hkv, d, keys.stride(0), keys.stride(1),
+                             _p(planes), _p(lo), _p(hi), _p(s2), _p(ws), ws.numel(),
+                             _stream(dev)), "fathom_pack")
+    return Packed(planes, lo, hi, s2, n)
+
+
+def plan(q: torch.Tensor, sigma2: torch.Tensor, budget, out=None) -> torch.Tensor:
+    """q [hq][d] fp32, sigma2 [hkv][d] fp32, budget int or sequence of hq ints."""
+    _require_gpu(q, sigma2)
+    hq, d = q.shape
+    hkv = sigma2.shape[0]
+    b = (ctypes.c_int32 * hq)(*([int(budget)] * hq if isinstance(budget, int)
+                                else [int(x) for x in budget]))
+    if out is None:
+        out = torch.empty((hq, d), dtype=torch.uint8, device=q.device)
+    _check(lib().fathom_plan(_p(q.contiguous()), hq, hkv, d, _p(sigma2.contiguous()), b,
+                             _p(out), _stream(q.device)), "fathom_plan")
+    return out
+
+
+def plan_fixed(q: torch.Tensor, r: int, out=None) -> torch.Tensor:
+    _require_gpu(q)
+    hq, d = q.shape
+    if out is None:
+        out = torch.empty((hq, d), dtype=torch.uint8, device=q.device)
+    _check(lib().fathom_plan_fixed(_p(q.contiguous()), hq, d, r, _p(out),
+                                   _stream(q.device)), "fathom_plan_fixed")
+    return out
+
+
+def scan(planes: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor, n: int,
+         q: torch.Tensor, plan_: torch.Tensor, meta: Optional[torch.Tensor] = None,
+         meta_scale: float = 0.0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """-> logits [hq][n] fp32.  planes may live in pinned host memory."""
+    _require_gpu(planes, lo, q, plan_)
+    hkv, d = lo.shape
+    hq = q.shape[0]
+    if out is None:
+        out = torch.empty((hq, max(n, 1)), dtype=torch.float32, device=q.device)
+    _check(lib().fathom_scan(_p(planes), _p(lo), _p(hi), n, hkv, d, _p(q), _p(plan_), hq,
+                             _p(meta), meta_scale, _p(out), out.stride(0),
+                             _stream(q.device)), "fathom_scan")
+    return out[:, :n]
+
+
+def topk(scores: torch.Tensor, k: int, group: int = 1, n: Optional[int] = None,
+         ws: Optional[torch.Tensor] = None, idx=None, vals=None):
+    """scores [rows][>=n] fp32 (row stride = scores.stride(0)) ->
+    (idx int32 [rows/group][k], vals fp32 [rows/group][k])."""
+    _require_gpu(scores)
+    rows = scores.shape[0]
+    n = scores.shape[1] if n is None else n
+    ro = rows // group
+    dev = scores.device
+    if idx is None:
+        idx = torch.empty((ro, k), dtype=torch.int32, device=dev)
+    if vals is None:
+        vals = torch.empty((ro, k), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(max(topk_workspace_bytes(ro, k), 1), dtype=torch.uint8, device=dev)
+    ld = max(scores.stride(0), n) if rows > 1 else max(scores.shape[1], n, 1)
+    _check(lib().fathom_topk(_p(scores), rows, n, ld, group, k, _p(idx), _p(vals), _p(ws),
+                             ws.numel(), _stream(dev)), "fathom_topk")
+    return idx, vals
+
+
+@dataclass
+class Session:
+    """One decode session of the batched calls (tensors on the GPU unless noted)."""
+    planes: torch.Tensor           # device or pinned host
+    lo: torch.Tensor
+    hi: torch.Tensor
+    n: int
+    q: torch.Tensor
+    plan: torch.Tensor
+    logits: torch.Tensor           # [hq][ld]
+    idx: Optional[torch.Tensor] = None
+    vals: Optional[torch.Tensor] = None
+    meta: Optional[torch.Tensor] = None
+    meta_scale: float = 0.0
+
+
+def _sessions(sess: Sequence[Session]):
+    arr = (_Session * len(sess))()
+    for i, s in enumerate(sess):
+        arr[i] = _Session(s.planes.data_ptr(), s.lo.data_ptr(), s.hi.data_ptr(), s.n,
+                          s.q.data_ptr(), s.plan.data_ptr(),
+                          s.meta.data_ptr() if s.meta is not None else None, s.meta_scale,
+                          s.logits.data_ptr(), s.logits.stride(0),
+                          s.idx.data_ptr() if s.idx is not None else None,
+                          s.vals.data_ptr() if s.vals is not None else None)
+    return arr
+
+
+def scan_batched(sess: Sequence[Session]):
+    s0 = sess[0]
+    hkv, d = s0.lo.shape
+    hq = s0.q.shape[0]
+    _check(lib().fathom_scan_batched(_sessions(sess), len(sess), hkv, d, hq,
+                                     _stream(s0.q.device)), "fathom_scan_batched")
+
+
+def topk_batched(sess: Sequence[Session], k: int, group: int = 1,
+                 ws: Optional[torch.Tensor] = None):
+    s0 = sess[0]
+    hq = s0.q.shape[0]
+    ro = hq // group
+    if ws is None:
+        ws = torch.empty(max(topk_workspace_bytes(ro * len(sess), k), 1), dtype=torch.uint8,
+                         device=s0.q.device)
+    _check(lib().fathom_topk_batched(_sessions(sess), len(sess), hq, group, k, _p(ws),
+                                     ws.numel(), _stream(s0.q.device)), "fathom_topk_batched")
+
+
+def read_prefixes(planes: torch.Tensor, n: int, plan_: torch.Tensor, hkv: int) -> torch.Tensor:
+    _require_gpu(plan_)
+    hq, d = plan_.shape
+    out = torch.empty((hq, n, d), dtype=torch.uint8, device=plan_.device)
+    _check(lib().fathom_read_prefixes(_p(planes), n, hkv, d, _p(plan_), hq, _p(out),
+                                      _stream(plan_.device)), "fathom_read_prefixes")
+    return out
+
+
+def plan_stats(plan_host: torch.Tensor, group: int):
+    """Host-side: (hist[5] of depths, union bits per group) of a CPU plan copy."""
+    p = plan_host.contiguous().cpu()
+    hq, d = p.shape
+    hist = (ctypes.c_uint32 * 5)()
+    ub = (ctypes.c_uint32 * (hq // group))()
+    _check(lib().fathom_plan_stats(ctypes.c_void_p(p.data_ptr()), hq, d, group, hist, ub),
+           "fathom_plan_stats")
+    return list(hist), list(ub)
+
+
+def probe_read(buf: torch.Tensor, out: torch.Tensor, blocks: int = 0):
+    """Stream-read `buf` (device or pinned host) once; out = 1-word device tensor."""
+    _check(lib().fathom_probe_read(_p(buf), buf.numel() * buf.element_size(), _p(out),
+                                   blocks, _stream(out.device)), "fathom_probe_read")

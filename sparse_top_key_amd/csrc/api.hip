@@ -1,0 +1,284 @@
+// Exported C ABI of libfathom (declared in include/fathom.h): argument
+// validation on the host, then kernel launches on the caller's stream.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "fathom_internal.h"
+
+namespace fathom {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+int32_t hip_fail(hipError_t e, const char *what) {
+  if (e == hipSuccess) return FATHOM_OK;
+  set_error("%s: %s", what, hipGetErrorString(e));
+  return FATHOM_ERR_HIP;
+}
+
+}  // namespace fathom
+
+using namespace fathom;
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) {               \
+      set_error(__VA_ARGS__);    \
+      return (code);             \
+    }                            \
+  } while (0)
+
+static hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+static int32_t check_d(int32_t d) {
+  REQUIRE(d > 0, FATHOM_ERR_INVALID_ARG, "d must be positive (got %d)", d);
+  REQUIRE(d == kD, FATHOM_ERR_UNSUPPORTED, "only d == %d is implemented (got %d)", kD, d);
+  return FATHOM_OK;
+}
+
+static int32_t check_heads(int32_t hq, int32_t hkv) {
+  REQUIRE(hkv >= 1 && hq >= 1, FATHOM_ERR_INVALID_ARG, "hq and hkv must be >= 1");
+  REQUIRE(hq % hkv == 0, FATHOM_ERR_INVALID_ARG, "hq (%d) must be a multiple of hkv (%d)",
+          hq, hkv);
+  return FATHOM_OK;
+}
+
+extern "C" {
+
+int32_t fathom_abi_version(void) { return FATHOM_ABI_VERSION; }
+
+const char *fathom_last_error(void) { return g_err; }
+
+int64_t fathom_plane_words(int64_t n) { return n < 0 ? 0 : plane_words(n); }
+
+int64_t fathom_planes_bytes(int64_t n, int32_t hkv, int32_t d) {
+  if (n < 0 || hkv < 1 || d < 1) return 0;
+  return (int64_t)hkv * d * kPlanes * plane_words(n) * (int64_t)sizeof(uint32_t);
+}
+
+int64_t fathom_pack_workspace_bytes(int64_t n, int32_t hkv, int32_t d) {
+  if (n < 1 || hkv < 1 || d != kD) return 0;
+  return pack_workspace_bytes(n, hkv);
+}
+
+int64_t fathom_topk_workspace_bytes(int32_t out_rows, int32_t k) {
+  if (out_rows < 1 || k < 1 || k > FATHOM_MAX_K) return 0;
+  return topk_workspace_bytes(out_rows);
+}
+
+int32_t fathom_pack(const void *keys, int32_t dtype, int64_t n, int32_t hkv, int32_t d,
+                    int64_t stride_tok, int64_t stride_head, uint32_t *planes, float *lo,
+                    float *hi, float *sigma2, void *ws, int64_t ws_bytes, void *stream) {
+  REQUIRE(keys && planes && lo && hi && sigma2, FATHOM_ERR_INVALID_ARG,
+          "fathom_pack: null pointer");
+  REQUIRE(dtype == FATHOM_F16 || dtype == FATHOM_F32, FATHOM_ERR_INVALID_ARG,
+          "fathom_pack: dtype must be FATHOM_F16 or FATHOM_F32 (got %d)", dtype);
+  REQUIRE(n >= 1 && n <= ((int64_t)1 << 31), FATHOM_ERR_INVALID_ARG,
+          "fathom_pack: n must be in [1, 2^31] (got %lld)", (long long)n);
+  REQUIRE(hkv >= 1, FATHOM_ERR_INVALID_ARG, "fathom_pack: hkv must be >= 1");
+  if (int32_t rc = check_d(d)) return rc;
+  REQUIRE(stride_tok >= 0 && stride_head >= 0, FATHOM_ERR_INVALID_ARG,
+          "fathom_pack: strides must be non-negative");
+  const int64_t need = pack_workspace_bytes(n, hkv);
+  REQUIRE(ws && ws_bytes >= need, FATHOM_ERR_WORKSPACE,
+          "fathom_pack: workspace of %lld bytes needed (got %lld)", (long long)need,
+          (long long)ws_bytes);
+  return launch_pack(keys, dtype, n, hkv, stride_tok, stride_head, planes, lo, hi, sigma2,
+                     ws, as_stream(stream));
+}
+
+int32_t fathom_plan(const float *q, int32_t hq, int32_t hkv, int32_t d,
+                    const float *sigma2, const int32_t *budget_bits, uint8_t *plan,
+                    void *stream) {
+  REQUIRE(q && sigma2 && budget_bits && plan, FATHOM_ERR_INVALID_ARG,
+          "fathom_plan: null pointer");
+  if (int32_t rc = check_heads(hq, hkv)) return rc;
+  if (int32_t rc = check_d(d)) return rc;
+  for (int32_t h = 0; h < hq; ++h)
+    REQUIRE(budget_bits[h] >= 0 && budget_bits[h] <= 4 * d, FATHOM_ERR_INVALID_ARG,
+            "fathom_plan: budget_bits[%d] = %d outside [0, %d]", h, budget_bits[h], 4 * d);
+  return launch_plan(q, hq, hkv, sigma2, budget_bits, plan, as_stream(stream));
+}
+
+int32_t fathom_plan_fixed(const float *q, int32_t hq, int32_t d, int32_t r, uint8_t *plan,
+                          void *stream) {
+  REQUIRE(q && plan, FATHOM_ERR_INVALID_ARG, "fathom_plan_fixed: null pointer");
+  REQUIRE(hq >= 1, FATHOM_ERR_INVALID_ARG, "fathom_plan_fixed: hq must be >= 1");
+  if (int32_t rc = check_d(d)) return rc;
+  REQUIRE(r >= 0 && r <= d, FATHOM_ERR_INVALID_ARG,
+          "fathom_plan_fixed: r = %d outside [0, %d]", r, d);
+  return launch_plan_fixed(q, hq, r, plan, as_stream(stream));
+}
+
+static int32_t check_scan_session(const fathom_session &s, int32_t hq, const char *who) {
+  REQUIRE(s.n >= 0 && s.n <= ((int64_t)1 << 31), FATHOM_ERR_INVALID_ARG,
+          "%s: n must be in [0, 2^31] (got %lld)", who, (long long)s.n);
+  if (s.n == 0) return FATHOM_OK;
+  REQUIRE(s.planes && s.lo && s.hi && s.q && s.plan && s.logits, FATHOM_ERR_INVALID_ARG,
+          "%s: null pointer", who);
+  REQUIRE(s.ld_logits >= s.n, FATHOM_ERR_INVALID_ARG, "%s: ld_logits (%lld) < n (%lld)",
+          who, (long long)s.ld_logits, (long long)s.n);
+  (void)hq;
+  return FATHOM_OK;
+}
+
+static ScanSession to_scan(const fathom_session &s) {
+  ScanSession o;
+  o.planes = s.planes;
+  o.lo = s.lo;
+  o.hi = s.hi;
+  o.n = s.n;
+  o.q = s.q;
+  o.plan = s.plan;
+  o.meta = s.meta;
+  o.meta_scale = s.meta_scale;
+  o.logits = s.logits;
+  o.ld = s.ld_logits;
+  return o;
+}
+
+int32_t fathom_scan(const uint32_t *planes, const float *lo, const float *hi, int64_t n,
+                    int32_t hkv, int32_t d, const float *q, const uint8_t *plan, int32_t hq,
+                    const uint8_t *meta, float meta_scale, float *logits, int64_t ld_logits,
+                    void *stream) {
+  if (int32_t rc = check_heads(hq, hkv)) return rc;
+  if (int32_t rc = check_d(d)) return rc;
+  fathom_session s{};
+  s.planes = planes;
+  s.lo = lo;
+  s.hi = hi;
+  s.n = n;
+  s.q = q;
+  s.plan = plan;
+  s.meta = meta;
+  s.meta_scale = meta_scale;
+  s.logits = logits;
+  s.ld_logits = ld_logits;
+  if (int32_t rc = check_scan_session(s, hq, "fathom_scan")) return rc;
+  if (n == 0) return FATHOM_OK;
+  ScanSession ss = to_scan(s);
+  return launch_scan(&ss, 1, hkv, hq, as_stream(stream));
+}
+
+int32_t fathom_scan_batched(const fathom_session *sessions, int32_t n_sessions, int32_t hkv,
+                            int32_t d, int32_t hq, void *stream) {
+  REQUIRE(sessions, FATHOM_ERR_INVALID_ARG, "fathom_scan_batched: null sessions");
+  REQUIRE(n_sessions >= 1 && n_sessions <= FATHOM_MAX_SESSIONS, FATHOM_ERR_INVALID_ARG,
+          "fathom_scan_batched: n_sessions must be in [1, %d]", FATHOM_MAX_SESSIONS);
+  if (int32_t rc = check_heads(hq, hkv)) return rc;
+  if (int32_t rc = check_d(d)) return rc;
+  ScanSession ss[FATHOM_MAX_SESSIONS];
+  int32_t m = 0;
+  for (int32_t i = 0; i < n_sessions; ++i) {
+    if (int32_t rc = check_scan_session(sessions[i], hq, "fathom_scan_batched")) return rc;
+    if (sessions[i].n > 0) ss[m++] = to_scan(sessions[i]);
+  }
+  if (m == 0) return FATHOM_OK;
+  return launch_scan(ss, m, hkv, hq, as_stream(stream));
+}
+
+static int32_t check_topk_common(int32_t rows, int32_t group, int32_t k, const char *who) {
+  REQUIRE(rows >= 1 && group >= 1 && rows % group == 0, FATHOM_ERR_INVALID_ARG,
+          "%s: rows (%d) must be a positive multiple of group (%d)", who, rows, group);
+  REQUIRE(k >= 1 && k <= FATHOM_MAX_K, FATHOM_ERR_INVALID_ARG,
+          "%s: k = %d outside [1, %d]", who, k, FATHOM_MAX_K);
+  return FATHOM_OK;
+}
+
+int32_t fathom_topk(const float *scores, int32_t rows, int64_t n, int64_t ld, int32_t group,
+                    int32_t k, int32_t *idx, float *vals, void *ws, int64_t ws_bytes,
+                    void *stream) {
+  if (int32_t rc = check_topk_common(rows, group, k, "fathom_topk")) return rc;
+  REQUIRE(idx && vals, FATHOM_ERR_INVALID_ARG, "fathom_topk: null output");
+  REQUIRE(n >= 0 && n < ((int64_t)1 << 31), FATHOM_ERR_INVALID_ARG,
+          "fathom_topk: n must be in [0, 2^31)");
+  REQUIRE(n == 0 || scores, FATHOM_ERR_INVALID_ARG, "fathom_topk: null scores");
+  REQUIRE(ld >= n, FATHOM_ERR_INVALID_ARG, "fathom_topk: ld < n");
+  const int64_t need = topk_workspace_bytes(rows / group);
+  REQUIRE(ws && ws_bytes >= need, FATHOM_ERR_WORKSPACE,
+          "fathom_topk: workspace of %lld bytes needed (got %lld)", (long long)need,
+          (long long)ws_bytes);
+  TopkSession t{scores, n, ld, idx, vals};
+  return launch_topk(&t, 1, rows / group, group, k, ws, as_stream(stream));
+}
+
+int32_t fathom_topk_batched(const fathom_session *sessions, int32_t n_sessions, int32_t hq,
+                            int32_t group, int32_t k, void *ws, int64_t ws_bytes,
+                            void *stream) {
+  REQUIRE(sessions, FATHOM_ERR_INVALID_ARG, "fathom_topk_batched: null sessions");
+  REQUIRE(n_sessions >= 1 && n_sessions <= FATHOM_MAX_SESSIONS, FATHOM_ERR_INVALID_ARG,
+          "fathom_topk_batched: n_sessions must be in [1, %d]", FATHOM_MAX_SESSIONS);
+  if (int32_t rc = check_topk_common(hq, group, k, "fathom_topk_batched")) return rc;
+  TopkSession ts[FATHOM_MAX_SESSIONS];
+  for (int32_t i = 0; i < n_sessions; ++i) {
+    const fathom_session &s = sessions[i];
+    REQUIRE(s.idx && s.vals, FATHOM_ERR_INVALID_ARG, "fathom_topk_batched: null output");
+    REQUIRE(s.n >= 0 && s.n < ((int64_t)1 << 31), FATHOM_ERR_INVALID_ARG,
+            "fathom_topk_batched: n must be in [0, 2^31)");
+    REQUIRE(s.n == 0 || s.logits, FATHOM_ERR_INVALID_ARG, "fathom_topk_batched: null logits");
+    REQUIRE(s.ld_logits >= s.n, FATHOM_ERR_INVALID_ARG, "fathom_topk_batched: ld < n");
+    ts[i] = TopkSession{s.logits, s.n, s.ld_logits, s.idx, s.vals};
+  }
+  const int64_t need = topk_workspace_bytes((int64_t)n_sessions * (hq / group));
+  REQUIRE(ws && ws_bytes >= need, FATHOM_ERR_WORKSPACE,
+          "fathom_topk_batched: workspace of %lld bytes needed (got %lld)", (long long)need,
+          (long long)ws_bytes);
+  return launch_topk(ts, n_sessions, hq / group, group, k, ws, as_stream(stream));
+}
+
+int32_t fathom_read_prefixes(const uint32_t *planes, int64_t n, int32_t hkv, int32_t d,
+                             const uint8_t *plan, int32_t hq, uint8_t *out, void *stream) {
+  REQUIRE(planes && plan && out, FATHOM_ERR_INVALID_ARG, "fathom_read_prefixes: null pointer");
+  REQUIRE(n >= 0 && n <= ((int64_t)1 << 31), FATHOM_ERR_INVALID_ARG,
+          "fathom_read_prefixes: bad n");
+  if (int32_t rc = check_heads(hq, hkv)) return rc;
+  if (int32_t rc = check_d(d)) return rc;
+  return launch_read_prefixes(planes, n, hkv, plan, hq, out, as_stream(stream));
+}
+
+int32_t fathom_plan_stats(const uint8_t *plan_host, int32_t hq, int32_t d, int32_t group,
+                          uint32_t *hist, uint32_t *union_bits) {
+  REQUIRE(plan_host && hist, FATHOM_ERR_INVALID_ARG, "fathom_plan_stats: null pointer");
+  REQUIRE(hq >= 1 && d >= 1 && group >= 1 && hq % group == 0, FATHOM_ERR_INVALID_ARG,
+          "fathom_plan_stats: bad shape");
+  for (int t = 0; t < 5; ++t) hist[t] = 0;
+  for (int32_t h = 0; h < hq; ++h)
+    for (int32_t c = 0; c < d; ++c) {
+      const uint8_t t = plan_host[(int64_t)h * d + c];
+      REQUIRE(t <= 4, FATHOM_ERR_INVALID_ARG, "fathom_plan_stats: depth %d > 4", (int)t);
+      ++hist[t];
+    }
+  if (union_bits) {
+    for (int32_t g = 0; g < hq / group; ++g) {
+      uint32_t bits = 0;
+      for (int32_t c = 0; c < d; ++c) {
+        uint8_t u = 0;
+        for (int32_t j = 0; j < group; ++j) {
+          const uint8_t t = plan_host[(int64_t)(g * group + j) * d + c];
+          u = t > u ? t : u;
+        }
+        bits += u;
+      }
+      union_bits[g] = bits;
+    }
+  }
+  return FATHOM_OK;
+}
+
+int32_t fathom_probe_read(const void *src, int64_t bytes, uint32_t *out, int32_t blocks,
+                          void *stream) {
+  REQUIRE(src && out, FATHOM_ERR_INVALID_ARG, "fathom_probe_read: null pointer");
+  REQUIRE(bytes > 0 && bytes % 16 == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0,
+          FATHOM_ERR_INVALID_ARG, "fathom_probe_read: need 16-byte aligned, 16-byte sized");
+  REQUIRE(blocks >= 0, FATHOM_ERR_INVALID_ARG, "fathom_probe_read: blocks < 0");
+  return launch_probe_read(src, bytes, out, blocks, as_stream(stream));
+}
+
+}  // extern "C"

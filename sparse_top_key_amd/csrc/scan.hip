@@ -1,0 +1,377 @@
+// Variable-depth plane scan (explainer, section 核心方法, read side): every
+// query head reads only the top t_c planes of each channel and scores all n
+// keys; the unread low bits sit at their midpoint.
+//
+// Arithmetic.  With delta_c = (hi_c - lo_c)/16 and m = the value of the top
+// t planes placed at their own bit positions (code with its low 4-t bits
+// cleared),
+//     s_i = C_h + sum_c gamma_hc * m_ic,
+//     gamma_hc = q_hc * delta_c            (0 when t_hc = 0),
+//     C_h = sum_c q_hc * (lo_c + delta_c * 2^(3 - t_hc))   (fp64, rounded once).
+// The per-key sum has one fp32 term per channel read, so its rounding error
+// is bounded by (terms + 1) * 2^-24 * sum|terms|, well inside 1e-5 * A_h.
+//
+// Work decomposition (MI355X-first; no counterpart on the pages).
+//  * A block takes one (session, kv head) and a run of 8192-key tiles; its 4
+//    waves take 2048 keys each, i.e. one 64-word block of every plane row:
+//    lane w owns plane word w (keys 32w..32w+31), so every plane load is one
+//    coalesced 256-byte wave access -- from HBM or zero-copy from pinned host
+//    memory, through the same code.
+//  * Slots: the distinct (channel, depth) pairs the kv head's query heads
+//    read.  A slot of depth u loads the top u planes of its channel (the
+//    union across heads is loaded from memory once; a shallower slot of the
+//    same channel re-reads cached words).  Each head uses exactly the slots of
+//    its own depths, so no masking is ever needed.  Slots are ordered by the
+//    set of heads that use them, then by channel, and processed 8 at a time;
+//    a group of 8 slots skips the heads that use none of them.
+//  * Per group: 32 plane rows (8 slots x 4 planes, unread planes = 0) are
+//    bit-transposed in registers (32x32 transpose, 5 stages of shift/select),
+//    giving per key a word of 8 nibble codes.  Nibbles become fp32 through
+//    byte conversions, then one fp32 FMA per (head, slot, key).
+//  * The next group's plane words are loaded while the current group is
+//    computed.
+#include "fathom_internal.h"
+
+namespace fathom {
+namespace {
+
+constexpr int kScanThreads = 256;
+constexpr int kWaveKeys = 2048;                   // 64 lanes x 32 keys
+constexpr int kTileKeys = kWaveKeys * (kScanThreads / 64);
+constexpr int kMaxSlots = kD * kPlanes;           // (channel, depth) pairs
+constexpr int kMaxGroups = kMaxSlots / 8;
+constexpr int kMaxGH = 4;                          // heads per launch chunk
+
+struct ScanSess {
+  const uint32_t *planes;
+  const float *lo, *hi, *q;
+  const uint8_t *plan, *meta;
+  float *logits;
+  int64_t n, W, ld;
+  float meta_scale;
+  int32_t block_begin;     // first block of this session in the grid
+  int32_t tiles_per_block;
+  int32_t vec_out;         // float4 logits stores are aligned
+};
+
+struct ScanArgs {
+  ScanSess s[kSessPerLaunch];
+  int32_t n_sess, hkv, group, head0;
+};
+
+// ---- 32x32 bit transpose ----------------------------------------------------
+// On entry x[r] bit k = element (r, k); on exit x[k] bit r = element (r, k).
+// Stage S swaps the off-diagonal SxS blocks of every 2Sx2S block.
+template <int S, uint32_t M>
+__device__ __forceinline__ void transpose_stage(uint32_t (&x)[32]) {
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    if ((r & S) == 0) {
+      const uint32_t a = x[r], b = x[r + S];
+      x[r] = (a & M) | ((b << S) & ~M);
+      x[r + S] = ((a >> S) & M) | (b & ~M);
+    }
+  }
+}
+
+__device__ __forceinline__ void transpose32(uint32_t (&x)[32]) {
+  transpose_stage<16, 0x0000FFFFu>(x);
+  transpose_stage<8, 0x00FF00FFu>(x);
+  transpose_stage<4, 0x0F0F0F0Fu>(x);
+  transpose_stage<2, 0x33333333u>(x);
+  transpose_stage<1, 0x55555555u>(x);
+}
+
+__device__ __forceinline__ int uniform(int v) {
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Rows 4j+p of x receive bit p of slot (grp*8 + j)'s code: plane slot 3-p of
+// its channel, loaded only when the slot's depth covers it.
+__device__ __forceinline__ void load_group(const uint32_t *__restrict__ pw,
+                                           int64_t W, const int16_t *slot_desc,
+                                           int grp, uint32_t (&x)[32]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int desc = uniform(slot_desc[grp * 8 + j]);
+    const int c = desc >> 3, dep = desc & 7;
+    const uint32_t *pc = pw + (int64_t)c * kPlanes * W;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t v = 0;
+      if (3 - p < dep) v = __builtin_nontemporal_load(pc + (3 - p) * W);
+      x[4 * j + p] = v;
+    }
+  }
+}
+
+template <int GH>
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
+  // ---- which session / kv head / tiles ------------------------------------
+  int si = 0;
+  for (int j = 1; j < a.n_sess; ++j)
+    if ((int)blockIdx.x >= a.s[j].block_begin) si = j;
+  const ScanSess &S = a.s[si];
+  const int local = blockIdx.x - S.block_begin;
+  const int g = local % a.hkv;
+  const int tile0 = (local / a.hkv) * S.tiles_per_block;
+  const int64_t n = S.n;
+  const int head_base = g * a.group + a.head0;
+
+  __shared__ uint8_t s_t[GH][kD];
+  __shared__ int32_t s_key[kMaxSlots];
+  __shared__ int16_t s_desc[kMaxSlots];       // (channel << 3) | depth
+  __shared__ float s_gam[kMaxSlots][GH];       // gamma per slot and head
+  __shared__ uint8_t s_gmask[kMaxGroups];      // heads using any slot of a group
+  __shared__ double s_c[GH][kD];
+  __shared__ float s_C[GH];
+  __shared__ int s_nslots;
+
+  const int tid = threadIdx.x;
+  if (tid == 0) s_nslots = 0;
+  if (tid < kD) {
+    const int c = tid;
+    const float lo = S.lo[g * kD + c];
+    const float delta = __fmul_rn(__fsub_rn(S.hi[g * kD + c], lo), 0.0625f);
+#pragma unroll
+    for (int j = 0; j < GH; ++j) {
+      const int t = S.plan[(int64_t)(head_base + j) * kD + c];
+      s_t[j][c] = (uint8_t)t;
+      // C_h term q * (lo + delta * 2^(3-t)) in fp64 (exact operands)
+      const double mid = (double)lo + (double)delta * (double)(1 << (4 - t)) * 0.5;
+      s_c[j][c] = (double)S.q[(int64_t)(head_base + j) * kD + c] * mid;
+    }
+  }
+  __syncthreads();
+  // ---- slots: distinct (channel, depth) pairs, keyed by (head set, c, depth)
+  for (int e = tid; e < kD * 4; e += kScanThreads) {
+    const int c = e >> 2, dep = (e & 3) + 1;
+    int memb = 0;
+#pragma unroll
+    for (int j = 0; j < GH; ++j) memb |= (s_t[j][c] == dep) << j;
+    if (memb) {
+      // larger head sets first; then channel, depth
+      const int key = ((15 - __popc(memb)) << 16) | (memb << 11) | (c << 2) | (dep - 1);
+      s_key[atomicAdd(&s_nslots, 1)] = key;
+    }
+  }
+  // fp64 reduction of C_h (fixed tree order)
+  for (int stride = kD / 2; stride > 0; stride >>= 1) {
+    __syncthreads();
+    if (tid < stride) {
+#pragma unroll
+      for (int j = 0; j < GH; ++j) s_c[j][tid] += s_c[j][tid + stride];
+    }
+  }
+  __syncthreads();
+  if (tid < GH) s_C[tid] = (float)s_c[tid][0];
+  const int nslots = s_nslots;
+  const int ngroups = (nslots + 7) >> 3;
+  for (int e = tid; e < nslots; e += kScanThreads) {
+    const int key = s_key[e];
+    int rank = 0;
+    for (int j = 0; j < nslots; ++j) rank += s_key[j] < key;
+    const int c = (key >> 2) & 127, dep = (key & 3) + 1;
+    const int memb = (key >> 11) & 31;
+    s_desc[rank] = (int16_t)((c << 3) | dep);
+    const float lo = S.lo[g * kD + c];
+    const float delta = __fmul_rn(__fsub_rn(S.hi[g * kD + c], lo), 0.0625f);
+#pragma unroll
+    for (int j = 0; j < GH; ++j)
+      s_gam[rank][j] = ((memb >> j) & 1)
+                           ? __fmul_rn(S.q[(int64_t)(head_base + j) * kD + c], delta)
+                           : 0.0f;
+  }
+  for (int e = nslots + tid; e < ngroups * 8; e += kScanThreads) {
+    s_desc[e] = 0;  // padding slot: depth 0, reads nothing, weight 0
+#pragma unroll
+    for (int j = 0; j < GH; ++j) s_gam[e][j] = 0.0f;
+  }
+  __syncthreads();
+  for (int gi = tid; gi < ngroups; gi += kScanThreads) {
+    int m = 0;
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int h = 0; h < GH; ++h) m |= (s_gam[gi * 8 + j][h] != 0.0f) << h;
+    s_gmask[gi] = (uint8_t)m;
+  }
+  __syncthreads();
+
+  // ---- main loop ------------------------------------------------------------
+  const int wave = tid >> 6, lane = tid & 63;
+  const uint32_t *gplanes = S.planes + (int64_t)g * kD * kPlanes * S.W;
+  float C[GH];
+#pragma unroll
+  for (int j = 0; j < GH; ++j) C[j] = s_C[j];
+
+  for (int tt = 0; tt < S.tiles_per_block; ++tt) {
+    const int64_t wkey0 = (int64_t)(tile0 + tt) * kTileKeys + (int64_t)wave * kWaveKeys;
+    if (wkey0 >= n) break;
+    const int64_t word = wkey0 / 32 + lane;
+    const uint32_t *pw = gplanes + word;
+
+    float acc[GH][32];
+#pragma unroll
+    for (int j = 0; j < GH; ++j)
+#pragma unroll
+      for (int k = 0; k < 32; ++k) acc[j][k] = C[j];
+
+    uint32_t xn[32];
+    if (ngroups > 0) load_group(pw, S.W, s_desc, 0, xn);
+    for (int grp = 0; grp < ngroups; ++grp) {
+      uint32_t x[32];
+#pragma unroll
+      for (int r = 0; r < 32; ++r) x[r] = xn[r];
+      if (grp + 1 < ngroups) load_group(pw, S.W, s_desc, grp + 1, xn);
+      transpose32(x);
+      const int gm = uniform(s_gmask[grp]);
+      float gv[GH][8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int h = 0; h < GH; ++h) gv[h][j] = s_gam[grp * 8 + j][h];
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const uint32_t y = x[k];
+        const uint32_t e = y & 0x0F0F0F0Fu;        // slots 0,2,4,6
+        const uint32_t o = (y >> 4) & 0x0F0F0F0Fu; // slots 1,3,5,7
+        float f[8];
+        f[0] = (float)(e & 0xFF);
+        f[1] = (float)(o & 0xFF);
+        f[2] = (float)((e >> 8) & 0xFF);
+        f[3] = (float)((o >> 8) & 0xFF);
+        f[4] = (float)((e >> 16) & 0xFF);
+        f[5] = (float)((o >> 16) & 0xFF);
+        f[6] = (float)(e >> 24);
+        f[7] = (float)(o >> 24);
+#pragma unroll
+        for (int h = 0; h < GH; ++h) {
+          if ((gm >> h) & 1) {
+            float s = acc[h][k];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s = __fmaf_rn(gv[h][j], f[j], s);
+            acc[h][k] = s;
+          }
+        }
+      }
+    }
+
+    // ---- optional 8-bit side stream (fixed-width baseline) ----------------
+    const int64_t key0 = word * 32;
+    if (S.meta) {
+      const uint8_t *mp = S.meta + (int64_t)g * n + key0;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const float m = key0 + k < n ? (float)mp[k] : 0.0f;
+#pragma unroll
+        for (int h = 0; h < GH; ++h) acc[h][k] = __fmaf_rn(S.meta_scale, m, acc[h][k]);
+      }
+    }
+
+    // ---- logits ------------------------------------------------------------
+#pragma unroll
+    for (int h = 0; h < GH; ++h) {
+      float *out = S.logits + (int64_t)(head_base + h) * S.ld + key0;
+      if (S.vec_out && key0 + 32 <= n) {
+#pragma unroll
+        for (int k = 0; k < 32; k += 4)
+          *reinterpret_cast<float4 *>(out + k) =
+              make_float4(acc[h][k], acc[h][k + 1], acc[h][k + 2], acc[h][k + 3]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 32; ++k)
+          if (key0 + k < n) out[k] = acc[h][k];
+      }
+    }
+  }
+}
+
+// out[h][i][c] = floor(code_ic / 2^(4 - t_hc)): the planes as a query reads them.
+__global__ __launch_bounds__(256) void read_prefixes_kernel(
+    const uint32_t *__restrict__ planes, int64_t n, int64_t W, int32_t group,
+    const uint8_t *__restrict__ plan, uint8_t *__restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
+  const int c = threadIdx.x & 127;
+  const int h = blockIdx.y;
+  if (i >= n) return;
+  const int g = h / group;
+  const int t = plan[(int64_t)h * kD + c];
+  const uint32_t *pc = planes + ((int64_t)g * kD + c) * kPlanes * W + i / 32;
+  int v = 0;
+  for (int s = 0; s < t; ++s) v = (v << 1) | ((pc[s * W] >> (i % 32)) & 1u);
+  out[((int64_t)h * n + i) * kD + c] = (uint8_t)v;
+}
+
+}  // namespace
+
+int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv,
+                    int32_t hq, hipStream_t s) {
+  const int32_t group = hq / hkv;
+  int dev = 0;
+  hipGetDevice(&dev);
+  int ncu = 256;
+  hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  for (int32_t s0 = 0; s0 < n_sess; s0 += kSessPerLaunch) {
+    const int32_t cnt = std::min(kSessPerLaunch, n_sess - s0);
+    for (int32_t head0 = 0; head0 < group; head0 += kMaxGH) {
+      const int GH = std::min(kMaxGH, group - head0);
+      ScanArgs a{};
+      a.n_sess = cnt;
+      a.hkv = hkv;
+      a.group = group;
+      a.head0 = head0;
+      int64_t total_tiles = 0;
+      for (int j = 0; j < cnt; ++j)
+        total_tiles += (sess[s0 + j].n + kTileKeys - 1) / kTileKeys * hkv;
+      // about 4 blocks per CU overall; each block amortises its plan set-up
+      // over several tiles of one (session, kv head)
+      const int64_t target_blocks = (int64_t)ncu * 4;
+      int32_t blocks = 0;
+      for (int j = 0; j < cnt; ++j) {
+        const ScanSession &in = sess[s0 + j];
+        ScanSess &o = a.s[j];
+        o.planes = in.planes;
+        o.lo = in.lo;
+        o.hi = in.hi;
+        o.q = in.q;
+        o.plan = in.plan;
+        o.meta = in.meta;
+        o.logits = in.logits;
+        o.n = in.n;
+        o.W = plane_words(in.n);
+        o.ld = in.ld;
+        o.meta_scale = in.meta_scale;
+        o.vec_out = ((reinterpret_cast<uintptr_t>(in.logits) & 15) == 0) && (in.ld % 4 == 0);
+        const int64_t tiles = (in.n + kTileKeys - 1) / kTileKeys;
+        int64_t tpb = 1;
+        if (total_tiles > target_blocks)
+          tpb = (total_tiles + target_blocks - 1) / target_blocks;
+        tpb = std::max<int64_t>(1, std::min<int64_t>(tpb, tiles));
+        o.tiles_per_block = (int32_t)tpb;
+        o.block_begin = blocks;
+        blocks += (int32_t)(((tiles + tpb - 1) / tpb) * hkv);
+      }
+      if (blocks == 0) continue;
+      switch (GH) {
+        case 1: hipLaunchKernelGGL(scan_kernel<1>, dim3(blocks), dim3(kScanThreads), 0, s, a); break;
+        case 2: hipLaunchKernelGGL(scan_kernel<2>, dim3(blocks), dim3(kScanThreads), 0, s, a); break;
+        case 3: hipLaunchKernelGGL(scan_kernel<3>, dim3(blocks), dim3(kScanThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL(scan_kernel<4>, dim3(blocks), dim3(kScanThreads), 0, s, a); break;
+      }
+      int32_t rc = hip_fail(hipGetLastError(), "scan launch");
+      if (rc) return rc;
+    }
+  }
+  return FATHOM_OK;
+}
+
+int32_t launch_read_prefixes(const uint32_t *planes, int64_t n, int32_t hkv,
+                             const uint8_t *plan, int32_t hq, uint8_t *out,
+                             hipStream_t s) {
+  if (n == 0) return FATHOM_OK;
+  hipLaunchKernelGGL(read_prefixes_kernel, dim3((unsigned)((n + 1) / 2), hq), dim3(256),
+                     0, s, planes, n, plane_words(n), hq / hkv, plan, out);
+  return hip_fail(hipGetLastError(), "read_prefixes launch");
+}
+
+}  // namespace fathom

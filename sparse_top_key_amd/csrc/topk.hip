@@ -1,0 +1,402 @@
+// Top-k key selection per decode step (explainer, problem statement: each
+// generated token keeps the top k of the n scored keys).  Ranking: score
+// descending, then index ascending; results are those of a full sort.
+//
+// Three launches per call (MI355X-first design; the pages give none):
+//   topk_sample   one block per output row: reads a sample of the row
+//                 (64-score runs spread evenly, about 16K scores), and radix-
+//                 selects a threshold T expected to leave about 2.5k scores
+//                 at or above it.  Rows of at most 8192 scores take T = 0 (all).
+//   topk_compact  the whole grid streams every row once and appends the
+//                 (score key, index) pairs >= T to the row's candidate list
+//                 (wave ballots, one atomic per wave and batch).
+//   topk_final    one block per output row: if the candidates hold at least k
+//                 and at most 8192 entries they contain the exact top k (every
+//                 score >= T is present), which are sorted in LDS (bitonic on
+//                 64-bit (key, ~index) words) and written out.  Otherwise the
+//                 block recomputes the row exactly: a 3-pass radix select over
+//                 the whole row finds the k-th key, an index-ordered pass
+//                 gathers the winners (ties at the k-th key by lowest index),
+//                 and the same LDS sort orders them.
+// Scores map to order-preserving uint32 keys after adding +0 (so -0 ranks as
+// +0); a GQA group's score is its rows' fp32 scores added in fp64, in row
+// order, rounded once.
+#include "fathom_internal.h"
+
+namespace fathom {
+namespace {
+
+constexpr int kBig = 1024;            // threads of the per-row kernels
+constexpr int kCompactThreads = 256;
+constexpr int kCompactChunk = 16384;  // scores per compact block
+constexpr int kRun = 64;              // contiguous scores per sample run
+constexpr int kHistBins = 2048;
+
+struct TopkSess {
+  const float *scores;
+  int64_t n, ld;
+  int32_t *idx;
+  float *vals;
+};
+
+struct TopkArgs {
+  TopkSess s[kSessPerLaunch];
+  int32_t rows_per_sess, group, k;
+  uint32_t *thr;
+  uint32_t *cnt;
+  uint64_t *cand;
+};
+
+__device__ __forceinline__ uint32_t to_key(float x) {
+  const uint32_t u = __float_as_uint(__fadd_rn(x, 0.0f));
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__device__ __forceinline__ float group_score(const float *__restrict__ row, int64_t ld,
+                                             int group, int64_t i) {
+  if (group == 1) return row[i];
+  double acc = 0.0;
+  for (int j = 0; j < group; ++j) acc = __dadd_rn(acc, (double)row[(int64_t)j * ld + i]);
+  return (float)acc;
+}
+
+struct RowRef {
+  const TopkSess *s;
+  const float *row;
+};
+
+__device__ __forceinline__ RowRef row_ref(const TopkArgs &a, int o) {
+  const int si = o / a.rows_per_sess;
+  const int r = o % a.rows_per_sess;
+  RowRef ref;
+  ref.s = &a.s[si];
+  ref.row = a.s[si].scores + (int64_t)r * a.group * a.s[si].ld;
+  return ref;
+}
+
+// Inclusive scan over the 1024 threads of a block (thread order).
+__device__ int block_inclusive_scan(int v, int *wave_tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off);
+    if (lane >= off) v += u;
+  }
+  if (lane == 63) wave_tot[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    int t = lane < kBig / 64 ? wave_tot[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int u = __shfl_up(t, off);
+      if (lane >= off) t += u;
+    }
+    if (lane < kBig / 64) wave_tot[lane] = t;
+  }
+  __syncthreads();
+  const int r = v + (wave > 0 ? wave_tot[wave - 1] : 0);
+  __syncthreads();
+  return r;
+}
+
+// Given hist[nbins] of the digits still in play, find digit d such that
+// (#digits > d) < rem <= (#digits >= d).  Returns d; *above = #digits > d.
+__device__ int find_digit(const int *hist, int nbins, int rem, int *above,
+                          int *wave_tot, int *s_res) {
+  // thread t owns digits hi = nbins-1-2t and hi-1 (descending order)
+  const int t = threadIdx.x;
+  const int d1 = nbins - 1 - 2 * t, d2 = d1 - 1;
+  const int c1 = d1 >= 0 ? hist[d1] : 0;
+  const int c2 = d2 >= 0 ? hist[d2] : 0;
+  const int incl = block_inclusive_scan(c1 + c2, wave_tot);
+  const int excl = incl - c1 - c2;
+  if (excl < rem && rem <= incl) {
+    if (excl + c1 >= rem) {
+      s_res[0] = d1;
+      s_res[1] = excl;
+    } else {
+      s_res[0] = d2;
+      s_res[1] = excl + c1;
+    }
+  }
+  __syncthreads();
+  const int d = s_res[0];
+  *above = s_res[1];
+  __syncthreads();
+  return d;
+}
+
+// Bitonic sort of s[0..P) descending (P a power of two, P <= kCandCap).
+__device__ void bitonic_desc(uint64_t *s, int P) {
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      __syncthreads();
+      for (int t = threadIdx.x; t < P / 2; t += kBig) {
+        const int lo = 2 * t - (t & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const uint64_t a = s[lo], b = s[hi];
+        if (desc ? (a < b) : (a > b)) {
+          s[lo] = b;
+          s[hi] = a;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ uint64_t compose(uint32_t key, int64_t i) {
+  return ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)i);
+}
+
+__device__ void write_out(const TopkSess &S, int r, int k, const uint64_t *s, int m) {
+  int32_t *idx = S.idx + (int64_t)r * k;
+  float *vals = S.vals + (int64_t)r * k;
+  for (int j = threadIdx.x; j < k; j += kBig) {
+    if (j < m) {
+      const uint64_t c = s[j];
+      idx[j] = (int32_t)(~(uint32_t)c);
+      vals[j] = from_key((uint32_t)(c >> 32));
+    } else {
+      idx[j] = -1;
+      vals[j] = -INFINITY;
+    }
+  }
+}
+
+// ---- sample -> threshold -----------------------------------------------------
+__global__ __launch_bounds__(kBig) void topk_sample_kernel(TopkArgs a) {
+  __shared__ uint32_t keys[kSampleTarget + kRun];
+  __shared__ int hist[kHistBins];
+  __shared__ int wave_tot[16];
+  __shared__ int s_res[2];
+  const int o = blockIdx.x;
+  const RowRef R = row_ref(a, o);
+  const int64_t n = R.s->n, ld = R.s->ld;
+  if (threadIdx.x == 0) a.cnt[o] = 0;
+  if (n <= kCandCap) {
+    if (threadIdx.x == 0) a.thr[o] = 0;
+    return;
+  }
+  // runs of kRun scores every `stride` scores, about kSampleTarget in all
+  int64_t stride = (n * kRun + kSampleTarget - 1) / kSampleTarget;
+  stride = (stride + kRun - 1) / kRun * kRun;
+  if (stride < kRun) stride = kRun;
+  const int runs = (int)((n + stride - 1) / stride);
+  const int m = runs * kRun;
+  for (int e = threadIdx.x; e < m; e += kBig) {
+    const int64_t pos = (int64_t)(e / kRun) * stride + (e % kRun);
+    keys[e] = pos < n ? to_key(group_score(R.row, ld, a.group, pos)) : 0u;
+  }
+  // rank of the threshold inside the sample: expect ~2.5k scores >= T
+  int64_t rs = ((int64_t)5 * a.k * m + 2 * n - 1) / (2 * n);
+  if (rs < 1) rs = 1;
+  if (rs > m) rs = m;
+  int rem = (int)rs;
+  uint32_t prefix = 0, pmask = 0;
+  const int shifts[3] = {21, 10, 0};
+  const int bits[3] = {11, 11, 10};
+  for (int pass = 0; pass < 3; ++pass) {
+    const int sh = shifts[pass], nb = 1 << bits[pass];
+    for (int b = threadIdx.x; b < kHistBins; b += kBig) hist[b] = 0;
+    __syncthreads();
+    for (int e = threadIdx.x; e < m; e += kBig) {
+      const uint32_t v = keys[e];
+      if ((v & pmask) == prefix) atomicAdd(&hist[(v >> sh) & (nb - 1)], 1);
+    }
+    __syncthreads();
+    int above = 0;
+    const int d = find_digit(hist, nb, rem, &above, wave_tot, s_res);
+    rem -= above;
+    prefix |= (uint32_t)d << sh;
+    pmask |= (uint32_t)(nb - 1) << sh;
+  }
+  if (threadIdx.x == 0) a.thr[o] = prefix;
+}
+
+// ---- stream the rows, keep scores >= T ----------------------------------------
+__global__ __launch_bounds__(kCompactThreads) void topk_compact_kernel(TopkArgs a) {
+  const int o = blockIdx.y;
+  const RowRef R = row_ref(a, o);
+  const int64_t n = R.s->n, ld = R.s->ld;
+  const int64_t base = (int64_t)blockIdx.x * kCompactChunk;
+  if (base >= n) return;
+  const uint32_t T = a.thr[o];
+  uint32_t *cnt = a.cnt + o;
+  uint64_t *cand = a.cand + (int64_t)o * kCandCap;
+  const int lane = threadIdx.x & 63;
+  const bool vec = a.group == 1 && ((reinterpret_cast<uintptr_t>(R.row) & 15) == 0);
+  for (int it = 0; it < kCompactChunk / (kCompactThreads * 4); ++it) {
+    const int64_t i0 = base + (int64_t)it * kCompactThreads * 4 + threadIdx.x * 4;
+    float v[4];
+    if (vec && i0 + 3 < n) {
+      const float4 f = *reinterpret_cast<const float4 *>(R.row + i0);
+      v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[e] = i0 + e < n ? group_score(R.row, ld, a.group, i0 + e) : 0.0f;
+    }
+    uint32_t key[4];
+    bool pred[4];
+    uint64_t bal[4];
+    int total = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      key[e] = to_key(v[e]);
+      pred[e] = (i0 + e < n) && key[e] >= T;
+      bal[e] = __ballot(pred[e]);
+      total += __popcll(bal[e]);
+    }
+    if (total == 0) continue;
+    uint32_t start = 0;
+    if (lane == 0) start = atomicAdd(cnt, (uint32_t)total);
+    start = __shfl(start, 0);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (pred[e]) {
+        const uint32_t pos = start + __popcll(bal[e] & below);
+        if (pos < (uint32_t)kCandCap) cand[pos] = compose(key[e], i0 + e);
+      }
+      start += __popcll(bal[e]);
+    }
+  }
+}
+
+// ---- exact selection of each row's top k -------------------------------------
+__global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
+  __shared__ uint64_t s[kCandCap];
+  __shared__ int hist[kHistBins];
+  __shared__ int wave_tot[16];
+  __shared__ int s_res[2];
+  __shared__ int s_count;
+  const int o = blockIdx.x;
+  const RowRef R = row_ref(a, o);
+  const TopkSess &S = *R.s;
+  const int r = o % a.rows_per_sess;
+  const int64_t n = S.n, ld = S.ld;
+  const int k = a.k;
+  const int kk = (int)(n < k ? n : k);
+  const uint32_t cnt = a.cnt[o];
+  const bool fast = (n <= kCandCap) || (cnt >= (uint32_t)k && cnt <= (uint32_t)kCandCap);
+  if (fast) {
+    const int m = (int)cnt;
+    int P = 1;
+    while (P < m) P <<= 1;
+    const uint64_t *cand = a.cand + (int64_t)o * kCandCap;
+    for (int j = threadIdx.x; j < P; j += kBig) s[j] = j < m ? cand[j] : 0ull;
+    bitonic_desc(s, P);
+    write_out(S, r, k, s, kk);
+    return;
+  }
+  // exact recomputation over the whole row
+  int rem = kk;
+  uint32_t prefix = 0, pmask = 0;
+  const int shifts[3] = {21, 10, 0};
+  const int bits[3] = {11, 11, 10};
+  for (int pass = 0; pass < 3; ++pass) {
+    const int sh = shifts[pass], nb = 1 << bits[pass];
+    for (int b = threadIdx.x; b < kHistBins; b += kBig) hist[b] = 0;
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < n; i += kBig) {
+      const uint32_t v = to_key(group_score(R.row, ld, a.group, i));
+      if ((v & pmask) == prefix) atomicAdd(&hist[(v >> sh) & (nb - 1)], 1);
+    }
+    __syncthreads();
+    int above = 0;
+    const int d = find_digit(hist, nb, rem, &above, wave_tot, s_res);
+    rem -= above;
+    prefix |= (uint32_t)d << sh;
+    pmask |= (uint32_t)(nb - 1) << sh;
+  }
+  const uint32_t kth = prefix;  // key of the kk-th largest score
+  const int need_eq = rem;      // how many scores equal to it are kept
+  if (threadIdx.x == 0) s_count = 0;
+  __syncthreads();
+  int eq_seen = 0;
+  for (int64_t b0 = 0; b0 < n; b0 += (int64_t)kBig * 4) {
+    uint32_t key[4];
+    int eqc = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t i = b0 + threadIdx.x * 4 + e;
+      key[e] = i < n ? to_key(group_score(R.row, ld, a.group, i)) : 0u;
+      eqc += (i < n && key[e] == kth);
+    }
+    const int incl = block_inclusive_scan(eqc, wave_tot);
+    int rank = eq_seen + incl - eqc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t i = b0 + threadIdx.x * 4 + e;
+      if (i >= n) continue;
+      bool take = key[e] > kth;
+      if (key[e] == kth) {
+        take = rank < need_eq;
+        ++rank;
+      }
+      if (take) {
+        const int pos = atomicAdd(&s_count, 1);
+        s[pos] = compose(key[e], i);
+      }
+    }
+    eq_seen += wave_tot[kBig / 64 - 1];
+    __syncthreads();
+  }
+  int P = 1;
+  while (P < kk) P <<= 1;
+  for (int j = kk + threadIdx.x; j < P; j += kBig) s[j] = 0ull;
+  bitonic_desc(s, P);
+  write_out(S, r, k, s, kk);
+}
+
+}  // namespace
+
+int64_t topk_workspace_bytes(int32_t out_rows) {
+  return (int64_t)out_rows * (2 * sizeof(uint32_t)) + 256 +
+         (int64_t)out_rows * kCandCap * sizeof(uint64_t);
+}
+
+int32_t launch_topk(const TopkSession *sess, int32_t n_sess, int32_t rows_per_sess,
+                    int32_t group, int32_t k, void *ws, hipStream_t s) {
+  for (int32_t s0 = 0; s0 < n_sess; s0 += kSessPerLaunch) {
+    const int32_t cnt = std::min(kSessPerLaunch, n_sess - s0);
+    const int32_t out_rows = cnt * rows_per_sess;
+    TopkArgs a{};
+    a.rows_per_sess = rows_per_sess;
+    a.group = group;
+    a.k = k;
+    // workspace: thr[out_rows] | cnt[out_rows] | pad | cand[out_rows][cap]
+    char *w = static_cast<char *>(ws);
+    const int64_t rows_before = (int64_t)s0 * rows_per_sess;
+    const int64_t total_rows = (int64_t)n_sess * rows_per_sess;
+    a.thr = reinterpret_cast<uint32_t *>(w) + rows_before;
+    a.cnt = reinterpret_cast<uint32_t *>(w) + total_rows + rows_before;
+    const int64_t head = (total_rows * 2 * sizeof(uint32_t) + 255) / 256 * 256;
+    a.cand = reinterpret_cast<uint64_t *>(w + head) + rows_before * kCandCap;
+    int64_t max_n = 0;
+    for (int j = 0; j < cnt; ++j) {
+      a.s[j].scores = sess[s0 + j].scores;
+      a.s[j].n = sess[s0 + j].n;
+      a.s[j].ld = sess[s0 + j].ld;
+      a.s[j].idx = sess[s0 + j].idx;
+      a.s[j].vals = sess[s0 + j].vals;
+      max_n = std::max(max_n, sess[s0 + j].n);
+    }
+    hipLaunchKernelGGL(topk_sample_kernel, dim3(out_rows), dim3(kBig), 0, s, a);
+    const int64_t chunks = (max_n + kCompactChunk - 1) / kCompactChunk;
+    if (chunks > 0)
+      hipLaunchKernelGGL(topk_compact_kernel, dim3((unsigned)chunks, out_rows),
+                         dim3(kCompactThreads), 0, s, a);
+    hipLaunchKernelGGL(topk_final_kernel, dim3(out_rows), dim3(kBig), 0, s, a);
+    int32_t rc = hip_fail(hipGetLastError(), "topk launch");
+    if (rc) return rc;
+  }
+  return FATHOM_OK;
+}
+
+}  // namespace fathom

@@ -1,0 +1,180 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, computes sizes, and rejects bad arguments on the host before any
+launch.  fathom_plan_stats is host-only and is checked against plans from the
+oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fathom.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import sparse_top_key_amd as fathom
+    if not os.path.exists(fathom.LIB_PATH):
+        from sparse_top_key_amd import build
+        build.build()
+    return fathom.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int32_t|int64_t|const char \*)\s*(fathom_\w+)\(",
+                                 text, re.M)))
+
+
+def test_header_declares_the_path():
+    names = declared_functions()
+    for f in ("fathom_pack", "fathom_plan", "fathom_plan_fixed", "fathom_scan",
+              "fathom_topk", "fathom_scan_batched", "fathom_topk_batched",
+              "fathom_read_prefixes", "fathom_plan_stats", "fathom_probe_read"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_top_key_amd", "libfathom.so"))
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_sizes(L):
+    assert L.fathom_abi_version() == 1
+    for n in (1, 31, 32, 2047, 2048, 2049, 1 << 20):
+        W = 64 * ((n + 2047) // 2048)
+        assert L.fathom_plane_words(n) == W
+        assert L.fathom_planes_bytes(n, 8, 128) == 8 * 128 * 4 * W * 4
+    assert L.fathom_pack_workspace_bytes(1 << 20, 8, 128) > 0
+    assert L.fathom_pack_workspace_bytes(0, 8, 128) == 0
+    assert L.fathom_pack_workspace_bytes(10, 8, 64) == 0
+    assert L.fathom_topk_workspace_bytes(32, 2048) >= 32 * 8192 * 8
+    assert L.fathom_topk_workspace_bytes(32, 2049) == 0
+    assert L.fathom_topk_workspace_bytes(0, 16) == 0
+
+
+DUMMY = ctypes.c_void_p(0x1000)
+
+
+def err(L):
+    return L.fathom_last_error().decode()
+
+
+def test_plan_validation(L):
+    b = (ctypes.c_int32 * 4)(92, 92, 92, 92)
+    assert L.fathom_plan(None, 4, 1, 128, DUMMY, b, DUMMY, None) == 1
+    assert L.fathom_plan(DUMMY, 4, 3, 128, DUMMY, b, DUMMY, None) == 1
+    assert "multiple" in err(L)
+    assert L.fathom_plan(DUMMY, 4, 1, 64, DUMMY, b, DUMMY, None) == 2
+    bad = (ctypes.c_int32 * 4)(92, 513, 92, 92)
+    assert L.fathom_plan(DUMMY, 4, 1, 128, DUMMY, bad, DUMMY, None) == 1
+    assert "budget_bits[1] = 513" in err(L)
+    neg = (ctypes.c_int32 * 4)(92, 0, -1, 92)
+    assert L.fathom_plan(DUMMY, 4, 1, 128, DUMMY, neg, DUMMY, None) == 1
+    assert L.fathom_plan_fixed(DUMMY, 4, 128, 129, DUMMY, None) == 1
+    assert L.fathom_plan_fixed(DUMMY, 4, 128, -1, DUMMY, None) == 1
+
+
+def test_pack_validation(L):
+    args = [DUMMY, 0, 100, 8, 128, 1024, 128, DUMMY, DUMMY, DUMMY, DUMMY]
+    ws_need = L.fathom_pack_workspace_bytes(100, 8, 128)
+    assert L.fathom_pack(None, *args[1:], DUMMY, ws_need, None) == 1
+    assert L.fathom_pack(DUMMY, 7, *args[2:], DUMMY, ws_need, None) == 1
+    a0 = list(args)
+    a0[2] = 0
+    assert L.fathom_pack(*a0, DUMMY, ws_need, None) == 1
+    a1 = list(args)
+    a1[4] = 96
+    assert L.fathom_pack(*a1, DUMMY, ws_need, None) == 2
+    assert L.fathom_pack(*args, DUMMY, ws_need - 1, None) == 4
+    assert L.fathom_pack(*args, None, ws_need, None) == 4
+
+
+def test_scan_validation(L):
+    base = [DUMMY, DUMMY, DUMMY, 100, 8, 128, DUMMY, DUMMY, 32, None, 0.0, DUMMY, 100, None]
+    a = list(base)
+    a[8] = 30                                     # hq not a multiple of hkv
+    assert L.fathom_scan(*a) == 1
+    a = list(base)
+    a[12] = 99                                    # ld < n
+    assert L.fathom_scan(*a) == 1
+    a = list(base)
+    a[0] = None
+    assert L.fathom_scan(*a) == 1
+    a = list(base)
+    a[5] = 256
+    assert L.fathom_scan(*a) == 2
+    a = list(base)
+    a[3] = -1
+    assert L.fathom_scan(*a) == 1
+
+
+def test_topk_validation(L):
+    ws = L.fathom_topk_workspace_bytes(32, 64)
+    base = [DUMMY, 32, 1000, 1000, 1, 64, DUMMY, DUMMY, DUMMY, ws, None]
+    a = list(base)
+    a[5] = 0
+    assert L.fathom_topk(*a) == 1
+    a[5] = 2049
+    assert L.fathom_topk(*a) == 1
+    a = list(base)
+    a[4] = 3                                      # 32 rows not a multiple of 3
+    assert L.fathom_topk(*a) == 1
+    a = list(base)
+    a[3] = 999                                    # ld < n
+    assert L.fathom_topk(*a) == 1
+    a = list(base)
+    a[9] = ws - 1
+    assert L.fathom_topk(*a) == 4
+    a = list(base)
+    a[6] = None
+    assert L.fathom_topk(*a) == 1
+
+
+def test_batched_validation(L):
+    import sparse_top_key_amd as fathom
+    arr = (fathom._Session * 2)()
+    assert L.fathom_scan_batched(arr, 0, 8, 128, 32, None) == 1
+    assert L.fathom_scan_batched(arr, 65, 8, 128, 32, None) == 1
+    arr[0].n = 10                                 # n > 0 with null pointers
+    assert L.fathom_scan_batched(arr, 2, 8, 128, 32, None) == 1
+    assert L.fathom_topk_batched(arr, 2, 32, 4, 0, DUMMY, 1 << 30, None) == 1
+
+
+def test_probe_validation(L):
+    assert L.fathom_probe_read(None, 16, DUMMY, 0, None) == 1
+    assert L.fathom_probe_read(DUMMY, 17, DUMMY, 0, None) == 1
+    assert L.fathom_probe_read(ctypes.c_void_p(0x1008), 16, DUMMY, 0, None) == 1
+
+
+@pytest.mark.parametrize("group", [1, 2, 4])
+def test_plan_stats_matches_oracle_plans(L, orc, group):
+    rng = np.random.default_rng(group)
+    hq, hkv, d = 8, 8 // group, 128
+    q = rng.standard_normal((hq, d)).astype(np.float32)
+    s2 = rng.uniform(0.1, 4, (hkv, d)).astype(np.float32)
+    budgets = rng.integers(0, 4 * d + 1, hq).astype(np.int32)
+    plan = orc.plan(q, s2, budgets)
+    hist = (ctypes.c_uint32 * 5)()
+    ub = (ctypes.c_uint32 * (hq // group))()
+    assert L.fathom_plan_stats(plan.ctypes.data_as(ctypes.c_void_p), hq, d, group, hist, ub) == 0
+    exp_hist = [int((plan == t).sum()) for t in range(5)]
+    assert list(hist) == exp_hist
+    exp_ub = [int(plan[g * group:(g + 1) * group].max(0).sum()) for g in range(hq // group)]
+    assert list(ub) == exp_ub
+    bad = plan.copy()
+    bad[0, 0] = 5
+    assert L.fathom_plan_stats(bad.ctypes.data_as(ctypes.c_void_p), hq, d, group, hist, ub) == 1
+
+
+def test_product_path_refuses_to_run_without_gpu():
+    import torch
+
+    import sparse_top_key_amd as fathom
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    with pytest.raises(fathom.FathomError):
+        fathom.pack(torch.zeros((64, 1, 128), dtype=torch.float16))

@@ -1,0 +1,187 @@
+"""GPU parity of fathom_scan: logits within 1e-5 * A_h of the oracle (fp64,
+rounded once), plane reads bit-exact, metamorphic properties bit-exact, and
+pinned-host planes giving the same bits as HBM planes."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from parity import assert_logits_close, logit_scale
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def F():
+    import sparse_top_key_amd as fathom
+    fathom.lib()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return fathom
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def make(F, seed, n, hkv, hq, dtype=torch.float16, outliers=4):
+    keys = synth.keys(seed, 0, n, hkv, 128, dtype, outliers, device=dev())
+    q = synth.queries(seed, 0, hq, 128, device=dev())
+    p = F.pack(keys)
+    torch.cuda.synchronize()
+    return keys, q, p
+
+
+def oracle_logits(orc, p, n, q, plan, meta=None, meta_scale=0.0):
+    return orc.scan(p.planes.cpu().numpy().view(np.uint32), p.lo.cpu().numpy(),
+                    p.hi.cpu().numpy(), n, q.cpu().numpy(), plan.cpu().numpy(),
+                    None if meta is None else meta.cpu().numpy(), meta_scale)
+
+
+def check(F, orc, p, n, q, plan, hkv, meta=None, meta_scale=0.0, ld=None):
+    hq = q.shape[0]
+    print(f"scan case n={n} hkv={hkv} hq={hq} meta={meta is not None}", flush=True)
+    out = None
+    if ld is not None:
+        out = torch.full((hq, ld), 7.0, device=dev())
+    got = F.scan(p.planes, p.lo, p.hi, n, q, plan, meta, meta_scale, out=out)
+    torch.cuda.synchronize()
+    ref = oracle_logits(orc, p, n, q, plan, meta, meta_scale)
+    A = logit_scale(q.cpu().numpy(), p.lo.cpu().numpy(), p.hi.cpu().numpy(), hq // hkv,
+                    meta_scale)
+    worst = assert_logits_close(got.cpu().numpy(), ref, A)
+    if out is not None:
+        assert torch.all(out[:, n:] == 7.0), "scan wrote past n"
+    return got, worst
+
+
+def test_scan_single_head_4096(F, orc):
+    w = synth.SINGLE_HEAD_4K
+    keys, q, p = make(F, w.seed, w.n, 1, 1, torch.float32, 0)
+    plan = F.plan(q, p.sigma2, w.budget)
+    check(F, orc, p, w.n, q, plan, 1)
+
+
+@pytest.mark.parametrize("budget", [68, 92, 136])
+def test_scan_qwen_shape(F, orc, budget):
+    keys, q, p = make(F, 21 + budget, 20000, 8, 32)
+    plan = F.plan(q, p.sigma2, budget)
+    check(F, orc, p, 20000, q, plan, 8)
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 8])
+def test_scan_group_sizes_and_odd_budgets(F, orc, G):
+    hkv = 2
+    hq = hkv * G
+    keys, q, p = make(F, 30 + G, 9000, hkv, hq)
+    rng = np.random.default_rng(G)
+    budgets = rng.integers(1, 140, hq).tolist()          # mostly not multiples of 4
+    plan = F.plan(q, p.sigma2, budgets)
+    check(F, orc, p, 9000, q, plan, hkv)
+
+
+@pytest.mark.parametrize("budget", [0, 4, 512])
+def test_scan_extreme_budgets(F, orc, budget):
+    keys, q, p = make(F, 40 + budget, 3000, 2, 8)
+    plan = F.plan(q, p.sigma2, budget)
+    got, _ = check(F, orc, p, 3000, q, plan, 2)
+    if budget == 0:
+        g = got.cpu().numpy()
+        assert np.all(g == g[:, :1])
+
+
+def test_scan_arbitrary_plans(F, orc):
+    """Any depth in 0..4 per (head, channel), also several depths per channel
+    inside a group (each distinct depth becomes its own slot)."""
+    keys, q, p = make(F, 50, 7000, 2, 8)
+    rng = np.random.default_rng(5)
+    plan = torch.from_numpy(rng.integers(0, 5, (8, 128)).astype(np.uint8)).to(dev())
+    check(F, orc, p, 7000, q, plan, 2)
+
+
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 2047, 2049, 8191, 8193, 16385])
+def test_scan_ragged_lengths(F, orc, n):
+    keys, q, p = make(F, 60, n, 2, 8)
+    plan = F.plan(q, p.sigma2, 92)
+    check(F, orc, p, n, q, plan, 2, ld=n + 37)
+
+
+def test_scan_fixed_plan_with_side_stream(F, orc):
+    n = 12345
+    keys, q, p = make(F, 70, n, 8, 32)
+    plan = F.plan_fixed(q, 32)
+    meta = synth.side_stream(70, 0, 8, n, device=dev())
+    check(F, orc, p, n, q, plan, 8, meta, 0.01)
+
+
+def test_read_prefixes_bit_exact(F, orc):
+    n = 3000
+    keys, q, p = make(F, 80, n, 2, 8)
+    plan = F.plan(q, p.sigma2, [1, 2, 3, 5, 18, 92, 200, 512])
+    got = F.read_prefixes(p.planes, n, plan, 2)
+    torch.cuda.synchronize()
+    ref = orc.read_prefixes(p.planes.cpu().numpy().view(np.uint32), n, plan.cpu().numpy(), 2)
+    np.testing.assert_array_equal(got.cpu().numpy(), ref)
+
+
+def test_unread_plane_bits_do_not_matter(F):
+    """Flip every bit the group's plans do not read: logits stay bit-identical."""
+    n = 10000
+    keys, q, p = make(F, 90, n, 8, 32)
+    plan = F.plan(q, p.sigma2, 92)
+    a = F.scan(p.planes, p.lo, p.hi, n, q, plan).clone()
+    depth = plan.view(8, 4, 128).max(1).values.cpu().numpy()      # [hkv][d]
+    flipped = p.planes.clone()
+    gen = torch.Generator(device=dev())
+    gen.manual_seed(9)
+    for g in range(8):
+        for c in range(128):
+            for s in range(int(depth[g, c]), 4):
+                flipped[g, c, s] = torch.randint(-2**31, 2**31 - 1, (flipped.shape[-1],),
+                                                 generator=gen, device=dev(), dtype=torch.int32)
+    b = F.scan(flipped, p.lo, p.hi, n, q, plan)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_channel_permutation_keeps_logits(F, orc):
+    """Permuting channels consistently (keys and queries) permutes the plan and
+    keeps the logits within tolerance (distinct importances)."""
+    n = 6000
+    keys, q, p = make(F, 91, n, 2, 8)
+    perm = torch.randperm(128, generator=torch.Generator().manual_seed(3)).to(dev())
+    keys2 = keys[:, :, perm].contiguous()
+    q2 = q[:, perm].contiguous()
+    p2 = F.pack(keys2)
+    plan1 = F.plan(q, p.sigma2, 92)
+    plan2 = F.plan(q2, p2.sigma2, 92)
+    torch.cuda.synchronize()
+    assert torch.equal(plan1[:, perm], plan2)
+    s1 = F.scan(p.planes, p.lo, p.hi, n, q, plan1)
+    s2 = F.scan(p2.planes, p2.lo, p2.hi, n, q2, plan2)
+    torch.cuda.synchronize()
+    A = logit_scale(q.cpu().numpy(), p.lo.cpu().numpy(), p.hi.cpu().numpy(), 4)
+    assert_logits_close(s2.cpu().numpy(), s1.cpu().numpy().astype(np.float64), A, 2e-5)
+
+
+def test_pinned_host_planes_match_hbm(F):
+    n = 50000
+    keys, q, p = make(F, 92, n, 8, 32)
+    plan = F.plan(q, p.sigma2, 92)
+    a = F.scan(p.planes, p.lo, p.hi, n, q, plan).clone()
+    host = torch.empty(p.planes.shape, dtype=p.planes.dtype, pin_memory=True)
+    host.copy_(p.planes)
+    torch.cuda.synchronize()
+    b = F.scan(host, p.lo, p.hi, n, q, plan)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_scan_is_deterministic(F):
+    n = 30000
+    keys, q, p = make(F, 93, n, 8, 32)
+    plan = F.plan(q, p.sigma2, 92)
+    a = F.scan(p.planes, p.lo, p.hi, n, q, plan).clone()
+    b = F.scan(p.planes, p.lo, p.hi, n, q, plan)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

@@ -463,3 +463,15 @@ def test_topk_all_equal_scores_take_lowest_indices(orc):
     S2[0, 3] = -0.0                 # -0 ties with +0
     idx2, _ = orc.topk(S2, 10)
     assert list(idx2[0]) == list(range(10))
+
+
+def test_scan_at_equals_full_scan(orc):
+    keys, q = make_layer(12, n=700)
+    n = keys.shape[0]
+    p = orc.pack(keys)
+    plan = orc.plan(q, p["sigma2"], [9, 50, 64, 3])
+    meta = np.random.default_rng(2).integers(0, 256, (2, n)).astype(np.uint8)
+    full = orc.scan(p["planes"], p["lo"], p["hi"], n, q, plan, meta, 0.5)
+    pick = np.array([0, 699, 5, 31, 32, 64, 333])
+    part = orc.scan_at(p["planes"], p["lo"], p["hi"], n, q, plan, pick, meta, 0.5)
+    np.testing.assert_array_equal(part, full[:, pick])
