@@ -1,0 +1,325 @@
+"""Throughput of Fathom's read path on one MI355X.
+
+One step = one decode step of one layer: fathom_plan (32 query heads, B = 92)
+-> fathom_scan (1,048,576 keys x 8 kv heads, union planes of each GQA group)
+-> fathom_topk (k = 2048 per query head), on the Qwen3-8B-shaped 1M-token
+layer with the K planes in pinned host memory read zero-copy (the offloaded
+case), and again with the planes in HBM.  Inputs (keys, queries) are seeded
+synthetic data already resident when timing starts; several layers rotate so
+that no step re-reads planes still held in the 256 MB last-level cache.
+
+Prints ONE JSON line.  value = key vectors (token x kv head) scored and
+selected per second, host-resident.  Also reported: the HBM-resident step,
+the in-library fixed 136-bit scan (top-32 |q| channels x 4 bits + an 8-bit
+per-key side stream) on identical inputs, streaming-read probes, and the CPU
+oracle on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sparse_top_key_amd as fathom  # noqa: E402
+import synth  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
+PCIE_PEAK_GBPS = 64.0         # PCIe Gen5 x16, published, one direction
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic.json")
+SCAN_SOURCE = os.path.join(ROOT, "sparse_top_key_amd", "csrc", "scan.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Layer:
+    """One layer's K cache (planes in HBM and in pinned host memory), its
+    queries, plans and output buffers."""
+
+    def __init__(self, w, layer, dev, host, fixed_r):
+        keys = synth.keys(w.seed, layer, w.n, w.hkv, w.d, w.dtype, w.outliers, device=dev)
+        p = fathom.pack(keys)
+        del keys
+        self.n = w.n
+        self.planes = p.planes
+        self.lo, self.hi, self.sigma2 = p.lo, p.hi, p.sigma2
+        self.host = None
+        if host:
+            self.host = torch.empty(p.planes.shape, dtype=p.planes.dtype, pin_memory=True)
+            self.host.copy_(p.planes)
+        self.q = synth.queries(w.seed, layer, w.hq, w.d, device=dev)
+        self.meta = synth.side_stream(w.seed, layer, w.hkv, w.n, device=dev)
+        self.meta_host = None
+        if host:
+            self.meta_host = torch.empty(self.meta.shape, dtype=torch.uint8, pin_memory=True)
+            self.meta_host.copy_(self.meta)
+        self.budget = [w.budget] * w.hq
+        self.plan = torch.empty((w.hq, w.d), dtype=torch.uint8, device=dev)
+        self.plan_fixed = fathom.plan_fixed(self.q, fixed_r)
+        self.logits = torch.empty((w.hq, w.n), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((w.hq, w.k), dtype=torch.int32, device=dev)
+        self.vals = torch.empty((w.hq, w.k), dtype=torch.float32, device=dev)
+
+
+def union_plane_bytes(plan, hkv, n):
+    """Plane bytes one scan reads: per kv head, sum_c max_{h in group} t_hc
+    bits per key (the planes of a GQA group are read once for the group)."""
+    p = plan.cpu()
+    hq = p.shape[0]
+    hist, ub = fathom.plan_stats(p, hq // hkv)
+    return sum(ub) * n // 8, ub, hist
+
+
+def run_steps(layers, w, ws, steps, mode, fixed=False):
+    """mode: 'host' or 'hbm'.  Returns per-step totals and per-call times (ms)."""
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for s in range(steps):
+        L = layers[s % len(layers)]
+        planes = L.host if mode == "host" else L.planes
+        meta = None
+        if fixed:
+            meta = L.meta_host if mode == "host" else L.meta
+        e = ev[s]
+        e[0].record()
+        if fixed:                                     # query-only plan of the baselines
+            plan = fathom.plan_fixed(L.q, 32, out=L.plan)
+        else:
+            plan = fathom.plan(L.q, L.sigma2, L.budget, out=L.plan)
+        e[1].record()
+        fathom.scan(planes, L.lo, L.hi, L.n, L.q, plan, meta, 0.0, out=L.logits)
+        e[2].record()
+        fathom.topk(L.logits, w.k, ws=ws, idx=L.idx, vals=L.vals)
+        e[3].record()
+    return ev
+
+
+def summarize(ev):
+    tot = [a[0].elapsed_time(a[3]) for a in ev]
+    plan = [a[0].elapsed_time(a[1]) for a in ev]
+    scan = [a[1].elapsed_time(a[2]) for a in ev]
+    topk = [a[2].elapsed_time(a[3]) for a in ev]
+    return dict(step_ms=float(np.mean(tot)), plan_ms=float(np.mean(plan)),
+                scan_ms=float(np.mean(scan)), topk_ms=float(np.mean(topk)),
+                scan_ms_p10=float(np.percentile(scan, 10)),
+                scan_ms_p90=float(np.percentile(scan, 90)))
+
+
+def timed(layers, w, ws, steps, warmup, mode, fixed=False):
+    run_steps(layers, w, ws, warmup, mode, fixed)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev = run_steps(layers, w, ws, steps, mode, fixed)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    r = summarize(ev)
+    r["wall_ms_per_step"] = wall * 1e3 / steps
+    return r
+
+
+def probes(dev):
+    out = torch.zeros(1, dtype=torch.int32, device=dev)
+    res = {}
+    dbuf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    hbuf = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    hbuf.fill_(1)
+    dbuf.fill_(1)
+    for name, buf, reps in (("hbm_read", dbuf, 10), ("host_read_zero_copy", hbuf, 3)):
+        best = 0.0
+        for blocks in (0, 1024, 4096):
+            fathom.probe_read(buf, out, blocks)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                fathom.probe_read(buf, out, blocks)
+            b.record()
+            torch.cuda.synchronize()
+            gbps = buf.numel() * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+            best = max(best, gbps)
+        res[name + "_GBps"] = round(best, 2)
+    d2 = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    d2.copy_(hbuf, non_blocking=True)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(3):
+        d2.copy_(hbuf, non_blocking=True)
+    b.record()
+    torch.cuda.synchronize()
+    res["h2d_copy_GBps"] = round(3 * d2.numel() / (a.elapsed_time(b) * 1e-3) / 1e9, 2)
+    del dbuf, hbuf, d2
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(layer0, w, n_sample):
+    """The CPU oracle, as it stands, on the first n_sample keys of one layer:
+    plan, scan (fp64) and top-k for all 32 query heads, one thread."""
+    from oracle import oracle
+    W = oracle.plane_words(n_sample)
+    planes = layer0.planes[..., :W].contiguous().cpu().numpy().view(np.uint32)
+    lo, hi = layer0.lo.cpu().numpy(), layer0.hi.cpu().numpy()
+    q, s2 = layer0.q.cpu().numpy(), layer0.sigma2.cpu().numpy()
+    t0 = time.perf_counter()
+    plan = oracle.plan(q, s2, w.budget)
+    logits = oracle.scan(planes, lo, hi, n_sample, q, plan)
+    oracle.topk(logits, w.k)
+    dt = time.perf_counter() - t0
+    return dict(value=round(n_sample * w.hkv / dt, 1), unit="keys/s", cores=1,
+                kind="oracle",
+                sample=(f"first {n_sample} keys of the 1M-key layer, all 8 kv heads / 32 "
+                        f"query heads: plan + fp64 scan + top-{w.k} (full sort), "
+                        f"{dt:.1f} s on 1 thread"))
+
+
+def scan_traffic_from_profiles():
+    """HBM bytes per scan launch from committed rocprofv3 counter runs, valid
+    only for the scan source they were taken on."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    h = hashlib.sha256(open(SCAN_SOURCE, "rb").read()).hexdigest()
+    if rec.get("scan_source_sha256") != h:
+        return None
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=4, help="rotating layers (cache defeat)")
+    ap.add_argument("--cpu-sample", type=int, default=131072)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--only", choices=["all", "hbm", "host"], default="all",
+                    help="profiling runs: restrict to one residency")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="counter runs: first copy 256 MiB device-to-device so the "
+                         "HBM byte counters can be scaled by a kernel of known traffic")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path "
+              "shards by kv head or token range, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    w = synth.LAYER_1M
+    fathom.lib()
+
+    if args.copy_calibration:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    probe = {} if args.no_probe else probes(dev)
+    log(f"probes: {probe}")
+
+    host = args.only in ("all", "host")
+    layers = [Layer(w, l, dev, host, 32) for l in range(args.layers)]
+    ws = torch.empty(fathom.topk_workspace_bytes(w.hq, w.k), dtype=torch.uint8, device=dev)
+    # plans once, for the byte accounting (the timed steps recompute them)
+    for L in layers:
+        fathom.plan(L.q, L.sigma2, L.budget, out=L.plan)
+    torch.cuda.synchronize()
+    # algorithmic plane bytes: mean over the rotating layers
+    per = [union_plane_bytes(L.plan, w.hkv, w.n) for L in layers]
+    plane_b = int(np.mean([x[0] for x in per]))
+    ub, hist = per[0][1], per[0][2]
+    fper = [union_plane_bytes(L.plan_fixed, w.hkv, w.n) for L in layers]
+    fixed_plan_b = int(np.mean([x[0] for x in fper]))
+    fub = fper[0][1]
+    meta_b = w.hkv * w.n
+    logits_b = w.hq * w.n * 4
+    log(f"union bits per kv head {ub}, depth histogram {hist}; fixed-136 union {fub}")
+
+    res = {}
+    for mode in (["host", "hbm"] if args.only == "all" else [args.only]):
+        res[mode] = timed(layers, w, ws, args.steps, args.warmup, mode)
+        res[mode + "_fixed"] = timed(layers, w, ws, args.steps, args.warmup, mode, fixed=True)
+        log(f"{mode}: {res[mode]}")
+        log(f"{mode} fixed-136: {res[mode + '_fixed']}")
+
+    keys_per_step = w.n * w.hkv
+    main_mode = "host" if "host" in res else "hbm"
+    r = res[main_mode]
+    value = keys_per_step / (r["step_ms"] * 1e-3)
+    traffic = scan_traffic_from_profiles()
+    if main_mode == "host":
+        achieved = plane_b / (r["scan_ms"] * 1e-3) / 1e9
+        roofline = {"bound": "host_link", "achieved": round(achieved, 2),
+                    "peak": PCIE_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / PCIE_PEAK_GBPS, 4),
+                    "traffic": (traffic or {}).get("host_scan_fetch_bytes"),
+                    "kernel": "scan_kernel<4, 32, 2> (planes in pinned host memory)",
+                    "algorithmic_bytes": plane_b,
+                    "frac_of_measured_link_peak": (round(achieved / probe["host_read_zero_copy_GBps"], 4)
+                                                   if probe else None)}
+    out = {
+        "metric": "keys scanned/s (1M-token layer, B=92, k=2048, planes zero-copy from pinned host)",
+        "value": round(value, 1),
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["step_ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded Qwen3-8B-shaped keys, log-uniform channel scales + 4 outlier channels, fp16)",
+        "config": {"workload": ("qwen3-8b layer: n=1048576 keys fp16, 8 kv heads x d128, "
+                                "32 query heads (GQA 4), B=92 bits/key, k=2048 per query head, "
+                                f"K planes {'in pinned host memory (zero-copy)' if main_mode == 'host' else 'in HBM'}"),
+                   "steps_rotate_layers": args.layers},
+    }
+    if main_mode == "host":
+        out["roofline"] = roofline
+    if "hbm" in res:
+        h = res["hbm"]
+        ach = (plane_b + logits_b) / (h["scan_ms"] * 1e-3) / 1e9
+        out["roofline_hbm"] = {
+            "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBPS, 4),
+            "traffic": (traffic or {}).get("hbm_scan_bytes"),
+            "kernel": "scan_kernel<4, 16, 0> (planes in HBM)",
+            "algorithmic_bytes": plane_b + logits_b,
+            "end_to_end_plane_GBps": round(plane_b / (h["step_ms"] * 1e-3) / 1e9, 1)}
+        if main_mode == "host":
+            out["hbm_resident"] = {"keys_per_s": round(keys_per_step / (h["step_ms"] * 1e-3), 1),
+                                   **{k: round(v, 4) for k, v in h.items()}}
+        else:
+            out["roofline"] = out.pop("roofline_hbm")
+    out["timings_ms"] = {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in res.items()}
+    for mode in ("host", "hbm"):
+        if mode in res:
+            out.setdefault("fixed136_speedup", {})[mode] = round(
+                res[mode + "_fixed"]["step_ms"] / res[mode]["step_ms"], 3)
+            out.setdefault("fixed136_scan_speedup", {})[mode] = round(
+                res[mode + "_fixed"]["scan_ms"] / res[mode]["scan_ms"], 3)
+    out["bytes"] = {"fathom_union_plane_bytes": plane_b, "fixed136_plane_bytes": fixed_plan_b,
+                    "fixed136_meta_bytes": meta_b, "logits_bytes": logits_b,
+                    "union_bits_per_kv_head": ub, "fixed136_union_bits": fub,
+                    "depth_histogram": hist}
+    out["probe"] = probe
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(layers[0], w, args.cpu_sample)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

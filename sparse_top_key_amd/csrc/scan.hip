@@ -36,8 +36,6 @@ namespace fathom {
 namespace {
 
 constexpr int kScanThreads = 256;
-constexpr int kWaveKeys = 2048;                   // 64 lanes x 32 keys
-constexpr int kTileKeys = kWaveKeys * (kScanThreads / 64);
 constexpr int kMaxSlots = kD * kPlanes;           // (channel, depth) pairs
 constexpr int kMaxGroups = kMaxSlots / 8;
 constexpr int kMaxGH = 4;                          // heads per launch chunk
@@ -51,6 +49,7 @@ struct ScanSess {
   float meta_scale;
   int32_t block_begin;     // first block of this session in the grid
   int32_t tiles_per_block;
+  int32_t blocks_per_head;
   int32_t vec_out;         // float4 logits stores are aligned
 };
 
@@ -62,10 +61,10 @@ struct ScanArgs {
 // ---- 32x32 bit transpose ----------------------------------------------------
 // On entry x[r] bit k = element (r, k); on exit x[k] bit r = element (r, k).
 // Stage S swaps the off-diagonal SxS blocks of every 2Sx2S block.
-template <int S, uint32_t M>
-__device__ __forceinline__ void transpose_stage(uint32_t (&x)[32]) {
+template <int N, int S, uint32_t M>
+__device__ __forceinline__ void transpose_stage(uint32_t (&x)[N]) {
 #pragma unroll
-  for (int r = 0; r < 32; ++r) {
+  for (int r = 0; r < N; ++r) {
     if ((r & S) == 0) {
       const uint32_t a = x[r], b = x[r + S];
       x[r] = (a & M) | ((b << S) & ~M);
@@ -75,37 +74,74 @@ __device__ __forceinline__ void transpose_stage(uint32_t (&x)[32]) {
 }
 
 __device__ __forceinline__ void transpose32(uint32_t (&x)[32]) {
-  transpose_stage<16, 0x0000FFFFu>(x);
-  transpose_stage<8, 0x00FF00FFu>(x);
-  transpose_stage<4, 0x0F0F0F0Fu>(x);
-  transpose_stage<2, 0x33333333u>(x);
-  transpose_stage<1, 0x55555555u>(x);
+  transpose_stage<32, 16, 0x0000FFFFu>(x);
+  transpose_stage<32, 8, 0x00FF00FFu>(x);
+  transpose_stage<32, 4, 0x0F0F0F0Fu>(x);
+  transpose_stage<32, 2, 0x33333333u>(x);
+  transpose_stage<32, 1, 0x55555555u>(x);
+}
+
+// Stages 8..1 on one 16-row half that stage 16 has already separated.
+__device__ __forceinline__ void transpose16(uint32_t (&x)[16]) {
+  transpose_stage<16, 8, 0x00FF00FFu>(x);
+  transpose_stage<16, 4, 0x0F0F0F0Fu>(x);
+  transpose_stage<16, 2, 0x33333333u>(x);
+  transpose_stage<16, 1, 0x55555555u>(x);
 }
 
 __device__ __forceinline__ int uniform(int v) {
   return __builtin_amdgcn_readfirstlane(v);
 }
+__device__ __forceinline__ float uniform_f(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
+// The 8 nibbles of a transposed word as fp32 values: two masks split the
+// nibbles into the low halves of bytes, then one byte conversion each.
+__device__ __forceinline__ void nibbles_to_f32(uint32_t y, float (&f)[8]) {
+  const uint32_t e = y & 0x0F0F0F0Fu;         // slots 0, 2, 4, 6
+  const uint32_t o = (y >> 4) & 0x0F0F0F0Fu;  // slots 1, 3, 5, 7
+  asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f[0]) : "v"(e));
+  asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f[1]) : "v"(o));
+  asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f[2]) : "v"(e));
+  asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f[3]) : "v"(o));
+  asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f[4]) : "v"(e));
+  asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f[5]) : "v"(o));
+  asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f[6]) : "v"(e));
+  asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f[7]) : "v"(o));
+}
 
 // Rows 4j+p of x receive bit p of slot (grp*8 + j)'s code: plane slot 3-p of
-// its channel, loaded only when the slot's depth covers it.
-__device__ __forceinline__ void load_group(const uint32_t *__restrict__ pw,
-                                           int64_t W, const int16_t *slot_desc,
-                                           int grp, uint32_t (&x)[32]) {
+// its channel, loaded only when the slot's depth covers it.  Loads are
+// buffer loads: a wave-uniform resource per channel (its 4 plane rows), a
+// wave-uniform row + block offset, and the lane's 32-bit byte offset `voff`.
+// The resource's size also bounds every access.
+constexpr int32_t kRsrcWord3 = 0x00020000;
+
+template <int AUX>
+__device__ __forceinline__ void load_group(const uint32_t *__restrict__ gplanes, int64_t W,
+                                           int32_t wbase, uint32_t voff,
+                                           const int16_t *slot_desc, int grp,
+                                           uint32_t (&x)[32]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int desc = uniform(slot_desc[grp * 8 + j]);
     const int c = desc >> 3, dep = desc & 7;
-    const uint32_t *pc = pw + (int64_t)c * kPlanes * W;
+    const uint32_t *pc = gplanes + (int64_t)c * kPlanes * W;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t *>(pc), (short)0, (int32_t)(W * kPlanes * 4), kRsrcWord3);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       uint32_t v = 0;
-      if (3 - p < dep) v = __builtin_nontemporal_load(pc + (3 - p) * W);
+      if (3 - p < dep)
+        v = __builtin_amdgcn_raw_buffer_load_b32(
+            rsrc, (int32_t)voff, (int32_t)(((3 - p) * W + wbase) * 4), AUX);
       x[4 * j + p] = v;
     }
   }
 }
 
-template <int GH>
+template <int GH, int KPL, int AUX>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   // ---- which session / kv head / tiles ------------------------------------
   int si = 0;
@@ -114,7 +150,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   const ScanSess &S = a.s[si];
   const int local = blockIdx.x - S.block_begin;
   const int g = local % a.hkv;
-  const int tile0 = (local / a.hkv) * S.tiles_per_block;
+  // block j of a kv head takes tiles j, j + B, j + 2B, ... (B blocks per
+  // head), so the blocks running together stream neighbouring addresses
+  const int tile0 = local / a.hkv;
+  const int tile_step = S.blocks_per_head;
   const int64_t n = S.n;
   const int head_base = g * a.group + a.head0;
 
@@ -198,70 +237,101 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   __syncthreads();
 
   // ---- main loop ------------------------------------------------------------
+  // KPL = 32: lane = one plane word (32 keys), a wave covers 64 words, and
+  // every wave load is one 256-byte access.  KPL = 16: lane = half a word
+  // (word lane & 31, keys 16*hf.. with hf = lane >> 5), a wave covers 32
+  // words; the first transpose stage keeps the lane's half (one byte permute
+  // per row) and the last four run on 16 registers -- half the accumulators,
+  // so more waves fit.
+  constexpr int kWords = KPL == 32 ? 64 : 32;
+  constexpr int kWaveK = kWords * 32;
+  constexpr int kTileK = kWaveK * (kScanThreads / 64);
   const int wave = tid >> 6, lane = tid & 63;
+  const int hf = KPL == 32 ? 0 : lane >> 5;
+  const uint32_t half_sel = hf ? 0x07060302u : 0x05040100u;
   const uint32_t *gplanes = S.planes + (int64_t)g * kD * kPlanes * S.W;
   float C[GH];
 #pragma unroll
   for (int j = 0; j < GH; ++j) C[j] = s_C[j];
 
   for (int tt = 0; tt < S.tiles_per_block; ++tt) {
-    const int64_t wkey0 = (int64_t)(tile0 + tt) * kTileKeys + (int64_t)wave * kWaveKeys;
+    const int64_t wkey0 =
+        (int64_t)(tile0 + tt * tile_step) * kTileK + (int64_t)wave * kWaveK;
     if (wkey0 >= n) break;
-    const int64_t word = wkey0 / 32 + lane;
-    const uint32_t *pw = gplanes + word;
+    const int wl = KPL == 32 ? lane : (lane & 31);
+    const int64_t word = wkey0 / 32 + wl;
+    const int32_t wbase = (int32_t)(wkey0 / 32);
+    const uint32_t voff = (uint32_t)wl * 4u;  // byte offset
 
-    float acc[GH][32];
+    float acc[GH][KPL];
 #pragma unroll
     for (int j = 0; j < GH; ++j)
 #pragma unroll
-      for (int k = 0; k < 32; ++k) acc[j][k] = C[j];
+      for (int k = 0; k < KPL; ++k) acc[j][k] = C[j];
 
     uint32_t xn[32];
-    if (ngroups > 0) load_group(pw, S.W, s_desc, 0, xn);
+    if (ngroups > 0) load_group<AUX>(gplanes, S.W, wbase, voff, s_desc, 0, xn);
     for (int grp = 0; grp < ngroups; ++grp) {
-      uint32_t x[32];
+      uint32_t y[KPL];
+      if constexpr (KPL == 32) {
 #pragma unroll
-      for (int r = 0; r < 32; ++r) x[r] = xn[r];
-      if (grp + 1 < ngroups) load_group(pw, S.W, s_desc, grp + 1, xn);
-      transpose32(x);
+        for (int r = 0; r < 32; ++r) y[r] = xn[r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) y[r] = __builtin_amdgcn_perm(xn[r + 16], xn[r], half_sel);
+      }
+      if (grp + 1 < ngroups) load_group<AUX>(gplanes, S.W, wbase, voff, s_desc, grp + 1, xn);
+      if constexpr (KPL == 32)
+        transpose32(y);
+      else
+        transpose16(y);
       const int gm = uniform(s_gmask[grp]);
+      // the group's weights, wave-uniform: held in scalar registers
       float gv[GH][8];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int h = 0; h < GH; ++h) gv[h][j] = s_gam[grp * 8 + j][h];
+        for (int h = 0; h < GH; ++h) gv[h][j] = uniform_f(s_gam[grp * 8 + j][h]);
+      if (gm == (1 << GH) - 1) {
 #pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        const uint32_t y = x[k];
-        const uint32_t e = y & 0x0F0F0F0Fu;        // slots 0,2,4,6
-        const uint32_t o = (y >> 4) & 0x0F0F0F0Fu; // slots 1,3,5,7
-        float f[8];
-        f[0] = (float)(e & 0xFF);
-        f[1] = (float)(o & 0xFF);
-        f[2] = (float)((e >> 8) & 0xFF);
-        f[3] = (float)((o >> 8) & 0xFF);
-        f[4] = (float)((e >> 16) & 0xFF);
-        f[5] = (float)((o >> 16) & 0xFF);
-        f[6] = (float)(e >> 24);
-        f[7] = (float)(o >> 24);
+        for (int k = 0; k < KPL; ++k) {
+          float f[8];
+          nibbles_to_f32(y[k], f);
 #pragma unroll
-        for (int h = 0; h < GH; ++h) {
-          if ((gm >> h) & 1) {
-            float s = acc[h][k];
+          for (int h = 0; h < GH; ++h) {
+            float sacc = acc[h][k];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) s = __fmaf_rn(gv[h][j], f[j], s);
-            acc[h][k] = s;
+            for (int j = 0; j < 8; ++j) sacc = __fmaf_rn(gv[h][j], f[j], sacc);
+            acc[h][k] = sacc;
           }
+          // keep one key's conversions live at a time (register budget)
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < KPL; ++k) {
+          float f[8];
+          nibbles_to_f32(y[k], f);
+#pragma unroll
+          for (int h = 0; h < GH; ++h) {
+            if ((gm >> h) & 1) {
+              float sacc = acc[h][k];
+#pragma unroll
+              for (int j = 0; j < 8; ++j) sacc = __fmaf_rn(gv[h][j], f[j], sacc);
+              acc[h][k] = sacc;
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
 
     // ---- optional 8-bit side stream (fixed-width baseline) ----------------
-    const int64_t key0 = word * 32;
+    const int64_t key0 = word * 32 + KPL * hf;
     if (S.meta) {
       const uint8_t *mp = S.meta + (int64_t)g * n + key0;
 #pragma unroll
-      for (int k = 0; k < 32; ++k) {
+      for (int k = 0; k < KPL; ++k) {
         const float m = key0 + k < n ? (float)mp[k] : 0.0f;
 #pragma unroll
         for (int h = 0; h < GH; ++h) acc[h][k] = __fmaf_rn(S.meta_scale, m, acc[h][k]);
@@ -272,14 +342,14 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
 #pragma unroll
     for (int h = 0; h < GH; ++h) {
       float *out = S.logits + (int64_t)(head_base + h) * S.ld + key0;
-      if (S.vec_out && key0 + 32 <= n) {
+      if (S.vec_out && key0 + KPL <= n) {
 #pragma unroll
-        for (int k = 0; k < 32; k += 4)
+        for (int k = 0; k < KPL; k += 4)
           *reinterpret_cast<float4 *>(out + k) =
               make_float4(acc[h][k], acc[h][k + 1], acc[h][k + 2], acc[h][k + 3]);
       } else {
 #pragma unroll
-        for (int k = 0; k < 32; ++k)
+        for (int k = 0; k < KPL; ++k)
           if (key0 + k < n) out[k] = acc[h][k];
       }
     }
@@ -302,6 +372,45 @@ __global__ __launch_bounds__(256) void read_prefixes_kernel(
   out[((int64_t)h * n + i) * kD + c] = (uint8_t)v;
 }
 
+// Kernel variants: planes in pinned host memory are read with whole-word
+// lanes (256-byte wave accesses) and streaming loads; planes in HBM with
+// half-word lanes (more resident waves for the arithmetic).
+struct Variant {
+  int kpl;
+  int aux;
+};
+constexpr Variant kHostVariant{32, 2};    // aux 2: non-temporal
+constexpr Variant kDeviceVariant{16, 0};
+
+using ScanFn = void (*)(ScanArgs);
+
+template <int KPL, int AUX>
+ScanFn pick(int GH) {
+  switch (GH) {
+    case 1: return scan_kernel<1, KPL, AUX>;
+    case 2: return scan_kernel<2, KPL, AUX>;
+    case 3: return scan_kernel<3, KPL, AUX>;
+    default: return scan_kernel<4, KPL, AUX>;
+  }
+}
+
+ScanFn kernel_for(bool host, int GH) {
+  return host ? pick<kHostVariant.kpl, kHostVariant.aux>(GH)
+              : pick<kDeviceVariant.kpl, kDeviceVariant.aux>(GH);
+}
+
+int resident_blocks_per_cu(bool host, int GH) {
+  static int cached[2][kMaxGH + 1] = {};
+  int &c = cached[host ? 1 : 0][GH];
+  if (c == 0) {
+    int nb = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &nb, kernel_for(host, GH), kScanThreads, 0);
+    c = (e == hipSuccess && nb > 0) ? nb : 1;
+  }
+  return c;
+}
+
 }  // namespace
 
 int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv,
@@ -311,6 +420,20 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv,
   hipGetDevice(&dev);
   int ncu = 256;
   hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  // residency of each session's planes: pinned host or device memory
+  bool any_host = false;
+  for (int32_t j = 0; j < n_sess; ++j) {
+    hipPointerAttribute_t attr;
+    const hipError_t e = hipPointerGetAttributes(&attr, sess[j].planes);
+    if (e != hipSuccess) {
+      hipGetLastError();
+      set_error("scan: planes of session %d are neither device nor pinned host memory", j);
+      return FATHOM_ERR_INVALID_ARG;
+    }
+    any_host |= attr.type == hipMemoryTypeHost;
+  }
+  const int kpl = any_host ? kHostVariant.kpl : kDeviceVariant.kpl;
+  const int64_t tile_keys = (int64_t)kpl * 64 * (kScanThreads / 64);
   for (int32_t s0 = 0; s0 < n_sess; s0 += kSessPerLaunch) {
     const int32_t cnt = std::min(kSessPerLaunch, n_sess - s0);
     for (int32_t head0 = 0; head0 < group; head0 += kMaxGH) {
@@ -322,10 +445,10 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv,
       a.head0 = head0;
       int64_t total_tiles = 0;
       for (int j = 0; j < cnt; ++j)
-        total_tiles += (sess[s0 + j].n + kTileKeys - 1) / kTileKeys * hkv;
-      // about 4 blocks per CU overall; each block amortises its plan set-up
-      // over several tiles of one (session, kv head)
-      const int64_t target_blocks = (int64_t)ncu * 4;
+        total_tiles += (sess[s0 + j].n + tile_keys - 1) / tile_keys * hkv;
+      // one round of resident blocks: every block takes the same number of
+      // tiles of one (session, kv head) and amortises its plan set-up
+      const int64_t target_blocks = (int64_t)ncu * resident_blocks_per_cu(any_host, GH);
       int32_t blocks = 0;
       for (int j = 0; j < cnt; ++j) {
         const ScanSession &in = sess[s0 + j];
@@ -342,22 +465,18 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv,
         o.ld = in.ld;
         o.meta_scale = in.meta_scale;
         o.vec_out = ((reinterpret_cast<uintptr_t>(in.logits) & 15) == 0) && (in.ld % 4 == 0);
-        const int64_t tiles = (in.n + kTileKeys - 1) / kTileKeys;
+        const int64_t tiles = (in.n + tile_keys - 1) / tile_keys;
         int64_t tpb = 1;
         if (total_tiles > target_blocks)
           tpb = (total_tiles + target_blocks - 1) / target_blocks;
         tpb = std::max<int64_t>(1, std::min<int64_t>(tpb, tiles));
         o.tiles_per_block = (int32_t)tpb;
+        o.blocks_per_head = (int32_t)((tiles + tpb - 1) / tpb);
         o.block_begin = blocks;
-        blocks += (int32_t)(((tiles + tpb - 1) / tpb) * hkv);
+        blocks += o.blocks_per_head * hkv;
       }
       if (blocks == 0) continue;
-      switch (GH) {
-        case 1: hipLaunchKernelGGL(scan_kernel<1>, dim3(blocks), dim3(kScanThreads), 0, s, a); break;
-        case 2: hipLaunchKernelGGL(scan_kernel<2>, dim3(blocks), dim3(kScanThreads), 0, s, a); break;
-        case 3: hipLaunchKernelGGL(scan_kernel<3>, dim3(blocks), dim3(kScanThreads), 0, s, a); break;
-        default: hipLaunchKernelGGL(scan_kernel<4>, dim3(blocks), dim3(kScanThreads), 0, s, a); break;
-      }
+      hipLaunchKernelGGL(kernel_for(any_host, GH), dim3(blocks), dim3(kScanThreads), 0, s, a);
       int32_t rc = hip_fail(hipGetLastError(), "scan launch");
       if (rc) return rc;
     }

@@ -31,6 +31,7 @@ constexpr int kCompactThreads = 256;
 constexpr int kCompactChunk = 16384;  // scores per compact block
 constexpr int kRun = 64;              // contiguous scores per sample run
 constexpr int kHistBins = 2048;
+constexpr int kStage = 2048;           // candidates staged per compact block
 
 struct TopkSess {
   const float *scores;
@@ -219,7 +220,13 @@ __global__ __launch_bounds__(kBig) void topk_sample_kernel(TopkArgs a) {
 }
 
 // ---- stream the rows, keep scores >= T ----------------------------------------
+// Candidates are staged in LDS and appended to the row's list with one global
+// atomic per block (all rows' counters share a cache line, so per-wave global
+// atomics would serialise in one L2 channel).  A block with more than kStage
+// candidates sends the overflow straight to the global list.
 __global__ __launch_bounds__(kCompactThreads) void topk_compact_kernel(TopkArgs a) {
+  __shared__ uint64_t stage[kStage];
+  __shared__ uint32_t s_n, s_base;
   const int o = blockIdx.y;
   const RowRef R = row_ref(a, o);
   const int64_t n = R.s->n, ld = R.s->ld;
@@ -229,7 +236,10 @@ __global__ __launch_bounds__(kCompactThreads) void topk_compact_kernel(TopkArgs 
   uint32_t *cnt = a.cnt + o;
   uint64_t *cand = a.cand + (int64_t)o * kCandCap;
   const int lane = threadIdx.x & 63;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const bool vec = a.group == 1 && ((reinterpret_cast<uintptr_t>(R.row) & 15) == 0);
+  if (threadIdx.x == 0) s_n = 0;
+  __syncthreads();
   for (int it = 0; it < kCompactChunk / (kCompactThreads * 4); ++it) {
     const int64_t i0 = base + (int64_t)it * kCompactThreads * 4 + threadIdx.x * 4;
     float v[4];
@@ -244,7 +254,7 @@ __global__ __launch_bounds__(kCompactThreads) void topk_compact_kernel(TopkArgs 
     uint32_t key[4];
     bool pred[4];
     uint64_t bal[4];
-    int total = 0;
+    uint32_t total = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       key[e] = to_key(v[e]);
@@ -254,23 +264,78 @@ __global__ __launch_bounds__(kCompactThreads) void topk_compact_kernel(TopkArgs 
     }
     if (total == 0) continue;
     uint32_t start = 0;
-    if (lane == 0) start = atomicAdd(cnt, (uint32_t)total);
+    if (lane == 0) start = atomicAdd(&s_n, total);
     start = __shfl(start, 0);
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    // positions >= kStage of this batch go to the global list directly
+    const uint32_t first_over = start > (uint32_t)kStage ? start : (uint32_t)kStage;
+    const uint32_t over = start + total > first_over ? start + total - first_over : 0u;
+    uint32_t gbase = 0;
+    if (over) {
+      if (lane == 0) gbase = atomicAdd(cnt, over);
+      gbase = __shfl(gbase, 0);
+    }
+    uint32_t off = start;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (pred[e]) {
-        const uint32_t pos = start + __popcll(bal[e] & below);
-        if (pos < (uint32_t)kCandCap) cand[pos] = compose(key[e], i0 + e);
+        const uint32_t pos = off + __popcll(bal[e] & below);
+        const uint64_t c = compose(key[e], i0 + e);
+        if (pos < (uint32_t)kStage) {
+          stage[pos] = c;
+        } else {
+          const uint32_t g = gbase + (pos - first_over);
+          if (g < (uint32_t)kCandCap) cand[g] = c;
+        }
       }
-      start += __popcll(bal[e]);
+      off += __popcll(bal[e]);
     }
   }
+  __syncthreads();
+  const uint32_t m = s_n < (uint32_t)kStage ? s_n : (uint32_t)kStage;
+  if (m == 0) return;
+  if (threadIdx.x == 0) s_base = atomicAdd(cnt, m);
+  __syncthreads();
+  const uint32_t b = s_base;
+  for (uint32_t j = threadIdx.x; j < m; j += kCompactThreads)
+    if (b + j < (uint32_t)kCandCap) cand[b + j] = stage[j];
+}
+
+// Exact kk-th largest of the unique 64-bit words s[0..m) by 11-bit radix
+// passes from the top bit; stops early once a whole digit bin is taken.
+// Returns T such that exactly kk words are >= T.
+__device__ uint64_t select_kth(const uint64_t *s, int m, int kk, int *hist, int *wave_tot,
+                               int *s_res) {
+  uint64_t prefix = 0, pmask = 0;
+  int rem = kk;
+  int hi = 64;
+  while (hi > 0) {
+    const int bits = hi >= 11 ? 11 : hi;
+    const int sh = hi - bits;
+    const int nb = 1 << bits;
+    for (int b = threadIdx.x; b < kHistBins; b += kBig) hist[b] = 0;
+    __syncthreads();
+    for (int j = threadIdx.x; j < m; j += kBig) {
+      const uint64_t v = s[j];
+      if ((v & pmask) == prefix) atomicAdd(&hist[(int)((v >> sh) & (uint64_t)(nb - 1))], 1);
+    }
+    __syncthreads();
+    int above = 0;
+    const int d = find_digit(hist, nb, rem, &above, wave_tot, s_res);
+    const int in_bin = hist[d];
+    __syncthreads();
+    rem -= above;
+    prefix |= (uint64_t)d << sh;
+    pmask |= (uint64_t)(nb - 1) << sh;
+    hi = sh;
+    if (in_bin == rem) break;  // the whole bin is kept: T = prefix, low bits 0
+  }
+  return prefix;
 }
 
 // ---- exact selection of each row's top k -------------------------------------
 __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
   __shared__ uint64_t s[kCandCap];
+  __shared__ uint64_t win[FATHOM_MAX_K];
   __shared__ int hist[kHistBins];
   __shared__ int wave_tot[16];
   __shared__ int s_res[2];
@@ -284,74 +349,73 @@ __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
   const int kk = (int)(n < k ? n : k);
   const uint32_t cnt = a.cnt[o];
   const bool fast = (n <= kCandCap) || (cnt >= (uint32_t)k && cnt <= (uint32_t)kCandCap);
+  if (threadIdx.x == 0) s_count = 0;
   if (fast) {
     const int m = (int)cnt;
-    int P = 1;
-    while (P < m) P <<= 1;
     const uint64_t *cand = a.cand + (int64_t)o * kCandCap;
-    for (int j = threadIdx.x; j < P; j += kBig) s[j] = j < m ? cand[j] : 0ull;
-    bitonic_desc(s, P);
-    write_out(S, r, k, s, kk);
-    return;
-  }
-  // exact recomputation over the whole row
-  int rem = kk;
-  uint32_t prefix = 0, pmask = 0;
-  const int shifts[3] = {21, 10, 0};
-  const int bits[3] = {11, 11, 10};
-  for (int pass = 0; pass < 3; ++pass) {
-    const int sh = shifts[pass], nb = 1 << bits[pass];
-    for (int b = threadIdx.x; b < kHistBins; b += kBig) hist[b] = 0;
+    for (int j = threadIdx.x; j < m; j += kBig) s[j] = cand[j];
     __syncthreads();
-    for (int64_t i = threadIdx.x; i < n; i += kBig) {
-      const uint32_t v = to_key(group_score(R.row, ld, a.group, i));
-      if ((v & pmask) == prefix) atomicAdd(&hist[(v >> sh) & (nb - 1)], 1);
+    if (kk > 0) {
+      const uint64_t T = m > kk ? select_kth(s, m, kk, hist, wave_tot, s_res) : 0ull;
+      for (int j = threadIdx.x; j < m; j += kBig)
+        if (s[j] >= T) win[atomicAdd(&s_count, 1)] = s[j];
     }
-    __syncthreads();
-    int above = 0;
-    const int d = find_digit(hist, nb, rem, &above, wave_tot, s_res);
-    rem -= above;
-    prefix |= (uint32_t)d << sh;
-    pmask |= (uint32_t)(nb - 1) << sh;
+  } else {
+    // exact recomputation over the whole row
+    int rem = kk;
+    uint32_t prefix = 0, pmask = 0;
+    const int shifts[3] = {21, 10, 0};
+    const int bits[3] = {11, 11, 10};
+    for (int pass = 0; pass < 3; ++pass) {
+      const int sh = shifts[pass], nb = 1 << bits[pass];
+      for (int b = threadIdx.x; b < kHistBins; b += kBig) hist[b] = 0;
+      __syncthreads();
+      for (int64_t i = threadIdx.x; i < n; i += kBig) {
+        const uint32_t v = to_key(group_score(R.row, ld, a.group, i));
+        if ((v & pmask) == prefix) atomicAdd(&hist[(v >> sh) & (nb - 1)], 1);
+      }
+      __syncthreads();
+      int above = 0;
+      const int d = find_digit(hist, nb, rem, &above, wave_tot, s_res);
+      rem -= above;
+      prefix |= (uint32_t)d << sh;
+      pmask |= (uint32_t)(nb - 1) << sh;
+    }
+    const uint32_t kth = prefix;  // key of the kk-th largest score
+    const int need_eq = rem;      // how many scores equal to it are kept
+    int eq_seen = 0;
+    for (int64_t b0 = 0; b0 < n; b0 += (int64_t)kBig * 4) {
+      uint32_t key[4];
+      int eqc = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t i = b0 + threadIdx.x * 4 + e;
+        key[e] = i < n ? to_key(group_score(R.row, ld, a.group, i)) : 0u;
+        eqc += (i < n && key[e] == kth);
+      }
+      const int incl = block_inclusive_scan(eqc, wave_tot);
+      int rank = eq_seen + incl - eqc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t i = b0 + threadIdx.x * 4 + e;
+        if (i >= n) continue;
+        bool take = key[e] > kth;
+        if (key[e] == kth) {
+          take = rank < need_eq;
+          ++rank;
+        }
+        if (take) win[atomicAdd(&s_count, 1)] = compose(key[e], i);
+      }
+      eq_seen += wave_tot[kBig / 64 - 1];
+      __syncthreads();
+    }
   }
-  const uint32_t kth = prefix;  // key of the kk-th largest score
-  const int need_eq = rem;      // how many scores equal to it are kept
-  if (threadIdx.x == 0) s_count = 0;
   __syncthreads();
-  int eq_seen = 0;
-  for (int64_t b0 = 0; b0 < n; b0 += (int64_t)kBig * 4) {
-    uint32_t key[4];
-    int eqc = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t i = b0 + threadIdx.x * 4 + e;
-      key[e] = i < n ? to_key(group_score(R.row, ld, a.group, i)) : 0u;
-      eqc += (i < n && key[e] == kth);
-    }
-    const int incl = block_inclusive_scan(eqc, wave_tot);
-    int rank = eq_seen + incl - eqc;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t i = b0 + threadIdx.x * 4 + e;
-      if (i >= n) continue;
-      bool take = key[e] > kth;
-      if (key[e] == kth) {
-        take = rank < need_eq;
-        ++rank;
-      }
-      if (take) {
-        const int pos = atomicAdd(&s_count, 1);
-        s[pos] = compose(key[e], i);
-      }
-    }
-    eq_seen += wave_tot[kBig / 64 - 1];
-    __syncthreads();
-  }
   int P = 1;
   while (P < kk) P <<= 1;
-  for (int j = kk + threadIdx.x; j < P; j += kBig) s[j] = 0ull;
-  bitonic_desc(s, P);
-  write_out(S, r, k, s, kk);
+  for (int j = kk + threadIdx.x; j < P; j += kBig) win[j] = 0ull;
+  bitonic_desc(win, P);
+  write_out(S, r, k, win, kk);
 }
 
 }  // namespace
