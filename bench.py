@@ -180,6 +180,168 @@ def cpu_baseline(layer0, w, n_sample):
                         f"{dt:.1f} s on 1 thread"))
 
 
+def _event_pair():
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def bench_pack(dev, reps=5):
+    """fathom_pack of one 1M-key layer (storage side, off the per-token path)."""
+    w = synth.LAYER_1M
+    keys = synth.keys(w.seed, 99, w.n, w.hkv, w.d, w.dtype, w.outliers, device=dev)
+    planes = torch.empty((w.hkv, w.d, 4, fathom.plane_words(w.n)), dtype=torch.int32, device=dev)
+    ws = torch.empty(fathom.pack_workspace_bytes(w.n, w.hkv), dtype=torch.uint8, device=dev)
+    fathom.pack(keys, planes=planes, ws=ws)
+    torch.cuda.synchronize()
+    a, b = _event_pair()
+    a.record()
+    for _ in range(reps):
+        fathom.pack(keys, planes=planes, ws=ws)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    alg = keys.numel() * keys.element_size() + planes.numel() * 4
+    return {"workload": "pack one 1M-key layer (fp16 keys -> planes, lo, hi, sigma2)",
+            "ms": round(ms, 3), "keys_per_s": round(w.n * w.hkv / (ms * 1e-3), 1),
+            "algorithmic_bytes": alg, "achieved_GBps": round(alg / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+def bench_layer_128k(dev, steps, warmup):
+    """131072-key layer, planes in HBM, B in {68, 92, 136}, k = 1024."""
+    w = synth.LAYER_128K
+    layers = []
+    for l in range(8):                      # 8 x 64 MiB of planes rotate past the MALL
+        keys = synth.keys(w.seed, l, w.n, w.hkv, w.d, w.dtype, w.outliers, device=dev)
+        p = fathom.pack(keys)
+        del keys
+        q = synth.queries(w.seed, l, w.hq, w.d, device=dev)
+        layers.append((p, q, torch.empty((w.hq, w.d), dtype=torch.uint8, device=dev),
+                       torch.empty((w.hq, w.n), device=dev)))
+    ws = torch.empty(fathom.topk_workspace_bytes(w.hq, w.k), dtype=torch.uint8, device=dev)
+    idx = torch.empty((w.hq, w.k), dtype=torch.int32, device=dev)
+    vals = torch.empty((w.hq, w.k), device=dev)
+    out = {"workload": "qwen3-8b layer n=131072, planes in HBM, k=1024"}
+    for B in (68, 92, 136):
+        def step(i):
+            p, q, plan, logits = layers[i % len(layers)]
+            fathom.plan(q, p.sigma2, B, out=plan)
+            fathom.scan(p.planes, p.lo, p.hi, w.n, q, plan, out=logits)
+            fathom.topk(logits, w.k, ws=ws, idx=idx, vals=vals)
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        a, b = _event_pair()
+        a.record()
+        for i in range(steps):
+            step(i)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        ub = [union_plane_bytes(L[2], w.hkv, w.n)[0] for L in layers]
+        out[f"B{B}"] = {"step_ms": round(ms, 4),
+                        "keys_per_s": round(w.n * w.hkv / (ms * 1e-3), 1),
+                        "union_plane_bytes": int(np.mean(ub))}
+    return out
+
+
+def bench_sessions(dev, steps, warmup):
+    """16 ragged sessions (64K..512K keys), per-session B, planes in pinned host
+    memory, one batched scan and one batched top-k (k = 1024 per query head)."""
+    w = synth.SESSIONS_16
+    lengths = synth.session_lengths(w)
+    budgets = synth.session_budgets(w)
+    sess, sig = [], []
+    for s_, (n, B) in enumerate(zip(lengths, budgets)):
+        keys = synth.keys(w.seed, 0, n, w.hkv, w.d, w.dtype, w.outliers, device=dev, session=s_)
+        p = fathom.pack(keys)
+        del keys
+        host = torch.empty(p.planes.shape, dtype=p.planes.dtype, pin_memory=True)
+        host.copy_(p.planes)
+        p.planes = None
+        q = synth.queries(w.seed, 0, w.hq, w.d, device=dev, session=s_)
+        plan = torch.empty((w.hq, w.d), dtype=torch.uint8, device=dev)
+        sess.append(fathom.Session(host, p.lo, p.hi, n, q, plan,
+                                   torch.empty((w.hq, n), device=dev),
+                                   torch.empty((w.hq, w.k), dtype=torch.int32, device=dev),
+                                   torch.empty((w.hq, w.k), device=dev)))
+        sig.append((p.sigma2, B))
+    ws = torch.empty(fathom.topk_workspace_bytes(w.hq * len(sess), w.k), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.empty_cache()
+
+    def step():
+        for S, (s2, B) in zip(sess, sig):
+            fathom.plan(S.q, s2, B, out=S.plan)
+        fathom.scan_batched(sess)
+        fathom.topk_batched(sess, w.k, group=1, ws=ws)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = _event_pair()
+    a.record()
+    for _ in range(steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    total = sum(lengths) * w.hkv
+    plane_b = sum(union_plane_bytes(S.plan, w.hkv, S.n)[0] for S in sess)
+    return {"workload": "16 sessions, n uniform in [64K, 512K] (sum %d keys), B per session "
+                        "from {68, 92, 136}, planes in pinned host memory, k=1024" % sum(lengths),
+            "step_ms": round(ms, 3), "keys_per_s": round(total / (ms * 1e-3), 1),
+            "union_plane_bytes": plane_b,
+            "link_GBps": round(plane_b / (ms * 1e-3) / 1e9, 2)}
+
+
+def bench_step36(dev, steps, warmup):
+    """Full decode step at 1M tokens: 36 layers x (plan, scan, top-k), B = 92
+    and the fixed-136 scan, planes in HBM and in pinned host memory."""
+    w = synth.STEP_36L_1M
+    layers = []
+    for l in range(w.layers):
+        keys = synth.keys(w.seed, l, w.n, w.hkv, w.d, w.dtype, w.outliers, device=dev)
+        p = fathom.pack(keys)
+        del keys
+        host = torch.empty(p.planes.shape, dtype=p.planes.dtype, pin_memory=True)
+        host.copy_(p.planes)
+        q = synth.queries(w.seed, l, w.hq, w.d, device=dev)
+        meta = synth.side_stream(w.seed, l, w.hkv, w.n, device=dev)
+        layers.append((p, host, q, meta))
+    plan = torch.empty((w.hq, w.d), dtype=torch.uint8, device=dev)
+    logits = torch.empty((w.hq, w.n), device=dev)
+    idx = torch.empty((w.hq, w.k), dtype=torch.int32, device=dev)
+    vals = torch.empty((w.hq, w.k), device=dev)
+    ws = torch.empty(fathom.topk_workspace_bytes(w.hq, w.k), dtype=torch.uint8, device=dev)
+    out = {"workload": "36 layers x 1M keys (18 GiB of planes), 32 query heads, k=2048"}
+    for mode in ("hbm", "host"):
+        for fixed in (False, True):
+            def step():
+                for p, host, q, meta in layers:
+                    if fixed:
+                        fathom.plan_fixed(q, 32, out=plan)
+                    else:
+                        fathom.plan(q, p.sigma2, w.budget, out=plan)
+                    fathom.scan(host if mode == "host" else p.planes, p.lo, p.hi, w.n, q, plan,
+                                meta if fixed else None, 0.0, out=logits)
+                    fathom.topk(logits, w.k, ws=ws, idx=idx, vals=vals)
+            for _ in range(warmup):
+                step()
+            torch.cuda.synchronize()
+            a, b = _event_pair()
+            a.record()
+            for _ in range(steps):
+                step()
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / steps
+            out[f"{mode}{'_fixed136' if fixed else ''}"] = {
+                "step_ms": round(ms, 3),
+                "keys_per_s": round(w.layers * w.n * w.hkv / (ms * 1e-3), 1)}
+        out[f"{mode}_speedup_vs_fixed136"] = round(
+            out[f"{mode}_fixed136"]["step_ms"] / out[mode]["step_ms"], 3)
+    return out
+
+
 def scan_traffic_from_profiles():
     """HBM bytes per scan launch from committed rocprofv3 counter runs, valid
     only for the scan source they were taken on."""
@@ -204,6 +366,8 @@ def main():
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--only", choices=["all", "hbm", "host"], default="all",
                     help="profiling runs: restrict to one residency")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other workloads (pack, 128K layer, 16 sessions, 36 layers)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="counter runs: first copy 256 MiB device-to-device so the "
                          "HBM byte counters can be scaled by a kernel of known traffic")
@@ -318,6 +482,22 @@ def main():
     out["probe"] = probe
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(layers[0], w, args.cpu_sample)
+    if not args.no_extra:
+        del layers
+        torch.cuda.empty_cache()
+        extra = {}
+        extra["pack"] = bench_pack(dev)
+        log(f"pack: {extra['pack']}")
+        torch.cuda.empty_cache()
+        extra["layer_131072_hbm"] = bench_layer_128k(dev, 50, 5)
+        log(f"128K layer: {extra['layer_131072_hbm']}")
+        torch.cuda.empty_cache()
+        extra["sessions_16_host"] = bench_sessions(dev, 5, 2)
+        log(f"16 sessions: {extra['sessions_16_host']}")
+        torch.cuda.empty_cache()
+        extra["step_36_layers"] = bench_step36(dev, 3, 1)
+        log(f"36-layer step: {extra['step_36_layers']}")
+        out["other_workloads"] = extra
     print(json.dumps(out), flush=True)
 
 
