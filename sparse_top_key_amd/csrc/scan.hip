@@ -58,6 +58,11 @@ struct ScanArgs {
   int32_t n_sess, hkv, group, head0;
 };
 
+// The kernels read their descriptors in place from the kernel-argument
+// segment (address space 4): indexing them by session then needs no copy.
+typedef __attribute__((address_space(4))) const ScanArgs KScanArgs;
+typedef __attribute__((address_space(4))) const ScanSess KScanSess;
+
 // ---- 32x32 bit transpose ----------------------------------------------------
 // On entry x[r] bit k = element (r, k); on exit x[k] bit r = element (r, k).
 // Stage S swaps the off-diagonal SxS blocks of every 2Sx2S block.
@@ -141,33 +146,28 @@ __device__ __forceinline__ void load_group(const uint32_t *__restrict__ gplanes,
   }
 }
 
-template <int GH, int KPL, int AUX>
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
-  // ---- which session / kv head / tiles ------------------------------------
-  int si = 0;
-  for (int j = 1; j < a.n_sess; ++j)
-    if ((int)blockIdx.x >= a.s[j].block_begin) si = j;
-  const ScanSess &S = a.s[si];
-  const int local = blockIdx.x - S.block_begin;
-  const int g = local % a.hkv;
-  // block j of a kv head takes tiles j, j + B, j + 2B, ... (B blocks per
-  // head), so the blocks running together stream neighbouring addresses
-  const int tile0 = local / a.hkv;
-  const int tile_step = S.blocks_per_head;
-  const int64_t n = S.n;
-  const int head_base = g * a.group + a.head0;
+// ---- slot table (per block: one session, one kv head, GH query heads) ------
+// Slots are the distinct (channel, depth) pairs the GH heads read.  A slot of
+// depth u stands for the value of the channel's top u planes, placed at their
+// own bit positions; head h uses exactly the slots at its own depths with
+// weight gamma = q_hc * delta_c.  Slots are ordered by the set of heads using
+// them (larger sets first), then channel, then depth.
+template <int GH>
+struct SlotTable {
+  uint8_t t[GH][kD];
+  int32_t key[kMaxSlots];
+  int16_t desc[kMaxSlots];       // (channel << 3) | depth; 0 = padding slot
+  float gam[kMaxSlots][GH];      // gamma per slot and head (0: head does not use it)
+  uint8_t gmask[kMaxGroups];     // heads using any slot of an 8-slot group
+  double c[GH][kD];
+  float C[GH];                   // C_h = sum_c q_hc (lo_c + delta_c 2^(3 - t_hc))
+  int nslots;
+};
 
-  __shared__ uint8_t s_t[GH][kD];
-  __shared__ int32_t s_key[kMaxSlots];
-  __shared__ int16_t s_desc[kMaxSlots];       // (channel << 3) | depth
-  __shared__ float s_gam[kMaxSlots][GH];       // gamma per slot and head
-  __shared__ uint8_t s_gmask[kMaxGroups];      // heads using any slot of a group
-  __shared__ double s_c[GH][kD];
-  __shared__ float s_C[GH];
-  __shared__ int s_nslots;
-
+template <int GH>
+__device__ void build_slot_table(SlotTable<GH> &T, KScanSess &S, int g, int head_base) {
   const int tid = threadIdx.x;
-  if (tid == 0) s_nslots = 0;
+  if (tid == 0) T.nslots = 0;
   if (tid < kD) {
     const int c = tid;
     const float lo = S.lo[g * kD + c];
@@ -175,23 +175,21 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
 #pragma unroll
     for (int j = 0; j < GH; ++j) {
       const int t = S.plan[(int64_t)(head_base + j) * kD + c];
-      s_t[j][c] = (uint8_t)t;
+      T.t[j][c] = (uint8_t)t;
       // C_h term q * (lo + delta * 2^(3-t)) in fp64 (exact operands)
       const double mid = (double)lo + (double)delta * (double)(1 << (4 - t)) * 0.5;
-      s_c[j][c] = (double)S.q[(int64_t)(head_base + j) * kD + c] * mid;
+      T.c[j][c] = (double)S.q[(int64_t)(head_base + j) * kD + c] * mid;
     }
   }
   __syncthreads();
-  // ---- slots: distinct (channel, depth) pairs, keyed by (head set, c, depth)
-  for (int e = tid; e < kD * 4; e += kScanThreads) {
+  for (int e = tid; e < kD * 4; e += blockDim.x) {
     const int c = e >> 2, dep = (e & 3) + 1;
     int memb = 0;
 #pragma unroll
-    for (int j = 0; j < GH; ++j) memb |= (s_t[j][c] == dep) << j;
+    for (int j = 0; j < GH; ++j) memb |= (T.t[j][c] == dep) << j;
     if (memb) {
-      // larger head sets first; then channel, depth
       const int key = ((15 - __popc(memb)) << 16) | (memb << 11) | (c << 2) | (dep - 1);
-      s_key[atomicAdd(&s_nslots, 1)] = key;
+      T.key[atomicAdd(&T.nslots, 1)] = key;
     }
   }
   // fp64 reduction of C_h (fixed tree order)
@@ -199,42 +197,80 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
     __syncthreads();
     if (tid < stride) {
 #pragma unroll
-      for (int j = 0; j < GH; ++j) s_c[j][tid] += s_c[j][tid + stride];
+      for (int j = 0; j < GH; ++j) T.c[j][tid] += T.c[j][tid + stride];
     }
   }
   __syncthreads();
-  if (tid < GH) s_C[tid] = (float)s_c[tid][0];
-  const int nslots = s_nslots;
+  if (tid < GH) T.C[tid] = (float)T.c[tid][0];
+  const int nslots = T.nslots;
   const int ngroups = (nslots + 7) >> 3;
-  for (int e = tid; e < nslots; e += kScanThreads) {
-    const int key = s_key[e];
+  for (int e = tid; e < nslots; e += blockDim.x) {
+    const int key = T.key[e];
     int rank = 0;
-    for (int j = 0; j < nslots; ++j) rank += s_key[j] < key;
+    for (int j = 0; j < nslots; ++j) rank += T.key[j] < key;
     const int c = (key >> 2) & 127, dep = (key & 3) + 1;
     const int memb = (key >> 11) & 31;
-    s_desc[rank] = (int16_t)((c << 3) | dep);
+    T.desc[rank] = (int16_t)((c << 3) | dep);
     const float lo = S.lo[g * kD + c];
     const float delta = __fmul_rn(__fsub_rn(S.hi[g * kD + c], lo), 0.0625f);
 #pragma unroll
     for (int j = 0; j < GH; ++j)
-      s_gam[rank][j] = ((memb >> j) & 1)
+      T.gam[rank][j] = ((memb >> j) & 1)
                            ? __fmul_rn(S.q[(int64_t)(head_base + j) * kD + c], delta)
                            : 0.0f;
   }
-  for (int e = nslots + tid; e < ngroups * 8; e += kScanThreads) {
-    s_desc[e] = 0;  // padding slot: depth 0, reads nothing, weight 0
+  for (int e = nslots + tid; e < ngroups * 8; e += blockDim.x) {
+    T.desc[e] = 0;
 #pragma unroll
-    for (int j = 0; j < GH; ++j) s_gam[e][j] = 0.0f;
+    for (int j = 0; j < GH; ++j) T.gam[e][j] = 0.0f;
   }
   __syncthreads();
-  for (int gi = tid; gi < ngroups; gi += kScanThreads) {
+  for (int gi = tid; gi < ngroups; gi += blockDim.x) {
     int m = 0;
     for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int h = 0; h < GH; ++h) m |= (s_gam[gi * 8 + j][h] != 0.0f) << h;
-    s_gmask[gi] = (uint8_t)m;
+      for (int h = 0; h < GH; ++h) m |= (T.gam[gi * 8 + j][h] != 0.0f) << h;
+    T.gmask[gi] = (uint8_t)m;
   }
   __syncthreads();
+}
+
+// Block -> (session, kv head, first tile); tiles are taken with a stride of
+// the number of blocks per head so that blocks running together stream
+// neighbouring addresses.
+struct BlockWork {
+  KScanSess *S;
+  int g, tile0, tile_step, head_base;
+};
+
+__device__ __forceinline__ BlockWork block_work(const ScanArgs &) {
+  // the descriptors are read in place from the kernel-argument segment (the
+  // kernels' only argument), so indexing them does not copy them to scratch
+  KScanArgs &a = *(KScanArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+  int si = 0;
+  for (int j = 1; j < a.n_sess; ++j)
+    if ((int)blockIdx.x >= a.s[j].block_begin) si = j;
+  BlockWork w;
+  w.S = &a.s[si];
+  const int local = blockIdx.x - w.S->block_begin;
+  w.g = local % a.hkv;
+  w.tile0 = local / a.hkv;
+  w.tile_step = w.S->blocks_per_head;
+  w.head_base = w.g * a.group + a.head0;
+  return w;
+}
+
+template <int GH, int KPL, int AUX>
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
+  const BlockWork bw = block_work(a);
+  KScanSess &S = *bw.S;
+  const int g = bw.g, tile0 = bw.tile0, tile_step = bw.tile_step, head_base = bw.head_base;
+  const int64_t n = S.n;
+  __shared__ SlotTable<GH> T;
+  build_slot_table<GH>(T, S, g, head_base);
+  const int tid = threadIdx.x;
+  const int ngroups = (T.nslots + 7) >> 3;
+  const int16_t *s_desc = T.desc;
 
   // ---- main loop ------------------------------------------------------------
   // KPL = 32: lane = one plane word (32 keys), a wave covers 64 words, and
@@ -252,7 +288,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   const uint32_t *gplanes = S.planes + (int64_t)g * kD * kPlanes * S.W;
   float C[GH];
 #pragma unroll
-  for (int j = 0; j < GH; ++j) C[j] = s_C[j];
+  for (int j = 0; j < GH; ++j) C[j] = T.C[j];
 
   for (int tt = 0; tt < S.tiles_per_block; ++tt) {
     const int64_t wkey0 =
@@ -285,13 +321,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
         transpose32(y);
       else
         transpose16(y);
-      const int gm = uniform(s_gmask[grp]);
+      const int gm = uniform(T.gmask[grp]);
       // the group's weights, wave-uniform: held in scalar registers
       float gv[GH][8];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int h = 0; h < GH; ++h) gv[h][j] = uniform_f(s_gam[grp * 8 + j][h]);
+        for (int h = 0; h < GH; ++h) gv[h][j] = uniform_f(T.gam[grp * 8 + j][h]);
       if (gm == (1 << GH) - 1) {
 #pragma unroll
         for (int k = 0; k < KPL; ++k) {
@@ -356,6 +392,158 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   }
 }
 
+// ---- matrix-core scan (planes in HBM) --------------------------------------
+// The contraction s_hi = C_h + sum_slot gamma_{h,slot} m_{slot,i} runs on
+// v_mfma_i32_16x16x64_i8 (rows: 4 heads x 4 limbs, columns: 16 keys, K: 64
+// slots).  Per head, gamma is put in fixed point G = rint(gamma 2^(30-E_h))
+// with 2^(E_h-1) <= max|gamma| < 2^E_h, and G is split into four balanced
+// signed 8-bit limbs, so the integer products and sums are exact; the
+// quantisation error is at most 2^-31 max|gamma| per weight, i.e. below
+// 15 * 512 * 2^-31 * max|gamma| <= 1.2e-7 A_h.  An fp32 epilogue combines the
+// limbs, scales by 2^(E_h-30) and adds C_h.
+//
+// A block takes 1024-key tiles (32 plane words per row).  For each pass of up
+// to 64 slots, its 4 waves bit-transpose 2 slot groups each (lane = plane word
+// of one group, 32 keys x 8 slots per lane) into an LDS table of per-key
+// nibble words; then each wave runs the MFMAs for 256 keys (16 blocks of 16
+// keys, 64 accumulator registers).
+constexpr int kMTileKeys = 1024;
+constexpr int kPassGroups = 8;                        // 8 groups x 8 slots = K 64
+constexpr int kMaxPasses = kMaxGroups / kPassGroups;  // 8
+constexpr int kGroupPitch = kMTileKeys + kMTileKeys / 32;  // 1056 words
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// LDS index of (group-in-pass gp, key): a skew of one word per 32 keys and
+// 16 words per group pair makes both the transpose stores and the operand
+// loads conflict-free.
+__device__ __forceinline__ int code_index(int gp, int key) {
+  return gp * kGroupPitch + key + (key >> 5) + 16 * (gp >> 1);
+}
+
+template <int GH>
+__global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(ScanArgs a) {
+  const BlockWork bw = block_work(a);
+  KScanSess &S = *bw.S;
+  const int g = bw.g, head_base = bw.head_base;
+  const int64_t n = S.n;
+  const int64_t W = S.W;
+  __shared__ SlotTable<GH> T;
+  __shared__ uint32_t s_codes[kPassGroups * kGroupPitch + 64];
+  __shared__ __align__(16) int32_t s_limbs[kMaxPasses][64][4];
+  __shared__ float s_scale[kMaxGH];
+  __shared__ int s_exp[kMaxGH];
+  build_slot_table<GH>(T, S, g, head_base);
+  const int tid = threadIdx.x;
+  const int nslots = T.nslots;
+  const int ngroups = (nslots + 7) >> 3;
+  const int npasses = (ngroups + kPassGroups - 1) / kPassGroups;
+
+  // fixed-point exponent per head
+  if (tid < GH) {
+    float m = 0.0f;
+    for (int sl = 0; sl < nslots; ++sl) m = fmaxf(m, fabsf(T.gam[sl][tid]));
+    int e = 0;
+    if (m > 0.0f) frexpf(m, &e);
+    s_exp[tid] = e;
+    s_scale[tid] = ldexpf(1.0f, e - 30);
+  }
+  __syncthreads();
+  // A operands: lane l = row (head (l%16)/4, limb (l%16)%4), slot chunk l/16;
+  // dword d, byte b <-> slot 64p + 16(l/16) + 8(d/2) + 2b + (d%2), the order
+  // in which the code words are split into bytes below.
+  uint8_t *limb_bytes = reinterpret_cast<uint8_t *>(&s_limbs[0][0][0]);
+  for (int idx = tid; idx < npasses * 64 * 16; idx += kScanThreads) {
+    const int p = idx >> 10, l = (idx >> 4) & 63, d = (idx >> 2) & 3, b = idx & 3;
+    const int r = l & 15, h = r >> 2, limb = r & 3, j = l >> 4;
+    const int slot = 64 * p + 16 * j + 8 * (d >> 1) + 2 * b + (d & 1);
+    int v = 0;
+    if (h < GH && slot < nslots) {
+      int G = (int)rintf(ldexpf(T.gam[slot][h], 30 - s_exp[h]));
+      for (int i = 0; i < limb; ++i) {
+        const int dg = ((G + 128) & 255) - 128;
+        G = (G - dg) >> 8;
+      }
+      v = ((G + 128) & 255) - 128;
+    }
+    limb_bytes[idx] = (uint8_t)(int8_t)v;
+  }
+  __syncthreads();
+
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wl = lane & 31, gsel = lane >> 5;
+  const int hh = lane >> 4;                 // head of this lane's results
+  const float Ch = hh < GH ? T.C[hh] : 0.0f;
+  const float scale = hh < GH ? s_scale[hh] : 0.0f;
+  const uint32_t *gplanes = S.planes + (int64_t)g * kD * kPlanes * W;
+
+  for (int tt = 0; tt < S.tiles_per_block; ++tt) {
+    const int64_t key0 = (int64_t)(bw.tile0 + tt * bw.tile_step) * kMTileKeys;
+    if (key0 >= n) break;  // uniform across the block
+    const int64_t wbase = key0 / 32;
+    v4i acc[16];
+#pragma unroll
+    for (int b = 0; b < 16; ++b) acc[b] = v4i{0, 0, 0, 0};
+
+    for (int p = 0; p < npasses; ++p) {
+      // ---- transpose phase: this lane's group, word wl of the tile
+      const int gp = 2 * wave + gsel;        // group within the pass
+      const int grp = kPassGroups * p + gp;
+      if (grp < ngroups) {
+        uint32_t x[32];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int desc = T.desc[grp * 8 + j];
+          const int c = desc >> 3, dep = desc & 7;
+          const uint32_t *pc = gplanes + (int64_t)c * kPlanes * W + wbase + wl;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint32_t v = 0;
+            if (3 - q < dep) v = __builtin_nontemporal_load(pc + (int64_t)(3 - q) * W);
+            x[4 * j + q] = v;
+          }
+        }
+        transpose32(x);
+#pragma unroll
+        for (int k = 0; k < 32; ++k) s_codes[code_index(gp, 32 * wl + k)] = x[k];
+      }
+      __syncthreads();
+      // ---- MFMA phase: 256 keys of this wave, 16 keys per instruction
+      const int4 av = *reinterpret_cast<const int4 *>(&s_limbs[p][lane][0]);
+      const v4i A = v4i{av.x, av.y, av.z, av.w};
+      const int j = lane >> 4;
+#pragma unroll
+      for (int b = 0; b < 16; ++b) {
+        const int key = 256 * wave + 16 * b + (lane & 15);
+        const uint32_t w0 = s_codes[code_index(2 * j, key)];
+        const uint32_t w1 = s_codes[code_index(2 * j + 1, key)];
+        const v4i B = v4i{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu),
+                          (int)(w1 & 0x0F0F0F0Fu), (int)((w1 >> 4) & 0x0F0F0F0Fu)};
+        acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, acc[b], 0, 0, 0);
+      }
+      __syncthreads();
+    }
+
+    // ---- epilogue: lane holds the 4 limb sums of (head hh, one key) per block
+    if (hh < GH) {
+      float *out = S.logits + (int64_t)(head_base + hh) * S.ld;
+#pragma unroll
+      for (int b = 0; b < 16; ++b) {
+        const int64_t key = key0 + 256 * wave + 16 * b + (lane & 15);
+        float t = (float)acc[b][3];
+        t = __fmaf_rn(t, 256.0f, (float)acc[b][2]);
+        t = __fmaf_rn(t, 256.0f, (float)acc[b][1]);
+        t = __fmaf_rn(t, 256.0f, (float)acc[b][0]);
+        float sv = __fmaf_rn(t, scale, Ch);
+        if (key < n) {
+          if (S.meta) sv = __fmaf_rn(S.meta_scale, (float)S.meta[(int64_t)g * n + key], sv);
+          out[key] = sv;
+        }
+      }
+    }
+  }
+}
+
 // out[h][i][c] = floor(code_ic / 2^(4 - t_hc)): the planes as a query reads them.
 __global__ __launch_bounds__(256) void read_prefixes_kernel(
     const uint32_t *__restrict__ planes, int64_t n, int64_t W, int32_t group,
@@ -394,9 +582,19 @@ ScanFn pick(int GH) {
   }
 }
 
+ScanFn pick_mfma(int GH) {
+  switch (GH) {
+    case 1: return scan_mfma_kernel<1>;
+    case 2: return scan_mfma_kernel<2>;
+    case 3: return scan_mfma_kernel<3>;
+    default: return scan_mfma_kernel<4>;
+  }
+}
+
+// Pinned-host planes: the link is the bound, the fp32 kernel with whole-word
+// lanes keeps 256-byte wave accesses.  HBM planes: the matrix-core kernel.
 ScanFn kernel_for(bool host, int GH) {
-  return host ? pick<kHostVariant.kpl, kHostVariant.aux>(GH)
-              : pick<kDeviceVariant.kpl, kDeviceVariant.aux>(GH);
+  return host ? pick<kHostVariant.kpl, kHostVariant.aux>(GH) : pick_mfma(GH);
 }
 
 int resident_blocks_per_cu(bool host, int GH) {
@@ -432,8 +630,8 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv,
     }
     any_host |= attr.type == hipMemoryTypeHost;
   }
-  const int kpl = any_host ? kHostVariant.kpl : kDeviceVariant.kpl;
-  const int64_t tile_keys = (int64_t)kpl * 64 * (kScanThreads / 64);
+  const int64_t tile_keys =
+      any_host ? (int64_t)kHostVariant.kpl * 64 * (kScanThreads / 64) : (int64_t)kMTileKeys;
   for (int32_t s0 = 0; s0 < n_sess; s0 += kSessPerLaunch) {
     const int32_t cnt = std::min(kSessPerLaunch, n_sess - s0);
     for (int32_t head0 = 0; head0 < group; head0 += kMaxGH) {
