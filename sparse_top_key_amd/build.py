@@ -24,6 +24,8 @@ CFLAGS = [
     "-ffp-contract=off", "-fno-fast-math",
     # packed fp32 arithmetic stays off in every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators stay in ordinary VGPRs (no AGPR copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

@@ -86,6 +86,28 @@ __device__ __forceinline__ void transpose32(uint32_t (&x)[32]) {
   transpose_stage<32, 1, 0x55555555u>(x);
 }
 
+// The same transpose; the two byte-granular stages (16 and 8) use one byte
+// permute per output word.
+__device__ __forceinline__ void transpose32_perm(uint32_t (&x)[32]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const uint32_t a = x[r], b = x[r + 16];
+    x[r] = __builtin_amdgcn_perm(b, a, 0x05040100u);       // a.lo16 | b.lo16 << 16
+    x[r + 16] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // a.hi16 | b.hi16 << 16
+  }
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    if ((r & 8) == 0) {
+      const uint32_t a = x[r], b = x[r + 8];
+      x[r] = __builtin_amdgcn_perm(b, a, 0x06020400u);      // bytes a0 b0 a2 b2
+      x[r + 8] = __builtin_amdgcn_perm(b, a, 0x07030501u);  // bytes a1 b1 a3 b3
+    }
+  }
+  transpose_stage<32, 4, 0x0F0F0F0Fu>(x);
+  transpose_stage<32, 2, 0x33333333u>(x);
+  transpose_stage<32, 1, 0x55555555u>(x);
+}
+
 // Stages 8..1 on one 16-row half that stage 16 has already separated.
 __device__ __forceinline__ void transpose16(uint32_t (&x)[16]) {
   transpose_stage<16, 8, 0x00FF00FFu>(x);
@@ -154,18 +176,24 @@ __device__ __forceinline__ void load_group(const uint32_t *__restrict__ gplanes,
 // them (larger sets first), then channel, then depth.
 template <int GH>
 struct SlotTable {
-  uint8_t t[GH][kD];
-  int32_t key[kMaxSlots];
   int16_t desc[kMaxSlots];       // (channel << 3) | depth; 0 = padding slot
   float gam[kMaxSlots][GH];      // gamma per slot and head (0: head does not use it)
   uint8_t gmask[kMaxGroups];     // heads using any slot of an 8-slot group
-  double c[GH][kD];
   float C[GH];                   // C_h = sum_c q_hc (lo_c + delta_c 2^(3 - t_hc))
   int nslots;
 };
 
+// Set-up-only storage; the matrix-core kernel overlays it on its code table.
 template <int GH>
-__device__ void build_slot_table(SlotTable<GH> &T, KScanSess &S, int g, int head_base) {
+struct SlotScratch {
+  double c[GH][kD];
+  int32_t key[kMaxSlots];
+  uint8_t t[GH][kD];
+};
+
+template <int GH>
+__device__ void build_slot_table(SlotTable<GH> &T, SlotScratch<GH> &X, KScanSess &S, int g,
+                                 int head_base) {
   const int tid = threadIdx.x;
   if (tid == 0) T.nslots = 0;
   if (tid < kD) {
@@ -175,10 +203,10 @@ __device__ void build_slot_table(SlotTable<GH> &T, KScanSess &S, int g, int head
 #pragma unroll
     for (int j = 0; j < GH; ++j) {
       const int t = S.plan[(int64_t)(head_base + j) * kD + c];
-      T.t[j][c] = (uint8_t)t;
+      X.t[j][c] = (uint8_t)t;
       // C_h term q * (lo + delta * 2^(3-t)) in fp64 (exact operands)
       const double mid = (double)lo + (double)delta * (double)(1 << (4 - t)) * 0.5;
-      T.c[j][c] = (double)S.q[(int64_t)(head_base + j) * kD + c] * mid;
+      X.c[j][c] = (double)S.q[(int64_t)(head_base + j) * kD + c] * mid;
     }
   }
   __syncthreads();
@@ -186,10 +214,10 @@ __device__ void build_slot_table(SlotTable<GH> &T, KScanSess &S, int g, int head
     const int c = e >> 2, dep = (e & 3) + 1;
     int memb = 0;
 #pragma unroll
-    for (int j = 0; j < GH; ++j) memb |= (T.t[j][c] == dep) << j;
+    for (int j = 0; j < GH; ++j) memb |= (X.t[j][c] == dep) << j;
     if (memb) {
       const int key = ((15 - __popc(memb)) << 16) | (memb << 11) | (c << 2) | (dep - 1);
-      T.key[atomicAdd(&T.nslots, 1)] = key;
+      X.key[atomicAdd(&T.nslots, 1)] = key;
     }
   }
   // fp64 reduction of C_h (fixed tree order)
@@ -197,17 +225,17 @@ __device__ void build_slot_table(SlotTable<GH> &T, KScanSess &S, int g, int head
     __syncthreads();
     if (tid < stride) {
 #pragma unroll
-      for (int j = 0; j < GH; ++j) T.c[j][tid] += T.c[j][tid + stride];
+      for (int j = 0; j < GH; ++j) X.c[j][tid] += X.c[j][tid + stride];
     }
   }
   __syncthreads();
-  if (tid < GH) T.C[tid] = (float)T.c[tid][0];
+  if (tid < GH) T.C[tid] = (float)X.c[tid][0];
   const int nslots = T.nslots;
   const int ngroups = (nslots + 7) >> 3;
   for (int e = tid; e < nslots; e += blockDim.x) {
-    const int key = T.key[e];
+    const int key = X.key[e];
     int rank = 0;
-    for (int j = 0; j < nslots; ++j) rank += T.key[j] < key;
+    for (int j = 0; j < nslots; ++j) rank += X.key[j] < key;
     const int c = (key >> 2) & 127, dep = (key & 3) + 1;
     const int memb = (key >> 11) & 31;
     T.desc[rank] = (int16_t)((c << 3) | dep);
@@ -267,7 +295,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   const int g = bw.g, tile0 = bw.tile0, tile_step = bw.tile_step, head_base = bw.head_base;
   const int64_t n = S.n;
   __shared__ SlotTable<GH> T;
-  build_slot_table<GH>(T, S, g, head_base);
+  __shared__ SlotScratch<GH> X;
+  build_slot_table<GH>(T, X, S, g, head_base);
   const int tid = threadIdx.x;
   const int ngroups = (T.nslots + 7) >> 3;
   const int16_t *s_desc = T.desc;
@@ -429,15 +458,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(ScanArgs a) {
   const int64_t n = S.n;
   const int64_t W = S.W;
   __shared__ SlotTable<GH> T;
-  __shared__ uint32_t s_codes[kPassGroups * kGroupPitch + 64];
+  __shared__ __align__(16) uint32_t s_codes[kPassGroups * kGroupPitch + 64];
+  static_assert(sizeof(SlotScratch<GH>) <= sizeof(s_codes), "set-up overlay");
   __shared__ __align__(16) int32_t s_limbs[kMaxPasses][64][4];
   __shared__ float s_scale[kMaxGH];
   __shared__ int s_exp[kMaxGH];
-  build_slot_table<GH>(T, S, g, head_base);
+  build_slot_table<GH>(T, *reinterpret_cast<SlotScratch<GH> *>(s_codes), S, g, head_base);
   const int tid = threadIdx.x;
   const int nslots = T.nslots;
   const int ngroups = (nslots + 7) >> 3;
-  const int npasses = (ngroups + kPassGroups - 1) / kPassGroups;
+  // at least one pass, so that a plan reading nothing still writes C_h
+  const int npasses = max(1, (ngroups + kPassGroups - 1) / kPassGroups);
 
   // fixed-point exponent per head
   if (tid < GH) {
@@ -475,69 +506,98 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(ScanArgs a) {
   const int hh = lane >> 4;                 // head of this lane's results
   const float Ch = hh < GH ? T.C[hh] : 0.0f;
   const float scale = hh < GH ? s_scale[hh] : 0.0f;
+  // descriptor fields read once
   const uint32_t *gplanes = S.planes + (int64_t)g * kD * kPlanes * W;
+  const int64_t ld = S.ld;
+  const uint8_t *meta = S.meta;
+  const float meta_scale = S.meta_scale;
+  float *out_row = hh < GH ? S.logits + (int64_t)(head_base + hh) * ld : nullptr;
+  const int tiles_per_block = S.tiles_per_block;
+  // One buffer resource over this kv head's planes (the launcher keeps them
+  // under 2 GiB).  Plane slot s of channel c, word w sits at byte
+  // c*chan_bytes + s*row_bytes + 4w; offsets past the resource read 0 and
+  // touch no memory, which is how unread planes are skipped.
+  const uint32_t row_bytes = (uint32_t)(W * 4);
+  const uint32_t chan_bytes = row_bytes * kPlanes;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t *>(gplanes), (short)0, (int32_t)(chan_bytes * kD), kRsrcWord3);
 
-  for (int tt = 0; tt < S.tiles_per_block; ++tt) {
-    const int64_t key0 = (int64_t)(bw.tile0 + tt * bw.tile_step) * kMTileKeys;
-    if (key0 >= n) break;  // uniform across the block
-    const int64_t wbase = key0 / 32;
-    v4i acc[16];
+  // Work items = (tile, pass).  The plane words of item i+1 are loaded while
+  // item i is transposed, multiplied and written out.
+  int ntiles = 0;
+  while (ntiles < tiles_per_block &&
+         (int64_t)(bw.tile0 + ntiles * bw.tile_step) * kMTileKeys < n)
+    ++ntiles;
+  const int nitems = ntiles * npasses;
+  const int gp = 2 * wave + gsel;  // this lane's group within a pass
+  auto issue = [&](int item, uint32_t(&x)[32]) {
+    const int tt = item / npasses, p = item - tt * npasses;
+    const int grp = kPassGroups * p + gp;
+    const uint32_t lane_off =
+        ((uint32_t)(bw.tile0 + tt * bw.tile_step) * (kMTileKeys / 32) + (uint32_t)wl) * 4u;
 #pragma unroll
-    for (int b = 0; b < 16; ++b) acc[b] = v4i{0, 0, 0, 0};
-
-    for (int p = 0; p < npasses; ++p) {
-      // ---- transpose phase: this lane's group, word wl of the tile
-      const int gp = 2 * wave + gsel;        // group within the pass
-      const int grp = kPassGroups * p + gp;
-      if (grp < ngroups) {
-        uint32_t x[32];
+    for (int j = 0; j < 8; ++j) {
+      const int desc = grp < ngroups ? T.desc[grp * 8 + j] : 0;
+      const uint32_t c = (uint32_t)desc >> 3, dep = (uint32_t)desc & 7u;
+      const uint32_t off = __umul24(c, chan_bytes) + lane_off;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int desc = T.desc[grp * 8 + j];
-          const int c = desc >> 3, dep = desc & 7;
-          const uint32_t *pc = gplanes + (int64_t)c * kPlanes * W + wbase + wl;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint32_t v = 0;
-            if (3 - q < dep) v = __builtin_nontemporal_load(pc + (int64_t)(3 - q) * W);
-            x[4 * j + q] = v;
-          }
-        }
-        transpose32(x);
-#pragma unroll
-        for (int k = 0; k < 32; ++k) s_codes[code_index(gp, 32 * wl + k)] = x[k];
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t sl = 3 - q;  // plane slot holding bit q
+        const uint32_t voff = sl < dep ? off : 0x80000000u;
+        x[4 * j + q] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int32_t)voff,
+                                                            (int32_t)(sl * row_bytes), 0);
       }
-      __syncthreads();
-      // ---- MFMA phase: 256 keys of this wave, 16 keys per instruction
-      const int4 av = *reinterpret_cast<const int4 *>(&s_limbs[p][lane][0]);
-      const v4i A = v4i{av.x, av.y, av.z, av.w};
-      const int j = lane >> 4;
-#pragma unroll
-      for (int b = 0; b < 16; ++b) {
-        const int key = 256 * wave + 16 * b + (lane & 15);
-        const uint32_t w0 = s_codes[code_index(2 * j, key)];
-        const uint32_t w1 = s_codes[code_index(2 * j + 1, key)];
-        const v4i B = v4i{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu),
-                          (int)(w1 & 0x0F0F0F0Fu), (int)((w1 >> 4) & 0x0F0F0F0Fu)};
-        acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, acc[b], 0, 0, 0);
-      }
-      __syncthreads();
     }
+  };
+
+  uint32_t xn[32];
+  if (nitems > 0) issue(0, xn);
+  v4i acc[16];
+  for (int it = 0; it < nitems; ++it) {
+    const int tt = it / npasses, p = it - tt * npasses;
+    uint32_t x[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) x[r] = xn[r];
+    if (it + 1 < nitems) issue(it + 1, xn);
+    // ---- transpose phase: this lane's group, word wl of the tile
+    if (kPassGroups * p + gp < ngroups) {
+      transpose32_perm(x);
+#pragma unroll
+      for (int k = 0; k < 32; ++k) s_codes[code_index(gp, 32 * wl + k)] = x[k];
+    }
+    __syncthreads();
+    // ---- MFMA phase: 256 keys of this wave, 16 keys per instruction
+    const int4 av = *reinterpret_cast<const int4 *>(&s_limbs[p][lane][0]);
+    const v4i A = v4i{av.x, av.y, av.z, av.w};
+    const int j = lane >> 4;
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      const int key = 256 * wave + 16 * b + (lane & 15);
+      const uint32_t w0 = s_codes[code_index(2 * j, key)];
+      const uint32_t w1 = s_codes[code_index(2 * j + 1, key)];
+      const v4i B = v4i{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu),
+                        (int)(w1 & 0x0F0F0F0Fu), (int)((w1 >> 4) & 0x0F0F0F0Fu)};
+      acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, p == 0 ? v4i{0, 0, 0, 0} : acc[b],
+                                                     0, 0, 0);
+    }
+    __syncthreads();
 
     // ---- epilogue: lane holds the 4 limb sums of (head hh, one key) per block
-    if (hh < GH) {
-      float *out = S.logits + (int64_t)(head_base + hh) * S.ld;
+    if (p == npasses - 1 && hh < GH) {
+      const int64_t kl = (int64_t)(bw.tile0 + tt * bw.tile_step) * kMTileKeys + 256 * wave +
+                         (lane & 15);
+      float *op = out_row + kl;
+      const bool full = kl - (lane & 15) + 256 <= n;
 #pragma unroll
       for (int b = 0; b < 16; ++b) {
-        const int64_t key = key0 + 256 * wave + 16 * b + (lane & 15);
-        float t = (float)acc[b][3];
-        t = __fmaf_rn(t, 256.0f, (float)acc[b][2]);
-        t = __fmaf_rn(t, 256.0f, (float)acc[b][1]);
-        t = __fmaf_rn(t, 256.0f, (float)acc[b][0]);
+        // limb pairs combine exactly in int32 (|sum| < 2^29)
+        const int lo = acc[b][0] + acc[b][1] * 256;
+        const int hi = acc[b][2] + acc[b][3] * 256;
+        const float t = __fmaf_rn((float)hi, 65536.0f, (float)lo);
         float sv = __fmaf_rn(t, scale, Ch);
-        if (key < n) {
-          if (S.meta) sv = __fmaf_rn(S.meta_scale, (float)S.meta[(int64_t)g * n + key], sv);
-          out[key] = sv;
+        if (full || kl + 16 * b < n) {
+          if (meta) sv = __fmaf_rn(meta_scale, (float)meta[(int64_t)g * n + kl + 16 * b], sv);
+          op[16 * b] = sv;
         }
       }
     }
@@ -592,7 +652,8 @@ ScanFn pick_mfma(int GH) {
 }
 
 // Pinned-host planes: the link is the bound, the fp32 kernel with whole-word
-// lanes keeps 256-byte wave accesses.  HBM planes: the matrix-core kernel.
+// lanes keeps 256-byte wave accesses.  HBM planes: the matrix-core kernel
+// (the fp32 kernel above 2^25 keys per session).
 ScanFn kernel_for(bool host, int GH) {
   return host ? pick<kHostVariant.kpl, kHostVariant.aux>(GH) : pick_mfma(GH);
 }
@@ -630,8 +691,13 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv,
     }
     any_host |= attr.type == hipMemoryTypeHost;
   }
+  // The matrix-core kernel addresses a kv head's planes with 32-bit buffer
+  // offsets: sessions up to 2^25 keys (2 GiB of planes per kv head).
+  int64_t max_n = 0;
+  for (int32_t j = 0; j < n_sess; ++j) max_n = std::max(max_n, sess[j].n);
+  const bool fp32_path = any_host || max_n > ((int64_t)1 << 25);
   const int64_t tile_keys =
-      any_host ? (int64_t)kHostVariant.kpl * 64 * (kScanThreads / 64) : (int64_t)kMTileKeys;
+      fp32_path ? (int64_t)kHostVariant.kpl * 64 * (kScanThreads / 64) : (int64_t)kMTileKeys;
   for (int32_t s0 = 0; s0 < n_sess; s0 += kSessPerLaunch) {
     const int32_t cnt = std::min(kSessPerLaunch, n_sess - s0);
     for (int32_t head0 = 0; head0 < group; head0 += kMaxGH) {
@@ -646,7 +712,7 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv,
         total_tiles += (sess[s0 + j].n + tile_keys - 1) / tile_keys * hkv;
       // one round of resident blocks: every block takes the same number of
       // tiles of one (session, kv head) and amortises its plan set-up
-      const int64_t target_blocks = (int64_t)ncu * resident_blocks_per_cu(any_host, GH);
+      const int64_t target_blocks = (int64_t)ncu * resident_blocks_per_cu(fp32_path, GH);
       int32_t blocks = 0;
       for (int j = 0; j < cnt; ++j) {
         const ScanSession &in = sess[s0 + j];
@@ -674,7 +740,7 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv,
         blocks += o.blocks_per_head * hkv;
       }
       if (blocks == 0) continue;
-      hipLaunchKernelGGL(kernel_for(any_host, GH), dim3(blocks), dim3(kScanThreads), 0, s, a);
+      hipLaunchKernelGGL(kernel_for(fp32_path, GH), dim3(blocks), dim3(kScanThreads), 0, s, a);
       int32_t rc = hip_fail(hipGetLastError(), "scan launch");
       if (rc) return rc;
     }
