@@ -130,23 +130,62 @@ __device__ int find_digit(const int *hist, int nbins, int rem, int *above,
   return d;
 }
 
-// Bitonic sort of s[0..P) descending (P a power of two, P <= kCandCap).
-__device__ void bitonic_desc(uint64_t *s, int P) {
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Sort w[0..m) descending (m <= FATHOM_MAX_K = 2048), entries past m read as
+// 0.  Bitonic network with each of the 1024 threads holding elements 2t and
+// 2t+1: stride 1 is a register compare, strides 2..64 exchange with the
+// partner lane in the same wave, and only strides >= 128 (10 steps) go
+// through LDS with barriers.
+__device__ void sort_winners_desc(uint64_t *w, int m) {
+  __syncthreads();
+  const int t = threadIdx.x;
+  uint64_t v[2];
+  v[0] = 2 * t < m ? w[2 * t] : 0ull;
+  v[1] = 2 * t + 1 < m ? w[2 * t + 1] : 0ull;
+  int P = 2;
+  while (P < m) P <<= 1;
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      __syncthreads();
-      for (int t = threadIdx.x; t < P / 2; t += kBig) {
-        const int lo = 2 * t - (t & (stride - 1));
-        const int hi = lo + stride;
-        const bool desc = (lo & size) == 0;
-        const uint64_t a = s[lo], b = s[hi];
-        if (desc ? (a < b) : (a > b)) {
-          s[lo] = b;
-          s[hi] = a;
+      if (stride == 1) {
+        const bool desc = ((2 * t) & size) == 0;
+        if (desc ? (v[0] < v[1]) : (v[0] > v[1])) {
+          const uint64_t x = v[0];
+          v[0] = v[1];
+          v[1] = x;
         }
+        continue;
+      }
+      const int pt = stride >> 1;  // partner thread distance
+      uint64_t o[2];
+      if (pt < 64) {
+        o[0] = shfl_xor64(v[0], pt);
+        o[1] = shfl_xor64(v[1], pt);
+      } else {
+        __syncthreads();
+        w[2 * t] = v[0];
+        w[2 * t + 1] = v[1];
+        __syncthreads();
+        o[0] = w[(2 * t) ^ stride];
+        o[1] = w[(2 * t + 1) ^ stride];
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int e = 2 * t + r;
+        const bool lo = (e & stride) == 0;
+        const bool desc = ((lo ? e : (e ^ stride)) & size) == 0;
+        const bool keep_max = (lo == desc);
+        const uint64_t mx = v[r] > o[r] ? v[r] : o[r], mn = v[r] > o[r] ? o[r] : v[r];
+        v[r] = keep_max ? mx : mn;
       }
     }
   }
+  __syncthreads();
+  w[2 * t] = v[0];
+  w[2 * t + 1] = v[1];
   __syncthreads();
 }
 
@@ -197,11 +236,13 @@ __global__ __launch_bounds__(kBig) void topk_sample_kernel(TopkArgs a) {
   int64_t rs = ((int64_t)5 * a.k * m + 2 * n - 1) / (2 * n);
   if (rs < 1) rs = 1;
   if (rs > m) rs = m;
+  // Two 11-bit radix passes: T = the top 22 bits of the rs-th largest sampled
+  // key, low bits 0 (it only has to leave about 2.5k scores at or above it).
   int rem = (int)rs;
   uint32_t prefix = 0, pmask = 0;
-  const int shifts[3] = {21, 10, 0};
-  const int bits[3] = {11, 11, 10};
-  for (int pass = 0; pass < 3; ++pass) {
+  const int shifts[2] = {21, 10};
+  const int bits[2] = {11, 11};
+  for (int pass = 0; pass < 2; ++pass) {
     const int sh = shifts[pass], nb = 1 << bits[pass];
     for (int b = threadIdx.x; b < kHistBins; b += kBig) hist[b] = 0;
     __syncthreads();
@@ -240,10 +281,23 @@ __global__ __launch_bounds__(kCompactThreads) void topk_compact_kernel(TopkArgs 
   const bool vec = a.group == 1 && ((reinterpret_cast<uintptr_t>(R.row) & 15) == 0);
   if (threadIdx.x == 0) s_n = 0;
   __syncthreads();
-  for (int it = 0; it < kCompactChunk / (kCompactThreads * 4); ++it) {
+  constexpr int kIters = kCompactChunk / (kCompactThreads * 4);
+  float4 pre[kIters];
+  const bool full = vec && base + kCompactChunk <= n;
+  if (full) {
+    // every load of the chunk in flight at once
+#pragma unroll
+    for (int it = 0; it < kIters; ++it)
+      pre[it] = *reinterpret_cast<const float4 *>(R.row + base + (int64_t)it * kCompactThreads * 4 +
+                                                  threadIdx.x * 4);
+  }
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
     const int64_t i0 = base + (int64_t)it * kCompactThreads * 4 + threadIdx.x * 4;
     float v[4];
-    if (vec && i0 + 3 < n) {
+    if (full) {
+      v[0] = pre[it].x; v[1] = pre[it].y; v[2] = pre[it].z; v[3] = pre[it].w;
+    } else if (vec && i0 + 3 < n) {
       const float4 f = *reinterpret_cast<const float4 *>(R.row + i0);
       v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
     } else {
@@ -411,10 +465,7 @@ __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
     }
   }
   __syncthreads();
-  int P = 1;
-  while (P < kk) P <<= 1;
-  for (int j = kk + threadIdx.x; j < P; j += kBig) win[j] = 0ull;
-  bitonic_desc(win, P);
+  sort_winners_desc(win, kk);
   write_out(S, r, k, win, kk);
 }
 
