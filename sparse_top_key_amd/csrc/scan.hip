@@ -424,46 +424,67 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
 // ---- matrix-core scan (planes in HBM) --------------------------------------
 // The contraction s_hi = C_h + sum_slot gamma_{h,slot} m_{slot,i} runs on
 // v_mfma_i32_16x16x64_i8 (rows: 4 heads x 4 limbs, columns: 16 keys, K: 64
-// slots).  Per head, gamma is put in fixed point G = rint(gamma 2^(30-E_h))
-// with 2^(E_h-1) <= max|gamma| < 2^E_h, and G is split into four balanced
-// signed 8-bit limbs, so the integer products and sums are exact; the
-// quantisation error is at most 2^-31 max|gamma| per weight, i.e. below
-// 15 * 512 * 2^-31 * max|gamma| <= 1.2e-7 A_h.  An fp32 epilogue combines the
-// limbs, scales by 2^(E_h-30) and adds C_h.
+// slots = one pass).  Per head, gamma is put in fixed point
+// G = rint(gamma 2^(30-E_h)) with 2^(E_h-1) <= max|gamma| < 2^E_h, and G is
+// split into four balanced signed 8-bit limbs, so the integer products and
+// sums of a pass are exact; the quantisation error is at most
+// 2^-31 max|gamma| per weight, i.e. below 15 * 512 * 2^-31 * max|gamma| <=
+// 1.2e-7 A_h.  Per pass, an fp32 step combines the limbs and adds
+// 2^(E_h-30) times them to the key's running value, which starts at C_h (one
+// rounding per pass).
 //
-// A block takes 1024-key tiles (32 plane words per row).  For each pass of up
-// to 64 slots, its 4 waves bit-transpose 2 slot groups each (lane = plane word
-// of one group, 32 keys x 8 slots per lane) into an LDS table of per-key
-// nibble words; then each wave runs the MFMAs for 256 keys (16 blocks of 16
-// keys, 64 accumulator registers).
-constexpr int kMTileKeys = 1024;
+// A block of 8 waves takes 2048-key tiles (64 plane words per row).  In a
+// pass, wave w reads slot group w (8 slots x 4 planes = 32 rows) with 16-byte
+// loads: a quarter of the wave (16 lanes) covers one row, 4 words per lane,
+// and one load instruction covers the 4 planes of one slot.  Two lane swaps
+// (32-lane halves, then 16-lane rows) regroup the words so that every lane
+// holds one plane word (32 keys) of all 32 rows, which it bit-transposes into
+// 32 per-key nibble words in LDS.  Then each wave runs the MFMAs for 256 keys
+// (16 blocks of 16 keys); its lanes end with 4 consecutive keys of one head,
+// written as one 16-byte store.  Wide loads matter: with 4-byte lanes the
+// memory pipeline, not HBM, limits the read rate at this occupancy.
+constexpr int kMThreads = 512;
+constexpr int kMTileKeys = 2048;
 constexpr int kPassGroups = 8;                        // 8 groups x 8 slots = K 64
 constexpr int kMaxPasses = kMaxGroups / kPassGroups;  // 8
-constexpr int kGroupPitch = kMTileKeys + kMTileKeys / 32;  // 1056 words
+// group pitch in the code table: >= 2113 words (2048 keys + skews), = 1 mod 4
+constexpr int kGroupPitch = 2113;
+constexpr uint32_t kUnread = 0x80000000u;  // at or past the end of any kv head's planes
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// LDS index of (group-in-pass gp, key): a skew of one word per 32 keys and
-// 16 words per group pair makes both the transpose stores and the operand
-// loads conflict-free.
+// LDS index of (group-in-pass gp, key).  Skews: one word per 32 keys, two
+// more per 1024 keys, and a pitch of 1 mod 4 between groups.  Transpose
+// stores (32 lanes at keys 32w + t, w = 4m + k, k in {0,1} or {2,3}) and
+// operand loads (16 lanes at keys 4n + e, two groups 2 apart) then hit 32
+// distinct banks.
 __device__ __forceinline__ int code_index(int gp, int key) {
-  return gp * kGroupPitch + key + (key >> 5) + 16 * (gp >> 1);
+  return gp * kGroupPitch + key + (key >> 5) + 2 * (key >> 10);
 }
 
+// Set-up-only state of the matrix-core kernel, overlaid on its code table.
 template <int GH>
-__global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(ScanArgs a) {
+struct MfmaSetup {
+  SlotTable<GH> T;
+  SlotScratch<GH> X;
+};
+
+template <int GH>
+__global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   const BlockWork bw = block_work(a);
   KScanSess &S = *bw.S;
   const int g = bw.g, head_base = bw.head_base;
   const int64_t n = S.n;
   const int64_t W = S.W;
-  __shared__ SlotTable<GH> T;
-  __shared__ __align__(16) uint32_t s_codes[kPassGroups * kGroupPitch + 64];
-  static_assert(sizeof(SlotScratch<GH>) <= sizeof(s_codes), "set-up overlay");
+  __shared__ __align__(16) uint32_t s_codes[kPassGroups * kGroupPitch + 4];
+  static_assert(sizeof(MfmaSetup<GH>) <= sizeof(s_codes), "set-up overlay");
   __shared__ __align__(16) int32_t s_limbs[kMaxPasses][64][4];
-  __shared__ float s_scale[kMaxGH];
+  __shared__ __align__(16) int16_t s_desc[kMaxSlots];
+  __shared__ float s_scale[kMaxGH], s_C[kMaxGH];
   __shared__ int s_exp[kMaxGH];
-  build_slot_table<GH>(T, *reinterpret_cast<SlotScratch<GH> *>(s_codes), S, g, head_base);
+  MfmaSetup<GH> &U = *reinterpret_cast<MfmaSetup<GH> *>(s_codes);
+  SlotTable<GH> &T = U.T;
+  build_slot_table<GH>(T, U.X, S, g, head_base);
   const int tid = threadIdx.x;
   const int nslots = T.nslots;
   const int ngroups = (nslots + 7) >> 3;
@@ -478,13 +499,16 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(ScanArgs a) {
     if (m > 0.0f) frexpf(m, &e);
     s_exp[tid] = e;
     s_scale[tid] = ldexpf(1.0f, e - 30);
+    s_C[tid] = T.C[tid];
   }
+  for (int e = tid; e < npasses * kPassGroups * 8; e += kMThreads)
+    s_desc[e] = e < nslots ? T.desc[e] : (int16_t)0;
   __syncthreads();
   // A operands: lane l = row (head (l%16)/4, limb (l%16)%4), slot chunk l/16;
   // dword d, byte b <-> slot 64p + 16(l/16) + 8(d/2) + 2b + (d%2), the order
   // in which the code words are split into bytes below.
   uint8_t *limb_bytes = reinterpret_cast<uint8_t *>(&s_limbs[0][0][0]);
-  for (int idx = tid; idx < npasses * 64 * 16; idx += kScanThreads) {
+  for (int idx = tid; idx < npasses * 64 * 16; idx += kMThreads) {
     const int p = idx >> 10, l = (idx >> 4) & 63, d = (idx >> 2) & 3, b = idx & 3;
     const int r = l & 15, h = r >> 2, limb = r & 3, j = l >> 4;
     const int slot = 64 * p + 16 * j + 8 * (d >> 1) + 2 * b + (d & 1);
@@ -499,28 +523,31 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(ScanArgs a) {
     }
     limb_bytes[idx] = (uint8_t)(int8_t)v;
   }
-  __syncthreads();
+  __syncthreads();  // the code table is free from here on
 
   const int wave = tid >> 6, lane = tid & 63;
-  const int wl = lane & 31, gsel = lane >> 5;
-  const int hh = lane >> 4;                 // head of this lane's results
-  const float Ch = hh < GH ? T.C[hh] : 0.0f;
+  const int quarter = lane >> 4, m16 = lane & 15;
+  const int hh = lane >> 4;  // head of this lane's results (MFMA row block)
+  const float Ch = hh < GH ? s_C[hh] : 0.0f;
   const float scale = hh < GH ? s_scale[hh] : 0.0f;
-  // descriptor fields read once
   const uint32_t *gplanes = S.planes + (int64_t)g * kD * kPlanes * W;
   const int64_t ld = S.ld;
-  const uint8_t *meta = S.meta;
+  const uint8_t *meta = S.meta ? S.meta + (int64_t)g * n : nullptr;
   const float meta_scale = S.meta_scale;
   float *out_row = hh < GH ? S.logits + (int64_t)(head_base + hh) * ld : nullptr;
+  const bool vec_out = S.vec_out != 0;
   const int tiles_per_block = S.tiles_per_block;
   // One buffer resource over this kv head's planes (the launcher keeps them
-  // under 2 GiB).  Plane slot s of channel c, word w sits at byte
-  // c*chan_bytes + s*row_bytes + 4w; offsets past the resource read 0 and
+  // within 2 GiB).  Plane slot s of channel c, word w sits at byte
+  // c*chan_bytes + s*row_bytes + 4w; offsets at or past kUnread read 0 and
   // touch no memory, which is how unread planes are skipped.
   const uint32_t row_bytes = (uint32_t)(W * 4);
   const uint32_t chan_bytes = row_bytes * kPlanes;
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t *>(gplanes), (short)0, (int32_t)(chan_bytes * kD), kRsrcWord3);
+  // quarter k loads code bit k, i.e. plane slot 3 - k, words 4*m16 .. +3
+  const uint32_t plane_sl = 3u - (uint32_t)quarter;
+  const uint32_t lane_part = plane_sl * row_bytes + (uint32_t)m16 * 16u;
 
   // Work items = (tile, pass).  The plane words of item i+1 are loaded while
   // item i is transposed, multiplied and written out.
@@ -529,75 +556,125 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(ScanArgs a) {
          (int64_t)(bw.tile0 + ntiles * bw.tile_step) * kMTileKeys < n)
     ++ntiles;
   const int nitems = ntiles * npasses;
-  const int gp = 2 * wave + gsel;  // this lane's group within a pass
   auto issue = [&](int item, uint32_t(&x)[32]) {
     const int tt = item / npasses, p = item - tt * npasses;
-    const int grp = kPassGroups * p + gp;
-    const uint32_t lane_off =
-        ((uint32_t)(bw.tile0 + tt * bw.tile_step) * (kMTileKeys / 32) + (uint32_t)wl) * 4u;
+    const int grp = kPassGroups * p + wave;
+    if (grp >= ngroups) return;  // empty group: nothing to read
+    const uint32_t tile_off = (uint32_t)(bw.tile0 + tt * bw.tile_step) * (kMTileKeys / 8);
+    const uint4 dv = *reinterpret_cast<const uint4 *>(&s_desc[grp * 8]);
+    const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int desc = grp < ngroups ? T.desc[grp * 8 + j] : 0;
-      const uint32_t c = (uint32_t)desc >> 3, dep = (uint32_t)desc & 7u;
-      const uint32_t off = __umul24(c, chan_bytes) + lane_off;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t sl = 3 - q;  // plane slot holding bit q
-        const uint32_t voff = sl < dep ? off : 0x80000000u;
-        x[4 * j + q] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int32_t)voff,
-                                                            (int32_t)(sl * row_bytes), 0);
-      }
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t desc = __builtin_amdgcn_readfirstlane((dw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+      const uint32_t c = desc >> 3, dep = desc & 7u;
+      const uint32_t voff = plane_sl < dep ? c * chan_bytes + tile_off + lane_part : kUnread;
+      const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int32_t)voff, 0, 0);
+      x[4 * i + 0] = (uint32_t)v[0];
+      x[4 * i + 1] = (uint32_t)v[1];
+      x[4 * i + 2] = (uint32_t)v[2];
+      x[4 * i + 3] = (uint32_t)v[3];
     }
   };
 
   uint32_t xn[32];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) xn[r] = 0;
   if (nitems > 0) issue(0, xn);
-  v4i acc[16];
+  float s[16];
   for (int it = 0; it < nitems; ++it) {
     const int tt = it / npasses, p = it - tt * npasses;
+    const int64_t tile_key0 = (int64_t)(bw.tile0 + tt * bw.tile_step) * kMTileKeys;
+    const bool has_group = kPassGroups * p + wave < ngroups;
+    // ---- regroup: quarter k ends with word 4*m16 + k of the 4 plane rows of
+    // every slot; 32-lane halves first, then 16-lane rows.
     uint32_t x[32];
+    if (has_group) {
 #pragma unroll
-    for (int r = 0; r < 32; ++r) x[r] = xn[r];
+      for (int i = 0; i < 8; ++i) {
+        const auto h02 = __builtin_amdgcn_permlane32_swap(xn[4 * i + 0], xn[4 * i + 2], false, false);
+        const auto h13 = __builtin_amdgcn_permlane32_swap(xn[4 * i + 1], xn[4 * i + 3], false, false);
+        x[4 * i + 0] = h02[0];
+        x[4 * i + 2] = h02[1];
+        x[4 * i + 1] = h13[0];
+        x[4 * i + 3] = h13[1];
+      }
+    }
     if (it + 1 < nitems) issue(it + 1, xn);
-    // ---- transpose phase: this lane's group, word wl of the tile
-    if (kPassGroups * p + gp < ngroups) {
-      transpose32_perm(x);
+    if (has_group) {
 #pragma unroll
-      for (int k = 0; k < 32; ++k) s_codes[code_index(gp, 32 * wl + k)] = x[k];
+      for (int i = 0; i < 8; ++i) {
+        const auto r01 = __builtin_amdgcn_permlane16_swap(x[4 * i + 0], x[4 * i + 1], false, false);
+        const auto r23 = __builtin_amdgcn_permlane16_swap(x[4 * i + 2], x[4 * i + 3], false, false);
+        x[4 * i + 0] = r01[0];
+        x[4 * i + 1] = r01[1];
+        x[4 * i + 2] = r23[0];
+        x[4 * i + 3] = r23[1];
+      }
+      // ---- transpose: x[4j+q] = bit q of slot j for keys 32w..32w+31 of the
+      // tile, w = 4*m16 + quarter; afterwards x[t] = the 8 codes of key 32w+t
+      transpose32_perm(x);
+      const int w = 4 * m16 + quarter;
+      uint32_t *dst = &s_codes[code_index(wave, 32 * w)];
+#pragma unroll
+      for (int t = 0; t < 32; ++t) dst[t] = x[t];
     }
     __syncthreads();
-    // ---- MFMA phase: 256 keys of this wave, 16 keys per instruction
+    // ---- MFMA phase: 256 keys of this wave; block b = 4*beta + e covers keys
+    // 64*beta + 4*n + e (n = lane % 16)
     const int4 av = *reinterpret_cast<const int4 *>(&s_limbs[p][lane][0]);
     const v4i A = v4i{av.x, av.y, av.z, av.w};
-    const int j = lane >> 4;
+    const int j = lane >> 4, nn = lane & 15;
+    if (p == 0) {
 #pragma unroll
-    for (int b = 0; b < 16; ++b) {
-      const int key = 256 * wave + 16 * b + (lane & 15);
-      const uint32_t w0 = s_codes[code_index(2 * j, key)];
-      const uint32_t w1 = s_codes[code_index(2 * j + 1, key)];
-      const v4i B = v4i{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu),
-                        (int)(w1 & 0x0F0F0F0Fu), (int)((w1 >> 4) & 0x0F0F0F0Fu)};
-      acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, p == 0 ? v4i{0, 0, 0, 0} : acc[b],
-                                                     0, 0, 0);
+      for (int b = 0; b < 16; ++b) s[b] = Ch;
+    }
+#pragma unroll
+    for (int beta = 0; beta < 4; ++beta) {
+      v4i acc[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = 256 * wave + 64 * beta + 4 * nn + e;
+        const uint32_t w0 = s_codes[code_index(2 * j, key)];
+        const uint32_t w1 = s_codes[code_index(2 * j + 1, key)];
+        const v4i B = v4i{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu),
+                          (int)(w1 & 0x0F0F0F0Fu), (int)((w1 >> 4) & 0x0F0F0F0Fu)};
+        acc[e] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // limb pairs combine exactly in int32 (|sum| < 2^29)
+        const int lo = acc[e][0] + acc[e][1] * 256;
+        const int hi = acc[e][2] + acc[e][3] * 256;
+        const float t = __fmaf_rn((float)hi, 65536.0f, (float)lo);
+        s[4 * beta + e] = __fmaf_rn(t, scale, s[4 * beta + e]);
+      }
     }
     __syncthreads();
 
-    // ---- epilogue: lane holds the 4 limb sums of (head hh, one key) per block
+    // ---- epilogue: 4 consecutive keys of head hh per beta
     if (p == npasses - 1 && hh < GH) {
-      const int64_t kl = (int64_t)(bw.tile0 + tt * bw.tile_step) * kMTileKeys + 256 * wave +
-                         (lane & 15);
-      float *op = out_row + kl;
-      const bool full = kl - (lane & 15) + 256 <= n;
+      const int64_t kb = tile_key0 + 256 * wave + 4 * nn;  // + 64*beta + e
+      if (meta) {
+        uint32_t mb[16];
 #pragma unroll
-      for (int b = 0; b < 16; ++b) {
-        // limb pairs combine exactly in int32 (|sum| < 2^29)
-        const int lo = acc[b][0] + acc[b][1] * 256;
-        const int hi = acc[b][2] + acc[b][3] * 256;
-        const float t = __fmaf_rn((float)hi, 65536.0f, (float)lo);
-        float sv = __fmaf_rn(t, scale, Ch);
-        if (full || kl + 16 * b < n) {
-          if (meta) sv = __fmaf_rn(meta_scale, (float)meta[(int64_t)g * n + kl + 16 * b], sv);
-          op[16 * b] = sv;
+        for (int b = 0; b < 16; ++b) {
+          const int64_t key = kb + 64 * (b >> 2) + (b & 3);
+          mb[b] = key < n ? meta[key] : 0u;
+        }
+#pragma unroll
+        for (int b = 0; b < 16; ++b) s[b] = __fmaf_rn(meta_scale, (float)mb[b], s[b]);
+      }
+      float *op = out_row + kb;
+      if (vec_out && tile_key0 + 256 * (wave + 1) <= n) {  // wave-uniform
+#pragma unroll
+        for (int beta = 0; beta < 4; ++beta)
+          *reinterpret_cast<float4 *>(op + 64 * beta) =
+              make_float4(s[4 * beta], s[4 * beta + 1], s[4 * beta + 2], s[4 * beta + 3]);
+      } else {
+#pragma unroll
+        for (int b = 0; b < 16; ++b) {
+          const int64_t off = 64 * (b >> 2) + (b & 3);
+          if (kb + off < n) op[off] = s[b];
         }
       }
     }
@@ -657,6 +734,7 @@ ScanFn pick_mfma(int GH) {
 ScanFn kernel_for(bool host, int GH) {
   return host ? pick<kHostVariant.kpl, kHostVariant.aux>(GH) : pick_mfma(GH);
 }
+int threads_for(bool host) { return host ? kScanThreads : kMThreads; }
 
 int resident_blocks_per_cu(bool host, int GH) {
   static int cached[2][kMaxGH + 1] = {};
@@ -664,7 +742,7 @@ int resident_blocks_per_cu(bool host, int GH) {
   if (c == 0) {
     int nb = 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &nb, kernel_for(host, GH), kScanThreads, 0);
+        &nb, kernel_for(host, GH), threads_for(host), 0);
     c = (e == hipSuccess && nb > 0) ? nb : 1;
   }
   return c;
@@ -740,7 +818,8 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv,
         blocks += o.blocks_per_head * hkv;
       }
       if (blocks == 0) continue;
-      hipLaunchKernelGGL(kernel_for(fp32_path, GH), dim3(blocks), dim3(kScanThreads), 0, s, a);
+      hipLaunchKernelGGL(kernel_for(fp32_path, GH), dim3(blocks), dim3(threads_for(fp32_path)), 0,
+                         s, a);
       int32_t rc = hip_fail(hipGetLastError(), "scan launch");
       if (rc) return rc;
     }
