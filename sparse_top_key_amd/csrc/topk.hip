@@ -135,23 +135,17 @@ __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// Sort w[0..m) descending (m <= FATHOM_MAX_K = 2048), entries past m read as
-// 0.  Bitonic network with each of the 1024 threads holding elements 2t and
-// 2t+1: stride 1 is a register compare, strides 2..64 exchange with the
-// partner lane in the same wave, and only strides >= 128 (10 steps) go
-// through LDS with barriers.
-__device__ void sort_winners_desc(uint64_t *w, int m) {
-  __syncthreads();
-  const int t = threadIdx.x;
-  uint64_t v[2];
-  v[0] = 2 * t < m ? w[2 * t] : 0ull;
-  v[1] = 2 * t + 1 < m ? w[2 * t + 1] : 0ull;
-  int P = 2;
-  while (P < m) P <<= 1;
-  for (int size = 2; size <= P; size <<= 1) {
+// In-wave bitonic sort of 128 words, descending: lane l holds elements 2l and
+// 2l+1.  Stride 1 is a register compare; strides 2..64 exchange with the
+// partner lane (distance stride/2).
+__device__ __forceinline__ void wave_sort128_desc(uint64_t (&v)[2]) {
+  const int l = threadIdx.x & 63;
+#pragma unroll
+  for (int size = 2; size <= 128; size <<= 1) {
+#pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       if (stride == 1) {
-        const bool desc = ((2 * t) & size) == 0;
+        const bool desc = ((2 * l) & size) == 0;
         if (desc ? (v[0] < v[1]) : (v[0] > v[1])) {
           const uint64_t x = v[0];
           v[0] = v[1];
@@ -159,22 +153,12 @@ __device__ void sort_winners_desc(uint64_t *w, int m) {
         }
         continue;
       }
-      const int pt = stride >> 1;  // partner thread distance
-      uint64_t o[2];
-      if (pt < 64) {
-        o[0] = shfl_xor64(v[0], pt);
-        o[1] = shfl_xor64(v[1], pt);
-      } else {
-        __syncthreads();
-        w[2 * t] = v[0];
-        w[2 * t + 1] = v[1];
-        __syncthreads();
-        o[0] = w[(2 * t) ^ stride];
-        o[1] = w[(2 * t + 1) ^ stride];
-      }
+      const int pt = stride >> 1;
+      const uint64_t o0 = shfl_xor64(v[0], pt), o1 = shfl_xor64(v[1], pt);
+      const uint64_t o[2] = {o0, o1};
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
-        const int e = 2 * t + r;
+        const int e = 2 * l + r;
         const bool lo = (e & stride) == 0;
         const bool desc = ((lo ? e : (e ^ stride)) & size) == 0;
         const bool keep_max = (lo == desc);
@@ -183,10 +167,54 @@ __device__ void sort_winners_desc(uint64_t *w, int m) {
       }
     }
   }
+}
+
+// Sort the m <= FATHOM_MAX_K = 2048 unique words w[0..m) descending, with
+// entries past m read as 0; tmp is scratch of the same size.  Each wave
+// sorts a run of 128 in registers, then merge-path rounds double the run
+// length: thread t finds by binary search how many of the first 2t outputs
+// of its pair of runs come from the first run, and writes outputs 2t, 2t+1.
+// Returns the buffer holding the result.
+__device__ uint64_t *sort_winners_desc(uint64_t *w, uint64_t *tmp, int m) {
+  int P = 128;
+  while (P < m) P <<= 1;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   __syncthreads();
-  w[2 * t] = v[0];
-  w[2 * t + 1] = v[1];
+  if (wave < P / 128) {
+    const int e0 = 128 * wave + 2 * lane;
+    uint64_t v[2] = {e0 < m ? w[e0] : 0ull, e0 + 1 < m ? w[e0 + 1] : 0ull};
+    wave_sort128_desc(v);
+    w[e0] = v[0];
+    w[e0 + 1] = v[1];
+  }
+  uint64_t *src = w, *dst = tmp;
+  for (int L = 128; L < P; L <<= 1) {
+    __syncthreads();
+    if (t < P / 2) {
+      const int base = (2 * t) / (2 * L) * (2 * L);
+      const int d = 2 * t - base;
+      const uint64_t *A = src + base, *B = src + base + L;
+      int lo = d > L ? d - L : 0, hi = d < L ? d : L;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (A[mid] > B[d - 1 - mid])
+          lo = mid + 1;
+        else
+          hi = mid;
+      }
+      int ia = lo, ib = d - lo;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const bool takeA = ib >= L || (ia < L && A[ia] > B[ib]);
+        dst[base + d + r] = takeA ? A[ia++] : B[ib++];
+      }
+    }
+    uint64_t *x = src;
+    src = dst;
+    dst = x;
+  }
   __syncthreads();
+  return src;
 }
 
 __device__ __forceinline__ uint64_t compose(uint32_t key, int64_t i) {
@@ -386,11 +414,93 @@ __device__ uint64_t select_kth(const uint64_t *s, int m, int kk, int *hist, int 
   return prefix;
 }
 
+// OR of v over the block.
+__device__ uint64_t block_or64(uint64_t v, uint64_t *red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v |= shfl_xor64(v, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint64_t r = 0;
+#pragma unroll
+  for (int w = 0; w < kBig / 64; ++w) r |= red[w];
+  __syncthreads();
+  return r;
+}
+
+// Writes the kk largest of the unique words src[0..m) (1 <= kk <= m) to
+// output row r in descending order, without sorting: words are bucketed by
+// the 11 bits below their common prefix, the buckets at or above the one
+// holding the kk-th word are laid out in descending bucket order, and each
+// word's rank is its bucket's offset plus the number of larger words in its
+// bucket.  Returns false, having written nothing, when one of those buckets
+// holds more than kMaxBucket words (the caller then sorts).
+constexpr int kMaxBucket = 128;
+
+__device__ bool bucket_rank_out(const uint64_t *src, int m, int kk, uint64_t *buck, int *hist,
+                                int *above, int *wave_tot, int *s_res, uint64_t *red,
+                                const TopkSess &S, int r, int k) {
+  const int t = threadIdx.x;
+  uint64_t diff = 0;
+  const uint64_t w0 = src[0];
+  for (int j = t; j < m; j += kBig) diff |= src[j] ^ w0;
+  diff = block_or64(diff, red);
+  const int hb = diff ? 63 - __clzll(diff) : 0;  // highest bit in which words differ
+  const int sh = hb > 10 ? hb - 10 : 0;
+  for (int b = t; b < kHistBins; b += kBig) hist[b] = 0;
+  if (t == 0) s_res[1] = 0;
+  __syncthreads();
+  for (int j = t; j < m; j += kBig) atomicAdd(&hist[(int)((src[j] >> sh) & (kHistBins - 1))], 1);
+  __syncthreads();
+  // above[d] = words in digits > d; thread t owns digits 2047-2t and 2046-2t
+  const int d1 = kHistBins - 1 - 2 * t, d2 = d1 - 1;
+  const int c1 = hist[d1], c2 = hist[d2];
+  const int incl = block_inclusive_scan(c1 + c2, wave_tot);
+  const int excl = incl - c1 - c2;
+  above[d1] = excl;
+  above[d2] = excl + c1;
+  if (excl < kk && kk <= excl + c1) s_res[0] = d1;
+  if (excl + c1 < kk && kk <= incl) s_res[0] = d2;
+  __syncthreads();
+  const int db = s_res[0];  // digit holding the kk-th word
+  if ((d1 >= db && c1 > kMaxBucket) || (d2 >= db && c2 > kMaxBucket)) s_res[1] = 1;
+  __syncthreads();
+  if (s_res[1]) return false;
+  // bucket order; above[d] becomes the end of bucket d
+  for (int j = t; j < m; j += kBig) {
+    const uint64_t w = src[j];
+    const int d = (int)((w >> sh) & (kHistBins - 1));
+    if (d >= db) buck[atomicAdd(&above[d], 1)] = w;
+  }
+  __syncthreads();
+  const int total = above[db];
+  int32_t *idx = S.idx + (int64_t)r * k;
+  float *vals = S.vals + (int64_t)r * k;
+  for (int p = t; p < total; p += kBig) {
+    const uint64_t w = buck[p];
+    const int d = (int)((w >> sh) & (kHistBins - 1));
+    const int c = hist[d];
+    const int b0 = above[d] - c;
+    int rank = b0;
+    for (int q = b0; q < b0 + c; ++q) rank += buck[q] > w;
+    if (rank < kk) {
+      idx[rank] = (int32_t)(~(uint32_t)w);
+      vals[rank] = from_key((uint32_t)(w >> 32));
+    }
+  }
+  for (int j = kk + t; j < k; j += kBig) {
+    idx[j] = -1;
+    vals[j] = -INFINITY;
+  }
+  return true;
+}
+
 // ---- exact selection of each row's top k -------------------------------------
 __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
   __shared__ uint64_t s[kCandCap];
-  __shared__ uint64_t win[FATHOM_MAX_K];
+  __shared__ uint64_t win[FATHOM_MAX_K + kMaxBucket];
   __shared__ int hist[kHistBins];
+  __shared__ int above[kHistBins];
+  __shared__ uint64_t red[kBig / 64];
   __shared__ int wave_tot[16];
   __shared__ int s_res[2];
   __shared__ int s_count;
@@ -409,6 +519,9 @@ __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
     const uint64_t *cand = a.cand + (int64_t)o * kCandCap;
     for (int j = threadIdx.x; j < m; j += kBig) s[j] = cand[j];
     __syncthreads();
+    if (kk > 0 &&
+        bucket_rank_out(s, m, kk, win, hist, above, wave_tot, s_res, red, S, r, k))
+      return;
     if (kk > 0) {
       const uint64_t T = m > kk ? select_kth(s, m, kk, hist, wave_tot, s_res) : 0ull;
       for (int j = threadIdx.x; j < m; j += kBig)
@@ -465,8 +578,12 @@ __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
     }
   }
   __syncthreads();
-  sort_winners_desc(win, kk);
-  write_out(S, r, k, win, kk);
+  // win[0..kk) holds the winners
+  if (!fast && kk > 0 &&
+      bucket_rank_out(win, kk, kk, s, hist, above, wave_tot, s_res, red, S, r, k))
+    return;
+  const uint64_t *sorted = sort_winners_desc(win, s, kk);
+  write_out(S, r, k, sorted, kk);
 }
 
 }  // namespace
