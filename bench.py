@@ -78,8 +78,10 @@ def union_plane_bytes(plan, hkv, n):
     return sum(ub) * n // 8, ub, hist
 
 
-def run_steps(layers, w, ws, steps, mode, fixed=False):
-    """mode: 'host' or 'hbm'.  Returns per-step totals and per-call times (ms)."""
+def run_steps(layers, w, ws, steps, mode, fixed=False, fused=False):
+    """mode: 'host' or 'hbm'.  fused: fathom_scan_topk in place of fathom_scan
+    then fathom_topk (ws must then be its workspace).  Returns per-step totals
+    and per-call times (ms)."""
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for s in range(steps):
         L = layers[s % len(layers)]
@@ -94,9 +96,14 @@ def run_steps(layers, w, ws, steps, mode, fixed=False):
         else:
             plan = fathom.plan(L.q, L.sigma2, L.budget, out=L.plan)
         e[1].record()
-        fathom.scan(planes, L.lo, L.hi, L.n, L.q, plan, meta, 0.0, out=L.logits)
-        e[2].record()
-        fathom.topk(L.logits, w.k, ws=ws, idx=L.idx, vals=L.vals)
+        if fused:
+            fathom.scan_topk(planes, L.lo, L.hi, L.n, L.q, plan, w.k, 1, meta, 0.0, ws=ws,
+                             idx=L.idx, vals=L.vals)
+            e[2].record()
+        else:
+            fathom.scan(planes, L.lo, L.hi, L.n, L.q, plan, meta, 0.0, out=L.logits)
+            e[2].record()
+            fathom.topk(L.logits, w.k, ws=ws, idx=L.idx, vals=L.vals)
         e[3].record()
     return ev
 
@@ -112,11 +119,11 @@ def summarize(ev):
                 scan_ms_p90=float(np.percentile(scan, 90)))
 
 
-def timed(layers, w, ws, steps, warmup, mode, fixed=False):
-    run_steps(layers, w, ws, warmup, mode, fixed)
+def timed(layers, w, ws, steps, warmup, mode, fixed=False, fused=False):
+    run_steps(layers, w, ws, warmup, mode, fixed, fused)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev = run_steps(layers, w, ws, steps, mode, fixed)
+    ev = run_steps(layers, w, ws, steps, mode, fixed, fused)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     r = summarize(ev)
@@ -396,6 +403,8 @@ def main():
     host = args.only in ("all", "host")
     layers = [Layer(w, l, dev, host, 32) for l in range(args.layers)]
     ws = torch.empty(fathom.topk_workspace_bytes(w.hq, w.k), dtype=torch.uint8, device=dev)
+    fws = torch.empty(fathom.scan_topk_workspace_bytes([w.n], w.hkv, w.hq, 1, w.k),
+                      dtype=torch.uint8, device=dev)
     # plans once, for the byte accounting (the timed steps recompute them)
     for L in layers:
         fathom.plan(L.q, L.sigma2, L.budget, out=L.plan)
@@ -415,8 +424,11 @@ def main():
     for mode in (["host", "hbm"] if args.only == "all" else [args.only]):
         res[mode] = timed(layers, w, ws, args.steps, args.warmup, mode)
         res[mode + "_fixed"] = timed(layers, w, ws, args.steps, args.warmup, mode, fixed=True)
-        log(f"{mode}: {res[mode]}")
-        log(f"{mode} fixed-136: {res[mode + '_fixed']}")
+        res[mode + "_fused"] = timed(layers, w, fws, args.steps, args.warmup, mode, fused=True)
+        res[mode + "_fixed_fused"] = timed(layers, w, fws, args.steps, args.warmup, mode,
+                                           fixed=True, fused=True)
+        for key in (mode, mode + "_fixed", mode + "_fused", mode + "_fixed_fused"):
+            log(f"{key}: {res[key]}")
 
     keys_per_step = w.n * w.hkv
     main_mode = "host" if "host" in res else "hbm"
@@ -460,12 +472,18 @@ def main():
             "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBPS, 4),
             "traffic": (traffic or {}).get("hbm_scan_bytes"),
-            "kernel": "scan_kernel<4, 16, 0> (planes in HBM)",
+            "kernel": "scan_mfma_kernel<4, 0> (planes in HBM, all logits written)",
             "algorithmic_bytes": plane_b + logits_b,
             "end_to_end_plane_GBps": round(plane_b / (h["step_ms"] * 1e-3) / 1e9, 1)}
         if main_mode == "host":
             out["hbm_resident"] = {"keys_per_s": round(keys_per_step / (h["step_ms"] * 1e-3), 1),
                                    **{k: round(v, 4) for k, v in h.items()}}
+            hf = res["hbm_fused"]
+            out["hbm_resident_fused"] = {
+                "keys_per_s": round(keys_per_step / (hf["step_ms"] * 1e-3), 1),
+                "step_ms": round(hf["step_ms"], 4),
+                "scan_topk_ms": round(hf["scan_ms"], 4),
+                "plane_GBps": round(plane_b / (hf["scan_ms"] * 1e-3) / 1e9, 1)}
         else:
             out["roofline"] = out.pop("roofline_hbm")
     out["timings_ms"] = {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in res.items()}
@@ -473,6 +491,8 @@ def main():
         if mode in res:
             out.setdefault("fixed136_speedup", {})[mode] = round(
                 res[mode + "_fixed"]["step_ms"] / res[mode]["step_ms"], 3)
+            out["fixed136_speedup"][mode + "_fused"] = round(
+                res[mode + "_fixed_fused"]["step_ms"] / res[mode + "_fused"]["step_ms"], 3)
             out.setdefault("fixed136_scan_speedup", {})[mode] = round(
                 res[mode + "_fixed"]["scan_ms"] / res[mode]["scan_ms"], 3)
     out["bytes"] = {"fathom_union_plane_bytes": plane_b, "fixed136_plane_bytes": fixed_plan_b,

@@ -188,6 +188,40 @@ int32_t fathom_topk_batched(const fathom_session *sessions, int32_t n_sessions,
                             int32_t hq, int32_t group, int32_t k, void *ws,
                             int64_t ws_bytes, void *stream);
 
+/* ---- scan + top-k in one call --------------------------------------------
+ * Explainer, problem statement (every decode step scores the n keys and keeps
+ * the top k) with the scan of section 核心方法 (read side): idx and vals are
+ * those of fathom_scan followed by fathom_topk on the same inputs (same
+ * scores, ranking, tie order and padding), but the logits of all keys are
+ * not written unless needed.  With planes in device memory, n <= 2^25 and
+ * group 1 or hq/hkv (<= 4), the call scores a sample of 16384 keys per row,
+ * sets a per-row threshold from it, scans again keeping only the
+ * (score, index) pairs at or above the threshold, and ranks those; a row
+ * whose candidate count falls outside [k, 8192] is recomputed from full
+ * logits in the workspace.  Otherwise (pinned host planes, other groups,
+ * longer sessions) the full logits go to the workspace and are ranked there.
+ *
+ * Arguments as for fathom_scan and fathom_topk (group over the hq rows);
+ * idx, vals  device outputs int32/fp32[hq/group][k].
+ * ws         device workspace of fathom_scan_topk_workspace_bytes bytes.
+ * Enqueues 6 or fewer kernel launches; nothing synchronises.               */
+int64_t fathom_scan_topk_workspace_bytes(const int64_t *n_host, int32_t n_sessions,
+                                         int32_t hkv, int32_t hq, int32_t group,
+                                         int32_t k);
+int32_t fathom_scan_topk(const uint32_t *planes, const float *lo,
+                         const float *hi, int64_t n, int32_t hkv, int32_t d,
+                         const float *q, const uint8_t *plan, int32_t hq,
+                         const uint8_t *meta, float meta_scale, int32_t group,
+                         int32_t k, int32_t *idx, float *vals, void *ws,
+                         int64_t ws_bytes, void *stream);
+/* Many sessions: descriptors as for fathom_scan_batched (logits and
+ * ld_logits ignored; idx, vals required).  n_host of the workspace query
+ * lists the sessions' n in order.                                           */
+int32_t fathom_scan_topk_batched(const fathom_session *sessions,
+                                 int32_t n_sessions, int32_t hkv, int32_t d,
+                                 int32_t hq, int32_t group, int32_t k, void *ws,
+                                 int64_t ws_bytes, void *stream);
+
 /* ---- observability -------------------------------------------------------
  * The plane reads themselves, for bit-exact checks: out[h][i][c] =
  * floor(code_ic / 2^(4-t_hc)) (0 where t = 0).  out device uint8[hq][n][d]. */

@@ -70,6 +70,10 @@ def lib():
             "fathom_read_prefixes": (I32, [P, I64, I32, I32, P, I32, P, P]),
             "fathom_plan_stats": (I32, [P, I32, I32, I32, P, P]),
             "fathom_probe_read": (I32, [P, I64, P, I32, P]),
+            "fathom_scan_topk_workspace_bytes": (I64, [P, I32, I32, I32, I32, I32]),
+            "fathom_scan_topk": (I32, [P, P, P, I64, I32, I32, P, P, I32, P, F, I32, I32, P, P,
+                                       P, I64, P]),
+            "fathom_scan_topk_batched": (I32, [P, I32, I32, I32, I32, I32, I32, P, I64, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -217,7 +221,7 @@ class Session:
     n: int
     q: torch.Tensor
     plan: torch.Tensor
-    logits: torch.Tensor           # [hq][ld]
+    logits: Optional[torch.Tensor] = None   # [hq][ld] (not used by scan_topk_batched)
     idx: Optional[torch.Tensor] = None
     vals: Optional[torch.Tensor] = None
     meta: Optional[torch.Tensor] = None
@@ -230,7 +234,8 @@ def _sessions(sess: Sequence[Session]):
         arr[i] = _Session(s.planes.data_ptr(), s.lo.data_ptr(), s.hi.data_ptr(), s.n,
                           s.q.data_ptr(), s.plan.data_ptr(),
                           s.meta.data_ptr() if s.meta is not None else None, s.meta_scale,
-                          s.logits.data_ptr(), s.logits.stride(0),
+                          s.logits.data_ptr() if s.logits is not None else None,
+                          s.logits.stride(0) if s.logits is not None else 0,
                           s.idx.data_ptr() if s.idx is not None else None,
                           s.vals.data_ptr() if s.vals is not None else None)
     return arr
@@ -254,6 +259,49 @@ def topk_batched(sess: Sequence[Session], k: int, group: int = 1,
                          device=s0.q.device)
     _check(lib().fathom_topk_batched(_sessions(sess), len(sess), hq, group, k, _p(ws),
                                      ws.numel(), _stream(s0.q.device)), "fathom_topk_batched")
+
+
+def scan_topk_workspace_bytes(ns: Sequence[int], hkv: int, hq: int, group: int, k: int) -> int:
+    arr = (ctypes.c_int64 * len(ns))(*[int(x) for x in ns])
+    return int(lib().fathom_scan_topk_workspace_bytes(arr, len(ns), hkv, hq, group, k))
+
+
+def scan_topk(planes: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor, n: int,
+              q: torch.Tensor, plan_: torch.Tensor, k: int, group: int = 1,
+              meta: Optional[torch.Tensor] = None, meta_scale: float = 0.0,
+              ws: Optional[torch.Tensor] = None, idx=None, vals=None):
+    """Scan + top-k in one call -> (idx int32 [hq/group][k], vals fp32 [hq/group][k]),
+    the result of scan() followed by topk()."""
+    _require_gpu(planes, lo, q, plan_)
+    hkv, d = lo.shape
+    hq = q.shape[0]
+    ro = hq // group
+    dev = q.device
+    if idx is None:
+        idx = torch.empty((ro, k), dtype=torch.int32, device=dev)
+    if vals is None:
+        vals = torch.empty((ro, k), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(max(scan_topk_workspace_bytes([n], hkv, hq, group, k), 1),
+                         dtype=torch.uint8, device=dev)
+    _check(lib().fathom_scan_topk(_p(planes), _p(lo), _p(hi), n, hkv, d, _p(q), _p(plan_), hq,
+                                  _p(meta), meta_scale, group, k, _p(idx), _p(vals), _p(ws),
+                                  ws.numel(), _stream(dev)), "fathom_scan_topk")
+    return idx, vals
+
+
+def scan_topk_batched(sess: Sequence[Session], k: int, group: int = 1,
+                      ws: Optional[torch.Tensor] = None):
+    """Scan + top-k of every session into its idx/vals."""
+    s0 = sess[0]
+    hkv, d = s0.lo.shape
+    hq = s0.q.shape[0]
+    if ws is None:
+        ws = torch.empty(max(scan_topk_workspace_bytes([s.n for s in sess], hkv, hq, group, k),
+                             1), dtype=torch.uint8, device=s0.q.device)
+    _check(lib().fathom_scan_topk_batched(_sessions(sess), len(sess), hkv, d, hq, group, k,
+                                          _p(ws), ws.numel(), _stream(s0.q.device)),
+           "fathom_scan_topk_batched")
 
 
 def read_prefixes(planes: torch.Tensor, n: int, plan_: torch.Tensor, hkv: int) -> torch.Tensor:

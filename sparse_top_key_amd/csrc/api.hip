@@ -130,7 +130,7 @@ static int32_t check_scan_session(const fathom_session &s, int32_t hq, const cha
 }
 
 static ScanSession to_scan(const fathom_session &s) {
-  ScanSession o;
+  ScanSession o{};  // fused-path fields stay null
   o.planes = s.planes;
   o.lo = s.lo;
   o.hi = s.hi;
@@ -205,8 +205,9 @@ int32_t fathom_topk(const float *scores, int32_t rows, int64_t n, int64_t ld, in
   REQUIRE(ws && ws_bytes >= need, FATHOM_ERR_WORKSPACE,
           "fathom_topk: workspace of %lld bytes needed (got %lld)", (long long)need,
           (long long)ws_bytes);
-  TopkSession t{scores, n, ld, idx, vals};
-  return launch_topk(&t, 1, rows / group, group, k, ws, as_stream(stream));
+  TopkSession t{scores, n, ld, idx, vals, n};
+  const TopkWs w = topk_ws_carve(ws, rows / group, rows / group);
+  return launch_topk(&t, 1, rows / group, group, k, w, as_stream(stream));
 }
 
 int32_t fathom_topk_batched(const fathom_session *sessions, int32_t n_sessions, int32_t hq,
@@ -224,13 +225,97 @@ int32_t fathom_topk_batched(const fathom_session *sessions, int32_t n_sessions, 
             "fathom_topk_batched: n must be in [0, 2^31)");
     REQUIRE(s.n == 0 || s.logits, FATHOM_ERR_INVALID_ARG, "fathom_topk_batched: null logits");
     REQUIRE(s.ld_logits >= s.n, FATHOM_ERR_INVALID_ARG, "fathom_topk_batched: ld < n");
-    ts[i] = TopkSession{s.logits, s.n, s.ld_logits, s.idx, s.vals};
+    ts[i] = TopkSession{s.logits, s.n, s.ld_logits, s.idx, s.vals, s.n};
   }
-  const int64_t need = topk_workspace_bytes((int64_t)n_sessions * (hq / group));
+  const int32_t out_rows = n_sessions * (hq / group);
+  const int64_t need = topk_workspace_bytes(out_rows);
   REQUIRE(ws && ws_bytes >= need, FATHOM_ERR_WORKSPACE,
           "fathom_topk_batched: workspace of %lld bytes needed (got %lld)", (long long)need,
           (long long)ws_bytes);
-  return launch_topk(ts, n_sessions, hq / group, group, k, ws, as_stream(stream));
+  const TopkWs w = topk_ws_carve(ws, out_rows, out_rows);
+  return launch_topk(ts, n_sessions, hq / group, group, k, w, as_stream(stream));
+}
+
+int64_t fathom_scan_topk_workspace_bytes(const int64_t *n_host, int32_t n_sessions,
+                                         int32_t hkv, int32_t hq, int32_t group, int32_t k) {
+  if (!n_host || n_sessions < 1 || n_sessions > FATHOM_MAX_SESSIONS || hkv < 1 || hq < 1 ||
+      hq % hkv != 0 || group < 1 || hq % group != 0 || k < 1 || k > FATHOM_MAX_K)
+    return 0;
+  for (int32_t i = 0; i < n_sessions; ++i)
+    if (n_host[i] < 0 || n_host[i] >= ((int64_t)1 << 31)) return 0;
+  return scan_topk_ws_bytes(n_host, n_sessions, hkv, hq, group);
+}
+
+static int32_t check_scan_topk_session(const fathom_session &s, const char *who) {
+  REQUIRE(s.n >= 0 && s.n < ((int64_t)1 << 31), FATHOM_ERR_INVALID_ARG,
+          "%s: n must be in [0, 2^31) (got %lld)", who, (long long)s.n);
+  REQUIRE(s.idx && s.vals, FATHOM_ERR_INVALID_ARG, "%s: null output", who);
+  if (s.n == 0) return FATHOM_OK;
+  REQUIRE(s.planes && s.lo && s.hi && s.q && s.plan, FATHOM_ERR_INVALID_ARG,
+          "%s: null pointer", who);
+  return FATHOM_OK;
+}
+
+static int32_t scan_topk_common(const fathom_session *sessions, int32_t n_sessions,
+                                int32_t hkv, int32_t d, int32_t hq, int32_t group, int32_t k,
+                                void *ws, int64_t ws_bytes, void *stream, const char *who) {
+  if (int32_t rc = check_heads(hq, hkv)) return rc;
+  if (int32_t rc = check_d(d)) return rc;
+  if (int32_t rc = check_topk_common(hq, group, k, who)) return rc;
+  ScanSession ss[FATHOM_MAX_SESSIONS];
+  int32_t *idx[FATHOM_MAX_SESSIONS];
+  float *vals[FATHOM_MAX_SESSIONS];
+  int64_t ns[FATHOM_MAX_SESSIONS];
+  for (int32_t i = 0; i < n_sessions; ++i) {
+    if (int32_t rc = check_scan_topk_session(sessions[i], who)) return rc;
+    fathom_session c = sessions[i];
+    c.logits = nullptr;
+    c.ld_logits = 0;
+    ss[i] = to_scan(c);
+    ss[i].sample = nullptr;
+    ss[i].thr = nullptr;
+    ss[i].cand = nullptr;
+    ss[i].seg_cnt = nullptr;
+    ss[i].redo = nullptr;
+    idx[i] = sessions[i].idx;
+    vals[i] = sessions[i].vals;
+    ns[i] = sessions[i].n;
+  }
+  const int64_t need = scan_topk_ws_bytes(ns, n_sessions, hkv, hq, group);
+  REQUIRE(ws && ws_bytes >= need, FATHOM_ERR_WORKSPACE,
+          "%s: workspace of %lld bytes needed (got %lld)", who, (long long)need,
+          (long long)ws_bytes);
+  return launch_scan_topk(ss, idx, vals, n_sessions, hkv, hq, group, k, ws, as_stream(stream));
+}
+
+int32_t fathom_scan_topk(const uint32_t *planes, const float *lo, const float *hi, int64_t n,
+                         int32_t hkv, int32_t d, const float *q, const uint8_t *plan,
+                         int32_t hq, const uint8_t *meta, float meta_scale, int32_t group,
+                         int32_t k, int32_t *idx, float *vals, void *ws, int64_t ws_bytes,
+                         void *stream) {
+  fathom_session s{};
+  s.planes = planes;
+  s.lo = lo;
+  s.hi = hi;
+  s.n = n;
+  s.q = q;
+  s.plan = plan;
+  s.meta = meta;
+  s.meta_scale = meta_scale;
+  s.idx = idx;
+  s.vals = vals;
+  return scan_topk_common(&s, 1, hkv, d, hq, group, k, ws, ws_bytes, stream,
+                          "fathom_scan_topk");
+}
+
+int32_t fathom_scan_topk_batched(const fathom_session *sessions, int32_t n_sessions,
+                                 int32_t hkv, int32_t d, int32_t hq, int32_t group, int32_t k,
+                                 void *ws, int64_t ws_bytes, void *stream) {
+  REQUIRE(sessions, FATHOM_ERR_INVALID_ARG, "fathom_scan_topk_batched: null sessions");
+  REQUIRE(n_sessions >= 1 && n_sessions <= FATHOM_MAX_SESSIONS, FATHOM_ERR_INVALID_ARG,
+          "fathom_scan_topk_batched: n_sessions must be in [1, %d]", FATHOM_MAX_SESSIONS);
+  return scan_topk_common(sessions, n_sessions, hkv, d, hq, group, k, ws, ws_bytes, stream,
+                          "fathom_scan_topk_batched");
 }
 
 int32_t fathom_read_prefixes(const uint32_t *planes, int64_t n, int32_t hkv, int32_t d,

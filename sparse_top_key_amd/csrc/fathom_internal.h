@@ -15,12 +15,45 @@ constexpr int kBlockKeys = 2048;        // keys per 64-word plane block
 constexpr int kSessPerLaunch = 16;      // sessions carried in one kernarg set
 constexpr int kCandCap = 8192;          // top-k candidates kept per row
 constexpr int kSampleTarget = 16384;    // sampled scores per row (threshold)
+constexpr int kSampleTiles = 8;         // 2048-key tiles a fused call scores first
+constexpr int kSampleKeys = kSampleTiles * kBlockKeys;
+constexpr int kCntStride = 32;          // candidate counters, one 128-byte line each
+// Candidate store of the fused call: per output row, one segment per scan
+// block of the row's kv head (at most kMaxSeg), kFusedCap words in all.
+constexpr int kMaxSeg = 1024;
+constexpr int kFusedCap = 32768;
 
 // Thread-local error text behind fathom_last_error().
 void set_error(const char *fmt, ...);
 int32_t hip_fail(hipError_t e, const char *what);
 
 inline int64_t plane_words(int64_t n) { return 64 * ((n + kBlockKeys - 1) / kBlockKeys); }
+
+// Scores as order-preserving unsigned keys (after adding +0, so -0 ranks as
+// +0), and the 64-bit candidate words (key, ~index): larger word = higher
+// score, then lower index.
+__device__ __forceinline__ uint32_t to_key(float x) {
+  const uint32_t u = __float_as_uint(__fadd_rn(x, 0.0f));
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+__device__ __forceinline__ uint64_t compose(uint32_t key, int64_t i) {
+  return ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)i);
+}
+
+// Top-k bookkeeping carved from a caller's workspace: per output row a
+// threshold key, a candidate counter (own cache line), a redo flag and
+// kCandCap candidate words; per (session, kv head) a recompute flag.
+struct TopkWs {
+  uint32_t *thr, *cnt, *flag, *redo;
+  uint64_t *cand;
+  uint32_t *seg_cnt;  // fused final only: [rows][kMaxSeg]
+  uint64_t *fcand;    // fused final only: [rows][kFusedCap]
+};
+int64_t topk_ws_bytes(int64_t out_rows, int64_t redo_slots);
+TopkWs topk_ws_carve(void *ws, int64_t out_rows, int64_t redo_slots);
 
 // ---- pack -------------------------------------------------------------------
 int64_t pack_workspace_bytes(int64_t n, int32_t hkv);
@@ -47,9 +80,30 @@ struct ScanSession {
   float meta_scale;
   float *logits;
   int64_t ld;
+  // fused scan + top-k (unused by plain scans)
+  float *sample;          // [hq][kSampleKeys] logits of the sampled tiles
+  const uint32_t *thr;    // [rows] threshold keys of the session's output rows
+  uint64_t *cand;         // [rows][kFusedCap] candidate segments
+  uint32_t *seg_cnt;      // [rows][kMaxSeg] candidates found by each block
+  const uint32_t *redo;   // [hkv]: recompute only the kv heads flagged here
 };
+// What a scan writes: every logit (into logits; only the flagged kv heads when
+// redo is set), the logits of the sampled tiles (into sample), or the
+// (score key, index) words of the keys whose score key reaches the row's
+// threshold (into cand): kScanCand with one output row per query head,
+// kScanCandGroup with one row per kv head scored by the sum of its
+// hq / hkv (<= 4) query heads.
+enum ScanMode { kScanLogits = 0, kScanSample = 1, kScanCand = 2, kScanCandGroup = 3 };
+// nseg_out (candidate mode, optional): per session, the blocks per kv head,
+// i.e. the candidate segments of each row.  one_block_per_head: a single
+// block per (session, kv head) takes all its tiles (a grid of hkv blocks per
+// session, for recomputations that are usually skipped).
 int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv,
-                    int32_t hq, hipStream_t s);
+                    int32_t hq, hipStream_t s, int32_t mode = kScanLogits,
+                    int32_t *nseg_out = nullptr, bool one_block_per_head = false);
+// Whether launch_scan can run the sample and candidate modes on these
+// sessions (planes in device memory, at most 2^25 keys each).
+bool scan_can_fuse(const ScanSession *sess, int32_t n_sess);
 int32_t launch_read_prefixes(const uint32_t *planes, int64_t n, int32_t hkv,
                              const uint8_t *plan, int32_t hq, uint8_t *out,
                              hipStream_t s);
@@ -60,10 +114,25 @@ struct TopkSession {
   int64_t n, ld;
   int32_t *idx;
   float *vals;
+  int64_t n_full;       // keys of the row the scores were sampled from (n if not sampled)
+  int32_t nseg;         // fused final: candidate segments per row (kFusedCap / nseg each)
 };
 int64_t topk_workspace_bytes(int32_t out_rows);
+// Plain: sample -> compact -> final over the scores.  Fused: threshold from
+// scores holding only the sampled logits, then (after the candidate scan) a
+// final pass that flags rows whose candidate count is out of range.  Redo:
+// exact final over full scores for the flagged rows only.
+enum TopkStage { kTopkAll = 0, kTopkThreshold = 1, kTopkFusedFinal = 2, kTopkRedoFinal = 3 };
 int32_t launch_topk(const TopkSession *sess, int32_t n_sess, int32_t rows_per_sess,
-                    int32_t group, int32_t k, void *ws, hipStream_t s);
+                    int32_t group, int32_t k, const TopkWs &w, hipStream_t s,
+                    int32_t stage = kTopkAll, int32_t rows_per_kv = 1, int32_t hkv = 1);
+
+// ---- scan + top-k -----------------------------------------------------------
+int64_t scan_topk_ws_bytes(const int64_t *n, int32_t n_sess, int32_t hkv, int32_t hq,
+                           int32_t group);
+int32_t launch_scan_topk(const ScanSession *in, int32_t *const *idx, float *const *vals,
+                         int32_t n_sess, int32_t hkv, int32_t hq, int32_t group, int32_t k,
+                         void *ws, hipStream_t s);
 
 // ---- probe ------------------------------------------------------------------
 int32_t launch_probe_read(const void *src, int64_t bytes, uint32_t *out,

@@ -51,6 +51,16 @@ struct ScanSess {
   int32_t tiles_per_block;
   int32_t blocks_per_head;
   int32_t vec_out;         // float4 logits stores are aligned
+  // tiles this launch visits (all, or the sampled ones) and real tiles
+  int32_t nvtiles, ntiles;
+  // fused scan + top-k
+  float *sample;
+  const uint32_t *thr;
+  uint32_t *cnt;
+  uint64_t *cand;
+  uint32_t *seg_cnt;
+  const uint32_t *redo;
+  int32_t seg_cap;         // candidate words per (row, block) segment
 };
 
 struct ScanArgs {
@@ -469,11 +479,12 @@ struct MfmaSetup {
   SlotScratch<GH> X;
 };
 
-template <int GH>
-__global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
+template <int GH, int MODE>
+__global__ __launch_bounds__(kMThreads, 4) void scan_mfma_kernel(ScanArgs a) {
   const BlockWork bw = block_work(a);
   KScanSess &S = *bw.S;
   const int g = bw.g, head_base = bw.head_base;
+  if (MODE == kScanLogits && S.redo && S.redo[g] == 0) return;  // kv head not flagged
   const int64_t n = S.n;
   const int64_t W = S.W;
   __shared__ __align__(16) uint32_t s_codes[kPassGroups * kGroupPitch + 4];
@@ -482,6 +493,7 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   __shared__ __align__(16) int16_t s_desc[kMaxSlots];
   __shared__ float s_scale[kMaxGH], s_C[kMaxGH];
   __shared__ int s_exp[kMaxGH];
+  __shared__ uint32_t s_segc[kMaxGH];  // candidates this block found per row
   MfmaSetup<GH> &U = *reinterpret_cast<MfmaSetup<GH> *>(s_codes);
   SlotTable<GH> &T = U.T;
   build_slot_table<GH>(T, U.X, S, g, head_base);
@@ -500,6 +512,7 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
     s_exp[tid] = e;
     s_scale[tid] = ldexpf(1.0f, e - 30);
     s_C[tid] = T.C[tid];
+    s_segc[tid] = 0;
   }
   for (int e = tid; e < npasses * kPassGroups * 8; e += kMThreads)
     s_desc[e] = e < nslots ? T.desc[e] : (int16_t)0;
@@ -551,16 +564,21 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
 
   // Work items = (tile, pass).  The plane words of item i+1 are loaded while
   // item i is transposed, multiplied and written out.
+  // Visited tile v of this block: all tiles, or (sample mode) nvtiles tiles
+  // spread evenly over the ntiles real ones.
+  const int nvtiles = S.nvtiles, ntiles_real = S.ntiles;
+  auto real_tile = [&](int v) -> int {
+    return MODE == kScanSample ? (int)((int64_t)v * ntiles_real / nvtiles) : v;
+  };
   int ntiles = 0;
-  while (ntiles < tiles_per_block &&
-         (int64_t)(bw.tile0 + ntiles * bw.tile_step) * kMTileKeys < n)
-    ++ntiles;
+  while (ntiles < tiles_per_block && bw.tile0 + ntiles * bw.tile_step < nvtiles) ++ntiles;
   const int nitems = ntiles * npasses;
   auto issue = [&](int item, uint32_t(&x)[32]) {
     const int tt = item / npasses, p = item - tt * npasses;
     const int grp = kPassGroups * p + wave;
     if (grp >= ngroups) return;  // empty group: nothing to read
-    const uint32_t tile_off = (uint32_t)(bw.tile0 + tt * bw.tile_step) * (kMTileKeys / 8);
+    const uint32_t tile_off =
+        (uint32_t)real_tile(bw.tile0 + tt * bw.tile_step) * (kMTileKeys / 8);
     const uint4 dv = *reinterpret_cast<const uint4 *>(&s_desc[grp * 8]);
     const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
@@ -576,6 +594,14 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
     }
   };
 
+  // threshold key of this lane's output row (candidate modes), read once
+  uint32_t row_thr = 0;
+  if constexpr (MODE == kScanCand) {
+    if (hh < GH) row_thr = S.thr[head_base + hh];
+  } else if constexpr (MODE == kScanCandGroup) {
+    row_thr = S.thr[g];
+  }
+
   uint32_t xn[32];
 #pragma unroll
   for (int r = 0; r < 32; ++r) xn[r] = 0;
@@ -583,7 +609,8 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   float s[16];
   for (int it = 0; it < nitems; ++it) {
     const int tt = it / npasses, p = it - tt * npasses;
-    const int64_t tile_key0 = (int64_t)(bw.tile0 + tt * bw.tile_step) * kMTileKeys;
+    const int vt = bw.tile0 + tt * bw.tile_step;
+    const int64_t tile_key0 = (int64_t)real_tile(vt) * kMTileKeys;
     const bool has_group = kPassGroups * p + wave < ngroups;
     // ---- regroup: quarter k ends with word 4*m16 + k of the 4 plane rows of
     // every slot; 32-lane halves first, then 16-lane rows.
@@ -652,9 +679,9 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
     __syncthreads();
 
     // ---- epilogue: 4 consecutive keys of head hh per beta
-    if (p == npasses - 1 && hh < GH) {
+    if (p == npasses - 1) {
       const int64_t kb = tile_key0 + 256 * wave + 4 * nn;  // + 64*beta + e
-      if (meta) {
+      if (meta && hh < GH) {
         uint32_t mb[16];
 #pragma unroll
         for (int b = 0; b < 16; ++b) {
@@ -664,19 +691,95 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
 #pragma unroll
         for (int b = 0; b < 16; ++b) s[b] = __fmaf_rn(meta_scale, (float)mb[b], s[b]);
       }
-      float *op = out_row + kb;
-      if (vec_out && tile_key0 + 256 * (wave + 1) <= n) {  // wave-uniform
+      const bool wave_full = tile_key0 + 256 * (wave + 1) <= n;  // wave-uniform
+      if constexpr (MODE == kScanLogits) {
+        if (hh < GH) {
+          float *op = out_row + kb;
+          if (vec_out && wave_full) {
 #pragma unroll
-        for (int beta = 0; beta < 4; ++beta)
-          *reinterpret_cast<float4 *>(op + 64 * beta) =
-              make_float4(s[4 * beta], s[4 * beta + 1], s[4 * beta + 2], s[4 * beta + 3]);
+            for (int beta = 0; beta < 4; ++beta)
+              *reinterpret_cast<float4 *>(op + 64 * beta) =
+                  make_float4(s[4 * beta], s[4 * beta + 1], s[4 * beta + 2], s[4 * beta + 3]);
+          } else {
+#pragma unroll
+            for (int b = 0; b < 16; ++b) {
+              const int64_t off = 64 * (b >> 2) + (b & 3);
+              if (kb + off < n) op[off] = s[b];
+            }
+          }
+        }
+      } else if constexpr (MODE == kScanSample) {
+        // sampled tile vt lands at vt * 2048 of the head's sample row; keys
+        // past n read as -inf
+        if (hh < GH) {
+          float *op = S.sample + (int64_t)(head_base + hh) * kSampleKeys +
+                      (int64_t)vt * kMTileKeys + 256 * wave + 4 * nn;
+#pragma unroll
+          for (int beta = 0; beta < 4; ++beta) {
+            float v4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              v4[e] = kb + 64 * beta + e < n ? s[4 * beta + e] : -INFINITY;
+            *reinterpret_cast<float4 *>(op + 64 * beta) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+          }
+        }
       } else {
+        // candidates: score key at or above the row's threshold
+        bool lane_rows = hh < GH;
+        int row = head_base + hh;
+        if constexpr (MODE == kScanCandGroup) {
+          // group score: the group's fp32 logits added in fp64 in head order,
+          // rounded once; lanes of head 0 hold the key's sum
 #pragma unroll
-        for (int b = 0; b < 16; ++b) {
-          const int64_t off = 64 * (b >> 2) + (b & 3);
-          if (kb + off < n) op[off] = s[b];
+          for (int b = 0; b < 16; ++b) {
+            double acc = (double)s[b];
+            const float s1 = __shfl_down(s[b], 16);
+            const float s2 = __shfl_down(s[b], 32);
+            const float s3 = __shfl_down(s[b], 48);
+            if (GH > 1) acc = __dadd_rn(acc, (double)s1);
+            if (GH > 2) acc = __dadd_rn(acc, (double)s2);
+            if (GH > 3) acc = __dadd_rn(acc, (double)s3);
+            s[b] = (float)acc;
+          }
+          lane_rows = hh == 0;
+          row = g;
+        }
+        if (lane_rows) {
+          const uint32_t T = row_thr;
+          // keys kb + 64*beta + e are valid while 64*beta + e < lim
+          const int lim = (int)min<int64_t>(n - kb, 256);
+          uint32_t mask = 0;
+#pragma unroll
+          for (int b = 0; b < 16; ++b)
+            mask |= (uint32_t)((64 * (b >> 2) + (b & 3) < lim) && to_key(s[b]) >= T) << b;
+          if (mask) {
+            // this block's segment of the row's candidate store
+            uint32_t pos = atomicAdd(&s_segc[MODE == kScanCandGroup ? 0 : hh],
+                                     (uint32_t)__popc(mask));
+            uint64_t *cl = S.cand + (int64_t)row * kFusedCap + (int64_t)bw.tile0 * S.seg_cap;
+            while (mask) {
+              const int b = __ffs(mask) - 1;
+              mask &= mask - 1;
+              if (pos < (uint32_t)S.seg_cap) {
+                float v = s[0];
+#pragma unroll
+                for (int j = 1; j < 16; ++j) v = b == j ? s[j] : v;
+                cl[pos] = compose(to_key(v), kb + 64 * (b >> 2) + (b & 3));
+              }
+              ++pos;
+            }
+          }
         }
       }
+    }
+  }
+  if constexpr (MODE == kScanCand || MODE == kScanCandGroup) {
+    // every block reports its count (above seg_cap: the segment overflowed)
+    __syncthreads();
+    const int rows = MODE == kScanCandGroup ? 1 : GH;
+    if (tid < rows) {
+      const int row = MODE == kScanCandGroup ? g : head_base + tid;
+      S.seg_cnt[(int64_t)row * kMaxSeg + bw.tile0] = s_segc[tid];
     }
   }
 }
@@ -719,65 +822,129 @@ ScanFn pick(int GH) {
   }
 }
 
-ScanFn pick_mfma(int GH) {
+template <int MODE>
+ScanFn pick_mfma_mode(int GH) {
   switch (GH) {
-    case 1: return scan_mfma_kernel<1>;
-    case 2: return scan_mfma_kernel<2>;
-    case 3: return scan_mfma_kernel<3>;
-    default: return scan_mfma_kernel<4>;
+    case 1: return scan_mfma_kernel<1, MODE>;
+    case 2: return scan_mfma_kernel<2, MODE>;
+    case 3: return scan_mfma_kernel<3, MODE>;
+    default: return scan_mfma_kernel<4, MODE>;
+  }
+}
+
+ScanFn pick_mfma(int GH, int mode) {
+  switch (mode) {
+    case kScanSample: return pick_mfma_mode<kScanSample>(GH);
+    case kScanCand: return pick_mfma_mode<kScanCand>(GH);
+    case kScanCandGroup: return pick_mfma_mode<kScanCandGroup>(GH);
+    default: return pick_mfma_mode<kScanLogits>(GH);
   }
 }
 
 // Pinned-host planes: the link is the bound, the fp32 kernel with whole-word
 // lanes keeps 256-byte wave accesses.  HBM planes: the matrix-core kernel
 // (the fp32 kernel above 2^25 keys per session).
-ScanFn kernel_for(bool host, int GH) {
-  return host ? pick<kHostVariant.kpl, kHostVariant.aux>(GH) : pick_mfma(GH);
+ScanFn kernel_for(bool host, int GH, int mode) {
+  return host ? pick<kHostVariant.kpl, kHostVariant.aux>(GH) : pick_mfma(GH, mode);
 }
 int threads_for(bool host) { return host ? kScanThreads : kMThreads; }
 
-int resident_blocks_per_cu(bool host, int GH) {
-  static int cached[2][kMaxGH + 1] = {};
-  int &c = cached[host ? 1 : 0][GH];
+int resident_blocks_per_cu(bool host, int GH, int mode) {
+  static int cached[2][kMaxGH + 1][4] = {};
+  int &c = cached[host ? 1 : 0][GH][mode];
   if (c == 0) {
     int nb = 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &nb, kernel_for(host, GH), threads_for(host), 0);
+        &nb, kernel_for(host, GH, mode), threads_for(host), 0);
     c = (e == hipSuccess && nb > 0) ? nb : 1;
   }
   return c;
 }
 
-}  // namespace
-
-int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv,
-                    int32_t hq, hipStream_t s) {
-  const int32_t group = hq / hkv;
-  int dev = 0;
-  hipGetDevice(&dev);
-  int ncu = 256;
-  hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-  // residency of each session's planes: pinned host or device memory
-  bool any_host = false;
+// Residency of the sessions' planes; false (error set) if some are neither
+// device nor pinned host memory.
+bool planes_residency(const ScanSession *sess, int32_t n_sess, bool *any_host) {
+  *any_host = false;
   for (int32_t j = 0; j < n_sess; ++j) {
     hipPointerAttribute_t attr;
     const hipError_t e = hipPointerGetAttributes(&attr, sess[j].planes);
     if (e != hipSuccess) {
-      hipGetLastError();
+      (void)hipGetLastError();
       set_error("scan: planes of session %d are neither device nor pinned host memory", j);
-      return FATHOM_ERR_INVALID_ARG;
+      return false;
     }
-    any_host |= attr.type == hipMemoryTypeHost;
+    *any_host |= attr.type == hipMemoryTypeHost;
   }
-  // The matrix-core kernel addresses a kv head's planes with 32-bit buffer
-  // offsets: sessions up to 2^25 keys (2 GiB of planes per kv head).
+  return true;
+}
+
+// The matrix-core kernel addresses a kv head's planes with 32-bit buffer
+// offsets: sessions up to 2^25 keys (2 GiB of planes per kv head).
+constexpr int64_t kMfmaMaxKeys = (int64_t)1 << 25;
+
+}  // namespace
+
+bool scan_can_fuse(const ScanSession *sess, int32_t n_sess) {
+  bool any_host = false;
+  if (!planes_residency(sess, n_sess, &any_host)) return false;
+  for (int32_t j = 0; j < n_sess; ++j)
+    if (sess[j].n > kMfmaMaxKeys) return false;
+  return !any_host;
+}
+
+int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_t hq,
+                    hipStream_t s, int32_t mode, int32_t *nseg_out, bool one_block_per_head) {
+  const int32_t group = hq / hkv;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  int ncu = 256;
+  (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  bool any_host = false;
+  if (!planes_residency(sess, n_sess, &any_host)) return FATHOM_ERR_INVALID_ARG;
   int64_t max_n = 0;
   for (int32_t j = 0; j < n_sess; ++j) max_n = std::max(max_n, sess[j].n);
-  const bool fp32_path = any_host || max_n > ((int64_t)1 << 25);
+  const bool fp32_path = any_host || max_n > kMfmaMaxKeys;
+  if (fp32_path && mode != kScanLogits) {
+    set_error("scan: sampled and candidate scans need device planes of at most 2^25 keys");
+    return FATHOM_ERR_UNSUPPORTED;
+  }
+  if (mode == kScanCandGroup && group > kMaxGH) {
+    set_error("scan: group candidate scans need hq/hkv <= %d", kMaxGH);
+    return FATHOM_ERR_UNSUPPORTED;
+  }
+  for (int32_t j = 0; j < n_sess; ++j)
+    if (fp32_path && sess[j].redo) {
+      set_error("scan: recompute flags need the matrix-core scan");
+      return FATHOM_ERR_UNSUPPORTED;
+    }
+  const bool cand = mode == kScanCand || mode == kScanCandGroup;
   const int64_t tile_keys =
       fp32_path ? (int64_t)kHostVariant.kpl * 64 * (kScanThreads / 64) : (int64_t)kMTileKeys;
+  // tiles a session's blocks visit: all, or the sampled ones
+  auto visited = [&](int64_t n) {
+    const int64_t t = (n + tile_keys - 1) / tile_keys;
+    return mode == kScanSample ? std::min<int64_t>(t, kSampleTiles) : t;
+  };
+  const int kernel_mode = fp32_path ? 0 : mode;
   for (int32_t s0 = 0; s0 < n_sess; s0 += kSessPerLaunch) {
     const int32_t cnt = std::min(kSessPerLaunch, n_sess - s0);
+    // One tiling per session for all head chunks: one round of resident
+    // blocks, every block taking the same number of tiles of one (session,
+    // kv head) to amortise its plan set-up.
+    int64_t total_tiles = 0;
+    for (int j = 0; j < cnt; ++j) total_tiles += visited(sess[s0 + j].n) * hkv;
+    const int64_t target_blocks =
+        (int64_t)ncu * resident_blocks_per_cu(fp32_path, std::min(kMaxGH, group), kernel_mode);
+    int64_t tpb_s[kSessPerLaunch];
+    for (int j = 0; j < cnt; ++j) {
+      const int64_t tiles = visited(sess[s0 + j].n);
+      int64_t tpb = 1;
+      if (one_block_per_head) tpb = std::max<int64_t>(1, tiles);
+      if (total_tiles > target_blocks) tpb = std::max(tpb, (total_tiles + target_blocks - 1) / target_blocks);
+      if (cand) tpb = std::max(tpb, (tiles + kMaxSeg - 1) / kMaxSeg);  // segments per row
+      tpb_s[j] = std::max<int64_t>(1, std::min<int64_t>(tpb, tiles));
+      if (nseg_out) nseg_out[s0 + j] = (int32_t)((tiles + tpb_s[j] - 1) / tpb_s[j]);
+    }
     for (int32_t head0 = 0; head0 < group; head0 += kMaxGH) {
       const int GH = std::min(kMaxGH, group - head0);
       ScanArgs a{};
@@ -785,12 +952,6 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv,
       a.hkv = hkv;
       a.group = group;
       a.head0 = head0;
-      int64_t total_tiles = 0;
-      for (int j = 0; j < cnt; ++j)
-        total_tiles += (sess[s0 + j].n + tile_keys - 1) / tile_keys * hkv;
-      // one round of resident blocks: every block takes the same number of
-      // tiles of one (session, kv head) and amortises its plan set-up
-      const int64_t target_blocks = (int64_t)ncu * resident_blocks_per_cu(fp32_path, GH);
       int32_t blocks = 0;
       for (int j = 0; j < cnt; ++j) {
         const ScanSession &in = sess[s0 + j];
@@ -807,19 +968,23 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv,
         o.ld = in.ld;
         o.meta_scale = in.meta_scale;
         o.vec_out = ((reinterpret_cast<uintptr_t>(in.logits) & 15) == 0) && (in.ld % 4 == 0);
-        const int64_t tiles = (in.n + tile_keys - 1) / tile_keys;
-        int64_t tpb = 1;
-        if (total_tiles > target_blocks)
-          tpb = (total_tiles + target_blocks - 1) / target_blocks;
-        tpb = std::max<int64_t>(1, std::min<int64_t>(tpb, tiles));
-        o.tiles_per_block = (int32_t)tpb;
-        o.blocks_per_head = (int32_t)((tiles + tpb - 1) / tpb);
+        o.sample = in.sample;
+        o.thr = in.thr;
+        o.cand = in.cand;
+        o.seg_cnt = in.seg_cnt;
+        o.redo = in.redo;
+        const int64_t tiles = visited(in.n);
+        o.nvtiles = (int32_t)tiles;
+        o.ntiles = (int32_t)((in.n + tile_keys - 1) / tile_keys);
+        o.tiles_per_block = (int32_t)tpb_s[j];
+        o.blocks_per_head = (int32_t)((tiles + tpb_s[j] - 1) / tpb_s[j]);
+        o.seg_cap = o.blocks_per_head > 0 ? kFusedCap / o.blocks_per_head : 0;
         o.block_begin = blocks;
         blocks += o.blocks_per_head * hkv;
       }
       if (blocks == 0) continue;
-      hipLaunchKernelGGL(kernel_for(fp32_path, GH), dim3(blocks), dim3(threads_for(fp32_path)), 0,
-                         s, a);
+      hipLaunchKernelGGL(kernel_for(fp32_path, GH, mode), dim3(blocks),
+                         dim3(threads_for(fp32_path)), 0, s, a);
       int32_t rc = hip_fail(hipGetLastError(), "scan launch");
       if (rc) return rc;
     }

@@ -38,23 +38,24 @@ struct TopkSess {
   int64_t n, ld;
   int32_t *idx;
   float *vals;
+  int64_t n_full;
+  int32_t nseg;
 };
 
 struct TopkArgs {
   TopkSess s[kSessPerLaunch];
   int32_t rows_per_sess, group, k;
+  int32_t stage;        // TopkStage
+  int32_t rows_per_kv;  // output rows per kv head (redo flags)
+  int32_t hkv;
   uint32_t *thr;
-  uint32_t *cnt;
+  uint32_t *cnt;        // stride kCntStride
+  uint32_t *flag;
+  uint32_t *redo;       // [session][hkv] of this launch
   uint64_t *cand;
+  uint32_t *seg_cnt;    // fused final: [rows][kMaxSeg]
+  uint64_t *fcand;      // fused final: [rows][kFusedCap]
 };
-
-__device__ __forceinline__ uint32_t to_key(float x) {
-  const uint32_t u = __float_as_uint(__fadd_rn(x, 0.0f));
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float from_key(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
 
 __device__ __forceinline__ float group_score(const float *__restrict__ row, int64_t ld,
                                              int group, int64_t i) {
@@ -217,10 +218,6 @@ __device__ uint64_t *sort_winners_desc(uint64_t *w, uint64_t *tmp, int m) {
   return src;
 }
 
-__device__ __forceinline__ uint64_t compose(uint32_t key, int64_t i) {
-  return ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)i);
-}
-
 __device__ void write_out(const TopkSess &S, int r, int k, const uint64_t *s, int m) {
   int32_t *idx = S.idx + (int64_t)r * k;
   float *vals = S.vals + (int64_t)r * k;
@@ -237,53 +234,114 @@ __device__ void write_out(const TopkSess &S, int r, int k, const uint64_t *s, in
 }
 
 // ---- sample -> threshold -----------------------------------------------------
+// Max, min and sum over the block (16 waves).
+__device__ void block_minmax_count(uint32_t &mx, uint32_t &mn, int &cnt, uint32_t *red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
+    cnt += __shfl_xor(cnt, off);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    red[wave] = mx;
+    red[16 + wave] = mn;
+    red[32 + wave] = (uint32_t)cnt;
+  }
+  __syncthreads();
+  mx = 0;
+  mn = 0xFFFFFFFFu;
+  cnt = 0;
+#pragma unroll
+  for (int w = 0; w < kBig / 64; ++w) {
+    mx = max(mx, red[w]);
+    mn = min(mn, red[16 + w]);
+    cnt += (int)red[32 + w];
+  }
+  __syncthreads();
+}
+
+// One block per output row: from a sample of the row (runs of 64 scores
+// spread evenly, about 16K in all; or all of a row of sampled logits), a
+// threshold key T expected to leave about 2.5k of the row's n_full scores at
+// or above it: the sample's keys are histogrammed on the 11 bits below their
+// common prefix and T is the lower edge of the bin holding the rs-th
+// largest.  Rows of at most 8192 scores take T = 0 (all).
 __global__ __launch_bounds__(kBig) void topk_sample_kernel(TopkArgs a) {
-  __shared__ uint32_t keys[kSampleTarget + kRun];
+  constexpr int kPer = (kSampleTarget + kRun + kBig - 1) / kBig;
   __shared__ int hist[kHistBins];
   __shared__ int wave_tot[16];
   __shared__ int s_res[2];
+  __shared__ uint32_t red[48];
   const int o = blockIdx.x;
   const RowRef R = row_ref(a, o);
-  const int64_t n = R.s->n, ld = R.s->ld;
-  if (threadIdx.x == 0) a.cnt[o] = 0;
-  if (n <= kCandCap) {
+  const int64_t n = R.s->n, ld = R.s->ld, n_full = R.s->n_full;
+  if (threadIdx.x == 0) {
+    a.cnt[(int64_t)o * kCntStride] = 0;
+    a.flag[o] = 0;
+    a.redo[(o / a.rows_per_sess) * a.hkv + (o % a.rows_per_sess) / a.rows_per_kv] = 0;
+  }
+  if (n_full <= kCandCap) {
     if (threadIdx.x == 0) a.thr[o] = 0;
     return;
   }
-  // runs of kRun scores every `stride` scores, about kSampleTarget in all
   int64_t stride = (n * kRun + kSampleTarget - 1) / kSampleTarget;
   stride = (stride + kRun - 1) / kRun * kRun;
   if (stride < kRun) stride = kRun;
   const int runs = (int)((n + stride - 1) / stride);
   const int m = runs * kRun;
-  for (int e = threadIdx.x; e < m; e += kBig) {
+  // every load of the thread in flight at once
+  uint32_t v[kPer];
+  uint32_t okm = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = threadIdx.x + j * kBig;
     const int64_t pos = (int64_t)(e / kRun) * stride + (e % kRun);
-    keys[e] = pos < n ? to_key(group_score(R.row, ld, a.group, pos)) : 0u;
+    const bool ok = e < m && pos < n;
+    v[j] = ok ? to_key(group_score(R.row, ld, a.group, pos)) : 0u;
+    okm |= (uint32_t)ok << j;
   }
-  // rank of the threshold inside the sample: expect ~2.5k scores >= T
-  int64_t rs = ((int64_t)5 * a.k * m + 2 * n - 1) / (2 * n);
-  if (rs < 1) rs = 1;
-  if (rs > m) rs = m;
-  // Two 11-bit radix passes: T = the top 22 bits of the rs-th largest sampled
-  // key, low bits 0 (it only has to leave about 2.5k scores at or above it).
+  uint32_t mx = 0, mn = 0xFFFFFFFFu;
+  int cnt = __popc(okm);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if ((okm >> j) & 1) {
+      mx = max(mx, v[j]);
+      mn = min(mn, v[j]);
+    }
+  block_minmax_count(mx, mn, cnt, red);
+  if (cnt == 0) {
+    if (threadIdx.x == 0) a.thr[o] = 0;
+    return;
+  }
+  // rank of the threshold inside the sample: ~2.5k of n_full at or above T
+  int64_t rs = ((int64_t)5 * a.k * cnt + 2 * n_full - 1) / (2 * n_full);
+  rs = rs < 1 ? 1 : (rs > cnt ? cnt : rs);
+  // Two 11-bit digits below the bits all sampled keys share: T = the rs-th
+  // largest key with its bits below the second digit cleared.
+  const uint32_t diff = mx ^ mn;
+  const int hb = diff ? 31 - __clz(diff) : 0;  // highest bit in which keys differ
+  int sh = hb > 10 ? hb - 10 : 0;
+  uint32_t prefix = sh + 11 >= 32 ? 0u : (mx >> (sh + 11)) << (sh + 11);
+  uint32_t pmask = sh + 11 >= 32 ? 0u : ~((1u << (sh + 11)) - 1u);
   int rem = (int)rs;
-  uint32_t prefix = 0, pmask = 0;
-  const int shifts[2] = {21, 10};
-  const int bits[2] = {11, 11};
   for (int pass = 0; pass < 2; ++pass) {
-    const int sh = shifts[pass], nb = 1 << bits[pass];
     for (int b = threadIdx.x; b < kHistBins; b += kBig) hist[b] = 0;
     __syncthreads();
-    for (int e = threadIdx.x; e < m; e += kBig) {
-      const uint32_t v = keys[e];
-      if ((v & pmask) == prefix) atomicAdd(&hist[(v >> sh) & (nb - 1)], 1);
-    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (((okm >> j) & 1) && (v[j] & pmask) == prefix)
+        atomicAdd(&hist[(v[j] >> sh) & (kHistBins - 1)], 1);
     __syncthreads();
     int above = 0;
-    const int d = find_digit(hist, nb, rem, &above, wave_tot, s_res);
+    const int d = find_digit(hist, kHistBins, rem, &above, wave_tot, s_res);
     rem -= above;
     prefix |= (uint32_t)d << sh;
-    pmask |= (uint32_t)(nb - 1) << sh;
+    pmask |= (uint32_t)(kHistBins - 1) << sh;
+    if (sh == 0) break;
+    // next digit: the 11 bits below (when fewer remain, it also spans bits
+    // the matching keys share, which keeps its order)
+    sh = sh > 11 ? sh - 11 : 0;
   }
   if (threadIdx.x == 0) a.thr[o] = prefix;
 }
@@ -302,7 +360,7 @@ __global__ __launch_bounds__(kCompactThreads) void topk_compact_kernel(TopkArgs 
   const int64_t base = (int64_t)blockIdx.x * kCompactChunk;
   if (base >= n) return;
   const uint32_t T = a.thr[o];
-  uint32_t *cnt = a.cnt + o;
+  uint32_t *cnt = a.cnt + (int64_t)o * kCntStride;
   uint64_t *cand = a.cand + (int64_t)o * kCandCap;
   const int lane = threadIdx.x & 63;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -504,6 +562,7 @@ __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
   __shared__ int wave_tot[16];
   __shared__ int s_res[2];
   __shared__ int s_count;
+  __shared__ int s_off[kMaxSeg + 1];
   const int o = blockIdx.x;
   const RowRef R = row_ref(a, o);
   const TopkSess &S = *R.s;
@@ -511,13 +570,60 @@ __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
   const int64_t n = S.n, ld = S.ld;
   const int k = a.k;
   const int kk = (int)(n < k ? n : k);
-  const uint32_t cnt = a.cnt[o];
-  const bool fast = (n <= kCandCap) || (cnt >= (uint32_t)k && cnt <= (uint32_t)kCandCap);
+  uint32_t cnt = 0;
+  bool fused_over = false;
+  if (a.stage == kTopkFusedFinal) {
+    // the row's candidates sit in one segment per scan block
+    const int nseg = S.nseg, seg_cap = kFusedCap / (nseg > 0 ? nseg : 1);
+    const int c = threadIdx.x < nseg ? (int)a.seg_cnt[(int64_t)o * kMaxSeg + threadIdx.x] : 0;
+    const int incl = block_inclusive_scan(c, wave_tot);
+    s_off[threadIdx.x] = incl - c;
+    if (threadIdx.x == kBig - 1) s_off[kMaxSeg] = incl;
+    if (threadIdx.x == 0) s_res[1] = 0;
+    __syncthreads();
+    if (c > seg_cap) s_res[1] = 1;
+    __syncthreads();
+    cnt = (uint32_t)s_off[kMaxSeg];
+    fused_over = s_res[1] != 0;
+    __syncthreads();
+  } else {
+    cnt = a.cnt[(int64_t)o * kCntStride];
+  }
+  bool fast = !fused_over &&
+              ((n <= kCandCap) || (cnt >= (uint32_t)k && cnt <= (uint32_t)kCandCap));
+  if (a.stage == kTopkRedoFinal) {
+    if (!a.flag[o]) return;  // this row was answered from its candidates
+    fast = false;
+  } else if (a.stage == kTopkFusedFinal && !fast) {
+    // too few or too many candidates: the row is recomputed from full logits
+    if (threadIdx.x == 0) {
+      a.flag[o] = 1;
+      a.redo[(o / a.rows_per_sess) * a.hkv + r / a.rows_per_kv] = 1;
+    }
+    return;
+  }
   if (threadIdx.x == 0) s_count = 0;
   if (fast) {
     const int m = (int)cnt;
-    const uint64_t *cand = a.cand + (int64_t)o * kCandCap;
-    for (int j = threadIdx.x; j < m; j += kBig) s[j] = cand[j];
+    if (a.stage == kTopkFusedFinal) {
+      const int nseg = S.nseg, seg_cap = kFusedCap / (nseg > 0 ? nseg : 1);
+      const uint64_t *fc = a.fcand + (int64_t)o * kFusedCap;
+      for (int j = threadIdx.x; j < m; j += kBig) {
+        // segment holding candidate j: the last b with s_off[b] <= j
+        int lo = 0, hi = nseg - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_off[mid] <= j)
+            lo = mid;
+          else
+            hi = mid - 1;
+        }
+        s[j] = fc[(int64_t)lo * seg_cap + (j - s_off[lo])];
+      }
+    } else {
+      const uint64_t *cand = a.cand + (int64_t)o * kCandCap;
+      for (int j = threadIdx.x; j < m; j += kBig) s[j] = cand[j];
+    }
     __syncthreads();
     if (kk > 0 &&
         bucket_rank_out(s, m, kk, win, hist, above, wave_tot, s_res, red, S, r, k))
@@ -588,13 +694,40 @@ __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
 
 }  // namespace
 
-int64_t topk_workspace_bytes(int32_t out_rows) {
-  return (int64_t)out_rows * (2 * sizeof(uint32_t)) + 256 +
-         (int64_t)out_rows * kCandCap * sizeof(uint64_t);
+// Workspace: thr[rows] | flag[rows] | redo[redo_slots] | pad to 256 |
+// cnt[rows][kCntStride] | cand[rows][kCandCap].
+static int64_t small_bytes(int64_t out_rows, int64_t redo_slots) {
+  return ((2 * out_rows + redo_slots) * (int64_t)sizeof(uint32_t) + 255) / 256 * 256;
 }
 
+int64_t topk_ws_bytes(int64_t out_rows, int64_t redo_slots) {
+  return small_bytes(out_rows, redo_slots) + out_rows * kCntStride * (int64_t)sizeof(uint32_t) +
+         out_rows * kCandCap * (int64_t)sizeof(uint64_t);
+}
+
+TopkWs topk_ws_carve(void *ws, int64_t out_rows, int64_t redo_slots) {
+  char *w = static_cast<char *>(ws);
+  TopkWs t;
+  t.thr = reinterpret_cast<uint32_t *>(w);
+  t.flag = t.thr + out_rows;
+  t.redo = t.flag + out_rows;
+  const int64_t small = small_bytes(out_rows, redo_slots);
+  t.cnt = reinterpret_cast<uint32_t *>(w + small);
+  t.cand = reinterpret_cast<uint64_t *>(w + small + out_rows * kCntStride * sizeof(uint32_t));
+  t.seg_cnt = nullptr;
+  t.fcand = nullptr;
+  return t;
+}
+
+int64_t topk_workspace_bytes(int32_t out_rows) { return topk_ws_bytes(out_rows, out_rows); }
+
 int32_t launch_topk(const TopkSession *sess, int32_t n_sess, int32_t rows_per_sess,
-                    int32_t group, int32_t k, void *ws, hipStream_t s) {
+                    int32_t group, int32_t k, const TopkWs &w, hipStream_t s, int32_t stage,
+                    int32_t rows_per_kv, int32_t hkv) {
+  if (stage == kTopkAll) {  // redo flags unused: one slot per row
+    hkv = rows_per_sess;
+    rows_per_kv = 1;
+  }
   for (int32_t s0 = 0; s0 < n_sess; s0 += kSessPerLaunch) {
     const int32_t cnt = std::min(kSessPerLaunch, n_sess - s0);
     const int32_t out_rows = cnt * rows_per_sess;
@@ -602,29 +735,39 @@ int32_t launch_topk(const TopkSession *sess, int32_t n_sess, int32_t rows_per_se
     a.rows_per_sess = rows_per_sess;
     a.group = group;
     a.k = k;
-    // workspace: thr[out_rows] | cnt[out_rows] | pad | cand[out_rows][cap]
-    char *w = static_cast<char *>(ws);
+    a.stage = stage;
+    a.rows_per_kv = rows_per_kv;
+    a.hkv = hkv;
     const int64_t rows_before = (int64_t)s0 * rows_per_sess;
-    const int64_t total_rows = (int64_t)n_sess * rows_per_sess;
-    a.thr = reinterpret_cast<uint32_t *>(w) + rows_before;
-    a.cnt = reinterpret_cast<uint32_t *>(w) + total_rows + rows_before;
-    const int64_t head = (total_rows * 2 * sizeof(uint32_t) + 255) / 256 * 256;
-    a.cand = reinterpret_cast<uint64_t *>(w + head) + rows_before * kCandCap;
+    a.thr = w.thr + rows_before;
+    a.flag = w.flag + rows_before;
+    a.redo = w.redo + (int64_t)s0 * hkv;
+    a.cnt = w.cnt + rows_before * kCntStride;
+    a.cand = w.cand + rows_before * kCandCap;
+    a.seg_cnt = w.seg_cnt ? w.seg_cnt + rows_before * kMaxSeg : nullptr;
+    a.fcand = w.fcand ? w.fcand + rows_before * kFusedCap : nullptr;
     int64_t max_n = 0;
     for (int j = 0; j < cnt; ++j) {
-      a.s[j].scores = sess[s0 + j].scores;
-      a.s[j].n = sess[s0 + j].n;
-      a.s[j].ld = sess[s0 + j].ld;
-      a.s[j].idx = sess[s0 + j].idx;
-      a.s[j].vals = sess[s0 + j].vals;
-      max_n = std::max(max_n, sess[s0 + j].n);
+      const TopkSession &in = sess[s0 + j];
+      a.s[j].scores = in.scores;
+      a.s[j].n = in.n;
+      a.s[j].ld = in.ld;
+      a.s[j].idx = in.idx;
+      a.s[j].vals = in.vals;
+      a.s[j].n_full = in.n_full;
+      a.s[j].nseg = in.nseg;
+      max_n = std::max(max_n, in.n);
     }
-    hipLaunchKernelGGL(topk_sample_kernel, dim3(out_rows), dim3(kBig), 0, s, a);
-    const int64_t chunks = (max_n + kCompactChunk - 1) / kCompactChunk;
-    if (chunks > 0)
-      hipLaunchKernelGGL(topk_compact_kernel, dim3((unsigned)chunks, out_rows),
-                         dim3(kCompactThreads), 0, s, a);
-    hipLaunchKernelGGL(topk_final_kernel, dim3(out_rows), dim3(kBig), 0, s, a);
+    if (stage == kTopkAll || stage == kTopkThreshold)
+      hipLaunchKernelGGL(topk_sample_kernel, dim3(out_rows), dim3(kBig), 0, s, a);
+    if (stage == kTopkAll) {
+      const int64_t chunks = (max_n + kCompactChunk - 1) / kCompactChunk;
+      if (chunks > 0)
+        hipLaunchKernelGGL(topk_compact_kernel, dim3((unsigned)chunks, out_rows),
+                           dim3(kCompactThreads), 0, s, a);
+    }
+    if (stage != kTopkThreshold)
+      hipLaunchKernelGGL(topk_final_kernel, dim3(out_rows), dim3(kBig), 0, s, a);
     int32_t rc = hip_fail(hipGetLastError(), "topk launch");
     if (rc) return rc;
   }

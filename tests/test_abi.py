@@ -144,6 +144,35 @@ def test_batched_validation(L):
     assert L.fathom_topk_batched(arr, 2, 32, 4, 0, DUMMY, 1 << 30, None) == 1
 
 
+def test_scan_topk_validation(L):
+    import sparse_top_key_amd as fathom
+    ns = (ctypes.c_int64 * 1)(1000)
+    ws = L.fathom_scan_topk_workspace_bytes(ns, 1, 8, 32, 1, 64)
+    # candidate lists of 32 rows + full logits of the 32 rows (fallback)
+    assert ws >= 32 * 8192 * 8 + 32 * 1000 * 4
+    assert L.fathom_scan_topk_workspace_bytes(ns, 1, 8, 30, 1, 64) == 0   # hq % hkv
+    assert L.fathom_scan_topk_workspace_bytes(ns, 1, 8, 32, 3, 64) == 0   # hq % group
+    assert L.fathom_scan_topk_workspace_bytes(ns, 1, 8, 32, 1, 2049) == 0
+    assert L.fathom_scan_topk_workspace_bytes(None, 1, 8, 32, 1, 64) == 0
+    assert L.fathom_scan_topk_workspace_bytes(ns, 0, 8, 32, 1, 64) == 0
+    neg = (ctypes.c_int64 * 1)(-5)
+    assert L.fathom_scan_topk_workspace_bytes(neg, 1, 8, 32, 1, 64) == 0
+    base = [DUMMY, DUMMY, DUMMY, 1000, 8, 128, DUMMY, DUMMY, 32, None, 0.0, 1, 64,
+            DUMMY, DUMMY, DUMMY, ws, None]
+    for pos, val, code in ((12, 0, 1), (12, 2049, 1), (11, 3, 1), (16, ws - 1, 4),
+                           (0, None, 1), (13, None, 1), (14, None, 1), (5, 64, 2),
+                           (8, 30, 1), (3, -1, 1), (15, None, 4)):
+        a = list(base)
+        a[pos] = val
+        assert L.fathom_scan_topk(*a) == code, (pos, val)
+    arr = (fathom._Session * 2)()
+    assert L.fathom_scan_topk_batched(arr, 0, 8, 128, 32, 1, 64, DUMMY, 1 << 40, None) == 1
+    assert L.fathom_scan_topk_batched(arr, 65, 8, 128, 32, 1, 64, DUMMY, 1 << 40, None) == 1
+    assert L.fathom_scan_topk_batched(None, 1, 8, 128, 32, 1, 64, DUMMY, 1 << 40, None) == 1
+    arr[0].n = 10                                 # n > 0 with null pointers
+    assert L.fathom_scan_topk_batched(arr, 2, 8, 128, 32, 1, 64, DUMMY, 1 << 40, None) == 1
+
+
 def test_probe_validation(L):
     assert L.fathom_probe_read(None, 16, DUMMY, 0, None) == 1
     assert L.fathom_probe_read(DUMMY, 17, DUMMY, 0, None) == 1

@@ -1,0 +1,209 @@
+"""GPU parity of fathom_scan_topk: idx and vals bit-identical to fathom_scan
+followed by fathom_topk on the same inputs (per query head and per GQA
+group; sampled-threshold path, all-candidates path, recompute path for rows
+whose candidate count is out of range, and the workspace-logits path for
+pinned host planes and other groups), and spot-checked against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from parity import assert_topk_tie_tolerant, logit_scale
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def F():
+    import sparse_top_key_amd as fathom
+    fathom.lib()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return fathom
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def layer(F, seed, n, hkv, hq, budget=92, fixed_r=None, dtype=torch.float16):
+    keys = synth.keys(seed, 0, n, hkv, 128, dtype, 4, device=dev())
+    q = synth.queries(seed, 0, hq, 128, device=dev())
+    p = F.pack(keys)
+    plan = F.plan_fixed(q, fixed_r) if fixed_r is not None else F.plan(q, p.sigma2, budget)
+    torch.cuda.synchronize()
+    return keys, q, p, plan
+
+
+def both(F, p, n, q, plan, k, group, meta=None, meta_scale=0.0, planes=None):
+    planes = p.planes if planes is None else planes
+    logits = F.scan(planes, p.lo, p.hi, n, q, plan, meta, meta_scale)
+    ref = F.topk(logits, k, group)
+    got = F.scan_topk(planes, p.lo, p.hi, n, q, plan, k, group, meta, meta_scale)
+    torch.cuda.synchronize()
+    return got, ref, logits
+
+
+def redo_flags(F, n, hkv, hq, group, k, run):
+    """Run `run(ws)` with a workspace of our own and return the per-row redo
+    flags the call left there (white-box: the workspace starts with the rows'
+    threshold words, then their redo flags)."""
+    rows = hq // group
+    ws = torch.zeros(F.scan_topk_workspace_bytes([n], hkv, hq, group, k), dtype=torch.uint8,
+                     device=dev())
+    run(ws)
+    torch.cuda.synchronize()
+    return ws[4 * rows:8 * rows].view(torch.int32).cpu()
+
+
+def assert_same(got, ref):
+    assert torch.equal(got[0], ref[0]), "idx differ"
+    assert torch.equal(got[1], ref[1]), "vals differ"
+
+
+@pytest.mark.parametrize("n,hkv,hq,k,group", [
+    (200000, 8, 32, 1024, 1),     # sampled threshold, per query head
+    (200000, 8, 32, 1024, 4),     # per GQA group (group sum in the scan)
+    (123457, 8, 32, 2048, 1),     # ragged tail, largest k
+    (100000, 4, 8, 1, 2),         # k = 1, groups of 2
+    (5000, 8, 32, 64, 1),         # n <= 8192: every key a candidate
+    (8192, 2, 8, 512, 4),
+    (8193, 2, 8, 512, 1),
+    (40000, 2, 16, 256, 1),       # 8 query heads per kv head (two head chunks)
+    (40000, 2, 16, 256, 8),       # group 8: logits in the workspace
+    (40000, 2, 8, 300, 2),        # group 2 of 4: logits in the workspace
+    (30000, 8, 8, 100, 1),        # one query head per kv head
+])
+def test_scan_topk_equals_scan_then_topk(F, n, hkv, hq, k, group):
+    print(f"scan_topk n={n} hkv={hkv} hq={hq} k={k} group={group}", flush=True)
+    _, q, p, plan = layer(F, 400 + n % 97, n, hkv, hq)
+    got, ref, _ = both(F, p, n, q, plan, k, group)
+    assert_same(got, ref)
+    if group == 1 or (group == hq // hkv and group <= 4):
+        # answered from candidate lists, nothing recomputed
+        flags = redo_flags(F, n, hkv, hq, group, k, lambda ws: F.scan_topk(
+            p.planes, p.lo, p.hi, n, q, plan, k, group, ws=ws))
+        assert torch.all(flags == 0)
+
+
+@pytest.mark.parametrize("budget", [68, 136, 7])
+def test_scan_topk_budgets(F, budget):
+    print(f"scan_topk budget={budget}", flush=True)
+    _, q, p, plan = layer(F, 500 + budget, 70000, 8, 32, budget)
+    got, ref, _ = both(F, p, 70000, q, plan, 512, 1)
+    assert_same(got, ref)
+
+
+def test_scan_topk_fixed_plan_with_side_stream(F):
+    n = 90000
+    print(f"scan_topk fixed-136 n={n}", flush=True)
+    _, q, p, plan = layer(F, 510, n, 8, 32, fixed_r=32)
+    meta = synth.side_stream(510, 0, 8, n, device=dev())
+    for group in (1, 4):
+        got, ref, _ = both(F, p, n, q, plan, 1024, group, meta, 0.01)
+        assert_same(got, ref)
+
+
+def test_scan_topk_all_ties_recomputes(F):
+    """B = 0: every logit of a row equals C_h, so every key reaches the
+    threshold, the candidate lists overflow and the rows are recomputed from
+    full logits; the top k are then the k lowest indices."""
+    n = 60000
+    print("scan_topk all ties", flush=True)
+    _, q, p, plan = layer(F, 520, n, 8, 32, budget=0)
+    for group in (1, 4):
+        got, ref, _ = both(F, p, n, q, plan, 256, group)
+        assert_same(got, ref)
+        assert torch.equal(got[0].cpu(), torch.arange(256, dtype=torch.int32).expand_as(got[0]))
+        flags = redo_flags(F, n, 8, 32, group, 256, lambda ws: F.scan_topk(
+            p.planes, p.lo, p.hi, n, q, plan, 256, group, ws=ws))
+        assert torch.all(flags == 1)
+
+
+def test_scan_topk_sample_misled_recomputes(F):
+    """Keys of the sampled tiles made much larger in one channel: the sampled
+    threshold is far from the rest of the row, so candidate counts fall
+    outside [k, 8192] and rows are recomputed; results still match."""
+    n = 64 * 2048
+    hkv, hq = 2, 8
+    keys = synth.keys(530, 0, n, hkv, 128, torch.float32, 0, device=dev())
+    q = synth.queries(530, 0, hq, 128, device=dev())
+    ntiles = n // 2048
+    for j in range(8):
+        t = j * ntiles // 8
+        keys[t * 2048:(t + 1) * 2048, :, 0] += 60.0
+    p = F.pack(keys)
+    # kv head 0's query heads weigh the planted channel up, kv head 1's down
+    # (thresholds far above / below the rest of the row; group sums too)
+    q[:, 0] = torch.where(torch.arange(hq, device=dev()) < hq // 2, 5.0, -5.0)
+    plan = F.plan(q, p.sigma2, 92)
+    torch.cuda.synchronize()
+    print("scan_topk misled sample", flush=True)
+    for group in (1, 4):
+        got, ref, _ = both(F, p, n, q, plan, 1024, group)
+        assert_same(got, ref)
+        flags = redo_flags(F, n, hkv, hq, group, 1024, lambda ws: F.scan_topk(
+            p.planes, p.lo, p.hi, n, q, plan, 1024, group, ws=ws))
+        assert torch.all(flags == 1)
+
+
+def test_scan_topk_pinned_host_planes(F):
+    n = 50000
+    print("scan_topk pinned host planes", flush=True)
+    _, q, p, plan = layer(F, 540, n, 8, 32)
+    host = torch.empty(p.planes.shape, dtype=p.planes.dtype, pin_memory=True)
+    host.copy_(p.planes)
+    torch.cuda.synchronize()
+    got, ref, _ = both(F, p, n, q, plan, 512, 4, planes=host)
+    assert_same(got, ref)
+
+
+def test_scan_topk_batched_sessions(F):
+    lengths = [70000, 5000, 0, 123457, 1, 16385]
+    budgets = [92, 68, 92, 136, 92, 91]
+    hkv, hq, k = 8, 32, 1024
+    for group in (1, 4):
+        sess, refs = [], []
+        for s, (n, B) in enumerate(zip(lengths, budgets)):
+            print(f"batched scan_topk session n={n} group={group}", flush=True)
+            keys = synth.keys(550, 0, max(n, 1), hkv, 128, torch.float16, 4, device=dev(),
+                              session=s)[:n]
+            q = synth.queries(550, 0, hq, 128, device=dev(), session=s)
+            if n > 0:
+                p = F.pack(keys)
+                planes, lo, hi, s2 = p.planes, p.lo, p.hi, p.sigma2
+            else:
+                planes = torch.zeros((hkv, 128, 4, 0), dtype=torch.int32, device=dev())
+                lo = torch.zeros((hkv, 128), device=dev())
+                hi = torch.ones((hkv, 128), device=dev())
+                s2 = torch.ones((hkv, 128), device=dev())
+            plan = F.plan(q, s2, B)
+            idx = torch.empty((hq // group, k), dtype=torch.int32, device=dev())
+            vals = torch.empty((hq // group, k), device=dev())
+            sess.append(F.Session(planes, lo, hi, n, q, plan, None, idx, vals))
+            if n > 0:
+                refs.append(F.topk(F.scan(planes, lo, hi, n, q, plan), k, group))
+            else:
+                refs.append(None)
+        F.scan_topk_batched(sess, k, group)
+        torch.cuda.synchronize()
+        for s, r in zip(sess, refs):
+            if r is None:
+                assert torch.all(s.idx == -1) and torch.all(torch.isinf(s.vals))
+            else:
+                assert torch.equal(s.idx, r[0]) and torch.equal(s.vals, r[1])
+
+
+def test_scan_topk_against_oracle(F, orc):
+    """Oracle logits (fp64 from the planes) ranked by the oracle's top-k: the
+    fused result agrees up to ties within the logit tolerance."""
+    n, hkv, hq, k = 30000, 2, 8, 512
+    print("scan_topk vs oracle", flush=True)
+    _, q, p, plan = layer(F, 560, n, hkv, hq)
+    idx, vals = F.scan_topk(p.planes, p.lo, p.hi, n, q, plan, k, 1)
+    torch.cuda.synchronize()
+    ref_logits = orc.scan(p.planes.cpu().numpy().view(np.uint32), p.lo.cpu().numpy(),
+                          p.hi.cpu().numpy(), n, q.cpu().numpy(), plan.cpu().numpy())
+    ridx, _ = orc.topk(ref_logits.astype(np.float32), k, 1)
+    A = logit_scale(q.cpu().numpy(), p.lo.cpu().numpy(), p.hi.cpu().numpy(), hq // hkv)
+    assert_topk_tie_tolerant(idx.cpu().numpy(), ridx, ref_logits, A, n, k)
