@@ -472,6 +472,15 @@ __device__ __forceinline__ int code_index(int gp, int key) {
   return gp * kGroupPitch + key + (key >> 5) + 2 * (key >> 10);
 }
 
+// The float t with (to_key(x) >= T) == (x >= t) for every finite x: T = 0
+// keeps everything; keys above the largest finite one keep nothing.
+__device__ __forceinline__ float key_threshold(uint32_t T) {
+  if (T == 0) return -INFINITY;
+  const float t = from_key(T);
+  if (t != t) return T >= 0x80000000u ? INFINITY : -INFINITY;  // NaN patterns
+  return t;
+}
+
 // Set-up-only state of the matrix-core kernel, overlaid on its code table.
 template <int GH>
 struct MfmaSetup {
@@ -479,7 +488,9 @@ struct MfmaSetup {
   SlotScratch<GH> X;
 };
 
-template <int GH, int MODE>
+// META: the sessions carry a side stream (its bytes are prefetched with the
+// planes, which costs registers the other variants do not spend).
+template <int GH, int MODE, bool META>
 __global__ __launch_bounds__(kMThreads, 4) void scan_mfma_kernel(ScanArgs a) {
   const BlockWork bw = block_work(a);
   KScanSess &S = *bw.S;
@@ -494,6 +505,7 @@ __global__ __launch_bounds__(kMThreads, 4) void scan_mfma_kernel(ScanArgs a) {
   __shared__ float s_scale[kMaxGH], s_C[kMaxGH];
   __shared__ int s_exp[kMaxGH];
   __shared__ uint32_t s_segc[kMaxGH];  // candidates this block found per row
+  __shared__ float s_tf[kMaxGH];       // float thresholds of the block's rows
   MfmaSetup<GH> &U = *reinterpret_cast<MfmaSetup<GH> *>(s_codes);
   SlotTable<GH> &T = U.T;
   build_slot_table<GH>(T, U.X, S, g, head_base);
@@ -513,6 +525,9 @@ __global__ __launch_bounds__(kMThreads, 4) void scan_mfma_kernel(ScanArgs a) {
     s_scale[tid] = ldexpf(1.0f, e - 30);
     s_C[tid] = T.C[tid];
     s_segc[tid] = 0;
+    // thresholds are read here, before any plane load is in flight
+    if constexpr (MODE == kScanCand) s_tf[tid] = key_threshold(S.thr[head_base + tid]);
+    if constexpr (MODE == kScanCandGroup) s_tf[tid] = key_threshold(S.thr[g]);
   }
   for (int e = tid; e < npasses * kPassGroups * 8; e += kMThreads)
     s_desc[e] = e < nslots ? T.desc[e] : (int16_t)0;
@@ -545,7 +560,7 @@ __global__ __launch_bounds__(kMThreads, 4) void scan_mfma_kernel(ScanArgs a) {
   const float scale = hh < GH ? s_scale[hh] : 0.0f;
   const uint32_t *gplanes = S.planes + (int64_t)g * kD * kPlanes * W;
   const int64_t ld = S.ld;
-  const uint8_t *meta = S.meta ? S.meta + (int64_t)g * n : nullptr;
+  const uint8_t *meta = META && S.meta ? S.meta + (int64_t)g * n : nullptr;
   const float meta_scale = S.meta_scale;
   float *out_row = hh < GH ? S.logits + (int64_t)(head_base + hh) * ld : nullptr;
   const bool vec_out = S.vec_out != 0;
@@ -594,13 +609,11 @@ __global__ __launch_bounds__(kMThreads, 4) void scan_mfma_kernel(ScanArgs a) {
     }
   };
 
-  // threshold key of this lane's output row (candidate modes), read once
-  uint32_t row_thr = 0;
-  if constexpr (MODE == kScanCand) {
-    if (hh < GH) row_thr = S.thr[head_base + hh];
-  } else if constexpr (MODE == kScanCandGroup) {
-    row_thr = S.thr[g];
-  }
+  // float threshold of this lane's output row (candidate modes)
+  const float row_tf = (MODE == kScanCand || MODE == kScanCandGroup) && hh < GH ? s_tf[hh] : 0.0f;
+  // side stream: 4 aligned bytes per beta when rows start on 4-byte bounds
+  const bool meta_words =
+      META && meta && ((reinterpret_cast<uintptr_t>(S.meta) & 3) == 0) && (n & 3) == 0;
 
   uint32_t xn[32];
 #pragma unroll
@@ -612,6 +625,16 @@ __global__ __launch_bounds__(kMThreads, 4) void scan_mfma_kernel(ScanArgs a) {
     const int vt = bw.tile0 + tt * bw.tile_step;
     const int64_t tile_key0 = (int64_t)real_tile(vt) * kMTileKeys;
     const bool has_group = kPassGroups * p + wave < ngroups;
+    // side-stream bytes of this tile, loaded before the next item's planes so
+    // that waiting for them does not wait for those
+    uint32_t mw[4] = {0u, 0u, 0u, 0u};
+    if (META && meta_words && p == npasses - 1 && hh < GH) {
+      const int64_t kb0 = tile_key0 + 256 * wave + 4 * (lane & 15);
+#pragma unroll
+      for (int beta = 0; beta < 4; ++beta)
+        if (kb0 + 64 * beta + 4 <= n)
+          mw[beta] = *reinterpret_cast<const uint32_t *>(meta + kb0 + 64 * beta);
+    }
     // ---- regroup: quarter k ends with word 4*m16 + k of the 4 plane rows of
     // every slot; 32-lane halves first, then 16-lane rows.
     uint32_t x[32];
@@ -681,7 +704,11 @@ __global__ __launch_bounds__(kMThreads, 4) void scan_mfma_kernel(ScanArgs a) {
     // ---- epilogue: 4 consecutive keys of head hh per beta
     if (p == npasses - 1) {
       const int64_t kb = tile_key0 + 256 * wave + 4 * nn;  // + 64*beta + e
-      if (meta && hh < GH) {
+      if (META && meta_words && hh < GH) {
+#pragma unroll
+        for (int b = 0; b < 16; ++b)
+          s[b] = __fmaf_rn(meta_scale, (float)((mw[b >> 2] >> (8 * (b & 3))) & 0xFFu), s[b]);
+      } else if (META && meta && hh < GH) {
         uint32_t mb[16];
 #pragma unroll
         for (int b = 0; b < 16; ++b) {
@@ -740,18 +767,21 @@ __global__ __launch_bounds__(kMThreads, 4) void scan_mfma_kernel(ScanArgs a) {
             if (GH > 2) acc = __dadd_rn(acc, (double)s2);
             if (GH > 3) acc = __dadd_rn(acc, (double)s3);
             s[b] = (float)acc;
+            // one key at a time (register budget)
+            __builtin_amdgcn_sched_barrier(0);
           }
           lane_rows = hh == 0;
           row = g;
         }
         if (lane_rows) {
-          const uint32_t T = row_thr;
-          // keys kb + 64*beta + e are valid while 64*beta + e < lim
-          const int lim = (int)min<int64_t>(n - kb, 256);
+          // s >= t as floats is to_key(s) >= T (see key_threshold); keys
+          // kb + 64*beta + e are valid while 64*beta + e < lim
+          const int64_t rem = n - kb;
+          const int lim = rem > 256 ? 256 : (int)rem;
           uint32_t mask = 0;
 #pragma unroll
           for (int b = 0; b < 16; ++b)
-            mask |= (uint32_t)((64 * (b >> 2) + (b & 3) < lim) && to_key(s[b]) >= T) << b;
+            mask |= (uint32_t)((64 * (b >> 2) + (b & 3) < lim) && s[b] >= row_tf) << b;
           if (mask) {
             // this block's segment of the row's candidate store
             uint32_t pos = atomicAdd(&s_segc[MODE == kScanCandGroup ? 0 : hh],
@@ -763,7 +793,7 @@ __global__ __launch_bounds__(kMThreads, 4) void scan_mfma_kernel(ScanArgs a) {
               if (pos < (uint32_t)S.seg_cap) {
                 float v = s[0];
 #pragma unroll
-                for (int j = 1; j < 16; ++j) v = b == j ? s[j] : v;
+                for (int q = 1; q < 16; ++q) v = b == q ? s[q] : v;
                 cl[pos] = compose(to_key(v), kb + 64 * (b >> 2) + (b & 3));
               }
               ++pos;
@@ -822,40 +852,45 @@ ScanFn pick(int GH) {
   }
 }
 
-template <int MODE>
+template <int MODE, bool META>
 ScanFn pick_mfma_mode(int GH) {
   switch (GH) {
-    case 1: return scan_mfma_kernel<1, MODE>;
-    case 2: return scan_mfma_kernel<2, MODE>;
-    case 3: return scan_mfma_kernel<3, MODE>;
-    default: return scan_mfma_kernel<4, MODE>;
+    case 1: return scan_mfma_kernel<1, MODE, META>;
+    case 2: return scan_mfma_kernel<2, MODE, META>;
+    case 3: return scan_mfma_kernel<3, MODE, META>;
+    default: return scan_mfma_kernel<4, MODE, META>;
   }
 }
 
-ScanFn pick_mfma(int GH, int mode) {
+template <bool META>
+ScanFn pick_mfma_meta(int GH, int mode) {
   switch (mode) {
-    case kScanSample: return pick_mfma_mode<kScanSample>(GH);
-    case kScanCand: return pick_mfma_mode<kScanCand>(GH);
-    case kScanCandGroup: return pick_mfma_mode<kScanCandGroup>(GH);
-    default: return pick_mfma_mode<kScanLogits>(GH);
+    case kScanSample: return pick_mfma_mode<kScanSample, META>(GH);
+    case kScanCand: return pick_mfma_mode<kScanCand, META>(GH);
+    case kScanCandGroup: return pick_mfma_mode<kScanCandGroup, META>(GH);
+    default: return pick_mfma_mode<kScanLogits, META>(GH);
   }
+}
+
+ScanFn pick_mfma(int GH, int mode, bool meta) {
+  return meta ? pick_mfma_meta<true>(GH, mode) : pick_mfma_meta<false>(GH, mode);
 }
 
 // Pinned-host planes: the link is the bound, the fp32 kernel with whole-word
 // lanes keeps 256-byte wave accesses.  HBM planes: the matrix-core kernel
 // (the fp32 kernel above 2^25 keys per session).
-ScanFn kernel_for(bool host, int GH, int mode) {
-  return host ? pick<kHostVariant.kpl, kHostVariant.aux>(GH) : pick_mfma(GH, mode);
+ScanFn kernel_for(bool host, int GH, int mode, bool meta) {
+  return host ? pick<kHostVariant.kpl, kHostVariant.aux>(GH) : pick_mfma(GH, mode, meta);
 }
 int threads_for(bool host) { return host ? kScanThreads : kMThreads; }
 
-int resident_blocks_per_cu(bool host, int GH, int mode) {
-  static int cached[2][kMaxGH + 1][4] = {};
-  int &c = cached[host ? 1 : 0][GH][mode];
+int resident_blocks_per_cu(bool host, int GH, int mode, bool meta) {
+  static int cached[2][kMaxGH + 1][4][2] = {};
+  int &c = cached[host ? 1 : 0][GH][mode][meta ? 1 : 0];
   if (c == 0) {
     int nb = 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &nb, kernel_for(host, GH, mode), threads_for(host), 0);
+        &nb, kernel_for(host, GH, mode, meta), threads_for(host), 0);
     c = (e == hipSuccess && nb > 0) ? nb : 1;
   }
   return c;
@@ -926,6 +961,8 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_
     return mode == kScanSample ? std::min<int64_t>(t, kSampleTiles) : t;
   };
   const int kernel_mode = fp32_path ? 0 : mode;
+  bool any_meta = false;
+  for (int32_t j = 0; j < n_sess; ++j) any_meta |= sess[j].meta != nullptr;
   for (int32_t s0 = 0; s0 < n_sess; s0 += kSessPerLaunch) {
     const int32_t cnt = std::min(kSessPerLaunch, n_sess - s0);
     // One tiling per session for all head chunks: one round of resident
@@ -934,7 +971,8 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_
     int64_t total_tiles = 0;
     for (int j = 0; j < cnt; ++j) total_tiles += visited(sess[s0 + j].n) * hkv;
     const int64_t target_blocks =
-        (int64_t)ncu * resident_blocks_per_cu(fp32_path, std::min(kMaxGH, group), kernel_mode);
+        (int64_t)ncu *
+        resident_blocks_per_cu(fp32_path, std::min(kMaxGH, group), kernel_mode, any_meta);
     int64_t tpb_s[kSessPerLaunch];
     for (int j = 0; j < cnt; ++j) {
       const int64_t tiles = visited(sess[s0 + j].n);
@@ -983,7 +1021,7 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_
         blocks += o.blocks_per_head * hkv;
       }
       if (blocks == 0) continue;
-      hipLaunchKernelGGL(kernel_for(fp32_path, GH, mode), dim3(blocks),
+      hipLaunchKernelGGL(kernel_for(fp32_path, GH, mode, any_meta), dim3(blocks),
                          dim3(threads_for(fp32_path)), 0, s, a);
       int32_t rc = hip_fail(hipGetLastError(), "scan launch");
       if (rc) return rc;
