@@ -290,16 +290,35 @@ __global__ __launch_bounds__(kBig) void topk_sample_kernel(TopkArgs a) {
   if (stride < kRun) stride = kRun;
   const int runs = (int)((n + stride - 1) / stride);
   const int m = runs * kRun;
-  // every load of the thread in flight at once
+  // every load of the thread in flight at once (one row: plain loads first,
+  // keys after)
   uint32_t v[kPer];
   uint32_t okm = 0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int e = threadIdx.x + j * kBig;
     const int64_t pos = (int64_t)(e / kRun) * stride + (e % kRun);
-    const bool ok = e < m && pos < n;
-    v[j] = ok ? to_key(group_score(R.row, ld, a.group, pos)) : 0u;
-    okm |= (uint32_t)ok << j;
+    okm |= (uint32_t)(e < m && pos < n) << j;
+  }
+  if (a.group == 1) {
+    // unconditional loads (positions out of the sample read element 0, which
+    // exists: n >= 1 here), so that all of them are issued before any wait
+    float f[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = threadIdx.x + j * kBig;
+      const int64_t pos = (int64_t)(e / kRun) * stride + (e % kRun);
+      f[j] = R.row[((okm >> j) & 1) ? pos : 0];
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) v[j] = ((okm >> j) & 1) ? to_key(f[j]) : 0u;
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = threadIdx.x + j * kBig;
+      const int64_t pos = (int64_t)(e / kRun) * stride + (e % kRun);
+      v[j] = ((okm >> j) & 1) ? to_key(group_score(R.row, ld, a.group, pos)) : 0u;
+    }
   }
   uint32_t mx = 0, mn = 0xFFFFFFFFu;
   int cnt = __popc(okm);
