@@ -8,28 +8,28 @@
 //     s_i = C_h + sum_c gamma_hc * m_ic,
 //     gamma_hc = q_hc * delta_c            (0 when t_hc = 0),
 //     C_h = sum_c q_hc * (lo_c + delta_c * 2^(3 - t_hc))   (fp64, rounded once).
-// The per-key sum has one fp32 term per channel read, so its rounding error
-// is bounded by (terms + 1) * 2^-24 * sum|terms|, well inside 1e-5 * A_h.
 //
-// Work decomposition (MI355X-first; no counterpart on the pages).
-//  * A block takes one (session, kv head) and a run of 8192-key tiles; its 4
-//    waves take 2048 keys each, i.e. one 64-word block of every plane row:
-//    lane w owns plane word w (keys 32w..32w+31), so every plane load is one
-//    coalesced 256-byte wave access -- from HBM or zero-copy from pinned host
-//    memory, through the same code.
-//  * Slots: the distinct (channel, depth) pairs the kv head's query heads
-//    read.  A slot of depth u loads the top u planes of its channel (the
-//    union across heads is loaded from memory once; a shallower slot of the
-//    same channel re-reads cached words).  Each head uses exactly the slots of
-//    its own depths, so no masking is ever needed.  Slots are ordered by the
-//    set of heads that use them, then by channel, and processed 8 at a time;
-//    a group of 8 slots skips the heads that use none of them.
-//  * Per group: 32 plane rows (8 slots x 4 planes, unread planes = 0) are
-//    bit-transposed in registers (32x32 transpose, 5 stages of shift/select),
-//    giving per key a word of 8 nibble codes.  Nibbles become fp32 through
-//    byte conversions, then one fp32 FMA per (head, slot, key).
-//  * The next group's plane words are loaded while the current group is
-//    computed.
+// Slots (both kernels): the distinct (channel, depth) pairs the query heads
+// of one kv head read.  A slot of depth u loads the top u planes of its
+// channel, so the union of the heads' reads comes from memory once; each head
+// weighs exactly the slots at its own depths.  Slots are ordered by the set
+// of heads that use them, then by channel, and handled 8 at a time: 32 plane
+// rows (8 slots x 4 planes, unread planes = 0), bit-transposed so that every
+// key gets one word of 8 nibble codes.
+//
+// Two kernels (the pages give no kernel design; both are MI355X-first):
+//  * scan_mfma_kernel, planes in HBM: the contraction over slots runs on the
+//    matrix cores with exact int8 limbs of gamma (see its comment).
+//  * scan_kernel, planes in pinned host memory (and sessions above 2^25
+//    keys): the link is the bound, so the fp32 FMA form is enough.  A block
+//    takes one (session, kv head) and a run of 8192-key tiles; its 4 waves
+//    take 2048 keys each: lane w owns plane word w (keys 32w..32w+31), so
+//    every plane load is one coalesced 256-byte wave access.  Nibbles become
+//    fp32 through byte conversions, then one FMA per (head, slot, key), with
+//    the weights in scalar registers; the next 8 slots' words are loaded
+//    while the current ones are computed.  The per-key sum has one fp32 term
+//    per channel read, so its rounding error is bounded by
+//    (terms + 1) * 2^-24 * sum|terms|, well inside 1e-5 * A_h.
 #include "fathom_internal.h"
 
 namespace fathom {
@@ -116,14 +116,6 @@ __device__ __forceinline__ void transpose32_perm(uint32_t (&x)[32]) {
   transpose_stage<32, 4, 0x0F0F0F0Fu>(x);
   transpose_stage<32, 2, 0x33333333u>(x);
   transpose_stage<32, 1, 0x55555555u>(x);
-}
-
-// Stages 8..1 on one 16-row half that stage 16 has already separated.
-__device__ __forceinline__ void transpose16(uint32_t (&x)[16]) {
-  transpose_stage<16, 8, 0x00FF00FFu>(x);
-  transpose_stage<16, 4, 0x0F0F0F0Fu>(x);
-  transpose_stage<16, 2, 0x33333333u>(x);
-  transpose_stage<16, 1, 0x55555555u>(x);
 }
 
 __device__ __forceinline__ int uniform(int v) {
@@ -298,7 +290,7 @@ __device__ __forceinline__ BlockWork block_work(const ScanArgs &) {
   return w;
 }
 
-template <int GH, int KPL, int AUX>
+template <int GH, int AUX>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   const BlockWork bw = block_work(a);
   KScanSess &S = *bw.S;
@@ -312,18 +304,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   const int16_t *s_desc = T.desc;
 
   // ---- main loop ------------------------------------------------------------
-  // KPL = 32: lane = one plane word (32 keys), a wave covers 64 words, and
-  // every wave load is one 256-byte access.  KPL = 16: lane = half a word
-  // (word lane & 31, keys 16*hf.. with hf = lane >> 5), a wave covers 32
-  // words; the first transpose stage keeps the lane's half (one byte permute
-  // per row) and the last four run on 16 registers -- half the accumulators,
-  // so more waves fit.
-  constexpr int kWords = KPL == 32 ? 64 : 32;
-  constexpr int kWaveK = kWords * 32;
+  // lane = one plane word (32 keys), a wave covers 64 words, and every wave
+  // load is one 256-byte access
+  constexpr int KPL = 32;
+  constexpr int kWaveK = 64 * 32;
   constexpr int kTileK = kWaveK * (kScanThreads / 64);
   const int wave = tid >> 6, lane = tid & 63;
-  const int hf = KPL == 32 ? 0 : lane >> 5;
-  const uint32_t half_sel = hf ? 0x07060302u : 0x05040100u;
   const uint32_t *gplanes = S.planes + (int64_t)g * kD * kPlanes * S.W;
   float C[GH];
 #pragma unroll
@@ -333,10 +319,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
     const int64_t wkey0 =
         (int64_t)(tile0 + tt * tile_step) * kTileK + (int64_t)wave * kWaveK;
     if (wkey0 >= n) break;
-    const int wl = KPL == 32 ? lane : (lane & 31);
-    const int64_t word = wkey0 / 32 + wl;
+    const int64_t word = wkey0 / 32 + lane;
     const int32_t wbase = (int32_t)(wkey0 / 32);
-    const uint32_t voff = (uint32_t)wl * 4u;  // byte offset
+    const uint32_t voff = (uint32_t)lane * 4u;  // byte offset
 
     float acc[GH][KPL];
 #pragma unroll
@@ -348,18 +333,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
     if (ngroups > 0) load_group<AUX>(gplanes, S.W, wbase, voff, s_desc, 0, xn);
     for (int grp = 0; grp < ngroups; ++grp) {
       uint32_t y[KPL];
-      if constexpr (KPL == 32) {
 #pragma unroll
-        for (int r = 0; r < 32; ++r) y[r] = xn[r];
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) y[r] = __builtin_amdgcn_perm(xn[r + 16], xn[r], half_sel);
-      }
+      for (int r = 0; r < 32; ++r) y[r] = xn[r];
       if (grp + 1 < ngroups) load_group<AUX>(gplanes, S.W, wbase, voff, s_desc, grp + 1, xn);
-      if constexpr (KPL == 32)
-        transpose32(y);
-      else
-        transpose16(y);
+      transpose32(y);
       const int gm = uniform(T.gmask[grp]);
       // the group's weights, wave-uniform: held in scalar registers
       float gv[GH][8];
@@ -402,7 +379,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
     }
 
     // ---- optional 8-bit side stream (fixed-width baseline) ----------------
-    const int64_t key0 = word * 32 + KPL * hf;
+    const int64_t key0 = word * 32;
     if (S.meta) {
       const uint8_t *mp = S.meta + (int64_t)g * n + key0;
 #pragma unroll
@@ -830,25 +807,20 @@ __global__ __launch_bounds__(256) void read_prefixes_kernel(
   out[((int64_t)h * n + i) * kD + c] = (uint8_t)v;
 }
 
-// Kernel variants: planes in pinned host memory are read with whole-word
-// lanes (256-byte wave accesses) and streaming loads; planes in HBM with
-// half-word lanes (more resident waves for the arithmetic).
-struct Variant {
-  int kpl;
-  int aux;
-};
-constexpr Variant kHostVariant{32, 2};    // aux 2: non-temporal
-constexpr Variant kDeviceVariant{16, 0};
+// The fp32 kernel reads with streaming (non-temporal) loads: the planes
+// stream once per step.
+constexpr int kHostAux = 2;
+constexpr int kHostTileKeys = 32 * 64 * (kScanThreads / 64);
 
 using ScanFn = void (*)(ScanArgs);
 
-template <int KPL, int AUX>
+template <int AUX>
 ScanFn pick(int GH) {
   switch (GH) {
-    case 1: return scan_kernel<1, KPL, AUX>;
-    case 2: return scan_kernel<2, KPL, AUX>;
-    case 3: return scan_kernel<3, KPL, AUX>;
-    default: return scan_kernel<4, KPL, AUX>;
+    case 1: return scan_kernel<1, AUX>;
+    case 2: return scan_kernel<2, AUX>;
+    case 3: return scan_kernel<3, AUX>;
+    default: return scan_kernel<4, AUX>;
   }
 }
 
@@ -880,7 +852,7 @@ ScanFn pick_mfma(int GH, int mode, bool meta) {
 // lanes keeps 256-byte wave accesses.  HBM planes: the matrix-core kernel
 // (the fp32 kernel above 2^25 keys per session).
 ScanFn kernel_for(bool host, int GH, int mode, bool meta) {
-  return host ? pick<kHostVariant.kpl, kHostVariant.aux>(GH) : pick_mfma(GH, mode, meta);
+  return host ? pick<kHostAux>(GH) : pick_mfma(GH, mode, meta);
 }
 int threads_for(bool host) { return host ? kScanThreads : kMThreads; }
 
@@ -954,7 +926,7 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_
     }
   const bool cand = mode == kScanCand || mode == kScanCandGroup;
   const int64_t tile_keys =
-      fp32_path ? (int64_t)kHostVariant.kpl * 64 * (kScanThreads / 64) : (int64_t)kMTileKeys;
+      fp32_path ? (int64_t)kHostTileKeys : (int64_t)kMTileKeys;
   // tiles a session's blocks visit: all, or the sampled ones
   auto visited = [&](int64_t n) {
     const int64_t t = (n + tile_keys - 1) / tile_keys;
