@@ -8,8 +8,12 @@
 //   pack_sigma    sigma^2 = Var(code) * delta^2 from the exact integer sums
 //
 // Every value is bit-identical to the CPU definition: min/max are exact, the
-// quantiser uses one IEEE fp32 subtract and one correctly rounded fp32 divide,
-// and the variance is evaluated from exact int64 sums in a fixed fp64 order.
+// quantiser's code is floor of one IEEE fp32 subtract followed by one
+// correctly rounded fp32 divide, and the variance is evaluated from exact
+// int64 sums in a fixed fp64 order.
+//
+// Keys whose rows are 16-byte aligned take the vector kernels (16-byte loads,
+// four key rows per wave instruction); other strides take the scalar ones.
 #include <hip/hip_fp16.h>
 
 #include "fathom_internal.h"
@@ -54,19 +58,35 @@ __global__ __launch_bounds__(kMinmaxThreads) void pack_minmax_kernel(
   }
 }
 
-__global__ __launch_bounds__(kD) void pack_range_kernel(
+// One block per kv head: 8 threads per channel split the partials, then a
+// reduction in LDS (min / max do not depend on the order).
+constexpr int kReduceThreads = 1024;
+constexpr int kReduceSlices = kReduceThreads / kD;
+
+__global__ __launch_bounds__(kReduceThreads) void pack_range_kernel(
     const float2 *__restrict__ part, int32_t nparts, int32_t hkv,
     float *__restrict__ lo, float *__restrict__ hi) {
-  const int h = blockIdx.x, c = threadIdx.x;
+  __shared__ float2 red[kReduceSlices][kD];
+  const int h = blockIdx.x, c = threadIdx.x % kD, sl = threadIdx.x / kD;
   float mn = INFINITY, mx = -INFINITY;
-  for (int p = 0; p < nparts; ++p) {
+#pragma unroll 8
+  for (int p = sl; p < nparts; p += kReduceSlices) {
     float2 v = part[((int64_t)p * hkv + h) * kD + c];
     mn = fminf(mn, v.x);
     mx = fmaxf(mx, v.y);
   }
-  // -0 and +0 are one key value: the stored ends are +0.
-  lo[h * kD + c] = __fadd_rn(mn, 0.0f);
-  hi[h * kD + c] = __fadd_rn(mx, 0.0f);
+  red[sl][c] = make_float2(mn, mx);
+  __syncthreads();
+  if (sl == 0) {
+#pragma unroll
+    for (int q = 1; q < kReduceSlices; ++q) {
+      mn = fminf(mn, red[q][c].x);
+      mx = fmaxf(mx, red[q][c].y);
+    }
+    // -0 and +0 are one key value: the stored ends are +0.
+    lo[h * kD + c] = __fadd_rn(mn, 0.0f);
+    hi[h * kD + c] = __fadd_rn(mx, 0.0f);
+  }
 }
 
 __device__ inline int quantise(float x, float lo, float delta) {
@@ -147,16 +167,324 @@ __global__ __launch_bounds__(kPlaneThreads) void pack_planes_kernel(
     sums[((int64_t)blockIdx.x * hkv + h) * kD + my_c] = make_int2(my_s1, my_s2);
 }
 
-__global__ __launch_bounds__(kD) void pack_sigma_kernel(
+// ---- vector kernels (16-byte aligned key rows) -------------------------------
+// Thread t of a 256-thread block owns channels 8j..8j+7 (j = t % 16) of key
+// row t / 16 of each 16-row step: a wave instruction reads 4 whole rows.
+constexpr int kVecThreads = 256;
+constexpr int kVecRows = kVecThreads / 16;
+
+// The 8 channels of one key row (16 bytes of fp16 or 32 of fp32).
+template <typename T>
+__device__ __forceinline__ void load_row8(const T *p, uint4 (&v)[2]);
+template <>
+__device__ __forceinline__ void load_row8<__half>(const __half *p, uint4 (&v)[2]) {
+  v[0] = *reinterpret_cast<const uint4 *>(p);
+  v[1] = make_uint4(0, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ void load_row8<float>(const float *p, uint4 (&v)[2]) {
+  v[0] = *reinterpret_cast<const uint4 *>(p);
+  v[1] = *reinterpret_cast<const uint4 *>(p + 4);
+}
+template <typename T>
+__device__ __forceinline__ void unpack_row8(const uint4 (&v)[2], float (&x)[8]);
+template <>
+__device__ __forceinline__ void unpack_row8<__half>(const uint4 (&v)[2], float (&x)[8]) {
+  const uint32_t w[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __half2float(__ushort_as_half((unsigned short)(w[i] & 0xFFFFu)));
+    x[2 * i + 1] = __half2float(__ushort_as_half((unsigned short)(w[i] >> 16)));
+  }
+}
+template <>
+__device__ __forceinline__ void unpack_row8<float>(const uint4 (&v)[2], float (&x)[8]) {
+  x[0] = __uint_as_float(v[0].x);
+  x[1] = __uint_as_float(v[0].y);
+  x[2] = __uint_as_float(v[0].z);
+  x[3] = __uint_as_float(v[0].w);
+  x[4] = __uint_as_float(v[1].x);
+  x[5] = __uint_as_float(v[1].y);
+  x[6] = __uint_as_float(v[1].z);
+  x[7] = __uint_as_float(v[1].w);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kVecThreads) void pack_minmax_vec_kernel(
+    const T *__restrict__ keys, int64_t n, int64_t stride_tok, int64_t stride_head,
+    int64_t chunk, float2 *__restrict__ part) {
+  __shared__ float s_mn[kVecRows][kD + 1], s_mx[kVecRows][kD + 1];
+  const int h = blockIdx.y, hkv = gridDim.y;
+  const int r = threadIdx.x >> 4, j = threadIdx.x & 15;
+  const int64_t i0 = (int64_t)blockIdx.x * chunk;
+  const int64_t i1 = min(n, i0 + chunk);
+  const T *base = keys + (int64_t)h * stride_head + 8 * j;
+  float mn[8], mx[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    mn[c] = INFINITY;
+    mx[c] = -INFINITY;
+  }
+  int64_t i = i0 + r;
+  // four rows in flight per thread
+  for (; i + 3 * kVecRows < i1; i += 4 * kVecRows) {
+    uint4 v[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load_row8<T>(base + (i + u * kVecRows) * stride_tok, v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float x[8];
+      unpack_row8<T>(v[u], x);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        mn[c] = fminf(mn[c], x[c]);
+        mx[c] = fmaxf(mx[c], x[c]);
+      }
+    }
+  }
+  for (; i < i1; i += kVecRows) {
+    uint4 v[2];
+    load_row8<T>(base + i * stride_tok, v);
+    float x[8];
+    unpack_row8<T>(v, x);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      mn[c] = fminf(mn[c], x[c]);
+      mx[c] = fmaxf(mx[c], x[c]);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    s_mn[r][8 * j + c] = mn[c];
+    s_mx[r][8 * j + c] = mx[c];
+  }
+  __syncthreads();
+  if (threadIdx.x < kD) {
+    const int c = threadIdx.x;
+    float a = INFINITY, b = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kVecRows; ++q) {
+      a = fminf(a, s_mn[q][c]);
+      b = fmaxf(b, s_mx[q][c]);
+    }
+    part[((int64_t)blockIdx.x * hkv + h) * kD + c] = make_float2(a, b);
+  }
+}
+
+// Code of y = fl(x - lo) >= 0 as the exact definition floor(RN(y / delta))
+// (clamped to 15), without the divide in almost every case.  q = RN(y * r)
+// with r = RN(1/delta) differs from y / delta by at most 2 * 2^-24 * 16 and
+// RN(y / delta) from y / delta by at most 2^-24 * 16, so whenever q is at
+// least 2^-14 away from every integer both have the same floor; otherwise
+// (and for delta = 0, or a reciprocal out of range, where q is 0, inf or NaN)
+// the correctly rounded divide decides.  Returns the code, or -1 when the
+// divide must decide.
+__device__ __forceinline__ int quantise_fast(float y, float r) {
+  const float q = __fmul_rn(y, r);
+  const float f = __builtin_amdgcn_fractf(q);
+  const bool safe = fabsf(__fsub_rn(f, 0.5f)) < 0.5f - 0x1p-14f;  // false for NaN
+  return safe ? (int)fminf(q, 15.5f) : -1;
+}
+
+// Stage S of a 32x32 bit transpose: swap the off-diagonal SxS blocks of
+// every 2Sx2S block.
+template <int S, uint32_t M>
+__device__ __forceinline__ void bit_stage(uint32_t (&x)[32]) {
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    if ((r & S) == 0) {
+      const uint32_t a = x[r], b = x[r + S];
+      x[r] = (a & M) | ((b << S) & ~M);
+      x[r + S] = ((a >> S) & M) | (b & ~M);
+    }
+  }
+}
+
+// 32x32 bit transpose: on entry x[t] bit b = element (t, b); on exit x[b]
+// bit t = element (t, b).  Byte permutes for the 16- and 8-bit stages,
+// shift/select for the rest.
+__device__ __forceinline__ void bit_transpose32(uint32_t (&x)[32]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const uint32_t a = x[r], b = x[r + 16];
+    x[r] = __builtin_amdgcn_perm(b, a, 0x05040100u);       // a.lo16 | b.lo16 << 16
+    x[r + 16] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // a.hi16 | b.hi16 << 16
+  }
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    if ((r & 8) == 0) {
+      const uint32_t a = x[r], b = x[r + 8];
+      x[r] = __builtin_amdgcn_perm(b, a, 0x06020400u);      // bytes a0 b0 a2 b2
+      x[r + 8] = __builtin_amdgcn_perm(b, a, 0x07030501u);  // bytes a1 b1 a3 b3
+    }
+  }
+  bit_stage<4, 0x0F0F0F0Fu>(x);
+  bit_stage<2, 0x33333333u>(x);
+  bit_stage<1, 0x55555555u>(x);
+}
+
+// One block = (2048-key tile, quarter Q of the channels, kv head), with the
+// quarter and the head varying fastest over the grid, so that the blocks
+// running together read whole key rows.
+//  * staging: thread t takes channels 32Q + 8j .. +7 (j = t % 4) of key rows
+//    t / 4, t / 4 + 64, ... (16-byte loads: a wave instruction reads the
+//    quarter of 16 rows; the next batch of rows is in flight while the
+//    current one is quantised) and stores each row's 8 codes as one dword of
+//    nibbles in LDS;
+//  * planes: wave G takes channels 32Q + 8G .. +7 and lane w the 32 keys of
+//    plane word w of the tile: it reads their 32 code dwords and
+//    bit-transposes them, so that word 4ci + p is bit p of channel
+//    32Q + 8G + ci's codes, i.e. one plane word; a store instruction then
+//    writes a whole 256-byte row segment.  S1 and S2 of the 8 channels follow
+//    from popcounts of the plane words (exact integers), summed over the wave.
+template <typename T>
+__global__ __launch_bounds__(kVecThreads) void pack_planes_vec_kernel(
+    const T *__restrict__ keys, int64_t n, int64_t stride_tok, int64_t stride_head,
+    int64_t W, int32_t hkv, const float *__restrict__ lo, const float *__restrict__ hi,
+    uint32_t *__restrict__ planes, int2 *__restrict__ sums) {
+  constexpr int kGroups = 4;                      // 8-channel groups per quarter
+  constexpr int kRowsPerStep = kVecThreads / kGroups;  // 64
+  constexpr int kSteps = kBlockKeys / kRowsPerStep;    // 32
+  constexpr int kBatch = sizeof(T) == 2 ? 8 : 4;       // rows per lane in flight
+  constexpr int kBatches = kSteps / kBatch;
+  // LDS dword of (key, group): 4 per key, each 32-key run shifted by one
+  // (one to one; staging stores and transpose reads meet at most two lanes
+  // per bank)
+  __shared__ uint32_t s_codes[kBlockKeys * kGroups + kBlockKeys / 32];
+  auto cidx = [](int key, int grp) { return key * kGroups + grp + (key >> 5); };
+  const int bx = blockIdx.x;
+  const int Q = bx & 3, h = (bx >> 2) % hkv, tile = (bx >> 2) / hkv;
+  const int tid = threadIdx.x;
+  const int jr = tid >> 2, j = tid & 3;     // staging: row offset, channel group
+  const int wave = tid >> 6, lane = tid & 63;
+  const int64_t key0 = (int64_t)tile * kBlockKeys;
+  const int cbase = 32 * Q + 8 * j;         // this thread's staging channels
+  const T *base = keys + (int64_t)h * stride_head + cbase;
+
+  float clo[8], crec[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float l = lo[h * kD + cbase + c];
+    clo[c] = l;
+    crec[c] = __fdiv_rn(1.0f, __fmul_rn(__fsub_rn(hi[h * kD + cbase + c], l), 0.0625f));
+  }
+
+  auto load_batch = [&](int bt, uint4 (&v)[kBatch][2]) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      int64_t i = key0 + (int64_t)(bt * kBatch + u) * kRowsPerStep + jr;
+      i = i < n ? i : n - 1;  // rows past n: any valid row, codes cleared below
+      load_row8<T>(base + i * stride_tok, v[u]);
+    }
+  };
+  uint4 vn[kBatch][2];
+  load_batch(0, vn);
+#pragma unroll 1
+  for (int bt = 0; bt < kBatches; ++bt) {
+    uint4 v[kBatch][2];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      v[u][0] = vn[u][0];
+      v[u][1] = vn[u][1];
+    }
+    if (bt + 1 < kBatches) load_batch(bt + 1, vn);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      float x[8];
+      unpack_row8<T>(v[u], x);
+      int code[8];
+      bool exact = false;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        code[c] = quantise_fast(__fsub_rn(x[c], clo[c]), crec[c]);
+        exact |= code[c] < 0;
+      }
+      if (exact) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          if (code[c] < 0) {
+            const float l = clo[c];
+            code[c] = quantise(x[c], l, __fmul_rn(__fsub_rn(hi[h * kD + cbase + c], l), 0.0625f));
+          }
+      }
+      const int key = (bt * kBatch + u) * kRowsPerStep + jr;
+      uint32_t w = 0;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) w |= (uint32_t)code[c] << (4 * c);
+      s_codes[cidx(key, j)] = key0 + key < n ? w : 0u;
+    }
+  }
+  __syncthreads();
+
+  // ---- planes and code sums: wave = channel group, lane = plane word
+  uint32_t x[32];
+#pragma unroll
+  for (int t = 0; t < 32; ++t) x[t] = s_codes[cidx(32 * lane + t, wave)];
+  bit_transpose32(x);
+  // this kv head's planes (at most 2 GiB: the launcher checks); lane offset
+  // of the group's first row plus the wave-uniform offset of row 4ci + s
+  const uint32_t row_bytes = (uint32_t)W * 4u;
+  const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+      planes + (int64_t)h * kD * kPlanes * W, (short)0, (int32_t)(row_bytes * kD * kPlanes),
+      0x00020000);
+  const int c0 = 32 * Q + 8 * wave;
+  const uint32_t voff = (uint32_t)c0 * kPlanes * row_bytes + (uint32_t)(tile * 64 + lane) * 4u;
+  int s1[8], s2[8];
+#pragma unroll
+  for (int ci = 0; ci < 8; ++ci) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      __builtin_amdgcn_raw_buffer_store_b32(x[4 * ci + p], prs, (int32_t)voff,
+                                            (int32_t)((4 * ci + 3 - p) * row_bytes), 0);
+    const uint32_t b0 = x[4 * ci], b1 = x[4 * ci + 1], b2 = x[4 * ci + 2], b3 = x[4 * ci + 3];
+    const int p0 = __popc(b0), p1 = __popc(b1), p2 = __popc(b2), p3 = __popc(b3);
+    s1[ci] = p0 + 2 * p1 + 4 * p2 + 8 * p3;
+    s2[ci] = p0 + 4 * p1 + 16 * p2 + 64 * p3 +
+             2 * (2 * __popc(b0 & b1) + 4 * __popc(b0 & b2) + 8 * __popc(b0 & b3) +
+                  8 * __popc(b1 & b2) + 16 * __popc(b1 & b3) + 32 * __popc(b2 & b3));
+  }
+  // sums over the wave's 64 lanes (integers: the order does not matter)
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1)
+#pragma unroll
+    for (int ci = 0; ci < 8; ++ci) {
+      s1[ci] += __shfl_xor(s1[ci], off);
+      s2[ci] += __shfl_xor(s2[ci], off);
+    }
+  if (lane < 8) {
+    int a = s1[0], b = s2[0];
+#pragma unroll
+    for (int ci = 1; ci < 8; ++ci) {
+      a = lane == ci ? s1[ci] : a;
+      b = lane == ci ? s2[ci] : b;
+    }
+    sums[((int64_t)tile * hkv + h) * kD + c0 + lane] = make_int2(a, b);
+  }
+}
+
+// One block per kv head: 8 threads per channel split the blocks' code sums
+// (exact integers, so the order does not matter), then sigma^2 in a fixed
+// fp64 order.
+__global__ __launch_bounds__(kReduceThreads) void pack_sigma_kernel(
     const int2 *__restrict__ sums, int32_t nblocks, int32_t hkv, int64_t n,
     const float *__restrict__ lo, const float *__restrict__ hi,
     float *__restrict__ sigma2) {
-  const int h = blockIdx.x, c = threadIdx.x;
+  __shared__ longlong2 red[kReduceSlices][kD];
+  const int h = blockIdx.x, c = threadIdx.x % kD, sl = threadIdx.x / kD;
   int64_t s1 = 0, s2 = 0;
-  for (int b = 0; b < nblocks; ++b) {
+#pragma unroll 8
+  for (int b = sl; b < nblocks; b += kReduceSlices) {
     int2 v = sums[((int64_t)b * hkv + h) * kD + c];
     s1 += v.x;
     s2 += v.y;
+  }
+  red[sl][c] = make_longlong2(s1, s2);
+  __syncthreads();
+  if (sl != 0) return;
+#pragma unroll
+  for (int q = 1; q < kReduceSlices; ++q) {
+    s1 += red[q][c].x;
+    s2 += red[q][c].y;
   }
   const float l = lo[h * kD + c];
   const float delta = __fmul_rn(__fsub_rn(hi[h * kD + c], l), 0.0625f);
@@ -196,14 +524,28 @@ int32_t launch_pack_t(const T *keys, int64_t n, int32_t hkv, int64_t stride_tok,
   float2 *part = reinterpret_cast<float2 *>(ws);
   int2 *sums = reinterpret_cast<int2 *>(static_cast<char *>(ws) + L.part_bytes);
   const int64_t W = plane_words(n);
-  hipLaunchKernelGGL(pack_minmax_kernel<T>, dim3(L.nparts, hkv), dim3(kMinmaxThreads),
-                     0, s, keys, n, stride_tok, stride_head, L.chunk, part);
-  hipLaunchKernelGGL(pack_range_kernel, dim3(hkv), dim3(kD), 0, s, part, L.nparts,
+  // 8 channels of a row are 16 (fp16) or 32 (fp32) bytes: vector loads need
+  // 16-byte aligned rows
+  constexpr int64_t kAlign = 16 / sizeof(T);
+  // (and the planes kernel addresses one kv head's planes with 32-bit offsets)
+  const bool vec = (reinterpret_cast<uintptr_t>(keys) % 16) == 0 && stride_tok % kAlign == 0 &&
+                   stride_head % kAlign == 0 && W * 4 * kPlanes * kD <= INT32_MAX;
+  if (vec)
+    hipLaunchKernelGGL(pack_minmax_vec_kernel<T>, dim3(L.nparts, hkv), dim3(kVecThreads), 0, s,
+                       keys, n, stride_tok, stride_head, L.chunk, part);
+  else
+    hipLaunchKernelGGL(pack_minmax_kernel<T>, dim3(L.nparts, hkv), dim3(kMinmaxThreads),
+                       0, s, keys, n, stride_tok, stride_head, L.chunk, part);
+  hipLaunchKernelGGL(pack_range_kernel, dim3(hkv), dim3(kReduceThreads), 0, s, part, L.nparts,
                      hkv, lo, hi);
-  hipLaunchKernelGGL(pack_planes_kernel<T>, dim3(L.nblocks, hkv), dim3(kPlaneThreads),
-                     0, s, keys, n, stride_tok, stride_head, W, lo, hi, planes, sums);
-  hipLaunchKernelGGL(pack_sigma_kernel, dim3(hkv), dim3(kD), 0, s, sums, L.nblocks,
-                     hkv, n, lo, hi, sigma2);
+  if (vec)
+    hipLaunchKernelGGL(pack_planes_vec_kernel<T>, dim3(L.nblocks * 4 * hkv), dim3(kVecThreads),
+                       0, s, keys, n, stride_tok, stride_head, W, hkv, lo, hi, planes, sums);
+  else
+    hipLaunchKernelGGL(pack_planes_kernel<T>, dim3(L.nblocks, hkv), dim3(kPlaneThreads),
+                       0, s, keys, n, stride_tok, stride_head, W, lo, hi, planes, sums);
+  hipLaunchKernelGGL(pack_sigma_kernel, dim3(hkv), dim3(kReduceThreads), 0, s, sums,
+                     L.nblocks, hkv, n, lo, hi, sigma2);
   return hip_fail(hipGetLastError(), "pack launch");
 }
 

@@ -71,6 +71,51 @@ def test_pack_strided_keys(F, orc):
     np.testing.assert_array_equal(p.sigma2.cpu().numpy(), ref["sigma2"])
 
 
+def test_pack_unaligned_strides_and_offset(F, orc):
+    # rows that are not 16-byte aligned take the scalar kernels
+    for dtype in (torch.float16, torch.float32):
+        big = synth.keys(15, 0, 2100, 3, 131, dtype, 0, device=dev())
+        keys = big[:, :, 1:129]
+        assert keys.stride() == (393, 131, 1)
+        check_pack(F, orc, keys)
+
+
+def test_pack_cell_boundaries(F, orc):
+    """Keys on and next to the quantiser's cell edges: the codes of values
+    whose quotient (x - lo) / delta is an integer, or one ulp away from it,
+    are decided by the correctly rounded divide."""
+    n = 4096
+    keys = synth.keys(16, 0, n, 2, 128, torch.float32, 0, device=dev())
+    grid = torch.arange(n, device=dev(), dtype=torch.float32) % 65 * 0.25  # lo 0, hi 16: delta 1
+    keys[:, 0, 0] = grid
+    keys[:, 0, 1] = torch.nextafter(grid, torch.full_like(grid, 100.0))
+    keys[:, 0, 2] = torch.nextafter(grid, torch.full_like(grid, -100.0))
+    keys[0, 0, 1:3] = 0.0
+    keys[1, 0, 1:3] = 16.0
+    keys[:, 1, 3] = torch.arange(n, device=dev(), dtype=torch.float32) % 17 * 0.1 - 0.7
+    keys[:, 1, 4] = torch.arange(n, device=dev(), dtype=torch.float32) % 33 * (1.0 / 3.0)
+    check_pack(F, orc, keys)
+
+
+def test_pack_every_fp16_value(F, orc):
+    """Each channel holds every finite fp16 value of its own range
+    [-lim*(1 + c%3), lim] (lim a power of two that varies with the channel),
+    shuffled and repeated; bit-exact against the oracle."""
+    bits = torch.arange(65536, dtype=torch.int32)
+    vals = bits.to(torch.int16).view(torch.float16)
+    vals = vals[torch.isfinite(vals)]
+    g = torch.Generator().manual_seed(17)
+    cols = []
+    for c in range(128):
+        lim = float(2.0 ** (c % 17 - 8))
+        v = vals[(vals.float() >= -lim * (1 + c % 3)) & (vals.float() <= lim)]
+        v = v[torch.randperm(v.numel(), generator=g)]
+        reps = -(-vals.numel() // v.numel())
+        cols.append(v.repeat(reps)[:vals.numel()])
+    keys = torch.stack(cols, dim=1).view(vals.numel(), 1, 128).to(dev())
+    check_pack(F, orc, keys)
+
+
 def test_pack_degenerate_channels(F, orc):
     n = 5000
     keys = synth.keys(13, 0, n, 2, 128, torch.float32, 0, device=dev())
