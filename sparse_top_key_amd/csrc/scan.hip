@@ -36,6 +36,7 @@ namespace fathom {
 namespace {
 
 constexpr int kScanThreads = 256;
+constexpr int kMinSetupThreads = 256;             // smallest block building a slot table
 constexpr int kMaxSlots = kD * kPlanes;           // (channel, depth) pairs
 constexpr int kMaxGroups = kMaxSlots / 8;
 constexpr int kMaxGH = 4;                          // heads per launch chunk
@@ -182,72 +183,132 @@ struct SlotTable {
   float gam[kMaxSlots][GH];      // gamma per slot and head (0: head does not use it)
   uint8_t gmask[kMaxGroups];     // heads using any slot of an 8-slot group
   float C[GH];                   // C_h = sum_c q_hc (lo_c + delta_c 2^(3 - t_hc))
+  uint32_t gmax[GH];             // bits of max |gamma| per head (non-negative floats)
   int nslots;
 };
 
 // Set-up-only storage; the matrix-core kernel overlays it on its code table.
+constexpr int kCandWaves = kD * 4 / 64;  // (channel, depth) candidates in waves of 64
 template <int GH>
 struct SlotScratch {
-  double c[GH][kD];
-  int32_t key[kMaxSlots];
+  float q[GH][kD];
+  float delta[kD];
   uint8_t t[GH][kD];
+  double cpart[2][GH];           // C_h halves (channels 0..63, 64..127)
+  int wcnt[kCandWaves][16];      // slots of each membership class per candidate wave
+  int wpre[kCandWaves][16];      // ... in the earlier candidate waves
+  int cbase[16];                 // first rank of each class
 };
 
+// Rank of a membership set (bit j: head j uses the slot) in the slot order:
+// more heads first, then by the set's value (15 marks "no slot").
+__device__ __forceinline__ int memb_class(int memb) {
+  // nibble m = class of set m: 15; 7 11 13 14; 3 5 6 9 10 12; 1 2 4 8; none
+  constexpr uint64_t kClass = 0x043A298E176D5CBFull;
+  return (int)((kClass >> (4 * memb)) & 15u);
+}
+
+// The slot table of one (session, kv head) and the GH query heads from
+// head_base.  Every step is parallel: per-channel terms in registers, C_h by
+// wave shuffles in a fixed fp64 order, slot ranks by counting ballots per
+// membership class, the per-head max |gamma| by LDS atomics.
 template <int GH>
 __device__ void build_slot_table(SlotTable<GH> &T, SlotScratch<GH> &X, KScanSess &S, int g,
                                  int head_base) {
   const int tid = threadIdx.x;
-  if (tid == 0) T.nslots = 0;
+  const int lane = tid & 63;
   if (tid < kD) {
     const int c = tid;
     const float lo = S.lo[g * kD + c];
-    const float delta = __fmul_rn(__fsub_rn(S.hi[g * kD + c], lo), 0.0625f);
+    const float hi = S.hi[g * kD + c];
+    int t[GH];
+    float q[GH];
 #pragma unroll
     for (int j = 0; j < GH; ++j) {
-      const int t = S.plan[(int64_t)(head_base + j) * kD + c];
-      X.t[j][c] = (uint8_t)t;
-      // C_h term q * (lo + delta * 2^(3-t)) in fp64 (exact operands)
-      const double mid = (double)lo + (double)delta * (double)(1 << (4 - t)) * 0.5;
-      X.c[j][c] = (double)S.q[(int64_t)(head_base + j) * kD + c] * mid;
+      t[j] = S.plan[(int64_t)(head_base + j) * kD + c];
+      q[j] = S.q[(int64_t)(head_base + j) * kD + c];
+    }
+    const float delta = __fmul_rn(__fsub_rn(hi, lo), 0.0625f);
+    X.delta[c] = delta;
+#pragma unroll
+    for (int j = 0; j < GH; ++j) {
+      X.t[j][c] = (uint8_t)t[j];
+      X.q[j][c] = q[j];
+      // C_h term q * (lo + delta * 2^(3-t)) in fp64 (exact operands), summed
+      // over the 64 channels of the wave by a butterfly
+      const double mid = (double)lo + (double)delta * (double)(1 << (4 - t[j])) * 0.5;
+      double v = (double)q[j] * mid;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) v = __dadd_rn(v, __shfl_xor(v, off));
+      if (lane == 0) X.cpart[tid >> 6][j] = v;
     }
   }
+  if (tid < GH) T.gmax[tid] = 0u;
   __syncthreads();
-  for (int e = tid; e < kD * 4; e += blockDim.x) {
+  if (tid < GH) T.C[tid] = (float)__dadd_rn(X.cpart[0][tid], X.cpart[1][tid]);
+  // ---- candidates (channel, depth) = e: membership class, counts per wave
+  constexpr int kIters = kD * 4 / kMinSetupThreads;
+  int memb_e[kIters], cls_e[kIters], pre_e[kIters];
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int e = tid + it * blockDim.x;
+    memb_e[it] = 0;
+    cls_e[it] = 15;
+    pre_e[it] = 0;
+    if (e >= kD * 4) continue;  // blocks of more than kD*4 threads
     const int c = e >> 2, dep = (e & 3) + 1;
     int memb = 0;
 #pragma unroll
     for (int j = 0; j < GH; ++j) memb |= (X.t[j][c] == dep) << j;
-    if (memb) {
-      const int key = ((15 - __popc(memb)) << 16) | (memb << 11) | (c << 2) | (dep - 1);
-      X.key[atomicAdd(&T.nslots, 1)] = key;
-    }
-  }
-  // fp64 reduction of C_h (fixed tree order)
-  for (int stride = kD / 2; stride > 0; stride >>= 1) {
-    __syncthreads();
-    if (tid < stride) {
+    const int k = memb_class(memb);
+    const uint64_t lt = (1ull << lane) - 1ull;
 #pragma unroll
-      for (int j = 0; j < GH; ++j) X.c[j][tid] += X.c[j][tid + stride];
+    for (int kk = 0; kk < 15; ++kk) {
+      const uint64_t m = __ballot(k == kk);
+      if (k == kk) pre_e[it] = __popcll(m & lt);
+      if (lane == 0) X.wcnt[e >> 6][kk] = __popcll(m);
     }
+    memb_e[it] = memb;
+    cls_e[it] = k;
   }
   __syncthreads();
-  if (tid < GH) T.C[tid] = (float)X.c[tid][0];
+  // class bases and per-wave prefixes (16 lanes of wave 0)
+  if (tid < 16) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < kCandWaves; ++w) {
+      const int cnt = tid < 15 ? X.wcnt[w][tid] : 0;
+      X.wpre[w][tid] = run;
+      run += cnt;
+    }
+    // exclusive scan of the class totals over the 16 lanes
+    int incl = run;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int o = __shfl_up(incl, off, 16);
+      if (tid >= off) incl += o;
+    }
+    X.cbase[tid] = incl - run;
+    if (tid == 15) T.nslots = incl;
+  }
+  __syncthreads();
   const int nslots = T.nslots;
   const int ngroups = (nslots + 7) >> 3;
-  for (int e = tid; e < nslots; e += blockDim.x) {
-    const int key = X.key[e];
-    int rank = 0;
-    for (int j = 0; j < nslots; ++j) rank += X.key[j] < key;
-    const int c = (key >> 2) & 127, dep = (key & 3) + 1;
-    const int memb = (key >> 11) & 31;
-    T.desc[rank] = (int16_t)((c << 3) | dep);
-    const float lo = S.lo[g * kD + c];
-    const float delta = __fmul_rn(__fsub_rn(S.hi[g * kD + c], lo), 0.0625f);
 #pragma unroll
-    for (int j = 0; j < GH; ++j)
-      T.gam[rank][j] = ((memb >> j) & 1)
-                           ? __fmul_rn(S.q[(int64_t)(head_base + j) * kD + c], delta)
-                           : 0.0f;
+  for (int it = 0; it < kIters; ++it) {
+    const int e = tid + it * blockDim.x;
+    const int k = cls_e[it];
+    if (e >= kD * 4 || k == 15) continue;
+    const int c = e >> 2, dep = (e & 3) + 1;
+    const int rank = X.cbase[k] + X.wpre[e >> 6][k] + pre_e[it];
+    T.desc[rank] = (int16_t)((c << 3) | dep);
+    const float delta = X.delta[c];
+#pragma unroll
+    for (int j = 0; j < GH; ++j) {
+      const float gm = ((memb_e[it] >> j) & 1) ? __fmul_rn(X.q[j][c], delta) : 0.0f;
+      T.gam[rank][j] = gm;
+      atomicMax(&T.gmax[j], __float_as_uint(fabsf(gm)));
+    }
   }
   for (int e = nslots + tid; e < ngroups * 8; e += blockDim.x) {
     T.desc[e] = 0;
@@ -430,7 +491,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
 // (16 blocks of 16 keys); its lanes end with 4 consecutive keys of one head,
 // written as one 16-byte store.  Wide loads matter: with 4-byte lanes the
 // memory pipeline, not HBM, limits the read rate at this occupancy.
-constexpr int kMThreads = 512;
+constexpr int kMThreads = 1024;                      // two halves of 8 waves
 constexpr int kMTileKeys = 2048;
 constexpr int kPassGroups = 8;                        // 8 groups x 8 slots = K 64
 constexpr int kMaxPasses = kMaxGroups / kPassGroups;  // 8
@@ -468,22 +529,22 @@ struct MfmaSetup {
 // META: the sessions carry a side stream (its bytes are prefetched with the
 // planes, which costs registers the other variants do not spend).
 template <int GH, int MODE, bool META>
-__global__ __launch_bounds__(kMThreads, 4) void scan_mfma_kernel(ScanArgs a) {
+__global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   const BlockWork bw = block_work(a);
   KScanSess &S = *bw.S;
   const int g = bw.g, head_base = bw.head_base;
   if (MODE == kScanLogits && S.redo && S.redo[g] == 0) return;  // kv head not flagged
   const int64_t n = S.n;
   const int64_t W = S.W;
-  __shared__ __align__(16) uint32_t s_codes[kPassGroups * kGroupPitch + 4];
-  static_assert(sizeof(MfmaSetup<GH>) <= sizeof(s_codes), "set-up overlay");
+  __shared__ __align__(16) uint32_t s_codes[2][kPassGroups * kGroupPitch + 4];  // per half
+  static_assert(sizeof(MfmaSetup<GH>) <= sizeof(s_codes[0]), "set-up overlay");
   __shared__ __align__(16) int32_t s_limbs[kMaxPasses][64][4];
   __shared__ __align__(16) int16_t s_desc[kMaxSlots];
   __shared__ float s_scale[kMaxGH], s_C[kMaxGH];
   __shared__ int s_exp[kMaxGH];
   __shared__ uint32_t s_segc[kMaxGH];  // candidates this block found per row
   __shared__ float s_tf[kMaxGH];       // float thresholds of the block's rows
-  MfmaSetup<GH> &U = *reinterpret_cast<MfmaSetup<GH> *>(s_codes);
+  MfmaSetup<GH> &U = *reinterpret_cast<MfmaSetup<GH> *>(s_codes[0]);
   SlotTable<GH> &T = U.T;
   build_slot_table<GH>(T, U.X, S, g, head_base);
   const int tid = threadIdx.x;
@@ -494,8 +555,7 @@ __global__ __launch_bounds__(kMThreads, 4) void scan_mfma_kernel(ScanArgs a) {
 
   // fixed-point exponent per head
   if (tid < GH) {
-    float m = 0.0f;
-    for (int sl = 0; sl < nslots; ++sl) m = fmaxf(m, fabsf(T.gam[sl][tid]));
+    const float m = __uint_as_float(T.gmax[tid]);
     int e = 0;
     if (m > 0.0f) frexpf(m, &e);
     s_exp[tid] = e;
@@ -530,7 +590,9 @@ __global__ __launch_bounds__(kMThreads, 4) void scan_mfma_kernel(ScanArgs a) {
   }
   __syncthreads();  // the code table is free from here on
 
-  const int wave = tid >> 6, lane = tid & 63;
+  // half = which of the block's two tiles of an item; wave = wave in the half
+  const int half = tid >> 9, wave = (tid >> 6) & 7, lane = tid & 63;
+  uint32_t *codes = s_codes[half];
   const int quarter = lane >> 4, m16 = lane & 15;
   const int hh = lane >> 4;  // head of this lane's results (MFMA row block)
   const float Ch = hh < GH ? s_C[hh] : 0.0f;
@@ -564,9 +626,12 @@ __global__ __launch_bounds__(kMThreads, 4) void scan_mfma_kernel(ScanArgs a) {
   };
   int ntiles = 0;
   while (ntiles < tiles_per_block && bw.tile0 + ntiles * bw.tile_step < nvtiles) ++ntiles;
-  const int nitems = ntiles * npasses;
+  // item i = (tile pair i / npasses, pass): half h takes tile 2 * pair + h
+  const int nitems = (ntiles + 1) / 2 * npasses;
   auto issue = [&](int item, uint32_t(&x)[32]) {
-    const int tt = item / npasses, p = item - tt * npasses;
+    const int ti = item / npasses, p = item - ti * npasses;
+    const int tt = 2 * ti + half;
+    if (tt >= ntiles) return;    // odd tile count: no tile for this half
     const int grp = kPassGroups * p + wave;
     if (grp >= ngroups) return;  // empty group: nothing to read
     const uint32_t tile_off =
@@ -598,14 +663,16 @@ __global__ __launch_bounds__(kMThreads, 4) void scan_mfma_kernel(ScanArgs a) {
   if (nitems > 0) issue(0, xn);
   float s[16];
   for (int it = 0; it < nitems; ++it) {
-    const int tt = it / npasses, p = it - tt * npasses;
+    const int ti = it / npasses, p = it - ti * npasses;
+    const int tt = 2 * ti + half;
+    const bool has_tile = tt < ntiles;  // half-uniform
     const int vt = bw.tile0 + tt * bw.tile_step;
     const int64_t tile_key0 = (int64_t)real_tile(vt) * kMTileKeys;
-    const bool has_group = kPassGroups * p + wave < ngroups;
+    const bool has_group = has_tile && kPassGroups * p + wave < ngroups;
     // side-stream bytes of this tile, loaded before the next item's planes so
     // that waiting for them does not wait for those
     uint32_t mw[4] = {0u, 0u, 0u, 0u};
-    if (META && meta_words && p == npasses - 1 && hh < GH) {
+    if (META && meta_words && has_tile && p == npasses - 1 && hh < GH) {
       const int64_t kb0 = tile_key0 + 256 * wave + 4 * (lane & 15);
 #pragma unroll
       for (int beta = 0; beta < 4; ++beta)
@@ -641,16 +708,17 @@ __global__ __launch_bounds__(kMThreads, 4) void scan_mfma_kernel(ScanArgs a) {
       // tile, w = 4*m16 + quarter; afterwards x[t] = the 8 codes of key 32w+t
       transpose32_perm(x);
       const int w = 4 * m16 + quarter;
-      uint32_t *dst = &s_codes[code_index(wave, 32 * w)];
+      uint32_t *dst = &codes[code_index(wave, 32 * w)];
 #pragma unroll
       for (int t = 0; t < 32; ++t) dst[t] = x[t];
     }
     __syncthreads();
     // ---- MFMA phase: 256 keys of this wave; block b = 4*beta + e covers keys
     // 64*beta + 4*n + e (n = lane % 16)
+    const int j = lane >> 4, nn = lane & 15;
+    if (has_tile) {
     const int4 av = *reinterpret_cast<const int4 *>(&s_limbs[p][lane][0]);
     const v4i A = v4i{av.x, av.y, av.z, av.w};
-    const int j = lane >> 4, nn = lane & 15;
     if (p == 0) {
 #pragma unroll
       for (int b = 0; b < 16; ++b) s[b] = Ch;
@@ -661,8 +729,8 @@ __global__ __launch_bounds__(kMThreads, 4) void scan_mfma_kernel(ScanArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int key = 256 * wave + 64 * beta + 4 * nn + e;
-        const uint32_t w0 = s_codes[code_index(2 * j, key)];
-        const uint32_t w1 = s_codes[code_index(2 * j + 1, key)];
+        const uint32_t w0 = codes[code_index(2 * j, key)];
+        const uint32_t w1 = codes[code_index(2 * j + 1, key)];
         const v4i B = v4i{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu),
                           (int)(w1 & 0x0F0F0F0Fu), (int)((w1 >> 4) & 0x0F0F0F0Fu)};
         acc[e] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
@@ -676,10 +744,11 @@ __global__ __launch_bounds__(kMThreads, 4) void scan_mfma_kernel(ScanArgs a) {
         s[4 * beta + e] = __fmaf_rn(t, scale, s[4 * beta + e]);
       }
     }
+    }  // has_tile
     __syncthreads();
 
     // ---- epilogue: 4 consecutive keys of head hh per beta
-    if (p == npasses - 1) {
+    if (has_tile && p == npasses - 1) {
       const int64_t kb = tile_key0 + 256 * wave + 4 * nn;  // + 64*beta + e
       if (META && meta_words && hh < GH) {
 #pragma unroll
