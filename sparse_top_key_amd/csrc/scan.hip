@@ -661,18 +661,30 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
 #pragma unroll
   for (int r = 0; r < 32; ++r) xn[r] = 0;
   if (nitems > 0) issue(0, xn);
+  // Ping-pong: the item sequence of half 1 runs one step behind half 0, and
+  // a step (between two barriers) is either the T phase of an item (regroup,
+  // next item's loads, transpose into the half's code table) or its M phase
+  // (matrix cores over the code table, then the epilogue).  While one half
+  // transposes, the other multiplies.
   float s[16];
-  for (int it = 0; it < nitems; ++it) {
+  uint32_t mw[4] = {0u, 0u, 0u, 0u};  // side-stream bytes, T phase -> M phase
+  const int nsteps = nitems > 0 ? 2 * nitems + 1 : 0;
+  for (int k = 0; k < nsteps; ++k) {
+    const int q = k - half;
+    if (q >= 0 && q < 2 * nitems) {
+    const int it = q >> 1;
     const int ti = it / npasses, p = it - ti * npasses;
     const int tt = 2 * ti + half;
     const bool has_tile = tt < ntiles;  // half-uniform
     const int vt = bw.tile0 + tt * bw.tile_step;
     const int64_t tile_key0 = (int64_t)real_tile(vt) * kMTileKeys;
     const bool has_group = has_tile && kPassGroups * p + wave < ngroups;
+    if ((q & 1) == 0) {
+    // ==== T phase
     // side-stream bytes of this tile, loaded before the next item's planes so
     // that waiting for them does not wait for those
-    uint32_t mw[4] = {0u, 0u, 0u, 0u};
     if (META && meta_words && has_tile && p == npasses - 1 && hh < GH) {
+      mw[0] = mw[1] = mw[2] = mw[3] = 0u;
       const int64_t kb0 = tile_key0 + 256 * wave + 4 * (lane & 15);
 #pragma unroll
       for (int beta = 0; beta < 4; ++beta)
@@ -712,7 +724,8 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
 #pragma unroll
       for (int t = 0; t < 32; ++t) dst[t] = x[t];
     }
-    __syncthreads();
+    } else {
+    // ==== M phase
     // ---- MFMA phase: 256 keys of this wave; block b = 4*beta + e covers keys
     // 64*beta + 4*n + e (n = lane % 16)
     const int j = lane >> 4, nn = lane & 15;
@@ -745,7 +758,6 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
       }
     }
     }  // has_tile
-    __syncthreads();
 
     // ---- epilogue: 4 consecutive keys of head hh per beta
     if (has_tile && p == npasses - 1) {
@@ -848,6 +860,9 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
         }
       }
     }
+    }  // M phase
+    }  // q in range
+    __syncthreads();
   }
   if constexpr (MODE == kScanCand || MODE == kScanCandGroup) {
     // every block reports its count (above seg_cap: the segment overflowed)
