@@ -86,7 +86,15 @@ struct ScanSession {
   uint64_t *cand;         // [rows][kFusedCap] candidate segments
   uint32_t *seg_cnt;      // [rows][kMaxSeg] candidates found by each block
   const uint32_t *redo;   // [hkv]: recompute only the kv heads flagged here
+  uint8_t *table;         // slot tables of the session's kv heads, or null
+  int32_t table_mode;     // ScanTable: what the scan does with them
 };
+// Slot tables (matrix-core scan): built in each block (kTableNone), built and
+// also stored for later scans of the same call (kTableWrite), or loaded from
+// what an earlier scan of the call stored (kTableRead).
+enum ScanTable { kTableNone = 0, kTableWrite = 1, kTableRead = 2 };
+// Bytes of the slot tables of one session (all its kv heads and head chunks).
+int64_t scan_table_bytes(int32_t hkv, int32_t hq);
 // What a scan writes: every logit (into logits; only the flagged kv heads when
 // redo is set), the logits of the sampled tiles (into sample), or the
 // (score key, index) words of the keys whose score key reaches the row's

@@ -62,6 +62,8 @@ struct ScanSess {
   uint32_t *seg_cnt;
   const uint32_t *redo;
   int32_t seg_cap;         // candidate words per (row, block) segment
+  uint8_t *table;          // slot records of the session, or null
+  int32_t table_mode;      // ScanTable
 };
 
 struct ScanArgs {
@@ -332,6 +334,7 @@ __device__ void build_slot_table(SlotTable<GH> &T, SlotScratch<GH> &X, KScanSess
 struct BlockWork {
   KScanSess *S;
   int g, tile0, tile_step, head_base;
+  int rec;  // slot record of (kv head, head chunk) in the session's tables
 };
 
 __device__ __forceinline__ BlockWork block_work(const ScanArgs &) {
@@ -348,6 +351,7 @@ __device__ __forceinline__ BlockWork block_work(const ScanArgs &) {
   w.tile0 = local / a.hkv;
   w.tile_step = w.S->blocks_per_head;
   w.head_base = w.g * a.group + a.head0;
+  w.rec = w.g * ((a.group + kMaxGH - 1) / kMaxGH) + a.head0 / kMaxGH;
   return w;
 }
 
@@ -526,6 +530,15 @@ struct MfmaSetup {
   SlotScratch<GH> X;
 };
 
+// What the main loop of the matrix-core scan needs from its set-up, as one
+// scan of a fused call stores it for the later ones.
+struct alignas(16) SlotRecord {
+  int32_t nslots, pad[3];
+  float C[kMaxGH], scale[kMaxGH];
+  int16_t desc[kMaxSlots];
+  int32_t limbs[kMaxPasses][64][4];
+};
+
 // META: the sessions carry a side stream (its bytes are prefetched with the
 // planes, which costs registers the other variants do not spend).
 template <int GH, int MODE, bool META>
@@ -544,51 +557,87 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   __shared__ int s_exp[kMaxGH];
   __shared__ uint32_t s_segc[kMaxGH];  // candidates this block found per row
   __shared__ float s_tf[kMaxGH];       // float thresholds of the block's rows
-  MfmaSetup<GH> &U = *reinterpret_cast<MfmaSetup<GH> *>(s_codes[0]);
-  SlotTable<GH> &T = U.T;
-  build_slot_table<GH>(T, U.X, S, g, head_base);
+  __shared__ int s_nslots;
   const int tid = threadIdx.x;
-  const int nslots = T.nslots;
-  const int ngroups = (nslots + 7) >> 3;
-  // at least one pass, so that a plan reading nothing still writes C_h
-  const int npasses = max(1, (ngroups + kPassGroups - 1) / kPassGroups);
-
-  // fixed-point exponent per head
+  SlotRecord *rec = S.table ? reinterpret_cast<SlotRecord *>(S.table) + bw.rec : nullptr;
+  if (S.table_mode == kTableRead) {
+    // the set-up an earlier scan of this call stored
+    if (tid == 0) s_nslots = rec->nslots;
+    if (tid < GH) {
+      s_scale[tid] = rec->scale[tid];
+      s_C[tid] = rec->C[tid];
+    }
+    constexpr int kDescVec = sizeof(rec->desc) / 16, kLimbVec = sizeof(rec->limbs) / 16;
+    if (tid < kDescVec)
+      reinterpret_cast<int4 *>(s_desc)[tid] = reinterpret_cast<const int4 *>(rec->desc)[tid];
+    for (int e = tid; e < kLimbVec; e += kMThreads)
+      reinterpret_cast<int4 *>(&s_limbs[0][0][0])[e] =
+          reinterpret_cast<const int4 *>(&rec->limbs[0][0][0])[e];
+  } else {
+    MfmaSetup<GH> &U = *reinterpret_cast<MfmaSetup<GH> *>(s_codes[0]);
+    SlotTable<GH> &T = U.T;
+    build_slot_table<GH>(T, U.X, S, g, head_base);
+    const int nslots = T.nslots;
+    const int ngroups = (nslots + 7) >> 3;
+    const int npasses = max(1, (ngroups + kPassGroups - 1) / kPassGroups);
+    // fixed-point exponent per head
+    if (tid < GH) {
+      const float m = __uint_as_float(T.gmax[tid]);
+      int e = 0;
+      if (m > 0.0f) frexpf(m, &e);
+      s_exp[tid] = e;
+      s_scale[tid] = ldexpf(1.0f, e - 30);
+      s_C[tid] = T.C[tid];
+    }
+    if (tid == 0) s_nslots = nslots;
+    for (int e = tid; e < npasses * kPassGroups * 8; e += kMThreads)
+      s_desc[e] = e < nslots ? T.desc[e] : (int16_t)0;
+    __syncthreads();
+    // A operands: lane l = row (head (l%16)/4, limb (l%16)%4), slot chunk l/16;
+    // dword d, byte b <-> slot 64p + 16(l/16) + 8(d/2) + 2b + (d%2), the order
+    // in which the code words are split into bytes below.
+    uint8_t *limb_bytes = reinterpret_cast<uint8_t *>(&s_limbs[0][0][0]);
+    for (int idx = tid; idx < npasses * 64 * 16; idx += kMThreads) {
+      const int p = idx >> 10, l = (idx >> 4) & 63, d = (idx >> 2) & 3, b = idx & 3;
+      const int r = l & 15, h = r >> 2, limb = r & 3, j = l >> 4;
+      const int slot = 64 * p + 16 * j + 8 * (d >> 1) + 2 * b + (d & 1);
+      int v = 0;
+      if (h < GH && slot < nslots) {
+        int G = (int)rintf(ldexpf(T.gam[slot][h], 30 - s_exp[h]));
+        for (int i = 0; i < limb; ++i) {
+          const int dg = ((G + 128) & 255) - 128;
+          G = (G - dg) >> 8;
+        }
+        v = ((G + 128) & 255) - 128;
+      }
+      limb_bytes[idx] = (uint8_t)(int8_t)v;
+    }
+  }
   if (tid < GH) {
-    const float m = __uint_as_float(T.gmax[tid]);
-    int e = 0;
-    if (m > 0.0f) frexpf(m, &e);
-    s_exp[tid] = e;
-    s_scale[tid] = ldexpf(1.0f, e - 30);
-    s_C[tid] = T.C[tid];
     s_segc[tid] = 0;
     // thresholds are read here, before any plane load is in flight
     if constexpr (MODE == kScanCand) s_tf[tid] = key_threshold(S.thr[head_base + tid]);
     if constexpr (MODE == kScanCandGroup) s_tf[tid] = key_threshold(S.thr[g]);
   }
-  for (int e = tid; e < npasses * kPassGroups * 8; e += kMThreads)
-    s_desc[e] = e < nslots ? T.desc[e] : (int16_t)0;
-  __syncthreads();
-  // A operands: lane l = row (head (l%16)/4, limb (l%16)%4), slot chunk l/16;
-  // dword d, byte b <-> slot 64p + 16(l/16) + 8(d/2) + 2b + (d%2), the order
-  // in which the code words are split into bytes below.
-  uint8_t *limb_bytes = reinterpret_cast<uint8_t *>(&s_limbs[0][0][0]);
-  for (int idx = tid; idx < npasses * 64 * 16; idx += kMThreads) {
-    const int p = idx >> 10, l = (idx >> 4) & 63, d = (idx >> 2) & 3, b = idx & 3;
-    const int r = l & 15, h = r >> 2, limb = r & 3, j = l >> 4;
-    const int slot = 64 * p + 16 * j + 8 * (d >> 1) + 2 * b + (d & 1);
-    int v = 0;
-    if (h < GH && slot < nslots) {
-      int G = (int)rintf(ldexpf(T.gam[slot][h], 30 - s_exp[h]));
-      for (int i = 0; i < limb; ++i) {
-        const int dg = ((G + 128) & 255) - 128;
-        G = (G - dg) >> 8;
-      }
-      v = ((G + 128) & 255) - 128;
-    }
-    limb_bytes[idx] = (uint8_t)(int8_t)v;
-  }
   __syncthreads();  // the code table is free from here on
+  const int nslots = s_nslots;
+  const int ngroups = (nslots + 7) >> 3;
+  // at least one pass, so that a plan reading nothing still writes C_h
+  const int npasses = max(1, (ngroups + kPassGroups - 1) / kPassGroups);
+  if (S.table_mode == kTableWrite && bw.tile0 == 0) {
+    // for the later scans of this call (one block per kv head stores it)
+    if (tid == 0) rec->nslots = nslots;
+    if (tid < GH) {
+      rec->scale[tid] = s_scale[tid];
+      rec->C[tid] = s_C[tid];
+    }
+    constexpr int kDescVec = sizeof(rec->desc) / 16;
+    if (tid < kDescVec)
+      reinterpret_cast<int4 *>(rec->desc)[tid] = reinterpret_cast<const int4 *>(s_desc)[tid];
+    for (int e = tid; e < npasses * 64; e += kMThreads)
+      reinterpret_cast<int4 *>(&rec->limbs[0][0][0])[e] =
+          reinterpret_cast<const int4 *>(&s_limbs[0][0][0])[e];
+  }
 
   // half = which of the block's two tiles of an item; wave = wave in the half
   const int half = tid >> 9, wave = (tid >> 6) & 7, lane = tid & 63;
@@ -975,6 +1024,11 @@ constexpr int64_t kMfmaMaxKeys = (int64_t)1 << 25;
 
 }  // namespace
 
+int64_t scan_table_bytes(int32_t hkv, int32_t hq) {
+  const int32_t group = hq / hkv;
+  return (int64_t)hkv * ((group + kMaxGH - 1) / kMaxGH) * (int64_t)sizeof(SlotRecord);
+}
+
 bool scan_can_fuse(const ScanSession *sess, int32_t n_sess) {
   bool any_host = false;
   if (!planes_residency(sess, n_sess, &any_host)) return false;
@@ -1067,6 +1121,8 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_
         o.cand = in.cand;
         o.seg_cnt = in.seg_cnt;
         o.redo = in.redo;
+        o.table = fp32_path ? nullptr : in.table;
+        o.table_mode = fp32_path || !in.table ? kTableNone : in.table_mode;
         const int64_t tiles = visited(in.n);
         o.nvtiles = (int32_t)tiles;
         o.ntiles = (int32_t)((in.n + tile_keys - 1) / tile_keys);

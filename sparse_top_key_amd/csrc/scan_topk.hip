@@ -48,7 +48,7 @@ int64_t sampled_keys(int64_t n) {
 }
 
 struct Layout {
-  int64_t topk_off, seg_off, fcand_off, sample_off, logits_off, total;
+  int64_t topk_off, seg_off, fcand_off, sample_off, table_off, table_bytes, logits_off, total;
   int64_t out_rows, redo_slots;
 };
 
@@ -60,8 +60,10 @@ Layout layout(const int64_t *n, int32_t n_sess, int32_t hkv, int32_t hq, int32_t
   L.seg_off = align256(topk_ws_bytes(L.out_rows, L.redo_slots));
   L.fcand_off = L.seg_off + align256(L.out_rows * kMaxSeg * (int64_t)sizeof(uint32_t));
   L.sample_off = L.fcand_off + align256(L.out_rows * kFusedCap * (int64_t)sizeof(uint64_t));
-  L.logits_off =
+  L.table_off =
       L.sample_off + align256((int64_t)n_sess * hq * kSampleKeys * (int64_t)sizeof(float));
+  L.table_bytes = align256(scan_table_bytes(hkv, hq));
+  L.logits_off = L.table_off + (int64_t)n_sess * L.table_bytes;
   int64_t logits = 0;
   for (int32_t s = 0; s < n_sess; ++s)
     logits += align256((int64_t)hq * ld_pad(n[s]) * (int64_t)sizeof(float));
@@ -105,6 +107,8 @@ int32_t launch_scan_topk(const ScanSession *in, int32_t *const *idx, float *cons
     c.cand = tw.fcand + row0 * kFusedCap;
     c.seg_cnt = tw.seg_cnt + row0 * kMaxSeg;
     c.redo = nullptr;
+    c.table = reinterpret_cast<uint8_t *>(w + L.table_off + (int64_t)j * L.table_bytes);
+    c.table_mode = kTableRead;
     fin[j] = TopkSession{c.logits, in[j].n, c.ld, idx[j], vals[j], in[j].n, 0};
     thr[j] = TopkSession{c.sample, sampled_keys(in[j].n), kSampleKeys, idx[j], vals[j],
                          in[j].n, 0};
@@ -114,20 +118,25 @@ int32_t launch_scan_topk(const ScanSession *in, int32_t *const *idx, float *cons
       ++m;
     }
   }
-  ScanSession plain[FATHOM_MAX_SESSIONS];
+  // plain: no recompute flags; the sample scan stores the slot tables, the
+  // candidate and recompute scans load them
+  ScanSession plain[FATHOM_MAX_SESSIONS], first[FATHOM_MAX_SESSIONS];
   for (int32_t j = 0; j < m; ++j) {
     plain[j] = sc[j];
     plain[j].redo = nullptr;
+    first[j] = plain[j];
+    first[j].table_mode = kTableWrite;
   }
 
   const bool group_ok = group == 1 || (group == hq / hkv && group <= 4);
   if (!group_ok || (m > 0 && !scan_can_fuse(sc, m))) {
+    for (int32_t j = 0; j < m; ++j) plain[j].table_mode = kTableNone;
     if (m > 0)
       if (int32_t rc = launch_scan(plain, m, hkv, hq, s)) return rc;
     return launch_topk(fin, n_sess, rows_per_sess, group, k, tw, s, kTopkAll);
   }
   if (m > 0)
-    if (int32_t rc = launch_scan(plain, m, hkv, hq, s, kScanSample)) return rc;
+    if (int32_t rc = launch_scan(first, m, hkv, hq, s, kScanSample)) return rc;
   if (int32_t rc = launch_topk(thr, n_sess, rows_per_sess, group, k, tw, s, kTopkThreshold,
                                rows_per_kv, hkv))
     return rc;
