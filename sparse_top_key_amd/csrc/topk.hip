@@ -636,17 +636,27 @@ __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
     if (a.stage == kTopkFusedFinal) {
       const int nseg = S.nseg, seg_cap = kFusedCap / (nseg > 0 ? nseg : 1);
       const uint64_t *fc = a.fcand + (int64_t)o * kFusedCap;
-      for (int j = threadIdx.x; j < m; j += kBig) {
-        // segment holding candidate j: the last b with s_off[b] <= j
-        int lo = 0, hi = nseg - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (s_off[mid] <= j)
-            lo = mid;
-          else
-            hi = mid - 1;
+      // kBig / nseg threads per segment; each has 8 loads in flight before it
+      // stores (segments hold at most seg_cap words: no overflow here)
+      const int tps = kBig / (nseg > 0 ? nseg : 1);
+      const int sg = threadIdx.x / tps, sub = threadIdx.x % tps;
+      if (sg < nseg) {
+        const int c = s_off[sg + 1] - s_off[sg];
+        const uint64_t *src = fc + (int64_t)sg * seg_cap;
+        uint64_t *dst = s + s_off[sg];
+        for (int b0 = sub; b0 < c; b0 += 8 * tps) {
+          uint64_t v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = b0 + u * tps;
+            v[u] = src[i < c ? i : c - 1];
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = b0 + u * tps;
+            if (i < c) dst[i] = v[u];
+          }
         }
-        s[j] = fc[(int64_t)lo * seg_cap + (j - s_off[lo])];
       }
     } else {
       const uint64_t *cand = a.cand + (int64_t)o * kCandCap;
