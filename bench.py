@@ -78,11 +78,14 @@ def union_plane_bytes(plan, hkv, n):
     return sum(ub) * n // 8, ub, hist
 
 
-def run_steps(layers, w, ws, steps, mode, fixed=False, fused=False):
+def run_steps(layers, w, ws, steps, mode, fixed=False, fused=False, per_call=True):
     """mode: 'host' or 'hbm'.  fused: fathom_scan_topk in place of fathom_scan
-    then fathom_topk (ws must then be its workspace).  Returns per-step totals
-    and per-call times (ms)."""
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    then fathom_topk (ws must then be its workspace).  per_call: events around
+    every call (for the per-call times); otherwise none, since an event
+    recorded between two calls stalls the stream for a few microseconds.
+    Returns the per-step event lists (empty lists when per_call is off)."""
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] if per_call else []
+          for _ in range(steps)]
     for s in range(steps):
         L = layers[s % len(layers)]
         planes = L.host if mode == "host" else L.planes
@@ -90,21 +93,26 @@ def run_steps(layers, w, ws, steps, mode, fixed=False, fused=False):
         if fixed:
             meta = L.meta_host if mode == "host" else L.meta
         e = ev[s]
-        e[0].record()
+        if per_call:
+            e[0].record()
         if fixed:                                     # query-only plan of the baselines
             plan = fathom.plan_fixed(L.q, 32, out=L.plan)
         else:
             plan = fathom.plan(L.q, L.sigma2, L.budget, out=L.plan)
-        e[1].record()
+        if per_call:
+            e[1].record()
         if fused:
             fathom.scan_topk(planes, L.lo, L.hi, L.n, L.q, plan, w.k, 1, meta, 0.0, ws=ws,
                              idx=L.idx, vals=L.vals)
-            e[2].record()
+            if per_call:
+                e[2].record()
         else:
             fathom.scan(planes, L.lo, L.hi, L.n, L.q, plan, meta, 0.0, out=L.logits)
-            e[2].record()
+            if per_call:
+                e[2].record()
             fathom.topk(L.logits, w.k, ws=ws, idx=L.idx, vals=L.vals)
-        e[3].record()
+        if per_call:
+            e[3].record()
     return ev
 
 
@@ -113,21 +121,29 @@ def summarize(ev):
     plan = [a[0].elapsed_time(a[1]) for a in ev]
     scan = [a[1].elapsed_time(a[2]) for a in ev]
     topk = [a[2].elapsed_time(a[3]) for a in ev]
-    return dict(step_ms=float(np.mean(tot)), plan_ms=float(np.mean(plan)),
+    return dict(call_step_ms=float(np.mean(tot)), plan_ms=float(np.mean(plan)),
                 scan_ms=float(np.mean(scan)), topk_ms=float(np.mean(topk)),
                 scan_ms_p10=float(np.percentile(scan, 10)),
                 scan_ms_p90=float(np.percentile(scan, 90)))
 
 
 def timed(layers, w, ws, steps, warmup, mode, fixed=False, fused=False):
-    run_steps(layers, w, ws, warmup, mode, fixed, fused)
+    """Throughput: K steps between one pair of events (and synchronisations);
+    then the same K steps again with events around every call, for the
+    per-call times (the scan's is the one the rooflines use)."""
+    run_steps(layers, w, ws, warmup, mode, fixed, fused, per_call=False)
     torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    ev = run_steps(layers, w, ws, steps, mode, fixed, fused)
+    a.record()
+    run_steps(layers, w, ws, steps, mode, fixed, fused, per_call=False)
+    b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    r = summarize(ev)
-    r["wall_ms_per_step"] = wall * 1e3 / steps
+    r = {"step_ms": a.elapsed_time(b) / steps, "wall_ms_per_step": wall * 1e3 / steps}
+    ev = run_steps(layers, w, ws, steps, mode, fixed, fused, per_call=True)
+    torch.cuda.synchronize()
+    r.update(summarize(ev))
     return r
 
 
@@ -252,11 +268,16 @@ def bench_pack(dev, reps=5):
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / reps
+    # keys read once and planes written; the range over all n keys must be
+    # known before the first code, so a second read of the keys is inherent
     alg = keys.numel() * keys.element_size() + planes.numel() * 4
+    two_pass = alg + keys.numel() * keys.element_size()
     return {"workload": "pack one 1M-key layer (fp16 keys -> planes, lo, hi, sigma2)",
             "ms": round(ms, 3), "keys_per_s": round(w.n * w.hkv / (ms * 1e-3), 1),
             "algorithmic_bytes": alg, "achieved_GBps": round(alg / (ms * 1e-3) / 1e9, 1),
-            "frac_of_hbm_peak": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+            "frac_of_hbm_peak": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "two_pass_bytes": two_pass,
+            "two_pass_GBps": round(two_pass / (ms * 1e-3) / 1e9, 1)}
 
 
 def bench_layer_128k(dev, steps, warmup):
@@ -365,8 +386,10 @@ def bench_step36(dev, steps, warmup):
     idx = torch.empty((w.hq, w.k), dtype=torch.int32, device=dev)
     vals = torch.empty((w.hq, w.k), device=dev)
     ws = torch.empty(fathom.topk_workspace_bytes(w.hq, w.k), dtype=torch.uint8, device=dev)
+    fws = torch.empty(fathom.scan_topk_workspace_bytes([w.n], w.hkv, w.hq, 1, w.k),
+                      dtype=torch.uint8, device=dev)
     out = {"workload": "36 layers x 1M keys (18 GiB of planes), 32 query heads, k=2048"}
-    for mode in ("hbm", "host"):
+    for mode in ("hbm", "host", "hbm_fused"):
         for fixed in (False, True):
             def step():
                 for p, host, q, meta in layers:
@@ -374,6 +397,11 @@ def bench_step36(dev, steps, warmup):
                         fathom.plan_fixed(q, 32, out=plan)
                     else:
                         fathom.plan(q, p.sigma2, w.budget, out=plan)
+                    if mode == "hbm_fused":
+                        fathom.scan_topk(p.planes, p.lo, p.hi, w.n, q, plan, w.k, 1,
+                                         meta if fixed else None, 0.0, ws=fws, idx=idx,
+                                         vals=vals)
+                        continue
                     fathom.scan(host if mode == "host" else p.planes, p.lo, p.hi, w.n, q, plan,
                                 meta if fixed else None, 0.0, out=logits)
                     fathom.topk(logits, w.k, ws=ws, idx=idx, vals=vals)

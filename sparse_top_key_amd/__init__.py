@@ -83,9 +83,15 @@ def lib():
     return _lib
 
 
+_GPU_SEEN = False
+
+
 def _require_gpu(*ts: torch.Tensor):
-    if not torch.cuda.is_available():
-        raise FathomError("libfathom needs a ROCm GPU (none visible)")
+    global _GPU_SEEN
+    if not _GPU_SEEN:
+        if not torch.cuda.is_available():
+            raise FathomError("libfathom needs a ROCm GPU (none visible)")
+        _GPU_SEEN = True
     for t in ts:
         if t is not None and not (t.is_cuda or t.is_pinned()):
             raise FathomError("tensor must be on the GPU (or pinned host memory)")

@@ -88,6 +88,7 @@ struct ScanSession {
   const uint32_t *redo;   // [hkv]: recompute only the kv heads flagged here
   uint8_t *table;         // slot tables of the session's kv heads, or null
   int32_t table_mode;     // ScanTable: what the scan does with them
+  int32_t residency;      // planes: 0 unknown (queried), 1 device, 2 pinned host
 };
 // Slot tables (matrix-core scan): built in each block (kTableNone), built and
 // also stored for later scans of the same call (kTableWrite), or loaded from
@@ -112,6 +113,10 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv,
 // Whether launch_scan can run the sample and candidate modes on these
 // sessions (planes in device memory, at most 2^25 keys each).
 bool scan_can_fuse(const ScanSession *sess, int32_t n_sess);
+// Queries the residency of every session's planes once and records it in the
+// sessions (later launch_scan calls on them skip the query); false (error
+// set) if some are neither device nor pinned host memory.
+bool resolve_residency(ScanSession *sess, int32_t n_sess);
 int32_t launch_read_prefixes(const uint32_t *planes, int64_t n, int32_t hkv,
                              const uint8_t *plan, int32_t hq, uint8_t *out,
                              hipStream_t s);

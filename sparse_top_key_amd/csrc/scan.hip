@@ -1006,6 +1006,10 @@ int resident_blocks_per_cu(bool host, int GH, int mode, bool meta) {
 bool planes_residency(const ScanSession *sess, int32_t n_sess, bool *any_host) {
   *any_host = false;
   for (int32_t j = 0; j < n_sess; ++j) {
+    if (sess[j].residency != 0) {  // already resolved for this call
+      *any_host |= sess[j].residency == 2;
+      continue;
+    }
     hipPointerAttribute_t attr;
     const hipError_t e = hipPointerGetAttributes(&attr, sess[j].planes);
     if (e != hipSuccess) {
@@ -1029,6 +1033,29 @@ int64_t scan_table_bytes(int32_t hkv, int32_t hq) {
   return (int64_t)hkv * ((group + kMaxGH - 1) / kMaxGH) * (int64_t)sizeof(SlotRecord);
 }
 
+bool resolve_residency(ScanSession *sess, int32_t n_sess) {
+  for (int32_t j = 0; j < n_sess; ++j) {
+    bool host = false;
+    if (!planes_residency(&sess[j], 1, &host)) return false;
+    sess[j].residency = host ? 2 : 1;
+  }
+  return true;
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  int &c = cached[dev & 63];
+  if (c == 0) {
+    int ncu = 256;
+    (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    c = ncu > 0 ? ncu : 256;
+  }
+  return c;
+}
+
 bool scan_can_fuse(const ScanSession *sess, int32_t n_sess) {
   bool any_host = false;
   if (!planes_residency(sess, n_sess, &any_host)) return false;
@@ -1040,10 +1067,7 @@ bool scan_can_fuse(const ScanSession *sess, int32_t n_sess) {
 int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_t hq,
                     hipStream_t s, int32_t mode, int32_t *nseg_out, bool one_block_per_head) {
   const int32_t group = hq / hkv;
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  int ncu = 256;
-  (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  const int ncu = device_cus();
   bool any_host = false;
   if (!planes_residency(sess, n_sess, &any_host)) return FATHOM_ERR_INVALID_ARG;
   int64_t max_n = 0;

@@ -128,6 +128,9 @@ int32_t launch_scan_topk(const ScanSession *in, int32_t *const *idx, float *cons
     first[j].table_mode = kTableWrite;
   }
 
+  // one residency query per session for the whole call
+  if (!resolve_residency(sc, m)) return FATHOM_ERR_INVALID_ARG;
+  for (int32_t j = 0; j < m; ++j) plain[j].residency = first[j].residency = sc[j].residency;
   const bool group_ok = group == 1 || (group == hq / hkv && group <= 4);
   if (!group_ok || (m > 0 && !scan_can_fuse(sc, m))) {
     for (int32_t j = 0; j < m; ++j) plain[j].table_mode = kTableNone;
