@@ -485,8 +485,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
 // 2^(E_h-30) times them to the key's running value, which starts at C_h (one
 // rounding per pass).
 //
-// A block of 8 waves takes 2048-key tiles (64 plane words per row).  In a
-// pass, wave w reads slot group w (8 slots x 4 planes = 32 rows) with 16-byte
+// One 1024-thread block per CU (one round of resident blocks); its two halves
+// of 8 waves each take one 2048-key tile (64 plane words per row) of an item,
+// with a code table of their own, and run one step apart (a step lies
+// between two barriers): while one half transposes an item, the other runs
+// the matrix cores over its previous one.  In a pass, wave w of a half reads
+// slot group w (8 slots x 4 planes = 32 rows) with 16-byte
 // loads: a quarter of the wave (16 lanes) covers one row, 4 words per lane,
 // and one load instruction covers the 4 planes of one slot.  Two lane swaps
 // (32-lane halves, then 16-lane rows) regroup the words so that every lane
