@@ -182,6 +182,103 @@ int orc_plan_fixed(const float *q, int hq, int d, int r, uint8_t *plan) {
   return ORC_OK;
 }
 
+/* Rate-distortion variant of the water-filling.  [EXP] key pseudocode notes
+ * that the original treats the allocation more finely than fill-to-cap and
+ * gives no table; [EXP] "反向注水 vs 固定预算" says that with close channel
+ * importances the budget spreads almost evenly.  Reading R16: each read bit
+ * of channel c at depth t (t = 0..3 bits already read) lowers the channel's
+ * distortion w_c * 4^-t by a gain proportional to w_c * 4^-t, and the budget
+ * buys the B largest gains (gain desc, then channel asc, then t asc).  A
+ * channel's gains fall with t, so the bits taken from a channel are always
+ * its top ones, and t_c = the number of its gains taken.  Gains are compared
+ * exactly in fp64 (w_c * 2^(-2t) is exact there).
+ * Same arguments and w_c as orc_plan.                                       */
+typedef struct {
+  double g;
+  int c, t;
+} orc_gain;
+
+static int orc_cmp_gain(const void *a, const void *b) {
+  const orc_gain *x = (const orc_gain *)a, *y = (const orc_gain *)b;
+  if (x->g > y->g) return -1;
+  if (x->g < y->g) return 1;
+  if (x->c != y->c) return x->c < y->c ? -1 : 1;
+  return (x->t < y->t) ? -1 : (x->t > y->t);
+}
+
+int orc_plan_rd(const float *q, int hq, int hkv, int d, const float *sigma2,
+                const int32_t *budget, uint8_t *plan) {
+  if (!q || !sigma2 || !budget || !plan || hq < 1 || hkv < 1 || hq % hkv)
+    return ORC_BAD;
+  const int G = hq / hkv;
+  orc_gain *gains = (orc_gain *)malloc(sizeof(orc_gain) * 4 * d);
+  if (!gains) return ORC_BAD;
+  for (int h = 0; h < hq; ++h) {
+    int B = budget[h];
+    if (B < 0 || B > 4 * d) {
+      free(gains);
+      return ORC_BAD;
+    }
+    const float *sg = sigma2 + (int64_t)(h / G) * d;
+    for (int c = 0; c < d; ++c) {
+      float qq = q[(int64_t)h * d + c] * q[(int64_t)h * d + c];
+      float w = qq * sg[c];
+      for (int t = 0; t < 4; ++t) {
+        gains[4 * c + t].g = ldexp((double)w, -2 * t);
+        gains[4 * c + t].c = c;
+        gains[4 * c + t].t = t;
+      }
+    }
+    qsort(gains, (size_t)4 * d, sizeof(orc_gain), orc_cmp_gain);
+    for (int c = 0; c < d; ++c) plan[(int64_t)h * d + c] = 0;
+    for (int j = 0; j < B; ++j) plan[(int64_t)h * d + gains[j].c] += 1;
+  }
+  free(gains);
+  return ORC_OK;
+}
+
+/* One plan per GQA group.  [EXP] "反向注水 vs 固定预算" lists sharing the
+ * channel importance across a GQA group as a direction (the pages decide per
+ * head).  Reading R17: the group's importance of channel c is
+ * sigma_c^2 * sum over the group's heads of q_hc^2, the squares added in fp32
+ * in head order and the product rounded once (fp32); the fill-to-cap walk of
+ * orc_plan spends budget[g] on it, and every head of the group gets that plan,
+ * so the group reads exactly budget[g] bits per key.
+ * budget [hkv] (one per kv head), plan out [hq][d].                          */
+int orc_plan_group(const float *q, int hq, int hkv, int d, const float *sigma2,
+                   const int32_t *budget, uint8_t *plan) {
+  if (!q || !sigma2 || !budget || !plan || hq < 1 || hkv < 1 || hq % hkv)
+    return ORC_BAD;
+  const int G = hq / hkv;
+  orc_wc *order = (orc_wc *)malloc(sizeof(orc_wc) * d);
+  if (!order) return ORC_BAD;
+  for (int g = 0; g < hkv; ++g) {
+    int B = budget[g];
+    if (B < 0 || B > 4 * d) {
+      free(order);
+      return ORC_BAD;
+    }
+    for (int c = 0; c < d; ++c) {
+      float sq = 0.0f;
+      for (int j = 0; j < G; ++j) {
+        float qc = q[(int64_t)(g * G + j) * d + c];
+        sq = sq + qc * qc;
+      }
+      order[c].w = sq * sigma2[(int64_t)g * d + c];
+      order[c].c = c;
+    }
+    qsort(order, d, sizeof(orc_wc), orc_cmp_w_desc);
+    int remaining = B;
+    for (int j = 0; j < d; ++j) {
+      int take = remaining <= 0 ? 0 : (remaining < 4 ? remaining : 4);
+      for (int k = 0; k < G; ++k) plan[(int64_t)(g * G + k) * d + order[j].c] = (uint8_t)take;
+      remaining -= take;
+    }
+  }
+  free(order);
+  return ORC_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* The 4-bit code of key i in channel c of kv head h, rebuilt bit by bit from
  * the planes (slot 3 - p holds bit p). */

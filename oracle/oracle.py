@@ -47,11 +47,14 @@ def _load():
         lib.orc_pack.argtypes = [P, L, I, I, L, L, P, P, P, P, P]
         lib.orc_plan.argtypes = [P, I, I, I, P, P, P]
         lib.orc_plan_fixed.argtypes = [P, I, I, I, P]
+        lib.orc_plan_rd.argtypes = [P, I, I, I, P, P, P]
+        lib.orc_plan_group.argtypes = [P, I, I, I, P, P, P]
         lib.orc_scan.argtypes = [P, P, P, L, I, I, P, P, I, P, F, P, L]
         lib.orc_scan_at.argtypes = [P, P, P, L, I, I, P, P, I, P, F, P, L, P]
         lib.orc_read_prefixes.argtypes = [P, L, I, I, P, I, P]
         lib.orc_topk.argtypes = [P, I, L, L, I, I, P, P]
-        for f in ("orc_pack", "orc_plan", "orc_plan_fixed", "orc_scan", "orc_scan_at",
+        for f in ("orc_pack", "orc_plan", "orc_plan_fixed", "orc_plan_rd", "orc_plan_group",
+                  "orc_scan", "orc_scan_at",
                   "orc_read_prefixes", "orc_topk"):
             getattr(lib, f).restype = I
         _lib = lib
@@ -100,6 +103,32 @@ def plan(q: np.ndarray, sigma2: np.ndarray, budget) -> np.ndarray:
     out = np.empty((hq, d), np.uint8)
     _check(_load().orc_plan(_ptr(q), hq, hkv, d, _ptr(sigma2), _ptr(b),
                             _ptr(out)), "plan")
+    return out
+
+
+def plan_rd(q: np.ndarray, sigma2: np.ndarray, budget) -> np.ndarray:
+    """Rate-distortion plan: the B largest gains w_c * 4^-t -> [hq][d] u8."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    sigma2 = np.ascontiguousarray(sigma2, dtype=np.float32)
+    hq, d = q.shape
+    hkv = sigma2.shape[0]
+    b = np.ascontiguousarray(np.broadcast_to(np.asarray(budget, np.int32), (hq,)))
+    out = np.empty((hq, d), np.uint8)
+    _check(_load().orc_plan_rd(_ptr(q), hq, hkv, d, _ptr(sigma2), _ptr(b),
+                               _ptr(out)), "plan_rd")
+    return out
+
+
+def plan_group(q: np.ndarray, sigma2: np.ndarray, budget) -> np.ndarray:
+    """One plan per GQA group; budget int or [hkv] -> [hq][d] u8."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    sigma2 = np.ascontiguousarray(sigma2, dtype=np.float32)
+    hq, d = q.shape
+    hkv = sigma2.shape[0]
+    b = np.ascontiguousarray(np.broadcast_to(np.asarray(budget, np.int32), (hkv,)))
+    out = np.empty((hq, d), np.uint8)
+    _check(_load().orc_plan_group(_ptr(q), hq, hkv, d, _ptr(sigma2), _ptr(b),
+                                  _ptr(out)), "plan_group")
     return out
 
 

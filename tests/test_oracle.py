@@ -285,6 +285,170 @@ def test_plan_fixed_is_top_r_abs_q_and_matches_equal_sigma(orc):
 
 
 # --------------------------------------------------------------------------
+# plan variants: rate-distortion greedy and one plan per GQA group
+
+def distortion(w, plans):
+    """sum_c w_c 4^-t_c for each row of plans (exact in fp64 here)."""
+    return (w[None, :].astype(np.float64) * np.ldexp(1.0, -2 * plans)).sum(1)
+
+
+def test_plan_rd_worked_examples(orc):
+    one = np.ones((1, 2), np.float32)
+    # w = (4, 1): fill-to-cap would give (3, 0), distortion 1/16 + 1; two
+    # bits on the first channel and one on the second give 1/4 + 1/4.
+    q = np.array([[2.0, 1.0]], np.float32)
+    assert list(orc.plan_rd(q, one, 3)[0]) == [2, 1]
+    assert list(orc.plan(q, one, 3)[0]) == [3, 0]
+    # B = 2 is a tie, (2,0) and (1,1) both cost 5/4: the lower channel wins.
+    assert list(orc.plan_rd(q, one, 2)[0]) == [2, 0]
+    # equal importances spread the budget evenly, lower channels first
+    e = np.ones((1, 4), np.float32)
+    for B in range(17):
+        exp = [B // 4 + (c < B % 4) for c in range(4)]
+        assert list(orc.plan_rd(e, e, B)[0]) == exp
+
+
+@pytest.mark.parametrize("d", [3, 4, 5])
+def test_plan_rd_is_distortion_minimiser_brute_force(orc, d):
+    rng = np.random.default_rng(200 + d)
+    plans = np.array(list(itertools.product(range(5), repeat=d)))
+    for trial in range(6):
+        q = rng.standard_normal((1, d)).astype(np.float32)
+        sigma2 = rng.uniform(0.1, 4, (1, d)).astype(np.float32)
+        w = w_order(q[0], sigma2[0])
+        for B in range(0, 4 * d + 1):
+            feas = plans[plans.sum(1) == B]
+            dist = distortion(w, feas)
+            got = orc.plan_rd(q, sigma2, B)[0].astype(np.int64)
+            assert got.sum() == B and got.max() <= 4
+            best = feas[dist == dist.min()]
+            assert len(best) == 1
+            np.testing.assert_array_equal(got, best[0])
+
+
+@pytest.mark.parametrize("B", [0, 1, 5, 64, 92, 136, 300, 511, 512])
+def test_plan_rd_no_improving_single_bit_move(orc, B):
+    """Moving one bit from any read channel to any channel with room never
+    lowers the distortion, and the budget is spent exactly."""
+    rng = np.random.default_rng(B + 7)
+    hq, hkv, d = 4, 2, 128
+    q = rng.standard_normal((hq, d)).astype(np.float32)
+    sigma2 = rng.uniform(0.01, 16, (hkv, d)).astype(np.float32)
+    plan = orc.plan_rd(q, sigma2, B).astype(np.int64)
+    assert np.all(plan.sum(1) == B) and np.all(plan <= 4)
+    for h in range(hq):
+        w = w_order(q[h], sigma2[h // 2]).astype(np.float64)
+        t = plan[h]
+        next_gain = np.where(t < 4, w * np.ldexp(1.0, -2 * t), -np.inf)
+        last_gain = np.where(t > 0, w * np.ldexp(1.0, -2 * (t - 1)), np.inf)
+        assert next_gain.max() <= last_gain.min()
+
+
+def test_plan_rd_equals_fill_to_cap_when_weights_are_far_apart(orc):
+    """When each importance exceeds the next by more than 4^3, every bit of a
+    channel is worth more than the first bit of the next: the walk results."""
+    d = 12
+    rng = np.random.default_rng(11)
+    w = np.ldexp(1.0, -7 * np.arange(d)).astype(np.float32)   # ratio 128
+    perm = rng.permutation(d)
+    sigma2 = w[perm][None, :]
+    q = np.ones((1, d), np.float32)
+    for B in range(4 * d + 1):
+        np.testing.assert_array_equal(orc.plan_rd(q, sigma2, B), orc.plan(q, sigma2, B))
+
+
+def test_plan_rd_rejects_out_of_range_budget(orc):
+    q = np.ones((1, 8), np.float32)
+    for B in (-1, 33):
+        with pytest.raises(ValueError):
+            orc.plan_rd(q, q, B)
+
+
+def group_weights64(q, sigma2, G):
+    hq, d = q.shape
+    qq = (q.astype(np.float64) ** 2).reshape(hq // G, G, d).sum(1)
+    return qq * sigma2.astype(np.float64)
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_plan_group_shares_one_plan_and_spends_group_budget(orc, G):
+    rng = np.random.default_rng(G)
+    hkv, d = 3, 128
+    q = rng.standard_normal((hkv * G, d)).astype(np.float32)
+    sigma2 = rng.uniform(0.01, 16, (hkv, d)).astype(np.float32)
+    budgets = np.array([0, 92, 512], np.int32)
+    plan = orc.plan_group(q, sigma2, budgets).astype(np.int64)
+    for g in range(hkv):
+        rows = plan[g * G:(g + 1) * G]
+        assert np.all(rows == rows[0])
+        assert rows[0].sum() == budgets[g] and rows[0].max() <= 4
+        # channels read in full outrank unread ones under the summed importance
+        W = group_weights64(q, sigma2, G)[g]
+        read, unread = W[rows[0] == 4], W[rows[0] == 0]
+        if read.size and unread.size:
+            assert read.min() >= unread.max()
+
+
+def test_plan_group_of_one_head_is_the_per_head_plan(orc):
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((6, 128)).astype(np.float32)
+    sigma2 = rng.uniform(0.01, 16, (6, 128)).astype(np.float32)
+    for B in (0, 3, 92, 136, 512):
+        np.testing.assert_array_equal(orc.plan_group(q, sigma2, B), orc.plan(q, sigma2, B))
+
+
+def test_plan_group_of_identical_heads_is_their_plan(orc):
+    """Two equal heads: the summed square is exactly twice each, so the order
+    (and the plan) is that of either head alone."""
+    rng = np.random.default_rng(22)
+    q1 = rng.standard_normal((2, 128)).astype(np.float32)
+    q = np.repeat(q1, 2, axis=0)
+    sigma2 = rng.uniform(0.01, 16, (2, 128)).astype(np.float32)
+    for B in (1, 92, 136):
+        np.testing.assert_array_equal(orc.plan_group(q, sigma2, B),
+                                      orc.plan(q, sigma2, B))
+
+
+@pytest.mark.parametrize("d", [3, 4, 5])
+def test_plan_group_maximises_summed_importance_brute_force(orc, d):
+    rng = np.random.default_rng(300 + d)
+    plans = np.array(list(itertools.product(range(5), repeat=d)))
+    G = 4
+    for trial in range(4):
+        q = rng.standard_normal((G, d)).astype(np.float32)
+        sigma2 = rng.uniform(0.1, 4, (1, d)).astype(np.float32)
+        W = group_weights64(q, sigma2, G)[0]
+        for B in range(0, 4 * d + 1):
+            feas = plans[plans.sum(1) == B]
+            val = feas @ W
+            best = feas[val == val.max()]
+            assert len(best) == 1
+            got = orc.plan_group(q, sigma2, B)
+            for h in range(G):
+                np.testing.assert_array_equal(got[h], best[0])
+
+
+def test_plan_group_is_invariant_to_head_order_within_group(orc):
+    """Integer-valued queries make every sum exact, so reordering the heads of
+    a group cannot change the plan."""
+    rng = np.random.default_rng(23)
+    G, d = 8, 128
+    q = rng.integers(-3, 4, (G, d)).astype(np.float32)
+    sigma2 = rng.integers(1, 5, (1, d)).astype(np.float32)
+    base = orc.plan_group(q, sigma2, 92)
+    perm = rng.permutation(G)
+    np.testing.assert_array_equal(orc.plan_group(q[perm], sigma2, 92), base)
+
+
+def test_plan_group_rejects_out_of_range_budget(orc):
+    q = np.ones((2, 8), np.float32)
+    s = np.ones((1, 8), np.float32)
+    for B in (-1, 33):
+        with pytest.raises(ValueError):
+            orc.plan_group(q, s, B)
+
+
+# --------------------------------------------------------------------------
 # scan
 
 def make_layer(seed, n=300, hkv=2, hq=4, d=16, dtype=np.float16):
