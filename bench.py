@@ -62,6 +62,7 @@ class Layer:
             self.meta_host = torch.empty(self.meta.shape, dtype=torch.uint8, pin_memory=True)
             self.meta_host.copy_(self.meta)
         self.budget = [w.budget] * w.hq
+        self.group_budget = [w.budget] * w.hkv
         self.plan = torch.empty((w.hq, w.d), dtype=torch.uint8, device=dev)
         self.plan_fixed = fathom.plan_fixed(self.q, fixed_r)
         self.logits = torch.empty((w.hq, w.n), dtype=torch.float32, device=dev)
@@ -78,9 +79,12 @@ def union_plane_bytes(plan, hkv, n):
     return sum(ub) * n // 8, ub, hist
 
 
-def run_steps(layers, w, ws, steps, mode, fixed=False, fused=False, per_call=True):
+def run_steps(layers, w, ws, steps, mode, fixed=False, fused=False, per_call=True,
+              variant=None):
     """mode: 'host' or 'hbm'.  fused: fathom_scan_topk in place of fathom_scan
-    then fathom_topk (ws must then be its workspace).  per_call: events around
+    then fathom_topk (ws must then be its workspace).  variant: None (the
+    fill-to-cap walk), 'rd' (rate-distortion plan) or 'group' (one plan per
+    GQA group, budget B per kv head).  per_call: events around
     every call (for the per-call times); otherwise none, since an event
     recorded between two calls stalls the stream for a few microseconds.
     Returns the per-step event lists (empty lists when per_call is off)."""
@@ -97,6 +101,10 @@ def run_steps(layers, w, ws, steps, mode, fixed=False, fused=False, per_call=Tru
             e[0].record()
         if fixed:                                     # query-only plan of the baselines
             plan = fathom.plan_fixed(L.q, 32, out=L.plan)
+        elif variant == "rd":
+            plan = fathom.plan_rd(L.q, L.sigma2, L.budget, out=L.plan)
+        elif variant == "group":
+            plan = fathom.plan_group(L.q, L.sigma2, L.group_budget, out=L.plan)
         else:
             plan = fathom.plan(L.q, L.sigma2, L.budget, out=L.plan)
         if per_call:
@@ -127,21 +135,21 @@ def summarize(ev):
                 scan_ms_p90=float(np.percentile(scan, 90)))
 
 
-def timed(layers, w, ws, steps, warmup, mode, fixed=False, fused=False):
+def timed(layers, w, ws, steps, warmup, mode, fixed=False, fused=False, variant=None):
     """Throughput: K steps between one pair of events (and synchronisations);
     then the same K steps again with events around every call, for the
     per-call times (the scan's is the one the rooflines use)."""
-    run_steps(layers, w, ws, warmup, mode, fixed, fused, per_call=False)
+    run_steps(layers, w, ws, warmup, mode, fixed, fused, per_call=False, variant=variant)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     a.record()
-    run_steps(layers, w, ws, steps, mode, fixed, fused, per_call=False)
+    run_steps(layers, w, ws, steps, mode, fixed, fused, per_call=False, variant=variant)
     b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     r = {"step_ms": a.elapsed_time(b) / steps, "wall_ms_per_step": wall * 1e3 / steps}
-    ev = run_steps(layers, w, ws, steps, mode, fixed, fused, per_call=True)
+    ev = run_steps(layers, w, ws, steps, mode, fixed, fused, per_call=True, variant=variant)
     torch.cuda.synchronize()
     r.update(summarize(ev))
     return r
@@ -436,6 +444,10 @@ def scan_traffic_from_profiles():
     return rec
 
 
+def res_modes(args):
+    return ["host", "hbm"] if args.only == "all" else [args.only]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -498,7 +510,7 @@ def main():
     log(f"union bits per kv head {ub}, depth histogram {hist}; fixed-136 union {fub}")
 
     res = {}
-    for mode in (["host", "hbm"] if args.only == "all" else [args.only]):
+    for mode in res_modes(args):
         res[mode] = timed(layers, w, ws, args.steps, args.warmup, mode)
         res[mode + "_fixed"] = timed(layers, w, ws, args.steps, args.warmup, mode, fixed=True)
         res[mode + "_fused"] = timed(layers, w, fws, args.steps, args.warmup, mode, fused=True)
@@ -506,6 +518,22 @@ def main():
                                            fixed=True, fused=True)
         for key in (mode, mode + "_fixed", mode + "_fused", mode + "_fixed_fused"):
             log(f"{key}: {res[key]}")
+
+    variants = {}
+    if not args.no_extra:
+        for var, fn, bud in (("rd", fathom.plan_rd, "budget"),
+                             ("group", fathom.plan_group, "group_budget")):
+            vper = [union_plane_bytes(fn(L.q, L.sigma2, getattr(L, bud)), w.hkv, w.n)
+                    for L in layers]
+            v = {"union_plane_bytes": int(np.mean([x[0] for x in vper])),
+                 "union_bits_per_kv_head": vper[0][1], "depth_histogram": vper[0][2]}
+            for mode in res_modes(args):
+                t = timed(layers, w, fws, args.steps, args.warmup, mode, fused=True,
+                          variant=var)
+                v[mode + "_fused"] = {"keys_per_s": round(w.n * w.hkv / (t["step_ms"] * 1e-3), 1),
+                                      **{k: round(x, 4) for k, x in t.items()}}
+                log(f"{var} {mode}_fused: {t}")
+            variants[var] = v
 
     keys_per_step = w.n * w.hkv
     main_mode = "host" if "host" in res else "hbm"
@@ -576,6 +604,10 @@ def main():
                     "fixed136_meta_bytes": meta_b, "logits_bytes": logits_b,
                     "union_bits_per_kv_head": ub, "fixed136_union_bits": fub,
                     "depth_histogram": hist}
+    if variants:
+        variants["note"] = ("B=92 per query head (rd) or per kv head (group: the whole GQA "
+                            "group reads 92 plane bits per key); fused scan + top-k steps")
+        out["plan_variants"] = variants
     out["probe"] = probe
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(layers[0], w, args.cpu_sample, args.cpu_sample_mt)

@@ -116,6 +116,35 @@ int32_t fathom_plan(const float *q, int32_t hq, int32_t hkv, int32_t d,
                     const float *sigma2, const int32_t *budget_bits,
                     uint8_t *plan, void *stream);
 
+/* Rate-distortion variant of the allocation.  The explainer's key-pseudocode
+ * section notes that the original allocates more finely than fill-to-cap,
+ * and its intuition section (反向注水 vs 固定预算) that close importances
+ * spread the budget; neither gives the rule, so this one is a reading: a
+ * channel read to depth t keeps an error term proportional to w_c * 4^-t
+ * (one more plane quarters the quantisation cell), reading bit t+1 gains in
+ * proportion to w_c * 4^-t, and the B largest gains are bought (ties: lower
+ * channel, then shallower bit), which minimises sum_c w_c * 4^-t_c over all
+ * plans with sum t_c = B, 0 <= t_c <= 4.  Gains are compared exactly (fp64).
+ * Same w_c, arguments, ownership and errors as fathom_plan; q and sigma2
+ * must be finite.  Output t_c in 0..4 with sum_c t_c = B.                  */
+int32_t fathom_plan_rd(const float *q, int32_t hq, int32_t hkv, int32_t d,
+                       const float *sigma2, const int32_t *budget_bits,
+                       uint8_t *plan, void *stream);
+
+/* One plan per GQA group.  The explainer's intuition section lists sharing
+ * the channel importance across a GQA group as a direction (the pages plan
+ * per head).  Group g (query heads g*G .. g*G+G-1, G = hq / hkv) uses
+ * W_c = fp32(sigma2_gc * S_c), S_c = the fp32 sum in head order of the
+ * rounded squares q_hc * q_hc, and the fill-to-cap walk of fathom_plan with
+ * budget_bits[g]; every head of the group receives that row, so the group's
+ * scan reads exactly budget_bits[g] plane bits per key.
+ * budget_bits  HOST int32[hkv], each in [0, 4d] (else FATHOM_ERR_INVALID_ARG)
+ * plan         device output uint8[hq][d] (G equal rows per group).
+ * Other arguments as for fathom_plan.                                       */
+int32_t fathom_plan_group(const float *q, int32_t hq, int32_t hkv, int32_t d,
+                          const float *sigma2, const int32_t *budget_bits,
+                          uint8_t *plan, void *stream);
+
 /* Fixed-width baseline plan (the pages' 136-bit scans read r = 32 channels
  * in full): the r channels with the largest |q_c| (ties: lower channel) get
  * t = 4, all others 0.  0 <= r <= d.                                        */

@@ -63,6 +63,8 @@ def lib():
             "fathom_pack": (I32, [P, I32, I64, I32, I32, I64, I64, P, P, P, P, P, I64, P]),
             "fathom_plan": (I32, [P, I32, I32, I32, P, P, P, P]),
             "fathom_plan_fixed": (I32, [P, I32, I32, I32, P, P]),
+            "fathom_plan_rd": (I32, [P, I32, I32, I32, P, P, P, P]),
+            "fathom_plan_group": (I32, [P, I32, I32, I32, P, P, P, P]),
             "fathom_scan": (I32, [P, P, P, I64, I32, I32, P, P, I32, P, F, P, I64, P]),
             "fathom_topk": (I32, [P, I32, I64, I64, I32, I32, P, P, P, I64, P]),
             "fathom_scan_batched": (I32, [P, I32, I32, I32, I32, P]),
@@ -158,18 +160,38 @@ def pack(keys: torch.Tensor, planes: Optional[torch.Tensor] = None,
     return Packed(planes, lo, hi, s2, n)
 
 
-def plan(q: torch.Tensor, sigma2: torch.Tensor, budget, out=None) -> torch.Tensor:
-    """q [hq][d] fp32, sigma2 [hkv][d] fp32, budget int or sequence of hq ints."""
+def _budgets(budget, count: int):
+    vals = [int(budget)] * count if isinstance(budget, int) else [int(x) for x in budget]
+    if len(vals) != count:
+        raise ValueError(f"expected {count} budgets, got {len(vals)}")
+    return (ctypes.c_int32 * count)(*vals)
+
+
+def _plan_call(fn: str, q, sigma2, budget, n_budgets: int, out):
     _require_gpu(q, sigma2)
     hq, d = q.shape
     hkv = sigma2.shape[0]
-    b = (ctypes.c_int32 * hq)(*([int(budget)] * hq if isinstance(budget, int)
-                                else [int(x) for x in budget]))
+    b = _budgets(budget, hq if n_budgets < 0 else n_budgets)
     if out is None:
         out = torch.empty((hq, d), dtype=torch.uint8, device=q.device)
-    _check(lib().fathom_plan(_p(q.contiguous()), hq, hkv, d, _p(sigma2.contiguous()), b,
-                             _p(out), _stream(q.device)), "fathom_plan")
+    _check(getattr(lib(), fn)(_p(q.contiguous()), hq, hkv, d, _p(sigma2.contiguous()), b,
+                              _p(out), _stream(q.device)), fn)
     return out
+
+
+def plan(q: torch.Tensor, sigma2: torch.Tensor, budget, out=None) -> torch.Tensor:
+    """q [hq][d] fp32, sigma2 [hkv][d] fp32, budget int or sequence of hq ints."""
+    return _plan_call("fathom_plan", q, sigma2, budget, -1, out)
+
+
+def plan_rd(q: torch.Tensor, sigma2: torch.Tensor, budget, out=None) -> torch.Tensor:
+    """Rate-distortion allocation; arguments as for plan."""
+    return _plan_call("fathom_plan_rd", q, sigma2, budget, -1, out)
+
+
+def plan_group(q: torch.Tensor, sigma2: torch.Tensor, budget, out=None) -> torch.Tensor:
+    """One plan per GQA group; budget int or sequence of hkv ints."""
+    return _plan_call("fathom_plan_group", q, sigma2, budget, sigma2.shape[0], out)
 
 
 def plan_fixed(q: torch.Tensor, r: int, out=None) -> torch.Tensor:

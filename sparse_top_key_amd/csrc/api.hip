@@ -107,6 +107,33 @@ int32_t fathom_plan(const float *q, int32_t hq, int32_t hkv, int32_t d,
   return launch_plan(q, hq, hkv, sigma2, budget_bits, plan, as_stream(stream));
 }
 
+int32_t fathom_plan_rd(const float *q, int32_t hq, int32_t hkv, int32_t d,
+                       const float *sigma2, const int32_t *budget_bits, uint8_t *plan,
+                       void *stream) {
+  REQUIRE(q && sigma2 && budget_bits && plan, FATHOM_ERR_INVALID_ARG,
+          "fathom_plan_rd: null pointer");
+  if (int32_t rc = check_heads(hq, hkv)) return rc;
+  if (int32_t rc = check_d(d)) return rc;
+  for (int32_t h = 0; h < hq; ++h)
+    REQUIRE(budget_bits[h] >= 0 && budget_bits[h] <= 4 * d, FATHOM_ERR_INVALID_ARG,
+            "fathom_plan_rd: budget_bits[%d] = %d outside [0, %d]", h, budget_bits[h], 4 * d);
+  return launch_plan_rd(q, hq, hkv, sigma2, budget_bits, plan, as_stream(stream));
+}
+
+int32_t fathom_plan_group(const float *q, int32_t hq, int32_t hkv, int32_t d,
+                          const float *sigma2, const int32_t *budget_bits, uint8_t *plan,
+                          void *stream) {
+  REQUIRE(q && sigma2 && budget_bits && plan, FATHOM_ERR_INVALID_ARG,
+          "fathom_plan_group: null pointer");
+  if (int32_t rc = check_heads(hq, hkv)) return rc;
+  if (int32_t rc = check_d(d)) return rc;
+  for (int32_t g = 0; g < hkv; ++g)
+    REQUIRE(budget_bits[g] >= 0 && budget_bits[g] <= 4 * d, FATHOM_ERR_INVALID_ARG,
+            "fathom_plan_group: budget_bits[%d] = %d outside [0, %d]", g, budget_bits[g],
+            4 * d);
+  return launch_plan_group(q, hq, hkv, sigma2, budget_bits, plan, as_stream(stream));
+}
+
 int32_t fathom_plan_fixed(const float *q, int32_t hq, int32_t d, int32_t r, uint8_t *plan,
                           void *stream) {
   REQUIRE(q && plan, FATHOM_ERR_INVALID_ARG, "fathom_plan_fixed: null pointer");

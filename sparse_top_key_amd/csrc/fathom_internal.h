@@ -66,6 +66,12 @@ int32_t launch_pack(const void *keys, int32_t dtype, int64_t n, int32_t hkv,
 int32_t launch_plan(const float *q, int32_t hq, int32_t hkv,
                     const float *sigma2, const int32_t *budget_host,
                     uint8_t *plan, hipStream_t s);
+int32_t launch_plan_rd(const float *q, int32_t hq, int32_t hkv,
+                       const float *sigma2, const int32_t *budget_host,
+                       uint8_t *plan, hipStream_t s);
+int32_t launch_plan_group(const float *q, int32_t hq, int32_t hkv,
+                          const float *sigma2, const int32_t *budget_host,
+                          uint8_t *plan, hipStream_t s);
 int32_t launch_plan_fixed(const float *q, int32_t hq, int32_t r, uint8_t *plan,
                           hipStream_t s);
 

@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_path():
     names = declared_functions()
-    for f in ("fathom_pack", "fathom_plan", "fathom_plan_fixed", "fathom_scan",
+    for f in ("fathom_pack", "fathom_plan", "fathom_plan_fixed", "fathom_plan_rd",
+              "fathom_plan_group", "fathom_scan",
               "fathom_topk", "fathom_scan_batched", "fathom_topk_batched",
               "fathom_read_prefixes", "fathom_plan_stats", "fathom_probe_read"):
         assert f in names
@@ -76,6 +77,23 @@ def test_plan_validation(L):
     assert L.fathom_plan(DUMMY, 4, 1, 128, DUMMY, neg, DUMMY, None) == 1
     assert L.fathom_plan_fixed(DUMMY, 4, 128, 129, DUMMY, None) == 1
     assert L.fathom_plan_fixed(DUMMY, 4, 128, -1, DUMMY, None) == 1
+
+
+def test_plan_variant_validation(L):
+    b = (ctypes.c_int32 * 4)(92, 92, 92, 92)
+    assert L.fathom_plan_rd(None, 4, 1, 128, DUMMY, b, DUMMY, None) == 1
+    assert L.fathom_plan_rd(DUMMY, 4, 3, 128, DUMMY, b, DUMMY, None) == 1
+    assert L.fathom_plan_rd(DUMMY, 4, 1, 64, DUMMY, b, DUMMY, None) == 2
+    bad = (ctypes.c_int32 * 4)(92, 92, 92, 513)
+    assert L.fathom_plan_rd(DUMMY, 4, 1, 128, DUMMY, bad, DUMMY, None) == 1
+    assert "fathom_plan_rd: budget_bits[3] = 513" in err(L)
+    # the group plan reads one budget per kv head: hkv = 2 checks entries 0, 1
+    g = (ctypes.c_int32 * 2)(92, -1)
+    assert L.fathom_plan_group(DUMMY, 4, 2, 128, DUMMY, g, DUMMY, None) == 1
+    assert "fathom_plan_group: budget_bits[1] = -1" in err(L)
+    assert L.fathom_plan_group(DUMMY, 4, 1, 128, DUMMY, None, DUMMY, None) == 1
+    assert L.fathom_plan_group(DUMMY, 6, 4, 128, DUMMY, b, DUMMY, None) == 1
+    assert L.fathom_plan_group(DUMMY, 4, 1, 96, DUMMY, b, DUMMY, None) == 2
 
 
 def test_pack_validation(L):
