@@ -82,7 +82,8 @@ def union_plane_bytes(plan, hkv, n):
 def run_steps(layers, w, ws, steps, mode, fixed=False, fused=False, per_call=True,
               variant=None):
     """mode: 'host' or 'hbm'.  fused: fathom_scan_topk in place of fathom_scan
-    then fathom_topk (ws must then be its workspace).  variant: None (the
+    then fathom_topk (ws must then be its workspace).  fixed: True (r = 32,
+    the 136-bit baseline) or the baseline's channel count r.  variant: None (the
     fill-to-cap walk), 'rd' (rate-distortion plan) or 'group' (one plan per
     GQA group, budget B per kv head).  per_call: events around
     every call (for the per-call times); otherwise none, since an event
@@ -100,7 +101,7 @@ def run_steps(layers, w, ws, steps, mode, fixed=False, fused=False, per_call=Tru
         if per_call:
             e[0].record()
         if fixed:                                     # query-only plan of the baselines
-            plan = fathom.plan_fixed(L.q, 32, out=L.plan)
+            plan = fathom.plan_fixed(L.q, 32 if fixed is True else int(fixed), out=L.plan)
         elif variant == "rd":
             plan = fathom.plan_rd(L.q, L.sigma2, L.budget, out=L.plan)
         elif variant == "group":
@@ -326,6 +327,60 @@ def bench_layer_128k(dev, steps, warmup):
     return out
 
 
+def plan_quality(dev, layers_q=2):
+    """Recall of each plan's top-k against the exact top-k of the fp64 logits
+    q . k of the fp16 keys (not timed; torch's matmul on the GPU is the
+    reference here, never part of the path).  1M-key layers, k = 2048 per
+    query head, mean over heads and layers."""
+    w = synth.LAYER_1M
+    G = w.hq // w.hkv
+    kinds = [("fathom_B92", lambda p, q: fathom.plan(q, p.sigma2, 92)),
+             ("rd_B92", lambda p, q: fathom.plan_rd(q, p.sigma2, 92)),
+             ("group_B92_per_kv_head", lambda p, q: fathom.plan_group(q, p.sigma2, 92)),
+             ("group_B368_per_kv_head", lambda p, q: fathom.plan_group(q, p.sigma2, 4 * 92)),
+             ("fathom_B68", lambda p, q: fathom.plan(q, p.sigma2, 68)),
+             ("rd_B68", lambda p, q: fathom.plan_rd(q, p.sigma2, 68)),
+             ("fathom_B136", lambda p, q: fathom.plan(q, p.sigma2, 136)),
+             ("rd_B136", lambda p, q: fathom.plan_rd(q, p.sigma2, 136)),
+             ("group_B176_per_kv_head", lambda p, q: fathom.plan_group(q, p.sigma2, 176)),
+             ("fixed136", None),
+             ("fixed_r16", 16),
+             ("full_4bit_B512", lambda p, q: fathom.plan(q, p.sigma2, 512))]
+    rec = {name: [] for name, _ in kinds}
+    bits = {name: [] for name, _ in kinds}
+    ws = torch.empty(fathom.scan_topk_workspace_bytes([w.n], w.hkv, w.hq, 1, w.k),
+                     dtype=torch.uint8, device=dev)
+    for l in range(layers_q):
+        keys = synth.keys(w.seed, l, w.n, w.hkv, w.d, w.dtype, w.outliers, device=dev)
+        q = synth.queries(w.seed, l, w.hq, w.d, device=dev)
+        p = fathom.pack(keys)
+        exact = []
+        for g in range(w.hkv):
+            K = keys[:, g, :].double()
+            s = q[g * G:(g + 1) * G].double() @ K.T
+            exact.append(torch.topk(s, w.k, dim=1).indices)
+            del K, s
+        exact = torch.cat(exact).cpu().numpy()
+        del keys
+        for name, fn in kinds:
+            if fn is None or isinstance(fn, int):
+                plan = fathom.plan_fixed(q, 32 if fn is None else fn)
+            else:
+                plan = fn(p, q)
+            idx, _ = fathom.scan_topk(p.planes, p.lo, p.hi, w.n, q, plan, w.k, 1, ws=ws)
+            got = idx.cpu().numpy()
+            rec[name].append(np.mean([len(np.intersect1d(got[h], exact[h])) / w.k
+                                      for h in range(w.hq)]))
+            bits[name].append(np.mean(union_plane_bytes(plan, w.hkv, w.n)[1]))
+        del p
+        torch.cuda.empty_cache()
+    return {"workload": f"{layers_q} x 1M-key layers, recall@2048 vs exact fp64 logits "
+                        "(fixed plans scored without the side stream's term)",
+            **{name: {"recall": round(float(np.mean(rec[name])), 4),
+                      "union_bits_per_kv_head": round(float(np.mean(bits[name])), 1)}
+               for name, _ in kinds}}
+
+
 def bench_sessions(dev, steps, warmup):
     """16 ragged sessions (64K..512K keys), per-session B, planes in pinned host
     memory, one batched scan and one batched top-k (k = 1024 per query head)."""
@@ -534,6 +589,17 @@ def main():
                                       **{k: round(x, 4) for k, x in t.items()}}
                 log(f"{var} {mode}_fused: {t}")
             variants[var] = v
+        # the r = 16 analogue of the baseline (64 plane bits + the 8-bit side
+        # stream per query head): the pages compare Fathom with it at equal time
+        fper16 = [union_plane_bytes(fathom.plan_fixed(L.q, 16), w.hkv, w.n) for L in layers]
+        v = {"union_plane_bytes": int(np.mean([x[0] for x in fper16])),
+             "meta_bytes": w.hkv * w.n, "union_bits_per_kv_head": fper16[0][1]}
+        for mode in res_modes(args):
+            t = timed(layers, w, fws, args.steps, args.warmup, mode, fixed=16, fused=True)
+            v[mode + "_fused"] = {"keys_per_s": round(w.n * w.hkv / (t["step_ms"] * 1e-3), 1),
+                                  **{k: round(x, 4) for k, x in t.items()}}
+            log(f"fixed r=16 {mode}_fused: {t}")
+        variants["fixed_r16"] = v
 
     keys_per_step = w.n * w.hkv
     main_mode = "host" if "host" in res else "hbm"
@@ -606,7 +672,15 @@ def main():
                     "depth_histogram": hist}
     if variants:
         variants["note"] = ("B=92 per query head (rd) or per kv head (group: the whole GQA "
-                            "group reads 92 plane bits per key); fused scan + top-k steps")
+                            "group reads 92 plane bits per key); fixed_r16: top-16 |q| channels "
+                            "x 4 bits + the 8-bit side stream; fused scan + top-k steps")
+        f16 = variants["fixed_r16"]
+        fb = plane_b
+        variants["fathom_vs_fixed_r16"] = {
+            "byte_ratio": round(fb / (f16["union_plane_bytes"] + f16["meta_bytes"]), 4),
+            **{m + "_time_ratio": round(res[m + "_fused"]["step_ms"] /
+                                        f16[m + "_fused"]["step_ms"], 4)
+               for m in res_modes(args)}}
         out["plan_variants"] = variants
     out["probe"] = probe
     if not args.no_cpu:
@@ -626,6 +700,9 @@ def main():
         torch.cuda.empty_cache()
         extra["step_36_layers"] = bench_step36(dev, 3, 1)
         log(f"36-layer step: {extra['step_36_layers']}")
+        torch.cuda.empty_cache()
+        extra["plan_quality"] = plan_quality(dev)
+        log(f"plan quality: {extra['plan_quality']}")
         out["other_workloads"] = extra
     print(json.dumps(out), flush=True)
 

@@ -144,7 +144,7 @@ __device__ __forceinline__ void nibbles_to_f32(uint32_t y, float (&f)[8]) {
 }
 
 // Rows 4j+p of x receive bit p of slot (grp*8 + j)'s code: plane slot 3-p of
-// its channel, loaded only when the slot's depth covers it.  Loads are
+// its channel, loaded only when it lies in the slot's plane range.  Loads are
 // buffer loads: a wave-uniform resource per channel (its 4 plane rows), a
 // wave-uniform row + block offset, and the lane's 32-bit byte offset `voff`.
 // The resource's size also bounds every access.
@@ -158,14 +158,14 @@ __device__ __forceinline__ void load_group(const uint32_t *__restrict__ gplanes,
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int desc = uniform(slot_desc[grp * 8 + j]);
-    const int c = desc >> 3, dep = desc & 7;
+    const int c = (desc >> 3) & (kD - 1), dep = desc & 7, top = desc >> 10;
     const uint32_t *pc = gplanes + (int64_t)c * kPlanes * W;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint32_t *>(pc), (short)0, (int32_t)(W * kPlanes * 4), kRsrcWord3);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       uint32_t v = 0;
-      if (3 - p < dep)
+      if (3 - p < dep && 3 - p >= top)
         v = __builtin_amdgcn_raw_buffer_load_b32(
             rsrc, (int32_t)voff, (int32_t)(((3 - p) * W + wbase) * 4), AUX);
       x[4 * j + p] = v;
@@ -174,14 +174,17 @@ __device__ __forceinline__ void load_group(const uint32_t *__restrict__ gplanes,
 }
 
 // ---- slot table (per block: one session, one kv head, GH query heads) ------
-// Slots are the distinct (channel, depth) pairs the GH heads read.  A slot of
-// depth u stands for the value of the channel's top u planes, placed at their
-// own bit positions; head h uses exactly the slots at its own depths with
-// weight gamma = q_hc * delta_c.  Slots are ordered by the set of heads using
-// them (larger sets first), then channel, then depth.
+// Slots are the distinct (channel, depth) pairs the GH heads read.  With
+// u_1 < u_2 < ... the distinct depths of channel c among the heads, slot
+// (c, u_k) stands for the plane slots u_{k-1} .. u_k - 1 of the channel
+// (u_0 = 0), placed at their own bit positions, so every plane is loaded once
+// per channel; a head reading c to depth t uses the slots with u_k <= t, each
+// with weight gamma = q_hc * delta_c, and their values add up to its top t
+// planes.  Slots are ordered by the set of heads using them (larger sets
+// first), then channel, then depth.
 template <int GH>
 struct SlotTable {
-  int16_t desc[kMaxSlots];       // (channel << 3) | depth; 0 = padding slot
+  int16_t desc[kMaxSlots];       // (u_{k-1} << 10) | (channel << 3) | u_k; 0 = padding
   float gam[kMaxSlots][GH];      // gamma per slot and head (0: head does not use it)
   uint8_t gmask[kMaxGroups];     // heads using any slot of an 8-slot group
   float C[GH];                   // C_h = sum_c q_hc (lo_c + delta_c 2^(3 - t_hc))
@@ -260,9 +263,13 @@ __device__ void build_slot_table(SlotTable<GH> &T, SlotScratch<GH> &X, KScanSess
     if (e >= kD * 4) continue;  // blocks of more than kD*4 threads
     const int c = e >> 2, dep = (e & 3) + 1;
     int memb = 0;
+    bool exact = false;
 #pragma unroll
-    for (int j = 0; j < GH; ++j) memb |= (X.t[j][c] == dep) << j;
-    const int k = memb_class(memb);
+    for (int j = 0; j < GH; ++j) {
+      memb |= (X.t[j][c] >= dep) << j;
+      exact |= X.t[j][c] == dep;
+    }
+    const int k = exact ? memb_class(memb) : 15;
     const uint64_t lt = (1ull << lane) - 1ull;
 #pragma unroll
     for (int kk = 0; kk < 15; ++kk) {
@@ -303,7 +310,13 @@ __device__ void build_slot_table(SlotTable<GH> &T, SlotScratch<GH> &X, KScanSess
     if (e >= kD * 4 || k == 15) continue;
     const int c = e >> 2, dep = (e & 3) + 1;
     const int rank = X.cbase[k] + X.wpre[e >> 6][k] + pre_e[it];
-    T.desc[rank] = (int16_t)((c << 3) | dep);
+    int top = 0;  // the next smaller depth read in this channel
+#pragma unroll
+    for (int j = 0; j < GH; ++j) {
+      const int tj = X.t[j][c];
+      if (tj < dep && tj > top) top = tj;
+    }
+    T.desc[rank] = (int16_t)((top << 10) | (c << 3) | dep);
     const float delta = X.delta[c];
 #pragma unroll
     for (int j = 0; j < GH; ++j) {
@@ -694,8 +707,9 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t desc = __builtin_amdgcn_readfirstlane((dw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-      const uint32_t c = desc >> 3, dep = desc & 7u;
-      const uint32_t voff = plane_sl < dep ? c * chan_bytes + tile_off + lane_part : kUnread;
+      const uint32_t c = (desc >> 3) & (kD - 1), dep = desc & 7u, top = desc >> 10;
+      const uint32_t voff =
+          plane_sl < dep && plane_sl >= top ? c * chan_bytes + tile_off + lane_part : kUnread;
       const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int32_t)voff, 0, 0);
       x[4 * i + 0] = (uint32_t)v[0];
       x[4 * i + 1] = (uint32_t)v[1];
