@@ -432,3 +432,71 @@ int orc_topk(const float *scores, int rows, int64_t n, int64_t ld, int group,
   free(all);
   return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Sparse decode attention over the selected keys.  [EXP] problem statement:
+ * every generated token runs attention over the top k of the n keys the scan
+ * kept; "与 V 端稀疏化互补" and the future-work list: V stays dense.  The
+ * pages give no layout for this step.  Reading R19: full-precision K and V
+ * rows of the selected keys (token-major, fp16 widened exactly to fp32 by the
+ * caller of this function), softmax over the selected keys only:
+ *   s_i = scale * sum_c q_c K_ic,  m = max s_i,  p_i = exp(s_i - m),
+ *   out_c = sum_i p_i V_ic / sum_i p_i,  lse = m + log(sum_i p_i),
+ * all in fp64 and rounded once to fp32.  Entries of idx below 0 are skipped
+ * (the padding of short rows); an entry listed twice counts twice.  A row
+ * with no entry gives out = 0 and lse = -inf.
+ * q [hq][d]; K, V element (token i, kv head g, channel c) at
+ * [i*stride_tok + g*stride_head + c]; idx [hq/group][k] (row o serves query
+ * heads o*group .. o*group+group-1, which share one kv head);
+ * out [hq][d], lse [hq].                                                    */
+int orc_sparse_attention(const float *q, int hq, int hkv, int d, const float *K,
+                         const float *V, int64_t n, int64_t stride_tok,
+                         int64_t stride_head, const int32_t *idx, int group, int k,
+                         float scale, float *out, float *lse) {
+  if (!q || !K || !V || !idx || !out || !lse || hq < 1 || hkv < 1 || d < 1 ||
+      hq % hkv || group < 1 || (hq / hkv) % group || k < 0 || n < 0)
+    return ORC_BAD;
+  const int G = hq / hkv;
+  double *s = (double *)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+  double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+  if (!s || !acc) {
+    free(s);
+    free(acc);
+    return ORC_BAD;
+  }
+  for (int o = 0; o < hq / group; ++o) {
+    const int32_t *row = idx + (int64_t)o * k;
+    for (int j = 0; j < k; ++j)
+      if (row[j] >= n) {
+        free(s);
+        free(acc);
+        return ORC_BAD;
+      }
+    for (int r = 0; r < group; ++r) {
+      const int h = o * group + r, g = h / G;
+      double m = -INFINITY;
+      for (int j = 0; j < k; ++j) {
+        if (row[j] < 0) continue;
+        const float *kr = K + (int64_t)row[j] * stride_tok + (int64_t)g * stride_head;
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c) dot += (double)q[(int64_t)h * d + c] * (double)kr[c];
+        s[j] = (double)scale * dot;
+        if (s[j] > m) m = s[j];
+      }
+      double l = 0.0;
+      for (int c = 0; c < d; ++c) acc[c] = 0.0;
+      for (int j = 0; j < k; ++j) {
+        if (row[j] < 0) continue;
+        const double p = exp(s[j] - m);
+        const float *vr = V + (int64_t)row[j] * stride_tok + (int64_t)g * stride_head;
+        l += p;
+        for (int c = 0; c < d; ++c) acc[c] += p * (double)vr[c];
+      }
+      for (int c = 0; c < d; ++c) out[(int64_t)h * d + c] = l > 0.0 ? (float)(acc[c] / l) : 0.0f;
+      lse[h] = l > 0.0 ? (float)(m + log(l)) : -INFINITY;
+    }
+  }
+  free(s);
+  free(acc);
+  return ORC_OK;
+}

@@ -53,9 +53,10 @@ def _load():
         lib.orc_scan_at.argtypes = [P, P, P, L, I, I, P, P, I, P, F, P, L, P]
         lib.orc_read_prefixes.argtypes = [P, L, I, I, P, I, P]
         lib.orc_topk.argtypes = [P, I, L, L, I, I, P, P]
+        lib.orc_sparse_attention.argtypes = [P, I, I, I, P, P, L, L, L, P, I, I, F, P, P]
         for f in ("orc_pack", "orc_plan", "orc_plan_fixed", "orc_plan_rd", "orc_plan_group",
                   "orc_scan", "orc_scan_at",
-                  "orc_read_prefixes", "orc_topk"):
+                  "orc_read_prefixes", "orc_topk", "orc_sparse_attention"):
             getattr(lib, f).restype = I
         _lib = lib
     return _lib
@@ -197,3 +198,23 @@ def topk(scores, k: int, group: int = 1):
     _check(_load().orc_topk(_ptr(scores), rows, n, max(n, 1), group, k,
                             _ptr(idx), _ptr(vals)), "topk")
     return idx, vals
+
+
+def sparse_attention(q, K, V, idx, group: int = 1, scale=None):
+    """q [hq][d]; K, V [n][hkv][d] (fp16 or fp32); idx [hq/group][k] int32
+    -> (out [hq][d] fp32, lse [hq] fp32).  scale defaults to 1/sqrt(d)."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    K = np.ascontiguousarray(K, dtype=np.float32)
+    V = np.ascontiguousarray(V, dtype=np.float32)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    hq, d = q.shape
+    n, hkv, _ = K.shape
+    k = idx.shape[1]
+    if scale is None:
+        scale = float(np.float32(1.0 / np.sqrt(d)))
+    out = np.empty((hq, d), np.float32)
+    lse = np.empty(hq, np.float32)
+    _check(_load().orc_sparse_attention(_ptr(q), hq, hkv, d, _ptr(K), _ptr(V), n, hkv * d, d,
+                                        _ptr(idx), group, k, scale, _ptr(out), _ptr(lse)),
+           "sparse_attention")
+    return out, lse

@@ -639,3 +639,127 @@ def test_scan_at_equals_full_scan(orc):
     pick = np.array([0, 699, 5, 31, 32, 64, 333])
     part = orc.scan_at(p["planes"], p["lo"], p["hi"], n, q, plan, pick, meta, 0.5)
     np.testing.assert_array_equal(part, full[:, pick])
+
+
+# --------------------------------------------------------------------------
+# sparse decode attention over the selected keys
+
+def attn_inputs(seed, n=300, hkv=2, hq=8, d=32):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((hq, d)).astype(np.float32)
+    K = rng.standard_normal((n, hkv, d)).astype(np.float16)
+    V = rng.standard_normal((n, hkv, d)).astype(np.float16)
+    return rng, q, K, V
+
+
+def sdpa_rows(q, K, V, rows_idx, G, scale):
+    """torch's dense scaled-dot-product attention (CPU, fp64) over the listed
+    key rows of each head's kv head."""
+    import torch
+    hq, d = q.shape
+    out = np.zeros((hq, d))
+    for h in range(hq):
+        sel = rows_idx[h]
+        k_ = torch.from_numpy(K[sel, h // G, :].astype(np.float64))[None, None]
+        v_ = torch.from_numpy(V[sel, h // G, :].astype(np.float64))[None, None]
+        q_ = torch.from_numpy(q[h].astype(np.float64))[None, None, None]
+        out[h] = torch.nn.functional.scaled_dot_product_attention(
+            q_, k_, v_, scale=scale)[0, 0, 0].numpy()
+    return out
+
+
+def test_sparse_attention_all_keys_is_dense_attention(orc):
+    _, q, K, V = attn_inputs(1)
+    n, hkv, d = K.shape
+    G = q.shape[0] // hkv
+    idx = np.tile(np.arange(n, dtype=np.int32), (q.shape[0], 1))
+    scale = float(np.float32(1 / np.sqrt(d)))
+    out, lse = orc.sparse_attention(q, K, V, idx)
+    ref = sdpa_rows(q, K, V, [np.arange(n)] * q.shape[0], G, scale)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-6)
+
+
+def test_sparse_attention_subset_and_duplicates_match_dense_on_rows(orc):
+    rng, q, K, V = attn_inputs(2)
+    n, hkv, d = K.shape
+    G = q.shape[0] // hkv
+    idx = rng.integers(0, n, (q.shape[0], 37)).astype(np.int32)
+    idx[:, 5] = idx[:, 6]                              # a key listed twice counts twice
+    out, _ = orc.sparse_attention(q, K, V, idx, scale=0.3)
+    ref = sdpa_rows(q, K, V, list(idx), G, 0.3)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-6)
+
+
+def test_sparse_attention_lse_is_logsumexp(orc):
+    from scipy.special import logsumexp
+    rng, q, K, V = attn_inputs(3)
+    n, hkv, d = K.shape
+    G = q.shape[0] // hkv
+    idx = rng.choice(n, (q.shape[0], 50)).astype(np.int32)
+    _, lse = orc.sparse_attention(q, K, V, idx, scale=0.7)
+    for h in range(q.shape[0]):
+        s = 0.7 * (K[idx[h], h // G, :].astype(np.float64) @ q[h].astype(np.float64))
+        assert abs(lse[h] - logsumexp(s)) <= 1e-6 * max(1.0, abs(logsumexp(s)))
+
+
+def test_sparse_attention_zero_query_averages_values(orc):
+    rng, q, K, V = attn_inputs(4)
+    q[:] = 0.0
+    n, hkv, d = K.shape
+    G = q.shape[0] // hkv
+    idx = np.stack([rng.choice(n, 20, replace=False) for _ in range(q.shape[0])]).astype(np.int32)
+    out, lse = orc.sparse_attention(q, K, V, idx)
+    for h in range(q.shape[0]):
+        np.testing.assert_allclose(out[h], V[idx[h], h // G, :].astype(np.float64).mean(0),
+                                   rtol=0, atol=1e-6)
+        assert abs(lse[h] - np.log(20)) < 1e-6
+
+
+def test_sparse_attention_dominant_key_returns_its_value(orc):
+    rng, q, K, V = attn_inputs(5, hq=2, hkv=1)
+    q[:] = 0.0
+    q[:, 0] = 1.0
+    K[:, 0, 0] = 0.0
+    K[17, 0, 0] = 8.0                                  # score gap 8 * 50 = 400
+    idx = np.array([[3, 17, 40, 99]] * 2, np.int32)
+    out, lse = orc.sparse_attention(q, K, V, idx, scale=50.0)
+    np.testing.assert_array_equal(out[0], V[17, 0, :].astype(np.float32))
+    assert lse[0] == np.float32(400.0)
+
+
+def test_sparse_attention_permutation_padding_and_group(orc):
+    rng, q, K, V = attn_inputs(6)
+    n, hkv, d = K.shape
+    hq = q.shape[0]
+    G = hq // hkv
+    idx = np.stack([rng.choice(n, 40, replace=False) for _ in range(hq)]).astype(np.int32)
+    out, lse = orc.sparse_attention(q, K, V, idx)
+    perm = idx[:, rng.permutation(40)]
+    o2, l2 = orc.sparse_attention(q, K, V, perm)
+    np.testing.assert_allclose(o2, out, rtol=0, atol=1e-6)
+    padded = np.concatenate([idx[:, :13], -np.ones((hq, 9), np.int32), idx[:, 13:]], 1)
+    o3, l3 = orc.sparse_attention(q, K, V, padded)
+    np.testing.assert_array_equal(o3, out)
+    np.testing.assert_array_equal(l3, lse)
+    # group mode: one idx row per group of G heads equals that row repeated
+    gidx = idx[::G]
+    og, lg = orc.sparse_attention(q, K, V, gidx, group=G)
+    orep, lrep = orc.sparse_attention(q, K, V, np.repeat(gidx, G, axis=0))
+    np.testing.assert_array_equal(og, orep)
+    np.testing.assert_array_equal(lg, lrep)
+    # groups of 2 inside GQA groups of 4
+    o2g, _ = orc.sparse_attention(q, K, V, idx[::2], group=2)
+    np.testing.assert_array_equal(o2g, orc.sparse_attention(q, K, V, np.repeat(idx[::2], 2, 0))[0])
+
+
+def test_sparse_attention_empty_rows_and_rejections(orc):
+    _, q, K, V = attn_inputs(7)
+    hq = q.shape[0]
+    out, lse = orc.sparse_attention(q, K, V, -np.ones((hq, 5), np.int32))
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+    out, lse = orc.sparse_attention(q, K, V, np.zeros((hq, 0), np.int32))
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+    with pytest.raises(ValueError):
+        orc.sparse_attention(q, K, V, np.full((hq, 3), K.shape[0], np.int32))
+    with pytest.raises(ValueError):                    # groups must not straddle kv heads
+        orc.sparse_attention(q, K, V, np.zeros((1, 3), np.int32), group=8)
