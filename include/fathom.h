@@ -3,6 +3,7 @@
  * path over a 4-bit, channel-major, bit-plane K cache:
  *
  *     fathom_pack -> fathom_plan -> fathom_scan -> fathom_topk
+ *                                  (-> fathom_sparse_attention)
  *
  * The method is the one described on the pages about "Fathom: Per-Query Read
  * Depth for Sparse Decoding over Offloaded KV Caches" (arXiv 2609.17652);
@@ -45,6 +46,7 @@ extern "C" {
 #define FATHOM_HEAD_DIM 128
 #define FATHOM_MAX_K 2048         /* largest k accepted by the top-k calls */
 #define FATHOM_MAX_SESSIONS 64    /* sessions per batched call */
+#define FATHOM_MAX_ATTN_K (1 << 20) /* selected keys per row of sparse attention */
 
 enum {
   FATHOM_OK = 0,
@@ -250,6 +252,44 @@ int32_t fathom_scan_topk_batched(const fathom_session *sessions,
                                  int32_t n_sessions, int32_t hkv, int32_t d,
                                  int32_t hq, int32_t group, int32_t k, void *ws,
                                  int64_t ws_bytes, void *stream);
+
+/* ---- sparse attention over the selected keys -------------------------------
+ * Explainer, problem statement: each generated token attends over the top k
+ * of its n keys; the future-work list keeps V dense.  The pages do not lay
+ * this step out.  Here the selected keys' full-precision K and V rows are
+ * gathered (token-major, in HBM or pinned host memory) and, per query head h
+ * with kv head g = h / (hq / hkv), over the entries of its index row:
+ *   s_i = scale * sum_c q_hc K_igc   (fp32 products and sums, channel order)
+ *   m = max s_i, p_i = exp(s_i - m), out_h = sum_i p_i V_ig / sum_i p_i,
+ *   lse_h = m + log(sum_i p_i)       (natural log)
+ * in fp32 (per 64 entries a partial (m, sum p, sum p V), merged by maxima).
+ *
+ * q        device fp32[hq][d]
+ * k_cache, v_cache  device or pinned-host rows of `dtype` (FATHOM_F16 or
+ *          FATHOM_F32); element (token i, kv head g, channel c) at
+ *          [i*stride_tok + g*stride_head + c].  Both 16-byte aligned, strides
+ *          multiples of 16 bytes (else FATHOM_ERR_UNSUPPORTED).  May be NULL
+ *          when n == 0.
+ * idx      device int32[hq/group][k]: row o serves query heads o*group ..
+ *          o*group+group-1 (group 1, 2, 4 or 8, dividing hq/hkv); e.g. the
+ *          idx of fathom_topk / fathom_scan_topk with the same group.
+ *          Entries < 0 (the padding of short rows) or >= n are skipped
+ *          without any memory access; an entry listed twice counts twice.
+ *          May be NULL when k == 0.
+ * scale    finite softmax scale (1/sqrt(d) for standard attention).
+ * out      device output fp32[hq][d]; lse device output fp32[hq].  A head
+ *          with no valid entry gets out = 0 and lse = -inf.
+ * ws       device workspace of fathom_attention_workspace_bytes(hq, k)
+ *          bytes (may be NULL when k == 0).
+ * Enqueues 2 kernels; 0 <= k <= FATHOM_MAX_ATTN_K.                         */
+int64_t fathom_attention_workspace_bytes(int32_t hq, int32_t k);
+int32_t fathom_sparse_attention(const float *q, int32_t hq, int32_t hkv, int32_t d,
+                                const void *k_cache, const void *v_cache,
+                                int32_t dtype, int64_t n, int64_t stride_tok,
+                                int64_t stride_head, const int32_t *idx,
+                                int32_t group, int32_t k, float scale, float *out,
+                                float *lse, void *ws, int64_t ws_bytes,
+                                void *stream);
 
 /* ---- observability -------------------------------------------------------
  * The plane reads themselves, for bit-exact checks: out[h][i][c] =

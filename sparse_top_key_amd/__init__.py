@@ -65,6 +65,9 @@ def lib():
             "fathom_plan_fixed": (I32, [P, I32, I32, I32, P, P]),
             "fathom_plan_rd": (I32, [P, I32, I32, I32, P, P, P, P]),
             "fathom_plan_group": (I32, [P, I32, I32, I32, P, P, P, P]),
+            "fathom_attention_workspace_bytes": (I64, [I32, I32]),
+            "fathom_sparse_attention": (I32, [P, I32, I32, I32, P, P, I32, I64, I64, I64, P,
+                                              I32, I32, F, P, P, P, I64, P]),
             "fathom_scan": (I32, [P, P, P, I64, I32, I32, P, P, I32, P, F, P, I64, P]),
             "fathom_topk": (I32, [P, I32, I64, I64, I32, I32, P, P, P, I64, P]),
             "fathom_scan_batched": (I32, [P, I32, I32, I32, I32, P]),
@@ -330,6 +333,46 @@ def scan_topk_batched(sess: Sequence[Session], k: int, group: int = 1,
     _check(lib().fathom_scan_topk_batched(_sessions(sess), len(sess), hkv, d, hq, group, k,
                                           _p(ws), ws.numel(), _stream(s0.q.device)),
            "fathom_scan_topk_batched")
+
+
+def attention_workspace_bytes(hq: int, k: int) -> int:
+    return int(lib().fathom_attention_workspace_bytes(hq, k))
+
+
+def sparse_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                     idx: torch.Tensor, group: int = 1, scale: Optional[float] = None,
+                     out=None, lse=None, ws=None):
+    """Attention of each query head over its selected keys.
+
+    q fp32 [hq][d]; k_cache, v_cache [n][hkv][d] fp16 or fp32 (device or
+    pinned host, same strides, channel stride 1); idx int32 [hq/group][k]
+    (entries < 0 or >= n skipped).  -> (out fp32 [hq][d], lse fp32 [hq])."""
+    _require_gpu(q, k_cache, v_cache, idx)
+    hq, d = q.shape
+    n, hkv, _ = k_cache.shape
+    if k_cache.stride() != v_cache.stride() or k_cache.dtype != v_cache.dtype:
+        raise FathomError("k_cache and v_cache must share dtype and strides")
+    if k_cache.stride(2) != 1:
+        raise FathomError("channel stride of the caches must be 1")
+    dtype = {torch.float16: F16, torch.float32: F32}.get(k_cache.dtype)
+    if dtype is None:
+        raise FathomError("caches must be float16 or float32")
+    k = idx.shape[1]
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    dev = q.device
+    if out is None:
+        out = torch.empty((hq, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((hq,), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(max(attention_workspace_bytes(hq, k), 1), dtype=torch.uint8, device=dev)
+    _check(lib().fathom_sparse_attention(_p(q.contiguous()), hq, hkv, d, _p(k_cache), _p(v_cache),
+                                         dtype, n, k_cache.stride(0), k_cache.stride(1),
+                                         _p(idx.contiguous()), group, k, float(scale), _p(out),
+                                         _p(lse), _p(ws), ws.numel(), _stream(dev)),
+           "fathom_sparse_attention")
+    return out, lse
 
 
 def read_prefixes(planes: torch.Tensor, n: int, plan_: torch.Tensor, hkv: int) -> torch.Tensor:

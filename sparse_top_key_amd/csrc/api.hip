@@ -1,5 +1,6 @@
 // Exported C ABI of libfathom (declared in include/fathom.h): argument
 // validation on the host, then kernel launches on the caller's stream.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -132,6 +133,54 @@ int32_t fathom_plan_group(const float *q, int32_t hq, int32_t hkv, int32_t d,
             "fathom_plan_group: budget_bits[%d] = %d outside [0, %d]", g, budget_bits[g],
             4 * d);
   return launch_plan_group(q, hq, hkv, sigma2, budget_bits, plan, as_stream(stream));
+}
+
+int64_t fathom_attention_workspace_bytes(int32_t hq, int32_t k) {
+  if (hq < 1 || k < 0 || k > FATHOM_MAX_ATTN_K) return 0;
+  return attn_workspace_bytes(hq, k);
+}
+
+int32_t fathom_sparse_attention(const float *q, int32_t hq, int32_t hkv, int32_t d,
+                                const void *k_cache, const void *v_cache, int32_t dtype,
+                                int64_t n, int64_t stride_tok, int64_t stride_head,
+                                const int32_t *idx, int32_t group, int32_t k, float scale,
+                                float *out, float *lse, void *ws, int64_t ws_bytes,
+                                void *stream) {
+  REQUIRE(q && out && lse && (idx || k == 0), FATHOM_ERR_INVALID_ARG,
+          "fathom_sparse_attention: null pointer");
+  if (int32_t rc = check_heads(hq, hkv)) return rc;
+  if (int32_t rc = check_d(d)) return rc;
+  REQUIRE(dtype == FATHOM_F16 || dtype == FATHOM_F32, FATHOM_ERR_INVALID_ARG,
+          "fathom_sparse_attention: dtype must be FATHOM_F16 or FATHOM_F32 (got %d)", dtype);
+  REQUIRE(n >= 0 && n <= ((int64_t)1 << 31), FATHOM_ERR_INVALID_ARG,
+          "fathom_sparse_attention: n must be in [0, 2^31] (got %lld)", (long long)n);
+  REQUIRE(n == 0 || (k_cache && v_cache), FATHOM_ERR_INVALID_ARG,
+          "fathom_sparse_attention: null K or V cache");
+  REQUIRE(k >= 0 && k <= FATHOM_MAX_ATTN_K, FATHOM_ERR_INVALID_ARG,
+          "fathom_sparse_attention: k must be in [0, %d] (got %d)", FATHOM_MAX_ATTN_K, k);
+  REQUIRE(group >= 1 && (hq / hkv) % group == 0, FATHOM_ERR_INVALID_ARG,
+          "fathom_sparse_attention: group (%d) must divide hq / hkv (%d)", group, hq / hkv);
+  REQUIRE(group == 1 || group == 2 || group == 4 || group == 8, FATHOM_ERR_UNSUPPORTED,
+          "fathom_sparse_attention: group must be 1, 2, 4 or 8 (got %d)", group);
+  REQUIRE(hq / group <= 65535, FATHOM_ERR_UNSUPPORTED,
+          "fathom_sparse_attention: at most 65535 index rows (got %d)", hq / group);
+  REQUIRE(std::isfinite(scale), FATHOM_ERR_INVALID_ARG,
+          "fathom_sparse_attention: scale must be finite");
+  REQUIRE(stride_tok >= 0 && stride_head >= 0, FATHOM_ERR_INVALID_ARG,
+          "fathom_sparse_attention: strides must be non-negative");
+  const int64_t vec = dtype == FATHOM_F16 ? 8 : 4;  // elements per 16 bytes
+  REQUIRE(stride_tok % vec == 0 && stride_head % vec == 0 &&
+              (reinterpret_cast<uintptr_t>(k_cache) & 15) == 0 &&
+              (reinterpret_cast<uintptr_t>(v_cache) & 15) == 0,
+          FATHOM_ERR_UNSUPPORTED,
+          "fathom_sparse_attention: K and V rows must start on 16-byte boundaries "
+          "(16-byte aligned caches, strides multiples of %lld elements)", (long long)vec);
+  const int64_t need = attn_workspace_bytes(hq, k);
+  REQUIRE(k == 0 || (ws && ws_bytes >= need), FATHOM_ERR_WORKSPACE,
+          "fathom_sparse_attention: workspace of %lld bytes needed (got %lld)",
+          (long long)need, (long long)ws_bytes);
+  return launch_attention(q, hq, hkv, k_cache, v_cache, dtype, n, stride_tok, stride_head, idx,
+                          group, k, scale, out, lse, ws, as_stream(stream));
 }
 
 int32_t fathom_plan_fixed(const float *q, int32_t hq, int32_t d, int32_t r, uint8_t *plan,

@@ -75,6 +75,13 @@ int32_t launch_plan_group(const float *q, int32_t hq, int32_t hkv,
 int32_t launch_plan_fixed(const float *q, int32_t hq, int32_t r, uint8_t *plan,
                           hipStream_t s);
 
+// ---- sparse attention -------------------------------------------------------
+int64_t attn_workspace_bytes(int32_t hq, int32_t k);
+int32_t launch_attention(const float *q, int32_t hq, int32_t hkv, const void *kc,
+                         const void *vc, int32_t dtype, int64_t n, int64_t stride_tok,
+                         int64_t stride_head, const int32_t *idx, int32_t group, int32_t k,
+                         float scale, float *out, float *lse, void *ws, hipStream_t s);
+
 // ---- scan -------------------------------------------------------------------
 struct ScanSession {
   const uint32_t *planes;

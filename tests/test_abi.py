@@ -225,3 +225,35 @@ def test_product_path_refuses_to_run_without_gpu():
         pytest.skip("a GPU is visible")
     with pytest.raises(fathom.FathomError):
         fathom.pack(torch.zeros((64, 1, 128), dtype=torch.float16))
+
+
+def test_attention_validation(L):
+    A = ctypes.c_void_p(0x10000)                  # 16-byte aligned dummy
+    U = ctypes.c_void_p(0x10008)                  # 8-byte aligned only
+    ws = L.fathom_attention_workspace_bytes(8, 2048)
+    assert ws == 8 * 32 * 130 * 4
+    assert L.fathom_attention_workspace_bytes(8, -1) == 0
+    base = [A, 8, 2, 128, A, A, 0, 1000, 256, 128, A, 1, 2048, ctypes.c_float(0.1), A, A, A,
+            ws, None]
+
+    def call(**kw):
+        # every case below fails validation, so nothing is ever enqueued
+        a = list(base)
+        pos = dict(q=0, hq=1, hkv=2, d=3, kc=4, vc=5, dtype=6, n=7, st=8, sh=9, idx=10,
+                   group=11, k=12, scale=13, ws=16, wsb=17)
+        for key, v in kw.items():
+            a[pos[key]] = v
+        return L.fathom_sparse_attention(*a)
+    assert call(q=None) == 1
+    assert call(hkv=3) == 1
+    assert call(d=64) == 2
+    assert call(dtype=5) == 1
+    assert call(kc=None) == 1
+    assert call(group=3) == 1                     # does not divide hq / hkv = 4
+    assert call(group=8) == 1
+    assert call(kc=U) == 2 and "16-byte" in err(L)
+    assert call(st=260) == 2
+    assert call(k=-1) == 1
+    assert call(wsb=ws - 1) == 4
+    assert call(scale=ctypes.c_float(float("inf"))) == 1
+    assert call(n=-1) == 1
