@@ -381,6 +381,71 @@ def plan_quality(dev, layers_q=2):
                for name, _ in kinds}}
 
 
+def bench_attention(dev, steps, warmup):
+    """Sparse attention over the k = 2048 keys fathom_scan_topk selects on the
+    1M-key layer (fp16 K and V, token-major), alone and as the last call of
+    the decode step plan -> scan_topk -> attention; K/V and planes in HBM and
+    in pinned host memory."""
+    w = synth.LAYER_1M
+    keys = synth.keys(w.seed, 0, w.n, w.hkv, w.d, w.dtype, w.outliers, device=dev)
+    vals = synth.keys(w.seed + 1, 0, w.n, w.hkv, w.d, w.dtype, 0, device=dev)
+    q = synth.queries(w.seed, 0, w.hq, w.d, device=dev)
+    p = fathom.pack(keys)
+    host = {}
+    for name, t in (("planes", p.planes), ("k", keys), ("v", vals)):
+        host[name] = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+        host[name].copy_(t)
+    plan = fathom.plan(q, p.sigma2, w.budget)
+    out = {"workload": "1M-key layer, fp16 K/V [n][8][128], 32 query heads, k=2048 selected keys"}
+    for group in (1, 4):
+        rows = w.hq // group
+        fws = torch.empty(fathom.scan_topk_workspace_bytes([w.n], w.hkv, w.hq, group, w.k),
+                          dtype=torch.uint8, device=dev)
+        idx = torch.empty((rows, w.k), dtype=torch.int32, device=dev)
+        vls = torch.empty((rows, w.k), dtype=torch.float32, device=dev)
+        fathom.scan_topk(p.planes, p.lo, p.hi, w.n, q, plan, w.k, group, ws=fws, idx=idx,
+                         vals=vls)
+        aws = torch.empty(fathom.attention_workspace_bytes(w.hq, w.k), dtype=torch.uint8,
+                          device=dev)
+        o = torch.empty((w.hq, w.d), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.hq,), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        nvalid = int((idx >= 0).sum())
+        alg = nvalid * 2 * w.d * 2 + idx.numel() * 4   # K and V rows + the indices
+        for res in ("hbm", "host"):
+            Kc, Vc = (keys, vals) if res == "hbm" else (host["k"], host["v"])
+            planes = p.planes if res == "hbm" else host["planes"]
+
+            def attn():
+                fathom.sparse_attention(q, Kc, Vc, idx, group, out=o, lse=lse, ws=aws)
+
+            def step():
+                fathom.plan(q, p.sigma2, w.budget, out=plan)
+                fathom.scan_topk(planes, p.lo, p.hi, w.n, q, plan, w.k, group, ws=fws,
+                                 idx=idx, vals=vls)
+                attn()
+            for fn, label in ((attn, "attention"), (step, "decode_step")):
+                for _ in range(warmup):
+                    fn()
+                torch.cuda.synchronize()
+                a, b = _event_pair()
+                a.record()
+                for _ in range(steps):
+                    fn()
+                b.record()
+                torch.cuda.synchronize()
+                ms = a.elapsed_time(b) / steps
+                rec = {"ms": round(ms, 4)}
+                if label == "attention":
+                    gbps = alg / (ms * 1e-3) / 1e9
+                    peak = HBM_PEAK_GBPS if res == "hbm" else PCIE_PEAK_GBPS
+                    rec.update({"algorithmic_bytes": alg, "GBps": round(gbps, 1),
+                                "frac_of_peak": round(gbps / peak, 4)})
+                out[f"group{group}_{res}_{label}"] = rec
+    del keys, vals, host
+    return out
+
+
 def bench_sessions(dev, steps, warmup):
     """16 ragged sessions (64K..512K keys), per-session B, planes in pinned host
     memory, one batched scan and one batched top-k (k = 1024 per query head)."""
@@ -700,6 +765,9 @@ def main():
         torch.cuda.empty_cache()
         extra["step_36_layers"] = bench_step36(dev, 3, 1)
         log(f"36-layer step: {extra['step_36_layers']}")
+        torch.cuda.empty_cache()
+        extra["attention_1m"] = bench_attention(dev, 20, 3)
+        log(f"attention: {extra['attention_1m']}")
         torch.cuda.empty_cache()
         extra["plan_quality"] = plan_quality(dev)
         log(f"plan quality: {extra['plan_quality']}")

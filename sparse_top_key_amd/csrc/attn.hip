@@ -8,13 +8,13 @@
 //   lse = m + log(sum p_i)  over the listed keys of each row.
 //
 // Two launches.  attn_partial_kernel: a 256-thread block takes 256 entries of
-// one index row; each wave owns 64 entries and produces a partial
-// (m, l, o[128]) per query head of the row.  Lane j scores entry j from its
-// own K row (16-byte loads, q broadcast from LDS); the wave's 64 V rows are
-// then read row by row, one coalesced 256-byte row per instruction, a batch
-// of them (64 fp16 rows, 32 fp32 rows) issued before the first use, so
-// host-resident rows overlap their latency.
-// attn_combine_kernel merges the partials of a head by their maxima.
+// one index row; each wave owns 64 of them and the block merges its waves'
+// (m, l, o[128]) into one partial per query head of the row.  The wave's V
+// rows are read row by row, one coalesced 256-byte row per instruction (lane
+// l holds channels 2l, 2l+1), the first batch (64 fp16 rows, 32 fp32 rows)
+// issued before the K rows so that the two gathers' latencies overlap; lane j
+// scores entry j from its own K row (16-byte loads, q broadcast from LDS).
+// attn_combine_kernel merges a head's block partials by their maxima.
 #include "fathom_internal.h"
 
 namespace fathom {
@@ -74,20 +74,27 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // grid (ceil(k / 256), rows); row r serves query heads r*GH .. r*GH+GH-1.
-// part[((r * nparts + wave_index) * GH + j) * kPart + ...]
+// Block b writes the merged partial of its 256 entries for each head:
+// part[((r * nparts + b) * GH + j) * kPart + ...], nparts = gridDim.x.
 template <typename T, int GH>
 __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
     const float *__restrict__ q, int32_t heads_per_kv, const T *__restrict__ kc,
     const T *__restrict__ vc, int64_t n, int64_t stride_tok, int64_t stride_head,
-    const int32_t *__restrict__ idx, int32_t k, float scale, float *__restrict__ part,
-    int32_t nparts) {
+    const int32_t *__restrict__ idx, int32_t k, float scale, float *__restrict__ part) {
+  using E = Elem<T>;
+  using Pair = typename E::Pair;
+  constexpr int kVecs = kD / E::kPerVec;       // 16-byte vectors per K row
+  constexpr int kKChunk = 16;                   // K vectors in flight per lane
+  constexpr int kVBatch = 256 / sizeof(Pair);   // V rows in flight per wave
+
   __shared__ float s_q[GH][kD];
+  __shared__ float s_ml[kAttnWaves][GH][2];     // per wave: max, sum of weights
+  __shared__ float s_o[kAttnWaves][GH][kD];     // per wave: weighted V sums
   const int r = blockIdx.y;
   const int h0 = r * GH;
   const int g = h0 / heads_per_kv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < GH * kD; e += kAttnThreads) s_q[e / kD][e % kD] = q[(int64_t)h0 * kD + e];
-  __syncthreads();
 
   const int j = blockIdx.x * kAttnBlockKeys + wave * 64 + lane;
   int key = -1;
@@ -98,11 +105,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
   const int64_t head_off = (int64_t)g * stride_head;
   const bool any = __ballot(key >= 0) != 0ull;
 
-  using E = Elem<T>;
-  using Pair = typename E::Pair;
-  constexpr int kVecs = kD / E::kPerVec;  // 16-byte vectors per K row
-  constexpr int kKChunk = 16;              // vectors in flight per lane
-  constexpr int kVBatch = 256 / sizeof(Pair);  // V rows in flight per wave
+  // ---- first batch of V rows, issued before the K rows: lane l holds
+  // channels 2l, 2l+1; a skipped entry reads row 0 with weight 0 -------------
+  Pair vr[kVBatch];
+  auto load_v = [&](int j0) {
+#pragma unroll
+    for (int jj = 0; jj < kVBatch; ++jj) {
+      const int kj = __builtin_amdgcn_readlane(key, j0 + jj);
+      const int64_t row = kj >= 0 ? kj : 0;
+      vr[jj] = *reinterpret_cast<const Pair *>(vc + row * stride_tok + head_off + 2 * lane);
+    }
+  };
+  if (any) load_v(0);
+  __syncthreads();  // s_q
 
   // ---- scores: lane j scores its own entry ---------------------------------
   float dot[GH];
@@ -128,30 +143,27 @@ __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
     }
   }
 
-  float m[GH], p[GH], l[GH];
+  float m[GH], p[GH];
 #pragma unroll
   for (int h = 0; h < GH; ++h) {
     const float sc = key >= 0 ? __fmul_rn(scale, dot[h]) : -INFINITY;
     m[h] = wave_max(sc);
     p[h] = key >= 0 ? expf(__fsub_rn(sc, m[h])) : 0.0f;
-    l[h] = wave_sum(p[h]);
+    const float l = wave_sum(p[h]);
+    if (lane == 0) {
+      s_ml[wave][h][0] = m[h];
+      s_ml[wave][h][1] = l;
+    }
   }
 
   // ---- o = sum_j p_j V_j over the wave's entries, in entry order -----------
-  // lane l holds channels 2l, 2l+1; a skipped entry reads row 0 with weight 0
   float o0[GH], o1[GH];
 #pragma unroll
   for (int h = 0; h < GH; ++h) o0[h] = o1[h] = 0.0f;
   if (any) {
 #pragma unroll
     for (int j0 = 0; j0 < 64; j0 += kVBatch) {
-      Pair vr[kVBatch];
-#pragma unroll
-      for (int jj = 0; jj < kVBatch; ++jj) {
-        const int kj = __builtin_amdgcn_readlane(key, j0 + jj);
-        const int64_t row = kj >= 0 ? kj : 0;
-        vr[jj] = *reinterpret_cast<const Pair *>(vc + row * stride_tok + head_off + 2 * lane);
-      }
+      if (j0 > 0) load_v(j0);
 #pragma unroll
       for (int jj = 0; jj < kVBatch; ++jj) {
         float a, b;
@@ -166,41 +178,79 @@ __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
       }
     }
   }
-  const int pi = blockIdx.x * kAttnWaves + wave;
-  if (pi < nparts) {
 #pragma unroll
-    for (int h = 0; h < GH; ++h) {
-      float *dst = part + ((int64_t)(r * nparts + pi) * GH + h) * kPart;
-      if (lane == 0) {
-        dst[0] = m[h];
-        dst[1] = l[h];
+  for (int h = 0; h < GH; ++h) {
+    s_o[wave][h][2 * lane] = o0[h];
+    s_o[wave][h][2 * lane + 1] = o1[h];
+  }
+  __syncthreads();
+
+  // ---- merge the block's waves in wave order: thread (h, c) ----------------
+  for (int e = tid; e < GH * kD; e += kAttnThreads) {
+    const int h = e / kD, c = e % kD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, s_ml[w][h][0]);
+    float L = 0.0f, o = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) {
+        const float mw = s_ml[w][h][0];
+        const float sc = mw == -INFINITY ? 0.0f : expf(__fsub_rn(mw, M));
+        L = fmaf(sc, s_ml[w][h][1], L);
+        o = fmaf(sc, s_o[w][h][c], o);
       }
-      dst[2 + 2 * lane] = o0[h];
-      dst[3 + 2 * lane] = o1[h];
     }
+    float *dst = part + ((int64_t)(r * gridDim.x + blockIdx.x) * GH + h) * kPart;
+    if (c == 0) {
+      dst[0] = M;
+      dst[1] = L;
+    }
+    dst[2 + c] = o;
   }
 }
 
-// One block of kD threads per query head h (idx row h / GH, head h % GH).
+// One block of kD threads per query head h (idx row h / GH, head h % GH):
+// the block partials of the head, merged by their maxima in block order.
+// Loads are issued kUnroll at a time so their latencies overlap.
 template <int GH>
 __global__ __launch_bounds__(kD) void attn_combine_kernel(const float *__restrict__ part,
                                                           int32_t nparts,
                                                           float *__restrict__ out,
                                                           float *__restrict__ lse) {
+  constexpr int kUnroll = 8;
   const int h = blockIdx.x, c = threadIdx.x;
   const int r = h / GH, hh = h % GH;
   const float *base = part + ((int64_t)r * nparts * GH + hh) * kPart;
+  const int64_t step = (int64_t)GH * kPart;
   float M = -INFINITY;
-  for (int i = 0; i < nparts; ++i) M = fmaxf(M, base[(int64_t)i * GH * kPart]);
+  for (int i0 = 0; i0 < nparts; i0 += kUnroll) {
+    float mv[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      mv[u] = i0 + u < nparts ? base[(i0 + u) * step] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) M = fmaxf(M, mv[u]);
+  }
   float L = 0.0f, o = 0.0f;
   if (M != -INFINITY) {
-    for (int i = 0; i < nparts; ++i) {
-      const float *pp = base + (int64_t)i * GH * kPart;
-      const float mi = pp[0];
-      if (mi == -INFINITY) continue;
-      const float w = expf(__fsub_rn(mi, M));
-      L = fmaf(w, pp[1], L);
-      o = fmaf(w, pp[2 + c], o);
+    for (int i0 = 0; i0 < nparts; i0 += kUnroll) {
+      float mv[kUnroll], lv[kUnroll], ov[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const bool in = i0 + u < nparts;
+        const float *pp = base + (in ? (i0 + u) * step : 0);
+        mv[u] = in ? pp[0] : -INFINITY;
+        lv[u] = pp[1];
+        ov[u] = pp[2 + c];
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if (mv[u] == -INFINITY) continue;
+        const float w = expf(__fsub_rn(mv[u], M));
+        L = fmaf(w, lv[u], L);
+        o = fmaf(w, ov[u], o);
+      }
     }
   }
   out[(int64_t)h * kD + c] = L > 0.0f ? __fdiv_rn(o, L) : 0.0f;
@@ -212,13 +262,13 @@ int32_t launch_attn_t(const float *q, int32_t hq, int32_t hkv, const void *kc, c
                       int64_t n, int64_t stride_tok, int64_t stride_head, const int32_t *idx,
                       int32_t k, float scale, float *out, float *lse, void *ws, hipStream_t s) {
   const int32_t rows = hq / GH;
-  const int32_t nparts = (k + 63) / 64;
+  const int32_t nparts = (k + kAttnBlockKeys - 1) / kAttnBlockKeys;
   float *part = static_cast<float *>(ws);
   if (nparts > 0) {
-    const dim3 grid((k + kAttnBlockKeys - 1) / kAttnBlockKeys, rows);
+    const dim3 grid(nparts, rows);
     hipLaunchKernelGGL((attn_partial_kernel<T, GH>), grid, dim3(kAttnThreads), 0, s, q, hq / hkv,
                        static_cast<const T *>(kc), static_cast<const T *>(vc), n, stride_tok,
-                       stride_head, idx, k, scale, part, nparts);
+                       stride_head, idx, k, scale, part);
   }
   hipLaunchKernelGGL((attn_combine_kernel<GH>), dim3(hq), dim3(kD), 0, s, part, nparts, out, lse);
   return hip_fail(hipGetLastError(), "sparse_attention launch");
@@ -240,7 +290,8 @@ int32_t launch_attn_dtype(int32_t group, const float *q, int32_t hq, int32_t hkv
 }  // namespace
 
 int64_t attn_workspace_bytes(int32_t hq, int32_t k) {
-  return (int64_t)hq * ((k + 63) / 64) * kPart * (int64_t)sizeof(float);
+  return (int64_t)hq * ((k + kAttnBlockKeys - 1) / kAttnBlockKeys) * kPart *
+         (int64_t)sizeof(float);
 }
 
 int32_t launch_attention(const float *q, int32_t hq, int32_t hkv, const void *kc, const void *vc,

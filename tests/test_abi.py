@@ -231,7 +231,7 @@ def test_attention_validation(L):
     A = ctypes.c_void_p(0x10000)                  # 16-byte aligned dummy
     U = ctypes.c_void_p(0x10008)                  # 8-byte aligned only
     ws = L.fathom_attention_workspace_bytes(8, 2048)
-    assert ws == 8 * 32 * 130 * 4
+    assert ws == 8 * 8 * 130 * 4                  # 8 partials of 256 entries per head
     assert L.fathom_attention_workspace_bytes(8, -1) == 0
     base = [A, 8, 2, 128, A, A, 0, 1000, 256, 128, A, 1, 2048, ctypes.c_float(0.1), A, A, A,
             ws, None]
