@@ -500,3 +500,50 @@ int orc_sparse_attention(const float *q, int hq, int hkv, int d, const float *K,
   free(acc);
   return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Append keys to a packed layer.  [EXP] deployment warnings, item 3: when the
+ * upstream 4-bit K is re-quantised nothing else has to be rebuilt, since the
+ * planes are that K; the stored 4-bit K is reused per token (关键实验与数据,
+ * storage cost).  Reading R20: a decode step's new keys are quantised with
+ * the layer's stored range, code = floor((x - lo) / delta) with the fp32
+ * subtract and divide of R2, clamped to 0..15; values outside [lo, hi] are
+ * counted.  delta == 0 gives code 0.  sigma^2 stays the stored estimate.  Bits of the tokens n_old ..
+ * n_old + m - 1 are set in plane rows of W words (W >= orc_plane_words of
+ * n_old + m); every other bit is left as it was.
+ * keys: element (new token j, kv head h, channel c) at
+ * keys[j*stride_tok + h*stride_head + c]; planes [hkv][d][4][W].
+ * Returns the number of clamped values through *clamped.                   */
+int orc_append(const float *keys, int64_t m, int hkv, int d, int64_t stride_tok,
+               int64_t stride_head, int64_t n_old, uint32_t *planes, int64_t W,
+               const float *lo, const float *hi, int64_t *clamped) {
+  if (!planes || !lo || !hi || !clamped || m < 0 || n_old < 0 || hkv < 1 || d < 1 ||
+      (m > 0 && !keys) || W < orc_plane_words(n_old + m))
+    return ORC_BAD;
+  int64_t count = 0;
+  for (int h = 0; h < hkv; ++h) {
+    for (int c = 0; c < d; ++c) {
+      const float l = lo[h * d + c], u = hi[h * d + c];
+      const float delta = (u - l) * 0.0625f;
+      uint32_t *pl = planes + ((int64_t)h * d + c) * 4 * W;
+      for (int64_t j = 0; j < m; ++j) {
+        const float x = keys[j * stride_tok + (int64_t)h * stride_head + c];
+        int code = 0;
+        if (delta != 0.0f) {
+          const float y = (x - l) / delta;
+          const double fl = floor((double)y);
+          code = fl < 0.0 ? 0 : (fl > 15.0 ? 15 : (int)fl);
+        }
+        count += (x < l || x > u);
+        const int64_t i = n_old + j;
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t bit = (uint32_t)((code >> (3 - s)) & 1);
+          uint32_t *word = pl + (int64_t)s * W + i / 32;
+          *word = (*word & ~(1u << (i % 32))) | (bit << (i % 32));
+        }
+      }
+    }
+  }
+  *clamped = count;
+  return ORC_OK;
+}

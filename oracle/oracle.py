@@ -53,10 +53,11 @@ def _load():
         lib.orc_scan_at.argtypes = [P, P, P, L, I, I, P, P, I, P, F, P, L, P]
         lib.orc_read_prefixes.argtypes = [P, L, I, I, P, I, P]
         lib.orc_topk.argtypes = [P, I, L, L, I, I, P, P]
+        lib.orc_append.argtypes = [P, L, I, I, L, L, L, P, L, P, P, P]
         lib.orc_sparse_attention.argtypes = [P, I, I, I, P, P, L, L, L, P, I, I, F, P, P]
         for f in ("orc_pack", "orc_plan", "orc_plan_fixed", "orc_plan_rd", "orc_plan_group",
                   "orc_scan", "orc_scan_at",
-                  "orc_read_prefixes", "orc_topk", "orc_sparse_attention"):
+                  "orc_read_prefixes", "orc_topk", "orc_sparse_attention", "orc_append"):
             getattr(lib, f).restype = I
         _lib = lib
     return _lib
@@ -218,3 +219,19 @@ def sparse_attention(q, K, V, idx, group: int = 1, scale=None):
                                         _ptr(idx), group, k, scale, _ptr(out), _ptr(lse)),
            "sparse_attention")
     return out, lse
+
+
+def append(keys_new, n_old: int, planes, lo, hi):
+    """Set the bits of keys_new [m][hkv][d] (fp16/fp32) at tokens n_old ..
+    n_old+m-1 of planes [hkv][d][4][W] (modified in place, uint32) with the
+    stored lo/hi.  Returns the number of values outside [lo, hi]."""
+    k32 = np.ascontiguousarray(keys_new, dtype=np.float32)
+    m, hkv, d = k32.shape
+    assert planes.dtype == np.uint32 and planes.flags["C_CONTIGUOUS"]
+    W = planes.shape[-1]
+    lo = np.ascontiguousarray(lo, dtype=np.float32)
+    hi = np.ascontiguousarray(hi, dtype=np.float32)
+    cnt = np.zeros(1, np.int64)
+    _check(_load().orc_append(_ptr(k32), m, hkv, d, hkv * d, d, n_old, _ptr(planes), W,
+                              _ptr(lo), _ptr(hi), _ptr(cnt)), "append")
+    return int(cnt[0])

@@ -763,3 +763,107 @@ def test_sparse_attention_empty_rows_and_rejections(orc):
         orc.sparse_attention(q, K, V, np.full((hq, 3), K.shape[0], np.int32))
     with pytest.raises(ValueError):                    # groups must not straddle kv heads
         orc.sparse_attention(q, K, V, np.zeros((1, 3), np.int32), group=8)
+
+
+# --------------------------------------------------------------------------
+# append (decode-time growth of a packed layer with its stored range)
+
+def keys_with_extremes_first(seed, n, hkv, d, n_first):
+    """fp16 keys whose per-channel min and max lie among the first n_first."""
+    rng = np.random.default_rng(seed)
+    k = (rng.standard_normal((n, hkv, d)) * rng.uniform(0.2, 3, (1, hkv, d))).astype(np.float16)
+    for h in range(hkv):
+        for c in range(d):
+            lo_i = int(np.argmin(k[:, h, c].astype(np.float32)))
+            k[[0, lo_i], h, c] = k[[lo_i, 0], h, c]
+            hi_i = 1 + int(np.argmax(k[1:, h, c].astype(np.float32)))
+            k[[1, hi_i], h, c] = k[[hi_i, 1], h, c]
+    assert n_first >= 2
+    return k
+
+
+def widen(planes, W):
+    hkv, d, four, W0 = planes.shape
+    out = np.zeros((hkv, d, four, W), np.uint32)
+    out[..., :W0] = planes
+    return out
+
+
+@pytest.mark.parametrize("n0,n", [(2, 5), (300, 1000), (2047, 2049), (2048, 4100), (31, 33)])
+def test_append_in_range_keys_equals_pack_of_all(orc, n0, n):
+    keys = keys_with_extremes_first(n0 + n, n, 2, 16, n0)
+    full = orc.pack(keys)
+    first = orc.pack(keys[:n0])
+    np.testing.assert_array_equal(first["lo"], full["lo"])
+    np.testing.assert_array_equal(first["hi"], full["hi"])
+    planes = widen(first["planes"], orc.plane_words(n))
+    cnt = orc.append(keys[n0:], n0, planes, first["lo"], first["hi"])
+    assert cnt == 0
+    np.testing.assert_array_equal(planes, full["planes"])
+
+
+def test_append_one_token_at_a_time_equals_one_call(orc):
+    keys = keys_with_extremes_first(8, 700, 2, 16, 100)
+    first = orc.pack(keys[:100])
+    W = orc.plane_words(700)
+    a = widen(first["planes"], W)
+    b = a.copy()
+    orc.append(keys[100:], 100, a, first["lo"], first["hi"])
+    for j in range(100, 700):
+        orc.append(keys[j:j + 1], j, b, first["lo"], first["hi"])
+    np.testing.assert_array_equal(a, b)
+
+
+def test_append_clamps_out_of_range_and_counts(orc):
+    rng = np.random.default_rng(9)
+    base = rng.standard_normal((500, 2, 16)).astype(np.float16)
+    p = orc.pack(base)
+    new = (rng.standard_normal((300, 2, 16)) * 3).astype(np.float16)   # many outside
+    W = orc.plane_words(800)
+    planes = widen(p["planes"], W)
+    cnt = orc.append(new, 500, planes, p["lo"], p["hi"])
+    x = new.astype(np.float32).transpose(1, 2, 0)                      # [hkv][d][m]
+    lo, hi = p["lo"][..., None], p["hi"][..., None]
+    delta = ((hi - lo) * np.float32(0.0625)).astype(np.float32)
+    q = np.floor(((x - lo).astype(np.float32) / delta).astype(np.float32))
+    expect = np.clip(q, 0, 15).astype(np.int64)
+    got = unpack_planes_vectorised(planes, 800)[:, :, 500:]
+    np.testing.assert_array_equal(got, expect)
+    assert cnt == int(((x < lo) | (x > hi)).sum()) and cnt > 0
+    # keys at the range ends land in codes 0 and 15 without counting
+    ends = np.stack([p["lo"], p["hi"]]).astype(np.float16)
+    c2 = orc.append(ends, 800, widen(planes, orc.plane_words(802)), p["lo"], p["hi"])
+    assert c2 == 0
+
+
+def test_append_leaves_every_other_bit_alone(orc):
+    rng = np.random.default_rng(10)
+    hkv, d, W = 2, 8, 128                                   # capacity 4096 keys
+    planes = rng.integers(0, 2 ** 32, (hkv, d, 4, W), dtype=np.uint64).astype(np.uint32)
+    before = planes.copy()
+    lo = np.full((hkv, d), -1, np.float32)
+    hi = np.full((hkv, d), 1, np.float32)
+    new = rng.uniform(-1, 1, (50, hkv, d)).astype(np.float32)
+    orc.append(new, 1000, planes, lo, hi)
+    tok = np.arange(W * 32)
+    touched = (tok >= 1000) & (tok < 1050)
+    b0 = np.unpackbits(before.view(np.uint8), bitorder="little").reshape(hkv, d, 4, W * 32)
+    b1 = np.unpackbits(planes.view(np.uint8), bitorder="little").reshape(hkv, d, 4, W * 32)
+    np.testing.assert_array_equal(b0[..., ~touched], b1[..., ~touched])
+    codes = b1[..., touched]
+    val = codes[:, :, 0] * 8 + codes[:, :, 1] * 4 + codes[:, :, 2] * 2 + codes[:, :, 3]
+    xs = new.transpose(1, 2, 0)
+    exp = np.clip(np.floor(((xs + 1).astype(np.float32) / np.float32(0.125))), 0, 15)
+    np.testing.assert_array_equal(val, exp)
+
+
+def test_append_constant_channel_and_rejections(orc):
+    lo = np.zeros((1, 4), np.float32)
+    hi = np.zeros((1, 4), np.float32)
+    planes = np.full((1, 4, 4, 64), 0xFFFFFFFF, np.uint32)
+    new = np.array([[[0, 0, 1, -2]]], np.float32)
+    cnt = orc.append(new, 5, planes, lo, hi)
+    assert cnt == 2
+    assert np.all(unpack_planes_vectorised(planes, 6)[0, :, 5] == 0)
+    with pytest.raises(ValueError):                        # rows too short for n_old + m
+        orc.append(np.zeros((2, 1, 4), np.float32), 2047, planes, lo, hi)
