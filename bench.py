@@ -446,6 +446,38 @@ def bench_attention(dev, steps, warmup):
     return out
 
 
+def bench_append(dev, steps, warmup):
+    """fathom_append on the 1M-key layer's planes (capacity for 2^20 + 8192
+    keys): one decode token (8 kv heads x 128 channels) and a 4096-key chunk."""
+    w = synth.LAYER_1M
+    n0 = w.n - 4096
+    keys = synth.keys(w.seed, 0, w.n, w.hkv, w.d, w.dtype, w.outliers, device=dev)
+    p = fathom.pack(keys[:n0])
+    planes = fathom.alloc_planes(w.n + 8192, w.hkv)
+    planes[..., :p.planes.shape[-1]].copy_(p.planes)
+    del p.planes
+    out = {"workload": "append to the 1M-key layer (fp16 keys, 8 kv heads, capacity 2^20+8192)"}
+    for m in (1, 4096):
+        def call():
+            fathom.append(keys[n0:n0 + m], n0, planes, p.lo, p.hi)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        a, b = _event_pair()
+        a.record()
+        for _ in range(steps):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        words = -(-(n0 % 32 + m) // 32)
+        alg = m * w.hkv * w.d * 2 + 2 * words * w.hkv * w.d * 4 * 4   # keys + plane words read and written
+        out[f"m{m}"] = {"us": round(ms * 1e3, 2), "algorithmic_bytes": alg,
+                        "GBps": round(alg / (ms * 1e-3) / 1e9, 1)}
+    del keys, planes
+    return out
+
+
 def bench_sessions(dev, steps, warmup):
     """16 ragged sessions (64K..512K keys), per-session B, planes in pinned host
     memory, one batched scan and one batched top-k (k = 1024 per query head)."""
@@ -765,6 +797,9 @@ def main():
         torch.cuda.empty_cache()
         extra["step_36_layers"] = bench_step36(dev, 3, 1)
         log(f"36-layer step: {extra['step_36_layers']}")
+        torch.cuda.empty_cache()
+        extra["append_1m"] = bench_append(dev, 50, 5)
+        log(f"append: {extra['append_1m']}")
         torch.cuda.empty_cache()
         extra["attention_1m"] = bench_attention(dev, 20, 3)
         log(f"attention: {extra['attention_1m']}")

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FATHOM_ABI_VERSION 1
+#define FATHOM_ABI_VERSION 2
 #define FATHOM_HEAD_DIM 128
 #define FATHOM_MAX_K 2048         /* largest k accepted by the top-k calls */
 #define FATHOM_MAX_SESSIONS 64    /* sessions per batched call */
@@ -211,6 +211,10 @@ typedef struct {
   int64_t ld_logits;
   int32_t *idx;           /* device int32[hq/group][k] (top-k output)       */
   float *vals;            /* device fp32[hq/group][k]                       */
+  int64_t plane_words;    /* row length W of planes in words: 0 means       */
+                          /* fathom_plane_words(n); a larger capacity (a    */
+                          /* multiple of 64, <= 2^26) lets a session grow by */
+                          /* fathom_append without moving its planes        */
 } fathom_session;
 
 int32_t fathom_scan_batched(const fathom_session *sessions, int32_t n_sessions,
@@ -252,6 +256,32 @@ int32_t fathom_scan_topk_batched(const fathom_session *sessions,
                                  int32_t n_sessions, int32_t hkv, int32_t d,
                                  int32_t hq, int32_t group, int32_t k, void *ws,
                                  int64_t ws_bytes, void *stream);
+
+/* ---- append (decode-time growth) -------------------------------------------
+ * Deployment warnings, item 3: the planes are the stored 4-bit K itself, so
+ * nothing else is rebuilt when K changes; a decode step adds its new keys to
+ * the stored K.  Here the m new keys become tokens n_old .. n_old+m-1 of a
+ * packed layer, quantised with the layer's stored range (no re-quantisation
+ * of earlier keys): code = floor((x - lo) / delta) with fp32 subtract and
+ * divide, delta = (hi - lo) * 1/16, clamped to 0..15; delta == 0 gives 0.
+ * sigma2 is left as stored.  Only those tokens' bits change.
+ *
+ * keys        device rows of `dtype`: element (new token j, kv head h,
+ *             channel c) at keys[j*stride_tok + h*stride_head + c]
+ * planes      device or pinned-host uint32[hkv][d][4][plane_words], rows of
+ *             plane_words >= fathom_plane_words(n_old + m) words, a multiple
+ *             of 64 (a capacity; scans of the grown layer pass it in
+ *             fathom_session.plane_words)
+ * lo, hi      device fp32[hkv][d] as stored by fathom_pack
+ * clamped     NULL, or a device uint32 to which the number of values outside
+ *             [lo, hi] is added (the caller may re-pack when it grows)
+ * Enqueues 1 kernel (none when m == 0).  Calls that write the same plane
+ * words (appends to one layer) must be ordered on one stream.              */
+int32_t fathom_append(const void *keys, int32_t dtype, int64_t m, int32_t hkv,
+                      int32_t d, int64_t stride_tok, int64_t stride_head,
+                      int64_t n_old, uint32_t *planes, int64_t plane_words,
+                      const float *lo, const float *hi, uint32_t *clamped,
+                      void *stream);
 
 /* ---- sparse attention over the selected keys -------------------------------
  * Explainer, problem statement: each generated token attends over the top k

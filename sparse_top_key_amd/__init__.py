@@ -41,6 +41,7 @@ class _Session(ctypes.Structure):
         ("meta", ctypes.c_void_p), ("meta_scale", ctypes.c_float),
         ("logits", ctypes.c_void_p), ("ld_logits", ctypes.c_int64),
         ("idx", ctypes.c_void_p), ("vals", ctypes.c_void_p),
+        ("plane_words", ctypes.c_int64),
     ]
 
 
@@ -66,6 +67,7 @@ def lib():
             "fathom_plan_rd": (I32, [P, I32, I32, I32, P, P, P, P]),
             "fathom_plan_group": (I32, [P, I32, I32, I32, P, P, P, P]),
             "fathom_attention_workspace_bytes": (I64, [I32, I32]),
+            "fathom_append": (I32, [P, I32, I64, I32, I32, I64, I64, I64, P, I64, P, P, P, P]),
             "fathom_sparse_attention": (I32, [P, I32, I32, I32, P, P, I32, I64, I64, I64, P,
                                               I32, I32, F, P, P, P, I64, P]),
             "fathom_scan": (I32, [P, P, P, I64, I32, I32, P, P, I32, P, F, P, I64, P]),
@@ -207,6 +209,11 @@ def plan_fixed(q: torch.Tensor, r: int, out=None) -> torch.Tensor:
     return out
 
 
+def _has_capacity(planes: torch.Tensor, n: int) -> bool:
+    """Planes laid out for more keys than n (rows longer than plane_words(n))."""
+    return planes.dim() == 4 and planes.shape[-1] != plane_words(n)
+
+
 def scan(planes: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor, n: int,
          q: torch.Tensor, plan_: torch.Tensor, meta: Optional[torch.Tensor] = None,
          meta_scale: float = 0.0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -216,6 +223,10 @@ def scan(planes: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor, n: int,
     hq = q.shape[0]
     if out is None:
         out = torch.empty((hq, max(n, 1)), dtype=torch.float32, device=q.device)
+    if _has_capacity(planes, n):
+        scan_batched([Session(planes, lo, hi, n, q, plan_, logits=out, meta=meta,
+                              meta_scale=meta_scale)])
+        return out[:, :n]
     _check(lib().fathom_scan(_p(planes), _p(lo), _p(hi), n, hkv, d, _p(q), _p(plan_), hq,
                              _p(meta), meta_scale, _p(out), out.stride(0),
                              _stream(q.device)), "fathom_scan")
@@ -268,7 +279,8 @@ def _sessions(sess: Sequence[Session]):
                           s.logits.data_ptr() if s.logits is not None else None,
                           s.logits.stride(0) if s.logits is not None else 0,
                           s.idx.data_ptr() if s.idx is not None else None,
-                          s.vals.data_ptr() if s.vals is not None else None)
+                          s.vals.data_ptr() if s.vals is not None else None,
+                          s.planes.shape[-1])
     return arr
 
 
@@ -315,6 +327,10 @@ def scan_topk(planes: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor, n: int,
     if ws is None:
         ws = torch.empty(max(scan_topk_workspace_bytes([n], hkv, hq, group, k), 1),
                          dtype=torch.uint8, device=dev)
+    if _has_capacity(planes, n):
+        scan_topk_batched([Session(planes, lo, hi, n, q, plan_, idx=idx, vals=vals, meta=meta,
+                                   meta_scale=meta_scale)], k, group, ws)
+        return idx, vals
     _check(lib().fathom_scan_topk(_p(planes), _p(lo), _p(hi), n, hkv, d, _p(q), _p(plan_), hq,
                                   _p(meta), meta_scale, group, k, _p(idx), _p(vals), _p(ws),
                                   ws.numel(), _stream(dev)), "fathom_scan_topk")
@@ -333,6 +349,34 @@ def scan_topk_batched(sess: Sequence[Session], k: int, group: int = 1,
     _check(lib().fathom_scan_topk_batched(_sessions(sess), len(sess), hkv, d, hq, group, k,
                                           _p(ws), ws.numel(), _stream(s0.q.device)),
            "fathom_scan_topk_batched")
+
+
+def append(keys: torch.Tensor, n_old: int, planes: torch.Tensor, lo: torch.Tensor,
+           hi: torch.Tensor, clamped: Optional[torch.Tensor] = None) -> None:
+    """Write keys [m][hkv][d] (fp16/fp32, channel stride 1) as tokens n_old ..
+    n_old+m-1 of planes [hkv][d][4][W] (W a capacity, see alloc_planes), with
+    the stored lo/hi.  clamped: optional 1-element int32 device tensor that
+    receives the count of values outside [lo, hi] (added to)."""
+    _require_gpu(keys, planes, lo)
+    m, hkv, d = keys.shape
+    if keys.stride(2) != 1:
+        raise FathomError("channel stride of keys must be 1")
+    dtype = {torch.float16: F16, torch.float32: F32}.get(keys.dtype)
+    if dtype is None:
+        raise FathomError("keys must be float16 or float32")
+    _check(lib().fathom_append(_p(keys), dtype, m, hkv, d, keys.stride(0), keys.stride(1),
+                               n_old, _p(planes), planes.shape[-1], _p(lo), _p(hi),
+                               _p(clamped), _stream(lo.device)), "fathom_append")
+
+
+def alloc_planes(capacity: int, hkv: int, d: int = D, device="cuda", pin_memory=False):
+    """Zeroed planes [hkv][d][4][W] with room for `capacity` keys."""
+    W = plane_words(capacity)
+    if pin_memory:
+        t = torch.zeros((hkv, d, 4, W), dtype=torch.int32, pin_memory=True)
+    else:
+        t = torch.zeros((hkv, d, 4, W), dtype=torch.int32, device=device)
+    return t
 
 
 def attention_workspace_bytes(hq: int, k: int) -> int:

@@ -135,6 +135,30 @@ int32_t fathom_plan_group(const float *q, int32_t hq, int32_t hkv, int32_t d,
   return launch_plan_group(q, hq, hkv, sigma2, budget_bits, plan, as_stream(stream));
 }
 
+int32_t fathom_append(const void *keys, int32_t dtype, int64_t m, int32_t hkv, int32_t d,
+                      int64_t stride_tok, int64_t stride_head, int64_t n_old,
+                      uint32_t *planes, int64_t plane_words_, const float *lo,
+                      const float *hi, uint32_t *clamped, void *stream) {
+  REQUIRE(planes && lo && hi && (keys || m == 0), FATHOM_ERR_INVALID_ARG,
+          "fathom_append: null pointer");
+  REQUIRE(dtype == FATHOM_F16 || dtype == FATHOM_F32, FATHOM_ERR_INVALID_ARG,
+          "fathom_append: dtype must be FATHOM_F16 or FATHOM_F32 (got %d)", dtype);
+  REQUIRE(hkv >= 1, FATHOM_ERR_INVALID_ARG, "fathom_append: hkv must be >= 1");
+  if (int32_t rc = check_d(d)) return rc;
+  REQUIRE(m >= 0 && n_old >= 0 && n_old + m <= ((int64_t)1 << 31), FATHOM_ERR_INVALID_ARG,
+          "fathom_append: need m >= 0, n_old >= 0, n_old + m <= 2^31");
+  REQUIRE(stride_tok >= 0 && stride_head >= 0, FATHOM_ERR_INVALID_ARG,
+          "fathom_append: strides must be non-negative");
+  REQUIRE(plane_words_ >= plane_words(n_old + m) && plane_words_ % 64 == 0 &&
+              plane_words_ <= ((int64_t)1 << 26),
+          FATHOM_ERR_INVALID_ARG,
+          "fathom_append: plane_words (%lld) must be a multiple of 64 in [%lld, 2^26]",
+          (long long)plane_words_, (long long)plane_words(n_old + m));
+  if (m == 0) return FATHOM_OK;
+  return launch_append(keys, dtype, m, hkv, stride_tok, stride_head, n_old, planes,
+                       plane_words_, lo, hi, clamped, as_stream(stream));
+}
+
 int64_t fathom_attention_workspace_bytes(int32_t hq, int32_t k) {
   if (hq < 1 || k < 0 || k > FATHOM_MAX_ATTN_K) return 0;
   return attn_workspace_bytes(hq, k);
@@ -193,9 +217,22 @@ int32_t fathom_plan_fixed(const float *q, int32_t hq, int32_t d, int32_t r, uint
   return launch_plan_fixed(q, hq, r, plan, as_stream(stream));
 }
 
+// Plane row length of a session: 0 (fathom_plane_words(n)) or a capacity of
+// at least that many words, in whole 2048-key blocks.
+static int32_t check_plane_words(const fathom_session &s, const char *who) {
+  REQUIRE(s.plane_words == 0 ||
+              (s.plane_words >= plane_words(s.n) && s.plane_words % 64 == 0 &&
+               s.plane_words <= ((int64_t)1 << 26)),
+          FATHOM_ERR_INVALID_ARG,
+          "%s: plane_words (%lld) must be 0 or a multiple of 64 in [%lld, 2^26]", who,
+          (long long)s.plane_words, (long long)plane_words(s.n));
+  return FATHOM_OK;
+}
+
 static int32_t check_scan_session(const fathom_session &s, int32_t hq, const char *who) {
   REQUIRE(s.n >= 0 && s.n <= ((int64_t)1 << 31), FATHOM_ERR_INVALID_ARG,
           "%s: n must be in [0, 2^31] (got %lld)", who, (long long)s.n);
+  if (int32_t rc = check_plane_words(s, who)) return rc;
   if (s.n == 0) return FATHOM_OK;
   REQUIRE(s.planes && s.lo && s.hi && s.q && s.plan && s.logits, FATHOM_ERR_INVALID_ARG,
           "%s: null pointer", who);
@@ -217,6 +254,7 @@ static ScanSession to_scan(const fathom_session &s) {
   o.meta_scale = s.meta_scale;
   o.logits = s.logits;
   o.ld = s.ld_logits;
+  o.W = s.plane_words;
   return o;
 }
 
@@ -326,6 +364,7 @@ static int32_t check_scan_topk_session(const fathom_session &s, const char *who)
   REQUIRE(s.n >= 0 && s.n < ((int64_t)1 << 31), FATHOM_ERR_INVALID_ARG,
           "%s: n must be in [0, 2^31) (got %lld)", who, (long long)s.n);
   REQUIRE(s.idx && s.vals, FATHOM_ERR_INVALID_ARG, "%s: null output", who);
+  if (int32_t rc = check_plane_words(s, who)) return rc;
   if (s.n == 0) return FATHOM_OK;
   REQUIRE(s.planes && s.lo && s.hi && s.q && s.plan, FATHOM_ERR_INVALID_ARG,
           "%s: null pointer", who);

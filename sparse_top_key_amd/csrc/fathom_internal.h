@@ -75,6 +75,12 @@ int32_t launch_plan_group(const float *q, int32_t hq, int32_t hkv,
 int32_t launch_plan_fixed(const float *q, int32_t hq, int32_t r, uint8_t *plan,
                           hipStream_t s);
 
+// ---- append -------------------------------------------------------------------
+int32_t launch_append(const void *keys, int32_t dtype, int64_t m, int32_t hkv,
+                      int64_t stride_tok, int64_t stride_head, int64_t n_old,
+                      uint32_t *planes, int64_t W, const float *lo, const float *hi,
+                      uint32_t *clamped, hipStream_t s);
+
 // ---- sparse attention -------------------------------------------------------
 int64_t attn_workspace_bytes(int32_t hq, int32_t k);
 int32_t launch_attention(const float *q, int32_t hq, int32_t hkv, const void *kc,
@@ -102,7 +108,9 @@ struct ScanSession {
   uint8_t *table;         // slot tables of the session's kv heads, or null
   int32_t table_mode;     // ScanTable: what the scan does with them
   int32_t residency;      // planes: 0 unknown (queried), 1 device, 2 pinned host
+  int64_t W;              // plane row length in words; 0: plane_words(n)
 };
+inline int64_t sess_words(const ScanSession &s) { return s.W > 0 ? s.W : plane_words(s.n); }
 // Slot tables (matrix-core scan): built in each block (kTableNone), built and
 // also stored for later scans of the same call (kTableWrite), or loaded from
 // what an earlier scan of the call stored (kTableRead).

@@ -1041,7 +1041,8 @@ bool planes_residency(const ScanSession *sess, int32_t n_sess, bool *any_host) {
 }
 
 // The matrix-core kernel addresses a kv head's planes with 32-bit buffer
-// offsets: sessions up to 2^25 keys (2 GiB of planes per kv head).
+// offsets: plane rows of up to 2^20 words, i.e. 2^25 keys (2 GiB of planes per
+// kv head).
 constexpr int64_t kMfmaMaxKeys = (int64_t)1 << 25;
 
 }  // namespace
@@ -1078,7 +1079,7 @@ bool scan_can_fuse(const ScanSession *sess, int32_t n_sess) {
   bool any_host = false;
   if (!planes_residency(sess, n_sess, &any_host)) return false;
   for (int32_t j = 0; j < n_sess; ++j)
-    if (sess[j].n > kMfmaMaxKeys) return false;
+    if (sess_words(sess[j]) > plane_words(kMfmaMaxKeys)) return false;
   return !any_host;
 }
 
@@ -1088,9 +1089,9 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_
   const int ncu = device_cus();
   bool any_host = false;
   if (!planes_residency(sess, n_sess, &any_host)) return FATHOM_ERR_INVALID_ARG;
-  int64_t max_n = 0;
-  for (int32_t j = 0; j < n_sess; ++j) max_n = std::max(max_n, sess[j].n);
-  const bool fp32_path = any_host || max_n > kMfmaMaxKeys;
+  int64_t max_w = 0;
+  for (int32_t j = 0; j < n_sess; ++j) max_w = std::max(max_w, sess_words(sess[j]));
+  const bool fp32_path = any_host || max_w > plane_words(kMfmaMaxKeys);
   if (fp32_path && mode != kScanLogits) {
     set_error("scan: sampled and candidate scans need device planes of at most 2^25 keys");
     return FATHOM_ERR_UNSUPPORTED;
@@ -1154,7 +1155,7 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_
         o.meta = in.meta;
         o.logits = in.logits;
         o.n = in.n;
-        o.W = plane_words(in.n);
+        o.W = sess_words(in);
         o.ld = in.ld;
         o.meta_scale = in.meta_scale;
         o.vec_out = ((reinterpret_cast<uintptr_t>(in.logits) & 15) == 0) && (in.ld % 4 == 0);

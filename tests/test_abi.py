@@ -31,7 +31,7 @@ def declared_functions():
 def test_header_declares_the_path():
     names = declared_functions()
     for f in ("fathom_pack", "fathom_plan", "fathom_plan_fixed", "fathom_plan_rd",
-              "fathom_plan_group", "fathom_scan",
+              "fathom_plan_group", "fathom_sparse_attention", "fathom_append", "fathom_scan",
               "fathom_topk", "fathom_scan_batched", "fathom_topk_batched",
               "fathom_read_prefixes", "fathom_plan_stats", "fathom_probe_read"):
         assert f in names
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_sizes(L):
-    assert L.fathom_abi_version() == 1
+    assert L.fathom_abi_version() == 2
     for n in (1, 31, 32, 2047, 2048, 2049, 1 << 20):
         W = 64 * ((n + 2047) // 2048)
         assert L.fathom_plane_words(n) == W
@@ -257,3 +257,34 @@ def test_attention_validation(L):
     assert call(wsb=ws - 1) == 4
     assert call(scale=ctypes.c_float(float("inf"))) == 1
     assert call(n=-1) == 1
+
+
+def test_append_validation(L):
+    A = ctypes.c_void_p(0x10000)
+    # every case below fails validation, so nothing is ever enqueued
+    base = [A, 0, 10, 8, 128, 1024, 128, 4090, A, 128, A, A, None, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return L.fathom_append(*a)
+    assert call(0, None) == 1                    # keys
+    assert call(1, 3) == 1                       # dtype
+    assert call(3, 0) == 1                       # hkv
+    assert call(4, 64) == 2                      # d
+    assert call(2, -1) == 1                      # m
+    assert call(9, 64) == 1 and "plane_words" in err(L)   # 4100 keys need 192 words
+    assert call(9, 200) == 1                     # not a multiple of 64
+    assert call(8, None) == 1                    # planes
+    assert call(7, -5) == 1                      # n_old
+
+
+def test_session_plane_words_validation(L):
+    from sparse_top_key_amd import _Session
+    A = 0x10000
+    s = (_Session * 1)()
+    s[0] = _Session(A, A, A, 5000, A, A, None, 0.0, A, 5000, None, None, 64)
+    assert L.fathom_scan_batched(s, 1, 8, 128, 32, None) == 1   # 5000 keys need 192 words
+    assert "plane_words" in err(L)
+    s[0] = _Session(A, A, A, 5000, A, A, None, 0.0, A, 5000, None, None, 200)
+    assert L.fathom_scan_batched(s, 1, 8, 128, 32, None) == 1   # not a multiple of 64
