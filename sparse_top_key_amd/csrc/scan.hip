@@ -881,19 +881,39 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
         int row = head_base + hh;
         if constexpr (MODE == kScanCandGroup) {
           // group score: the group's fp32 logits added in fp64 in head order,
-          // rounded once; lanes of head 0 hold the key's sum
+          // rounded once; lanes of head 0 hold the key's sum.  An fp32 sum
+          // first: its error plus the final rounding stay below
+          // 8 * 2^-24 * sum |s_h| (+ 2^-126 near zero), so a key whose fp32
+          // sum misses the threshold by more than that is no candidate, and
+          // the exact sum is formed only when some lane of the wave is
+          // within that margin (every other lane's value is never used)
 #pragma unroll
           for (int b = 0; b < 16; ++b) {
-            double acc = (double)s[b];
-            const float s1 = __shfl_down(s[b], 16);
-            const float s2 = __shfl_down(s[b], 32);
-            const float s3 = __shfl_down(s[b], 48);
-            if (GH > 1) acc = __dadd_rn(acc, (double)s1);
-            if (GH > 2) acc = __dadd_rn(acc, (double)s2);
-            if (GH > 3) acc = __dadd_rn(acc, (double)s3);
-            s[b] = (float)acc;
-            // one key at a time (register budget)
-            __builtin_amdgcn_sched_barrier(0);
+            // rows of 16 lanes are heads; row 0 receives rows 1, 2, 3 by
+            // lane-row swaps (VALU, no LDS round trip)
+            const uint32_t v = __float_as_uint(s[b]);
+            const auto p16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+            const auto p32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+            const auto p48 = __builtin_amdgcn_permlane16_swap(p32[1], p32[1], false, false);
+            const float s1 = __uint_as_float(p16[1]);
+            const float s2 = __uint_as_float(p32[1]);
+            const float s3 = __uint_as_float(p48[1]);
+            float approx = s[b], mag = fabsf(s[b]);
+            if (GH > 1) { approx = __fadd_rn(approx, s1); mag = __fadd_rn(mag, fabsf(s1)); }
+            if (GH > 2) { approx = __fadd_rn(approx, s2); mag = __fadd_rn(mag, fabsf(s2)); }
+            if (GH > 3) { approx = __fadd_rn(approx, s3); mag = __fadd_rn(mag, fabsf(s3)); }
+            const float margin = __fmaf_rn(mag, 4.76837158203125e-07f /* 2^-21 */,
+                                           1.1754943508222875e-38f /* 2^-126 */);
+            const bool near = hh == 0 && __fadd_rn(approx, margin) >= row_tf;
+            if (__ballot(near) != 0ull) {
+              double acc = (double)s[b];
+              if (GH > 1) acc = __dadd_rn(acc, (double)s1);
+              if (GH > 2) acc = __dadd_rn(acc, (double)s2);
+              if (GH > 3) acc = __dadd_rn(acc, (double)s3);
+              s[b] = (float)acc;
+            } else {
+              s[b] = approx;
+            }
           }
           lane_rows = hh == 0;
           row = g;
