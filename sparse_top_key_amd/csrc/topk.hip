@@ -322,11 +322,30 @@ __global__ __launch_bounds__(kBig) void topk_sample_kernel(TopkArgs a) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) v[j] = ((okm >> j) & 1) ? to_key(f[j]) : 0u;
   } else {
+    // group scores: rows added in fp64 in row order (as group_score does);
+    // per row and half of the samples, every load is issued before the adds
+    constexpr int kHalf = (kPer + 1) / 2;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int e = threadIdx.x + j * kBig;
-      const int64_t pos = (int64_t)(e / kRun) * stride + (e % kRun);
-      v[j] = ((okm >> j) & 1) ? to_key(group_score(R.row, ld, a.group, pos)) : 0u;
+    for (int j0 = 0; j0 < kPer; j0 += kHalf) {
+      double acc[kHalf];
+#pragma unroll
+      for (int u = 0; u < kHalf; ++u) acc[u] = 0.0;
+      for (int r = 0; r < a.group; ++r) {
+        const float *rr = R.row + (int64_t)r * ld;
+        float f[kHalf];
+#pragma unroll
+        for (int u = 0; u < kHalf; ++u) {
+          const int j = j0 + u;
+          const int e = threadIdx.x + j * kBig;
+          const int64_t pos = (int64_t)(e / kRun) * stride + (e % kRun);
+          f[u] = (j < kPer && ((okm >> j) & 1)) ? rr[pos] : rr[0];
+        }
+#pragma unroll
+        for (int u = 0; u < kHalf; ++u) acc[u] = __dadd_rn(acc[u], (double)f[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kHalf; ++u)
+        if (j0 + u < kPer) v[j0 + u] = ((okm >> (j0 + u)) & 1) ? to_key((float)acc[u]) : 0u;
     }
   }
   uint32_t mx = 0, mn = 0xFFFFFFFFu;
