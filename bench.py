@@ -80,12 +80,13 @@ def union_plane_bytes(plan, hkv, n):
 
 
 def run_steps(layers, w, ws, steps, mode, fixed=False, fused=False, per_call=True,
-              variant=None):
+              variant=None, with_meta=True):
     """mode: 'host' or 'hbm'.  fused: fathom_scan_topk in place of fathom_scan
     then fathom_topk (ws must then be its workspace).  fixed: True (r = 32,
     the 136-bit baseline) or the baseline's channel count r.  variant: None (the
     fill-to-cap walk), 'rd' (rate-distortion plan) or 'group' (one plan per
-    GQA group, budget B per kv head).  per_call: events around
+    GQA group, budget B per kv head).  with_meta: the fixed baselines read
+    their 8-bit side stream (fixed-136); without it, r = 32 is fixed-128.  per_call: events around
     every call (for the per-call times); otherwise none, since an event
     recorded between two calls stalls the stream for a few microseconds.
     Returns the per-step event lists (empty lists when per_call is off)."""
@@ -95,7 +96,7 @@ def run_steps(layers, w, ws, steps, mode, fixed=False, fused=False, per_call=Tru
         L = layers[s % len(layers)]
         planes = L.host if mode == "host" else L.planes
         meta = None
-        if fixed:
+        if fixed and with_meta:
             meta = L.meta_host if mode == "host" else L.meta
         e = ev[s]
         if per_call:
@@ -136,21 +137,23 @@ def summarize(ev):
                 scan_ms_p90=float(np.percentile(scan, 90)))
 
 
-def timed(layers, w, ws, steps, warmup, mode, fixed=False, fused=False, variant=None):
+def timed(layers, w, ws, steps, warmup, mode, fixed=False, fused=False, variant=None,
+          with_meta=True):
     """Throughput: K steps between one pair of events (and synchronisations);
     then the same K steps again with events around every call, for the
     per-call times (the scan's is the one the rooflines use)."""
-    run_steps(layers, w, ws, warmup, mode, fixed, fused, per_call=False, variant=variant)
+    kw = dict(variant=variant, with_meta=with_meta)
+    run_steps(layers, w, ws, warmup, mode, fixed, fused, per_call=False, **kw)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     a.record()
-    run_steps(layers, w, ws, steps, mode, fixed, fused, per_call=False, variant=variant)
+    run_steps(layers, w, ws, steps, mode, fixed, fused, per_call=False, **kw)
     b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     r = {"step_ms": a.elapsed_time(b) / steps, "wall_ms_per_step": wall * 1e3 / steps}
-    ev = run_steps(layers, w, ws, steps, mode, fixed, fused, per_call=True, variant=variant)
+    ev = run_steps(layers, w, ws, steps, mode, fixed, fused, per_call=True, **kw)
     torch.cuda.synchronize()
     r.update(summarize(ev))
     return r
@@ -247,8 +250,17 @@ def cpu_baseline(layer0, w, n_sample, n_sample_mt):
         list(ex.map(scan_piece, pieces))
         list(ex.map(topk_head, range(hkv)))
         dtm = time.perf_counter() - t0
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f
+                              if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    plane_bytes_mt = n_sample_mt * hkv * 176 // 8   # about 176 union bits per (kv head, key)
     return dict(value=round(n_sample_mt * hkv / dtm, 1), unit="keys/s", cores=cores,
-                kind="oracle",
+                kind="oracle", cpu_model=cpu_model,
+                plane_bytes_per_s_approx=round(plane_bytes_mt / dtm, 1),
                 sample=(f"first {n_sample_mt} keys of the 1M-key layer, all {hkv} kv heads / "
                         f"{hq} query heads: plan + fp64 scan + top-{w.k} (full sort), "
                         f"{dtm:.1f} s on {cores} threads ({len(pieces)} scan pieces of "
@@ -697,6 +709,16 @@ def main():
                                   **{k: round(x, 4) for k, x in t.items()}}
             log(f"fixed r=16 {mode}_fused: {t}")
         variants["fixed_r16"] = v
+        # fixed-128: the r = 32 plan without the side stream
+        v = {"union_plane_bytes": fixed_plan_b}
+        for mode in res_modes(args):
+            t = timed(layers, w, fws, args.steps, args.warmup, mode, fixed=True, fused=True,
+                      with_meta=False)
+            v[mode + "_fused"] = {"keys_per_s": round(w.n * w.hkv / (t["step_ms"] * 1e-3), 1),
+                                  **{k: round(x, 4) for k, x in t.items()}}
+            v[mode + "_speedup_of_fathom"] = round(t["step_ms"] / res[mode + "_fused"]["step_ms"], 3)
+            log(f"fixed-128 {mode}_fused: {t}")
+        variants["fixed128"] = v
 
     keys_per_step = w.n * w.hkv
     main_mode = "host" if "host" in res else "hbm"
@@ -712,7 +734,9 @@ def main():
                     "kernel": "scan_kernel<4, 32, 2> (planes in pinned host memory)",
                     "algorithmic_bytes": plane_b,
                     "frac_of_measured_link_peak": (round(achieved / probe["host_read_zero_copy_GBps"], 4)
-                                                   if probe else None)}
+                                                   if probe else None),
+                    "end_to_end_frac": round(plane_b / (r["step_ms"] * 1e-3) / 1e9 /
+                                             PCIE_PEAK_GBPS, 4)}
     out = {
         "metric": "keys scanned/s (1M-token layer, B=92, k=2048, planes zero-copy from pinned host)",
         "value": round(value, 1),
@@ -721,6 +745,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(r["step_ms"], 4),
+        "query_keys_per_s": round(value * w.hq / w.hkv, 1),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
