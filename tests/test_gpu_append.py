@@ -136,3 +136,24 @@ def test_batched_sessions_with_capacity_planes(F):
     torch.cuda.synchronize()
     for s, (ri, rv) in zip(sess, refs):
         assert torch.equal(s.idx, ri) and torch.equal(s.vals, rv)
+
+
+def test_pinned_capacity_planes_scan_like_compact(F):
+    """Host-resident planes take the host-link kernel: capacity and compact
+    layouts of the same keys give identical logits and top-k."""
+    n = 9000
+    keys = synth.keys(75, 0, n, 2, 128, torch.float16, 4, device=dev())
+    p = F.pack(keys)
+    cap = F.alloc_planes(3 * 2048 * 2 + 100, 2, pin_memory=True)
+    cap[..., :p.planes.shape[-1]].copy_(p.planes)
+    compact = torch.empty(p.planes.shape, dtype=p.planes.dtype, pin_memory=True)
+    compact.copy_(p.planes)
+    q = synth.queries(75, 0, 8, 128, device=dev())
+    plan = F.plan(q, p.sigma2, 92)
+    a = F.scan(cap, p.lo, p.hi, n, q, plan)
+    b = F.scan(compact, p.lo, p.hi, n, q, plan)
+    ia, va = F.scan_topk(cap, p.lo, p.hi, n, q, plan, 300, 1)
+    ib, vb = F.scan_topk(compact, p.lo, p.hi, n, q, plan, 300, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(ia, ib) and torch.equal(va, vb)
