@@ -323,9 +323,9 @@ __device__ __forceinline__ void bit_transpose32(uint32_t (&x)[32]) {
   bit_stage<1, 0x55555555u>(x);
 }
 
-// One block = (2048-key tile, quarter Q of the channels, kv head), with the
-// quarter and the head varying fastest over the grid, so that the blocks
-// running together read whole key rows.
+// One block = (2048-key tile, quarter Q of the channels, kv head); the blocks
+// of one tile's quarters run together on one XCD, so that together they read
+// whole key rows through one L2.
 //  * staging: thread t takes channels 32Q + 8j .. +7 (j = t % 4) of key rows
 //    t / 4, t / 4 + 64, ... (16-byte loads: a wave instruction reads the
 //    quarter of 16 rows; the next batch of rows is in flight while the
@@ -352,8 +352,15 @@ __global__ __launch_bounds__(kVecThreads) void pack_planes_vec_kernel(
   // per bank)
   __shared__ uint32_t s_codes[kBlockKeys * kGroups + kBlockKeys / 32];
   auto cidx = [](int key, int grp) { return key * kGroups + grp + (key >> 5); };
+  // Block index -> (tile, kv head) pair and quarter: the four quarters of a
+  // pair are 8 indices apart, which the dispatcher's round robin over the 8
+  // XCDs places on one XCD back to back, so the quarter rows of a key (parts
+  // of the same cache lines) meet in one L2 instead of being fetched by two.
   const int bx = blockIdx.x;
-  const int Q = bx & 3, h = (bx >> 2) % hkv, tile = (bx >> 2) / hkv;
+  const int pair = (bx >> 5) * 8 + (bx & 7);
+  const int Q = (bx >> 3) & 3;
+  if (pair >= (int)(W / 64) * hkv) return;  // padding of the last group of 8 pairs
+  const int h = pair % hkv, tile = pair / hkv;
   const int tid = threadIdx.x;
   const int jr = tid >> 2, j = tid & 3;     // staging: row offset, channel group
   const int wave = tid >> 6, lane = tid & 63;
@@ -539,7 +546,8 @@ int32_t launch_pack_t(const T *keys, int64_t n, int32_t hkv, int64_t stride_tok,
   hipLaunchKernelGGL(pack_range_kernel, dim3(hkv), dim3(kReduceThreads), 0, s, part, L.nparts,
                      hkv, lo, hi);
   if (vec)
-    hipLaunchKernelGGL(pack_planes_vec_kernel<T>, dim3(L.nblocks * 4 * hkv), dim3(kVecThreads),
+    hipLaunchKernelGGL(pack_planes_vec_kernel<T>,
+                       dim3((unsigned)(((int64_t)L.nblocks * hkv + 7) / 8 * 32)), dim3(kVecThreads),
                        0, s, keys, n, stride_tok, stride_head, W, hkv, lo, hi, planes, sums);
   else
     hipLaunchKernelGGL(pack_planes_kernel<T>, dim3(L.nblocks, hkv), dim3(kPlaneThreads),
