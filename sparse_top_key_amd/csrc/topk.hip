@@ -538,8 +538,11 @@ __device__ uint64_t block_or64(uint64_t v, uint64_t *red) {
 // holding the kk-th word are laid out in descending bucket order, and each
 // word's rank is its bucket's offset plus the number of larger words in its
 // bucket.  Returns false, having written nothing, when one of those buckets
-// holds more than kMaxBucket words (the caller then sorts).
-constexpr int kMaxBucket = 128;
+// holds more than kMaxBucket words (the caller then sorts).  Buckets grow
+// when the candidates span two binades, so that the binning window starts in
+// the exponent bits; a word's rank is a loop over its bucket, and even at 512
+// words that costs far less than the sort it avoids.
+constexpr int kMaxBucket = 512;
 
 __device__ bool bucket_rank_out(const uint64_t *src, int m, int kk, uint64_t *buck, int *hist,
                                 int *above, int *wave_tot, int *s_res, uint64_t *red,
