@@ -56,6 +56,18 @@ def test_topk_heavy_ties(F, orc):
     check(F, orc, S, 1000)
 
 
+def test_topk_bucket_overflow_sorts(F, orc):
+    """One outlier far above a tight cluster of distinct scores: the binning
+    window starts in the exponent bits, the cluster fills one bucket far
+    beyond the exact-ranking cap, and the radix select plus sort decides."""
+    rng = np.random.default_rng(4)
+    S = (1.0 + rng.uniform(0, 1e-3, (3, 6000))).astype(np.float32)
+    S[:, 17] = 1e6
+    S[1, 100:200] = S[1, 300]                         # ties inside the cluster as well
+    check(F, orc, S, 2048)
+    check(F, orc, S, 700)
+
+
 def test_topk_all_equal_takes_lowest_indices(F, orc):
     S = np.full((2, 30000), 1.5, np.float32)            # forces the exact fallback
     check(F, orc, S, 2048)
