@@ -547,3 +547,120 @@ int orc_append(const float *keys, int64_t m, int hkv, int d, int64_t stride_tok,
   *clamped = count;
   return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Per-channel code histograms.  hist[h][c][v] = number of keys i < n whose
+ * 4-bit code in channel c of kv head h is v, read back bit by bit from the
+ * planes (rows of W words).                                                 */
+int orc_code_hist(const uint32_t *planes, int64_t n, int hkv, int d, int64_t W,
+                  uint32_t *hist) {
+  if (!planes || !hist || n < 0 || hkv < 1 || d < 1 || W < orc_plane_words(n)) return ORC_BAD;
+  for (int h = 0; h < hkv; ++h)
+    for (int c = 0; c < d; ++c) {
+      uint32_t *hc = hist + ((int64_t)h * d + c) * 16;
+      const uint32_t *pl = planes + ((int64_t)h * d + c) * 4 * W;
+      for (int v = 0; v < 16; ++v) hc[v] = 0;
+      for (int64_t i = 0; i < n; ++i) {
+        int code = 0;
+        for (int s = 0; s < 4; ++s) code = (code << 1) | (int)((pl[s * W + i / 32] >> (i % 32)) & 1u);
+        hc[code] += 1;
+      }
+    }
+  return ORC_OK;
+}
+
+/* Calibrated allocation.  [EXP] key pseudocode: the original allocates more
+ * finely than fill-to-cap without saying how; the intuition section ties the
+ * allocation to how much each channel's error moves the logit.  Reading R21:
+ * reading channel c to depth t leaves, per key, the gap between its 4-bit
+ * value and the t-bit cell centre (R11); over the layer's keys that error is
+ * E_c(t) * delta_c^2 with
+ *     E_c(t) = sum_v hist_c[v] * ((v mod 2^(4-t)) + 1/2 - 2^(3-t))^2
+ * (exact in fp64: counts times quarter-integers), and it enters query head
+ * h's logit with weight q_hc^2.  The plan minimises
+ *     sum_c cost_hc(t_c),  cost_hc(t) = fl64(fl64(q_hc^2 * delta_c^2) * E_c(t))
+ * (q_hc^2 and delta_c^2 exact in fp64) over all plans with sum t_c = B,
+ * 0 <= t_c <= 4, by dynamic programming over the channels in order:
+ *     F_0 = [0, inf, ...];  F_{c+1}[b] = min_t F_c[b - t] + cost_hc(t)
+ * (one fp64 add each; t tried in increasing order, a later t replaces the
+ * best only when strictly smaller), then the choices are followed back from
+ * F_d[B].  delta_c = fl32(fl32(hi - lo) * 1/16) as in R2.
+ * hist [hkv][d][16]; budget [hq]; plan out [hq][d].                         */
+/* E_c(t) of R21 for every (kv head, channel) and t = 0..4, in delta^2 units:
+ * E out [hkv][d][5].                                                        */
+int orc_depth_errors(const uint32_t *hist, int hkv, int d, double *E) {
+  if (!hist || !E || hkv < 1 || d < 1) return ORC_BAD;
+  for (int64_t hc = 0; hc < (int64_t)hkv * d; ++hc)
+    for (int t = 0; t <= 4; ++t) {
+      const int m = 1 << (4 - t);
+      double e = 0.0;
+      for (int v = 0; v < 16; ++v) {
+        const double off = (double)(v % m) + 0.5 - 0.5 * m;
+        e += (double)hist[hc * 16 + v] * (off * off);
+      }
+      E[hc * 5 + t] = e;
+    }
+  return ORC_OK;
+}
+
+int orc_plan_calibrated(const float *q, int hq, int hkv, int d, const float *lo,
+                        const float *hi, const uint32_t *hist, const int32_t *budget,
+                        uint8_t *plan) {
+  if (!q || !lo || !hi || !hist || !budget || !plan || hq < 1 || hkv < 1 || hq % hkv || d < 1)
+    return ORC_BAD;
+  const int G = hq / hkv;
+  double *cost = (double *)malloc(sizeof(double) * 5 * d);
+  double *E = (double *)malloc(sizeof(double) * 5 * d * hkv);
+  double *F = (double *)malloc(sizeof(double) * (4 * d + 1));
+  double *Fn = (double *)malloc(sizeof(double) * (4 * d + 1));
+  uint8_t *choice = (uint8_t *)malloc((size_t)d * (4 * d + 1));
+  int rc = ORC_OK;
+  if (!cost || !E || !F || !Fn || !choice || orc_depth_errors(hist, hkv, d, E) != ORC_OK) {
+    rc = ORC_BAD;
+    goto done;
+  }
+  for (int h = 0; h < hq; ++h) {
+    const int B = budget[h];
+    if (B < 0 || B > 4 * d) {
+      rc = ORC_BAD;
+      goto done;
+    }
+    const int g = h / G;
+    for (int c = 0; c < d; ++c) {
+      const float delta = (hi[g * d + c] - lo[g * d + c]) * 0.0625f;
+      const double qd = (double)q[(int64_t)h * d + c] * (double)q[(int64_t)h * d + c] *
+                        ((double)delta * (double)delta);
+      for (int t = 0; t <= 4; ++t) cost[c * 5 + t] = qd * E[((int64_t)g * d + c) * 5 + t];
+    }
+    for (int b = 0; b <= B; ++b) F[b] = b == 0 ? 0.0 : INFINITY;
+    for (int c = 0; c < d; ++c) {
+      for (int b = 0; b <= B; ++b) {
+        double best = INFINITY;
+        int bt = 0;
+        for (int t = 0; t <= 4 && t <= b; ++t) {
+          const double v = F[b - t] + cost[c * 5 + t];
+          if (v < best) {
+            best = v;
+            bt = t;
+          }
+        }
+        Fn[b] = best;
+        choice[(int64_t)c * (4 * d + 1) + b] = (uint8_t)bt;
+      }
+      for (int b = 0; b <= B; ++b) F[b] = Fn[b];
+    }
+    int b = B;
+    for (int c = d - 1; c >= 0; --c) {
+      const int t = choice[(int64_t)c * (4 * d + 1) + b];
+      plan[(int64_t)h * d + c] = (uint8_t)t;
+      b -= t;
+    }
+  }
+done:
+  free(cost);
+  free(E);
+  free(F);
+  free(Fn);
+  free(choice);
+  return rc;
+}

@@ -54,10 +54,14 @@ def _load():
         lib.orc_read_prefixes.argtypes = [P, L, I, I, P, I, P]
         lib.orc_topk.argtypes = [P, I, L, L, I, I, P, P]
         lib.orc_append.argtypes = [P, L, I, I, L, L, L, P, L, P, P, P]
+        lib.orc_code_hist.argtypes = [P, L, I, I, L, P]
+        lib.orc_depth_errors.argtypes = [P, I, I, P]
+        lib.orc_plan_calibrated.argtypes = [P, I, I, I, P, P, P, P, P]
         lib.orc_sparse_attention.argtypes = [P, I, I, I, P, P, L, L, L, P, I, I, F, P, P]
         for f in ("orc_pack", "orc_plan", "orc_plan_fixed", "orc_plan_rd", "orc_plan_group",
                   "orc_scan", "orc_scan_at",
-                  "orc_read_prefixes", "orc_topk", "orc_sparse_attention", "orc_append"):
+                  "orc_read_prefixes", "orc_topk", "orc_sparse_attention", "orc_append", "orc_code_hist", "orc_depth_errors",
+                  "orc_plan_calibrated"):
             getattr(lib, f).restype = I
         _lib = lib
     return _lib
@@ -235,3 +239,36 @@ def append(keys_new, n_old: int, planes, lo, hi):
     _check(_load().orc_append(_ptr(k32), m, hkv, d, hkv * d, d, n_old, _ptr(planes), W,
                               _ptr(lo), _ptr(hi), _ptr(cnt)), "append")
     return int(cnt[0])
+
+
+def code_hist(planes, n: int):
+    """planes [hkv][d][4][W] uint32 -> hist [hkv][d][16] uint32 of keys < n."""
+    planes = np.ascontiguousarray(planes, dtype=np.uint32)
+    hkv, d, _, W = planes.shape
+    out = np.empty((hkv, d, 16), np.uint32)
+    _check(_load().orc_code_hist(_ptr(planes), n, hkv, d, W, _ptr(out)), "code_hist")
+    return out
+
+
+def depth_errors(hist):
+    """hist [hkv][d][16] -> E [hkv][d][5] (fp64, delta^2 units)."""
+    hist = np.ascontiguousarray(hist, dtype=np.uint32)
+    hkv, d, _ = hist.shape
+    out = np.empty((hkv, d, 5), np.float64)
+    _check(_load().orc_depth_errors(_ptr(hist), hkv, d, _ptr(out)), "depth_errors")
+    return out
+
+
+def plan_calibrated(q, lo, hi, hist, budget) -> np.ndarray:
+    """q [hq][d], lo/hi [hkv][d], hist [hkv][d][16], budget int or [hq] -> plan."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    lo = np.ascontiguousarray(lo, dtype=np.float32)
+    hi = np.ascontiguousarray(hi, dtype=np.float32)
+    hist = np.ascontiguousarray(hist, dtype=np.uint32)
+    hq, d = q.shape
+    hkv = lo.shape[0]
+    b = np.ascontiguousarray(np.broadcast_to(np.asarray(budget, np.int32), (hq,)))
+    out = np.empty((hq, d), np.uint8)
+    _check(_load().orc_plan_calibrated(_ptr(q), hq, hkv, d, _ptr(lo), _ptr(hi), _ptr(hist),
+                                       _ptr(b), _ptr(out)), "plan_calibrated")
+    return out

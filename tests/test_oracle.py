@@ -867,3 +867,123 @@ def test_append_constant_channel_and_rejections(orc):
     assert np.all(unpack_planes_vectorised(planes, 6)[0, :, 5] == 0)
     with pytest.raises(ValueError):                        # rows too short for n_old + m
         orc.append(np.zeros((2, 1, 4), np.float32), 2047, planes, lo, hi)
+
+
+# --------------------------------------------------------------------------
+# calibrated allocation: code histograms, depth errors, exact DP
+
+def test_code_hist_counts_the_quantiser_codes(orc):
+    rng = np.random.default_rng(31)
+    keys = (rng.standard_normal((3000, 2, 16)) * rng.uniform(0.3, 2, (1, 2, 16))).astype(np.float16)
+    p = orc.pack(keys)
+    hist = orc.code_hist(p["planes"], 3000)
+    for h in range(2):
+        for c in range(16):
+            codes = t_bit_quantizer(keys[:, h, c].astype(np.float32), p["lo"][h, c],
+                                    p["hi"][h, c], 4)
+            np.testing.assert_array_equal(hist[h, c], np.bincount(codes, minlength=16))
+
+
+def test_depth_errors_are_squared_gaps_of_the_raw_keys(orc):
+    """E(t) * delta^2 = sum over keys of (4-bit value - t-bit reconstruction)^2,
+    both computed here from the raw keys with the independent quantiser."""
+    rng = np.random.default_rng(32)
+    keys = (rng.standard_normal((2500, 1, 8)) * 1.7).astype(np.float32)
+    p = orc.pack(keys)
+    E = orc.depth_errors(orc.code_hist(p["planes"], 2500))
+    for c in range(8):
+        x = keys[:, 0, c]
+        lo, hi = p["lo"][0, c], p["hi"][0, c]
+        delta = float(np.float32(np.float32(hi - lo) * np.float32(0.0625)))
+        x4 = lo + (t_bit_quantizer(x, lo, hi, 4) + 0.5) * delta
+        for t in range(5):
+            cell = delta * 2 ** (4 - t)
+            xt = lo + (t_bit_quantizer(x, lo, hi, t) + 0.5) * cell
+            ref = float(((x4 - xt) ** 2).sum()) / delta ** 2
+            assert abs(E[0, c, t] - ref) <= 1e-9 * max(1.0, ref), (c, t)
+    assert np.all(E[..., 4] == 0)
+
+
+def test_depth_errors_of_a_point_mass_and_a_uniform_channel(orc):
+    """Worked by hand from the cell centres: every key at code 8 leaves
+    offsets 0.5, -3.5, -1.5, -0.5, 0 at depths 0..4; one key per code gives
+    sum (v + 1/2 - 8)^2 = 340 at depth 0 and 16 (m^2 - 1) / 12 per cell of m
+    codes after."""
+    hist = np.zeros((1, 2, 16), np.uint32)
+    hist[0, 0, 8] = 16
+    hist[0, 1, :] = 1
+    E = orc.depth_errors(hist)
+    np.testing.assert_array_equal(E[0, 0], 16 * np.array([0.25, 12.25, 2.25, 0.25, 0]))
+    np.testing.assert_array_equal(E[0, 1], [340, 84, 20, 4, 0])
+
+
+def test_plan_calibrated_skips_depths_that_add_error(orc):
+    """Channel 0: weight 10, every key at code 8; channel 1: weight 1, one key
+    per code.  Per-depth costs (weight x E): channel 0 [40, 1960, 360, 40, 0],
+    channel 1 [340, 84, 20, 4, 0].  A single bit of channel 0 makes its error
+    worse than reading nothing, so with B = 5 the exact minimum is (3, 2)
+    (cost 60), where filling channel 1 first and giving channel 0 the rest
+    would cost 1960."""
+    hist = np.zeros((1, 2, 16), np.uint32)
+    hist[0, 0, 8] = 16
+    hist[0, 1, :] = 1
+    lo = np.zeros((1, 2), np.float32)
+    hi = np.full((1, 2), 16.0, np.float32)                       # delta = 1
+    q = np.array([[np.sqrt(10.0), 1.0]], np.float32)
+    expect = {1: [0, 1], 3: [0, 3], 4: [0, 4], 5: [3, 2], 6: [4, 2], 7: [4, 3], 8: [4, 4]}
+    for B, plan in expect.items():
+        assert list(orc.plan_calibrated(q, lo, hi, hist, B)[0]) == plan, B
+
+
+@pytest.mark.parametrize("d", [3, 4, 5])
+def test_plan_calibrated_is_the_brute_force_minimum(orc, d):
+    rng = np.random.default_rng(400 + d)
+    plans = np.array(list(itertools.product(range(5), repeat=d)))
+    for trial in range(4):
+        q = rng.standard_normal((1, d)).astype(np.float32)
+        lo = rng.uniform(-3, -1, (1, d)).astype(np.float32)
+        hi = rng.uniform(1, 3, (1, d)).astype(np.float32)
+        hist = rng.integers(0, 200, (1, d, 16)).astype(np.uint32)
+        E = orc.depth_errors(hist)[0]
+        delta = ((hi - lo) * np.float32(0.0625)).astype(np.float32)[0].astype(np.float64)
+        w = q[0].astype(np.float64) ** 2 * delta ** 2
+        cost = w[:, None] * E                                     # [d][5]
+        for B in range(0, 4 * d + 1):
+            feas = plans[plans.sum(1) == B]
+            tot = np.zeros(len(feas))
+            for c in range(d):                                    # channel order, fp64
+                tot = tot + cost[c, feas[:, c]]
+            best = feas[tot == tot.min()]
+            got = orc.plan_calibrated(q, lo, hi, hist, B)[0]
+            assert len(best) == 1
+            np.testing.assert_array_equal(got, best[0])
+
+
+def test_plan_calibrated_on_uniform_channels_is_the_rd_plan(orc):
+    """With every code equally frequent, reading bit t+1 removes a quarter of
+    what bit t removed, so the exact minimum is the rate-distortion greedy on
+    the weights q^2 delta^2."""
+    rng = np.random.default_rng(41)
+    hq, hkv, d = 4, 2, 32
+    q = rng.standard_normal((hq, d)).astype(np.float32)
+    lo = rng.uniform(-3, -1, (hkv, d)).astype(np.float32)
+    hi = rng.uniform(1, 3, (hkv, d)).astype(np.float32)
+    hist = np.full((hkv, d, 16), 7, np.uint32)
+    delta2 = (((hi - lo) * np.float32(0.0625)).astype(np.float32) ** 2).astype(np.float32)
+    for B in (0, 5, 40, 77, 128):
+        np.testing.assert_array_equal(orc.plan_calibrated(q, lo, hi, hist, B),
+                                      orc.plan_rd(q, delta2, B))
+
+
+@pytest.mark.parametrize("B", [0, 1, 92, 136, 512])
+def test_plan_calibrated_spends_the_budget(orc, B):
+    rng = np.random.default_rng(B + 50)
+    keys = synth_like = (rng.standard_normal((4000, 2, 128)) *
+                         rng.uniform(0.1, 4, (1, 2, 128))).astype(np.float16)
+    p = orc.pack(keys)
+    hist = orc.code_hist(p["planes"], 4000)
+    q = rng.standard_normal((8, 128)).astype(np.float32)
+    plan = orc.plan_calibrated(q, p["lo"], p["hi"], hist, B).astype(np.int64)
+    assert np.all(plan.sum(1) == B) and np.all(plan <= 4)
+    with pytest.raises(ValueError):
+        orc.plan_calibrated(q, p["lo"], p["hi"], hist, 513)
