@@ -147,6 +147,39 @@ int32_t fathom_plan_group(const float *q, int32_t hq, int32_t hkv, int32_t d,
                           const float *sigma2, const int32_t *budget_bits,
                           uint8_t *plan, void *stream);
 
+/* Calibrated allocation (two calls).  The explainer's key-pseudocode section
+ * says the original allocates more finely than fill-to-cap without giving
+ * the rule; this is a stated reading that measures each channel's error on
+ * the layer itself.
+ *
+ * fathom_code_hist: hist[h][c][v] = number of keys i < n whose 4-bit code in
+ * channel c of kv head h is v (v = 0..15), read from the planes.
+ *   planes  device or pinned-host, 16-byte aligned, rows of plane_words
+ *           words (0: fathom_plane_words(n)); bits of keys >= n are ignored
+ *   hist    device output uint32[hkv][d][16]
+ *
+ * fathom_plan_calibrated: reading channel c to depth t leaves each key the
+ * gap between its 4-bit value and its t-bit cell centre; over the layer that
+ * is delta_c^2 * E_c(t), E_c(t) = sum_v hist_c[v] * (v mod 2^(4-t) + 1/2 -
+ * 2^(3-t))^2 (exact in fp64), and it moves head h's logit with weight
+ * q_hc^2.  The plan minimises sum_c cost_hc(t_c),
+ * cost_hc(t) = fl64(fl64(q_hc^2 * delta_c^2) * E_c(t)), delta_c =
+ * fl32(fl32(hi - lo) * 1/16), over all plans with sum t_c = B, 0 <= t_c <= 4
+ * (dynamic programming over the channels in order, fp64 sums; on equal sums
+ * the smaller t of the later channel wins).  Unlike fill-to-cap it skips
+ * depths that leave more error than reading less (a channel whose keys sit
+ * near its range's midpoint gains nothing from its top bit).
+ *   q            device fp32[hq][d];  lo, hi device fp32[hkv][d] (fathom_pack)
+ *   hist         device uint32[hkv][d][16] (fathom_code_hist)
+ *   budget_bits  HOST int32[hq], each in [0, 4d]
+ *   plan         device output uint8[hq][d], sum_c t_c = B.                  */
+int32_t fathom_code_hist(const uint32_t *planes, int64_t n, int32_t hkv, int32_t d,
+                         int64_t plane_words, uint32_t *hist, void *stream);
+int32_t fathom_plan_calibrated(const float *q, int32_t hq, int32_t hkv, int32_t d,
+                               const float *lo, const float *hi,
+                               const uint32_t *hist, const int32_t *budget_bits,
+                               uint8_t *plan, void *stream);
+
 /* Fixed-width baseline plan (the pages' 136-bit scans read r = 32 channels
  * in full): the r channels with the largest |q_c| (ties: lower channel) get
  * t = 4, all others 0.  0 <= r <= d.                                        */

@@ -66,6 +66,8 @@ def lib():
             "fathom_plan_fixed": (I32, [P, I32, I32, I32, P, P]),
             "fathom_plan_rd": (I32, [P, I32, I32, I32, P, P, P, P]),
             "fathom_plan_group": (I32, [P, I32, I32, I32, P, P, P, P]),
+            "fathom_code_hist": (I32, [P, I64, I32, I32, I64, P, P]),
+            "fathom_plan_calibrated": (I32, [P, I32, I32, I32, P, P, P, P, P, P]),
             "fathom_attention_workspace_bytes": (I64, [I32, I32]),
             "fathom_append": (I32, [P, I32, I64, I32, I32, I64, I64, I64, P, I64, P, P, P, P]),
             "fathom_sparse_attention": (I32, [P, I32, I32, I32, P, P, I32, I64, I64, I64, P,
@@ -197,6 +199,35 @@ def plan_rd(q: torch.Tensor, sigma2: torch.Tensor, budget, out=None) -> torch.Te
 def plan_group(q: torch.Tensor, sigma2: torch.Tensor, budget, out=None) -> torch.Tensor:
     """One plan per GQA group; budget int or sequence of hkv ints."""
     return _plan_call("fathom_plan_group", q, sigma2, budget, sigma2.shape[0], out)
+
+
+def code_hist(planes: torch.Tensor, n: int, out=None) -> torch.Tensor:
+    """Histogram of the 4-bit codes per (kv head, channel) -> int32 [hkv][d][16]
+    (counts, stored as int32)."""
+    _require_gpu(planes)
+    hkv, d = planes.shape[0], planes.shape[1]
+    if out is None:
+        out = torch.empty((hkv, d, 16), dtype=torch.int32, device=planes.device
+                          if planes.is_cuda else "cuda")
+    _check(lib().fathom_code_hist(_p(planes), n, hkv, d, planes.shape[-1], _p(out),
+                                  _stream(out.device)), "fathom_code_hist")
+    return out
+
+
+def plan_calibrated(q: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor, hist: torch.Tensor,
+                    budget, out=None) -> torch.Tensor:
+    """Calibrated allocation (exact DP on measured per-depth errors); budget int
+    or sequence of hq ints."""
+    _require_gpu(q, lo, hist)
+    hq, d = q.shape
+    hkv = lo.shape[0]
+    b = _budgets(budget, hq)
+    if out is None:
+        out = torch.empty((hq, d), dtype=torch.uint8, device=q.device)
+    _check(lib().fathom_plan_calibrated(_p(q.contiguous()), hq, hkv, d, _p(lo.contiguous()),
+                                        _p(hi.contiguous()), _p(hist.contiguous()), b, _p(out),
+                                        _stream(q.device)), "fathom_plan_calibrated")
+    return out
 
 
 def plan_fixed(q: torch.Tensor, r: int, out=None) -> torch.Tensor:

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfathom.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "pack.hip", "plan.hip", "scan.hip", "topk.hip", "scan_topk.hip", "probe.hip", "attn.hip", "append.hip"]
+SOURCES = ["api.hip", "pack.hip", "plan.hip", "scan.hip", "topk.hip", "scan_topk.hip", "probe.hip", "attn.hip", "append.hip", "calib.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

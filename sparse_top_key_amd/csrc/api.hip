@@ -207,6 +207,37 @@ int32_t fathom_sparse_attention(const float *q, int32_t hq, int32_t hkv, int32_t
                           group, k, scale, out, lse, ws, as_stream(stream));
 }
 
+int32_t fathom_code_hist(const uint32_t *planes, int64_t n, int32_t hkv, int32_t d,
+                         int64_t plane_words_, uint32_t *hist, void *stream) {
+  REQUIRE(planes && hist, FATHOM_ERR_INVALID_ARG, "fathom_code_hist: null pointer");
+  REQUIRE(hkv >= 1, FATHOM_ERR_INVALID_ARG, "fathom_code_hist: hkv must be >= 1");
+  if (int32_t rc = check_d(d)) return rc;
+  REQUIRE(n >= 0 && n <= ((int64_t)1 << 31), FATHOM_ERR_INVALID_ARG,
+          "fathom_code_hist: n must be in [0, 2^31] (got %lld)", (long long)n);
+  const int64_t W = plane_words_ == 0 ? plane_words(n) : plane_words_;
+  REQUIRE(W >= plane_words(n) && W % 64 == 0 && W <= ((int64_t)1 << 26),
+          FATHOM_ERR_INVALID_ARG,
+          "fathom_code_hist: plane_words (%lld) must be 0 or a multiple of 64 in [%lld, 2^26]",
+          (long long)plane_words_, (long long)plane_words(n));
+  REQUIRE((reinterpret_cast<uintptr_t>(planes) & 15) == 0, FATHOM_ERR_UNSUPPORTED,
+          "fathom_code_hist: planes must be 16-byte aligned");
+  return launch_code_hist(planes, n, hkv, W, hist, as_stream(stream));
+}
+
+int32_t fathom_plan_calibrated(const float *q, int32_t hq, int32_t hkv, int32_t d,
+                               const float *lo, const float *hi, const uint32_t *hist,
+                               const int32_t *budget_bits, uint8_t *plan, void *stream) {
+  REQUIRE(q && lo && hi && hist && budget_bits && plan, FATHOM_ERR_INVALID_ARG,
+          "fathom_plan_calibrated: null pointer");
+  if (int32_t rc = check_heads(hq, hkv)) return rc;
+  if (int32_t rc = check_d(d)) return rc;
+  for (int32_t h = 0; h < hq; ++h)
+    REQUIRE(budget_bits[h] >= 0 && budget_bits[h] <= 4 * d, FATHOM_ERR_INVALID_ARG,
+            "fathom_plan_calibrated: budget_bits[%d] = %d outside [0, %d]", h, budget_bits[h],
+            4 * d);
+  return launch_plan_calibrated(q, hq, hkv, lo, hi, hist, budget_bits, plan, as_stream(stream));
+}
+
 int32_t fathom_plan_fixed(const float *q, int32_t hq, int32_t d, int32_t r, uint8_t *plan,
                           void *stream) {
   REQUIRE(q && plan, FATHOM_ERR_INVALID_ARG, "fathom_plan_fixed: null pointer");

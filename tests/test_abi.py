@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_path():
     names = declared_functions()
     for f in ("fathom_pack", "fathom_plan", "fathom_plan_fixed", "fathom_plan_rd",
-              "fathom_plan_group", "fathom_sparse_attention", "fathom_append", "fathom_scan",
+              "fathom_plan_group", "fathom_sparse_attention", "fathom_append",
+              "fathom_code_hist", "fathom_plan_calibrated", "fathom_scan",
               "fathom_topk", "fathom_scan_batched", "fathom_topk_batched",
               "fathom_read_prefixes", "fathom_plan_stats", "fathom_probe_read"):
         assert f in names
@@ -288,3 +289,19 @@ def test_session_plane_words_validation(L):
     assert "plane_words" in err(L)
     s[0] = _Session(A, A, A, 5000, A, A, None, 0.0, A, 5000, None, None, 200)
     assert L.fathom_scan_batched(s, 1, 8, 128, 32, None) == 1   # not a multiple of 64
+
+
+def test_calibrated_validation(L):
+    A = ctypes.c_void_p(0x10000)
+    U = ctypes.c_void_p(0x10004)
+    # every case below fails validation, so nothing is ever enqueued
+    assert L.fathom_code_hist(None, 100, 8, 128, 0, A, None) == 1
+    assert L.fathom_code_hist(A, 100, 8, 64, 0, A, None) == 2
+    assert L.fathom_code_hist(A, -1, 8, 128, 0, A, None) == 1
+    assert L.fathom_code_hist(A, 5000, 8, 128, 64, A, None) == 1    # 5000 keys need 192 words
+    assert L.fathom_code_hist(U, 100, 8, 128, 0, A, None) == 2 and "16-byte" in err(L)
+    b = (ctypes.c_int32 * 4)(92, 92, 600, 92)
+    assert L.fathom_plan_calibrated(A, 4, 1, 128, A, A, A, b, A, None) == 1
+    assert "budget_bits[2] = 600" in err(L)
+    assert L.fathom_plan_calibrated(A, 4, 3, 128, A, A, A, b, A, None) == 1
+    assert L.fathom_plan_calibrated(A, 4, 1, 128, A, A, None, b, A, None) == 1
