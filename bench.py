@@ -63,6 +63,7 @@ class Layer:
             self.meta_host.copy_(self.meta)
         self.budget = [w.budget] * w.hq
         self.group_budget = [w.budget] * w.hkv
+        self.hist = fathom.code_hist(p.planes, w.n)     # per-layer statistic, like sigma2
         self.plan = torch.empty((w.hq, w.d), dtype=torch.uint8, device=dev)
         self.plan_fixed = fathom.plan_fixed(self.q, fixed_r)
         self.logits = torch.empty((w.hq, w.n), dtype=torch.float32, device=dev)
@@ -107,6 +108,8 @@ def run_steps(layers, w, ws, steps, mode, fixed=False, fused=False, per_call=Tru
             plan = fathom.plan_rd(L.q, L.sigma2, L.budget, out=L.plan)
         elif variant == "group":
             plan = fathom.plan_group(L.q, L.sigma2, L.group_budget, out=L.plan)
+        elif variant == "calibrated":
+            plan = fathom.plan_calibrated(L.q, L.lo, L.hi, L.hist, L.budget, out=L.plan)
         else:
             plan = fathom.plan(L.q, L.sigma2, L.budget, out=L.plan)
         if per_call:
@@ -348,6 +351,12 @@ def plan_quality(dev, layers_q=2):
     G = w.hq // w.hkv
     kinds = [("fathom_B92", lambda p, q: fathom.plan(q, p.sigma2, 92)),
              ("rd_B92", lambda p, q: fathom.plan_rd(q, p.sigma2, 92)),
+             ("calibrated_B92", lambda p, q: fathom.plan_calibrated(
+                 q, p.lo, p.hi, fathom.code_hist(p.planes, p.n), 92)),
+             ("calibrated_B68", lambda p, q: fathom.plan_calibrated(
+                 q, p.lo, p.hi, fathom.code_hist(p.planes, p.n), 68)),
+             ("calibrated_B136", lambda p, q: fathom.plan_calibrated(
+                 q, p.lo, p.hi, fathom.code_hist(p.planes, p.n), 136)),
              ("group_B92_per_kv_head", lambda p, q: fathom.plan_group(q, p.sigma2, 92)),
              ("group_B368_per_kv_head", lambda p, q: fathom.plan_group(q, p.sigma2, 4 * 92)),
              ("fathom_B68", lambda p, q: fathom.plan(q, p.sigma2, 68)),
@@ -686,9 +695,15 @@ def main():
     variants = {}
     if not args.no_extra:
         for var, fn, bud in (("rd", fathom.plan_rd, "budget"),
-                             ("group", fathom.plan_group, "group_budget")):
-            vper = [union_plane_bytes(fn(L.q, L.sigma2, getattr(L, bud)), w.hkv, w.n)
-                    for L in layers]
+                             ("group", fathom.plan_group, "group_budget"),
+                             ("calibrated", None, "budget")):
+            if fn is None:
+                vper = [union_plane_bytes(fathom.plan_calibrated(L.q, L.lo, L.hi, L.hist,
+                                                                 L.budget), w.hkv, w.n)
+                        for L in layers]
+            else:
+                vper = [union_plane_bytes(fn(L.q, L.sigma2, getattr(L, bud)), w.hkv, w.n)
+                        for L in layers]
             v = {"union_plane_bytes": int(np.mean([x[0] for x in vper])),
                  "union_bits_per_kv_head": vper[0][1], "depth_histogram": vper[0][2]}
             for mode in res_modes(args):
@@ -793,9 +808,9 @@ def main():
                     "union_bits_per_kv_head": ub, "fixed136_union_bits": fub,
                     "depth_histogram": hist}
     if variants:
-        variants["note"] = ("B=92 per query head (rd) or per kv head (group: the whole GQA "
-                            "group reads 92 plane bits per key); fixed_r16: top-16 |q| channels "
-                            "x 4 bits + the 8-bit side stream; fused scan + top-k steps")
+        variants["note"] = ("B=92 per query head (rd, calibrated) or per kv head (group: the "
+                            "whole GQA group reads 92 plane bits per key); fixed_r16: top-16 |q| "
+                            "channels x 4 bits + the 8-bit side stream; fused scan + top-k steps")
         f16 = variants["fixed_r16"]
         fb = plane_b
         variants["fathom_vs_fixed_r16"] = {

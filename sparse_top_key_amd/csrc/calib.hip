@@ -110,26 +110,39 @@ __global__ __launch_bounds__(kDpThreads) void plan_calibrated_kernel(
   }
   for (int b = lane; b <= B; b += kDpThreads) s_f[0][b] = b == 0 ? 0.0 : INFINITY;
   __syncthreads();
-  // ---- F_{c+1}[b] = min_t F_c[b - t] + cost_c(t); t ascending, strict <
+  // ---- F_{c+1}[b] = min_t F_c[b - t] + cost_c(t); t ascending, strict <.
+  // All reads of a step are issued together: a state's five predecessors
+  // come from clamped (always valid) indices, and a depth above the state's
+  // bit count is a +inf candidate, which never wins.
+  constexpr int kStates = (kMaxBudget + kDpThreads) / kDpThreads;  // per lane
   int cur = 0;
   for (int c = 0; c < kD; ++c) {
     double ct[kPlanes + 1];
 #pragma unroll
     for (int t = 0; t <= kPlanes; ++t) ct[t] = s_cost[c][t];
-    for (int b = lane; b <= B; b += kDpThreads) {
+#pragma unroll
+    for (int j = 0; j < kStates; ++j) {
+      if (kDpThreads * j > B) break;  // wave-uniform: no state of this round
+      // lanes past B compute a copy of state B (never stored): every read
+      // stays inside the row of B + 1 states
+      const int b = min(lane + kDpThreads * j, B);
+      double fv[kPlanes + 1];
+#pragma unroll
+      for (int t = 0; t <= kPlanes; ++t) fv[t] = s_f[cur][b >= t ? b - t : 0];
       double best = INFINITY;
       int bt = 0;
 #pragma unroll
       for (int t = 0; t <= kPlanes; ++t) {
-        if (t > b) break;
-        const double v = __dadd_rn(s_f[cur][b - t], ct[t]);
+        const double v = t <= b ? __dadd_rn(fv[t], ct[t]) : INFINITY;
         if (v < best) {
           best = v;
           bt = t;
         }
       }
-      s_f[cur ^ 1][b] = best;
-      s_choice[c][b] = (uint8_t)bt;
+      if (lane + kDpThreads * j <= B) {
+        s_f[cur ^ 1][b] = best;
+        s_choice[c][b] = (uint8_t)bt;
+      }
     }
     __syncthreads();
     cur ^= 1;
