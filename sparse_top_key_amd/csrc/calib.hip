@@ -12,8 +12,9 @@
 //    sum_c fl64(fl64(q_hc^2 delta_c^2) E_c(t_c)) under sum t_c = B, found by
 //    dynamic programming over the channels in order.  One 64-lane wave per
 //    head: lane l keeps the states b = l, l + 64, ... of the running minimum
-//    (fp64, LDS), each channel's choice of t per state goes to a
-//    128 x (B + 1) byte table in LDS, and lane 0 follows the choices back.
+//    (fp64, in registers, predecessors by lane shifts), each channel's choice
+//    of t per state goes to a 128 x (B + 1) byte table in LDS, and lane 0
+//    follows the choices back.
 #include "fathom_internal.h"
 
 namespace fathom {
@@ -72,13 +73,31 @@ __global__ __launch_bounds__(kHistThreads) void code_hist_kernel(const uint32_t 
   if (tid < 16) hist[(int64_t)blockIdx.x * 16 + tid] = s_cnt[tid];
 }
 
-// One 64-lane block per query head h = h0 + blockIdx.x.
+// Whole-wave shift by one lane to the right (lane l gets lane l - 1's value;
+// lane 0 gets `carry`), for fp64 values as two 32-bit DPP moves.
+__device__ __forceinline__ double wave_shr1(double x, double carry) {
+  const int lo = __double2loint(x), hi = __double2hiint(x);
+  const int clo = __double2loint(carry), chi = __double2hiint(carry);
+  const int rlo = __builtin_amdgcn_update_dpp(clo, lo, 0x138 /* wave_shr:1 */, 0xF, 0xF, false);
+  const int rhi = __builtin_amdgcn_update_dpp(chi, hi, 0x138 /* wave_shr:1 */, 0xF, 0xF, false);
+  return __hiloint2double(rhi, rlo);
+}
+// The value of lane 63, in every lane.
+__device__ __forceinline__ double lane63(double x) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(x), 63);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(x), 63);
+  return __hiloint2double(hi, lo);
+}
+
+// One 64-lane block per query head h = h0 + blockIdx.x.  J = rounds of 64
+// states per lane, enough for the largest budget of the launch (no branches
+// on the budget inside the channel loop).
+template <int J>
 __global__ __launch_bounds__(kDpThreads) void plan_calibrated_kernel(
     const float *__restrict__ q, int32_t group, int32_t h0, const float *__restrict__ lo,
     const float *__restrict__ hi, const uint32_t *__restrict__ hist, DpBudgets budgets,
     uint8_t *__restrict__ plan) {
   __shared__ double s_cost[kD][kPlanes + 1];
-  __shared__ double s_f[2][kMaxBudget + 1];
   __shared__ uint8_t s_choice[kD][kMaxBudget + 1];
   __shared__ uint8_t s_plan[kD];
   const int h = h0 + blockIdx.x;
@@ -108,45 +127,59 @@ __global__ __launch_bounds__(kDpThreads) void plan_calibrated_kernel(
       s_cost[c][t] = __dmul_rn(qd, e);
     }
   }
-  for (int b = lane; b <= B; b += kDpThreads) s_f[0][b] = b == 0 ? 0.0 : INFINITY;
   __syncthreads();
   // ---- F_{c+1}[b] = min_t F_c[b - t] + cost_c(t); t ascending, strict <.
-  // All reads of a step are issued together: a state's five predecessors
-  // come from clamped (always valid) indices, and a depth above the state's
-  // bit count is a +inf candidate, which never wins.
-  constexpr int kStates = (kMaxBudget + kDpThreads) / kDpThreads;  // per lane
-  int cur = 0;
+  // Lane l keeps F at the states b = l + 64 j in registers (j < J).
+  // F_c[b - t] reaches lane l by t shifts of one lane to the right across
+  // the whole wave; lane 0 of round j takes lane 63 of round j - 1 (none for
+  // j = 0: those states are negative, +inf).  No LDS round trip per channel:
+  // only the choices are stored.  A depth above a state's bit count is a
+  // +inf candidate, which never wins; states past B are computed but only
+  // ever feed states past B.
+  double f[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) f[j] = (lane == 0 && j == 0) ? 0.0 : INFINITY;
+  double cn[kPlanes + 1];  // the next channel's costs, loaded a step ahead
+#pragma unroll
+  for (int t = 0; t <= kPlanes; ++t) cn[t] = s_cost[0][t];
   for (int c = 0; c < kD; ++c) {
     double ct[kPlanes + 1];
 #pragma unroll
-    for (int t = 0; t <= kPlanes; ++t) ct[t] = s_cost[c][t];
+    for (int t = 0; t <= kPlanes; ++t) {
+      ct[t] = cn[t];
+      cn[t] = s_cost[c + 1 < kD ? c + 1 : c][t];
+    }
+    double sh[J], best[J];
+    int bt[J];
 #pragma unroll
-    for (int j = 0; j < kStates; ++j) {
-      if (kDpThreads * j > B) break;  // wave-uniform: no state of this round
-      // lanes past B compute a copy of state B (never stored): every read
-      // stays inside the row of B + 1 states
-      const int b = min(lane + kDpThreads * j, B);
-      double fv[kPlanes + 1];
+    for (int j = 0; j < J; ++j) {
+      sh[j] = f[j];
+      best[j] = __dadd_rn(f[j], ct[0]);  // t = 0: every state has it
+      bt[j] = 0;
+    }
 #pragma unroll
-      for (int t = 0; t <= kPlanes; ++t) fv[t] = s_f[cur][b >= t ? b - t : 0];
-      double best = INFINITY;
-      int bt = 0;
+    for (int t = 1; t <= kPlanes; ++t) {
+      double nsh[J];
 #pragma unroll
-      for (int t = 0; t <= kPlanes; ++t) {
-        const double v = t <= b ? __dadd_rn(fv[t], ct[t]) : INFINITY;
-        if (v < best) {
-          best = v;
-          bt = t;
-        }
-      }
-      if (lane + kDpThreads * j <= B) {
-        s_f[cur ^ 1][b] = best;
-        s_choice[c][b] = (uint8_t)bt;
+      for (int j = 0; j < J; ++j) nsh[j] = wave_shr1(sh[j], j > 0 ? lane63(sh[j - 1]) : INFINITY);
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        sh[j] = nsh[j];
+        const int b = lane + kDpThreads * j;
+        const double v = t <= b ? __dadd_rn(sh[j], ct[t]) : INFINITY;
+        const bool better = v < best[j];
+        best[j] = better ? v : best[j];
+        bt[j] = better ? t : bt[j];
       }
     }
-    __syncthreads();
-    cur ^= 1;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      f[j] = best[j];
+      const int b = lane + kDpThreads * j;
+      if (b <= B) s_choice[c][b] = (uint8_t)bt[j];
+    }
   }
+  __syncthreads();
   // ---- follow the choices back from F_d[B]
   if (lane == 0) {
     int b = B;
@@ -178,8 +211,21 @@ int32_t launch_plan_calibrated(const float *q, int32_t hq, int32_t hkv, const fl
     const int32_t cnt = std::min(kDpHeadsPerLaunch, hq - h0);
     DpBudgets b{};
     for (int i = 0; i < cnt; ++i) b.b[i] = budget_host[h0 + i];
-    hipLaunchKernelGGL(plan_calibrated_kernel, dim3(cnt), dim3(kDpThreads), 0, s, q, group, h0,
-                       lo, hi, hist, b, plan);
+    int maxb = 0;
+    for (int i = 0; i < cnt; ++i) maxb = std::max(maxb, b.b[i]);
+    const int J = maxb / kDpThreads + 1;  // 1..9
+    const dim3 grid(cnt), block(kDpThreads);
+    switch (J) {
+#define FATHOM_DP_CASE(K)                                                                     \
+  case K:                                                                                     \
+    hipLaunchKernelGGL(plan_calibrated_kernel<K>, grid, block, 0, s, q, group, h0, lo, hi, hist, \
+                       b, plan);                                                              \
+    break;
+      FATHOM_DP_CASE(1) FATHOM_DP_CASE(2) FATHOM_DP_CASE(3) FATHOM_DP_CASE(4)
+      FATHOM_DP_CASE(5) FATHOM_DP_CASE(6) FATHOM_DP_CASE(7) FATHOM_DP_CASE(8)
+      default: FATHOM_DP_CASE(9)
+#undef FATHOM_DP_CASE
+    }
   }
   return hip_fail(hipGetLastError(), "plan_calibrated launch");
 }
