@@ -664,3 +664,75 @@ done:
   free(choice);
   return rc;
 }
+
+/* One calibrated plan per GQA group (readings R17 and R21 together): the
+ * group's weight of channel c is S_c * delta_c^2, S_c = the fp64 sum in head
+ * order of the squares q_hc^2 (each exact in fp64, and so is their sum), the
+ * cost of depth t is fl64(fl64(S_c * delta_c^2) * E_c(t)), and the same DP
+ * spends budget[g] (one per kv head); every head of the group gets the row.
+ * A group of one head gives exactly orc_plan_calibrated.
+ * budget [hkv]; plan out [hq][d].                                           */
+int orc_plan_calibrated_group(const float *q, int hq, int hkv, int d, const float *lo,
+                              const float *hi, const uint32_t *hist, const int32_t *budget,
+                              uint8_t *plan) {
+  if (!q || !lo || !hi || !hist || !budget || !plan || hq < 1 || hkv < 1 || hq % hkv || d < 1)
+    return ORC_BAD;
+  const int G = hq / hkv;
+  double *E = (double *)malloc(sizeof(double) * 5 * d * hkv);
+  double *cost = (double *)malloc(sizeof(double) * 5 * d);
+  double *F = (double *)malloc(sizeof(double) * (4 * d + 1));
+  double *Fn = (double *)malloc(sizeof(double) * (4 * d + 1));
+  uint8_t *choice = (uint8_t *)malloc((size_t)d * (4 * d + 1));
+  int rc = ORC_OK;
+  if (!E || !cost || !F || !Fn || !choice || orc_depth_errors(hist, hkv, d, E) != ORC_OK) {
+    rc = ORC_BAD;
+    goto done;
+  }
+  for (int g = 0; g < hkv; ++g) {
+    const int B = budget[g];
+    if (B < 0 || B > 4 * d) {
+      rc = ORC_BAD;
+      goto done;
+    }
+    for (int c = 0; c < d; ++c) {
+      const float delta = (hi[g * d + c] - lo[g * d + c]) * 0.0625f;
+      double S = 0.0;
+      for (int j = 0; j < G; ++j) {
+        const double qc = (double)q[(int64_t)(g * G + j) * d + c];
+        S = S + qc * qc;
+      }
+      const double wd = S * ((double)delta * (double)delta);
+      for (int t = 0; t <= 4; ++t) cost[c * 5 + t] = wd * E[((int64_t)g * d + c) * 5 + t];
+    }
+    for (int b = 0; b <= B; ++b) F[b] = b == 0 ? 0.0 : INFINITY;
+    for (int c = 0; c < d; ++c) {
+      for (int b = 0; b <= B; ++b) {
+        double best = INFINITY;
+        int bt = 0;
+        for (int t = 0; t <= 4 && t <= b; ++t) {
+          const double v = F[b - t] + cost[c * 5 + t];
+          if (v < best) {
+            best = v;
+            bt = t;
+          }
+        }
+        Fn[b] = best;
+        choice[(int64_t)c * (4 * d + 1) + b] = (uint8_t)bt;
+      }
+      for (int b = 0; b <= B; ++b) F[b] = Fn[b];
+    }
+    int b = B;
+    for (int c = d - 1; c >= 0; --c) {
+      const int t = choice[(int64_t)c * (4 * d + 1) + b];
+      for (int j = 0; j < G; ++j) plan[(int64_t)(g * G + j) * d + c] = (uint8_t)t;
+      b -= t;
+    }
+  }
+done:
+  free(E);
+  free(cost);
+  free(F);
+  free(Fn);
+  free(choice);
+  return rc;
+}

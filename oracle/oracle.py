@@ -57,11 +57,12 @@ def _load():
         lib.orc_code_hist.argtypes = [P, L, I, I, L, P]
         lib.orc_depth_errors.argtypes = [P, I, I, P]
         lib.orc_plan_calibrated.argtypes = [P, I, I, I, P, P, P, P, P]
+        lib.orc_plan_calibrated_group.argtypes = [P, I, I, I, P, P, P, P, P]
         lib.orc_sparse_attention.argtypes = [P, I, I, I, P, P, L, L, L, P, I, I, F, P, P]
         for f in ("orc_pack", "orc_plan", "orc_plan_fixed", "orc_plan_rd", "orc_plan_group",
                   "orc_scan", "orc_scan_at",
                   "orc_read_prefixes", "orc_topk", "orc_sparse_attention", "orc_append", "orc_code_hist", "orc_depth_errors",
-                  "orc_plan_calibrated"):
+                  "orc_plan_calibrated", "orc_plan_calibrated_group"):
             getattr(lib, f).restype = I
         _lib = lib
     return _lib
@@ -271,4 +272,20 @@ def plan_calibrated(q, lo, hi, hist, budget) -> np.ndarray:
     out = np.empty((hq, d), np.uint8)
     _check(_load().orc_plan_calibrated(_ptr(q), hq, hkv, d, _ptr(lo), _ptr(hi), _ptr(hist),
                                        _ptr(b), _ptr(out)), "plan_calibrated")
+    return out
+
+
+def plan_calibrated_group(q, lo, hi, hist, budget) -> np.ndarray:
+    """One calibrated plan per GQA group; budget int or [hkv] -> plan [hq][d]."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    lo = np.ascontiguousarray(lo, dtype=np.float32)
+    hi = np.ascontiguousarray(hi, dtype=np.float32)
+    hist = np.ascontiguousarray(hist, dtype=np.uint32)
+    hq, d = q.shape
+    hkv = lo.shape[0]
+    b = np.ascontiguousarray(np.broadcast_to(np.asarray(budget, np.int32), (hkv,)))
+    out = np.empty((hq, d), np.uint8)
+    _check(_load().orc_plan_calibrated_group(_ptr(q), hq, hkv, d, _ptr(lo), _ptr(hi),
+                                             _ptr(hist), _ptr(b), _ptr(out)),
+           "plan_calibrated_group")
     return out

@@ -987,3 +987,75 @@ def test_plan_calibrated_spends_the_budget(orc, B):
     assert np.all(plan.sum(1) == B) and np.all(plan <= 4)
     with pytest.raises(ValueError):
         orc.plan_calibrated(q, p["lo"], p["hi"], hist, 513)
+
+
+def calib_inputs(seed, hq, hkv, d, n=3000):
+    rng = np.random.default_rng(seed)
+    keys = (rng.standard_normal((n, hkv, d)) * rng.uniform(0.2, 3, (1, hkv, d))).astype(np.float16)
+    p = orc_pack_cached(keys)
+    q = rng.standard_normal((hq, d)).astype(np.float32)
+    return q, p
+
+
+def orc_pack_cached(keys):
+    from oracle import oracle
+    p = oracle.pack(keys)
+    p["hist"] = oracle.code_hist(p["planes"], keys.shape[0])
+    return p
+
+
+def test_plan_calibrated_group_of_one_head_is_the_per_head_plan(orc):
+    q, p = calib_inputs(60, 6, 6, 128)
+    for B in (0, 7, 92, 136, 512):
+        np.testing.assert_array_equal(
+            orc.plan_calibrated_group(q, p["lo"], p["hi"], p["hist"], B),
+            orc.plan_calibrated(q, p["lo"], p["hi"], p["hist"], B))
+
+
+@pytest.mark.parametrize("G", [2, 4])
+def test_plan_calibrated_group_of_identical_heads_is_their_plan(orc, G):
+    """G equal heads: the summed square is exactly G times each (a power of
+    two), so every cost scales exactly and the plan is the single head's."""
+    q1, p = calib_inputs(61 + G, 2, 2, 128)
+    q = np.repeat(q1, G, axis=0)
+    for B in (1, 92, 176):
+        grp = orc.plan_calibrated_group(q, p["lo"], p["hi"], p["hist"], B)
+        one = orc.plan_calibrated(q1, p["lo"], p["hi"], p["hist"], B)
+        np.testing.assert_array_equal(grp, np.repeat(one, G, axis=0))
+
+
+@pytest.mark.parametrize("d", [3, 4, 5])
+def test_plan_calibrated_group_is_the_brute_force_minimum(orc, d):
+    rng = np.random.default_rng(600 + d)
+    plans = np.array(list(itertools.product(range(5), repeat=d)))
+    G = 3
+    for trial in range(3):
+        q = rng.standard_normal((G, d)).astype(np.float32)
+        lo = rng.uniform(-3, -1, (1, d)).astype(np.float32)
+        hi = rng.uniform(1, 3, (1, d)).astype(np.float32)
+        hist = rng.integers(0, 200, (1, d, 16)).astype(np.uint32)
+        E = orc.depth_errors(hist)[0]
+        delta = ((hi - lo) * np.float32(0.0625)).astype(np.float32)[0].astype(np.float64)
+        S = (q.astype(np.float64) ** 2).sum(0)
+        cost = (S * delta ** 2)[:, None] * E
+        for B in range(0, 4 * d + 1):
+            feas = plans[plans.sum(1) == B]
+            tot = np.zeros(len(feas))
+            for c in range(d):
+                tot = tot + cost[c, feas[:, c]]
+            best = feas[tot == tot.min()]
+            assert len(best) == 1
+            got = orc.plan_calibrated_group(q, lo, hi, hist, B)
+            for h in range(G):
+                np.testing.assert_array_equal(got[h], best[0])
+
+
+def test_plan_calibrated_group_spends_each_group_budget(orc):
+    q, p = calib_inputs(62, 12, 3, 128)
+    budgets = np.array([0, 92, 512], np.int32)
+    plan = orc.plan_calibrated_group(q, p["lo"], p["hi"], p["hist"], budgets).astype(np.int64)
+    for g in range(3):
+        rows = plan[g * 4:(g + 1) * 4]
+        assert np.all(rows == rows[0]) and rows[0].sum() == budgets[g]
+    with pytest.raises(ValueError):
+        orc.plan_calibrated_group(q, p["lo"], p["hi"], p["hist"], [1, 2, 513])
