@@ -179,6 +179,15 @@ int32_t fathom_plan_calibrated(const float *q, int32_t hq, int32_t hkv, int32_t 
                                const float *lo, const float *hi,
                                const uint32_t *hist, const int32_t *budget_bits,
                                uint8_t *plan, void *stream);
+/* The same allocation once per GQA group (as fathom_plan_group does for the
+ * walk): the group's weight of channel c is delta_c^2 times the fp64 sum, in
+ * head order, of q_hc^2 over its heads; budget_bits is HOST int32[hkv]; every
+ * head of the group receives the row.  With one head per group it equals
+ * fathom_plan_calibrated.                                                   */
+int32_t fathom_plan_calibrated_group(const float *q, int32_t hq, int32_t hkv, int32_t d,
+                                     const float *lo, const float *hi,
+                                     const uint32_t *hist, const int32_t *budget_bits,
+                                     uint8_t *plan, void *stream);
 
 /* Fixed-width baseline plan (the pages' 136-bit scans read r = 32 channels
  * in full): the r channels with the largest |q_c| (ties: lower channel) get

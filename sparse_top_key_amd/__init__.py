@@ -68,6 +68,7 @@ def lib():
             "fathom_plan_group": (I32, [P, I32, I32, I32, P, P, P, P]),
             "fathom_code_hist": (I32, [P, I64, I32, I32, I64, P, P]),
             "fathom_plan_calibrated": (I32, [P, I32, I32, I32, P, P, P, P, P, P]),
+            "fathom_plan_calibrated_group": (I32, [P, I32, I32, I32, P, P, P, P, P, P]),
             "fathom_attention_workspace_bytes": (I64, [I32, I32]),
             "fathom_append": (I32, [P, I32, I64, I32, I32, I64, I64, I64, P, I64, P, P, P, P]),
             "fathom_sparse_attention": (I32, [P, I32, I32, I32, P, P, I32, I64, I64, I64, P,
@@ -227,6 +228,23 @@ def plan_calibrated(q: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor, hist: t
     _check(lib().fathom_plan_calibrated(_p(q.contiguous()), hq, hkv, d, _p(lo.contiguous()),
                                         _p(hi.contiguous()), _p(hist.contiguous()), b, _p(out),
                                         _stream(q.device)), "fathom_plan_calibrated")
+    return out
+
+
+def plan_calibrated_group(q: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor,
+                          hist: torch.Tensor, budget, out=None) -> torch.Tensor:
+    """One calibrated plan per GQA group; budget int or sequence of hkv ints."""
+    _require_gpu(q, lo, hist)
+    hq, d = q.shape
+    hkv = lo.shape[0]
+    b = _budgets(budget, hkv)
+    if out is None:
+        out = torch.empty((hq, d), dtype=torch.uint8, device=q.device)
+    _check(lib().fathom_plan_calibrated_group(_p(q.contiguous()), hq, hkv, d,
+                                              _p(lo.contiguous()), _p(hi.contiguous()),
+                                              _p(hist.contiguous()), b, _p(out),
+                                              _stream(q.device)),
+           "fathom_plan_calibrated_group")
     return out
 
 

@@ -235,7 +235,23 @@ int32_t fathom_plan_calibrated(const float *q, int32_t hq, int32_t hkv, int32_t 
     REQUIRE(budget_bits[h] >= 0 && budget_bits[h] <= 4 * d, FATHOM_ERR_INVALID_ARG,
             "fathom_plan_calibrated: budget_bits[%d] = %d outside [0, %d]", h, budget_bits[h],
             4 * d);
-  return launch_plan_calibrated(q, hq, hkv, lo, hi, hist, budget_bits, plan, as_stream(stream));
+  return launch_plan_calibrated(q, hq, hkv, lo, hi, hist, budget_bits, plan, false,
+                                as_stream(stream));
+}
+
+int32_t fathom_plan_calibrated_group(const float *q, int32_t hq, int32_t hkv, int32_t d,
+                                     const float *lo, const float *hi, const uint32_t *hist,
+                                     const int32_t *budget_bits, uint8_t *plan, void *stream) {
+  REQUIRE(q && lo && hi && hist && budget_bits && plan, FATHOM_ERR_INVALID_ARG,
+          "fathom_plan_calibrated_group: null pointer");
+  if (int32_t rc = check_heads(hq, hkv)) return rc;
+  if (int32_t rc = check_d(d)) return rc;
+  for (int32_t g = 0; g < hkv; ++g)
+    REQUIRE(budget_bits[g] >= 0 && budget_bits[g] <= 4 * d, FATHOM_ERR_INVALID_ARG,
+            "fathom_plan_calibrated_group: budget_bits[%d] = %d outside [0, %d]", g,
+            budget_bits[g], 4 * d);
+  return launch_plan_calibrated(q, hq, hkv, lo, hi, hist, budget_bits, plan, true,
+                                as_stream(stream));
 }
 
 int32_t fathom_plan_fixed(const float *q, int32_t hq, int32_t d, int32_t r, uint8_t *plan,

@@ -92,16 +92,19 @@ __device__ __forceinline__ double lane63(double x) {
 // One 64-lane block per query head h = h0 + blockIdx.x.  J = rounds of 64
 // states per lane, enough for the largest budget of the launch (no branches
 // on the budget inside the channel loop).
+// A plan covers `rows` consecutive query heads from row0 = p * rows (1: per
+// head; the group size: one plan per GQA group, whose weight is the fp64 sum
+// in head order of the heads' squared queries, exactly q * q for one head).
 template <int J>
 __global__ __launch_bounds__(kDpThreads) void plan_calibrated_kernel(
-    const float *__restrict__ q, int32_t group, int32_t h0, const float *__restrict__ lo,
-    const float *__restrict__ hi, const uint32_t *__restrict__ hist, DpBudgets budgets,
-    uint8_t *__restrict__ plan) {
+    const float *__restrict__ q, int32_t group, int32_t rows, int32_t p0,
+    const float *__restrict__ lo, const float *__restrict__ hi,
+    const uint32_t *__restrict__ hist, DpBudgets budgets, uint8_t *__restrict__ plan) {
   __shared__ double s_cost[kD][kPlanes + 1];
   __shared__ uint8_t s_choice[kD][kMaxBudget + 1];
   __shared__ uint8_t s_plan[kD];
-  const int h = h0 + blockIdx.x;
-  const int g = h / group;
+  const int row0 = (p0 + blockIdx.x) * rows;
+  const int g = row0 / group;
   const int lane = threadIdx.x;
   const int B = budgets.b[blockIdx.x];
   // ---- per-channel costs: lane takes channels lane and lane + 64
@@ -109,8 +112,12 @@ __global__ __launch_bounds__(kDpThreads) void plan_calibrated_kernel(
   for (int k = 0; k < 2; ++k) {
     const int c = lane + 64 * k;
     const float delta = __fmul_rn(__fsub_rn(hi[g * kD + c], lo[g * kD + c]), 0.0625f);
-    const double qc = (double)q[(int64_t)h * kD + c];
-    const double qd = __dmul_rn(__dmul_rn(qc, qc), __dmul_rn((double)delta, (double)delta));
+    double sq = 0.0;
+    for (int r = 0; r < rows; ++r) {
+      const double qc = (double)q[(int64_t)(row0 + r) * kD + c];
+      sq = __dadd_rn(sq, __dmul_rn(qc, qc));
+    }
+    const double qd = __dmul_rn(sq, __dmul_rn((double)delta, (double)delta));
     const uint32_t *hc = hist + ((int64_t)g * kD + c) * 16;
     uint32_t hv[16];
 #pragma unroll
@@ -190,8 +197,10 @@ __global__ __launch_bounds__(kDpThreads) void plan_calibrated_kernel(
     }
   }
   __syncthreads();
-  plan[(int64_t)h * kD + lane] = s_plan[lane];
-  plan[(int64_t)h * kD + lane + 64] = s_plan[lane + 64];
+  for (int r = 0; r < rows; ++r) {
+    plan[(int64_t)(row0 + r) * kD + lane] = s_plan[lane];
+    plan[(int64_t)(row0 + r) * kD + lane + 64] = s_plan[lane + 64];
+  }
 }
 
 }  // namespace
@@ -205,10 +214,13 @@ int32_t launch_code_hist(const uint32_t *planes, int64_t n, int32_t hkv, int64_t
 
 int32_t launch_plan_calibrated(const float *q, int32_t hq, int32_t hkv, const float *lo,
                                const float *hi, const uint32_t *hist,
-                               const int32_t *budget_host, uint8_t *plan, hipStream_t s) {
+                               const int32_t *budget_host, uint8_t *plan, bool per_group,
+                               hipStream_t s) {
   const int32_t group = hq / hkv;
-  for (int32_t h0 = 0; h0 < hq; h0 += kDpHeadsPerLaunch) {
-    const int32_t cnt = std::min(kDpHeadsPerLaunch, hq - h0);
+  const int32_t rows = per_group ? group : 1;
+  const int32_t nplans = hq / rows;
+  for (int32_t h0 = 0; h0 < nplans; h0 += kDpHeadsPerLaunch) {
+    const int32_t cnt = std::min(kDpHeadsPerLaunch, nplans - h0);
     DpBudgets b{};
     for (int i = 0; i < cnt; ++i) b.b[i] = budget_host[h0 + i];
     int maxb = 0;
@@ -218,8 +230,8 @@ int32_t launch_plan_calibrated(const float *q, int32_t hq, int32_t hkv, const fl
     switch (J) {
 #define FATHOM_DP_CASE(K)                                                                     \
   case K:                                                                                     \
-    hipLaunchKernelGGL(plan_calibrated_kernel<K>, grid, block, 0, s, q, group, h0, lo, hi, hist, \
-                       b, plan);                                                              \
+    hipLaunchKernelGGL(plan_calibrated_kernel<K>, grid, block, 0, s, q, group, rows, h0, lo, hi, \
+                       hist, b, plan);                                                        \
     break;
       FATHOM_DP_CASE(1) FATHOM_DP_CASE(2) FATHOM_DP_CASE(3) FATHOM_DP_CASE(4)
       FATHOM_DP_CASE(5) FATHOM_DP_CASE(6) FATHOM_DP_CASE(7) FATHOM_DP_CASE(8)

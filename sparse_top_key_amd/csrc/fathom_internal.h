@@ -80,7 +80,8 @@ int32_t launch_code_hist(const uint32_t *planes, int64_t n, int32_t hkv, int64_t
                          uint32_t *hist, hipStream_t s);
 int32_t launch_plan_calibrated(const float *q, int32_t hq, int32_t hkv, const float *lo,
                                const float *hi, const uint32_t *hist,
-                               const int32_t *budget_host, uint8_t *plan, hipStream_t s);
+                               const int32_t *budget_host, uint8_t *plan, bool per_group,
+                               hipStream_t s);
 
 // ---- append -------------------------------------------------------------------
 int32_t launch_append(const void *keys, int32_t dtype, int64_t m, int32_t hkv,

@@ -32,7 +32,8 @@ def test_header_declares_the_path():
     names = declared_functions()
     for f in ("fathom_pack", "fathom_plan", "fathom_plan_fixed", "fathom_plan_rd",
               "fathom_plan_group", "fathom_sparse_attention", "fathom_append",
-              "fathom_code_hist", "fathom_plan_calibrated", "fathom_scan",
+              "fathom_code_hist", "fathom_plan_calibrated", "fathom_plan_calibrated_group",
+              "fathom_scan",
               "fathom_topk", "fathom_scan_batched", "fathom_topk_batched",
               "fathom_read_prefixes", "fathom_plan_stats", "fathom_probe_read"):
         assert f in names
@@ -305,3 +306,7 @@ def test_calibrated_validation(L):
     assert "budget_bits[2] = 600" in err(L)
     assert L.fathom_plan_calibrated(A, 4, 3, 128, A, A, A, b, A, None) == 1
     assert L.fathom_plan_calibrated(A, 4, 1, 128, A, A, None, b, A, None) == 1
+    g = (ctypes.c_int32 * 2)(92, 513)            # one budget per kv head
+    assert L.fathom_plan_calibrated_group(A, 4, 2, 128, A, A, A, g, A, None) == 1
+    assert "budget_bits[1] = 513" in err(L)
+    assert L.fathom_plan_calibrated_group(A, 4, 3, 128, A, A, A, g, A, None) == 1

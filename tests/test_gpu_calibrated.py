@@ -109,3 +109,20 @@ def test_scan_topk_with_calibrated_plans(F):
     torch.cuda.synchronize()
     assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])
     assert int(plan.to(torch.int64).sum(1).min()) == 92
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (8, 8), (64, 1), (144, 72)])
+@pytest.mark.parametrize("budget", [0, 3, 92, 176, 512, "random"])
+def test_plan_calibrated_group_bit_exact(F, orc, hq, hkv, budget):
+    print(f"plan_calibrated_group hq={hq} hkv={hkv} budget={budget}", flush=True)
+    keys, q = layer(94 + hq, 8000, hkv, hq)
+    p = F.pack(keys)
+    hist = F.code_hist(p.planes, 8000)
+    rng = np.random.default_rng(hq + hkv)
+    B = (rng.integers(0, 513, hkv).astype(np.int32) if budget == "random"
+         else np.full(hkv, budget, np.int32))
+    plan = F.plan_calibrated_group(q, p.lo, p.hi, hist, B.tolist())
+    torch.cuda.synchronize()
+    ref = orc.plan_calibrated_group(q.cpu().numpy(), p.lo.cpu().numpy(), p.hi.cpu().numpy(),
+                                    u32(hist), B)
+    np.testing.assert_array_equal(plan.cpu().numpy(), ref)
