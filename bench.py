@@ -63,6 +63,7 @@ class Layer:
             self.meta_host.copy_(self.meta)
         self.budget = [w.budget] * w.hq
         self.group_budget = [w.budget] * w.hkv
+        self.group_budget176 = [176] * w.hkv     # about the per-head plans' union bits
         self.hist = fathom.code_hist(p.planes, w.n)     # per-layer statistic, like sigma2
         self.plan = torch.empty((w.hq, w.d), dtype=torch.uint8, device=dev)
         self.plan_fixed = fathom.plan_fixed(self.q, fixed_r)
@@ -110,6 +111,9 @@ def run_steps(layers, w, ws, steps, mode, fixed=False, fused=False, per_call=Tru
             plan = fathom.plan_group(L.q, L.sigma2, L.group_budget, out=L.plan)
         elif variant == "calibrated":
             plan = fathom.plan_calibrated(L.q, L.lo, L.hi, L.hist, L.budget, out=L.plan)
+        elif variant == "group_calibrated":
+            plan = fathom.plan_calibrated_group(L.q, L.lo, L.hi, L.hist, L.group_budget176,
+                                                out=L.plan)
         else:
             plan = fathom.plan(L.q, L.sigma2, L.budget, out=L.plan)
         if per_call:
@@ -364,6 +368,10 @@ def plan_quality(dev, layers_q=2):
              ("fathom_B136", lambda p, q: fathom.plan(q, p.sigma2, 136)),
              ("rd_B136", lambda p, q: fathom.plan_rd(q, p.sigma2, 136)),
              ("group_B176_per_kv_head", lambda p, q: fathom.plan_group(q, p.sigma2, 176)),
+             ("group_calibrated_B176_per_kv_head", lambda p, q: fathom.plan_calibrated_group(
+                 q, p.lo, p.hi, fathom.code_hist(p.planes, p.n), 176)),
+             ("group_calibrated_B92_per_kv_head", lambda p, q: fathom.plan_calibrated_group(
+                 q, p.lo, p.hi, fathom.code_hist(p.planes, p.n), 92)),
              ("fixed136", None),
              ("fixed_r16", 16),
              ("full_4bit_B512", lambda p, q: fathom.plan(q, p.sigma2, 512))]
@@ -696,11 +704,15 @@ def main():
     if not args.no_extra:
         for var, fn, bud in (("rd", fathom.plan_rd, "budget"),
                              ("group", fathom.plan_group, "group_budget"),
-                             ("calibrated", None, "budget")):
-            if fn is None:
+                             ("calibrated", None, "budget"),
+                             ("group_calibrated", None, "group_budget176")):
+            if var == "calibrated":
                 vper = [union_plane_bytes(fathom.plan_calibrated(L.q, L.lo, L.hi, L.hist,
                                                                  L.budget), w.hkv, w.n)
                         for L in layers]
+            elif var == "group_calibrated":
+                vper = [union_plane_bytes(fathom.plan_calibrated_group(
+                    L.q, L.lo, L.hi, L.hist, L.group_budget176), w.hkv, w.n) for L in layers]
             else:
                 vper = [union_plane_bytes(fn(L.q, L.sigma2, getattr(L, bud)), w.hkv, w.n)
                         for L in layers]
@@ -809,8 +821,9 @@ def main():
                     "depth_histogram": hist}
     if variants:
         variants["note"] = ("B=92 per query head (rd, calibrated) or per kv head (group: the "
-                            "whole GQA group reads 92 plane bits per key); fixed_r16: top-16 |q| "
-                            "channels x 4 bits + the 8-bit side stream; fused scan + top-k steps")
+                            "whole GQA group reads 92 plane bits per key; group_calibrated: 176, "
+                            "about the per-head plans' union); fixed_r16: top-16 |q| channels x 4 "
+                            "bits + the 8-bit side stream; fused scan + top-k steps")
         f16 = variants["fixed_r16"]
         fb = plane_b
         variants["fathom_vs_fixed_r16"] = {
