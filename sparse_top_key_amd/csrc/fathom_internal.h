@@ -23,6 +23,9 @@ constexpr int kCntStride = 32;          // candidate counters, one 128-byte line
 constexpr int kMaxSeg = 1024;
 constexpr int kFusedCap = 32768;
 
+// Compute units of the current device (queried once per device).
+int device_cus();
+
 // Thread-local error text behind fathom_last_error().
 void set_error(const char *fmt, ...);
 int32_t hip_fail(hipError_t e, const char *what);

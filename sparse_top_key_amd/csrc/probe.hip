@@ -29,12 +29,7 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const uint4 *__restrict
 
 int32_t launch_probe_read(const void *src, int64_t bytes, uint32_t *out, int32_t blocks,
                           hipStream_t s) {
-  if (blocks == 0) {
-    int dev = 0, ncu = 256;
-    hipGetDevice(&dev);
-    hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    blocks = ncu * 8;
-  }
+  if (blocks == 0) blocks = device_cus() * 8;
   hipLaunchKernelGGL(probe_read_kernel, dim3(blocks), dim3(256), 0, s,
                      static_cast<const uint4 *>(src), bytes / 16, out);
   return hip_fail(hipGetLastError(), "probe launch");
