@@ -138,3 +138,38 @@ def test_full_layer_1m_spot_checks(F, orc, resident):
     sel = idx[0].cpu().numpy()
     sref = orc.scan_at(planes_np[:1], lo[:1], hi[:1], n, qn[:1], pn[:1], sel)[0]
     assert np.all(sref >= vals[0, -1].item() - 2e-5 * A[0])
+
+
+@pytest.mark.parametrize("layer", [0, 17, 35])
+def test_step_36_layers_spot_parity(F, orc, layer):
+    """Spot parity of the 36-layer decode step's own layers (its seeded keys
+    and queries): the plan bit-exact, sampled logits within tolerance, the
+    fused scan + top-k bit-identical to scan then top-k, and two rows' top-k
+    bit-exact against the oracle's sort of the GPU logits."""
+    w = synth.STEP_36L_1M
+    n = w.n
+    print(f"36-layer step, layer {layer}", flush=True)
+    keys = synth.keys(w.seed, layer, n, w.hkv, 128, w.dtype, w.outliers, device=dev())
+    q = synth.queries(w.seed, layer, w.hq, 128, device=dev())
+    p = F.pack(keys)
+    del keys
+    plan = F.plan(q, p.sigma2, w.budget)
+    logits = F.scan(p.planes, p.lo, p.hi, n, q, plan)
+    idx, vals = F.topk(logits, w.k)
+    fidx, fvals = F.scan_topk(p.planes, p.lo, p.hi, n, q, plan, w.k, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(fidx, idx) and torch.equal(fvals, vals)
+    planes_np = p.planes.cpu().numpy().view(np.uint32)
+    lo, hi = p.lo.cpu().numpy(), p.hi.cpu().numpy()
+    qn, pn = q.cpu().numpy(), plan.cpu().numpy()
+    np.testing.assert_array_equal(pn, orc.plan(qn, p.sigma2.cpu().numpy(), w.budget))
+    rng = np.random.default_rng(layer)
+    pick = np.unique(np.concatenate([rng.integers(0, n, 1000), np.arange(n - 20, n)]))
+    ref = orc.scan_at(planes_np, lo, hi, n, qn, pn, pick)
+    A = logit_scale(qn, lo, hi, 4)
+    L = logits.cpu().numpy()
+    assert_logits_close(L[:, pick], ref, A)
+    for r in (layer % 32, 31 - layer % 32):
+        ridx, rvals = orc.topk(L[r:r + 1], w.k)
+        np.testing.assert_array_equal(idx[r:r + 1].cpu().numpy(), ridx)
+        np.testing.assert_array_equal(vals[r:r + 1].cpu().numpy(), rvals)
