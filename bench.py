@@ -166,6 +166,46 @@ def timed(layers, w, ws, steps, warmup, mode, fixed=False, fused=False, variant=
     return r
 
 
+def scan_traffic_probe(layers, w, steps, warmup, dense=False, rows_out=None):
+    """The HBM logits scan's own bytes moved with none of its arithmetic: per
+    layer, the plane rows its union plan reads and all its logits rows, rotating
+    layers like the scan.  dense: the same number of plane rows per kv head, as
+    whole channels (every load instruction full).  rows_out: logits rows written
+    per kv head (default all of its query heads; 0 = reads only, as the fused
+    call's candidate scan).  -> mean ms per launch."""
+    g = w.hq // w.hkv
+    rows_out = g if rows_out is None else rows_out
+    depths = [L.plan.view(w.hkv, g, w.d).amax(1).contiguous() for L in layers]
+    if dense:
+        packed = []
+        for dp in depths:
+            rows = dp.to(torch.int64).sum(1).tolist()
+            t = torch.zeros((w.hkv, w.d), dtype=torch.uint8)
+            for kv, u in enumerate(rows):
+                t[kv, :u // 4] = 4
+                if u % 4:
+                    t[kv, u // 4] = u % 4
+            packed.append(t.to(dp.device))
+        depths = packed
+    sink = torch.zeros(1, dtype=torch.int32, device=layers[0].q.device)
+
+    def launch(i):
+        L = layers[i % len(layers)]
+        fathom.probe_scan_traffic(L.planes, L.n, depths[i % len(layers)], rows_out,
+                                  L.logits if rows_out else None, sink)
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        launch(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
 def probes(dev):
     out = torch.zeros(1, dtype=torch.int32, device=dev)
     res = {}
@@ -689,6 +729,14 @@ def main():
     meta_b = w.hkv * w.n
     logits_b = w.hq * w.n * 4
     log(f"union bits per kv head {ub}, depth histogram {hist}; fixed-136 union {fub}")
+    traffic_probe_ms = dense_probe_ms = reads_probe_ms = None
+    if probe and "hbm" in res_modes(args):
+        traffic_probe_ms = scan_traffic_probe(layers, w, args.steps, args.warmup)
+        dense_probe_ms = scan_traffic_probe(layers, w, args.steps, args.warmup, dense=True)
+        reads_probe_ms = scan_traffic_probe(layers, w, args.steps, args.warmup, rows_out=0)
+        log(f"scan-traffic probe: {traffic_probe_ms * 1e3:.1f} us per launch "
+            f"(as whole channels: {dense_probe_ms * 1e3:.1f} us; "
+            f"plane reads only: {reads_probe_ms * 1e3:.1f} us)")
 
     res = {}
     for mode in res_modes(args):
@@ -795,6 +843,17 @@ def main():
             "kernel": "scan_mfma_kernel<4, 0, false> (planes in HBM, all logits written)",
             "algorithmic_bytes": plane_b + logits_b,
             "end_to_end_plane_GBps": round(plane_b / (h["step_ms"] * 1e-3) / 1e9, 1)}
+        if traffic_probe_ms:
+            # the same bytes moved by fathom_probe_scan_traffic, with no arithmetic
+            pat = (plane_b + logits_b) / (traffic_probe_ms * 1e-3) / 1e9
+            out["roofline_hbm"]["scan_traffic_probe_GBps"] = round(pat, 1)
+            out["roofline_hbm"]["frac_of_scan_traffic_probe"] = round(ach / pat, 4)
+            # the same number of plane rows per kv head read as whole channels
+            out["roofline_hbm"]["scan_traffic_probe_whole_channels_GBps"] = round(
+                (plane_b + logits_b) / (dense_probe_ms * 1e-3) / 1e9, 1)
+            # the plane reads alone (the fused call's candidate scan writes no logits)
+            out["roofline_hbm"]["scan_traffic_probe_reads_only_GBps"] = round(
+                plane_b / (reads_probe_ms * 1e-3) / 1e9, 1)
         if main_mode == "host":
             out["hbm_resident"] = {"keys_per_s": round(keys_per_step / (h["step_ms"] * 1e-3), 1),
                                    **{k: round(v, 4) for k, v in h.items()}}

@@ -386,6 +386,21 @@ int32_t fathom_plan_stats(const uint8_t *plan_host, int32_t hq, int32_t d,
 int32_t fathom_probe_read(const void *src, int64_t bytes, uint32_t *out,
                           int32_t blocks, void *stream);
 
+/* Scan-traffic probe, the measured ceiling for an HBM-resident logits scan's
+ * own access pattern: it moves the bytes that scan moves with none of its
+ * arithmetic.  Device planes [hkv][128][4][n/32] (16-byte aligned), device
+ * depth uint8[hkv][128] (plane slots read per channel, clamped to 0..4; for
+ * a scan, the largest t_hc of the kv head's query heads).  Per 2048-key tile
+ * of each kv head it reads, with 16-byte lanes, the tile's 256 bytes of
+ * every plane row below the channel's depth, and writes rows_out (0..16)
+ * device fp32 rows of the tile: out row g*rows_out + r, row stride ld >= n
+ * (ld % 4 == 0; out 16-byte aligned; unused when rows_out == 0).  The values
+ * written carry no meaning; one checksum word goes to device sink
+ * (uint32[1]).  n > 0 and a multiple of 2048, hkv 1..64.  One kernel.       */
+int32_t fathom_probe_scan_traffic(const uint32_t *planes, int64_t n, int32_t hkv,
+                                  const uint8_t *depth, int32_t rows_out, float *out,
+                                  int64_t ld, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

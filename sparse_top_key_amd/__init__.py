@@ -80,6 +80,7 @@ def lib():
             "fathom_read_prefixes": (I32, [P, I64, I32, I32, P, I32, P, P]),
             "fathom_plan_stats": (I32, [P, I32, I32, I32, P, P]),
             "fathom_probe_read": (I32, [P, I64, P, I32, P]),
+            "fathom_probe_scan_traffic": (I32, [P, I64, I32, P, I32, P, I64, P, P]),
             "fathom_scan_topk_workspace_bytes": (I64, [P, I32, I32, I32, I32, I32]),
             "fathom_scan_topk": (I32, [P, P, P, I64, I32, I32, P, P, I32, P, F, I32, I32, P, P,
                                        P, I64, P]),
@@ -492,3 +493,16 @@ def probe_read(buf: torch.Tensor, out: torch.Tensor, blocks: int = 0):
     """Stream-read `buf` (device or pinned host) once; out = 1-word device tensor."""
     _check(lib().fathom_probe_read(_p(buf), buf.numel() * buf.element_size(), _p(out),
                                    blocks, _stream(out.device)), "fathom_probe_read")
+
+
+def probe_scan_traffic(planes: torch.Tensor, n: int, depth: torch.Tensor, rows_out: int,
+                       out: Optional[torch.Tensor], sink: torch.Tensor):
+    """Move the bytes of an HBM logits scan with no arithmetic: planes [hkv][128][4][n/32]
+    on the GPU, depth uint8 [hkv][128] (plane slots read per channel), out fp32 rows
+    [hkv*rows_out][>= n] (values meaningless), sink a 1-word device tensor."""
+    _require_gpu(planes, depth, sink)
+    hkv = planes.shape[0]
+    ld = out.stride(0) if out is not None else 0
+    _check(lib().fathom_probe_scan_traffic(_p(planes), n, hkv, _p(depth.contiguous()), rows_out,
+                                           _p(out), ld, _p(sink), _stream(sink.device)),
+           "fathom_probe_scan_traffic")

@@ -528,4 +528,23 @@ int32_t fathom_probe_read(const void *src, int64_t bytes, uint32_t *out, int32_t
   return launch_probe_read(src, bytes, out, blocks, as_stream(stream));
 }
 
+int32_t fathom_probe_scan_traffic(const uint32_t *planes, int64_t n, int32_t hkv,
+                                  const uint8_t *depth, int32_t rows_out, float *out,
+                                  int64_t ld, uint32_t *sink, void *stream) {
+  REQUIRE(planes && depth && sink, FATHOM_ERR_INVALID_ARG,
+          "fathom_probe_scan_traffic: null pointer");
+  REQUIRE(n > 0 && n % 2048 == 0 && n <= ((int64_t)1 << 31), FATHOM_ERR_INVALID_ARG,
+          "fathom_probe_scan_traffic: n must be a positive multiple of 2048");
+  REQUIRE(hkv >= 1 && hkv <= 64, FATHOM_ERR_INVALID_ARG, "fathom_probe_scan_traffic: hkv");
+  REQUIRE(rows_out >= 0 && rows_out <= 16, FATHOM_ERR_INVALID_ARG,
+          "fathom_probe_scan_traffic: rows_out must be 0..16");
+  REQUIRE(rows_out == 0 || (out && ld >= n), FATHOM_ERR_INVALID_ARG,
+          "fathom_probe_scan_traffic: out must hold hkv*rows_out rows of ld >= n");
+  REQUIRE((reinterpret_cast<uintptr_t>(planes) & 15) == 0 &&
+              (rows_out == 0 || ((reinterpret_cast<uintptr_t>(out) & 15) == 0 && ld % 4 == 0)),
+          FATHOM_ERR_INVALID_ARG, "fathom_probe_scan_traffic: planes and out rows need 16-byte alignment");
+  return launch_probe_scan_traffic(planes, n, hkv, depth, rows_out, out, ld, sink,
+                                   as_stream(stream));
+}
+
 }  // extern "C"

@@ -180,6 +180,9 @@ int32_t launch_scan_topk(const ScanSession *in, int32_t *const *idx, float *cons
                          void *ws, hipStream_t s);
 
 // ---- probe ------------------------------------------------------------------
+int32_t launch_probe_scan_traffic(const uint32_t *planes, int64_t n, int32_t hkv,
+                                  const uint8_t *depth, int32_t rows_out, float *out,
+                                  int64_t ld, uint32_t *sink, hipStream_t s);
 int32_t launch_probe_read(const void *src, int64_t bytes, uint32_t *out,
                           int32_t blocks, hipStream_t s);
 

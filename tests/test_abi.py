@@ -35,7 +35,8 @@ def test_header_declares_the_path():
               "fathom_code_hist", "fathom_plan_calibrated", "fathom_plan_calibrated_group",
               "fathom_scan",
               "fathom_topk", "fathom_scan_batched", "fathom_topk_batched",
-              "fathom_read_prefixes", "fathom_plan_stats", "fathom_probe_read"):
+              "fathom_read_prefixes", "fathom_plan_stats", "fathom_probe_read",
+              "fathom_probe_scan_traffic"):
         assert f in names
 
 
@@ -197,6 +198,22 @@ def test_probe_validation(L):
     assert L.fathom_probe_read(None, 16, DUMMY, 0, None) == 1
     assert L.fathom_probe_read(DUMMY, 17, DUMMY, 0, None) == 1
     assert L.fathom_probe_read(ctypes.c_void_p(0x1008), 16, DUMMY, 0, None) == 1
+    # scan-traffic probe: every argument is checked before anything is launched
+    st = L.fathom_probe_scan_traffic
+    assert st(None, 4096, 2, DUMMY, 4, DUMMY, 4096, DUMMY, None) == 1
+    assert st(DUMMY, 4096, 2, None, 4, DUMMY, 4096, DUMMY, None) == 1
+    assert st(DUMMY, 4096, 2, DUMMY, 4, DUMMY, 4096, None, None) == 1
+    assert st(DUMMY, 0, 2, DUMMY, 4, DUMMY, 4096, DUMMY, None) == 1
+    assert st(DUMMY, 4095, 2, DUMMY, 4, DUMMY, 4096, DUMMY, None) == 1
+    assert st(DUMMY, 4096, 0, DUMMY, 4, DUMMY, 4096, DUMMY, None) == 1
+    assert st(DUMMY, 4096, 65, DUMMY, 4, DUMMY, 4096, DUMMY, None) == 1
+    assert st(DUMMY, 4096, 2, DUMMY, 17, DUMMY, 4096, DUMMY, None) == 1
+    assert st(DUMMY, 4096, 2, DUMMY, -1, DUMMY, 4096, DUMMY, None) == 1
+    assert st(DUMMY, 4096, 2, DUMMY, 4, None, 4096, DUMMY, None) == 1
+    assert st(DUMMY, 4096, 2, DUMMY, 4, DUMMY, 4095, DUMMY, None) == 1
+    assert st(DUMMY, 4096, 2, DUMMY, 4, DUMMY, 4098, DUMMY, None) == 1
+    assert st(ctypes.c_void_p(0x1008), 4096, 2, DUMMY, 4, DUMMY, 4096, DUMMY, None) == 1
+    assert st(DUMMY, 4096, 2, DUMMY, 4, ctypes.c_void_p(0x1004), 4096, DUMMY, None) == 1
 
 
 @pytest.mark.parametrize("group", [1, 2, 4])
