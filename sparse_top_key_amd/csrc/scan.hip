@@ -760,19 +760,18 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
     }
     // ---- regroup: quarter k ends with word 4*m16 + k of the 4 plane rows of
     // every slot; 32-lane halves first, then 16-lane rows.
-    uint32_t x[32];
+    uint32_t(&x)[32] = xn;  // regrouped and transposed in place
     if (has_group) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const auto h02 = __builtin_amdgcn_permlane32_swap(xn[4 * i + 0], xn[4 * i + 2], false, false);
-        const auto h13 = __builtin_amdgcn_permlane32_swap(xn[4 * i + 1], xn[4 * i + 3], false, false);
+        const auto h02 = __builtin_amdgcn_permlane32_swap(x[4 * i + 0], x[4 * i + 2], false, false);
+        const auto h13 = __builtin_amdgcn_permlane32_swap(x[4 * i + 1], x[4 * i + 3], false, false);
         x[4 * i + 0] = h02[0];
         x[4 * i + 2] = h02[1];
         x[4 * i + 1] = h13[0];
         x[4 * i + 3] = h13[1];
       }
     }
-    if (it + 1 < nitems) issue(it + 1, xn);
     if (has_group) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -791,6 +790,9 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
 #pragma unroll
       for (int t = 0; t < 32; ++t) dst[t] = x[t];
     }
+    // the next item's words load into the same registers once these are in
+    // the code table
+    if (it + 1 < nitems) issue(it + 1, xn);
     } else {
     // ==== M phase
     // ---- MFMA phase: 256 keys of this wave; block b = 4*beta + e covers keys
