@@ -682,8 +682,8 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   const uint32_t plane_sl = 3u - (uint32_t)quarter;
   const uint32_t lane_part = plane_sl * row_bytes + (uint32_t)m16 * 16u;
 
-  // Work items = (tile, pass).  The plane words of item i+1 are loaded while
-  // item i is transposed, multiplied and written out.
+  // Work items = (tile, pass).  The plane words of item i+1 are loaded once
+  // item i is in the code table, while it is multiplied and written out.
   // Visited tile v of this block: all tiles, or (sample mode) nvtiles tiles
   // spread evenly over the ntiles real ones.
   const int nvtiles = S.nvtiles, ntiles_real = S.ntiles;
