@@ -1,5 +1,5 @@
 """The bench's command-line contract that needs no GPU: more than one GPU is
-refused with a message (this build measures one GPU), before any GPU work."""
+refused with a message (the benchmark runs on one GPU), before any GPU work."""
 import os
 import subprocess
 import sys
