@@ -16,7 +16,8 @@
  *    (NULL = the default stream).  Every GPU call only enqueues work on that
  *    stream; nothing synchronises inside the library.
  *  - Ownership: the caller allocates and frees every buffer (inputs, outputs,
- *    workspaces).  The library never allocates, frees or keeps pointers.
+ *    workspaces).  The library never allocates, frees or keeps pointers; the
+ *    one exception is the static device array of fathom_topk_noalloc.
  *  - Device pointers are HBM pointers unless an argument says it may also be
  *    pinned host memory (allocated with hipHostMalloc, e.g. torch's
  *    pin_memory); such memory is read zero-copy over the host link.
@@ -234,6 +235,22 @@ int32_t fathom_scan(const uint32_t *planes, const float *lo, const float *hi,
 int32_t fathom_topk(const float *scores, int32_t rows, int64_t n, int64_t ld,
                     int32_t group, int32_t k, int32_t *idx, float *vals,
                     void *ws, int64_t ws_bytes, void *stream);
+
+/* ---- top-k for callers that cannot allocate -------------------------------
+ * For callers that cannot call hipMalloc or pass a workspace (code under HIP
+ * graph capture, serving loops that forbid allocation): fathom_topk with its
+ * workspace taken from a static device array inside the library, of
+ * FATHOM_NOALLOC_MAX_ROWS output rows (about 4 MiB per GPU, held from the
+ * library's load until the process ends).  Same arguments, ranking, padding
+ * and results as fathom_topk, minus ws / ws_bytes; allocates nothing.
+ * rows / group > FATHOM_NOALLOC_MAX_ROWS -> FATHOM_ERR_WORKSPACE.  Every
+ * call on one GPU uses that GPU's one array (the kernels reset what must
+ * start at zero): calls that overlap on one GPU (two streams, or two host
+ * threads without ordering) race and must be ordered by the caller.        */
+#define FATHOM_NOALLOC_MAX_ROWS 64
+int32_t fathom_topk_noalloc(const float *scores, int32_t rows, int64_t n, int64_t ld,
+                            int32_t group, int32_t k, int32_t *idx, float *vals,
+                            void *stream);
 
 /* ---- many sessions in one launch ----------------------------------------
  * Ragged multi-session decode: every session has its own K cache (planes,

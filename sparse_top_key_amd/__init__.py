@@ -75,6 +75,7 @@ def lib():
                                               I32, I32, F, P, P, P, I64, P]),
             "fathom_scan": (I32, [P, P, P, I64, I32, I32, P, P, I32, P, F, P, I64, P]),
             "fathom_topk": (I32, [P, I32, I64, I64, I32, I32, P, P, P, I64, P]),
+            "fathom_topk_noalloc": (I32, [P, I32, I64, I64, I32, I32, P, P, P]),
             "fathom_scan_batched": (I32, [P, I32, I32, I32, I32, P]),
             "fathom_topk_batched": (I32, [P, I32, I32, I32, I32, P, I64, P]),
             "fathom_read_prefixes": (I32, [P, I64, I32, I32, P, I32, P, P]),

@@ -371,6 +371,30 @@ int32_t fathom_topk(const float *scores, int32_t rows, int64_t n, int64_t ld, in
   return launch_topk(&t, 1, rows / group, group, k, w, as_stream(stream));
 }
 
+int32_t fathom_topk_noalloc(const float *scores, int32_t rows, int64_t n, int64_t ld,
+                            int32_t group, int32_t k, int32_t *idx, float *vals,
+                            void *stream) {
+  if (int32_t rc = check_topk_common(rows, group, k, "fathom_topk_noalloc")) return rc;
+  REQUIRE(idx && vals, FATHOM_ERR_INVALID_ARG, "fathom_topk_noalloc: null output");
+  REQUIRE(n >= 0 && n < ((int64_t)1 << 31), FATHOM_ERR_INVALID_ARG,
+          "fathom_topk_noalloc: n must be in [0, 2^31)");
+  REQUIRE(n == 0 || scores, FATHOM_ERR_INVALID_ARG, "fathom_topk_noalloc: null scores");
+  REQUIRE(ld >= n, FATHOM_ERR_INVALID_ARG, "fathom_topk_noalloc: ld < n");
+  const int32_t out_rows = rows / group;
+  REQUIRE(out_rows <= FATHOM_NOALLOC_MAX_ROWS, FATHOM_ERR_WORKSPACE,
+          "fathom_topk_noalloc: %d output rows exceed the static scratch's %d",
+          out_rows, FATHOM_NOALLOC_MAX_ROWS);
+  const int64_t need = topk_workspace_bytes(out_rows);
+  REQUIRE(need <= noalloc_scratch_bytes(), FATHOM_ERR_WORKSPACE,
+          "fathom_topk_noalloc: %lld bytes of scratch needed, %lld held", (long long)need,
+          (long long)noalloc_scratch_bytes());
+  void *ws = nullptr;
+  if (int32_t rc = noalloc_scratch(&ws)) return rc;
+  TopkSession t{scores, n, ld, idx, vals, n};
+  const TopkWs w = topk_ws_carve(ws, out_rows, out_rows);
+  return launch_topk(&t, 1, out_rows, group, k, w, as_stream(stream));
+}
+
 int32_t fathom_topk_batched(const fathom_session *sessions, int32_t n_sessions, int32_t hq,
                             int32_t group, int32_t k, void *ws, int64_t ws_bytes,
                             void *stream) {

@@ -172,6 +172,12 @@ int32_t launch_topk(const TopkSession *sess, int32_t n_sess, int32_t rows_per_se
                     int32_t group, int32_t k, const TopkWs &w, hipStream_t s,
                     int32_t stage = kTopkAll, int32_t rows_per_kv = 1, int32_t hkv = 1);
 
+// ---- no-allocation scratch (noalloc.hip) ------------------------------------
+// Device address of the current device's static scratch array (looked up once
+// per device) and its size in bytes.
+int32_t noalloc_scratch(void **ptr);
+int64_t noalloc_scratch_bytes();
+
 // ---- scan + top-k -----------------------------------------------------------
 int64_t scan_topk_ws_bytes(const int64_t *n, int32_t n_sess, int32_t hkv, int32_t hq,
                            int32_t group);

@@ -36,7 +36,7 @@ def test_header_declares_the_path():
               "fathom_scan",
               "fathom_topk", "fathom_scan_batched", "fathom_topk_batched",
               "fathom_read_prefixes", "fathom_plan_stats", "fathom_probe_read",
-              "fathom_probe_scan_traffic"):
+              "fathom_probe_scan_traffic", "fathom_topk_noalloc"):
         assert f in names
 
 
@@ -153,6 +153,27 @@ def test_topk_validation(L):
     a = list(base)
     a[6] = None
     assert L.fathom_topk(*a) == 1
+
+
+def test_topk_noalloc_validation(L):
+    # every rejection happens on the host, before the scratch array is looked up
+    base = [DUMMY, 32, 1000, 1000, 1, 64, DUMMY, DUMMY, None]
+    a = list(base)
+    a[5] = 2049
+    assert L.fathom_topk_noalloc(*a) == 1
+    a = list(base)
+    a[4] = 3
+    assert L.fathom_topk_noalloc(*a) == 1
+    a = list(base)
+    a[3] = 999
+    assert L.fathom_topk_noalloc(*a) == 1
+    a = list(base)
+    a[6] = None
+    assert L.fathom_topk_noalloc(*a) == 1
+    a = list(base)
+    a[1] = 65                                     # 65 output rows > 64 held
+    assert L.fathom_topk_noalloc(*a) == 4
+    assert "exceed" in err(L)
 
 
 def test_batched_validation(L):
