@@ -30,6 +30,8 @@
 //    while the current ones are computed.  The per-key sum has one fp32 term
 //    per channel read, so its rounding error is bounded by
 //    (terms + 1) * 2^-24 * sum|terms|, well inside 1e-5 * A_h.
+#include <climits>
+
 #include "fathom_internal.h"
 
 namespace fathom {
@@ -498,21 +500,25 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
 // 2^(E_h-30) times them to the key's running value, which starts at C_h (one
 // rounding per pass).
 //
-// One 1024-thread block per CU (one round of resident blocks); its two halves
-// of 8 waves each take one 2048-key tile (64 plane words per row) of an item,
-// with a code table of their own, and run one step apart (a step lies
-// between two barriers): while one half transposes an item, the other runs
-// the matrix cores over its previous one.  In a pass, wave w of a half reads
-// slot group w (8 slots x 4 planes = 32 rows) with 16-byte
-// loads: a quarter of the wave (16 lanes) covers one row, 4 words per lane,
-// and one load instruction covers the 4 planes of one slot.  Two lane swaps
-// (32-lane halves, then 16-lane rows) regroup the words so that every lane
-// holds one plane word (32 keys) of all 32 rows, which it bit-transposes into
-// 32 per-key nibble words in LDS.  Then each wave runs the MFMAs for 256 keys
-// (16 blocks of 16 keys); its lanes end with 4 consecutive keys of one head,
-// written as one 16-byte store.  Wide loads matter: with 4-byte lanes the
-// memory pipeline, not HBM, limits the read rate at this occupancy.
-constexpr int kMThreads = 1024;                      // two halves of 8 waves
+// One 1024-thread block per CU (one round of resident blocks) over 2048-key
+// tiles; an item is one pass (64 slots) of one tile.  Its 16 waves split into
+// 8 producers and 8 consumers that pass items through two code buffers in LDS,
+// with counters instead of block barriers (a block barrier made the waves that
+// finished first wait for the slowest every step).
+//  * Producers: a task is one slot group (8 slots x 4 planes = 32 rows) of one
+//    tile, read with 16-byte loads: a quarter of the wave (16 lanes) covers one
+//    row, 4 words per lane, and one load instruction covers the 4 planes of
+//    one slot.  Tasks go round-robin to the 8 producer waves, each keeping two
+//    in flight.  Two lane swaps (32-lane halves, then 16-lane rows) regroup the
+//    words so that every lane holds one plane word (32 keys) of all 32 rows,
+//    which it bit-transposes into 32 per-key nibble words in the item's buffer.
+//  * Consumers: wave v runs the MFMAs for keys 256v .. 256v+255 of the item (16
+//    blocks of 16 keys x 64 slots); its lanes end with 4 consecutive keys of
+//    one head, written as one 16-byte store (or tested against the row's
+//    threshold).  Consumers win issue arbitration: their phases set the pace.
+// Wide loads matter: with 4-byte lanes the memory pipeline, not HBM, limits
+// the read rate at this occupancy.
+constexpr int kMThreads = 1024;                      // 8 producer + 8 consumer waves
 constexpr int kMTileKeys = 2048;
 constexpr int kPassGroups = 8;                        // 8 groups x 8 slots = K 64
 constexpr int kMaxPasses = kMaxGroups / kPassGroups;  // 8
@@ -538,6 +544,55 @@ __device__ __forceinline__ float key_threshold(uint32_t T) {
   const float t = from_key(T);
   if (t != t) return T >= 0x80000000u ? INFINITY : -INFINITY;  // NaN patterns
   return t;
+}
+
+// ---- code-buffer ring between the waves of one block -------------------------
+// Counters in LDS that only grow.  A wave signals once its own LDS accesses
+// to the buffer are complete (lgkmcnt 0, then one LDS add by lane 0); a wave
+// that waits spins, sleeping between reads, until the count reaches the
+// target.  Every wave of the block takes part in every round, so the targets
+// are always reached; the spin is capped all the same (~10^8 cycles), so no
+// wave can wait forever.
+constexpr uint32_t kRingSpinCap = 1u << 21;
+#ifndef FATHOM_RING_SLEEP
+#define FATHOM_RING_SLEEP 1
+#endif
+
+__device__ __forceinline__ void ring_wait(uint32_t *ctr, uint32_t target) {
+  for (uint32_t spin = 0; spin < kRingSpinCap; ++spin) {
+    const uint32_t v = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+    if (v >= target) break;
+    __builtin_amdgcn_s_sleep(FATHOM_RING_SLEEP);
+  }
+  asm volatile("" ::: "memory");  // buffer accesses stay after the wait
+}
+
+__device__ __forceinline__ void ring_signal(uint32_t *ctr) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if ((threadIdx.x & 63) == 0)
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Lower bound on the high limb pair hi = a2 + 256*a3 of every key whose
+// one-pass score s = fl(fl(fl(hi)*65536 + fl(lo))*scale + C) reaches tf
+// (scale > 0, |hi|, |lo| < 2^26: each limb sum is below 64*128*15 < 2^17).
+// s >= tf gives t*scale + C >= tf*(1 - 2^-23) - 2^-149 for t = fl(hi*65536 +
+// lo), hence hi*65536 + lo >= (tf - C)/scale minus relative rounding terms
+// of 2^-23 and the |lo| bound; all margins below are taken with room (2^-20
+// relative, 2^27 absolute), and the result rounds down.  A key with hi below
+// the bound cannot be a candidate.
+__device__ __forceinline__ int hi_bound(float tf, float C, float scale) {
+  if (tf == -INFINITY) return INT_MIN;
+  if (tf == INFINITY) return INT_MAX;
+  const double tfd = tf, Cd = C, sc = scale;
+  const double rel = 9.5367431640625e-07;  // 2^-20
+  double x = (tfd - Cd - rel * (fabs(tfd) + fabs(Cd))) / sc;
+  x -= rel * fabs(x) + 134217728.0;        // + 2^27 for lo and the roundings
+  const double h = floor(x / 65536.0) - 1.0;
+  if (h <= (double)INT_MIN) return INT_MIN;
+  if (h >= (double)INT_MAX) return INT_MAX;
+  return (int)h;
 }
 
 // Set-up-only state of the matrix-core kernel, overlaid on its code table.
@@ -566,7 +621,7 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   if (MODE == kScanLogits && S.redo && S.redo[g] == 0) return;  // kv head not flagged
   const int64_t n = S.n;
   const int64_t W = S.W;
-  __shared__ __align__(16) uint32_t s_codes[2][kPassGroups * kGroupPitch + 4];  // per half
+  __shared__ __align__(16) uint32_t s_codes[2][kPassGroups * kGroupPitch + 4];  // the ring's buffers
   static_assert(sizeof(MfmaSetup<GH>) <= sizeof(s_codes[0]), "set-up overlay");
   __shared__ __align__(16) int32_t s_limbs[kMaxPasses][64][4];
   __shared__ __align__(16) int16_t s_desc[kMaxSlots];
@@ -574,7 +629,12 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   __shared__ int s_exp[kMaxGH];
   __shared__ uint32_t s_segc[kMaxGH];  // candidates this block found per row
   __shared__ float s_tf[kMaxGH];       // float thresholds of the block's rows
+  __shared__ int s_ht[kMaxGH];         // integer pre-check bounds (see hi_bound)
   __shared__ int s_nslots;
+  // code-buffer ring: [0..1] groups stored in buffer 0/1 (one count per
+  // producer task), [2..3] releases (one per consumer wave and item); counts
+  // only grow during a launch
+  __shared__ uint32_t s_ring[4];
   const int tid = threadIdx.x;
   SlotRecord *rec = S.table ? reinterpret_cast<SlotRecord *>(S.table) + bw.rec : nullptr;
   if (S.table_mode == kTableRead) {
@@ -630,10 +690,14 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
       limb_bytes[idx] = (uint8_t)(int8_t)v;
     }
   }
+  if (tid < 4) s_ring[tid] = 0u;
   if (tid < GH) {
     s_segc[tid] = 0;
     // thresholds are read here, before any plane load is in flight
-    if constexpr (MODE == kScanCand) s_tf[tid] = key_threshold(S.thr[head_base + tid]);
+    if constexpr (MODE == kScanCand) {
+      s_tf[tid] = key_threshold(S.thr[head_base + tid]);
+      s_ht[tid] = hi_bound(s_tf[tid], s_C[tid], s_scale[tid]);
+    }
     if constexpr (MODE == kScanCandGroup) s_tf[tid] = key_threshold(S.thr[g]);
   }
   __syncthreads();  // the code table is free from here on
@@ -656,9 +720,10 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
           reinterpret_cast<const int4 *>(&s_limbs[0][0][0])[e];
   }
 
-  // half = which of the block's two tiles of an item; wave = wave in the half
-  const int half = tid >> 9, wave = (tid >> 6) & 7, lane = tid & 63;
-  uint32_t *codes = s_codes[half];
+  // role 0: producer waves (load, regroup, transpose into a code buffer);
+  // role 1: consumer waves (matrix cores over the buffer, epilogue).  wave =
+  // index within the role.
+  const int role = tid >> 9, wave = (tid >> 6) & 7, lane = tid & 63;
   const int quarter = lane >> 4, m16 = lane & 15;
   const int hh = lane >> 4;  // head of this lane's results (MFMA row block)
   const float Ch = hh < GH ? s_C[hh] : 0.0f;
@@ -682,41 +747,16 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   const uint32_t plane_sl = 3u - (uint32_t)quarter;
   const uint32_t lane_part = plane_sl * row_bytes + (uint32_t)m16 * 16u;
 
-  // Work items = (tile, pass).  The plane words of item i+1 are loaded once
-  // item i is in the code table, while it is multiplied and written out.
-  // Visited tile v of this block: all tiles, or (sample mode) nvtiles tiles
-  // spread evenly over the ntiles real ones.
+  // Work items = (tile, pass) of this block's tiles in order; item i goes
+  // through code buffer i % 2.  Visited tile v of this block: all tiles, or
+  // (sample mode) nvtiles tiles spread evenly over the ntiles real ones.
   const int nvtiles = S.nvtiles, ntiles_real = S.ntiles;
   auto real_tile = [&](int v) -> int {
     return MODE == kScanSample ? (int)((int64_t)v * ntiles_real / nvtiles) : v;
   };
   int ntiles = 0;
   while (ntiles < tiles_per_block && bw.tile0 + ntiles * bw.tile_step < nvtiles) ++ntiles;
-  // item i = (tile pair i / npasses, pass): half h takes tile 2 * pair + h
-  const int nitems = (ntiles + 1) / 2 * npasses;
-  auto issue = [&](int item, uint32_t(&x)[32]) {
-    const int ti = item / npasses, p = item - ti * npasses;
-    const int tt = 2 * ti + half;
-    if (tt >= ntiles) return;    // odd tile count: no tile for this half
-    const int grp = kPassGroups * p + wave;
-    if (grp >= ngroups) return;  // empty group: nothing to read
-    const uint32_t tile_off =
-        (uint32_t)real_tile(bw.tile0 + tt * bw.tile_step) * (kMTileKeys / 8);
-    const uint4 dv = *reinterpret_cast<const uint4 *>(&s_desc[grp * 8]);
-    const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t desc = __builtin_amdgcn_readfirstlane((dw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-      const uint32_t c = (desc >> 3) & (kD - 1), dep = desc & 7u, top = desc >> 10;
-      const uint32_t voff =
-          plane_sl < dep && plane_sl >= top ? c * chan_bytes + tile_off + lane_part : kUnread;
-      const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int32_t)voff, 0, 0);
-      x[4 * i + 0] = (uint32_t)v[0];
-      x[4 * i + 1] = (uint32_t)v[1];
-      x[4 * i + 2] = (uint32_t)v[2];
-      x[4 * i + 3] = (uint32_t)v[3];
-    }
-  };
+  const int nitems = ntiles * npasses;
 
   // float threshold of this lane's output row (candidate modes)
   const float row_tf = (MODE == kScanCand || MODE == kScanCandGroup) && hh < GH ? s_tf[hh] : 0.0f;
@@ -724,44 +764,50 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   const bool meta_words =
       META && meta && ((reinterpret_cast<uintptr_t>(S.meta) & 3) == 0) && (n & 3) == 0;
 
-  uint32_t xn[32];
+  if (role == 0) {
+    // ==== producers.  A task is one slot group of one tile: 32 plane rows
+    // (8 slots x 4 planes) read with 16-byte loads, regrouped, transposed and
+    // stored in the code buffer of its item (tile, pass = group / 8).  The
+    // ntiles * ngroups tasks go round-robin to the 8 producer waves, so that
+    // all of them keep loads in flight whatever the group count; each wave
+    // has two tasks in flight.
+    const int ntasks = ntiles * ngroups;
+    // Every call issues its 8 loads, also for a task past the last (their
+    // offsets lie past the buffer: they read 0 and touch no memory), so that
+    // the loads of the two tasks in flight always complete in issue order
+    // and the wait for the older one leaves the newer one in flight.
+    auto issue = [&](int k, uint32_t(&x)[32]) {
+      const bool live = k < ntasks;  // wave-uniform
+      const int ti = live ? k / ngroups : 0;
+      const int grp = live ? k - ti * ngroups : 0;
+      const uint32_t tile_off =
+          live ? (uint32_t)real_tile(bw.tile0 + ti * bw.tile_step) * (kMTileKeys / 8) : 0u;
+      const uint4 dv = *reinterpret_cast<const uint4 *>(&s_desc[grp * 8]);
+      const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
-  for (int r = 0; r < 32; ++r) xn[r] = 0;
-  if (nitems > 0) issue(0, xn);
-  // Ping-pong: the item sequence of half 1 runs one step behind half 0, and
-  // a step (between two barriers) is either the T phase of an item (regroup,
-  // next item's loads, transpose into the half's code table) or its M phase
-  // (matrix cores over the code table, then the epilogue).  While one half
-  // transposes, the other multiplies.
-  float s[16];
-  uint32_t mw[4] = {0u, 0u, 0u, 0u};  // side-stream bytes, T phase -> M phase
-  const int nsteps = nitems > 0 ? 2 * nitems + 1 : 0;
-  for (int k = 0; k < nsteps; ++k) {
-    const int q = k - half;
-    if (q >= 0 && q < 2 * nitems) {
-    const int it = q >> 1;
-    const int ti = it / npasses, p = it - ti * npasses;
-    const int tt = 2 * ti + half;
-    const bool has_tile = tt < ntiles;  // half-uniform
-    const int vt = bw.tile0 + tt * bw.tile_step;
-    const int64_t tile_key0 = (int64_t)real_tile(vt) * kMTileKeys;
-    const bool has_group = has_tile && kPassGroups * p + wave < ngroups;
-    if ((q & 1) == 0) {
-    // ==== T phase
-    // side-stream bytes of this tile, loaded before the next item's planes so
-    // that waiting for them does not wait for those
-    if (META && meta_words && has_tile && p == npasses - 1 && hh < GH) {
-      mw[0] = mw[1] = mw[2] = mw[3] = 0u;
-      const int64_t kb0 = tile_key0 + 256 * wave + 4 * (lane & 15);
-#pragma unroll
-      for (int beta = 0; beta < 4; ++beta)
-        if (kb0 + 64 * beta + 4 <= n)
-          mw[beta] = *reinterpret_cast<const uint32_t *>(meta + kb0 + 64 * beta);
-    }
-    // ---- regroup: quarter k ends with word 4*m16 + k of the 4 plane rows of
-    // every slot; 32-lane halves first, then 16-lane rows.
-    uint32_t(&x)[32] = xn;  // regrouped and transposed in place
-    if (has_group) {
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t desc =
+            __builtin_amdgcn_readfirstlane((dw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+        const uint32_t c = (desc >> 3) & (kD - 1), dep = desc & 7u, top = desc >> 10;
+        const uint32_t voff = live && plane_sl < dep && plane_sl >= top
+                                  ? c * chan_bytes + tile_off + lane_part
+                                  : kUnread;
+        const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int32_t)voff, 0, 0);
+        x[4 * i + 0] = (uint32_t)v[0];
+        x[4 * i + 1] = (uint32_t)v[1];
+        x[4 * i + 2] = (uint32_t)v[2];
+        x[4 * i + 3] = (uint32_t)v[3];
+      }
+    };
+    // regroup and transpose task k's words in place and store them in its
+    // item's code buffer, once the consumers have released that buffer
+    auto produce = [&](int k, uint32_t(&x)[32]) {
+      const int ti = k / ngroups, grp = k - ti * ngroups;
+      const int item = ti * npasses + (grp >> 3);
+      const int b = item & 1;
+      ring_wait(&s_ring[2 + b], 8u * (uint32_t)(item >> 1));  // buffer free
+      // quarter k ends with word 4*m16 + k of the 4 plane rows of every
+      // slot: 32-lane halves first, then 16-lane rows
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const auto h02 = __builtin_amdgcn_permlane32_swap(x[4 * i + 0], x[4 * i + 2], false, false);
@@ -771,8 +817,6 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
         x[4 * i + 1] = h13[0];
         x[4 * i + 3] = h13[1];
       }
-    }
-    if (has_group) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const auto r01 = __builtin_amdgcn_permlane16_swap(x[4 * i + 0], x[4 * i + 1], false, false);
@@ -782,68 +826,141 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
         x[4 * i + 2] = r23[0];
         x[4 * i + 3] = r23[1];
       }
-      // ---- transpose: x[4j+q] = bit q of slot j for keys 32w..32w+31 of the
-      // tile, w = 4*m16 + quarter; afterwards x[t] = the 8 codes of key 32w+t
+      // x[4j+q] = bit q of slot j for keys 32w..32w+31 of the tile,
+      // w = 4*m16 + quarter; afterwards x[t] = the 8 codes of key 32w+t
       transpose32_perm(x);
       const int w = 4 * m16 + quarter;
-      uint32_t *dst = &codes[code_index(wave, 32 * w)];
+      uint32_t *dst = &s_codes[b][code_index(grp & 7, 32 * w)];
 #pragma unroll
       for (int t = 0; t < 32; ++t) dst[t] = x[t];
+      ring_signal(&s_ring[b]);  // one group of the buffer filled
+    };
+    uint32_t x0[32], x1[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) x0[r] = x1[r] = 0;
+    issue(wave, x0);
+    issue(wave + 8, x1);
+    for (int k = wave; k < ntasks; k += 16) {
+      produce(k, x0);
+      issue(k + 16, x0);
+      if (k + 8 < ntasks) produce(k + 8, x1);
+      issue(k + 24, x1);
     }
-    // the next item's words load into the same registers once these are in
-    // the code table
-    if (it + 1 < nitems) issue(it + 1, xn);
-    } else {
-    // ==== M phase
-    // ---- MFMA phase: 256 keys of this wave; block b = 4*beta + e covers keys
-    // 64*beta + 4*n + e (n = lane % 16)
+  } else {
+    // ==== consumers: wave v multiplies keys 256v .. 256v+255 of every item
+    // (16 MFMAs of 16 keys x 64 slots); block b = 4*beta + e covers keys
+    // 64*beta + 4*n + e (n = lane % 16); each lane ends with 4 consecutive
+    // keys of head hh per beta.
     const int j = lane >> 4, nn = lane & 15;
-    if (has_tile) {
-    const int4 av = *reinterpret_cast<const int4 *>(&s_limbs[p][lane][0]);
-    const v4i A = v4i{av.x, av.y, av.z, av.w};
-    if (p == 0) {
+    // the consumers, whose matrix and epilogue phases set the pace, win
+    // issue arbitration over the producers (whose loads run well ahead)
+    __builtin_amdgcn_s_setprio(1);
+    float s[16];
+    uint32_t fill_target[2] = {0u, 0u};  // groups stored in each buffer so far
+    for (int it = 0; it < nitems; ++it) {
+      const int b = it & 1;
+      const int ti = it / npasses, p = it - ti * npasses;
+      fill_target[b] += (uint32_t)max(0, min(kPassGroups, ngroups - kPassGroups * p));
+      const int vt = bw.tile0 + ti * bw.tile_step;
+      const int64_t tile_key0 = (int64_t)real_tile(vt) * kMTileKeys;
+      const bool last_pass = p == npasses - 1;
+      // side-stream bytes of this wave's keys, loaded before the wait
+      uint32_t mw[4] = {0u, 0u, 0u, 0u};
+      if (META && meta_words && last_pass && hh < GH) {
+        const int64_t kb0 = tile_key0 + 256 * wave + 4 * nn;
 #pragma unroll
-      for (int b = 0; b < 16; ++b) s[b] = Ch;
-    }
+        for (int beta = 0; beta < 4; ++beta)
+          if (kb0 + 64 * beta + 4 <= n)
+            mw[beta] = *reinterpret_cast<const uint32_t *>(meta + kb0 + 64 * beta);
+      }
+      const int4 av = *reinterpret_cast<const int4 *>(&s_limbs[p][lane][0]);
+      const v4i A = v4i{av.x, av.y, av.z, av.w};
+      if (p == 0) {
 #pragma unroll
-    for (int beta = 0; beta < 4; ++beta) {
-      v4i acc[4];
+        for (int q = 0; q < 16; ++q) s[q] = Ch;
+      }
+      ring_wait(&s_ring[b], fill_target[b]);  // every group of the item stored
+      const uint32_t *codes = s_codes[b];
+      if (MODE == kScanCand && !META && npasses == 1) {
+        // one pass, one row per head: the exact score of a key is formed
+        // only where some lane's high limb pair reaches the row's integer
+        // bound (hi_bound), which no candidate misses; then the same fp32
+        // steps as below decide it
+        const int64_t kb = tile_key0 + 256 * wave + 4 * nn;  // + 64*beta + e
+        const int64_t rem = n - kb;
+        const int lim = hh < GH ? (rem > 256 ? 256 : (int)rem) : 0;
+        const int ht = hh < GH ? s_ht[hh] : INT_MAX;
+        uint64_t *cl = S.cand + (int64_t)(head_base + (hh < GH ? hh : 0)) * kFusedCap +
+                       (int64_t)bw.tile0 * S.seg_cap;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = 256 * wave + 64 * beta + 4 * nn + e;
-        const uint32_t w0 = codes[code_index(2 * j, key)];
-        const uint32_t w1 = codes[code_index(2 * j + 1, key)];
-        const v4i B = v4i{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu),
-                          (int)(w1 & 0x0F0F0F0Fu), (int)((w1 >> 4) & 0x0F0F0F0Fu)};
-        acc[e] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
+        for (int beta = 0; beta < 4; ++beta) {
+          v4i acc[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = 256 * wave + 64 * beta + 4 * nn + e;
+            const uint32_t w0 = codes[code_index(2 * j, key)];
+            const uint32_t w1 = codes[code_index(2 * j + 1, key)];
+            const v4i B = v4i{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu),
+                              (int)(w1 & 0x0F0F0F0Fu), (int)((w1 >> 4) & 0x0F0F0F0Fu)};
+            acc[e] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int hi = acc[e][2] + acc[e][3] * 256;
+            const bool maybe = 64 * beta + e < lim && hi >= ht;
+            if (__ballot(maybe) != 0ull) {
+              const int lo = acc[e][0] + acc[e][1] * 256;
+              const float t = __fmaf_rn((float)hi, 65536.0f, (float)lo);
+              const float v = __fmaf_rn(t, scale, Ch);
+              if (maybe && v >= row_tf) {
+                const uint32_t pos = atomicAdd(&s_segc[hh], 1u);
+                if (pos < (uint32_t)S.seg_cap) cl[pos] = compose(to_key(v), kb + 64 * beta + e);
+              }
+            }
+          }
+        }
+        ring_signal(&s_ring[2 + b]);  // buffer read (by this wave)
+        continue;
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // limb pairs combine exactly in int32 (|sum| < 2^29)
-        const int lo = acc[e][0] + acc[e][1] * 256;
-        const int hi = acc[e][2] + acc[e][3] * 256;
-        const float t = __fmaf_rn((float)hi, 65536.0f, (float)lo);
-        s[4 * beta + e] = __fmaf_rn(t, scale, s[4 * beta + e]);
+      for (int beta = 0; beta < 4; ++beta) {
+        v4i acc[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = 256 * wave + 64 * beta + 4 * nn + e;
+          const uint32_t w0 = codes[code_index(2 * j, key)];
+          const uint32_t w1 = codes[code_index(2 * j + 1, key)];
+          const v4i B = v4i{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu),
+                            (int)(w1 & 0x0F0F0F0Fu), (int)((w1 >> 4) & 0x0F0F0F0Fu)};
+          acc[e] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // limb pairs combine exactly in int32 (|sum| < 2^29)
+          const int lo = acc[e][0] + acc[e][1] * 256;
+          const int hi = acc[e][2] + acc[e][3] * 256;
+          const float t = __fmaf_rn((float)hi, 65536.0f, (float)lo);
+          s[4 * beta + e] = __fmaf_rn(t, scale, s[4 * beta + e]);
+        }
       }
-    }
-    }  // has_tile
+      ring_signal(&s_ring[2 + b]);  // buffer read (by this wave)
+      if (!last_pass) continue;
 
-    // ---- epilogue: 4 consecutive keys of head hh per beta
-    if (has_tile && p == npasses - 1) {
+      // ---- epilogue: 4 consecutive keys of head hh per beta
       const int64_t kb = tile_key0 + 256 * wave + 4 * nn;  // + 64*beta + e
       if (META && meta_words && hh < GH) {
 #pragma unroll
-        for (int b = 0; b < 16; ++b)
-          s[b] = __fmaf_rn(meta_scale, (float)((mw[b >> 2] >> (8 * (b & 3))) & 0xFFu), s[b]);
+        for (int q = 0; q < 16; ++q)
+          s[q] = __fmaf_rn(meta_scale, (float)((mw[q >> 2] >> (8 * (q & 3))) & 0xFFu), s[q]);
       } else if (META && meta && hh < GH) {
         uint32_t mb[16];
 #pragma unroll
-        for (int b = 0; b < 16; ++b) {
-          const int64_t key = kb + 64 * (b >> 2) + (b & 3);
-          mb[b] = key < n ? meta[key] : 0u;
+        for (int q = 0; q < 16; ++q) {
+          const int64_t key = kb + 64 * (q >> 2) + (q & 3);
+          mb[q] = key < n ? meta[key] : 0u;
         }
 #pragma unroll
-        for (int b = 0; b < 16; ++b) s[b] = __fmaf_rn(meta_scale, (float)mb[b], s[b]);
+        for (int q = 0; q < 16; ++q) s[q] = __fmaf_rn(meta_scale, (float)mb[q], s[q]);
       }
       const bool wave_full = tile_key0 + 256 * (wave + 1) <= n;  // wave-uniform
       if constexpr (MODE == kScanLogits) {
@@ -856,9 +973,9 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
                   make_float4(s[4 * beta], s[4 * beta + 1], s[4 * beta + 2], s[4 * beta + 3]);
           } else {
 #pragma unroll
-            for (int b = 0; b < 16; ++b) {
-              const int64_t off = 64 * (b >> 2) + (b & 3);
-              if (kb + off < n) op[off] = s[b];
+            for (int q = 0; q < 16; ++q) {
+              const int64_t off = 64 * (q >> 2) + (q & 3);
+              if (kb + off < n) op[off] = s[q];
             }
           }
         }
@@ -890,17 +1007,17 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
           // the exact sum is formed only when some lane of the wave is
           // within that margin (every other lane's value is never used)
 #pragma unroll
-          for (int b = 0; b < 16; ++b) {
+          for (int q = 0; q < 16; ++q) {
             // rows of 16 lanes are heads; row 0 receives rows 1, 2, 3 by
             // lane-row swaps (VALU, no LDS round trip)
-            const uint32_t v = __float_as_uint(s[b]);
+            const uint32_t v = __float_as_uint(s[q]);
             const auto p16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
             const auto p32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
             const auto p48 = __builtin_amdgcn_permlane16_swap(p32[1], p32[1], false, false);
             const float s1 = __uint_as_float(p16[1]);
             const float s2 = __uint_as_float(p32[1]);
             const float s3 = __uint_as_float(p48[1]);
-            float approx = s[b], mag = fabsf(s[b]);
+            float approx = s[q], mag = fabsf(s[q]);
             if (GH > 1) { approx = __fadd_rn(approx, s1); mag = __fadd_rn(mag, fabsf(s1)); }
             if (GH > 2) { approx = __fadd_rn(approx, s2); mag = __fadd_rn(mag, fabsf(s2)); }
             if (GH > 3) { approx = __fadd_rn(approx, s3); mag = __fadd_rn(mag, fabsf(s3)); }
@@ -908,40 +1025,45 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
                                            1.1754943508222875e-38f /* 2^-126 */);
             const bool near = hh == 0 && __fadd_rn(approx, margin) >= row_tf;
             if (__ballot(near) != 0ull) {
-              double acc = (double)s[b];
+              double acc = (double)s[q];
               if (GH > 1) acc = __dadd_rn(acc, (double)s1);
               if (GH > 2) acc = __dadd_rn(acc, (double)s2);
               if (GH > 3) acc = __dadd_rn(acc, (double)s3);
-              s[b] = (float)acc;
+              s[q] = (float)acc;
             } else {
-              s[b] = approx;
+              s[q] = approx;
             }
           }
           lane_rows = hh == 0;
           row = g;
         }
-        if (lane_rows) {
+        // most waves hold no candidate at all: one max per lane and a ballot
+        // decide whether the per-key tests run
+        float mx = s[0];
+#pragma unroll
+        for (int q = 1; q < 16; ++q) mx = fmaxf(mx, s[q]);
+        if (__ballot(lane_rows && mx >= row_tf) != 0ull && lane_rows) {
           // s >= t as floats is to_key(s) >= T (see key_threshold); keys
           // kb + 64*beta + e are valid while 64*beta + e < lim
           const int64_t rem = n - kb;
           const int lim = rem > 256 ? 256 : (int)rem;
           uint32_t mask = 0;
 #pragma unroll
-          for (int b = 0; b < 16; ++b)
-            mask |= (uint32_t)((64 * (b >> 2) + (b & 3) < lim) && s[b] >= row_tf) << b;
+          for (int q = 0; q < 16; ++q)
+            mask |= (uint32_t)((64 * (q >> 2) + (q & 3) < lim) && s[q] >= row_tf) << q;
           if (mask) {
             // this block's segment of the row's candidate store
             uint32_t pos = atomicAdd(&s_segc[MODE == kScanCandGroup ? 0 : hh],
                                      (uint32_t)__popc(mask));
             uint64_t *cl = S.cand + (int64_t)row * kFusedCap + (int64_t)bw.tile0 * S.seg_cap;
             while (mask) {
-              const int b = __ffs(mask) - 1;
+              const int q = __ffs(mask) - 1;
               mask &= mask - 1;
               if (pos < (uint32_t)S.seg_cap) {
                 float v = s[0];
 #pragma unroll
-                for (int q = 1; q < 16; ++q) v = b == q ? s[q] : v;
-                cl[pos] = compose(to_key(v), kb + 64 * (b >> 2) + (b & 3));
+                for (int u = 1; u < 16; ++u) v = q == u ? s[u] : v;
+                cl[pos] = compose(to_key(v), kb + 64 * (q >> 2) + (q & 3));
               }
               ++pos;
             }
@@ -949,9 +1071,6 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
         }
       }
     }
-    }  // M phase
-    }  // q in range
-    __syncthreads();
   }
   if constexpr (MODE == kScanCand || MODE == kScanCandGroup) {
     // every block reports its count (above seg_cap: the segment overflowed)
