@@ -19,7 +19,9 @@ constexpr int kSampleTiles = 8;         // 2048-key tiles a fused call scores fi
 constexpr int kSampleKeys = kSampleTiles * kBlockKeys;
 constexpr int kCntStride = 32;          // candidate counters, one 128-byte line each
 // Candidate store of the fused call: per output row, one segment per scan
-// block of the row's kv head (at most kMaxSeg), kFusedCap words in all.
+// block of the row's kv head (at most kMaxSeg), kFusedCap words in all; a
+// block whose candidates outgrow its segment puts the rest in the row's
+// overflow list (kCandCap words, one global counter per row).
 constexpr int kMaxSeg = 1024;
 constexpr int kFusedCap = 32768;
 
@@ -115,6 +117,8 @@ struct ScanSession {
   const uint32_t *thr;    // [rows] threshold keys of the session's output rows
   uint64_t *cand;         // [rows][kFusedCap] candidate segments
   uint32_t *seg_cnt;      // [rows][kMaxSeg] candidates found by each block
+  uint32_t *ovf_cnt;      // [rows] (stride kCntStride): candidates past their segment
+  uint64_t *ovf;          // [rows][kCandCap] ... stored here, in arrival order
   const uint32_t *redo;   // [hkv]: recompute only the kv heads flagged here
   uint8_t *table;         // slot tables of the session's kv heads, or null
   int32_t table_mode;     // ScanTable: what the scan does with them

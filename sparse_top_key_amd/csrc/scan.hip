@@ -62,6 +62,8 @@ struct ScanSess {
   uint32_t *cnt;
   uint64_t *cand;
   uint32_t *seg_cnt;
+  uint32_t *ovf_cnt;
+  uint64_t *ovf;
   const uint32_t *redo;
   int32_t seg_cap;         // candidate words per (row, block) segment
   uint8_t *table;          // slot records of the session, or null
@@ -595,6 +597,18 @@ __device__ __forceinline__ int hi_bound(float tf, float C, float scale) {
   return (int)h;
 }
 
+// Stores candidate word `wd` of output row `row` at position pos of the scan
+// block's segment, or, past the segment, in the row's overflow list.
+__device__ __forceinline__ void store_candidate(KScanSess &S, int row, int seg, uint32_t pos,
+                                                uint64_t wd) {
+  if (pos < (uint32_t)S.seg_cap) {
+    S.cand[(int64_t)row * kFusedCap + (int64_t)seg * S.seg_cap + pos] = wd;
+  } else {
+    const uint32_t g = atomicAdd(&S.ovf_cnt[(int64_t)row * kCntStride], 1u);
+    if (g < (uint32_t)kCandCap) S.ovf[(int64_t)row * kCandCap + g] = wd;
+  }
+}
+
 // Set-up-only state of the matrix-core kernel, overlaid on its code table.
 template <int GH>
 struct MfmaSetup {
@@ -890,8 +904,6 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
         const int64_t rem = n - kb;
         const int lim = hh < GH ? (rem > 256 ? 256 : (int)rem) : 0;
         const int ht = hh < GH ? s_ht[hh] : INT_MAX;
-        uint64_t *cl = S.cand + (int64_t)(head_base + (hh < GH ? hh : 0)) * kFusedCap +
-                       (int64_t)bw.tile0 * S.seg_cap;
 #pragma unroll
         for (int beta = 0; beta < 4; ++beta) {
           v4i acc[4];
@@ -914,7 +926,8 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
               const float v = __fmaf_rn(t, scale, Ch);
               if (maybe && v >= row_tf) {
                 const uint32_t pos = atomicAdd(&s_segc[hh], 1u);
-                if (pos < (uint32_t)S.seg_cap) cl[pos] = compose(to_key(v), kb + 64 * beta + e);
+                store_candidate(S, head_base + hh, bw.tile0, pos,
+                                compose(to_key(v), kb + 64 * beta + e));
               }
             }
           }
@@ -1055,16 +1068,13 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
             // this block's segment of the row's candidate store
             uint32_t pos = atomicAdd(&s_segc[MODE == kScanCandGroup ? 0 : hh],
                                      (uint32_t)__popc(mask));
-            uint64_t *cl = S.cand + (int64_t)row * kFusedCap + (int64_t)bw.tile0 * S.seg_cap;
             while (mask) {
               const int q = __ffs(mask) - 1;
               mask &= mask - 1;
-              if (pos < (uint32_t)S.seg_cap) {
-                float v = s[0];
+              float v = s[0];
 #pragma unroll
-                for (int u = 1; u < 16; ++u) v = q == u ? s[u] : v;
-                cl[pos] = compose(to_key(v), kb + 64 * (q >> 2) + (q & 3));
-              }
+              for (int u = 1; u < 16; ++u) v = q == u ? s[u] : v;
+              store_candidate(S, row, bw.tile0, pos, compose(to_key(v), kb + 64 * (q >> 2) + (q & 3)));
               ++pos;
             }
           }
@@ -1073,7 +1083,8 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
     }
   }
   if constexpr (MODE == kScanCand || MODE == kScanCandGroup) {
-    // every block reports its count (above seg_cap: the segment overflowed)
+    // every block reports its count (above seg_cap: the rest is in the
+    // row's overflow list)
     __syncthreads();
     const int rows = MODE == kScanCandGroup ? 1 : GH;
     if (tid < rows) {
@@ -1304,6 +1315,8 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_
         o.thr = in.thr;
         o.cand = in.cand;
         o.seg_cnt = in.seg_cnt;
+        o.ovf_cnt = in.ovf_cnt;
+        o.ovf = in.ovf;
         o.redo = in.redo;
         o.table = fp32_path ? nullptr : in.table;
         o.table_mode = fp32_path || !in.table ? kTableNone : in.table_mode;

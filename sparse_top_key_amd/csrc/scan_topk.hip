@@ -9,17 +9,19 @@
 //                     row's n scores at or above it (all keys when n <= 8192),
 //   3. candidate scan every key scored again, the (score key, index) words of
 //                     those >= T stored in the row's candidate segment of the
-//                     scan block (block-local counters in LDS, no global
-//                     atomics),
+//                     scan block (block-local counters in LDS); a block that
+//                     finds more than its segment holds (top keys clustered in
+//                     one stretch of the row) appends the rest to the row's
+//                     overflow list (one global counter per row),
 //   4. final          the exact top k of each row whose candidate count lies
 //                     in [k, 8192], ranked and written; other rows flagged,
-//   5. redo scan      full logits of the flagged rows' kv heads, one block
-//                     per kv head (blocks of unflagged kv heads return at
-//                     once),
+//   5. redo scan      full logits of the flagged rows' kv heads, tiled like
+//                     any scan (blocks of unflagged kv heads return at once),
 //   6. redo final     exact top k of the flagged rows from those logits.
 // Every score >= T is a candidate, so a row with k..8192 candidates holds
-// its exact top k; the redo steps cover every other row.  Steps 5-6 cost one
-// early-exiting launch each when no row is flagged.
+// its exact top k; the redo steps cover every other row (a sample that
+// misjudged the row, or more than 8192 scores tied at the threshold).  Steps
+// 5-6 cost one early-exiting launch each when no row is flagged.
 //
 // Planes in pinned host memory, sessions above 2^25 keys, or groups other
 // than 1 and hq/hkv <= 4: the logits go to the workspace and fathom_topk's
@@ -106,6 +108,11 @@ int32_t launch_scan_topk(const ScanSession *in, int32_t *const *idx, float *cons
     c.thr = tw.thr + row0;
     c.cand = tw.fcand + row0 * kFusedCap;
     c.seg_cnt = tw.seg_cnt + row0 * kMaxSeg;
+    // overflow lists: the candidate lists and counters of the plain top-k,
+    // which the fused call does not otherwise use (the threshold stage
+    // zeroes the counters)
+    c.ovf_cnt = tw.cnt + row0 * kCntStride;
+    c.ovf = tw.cand + row0 * kCandCap;
     c.redo = nullptr;
     c.table = reinterpret_cast<uint8_t *>(w + L.table_off + (int64_t)j * L.table_bytes);
     c.table_mode = kTableRead;
@@ -153,7 +160,7 @@ int32_t launch_scan_topk(const ScanSession *in, int32_t *const *idx, float *cons
                                rows_per_kv, hkv))
     return rc;
   if (m > 0)
-    if (int32_t rc = launch_scan(sc, m, hkv, hq, s, kScanLogits, nullptr, true)) return rc;
+    if (int32_t rc = launch_scan(sc, m, hkv, hq, s, kScanLogits)) return rc;
   return launch_topk(fin, n_sess, rows_per_sess, group, k, tw, s, kTopkRedoFinal, rows_per_kv,
                      hkv);
 }

@@ -621,26 +621,26 @@ __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
   const int k = a.k;
   const int kk = (int)(n < k ? n : k);
   uint32_t cnt = 0;
-  bool fused_over = false;
   if (a.stage == kTopkFusedFinal) {
-    // the row's candidates sit in one segment per scan block
+    // the row's candidates: min(c, seg_cap) words in each scan block's
+    // segment, the rest of each block's count in the row's overflow list
+    // (which then holds sum_b max(0, c_b - seg_cap) words)
     const int nseg = S.nseg, seg_cap = kFusedCap / (nseg > 0 ? nseg : 1);
     const int c = threadIdx.x < nseg ? (int)a.seg_cnt[(int64_t)o * kMaxSeg + threadIdx.x] : 0;
-    const int incl = block_inclusive_scan(c, wave_tot);
-    s_off[threadIdx.x] = incl - c;
+    const int kept = c < seg_cap ? c : seg_cap;
+    const int incl = block_inclusive_scan(kept, wave_tot);
+    s_off[threadIdx.x] = incl - kept;
     if (threadIdx.x == kBig - 1) s_off[kMaxSeg] = incl;
     if (threadIdx.x == 0) s_res[1] = 0;
     __syncthreads();
-    if (c > seg_cap) s_res[1] = 1;
+    if (c > 0) atomicAdd(&s_res[1], c);
     __syncthreads();
-    cnt = (uint32_t)s_off[kMaxSeg];
-    fused_over = s_res[1] != 0;
+    cnt = (uint32_t)s_res[1];
     __syncthreads();
   } else {
     cnt = a.cnt[(int64_t)o * kCntStride];
   }
-  bool fast = !fused_over &&
-              ((n <= kCandCap) || (cnt >= (uint32_t)k && cnt <= (uint32_t)kCandCap));
+  bool fast = (n <= kCandCap) || (cnt >= (uint32_t)k && cnt <= (uint32_t)kCandCap);
   if (a.stage == kTopkRedoFinal) {
     if (!a.flag[o]) return;  // this row was answered from its candidates
     fast = false;
@@ -663,7 +663,7 @@ __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
       const int tps = kBig / (nseg > 0 ? nseg : 1);
       const int sg = threadIdx.x / tps, sub = threadIdx.x % tps;
       if (sg < nseg) {
-        const int c = s_off[sg + 1] - s_off[sg];
+        const int c = (sg + 1 < nseg ? s_off[sg + 1] : s_off[kMaxSeg]) - s_off[sg];
         const uint64_t *src = fc + (int64_t)sg * seg_cap;
         uint64_t *dst = s + s_off[sg];
         for (int b0 = sub; b0 < c; b0 += 8 * tps) {
@@ -680,6 +680,10 @@ __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
           }
         }
       }
+      // then the overflow list (m <= kCandCap words in all)
+      const int stored = s_off[kMaxSeg];
+      const uint64_t *ov = a.cand + (int64_t)o * kCandCap;
+      for (int j = threadIdx.x; j < m - stored; j += kBig) s[stored + j] = ov[j];
     } else {
       const uint64_t *cand = a.cand + (int64_t)o * kCandCap;
       for (int j = threadIdx.x; j < m; j += kBig) s[j] = cand[j];

@@ -277,9 +277,18 @@ def test_layer_1m_clustered_top_keys(F, orc, layer_1m, group):
     plan = F.plan(q, p.sigma2, w.budget)
     logits = F.scan(p.planes, p.lo, p.hi, n, q, plan)
     idx, vals = F.topk(logits, w.k, group=group)
-    fidx, fvals = F.scan_topk(p.planes, p.lo, p.hi, n, q, plan, w.k, group)
+    ws = torch.empty(F.scan_topk_workspace_bytes([n], w.hkv, w.hq, group, w.k),
+                     dtype=torch.uint8, device=dev())
+    fidx, fvals = F.scan_topk(p.planes, p.lo, p.hi, n, q, plan, w.k, group, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(fidx, idx) and torch.equal(fvals, vals)
+    # the clustered row is answered from its candidates (the blocks' segments
+    # and the row's overflow list), not recomputed from full logits: the
+    # workspace starts with one threshold word, then one recompute flag per
+    # output row
+    rows = w.hq // group
+    flags = ws[4 * rows:8 * rows].view(torch.int32).cpu().numpy()
+    assert not flags.any(), flags
     row = head if group == 1 else head // G
     sel = set(fidx[row].cpu().tolist())
     planted = set(range(tile * 2048, tile * 2048 + m))
