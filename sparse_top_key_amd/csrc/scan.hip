@@ -904,35 +904,48 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
         const int64_t rem = n - kb;
         const int lim = hh < GH ? (rem > 256 ? 256 : (int)rem) : 0;
         const int ht = hh < GH ? s_ht[hh] : INT_MAX;
+        // all 16 products first; the buffer is released once they are issued
+        v4i acc[16];
 #pragma unroll
-        for (int beta = 0; beta < 4; ++beta) {
-          v4i acc[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int key = 256 * wave + 64 * beta + 4 * nn + e;
-            const uint32_t w0 = codes[code_index(2 * j, key)];
-            const uint32_t w1 = codes[code_index(2 * j + 1, key)];
-            const v4i B = v4i{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu),
-                              (int)(w1 & 0x0F0F0F0Fu), (int)((w1 >> 4) & 0x0F0F0F0Fu)};
-            acc[e] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int hi = acc[e][2] + acc[e][3] * 256;
-            const bool maybe = 64 * beta + e < lim && hi >= ht;
-            if (__ballot(maybe) != 0ull) {
-              const int lo = acc[e][0] + acc[e][1] * 256;
-              const float t = __fmaf_rn((float)hi, 65536.0f, (float)lo);
-              const float v = __fmaf_rn(t, scale, Ch);
-              if (maybe && v >= row_tf) {
-                const uint32_t pos = atomicAdd(&s_segc[hh], 1u);
-                store_candidate(S, head_base + hh, bw.tile0, pos,
-                                compose(to_key(v), kb + 64 * beta + e));
-              }
-            }
-          }
+        for (int q = 0; q < 16; ++q) {
+          const int key = 256 * wave + 64 * (q >> 2) + 4 * nn + (q & 3);
+          const uint32_t w0 = codes[code_index(2 * j, key)];
+          const uint32_t w1 = codes[code_index(2 * j + 1, key)];
+          const v4i B = v4i{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu),
+                            (int)(w1 & 0x0F0F0F0Fu), (int)((w1 >> 4) & 0x0F0F0F0Fu)};
+          acc[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
         }
         ring_signal(&s_ring[2 + b]);  // buffer read (by this wave)
+        // key kb + 64*(q/4) + q%4 may be a candidate only if its high limb
+        // pair reaches the bound; exact scores where some lane needs one
+        uint32_t mask = 0;
+        float sv[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int hi = acc[q][2] + acc[q][3] * 256;
+          const bool maybe = 64 * (q >> 2) + (q & 3) < lim && hi >= ht;
+          sv[q] = 0.0f;
+          if (__ballot(maybe) != 0ull) {
+            const int lo = acc[q][0] + acc[q][1] * 256;
+            const float t = __fmaf_rn((float)hi, 65536.0f, (float)lo);
+            sv[q] = __fmaf_rn(t, scale, Ch);
+            mask |= (uint32_t)(maybe && sv[q] >= row_tf) << q;
+          }
+        }
+        if (mask) {
+          // this block's segment of the row's candidate store
+          uint32_t pos = atomicAdd(&s_segc[hh], (uint32_t)__popc(mask));
+          while (mask) {
+            const int q = __ffs(mask) - 1;
+            mask &= mask - 1;
+            float v = sv[0];
+#pragma unroll
+            for (int u = 1; u < 16; ++u) v = q == u ? sv[u] : v;
+            store_candidate(S, head_base + hh, bw.tile0, pos,
+                            compose(to_key(v), kb + 64 * (q >> 2) + (q & 3)));
+            ++pos;
+          }
+        }
         continue;
       }
 #pragma unroll
