@@ -269,8 +269,10 @@ def cpu_baseline(layer0, w, n_sample, n_sample_mt):
     dt1 = time.perf_counter() - t0
     del logits, p1
 
-    # all cores: pieces of whole 2048-key tiles
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    # all the cores this process may use, up to the 16 host cores that go with
+    # one GPU on this kind of box: pieces of whole 2048-key tiles
+    visible = len(os.sched_getaffinity(0))
+    cores = max(1, min(16, visible))
     chunks = max(1, -(-cores // hkv))
     tiles = -(-n_sample_mt // 2048)
     bounds = [min(n_sample_mt, (tiles * j // chunks) * 2048) for j in range(chunks + 1)]
@@ -299,14 +301,22 @@ def cpu_baseline(layer0, w, n_sample, n_sample_mt):
         dtm = time.perf_counter() - t0
     cpu_model = None
     try:
+        fields = {}
         with open("/proc/cpuinfo") as f:
-            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f
-                              if ln.startswith("model name")), None)
+            for ln in f:
+                if ":" in ln:
+                    k_, v_ = ln.split(":", 1)
+                    fields.setdefault(k_.strip(), v_.strip())
+        cpu_model = (f"{fields.get('model name', '?')} (vendor {fields.get('vendor_id', '?')}, "
+                     f"family {fields.get('cpu family', '?')}, model {fields.get('model', '?')}, "
+                     f"stepping {fields.get('stepping', '?')}, {fields.get('cpu MHz', '?')} MHz)")
     except OSError:
         pass
     plane_bytes_mt = n_sample_mt * hkv * 176 // 8   # about 176 union bits per (kv head, key)
     return dict(value=round(n_sample_mt * hkv / dtm, 1), unit="keys/s", cores=cores,
-                kind="oracle", cpu_model=cpu_model,
+                kind="oracle", cpu_model=cpu_model, cpus_visible=visible,
+                cores_note=("threads used: every CPU this process may use "
+                            f"({visible}), at most the 16 host cores that go with one GPU"),
                 plane_bytes_per_s_approx=round(plane_bytes_mt / dtm, 1),
                 sample=(f"first {n_sample_mt} keys of the 1M-key layer, all {hkv} kv heads / "
                         f"{hq} query heads: plan + fp64 scan + top-{w.k} (full sort), "
@@ -380,10 +390,94 @@ def bench_layer_128k(dev, steps, warmup):
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / steps
         ub = [union_plane_bytes(L[2], w.hkv, w.n)[0] for L in layers]
+        # the same step through the fused call (plan -> scan_topk, planes in HBM)
+        fws = torch.empty(fathom.scan_topk_workspace_bytes([w.n], w.hkv, w.hq, 1, w.k),
+                          dtype=torch.uint8, device=dev)
+
+        def fstep(i):
+            p, q, plan, _ = layers[i % len(layers)]
+            fathom.plan(q, p.sigma2, B, out=plan)
+            fathom.scan_topk(p.planes, p.lo, p.hi, w.n, q, plan, w.k, 1, ws=fws, idx=idx,
+                             vals=vals)
+        for i in range(warmup):
+            fstep(i)
+        torch.cuda.synchronize()
+        a, b = _event_pair()
+        a.record()
+        for i in range(steps):
+            fstep(i)
+        b.record()
+        torch.cuda.synchronize()
+        fms = a.elapsed_time(b) / steps
+        ubm = int(np.mean(ub))
+        gbps = ubm / (fms * 1e-3) / 1e9
         out[f"B{B}"] = {"step_ms": round(ms, 4),
                         "keys_per_s": round(w.n * w.hkv / (ms * 1e-3), 1),
-                        "union_plane_bytes": int(np.mean(ub))}
+                        "union_plane_bytes": ubm,
+                        "fused_step_ms": round(fms, 4),
+                        "fused_keys_per_s": round(w.n * w.hkv / (fms * 1e-3), 1),
+                        "fused_roofline": {"bound": "hbm", "achieved": round(gbps, 1),
+                                           "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                           "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                                           "algorithmic_bytes": ubm}}
+        del fws
     return out
+
+
+def bench_clustered(dev, steps, warmup, iid_step_ms):
+    """The 1M-key layer with 1,500 top-scoring keys planted inside one
+    2048-key tile of one query head's kv head (a different head and tile per
+    layer): one scan block finds more candidates than its share of the row's
+    candidate store.  Fused HBM step time against the i.i.d. layers', and the
+    rows recomputed from full logits."""
+    w = synth.LAYER_1M
+    G = w.hq // w.hkv
+    layers = []
+    for l in range(4):
+        keys = synth.keys(w.seed, l, w.n, w.hkv, w.d, w.dtype, w.outliers, device=dev)
+        q = synth.queries(w.seed, l, w.hq, w.d, device=dev)
+        head, tile, m = 5 + 7 * l, 101 + 97 * l, 1500
+        g = head // G
+        sd = keys[:, g, :].float().std(0)
+        v = (3.0 * sd * torch.sign(q[head])).to(keys.dtype)
+        t0 = tile * 2048
+        keys[t0:t0 + m, g, :] = v
+        keys[t0:t0 + m, g, 0] = (v[0].float() + 0.01 * sd[0] * torch.arange(
+            m, device=dev, dtype=torch.float32) / m).to(keys.dtype)
+        p = fathom.pack(keys)
+        del keys
+        layers.append((p, q, torch.empty((w.hq, w.d), dtype=torch.uint8, device=dev)))
+    fws = torch.empty(fathom.scan_topk_workspace_bytes([w.n], w.hkv, w.hq, 1, w.k),
+                      dtype=torch.uint8, device=dev)
+    idx = torch.empty((w.hq, w.k), dtype=torch.int32, device=dev)
+    vals = torch.empty((w.hq, w.k), device=dev)
+
+    def step(i):
+        p, q, plan = layers[i % len(layers)]
+        fathom.plan(q, p.sigma2, w.budget, out=plan)
+        fathom.scan_topk(p.planes, p.lo, p.hi, w.n, q, plan, w.k, 1, ws=fws, idx=idx, vals=vals)
+    flagged = 0
+    for i in range(len(layers)):
+        step(i)
+        torch.cuda.synchronize()
+        # the workspace starts with one threshold word, then one recompute
+        # flag per output row
+        flagged += int(fws[4 * w.hq:8 * w.hq].view(torch.int32).ne(0).sum())
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    a, b = _event_pair()
+    a.record()
+    for i in range(steps):
+        step(i)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    return {"workload": ("1M-key layer, planes in HBM, B=92, k=2048: 1500 top keys of one "
+                         "query head inside one 2048-key tile"),
+            "fused_step_ms": round(ms, 4), "iid_fused_step_ms": round(iid_step_ms, 4),
+            "ratio_to_iid": round(ms / iid_step_ms, 3),
+            "rows_recomputed": flagged, "rows_total": len(layers) * w.hq}
 
 
 def plan_quality(dev, layers_q=2):
@@ -665,6 +759,23 @@ def scan_traffic_from_profiles():
     return rec
 
 
+CAND_FILE = os.path.join(ROOT, "profiles", "scan_topk_1m_layer_candidate_scan.json")
+
+
+def candidate_scan_from_profiles():
+    """The fused call's candidate-scan kernel time from the committed kernel
+    trace (valid only for the scan source it was taken on)."""
+    if not os.path.exists(CAND_FILE):
+        return None
+    with open(CAND_FILE) as f:
+        rec = json.load(f)
+    h = hashlib.sha256(open(SCAN_SOURCE, "rb").read()).hexdigest()
+    if rec.get("scan_source_sha256") != h:
+        return None
+    rec["file"] = os.path.relpath(CAND_FILE, ROOT)
+    return rec
+
+
 def res_modes(args):
     return ["host", "hbm"] if args.only == "all" else [args.only]
 
@@ -806,7 +917,7 @@ def main():
                     "peak": PCIE_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / PCIE_PEAK_GBPS, 4),
                     "traffic": (traffic or {}).get("host_scan_fetch_bytes"),
-                    "kernel": "scan_kernel<4, 32, 2> (planes in pinned host memory)",
+                    "kernel": "scan_kernel<4, 2> (planes in pinned host memory, fp32 FMA form)",
                     "algorithmic_bytes": plane_b,
                     "frac_of_measured_link_peak": (round(achieved / probe["host_read_zero_copy_GBps"], 4)
                                                    if probe else None),
@@ -835,19 +946,38 @@ def main():
         out["roofline"] = roofline
     if "hbm" in res:
         h = res["hbm"]
-        ach = (plane_b + logits_b) / (h["scan_ms"] * 1e-3) / 1e9
+        # algorithmic bytes: the union plane bytes alone; the fp32 logits the
+        # unfused scan writes (and top-k reads back) are not the method's
+        ach = plane_b / (h["scan_ms"] * 1e-3) / 1e9
         out["roofline_hbm"] = {
             "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBPS, 4),
             "traffic": (traffic or {}).get("hbm_scan_bytes"),
             "kernel": "scan_mfma_kernel<4, 0, false> (planes in HBM, all logits written)",
-            "algorithmic_bytes": plane_b + logits_b,
+            "algorithmic_bytes": plane_b,
+            "non_algorithmic_bytes": logits_b,
+            "achieved_with_logits_GBps": round((plane_b + logits_b) / (h["scan_ms"] * 1e-3) / 1e9, 1),
             "end_to_end_plane_GBps": round(plane_b / (h["step_ms"] * 1e-3) / 1e9, 1)}
+        hf = res["hbm_fused"]
+        e2e = plane_b / (hf["step_ms"] * 1e-3) / 1e9
+        out["roofline_hbm_fused_step"] = {
+            "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS,
+            "what": "union plane bytes over the whole plan + scan_topk step (event-timed)",
+            "achieved": round(e2e, 1), "frac": round(e2e / HBM_PEAK_GBPS, 4),
+            "algorithmic_bytes": plane_b, "step_ms": round(hf["step_ms"], 4)}
+        cand = candidate_scan_from_profiles()
+        if cand:
+            ca = plane_b / (cand["candidate_scan_us"] * 1e-6) / 1e9
+            out["roofline_hbm_fused_step"]["candidate_scan"] = {
+                "kernel": cand["kernel"], "avg_us_kernel_trace": cand["candidate_scan_us"],
+                "achieved": round(ca, 1), "frac": round(ca / HBM_PEAK_GBPS, 4),
+                "source": cand["file"]}
         if traffic_probe_ms:
             # the same bytes moved by fathom_probe_scan_traffic, with no arithmetic
             pat = (plane_b + logits_b) / (traffic_probe_ms * 1e-3) / 1e9
             out["roofline_hbm"]["scan_traffic_probe_GBps"] = round(pat, 1)
-            out["roofline_hbm"]["frac_of_scan_traffic_probe"] = round(ach / pat, 4)
+            out["roofline_hbm"]["frac_of_scan_traffic_probe"] = round(
+                (plane_b + logits_b) / (h["scan_ms"] * 1e-3) / 1e9 / pat, 4)
             # the same number of plane rows per kv head read as whole channels
             out["roofline_hbm"]["scan_traffic_probe_whole_channels_GBps"] = round(
                 (plane_b + logits_b) / (dense_probe_ms * 1e-3) / 1e9, 1)
@@ -866,6 +996,11 @@ def main():
         else:
             out["roofline"] = out.pop("roofline_hbm")
     out["timings_ms"] = {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in res.items()}
+    out["timings_note"] = ("*_fused rows call fathom_scan_topk; with planes in pinned host memory "
+                           "('host_fused', 'host_fixed_fused') that call scans the logits into "
+                           "its workspace and runs the plain top-k on them (the sampled "
+                           "candidate scan needs device-resident planes), so those rows time "
+                           "scan then top-k inside one call")
     for mode in ("host", "hbm"):
         if mode in res:
             out.setdefault("fixed136_speedup", {})[mode] = round(
@@ -898,6 +1033,10 @@ def main():
         del layers
         torch.cuda.empty_cache()
         extra = {}
+        if "hbm_fused" in res:
+            extra["clustered_1m_hbm"] = bench_clustered(dev, 30, 5, res["hbm_fused"]["step_ms"])
+            log(f"clustered: {extra['clustered_1m_hbm']}")
+            torch.cuda.empty_cache()
         extra["pack"] = bench_pack(dev)
         log(f"pack: {extra['pack']}")
         torch.cuda.empty_cache()

@@ -597,16 +597,40 @@ __device__ __forceinline__ int hi_bound(float tf, float C, float scale) {
   return (int)h;
 }
 
-// Stores candidate word `wd` of output row `row` at position pos of the scan
-// block's segment, or, past the segment, in the row's overflow list.
-__device__ __forceinline__ void store_candidate(KScanSess &S, int row, int seg, uint32_t pos,
-                                                uint64_t wd) {
-  if (pos < (uint32_t)S.seg_cap) {
-    S.cand[(int64_t)row * kFusedCap + (int64_t)seg * S.seg_cap + pos] = wd;
+// Where the candidate words of one lane go: positions pos, pos+1, ... of the
+// scan block's segment of output row `row`, and past its end the row's
+// overflow list, whose slots the lane takes with one global add for all of
+// its overflowing words (top keys clustered in one stretch of the row send
+// hundreds of words from one block; one atomic per word would serialise).
+struct CandSink {
+  uint64_t *seg;       // the block's segment of the row
+  uint64_t *ovf;       // the row's overflow list
+  uint32_t pos, cap;   // next segment position; segment capacity
+  uint32_t obase;      // first overflow slot of this lane
+};
+
+__device__ __forceinline__ CandSink cand_sink(KScanSess &S, int row, int seg, uint32_t pos,
+                                              uint32_t count) {
+  CandSink c;
+  c.seg = S.cand + (int64_t)row * kFusedCap + (int64_t)seg * S.seg_cap;
+  c.ovf = S.ovf + (int64_t)row * kCandCap;
+  c.pos = pos;
+  c.cap = (uint32_t)S.seg_cap;
+  const uint32_t in_seg = pos >= c.cap ? 0u : (c.cap - pos < count ? c.cap - pos : count);
+  c.obase = 0;
+  if (count > in_seg)
+    c.obase = atomicAdd(&S.ovf_cnt[(int64_t)row * kCntStride], count - in_seg);
+  return c;
+}
+
+__device__ __forceinline__ void cand_put(CandSink &c, uint64_t wd) {
+  if (c.pos < c.cap) {
+    c.seg[c.pos] = wd;
   } else {
-    const uint32_t g = atomicAdd(&S.ovf_cnt[(int64_t)row * kCntStride], 1u);
-    if (g < (uint32_t)kCandCap) S.ovf[(int64_t)row * kCandCap + g] = wd;
+    if (c.obase < (uint32_t)kCandCap) c.ovf[c.obase] = wd;
+    ++c.obase;
   }
+  ++c.pos;
 }
 
 // Set-up-only state of the matrix-core kernel, overlaid on its code table.
@@ -934,16 +958,15 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
         }
         if (mask) {
           // this block's segment of the row's candidate store
-          uint32_t pos = atomicAdd(&s_segc[hh], (uint32_t)__popc(mask));
+          const uint32_t c = (uint32_t)__popc(mask);
+          CandSink sink = cand_sink(S, head_base + hh, bw.tile0, atomicAdd(&s_segc[hh], c), c);
           while (mask) {
             const int q = __ffs(mask) - 1;
             mask &= mask - 1;
             float v = sv[0];
 #pragma unroll
             for (int u = 1; u < 16; ++u) v = q == u ? sv[u] : v;
-            store_candidate(S, head_base + hh, bw.tile0, pos,
-                            compose(to_key(v), kb + 64 * (q >> 2) + (q & 3)));
-            ++pos;
+            cand_put(sink, compose(to_key(v), kb + 64 * (q >> 2) + (q & 3)));
           }
         }
         continue;
@@ -1079,16 +1102,16 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
             mask |= (uint32_t)((64 * (q >> 2) + (q & 3) < lim) && s[q] >= row_tf) << q;
           if (mask) {
             // this block's segment of the row's candidate store
-            uint32_t pos = atomicAdd(&s_segc[MODE == kScanCandGroup ? 0 : hh],
-                                     (uint32_t)__popc(mask));
+            const uint32_t c = (uint32_t)__popc(mask);
+            CandSink sink = cand_sink(
+                S, row, bw.tile0, atomicAdd(&s_segc[MODE == kScanCandGroup ? 0 : hh], c), c);
             while (mask) {
               const int q = __ffs(mask) - 1;
               mask &= mask - 1;
               float v = s[0];
 #pragma unroll
               for (int u = 1; u < 16; ++u) v = q == u ? s[u] : v;
-              store_candidate(S, row, bw.tile0, pos, compose(to_key(v), kb + 64 * (q >> 2) + (q & 3)));
-              ++pos;
+              cand_put(sink, compose(to_key(v), kb + 64 * (q >> 2) + (q & 3)));
             }
           }
         }
