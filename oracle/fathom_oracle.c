@@ -112,10 +112,10 @@ int orc_pack(const float *keys, int64_t n, int hkv, int d, int64_t stride_tok,
 /* Plan.  [EXP] core method, read side, and the key pseudocode: each query
  * has a budget of B bits per key; channel importance is the key-channel
  * variance weighted by the query (R6: w_c = (q_c*q_c)*sigma_c^2 in fp32,
- * multiply then multiply, no fused multiply-add); channels are visited in
- * descending w (R8: equal w visits the lower channel index first) and each
- * takes min(4, remaining budget) bits until the budget is spent (R7: the
- * explicit fill-to-cap walk), so unimportant channels get 0 bits.
+ * multiply then multiply, no fused multiply-add); the budget fills channels
+ * up to the 4-bit cap in descending w (R8: equal w puts the lower channel
+ * index first; R7: fill-to-cap), so with that order the first B / 4
+ * channels get 4 bits, the next one B % 4, and the rest none.
  * R9: 0 <= B <= 4d.
  * q [hq][d] fp32, sigma2 [hkv][d], budget [hq], plan out [hq][d] uint8.
  * Query head h uses kv head h / (hq / hkv) (R12).                          */
@@ -151,11 +151,15 @@ int orc_plan(const float *q, int hq, int hkv, int d, const float *sigma2,
       order[c].c = c;
     }
     qsort(order, d, sizeof(orc_wc), orc_cmp_w_desc);
-    int remaining = B;
+    /* the budget fills channels to the 4-bit cap in that order: the first
+       B / 4 channels are read in full, the next one gets the remaining
+       B % 4 bits, every later channel none */
+    const int full = B / 4, part = B % 4;
     for (int j = 0; j < d; ++j) {
-      int take = remaining <= 0 ? 0 : (remaining < 4 ? remaining : 4);
-      plan[(int64_t)h * d + order[j].c] = (uint8_t)take;
-      remaining -= take;
+      uint8_t t = 0;
+      if (j < full) t = 4;
+      else if (j == full) t = (uint8_t)part;
+      plan[(int64_t)h * d + order[j].c] = t;
     }
   }
   free(order);
