@@ -553,6 +553,183 @@ int orc_append(const float *keys, int64_t m, int hkv, int d, int64_t stride_tok,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Per-block ranges.  [EXP] deployment warnings, item 3 (the planes are the
+ * stored 4-bit K; re-quantising it must not force anything else to be
+ * rebuilt) and the problem statement (long sessions that grow by a token per
+ * decode step).  Reading R22: the range (lo, hi) of a channel is kept per
+ * block of ORC_RB = 2048 consecutive keys instead of per layer, so a session
+ * whose key ranges drift quantises its later blocks with ranges of their own
+ * and no stored code is ever re-quantised.
+ *   pack:   each block's range is the min and max of its own keys (R2 and R4
+ *           within the block: delta_b = (hi_b - lo_b) / 16, codes clamped to
+ *           15, -0 stored as +0); planes as orc_pack.
+ *   sigma2: the pooled within-block variance of the dequantised values,
+ *           sum over blocks in block order of fp64(var_b * (n_b / n)), var_b
+ *           = fp64(fp64((n_b S2_b - S1_b^2) / (n_b n_b)) * delta_b^2) exactly
+ *           as R5 computes it for one block, rounded once to fp32 (so a layer
+ *           of one block has R5's sigma2).
+ *   scan:   key i of block b = i / ORC_RB reads lo_b, delta_b in the formula
+ *           of orc_scan.
+ *   append: a block that holds no key before the call takes, per (kv head,
+ *           channel), the range of the block before it widened to cover the
+ *           keys the call puts in it (block 0: those keys' own min and max);
+ *           a block that already holds keys keeps its range, and keys outside
+ *           it are clamped and counted as in orc_append.
+ * lo, hi: [hkv][d][nbc] with nbc >= the number of blocks (a capacity).       */
+#define ORC_RB 2048
+
+int64_t orc_range_blocks(int64_t n) { return (n + ORC_RB - 1) / ORC_RB; }
+
+static int orc_quantise(float x, float l, float delta) {
+  if (delta == 0.0f) return 0;
+  const double fl = floor((double)((x - l) / delta));
+  return fl < 0.0 ? 0 : (fl > 15.0 ? 15 : (int)fl);
+}
+
+int orc_pack_blocked(const float *keys, int64_t n, int hkv, int d, int64_t stride_tok,
+                     int64_t stride_head, uint32_t *planes, float *lo, float *hi,
+                     int64_t nbc, float *sigma2) {
+  const int64_t nb = orc_range_blocks(n);
+  if (!keys || !planes || !lo || !hi || !sigma2 || n < 1 || hkv < 1 || d < 1 || nbc < nb)
+    return ORC_BAD;
+  const int64_t W = orc_plane_words(n);
+  memset(planes, 0, (size_t)hkv * d * 4 * W * sizeof(uint32_t));
+  for (int h = 0; h < hkv; ++h) {
+    for (int c = 0; c < d; ++c) {
+      const float *col = keys + (int64_t)h * stride_head + c;
+      uint32_t *pl = planes + ((int64_t)h * d + c) * 4 * W;
+      double acc = 0.0;
+      for (int64_t b = 0; b < nb; ++b) {
+        const int64_t i0 = b * ORC_RB, i1 = i0 + ORC_RB < n ? i0 + ORC_RB : n;
+        float mn = col[i0 * stride_tok], mx = mn;
+        for (int64_t i = i0 + 1; i < i1; ++i) {
+          const float x = col[i * stride_tok];
+          if (x < mn) mn = x;
+          if (x > mx) mx = x;
+        }
+        mn = mn + 0.0f;
+        mx = mx + 0.0f;
+        const float delta = (mx - mn) * 0.0625f;
+        lo[((int64_t)h * d + c) * nbc + b] = mn;
+        hi[((int64_t)h * d + c) * nbc + b] = mx;
+        int64_t s1 = 0, s2 = 0;
+        for (int64_t i = i0; i < i1; ++i) {
+          const int code = orc_quantise(col[i * stride_tok], mn, delta);
+          s1 += code;
+          s2 += (int64_t)code * code;
+          for (int p = 0; p < 4; ++p)
+            if ((code >> p) & 1) pl[(3 - p) * W + i / 32] |= 1u << (i % 32);
+        }
+        const int64_t nn = i1 - i0;
+        const double var_code = (double)(nn * s2 - s1 * s1) / ((double)nn * (double)nn);
+        const double var = var_code * ((double)delta * (double)delta);
+        acc += var * ((double)nn / (double)n);
+      }
+      sigma2[h * d + c] = (float)acc;
+    }
+  }
+  return ORC_OK;
+}
+
+static double orc_score_blocked(const uint32_t *planes, int64_t W, const float *lo,
+                                const float *hi, int64_t nbc, int d, int g, const float *qh,
+                                const uint8_t *ph, int64_t i) {
+  const int64_t b = i / ORC_RB;
+  double s = 0.0;
+  for (int c = 0; c < d; ++c) {
+    const int t = ph[c];
+    const float l = lo[((int64_t)g * d + c) * nbc + b], u = hi[((int64_t)g * d + c) * nbc + b];
+    const float delta = (u - l) * 0.0625f;
+    const int r = orc_prefix(orc_code_from_planes(planes, W, d, g, c, i), t);
+    const double cell = (double)delta * (double)(1 << (4 - t));
+    s += (double)qh[c] * ((double)l + ((double)r + 0.5) * cell);
+  }
+  return s;
+}
+
+int orc_scan_blocked(const uint32_t *planes, const float *lo, const float *hi, int64_t nbc,
+                     int64_t n, int hkv, int d, const float *q, const uint8_t *plan, int hq,
+                     float *logits, int64_t ld) {
+  if (!planes || !lo || !hi || !q || !plan || !logits || n < 0 || hkv < 1 || hq % hkv ||
+      ld < n || nbc < orc_range_blocks(n))
+    return ORC_BAD;
+  const int G = hq / hkv;
+  const int64_t W = orc_plane_words(n);
+  for (int h = 0; h < hq; ++h)
+    for (int64_t i = 0; i < n; ++i)
+      logits[(int64_t)h * ld + i] = (float)orc_score_blocked(
+          planes, W, lo, hi, nbc, d, h / G, q + (int64_t)h * d, plan + (int64_t)h * d, i);
+  return ORC_OK;
+}
+
+int orc_scan_blocked_at(const uint32_t *planes, const float *lo, const float *hi, int64_t nbc,
+                        int64_t n, int hkv, int d, const float *q, const uint8_t *plan, int hq,
+                        const int64_t *keys, int64_t nk, float *out) {
+  if (!planes || !lo || !hi || !q || !plan || !keys || !out || hkv < 1 || hq % hkv ||
+      nbc < orc_range_blocks(n))
+    return ORC_BAD;
+  const int G = hq / hkv;
+  const int64_t W = orc_plane_words(n);
+  for (int h = 0; h < hq; ++h)
+    for (int64_t j = 0; j < nk; ++j) {
+      if (keys[j] < 0 || keys[j] >= n) return ORC_BAD;
+      out[(int64_t)h * nk + j] = (float)orc_score_blocked(
+          planes, W, lo, hi, nbc, d, h / G, q + (int64_t)h * d, plan + (int64_t)h * d, keys[j]);
+    }
+  return ORC_OK;
+}
+
+int orc_append_blocked(const float *keys, int64_t m, int hkv, int d, int64_t stride_tok,
+                       int64_t stride_head, int64_t n_old, uint32_t *planes, int64_t W,
+                       float *lo, float *hi, int64_t nbc, int64_t *clamped) {
+  if (!planes || !lo || !hi || !clamped || m < 0 || n_old < 0 || hkv < 1 || d < 1 ||
+      (m > 0 && !keys) || W < orc_plane_words(n_old + m) ||
+      nbc < orc_range_blocks(n_old + m))
+    return ORC_BAD;
+  int64_t count = 0;
+  const int64_t first_new = orc_range_blocks(n_old);  /* blocks with no key yet */
+  const int64_t nb_end = orc_range_blocks(n_old + m);
+  for (int h = 0; h < hkv; ++h) {
+    for (int c = 0; c < d; ++c) {
+      float *lrow = lo + ((int64_t)h * d + c) * nbc, *hrow = hi + ((int64_t)h * d + c) * nbc;
+      /* ranges of the blocks this call starts, in block order */
+      for (int64_t b = first_new; b < nb_end; ++b) {
+        const int64_t i0 = b * ORC_RB, i1 = i0 + ORC_RB < n_old + m ? i0 + ORC_RB : n_old + m;
+        float mn, mx;
+        if (b > 0) {
+          mn = lrow[b - 1];
+          mx = hrow[b - 1];
+        } else {
+          mn = mx = keys[(i0 - n_old) * stride_tok + (int64_t)h * stride_head + c];
+        }
+        for (int64_t i = i0; i < i1; ++i) {
+          const float x = keys[(i - n_old) * stride_tok + (int64_t)h * stride_head + c];
+          if (x < mn) mn = x;
+          if (x > mx) mx = x;
+        }
+        lrow[b] = mn + 0.0f;
+        hrow[b] = mx + 0.0f;
+      }
+      uint32_t *pl = planes + ((int64_t)h * d + c) * 4 * W;
+      for (int64_t j = 0; j < m; ++j) {
+        const int64_t i = n_old + j, b = i / ORC_RB;
+        const float l = lrow[b], u = hrow[b];
+        const float x = keys[j * stride_tok + (int64_t)h * stride_head + c];
+        const int code = orc_quantise(x, l, (u - l) * 0.0625f);
+        count += (x < l || x > u);
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t bit = (uint32_t)((code >> (3 - s)) & 1);
+          uint32_t *word = pl + (int64_t)s * W + i / 32;
+          *word = (*word & ~(1u << (i % 32))) | (bit << (i % 32));
+        }
+      }
+    }
+  }
+  *clamped = count;
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Per-channel code histograms.  hist[h][c][v] = number of keys i < n whose
  * 4-bit code in channel c of kv head h is v, read back bit by bit from the
  * planes (rows of W words).                                                 */

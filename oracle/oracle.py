@@ -54,6 +54,12 @@ def _load():
         lib.orc_read_prefixes.argtypes = [P, L, I, I, P, I, P]
         lib.orc_topk.argtypes = [P, I, L, L, I, I, P, P]
         lib.orc_append.argtypes = [P, L, I, I, L, L, L, P, L, P, P, P]
+        lib.orc_range_blocks.restype = L
+        lib.orc_range_blocks.argtypes = [L]
+        lib.orc_pack_blocked.argtypes = [P, L, I, I, L, L, P, P, P, L, P]
+        lib.orc_scan_blocked.argtypes = [P, P, P, L, L, I, I, P, P, I, P, L]
+        lib.orc_scan_blocked_at.argtypes = [P, P, P, L, L, I, I, P, P, I, P, L, P]
+        lib.orc_append_blocked.argtypes = [P, L, I, I, L, L, L, P, L, P, P, L, P]
         lib.orc_code_hist.argtypes = [P, L, I, I, L, P]
         lib.orc_depth_errors.argtypes = [P, I, I, P]
         lib.orc_plan_calibrated.argtypes = [P, I, I, I, P, P, P, P, P]
@@ -62,7 +68,8 @@ def _load():
         for f in ("orc_pack", "orc_plan", "orc_plan_fixed", "orc_plan_rd", "orc_plan_group",
                   "orc_scan", "orc_scan_at",
                   "orc_read_prefixes", "orc_topk", "orc_sparse_attention", "orc_append", "orc_code_hist", "orc_depth_errors",
-                  "orc_plan_calibrated", "orc_plan_calibrated_group"):
+                  "orc_plan_calibrated", "orc_plan_calibrated_group", "orc_pack_blocked",
+                  "orc_scan_blocked", "orc_scan_blocked_at", "orc_append_blocked"):
             getattr(lib, f).restype = I
         _lib = lib
     return _lib
@@ -289,3 +296,76 @@ def plan_calibrated_group(q, lo, hi, hist, budget) -> np.ndarray:
                                              _ptr(hist), _ptr(b), _ptr(out)),
            "plan_calibrated_group")
     return out
+
+
+# ---- per-block ranges (reading R22) -------------------------------------------
+RANGE_BLOCK = 2048
+
+
+def range_blocks(n: int) -> int:
+    return int(_load().orc_range_blocks(n))
+
+
+def pack_blocked(keys: np.ndarray, nbc=None):
+    """keys [n][hkv][d] -> dict(planes [hkv][d][4][W] uint32, lo/hi [hkv][d][nbc]
+    fp32 per 2048-key block, sigma2 [hkv][d] fp32 (pooled within-block))."""
+    k = np.ascontiguousarray(keys, dtype=np.float32)
+    n, hkv, d = k.shape
+    nb = range_blocks(n)
+    nbc = nb if nbc is None else nbc
+    W = plane_words(n)
+    planes = np.zeros((hkv, d, 4, W), np.uint32)
+    lo = np.zeros((hkv, d, nbc), np.float32)
+    hi = np.zeros((hkv, d, nbc), np.float32)
+    s2 = np.zeros((hkv, d), np.float32)
+    _check(_load().orc_pack_blocked(_ptr(k), n, hkv, d, hkv * d, d, _ptr(planes), _ptr(lo),
+                                    _ptr(hi), nbc, _ptr(s2)), "pack_blocked")
+    return {"planes": planes, "lo": lo, "hi": hi, "sigma2": s2}
+
+
+def scan_blocked(planes, lo, hi, n: int, q, plan_):
+    """Logits [hq][n] fp32 of a layer packed with per-block ranges lo/hi
+    [hkv][d][nbc]."""
+    planes = np.ascontiguousarray(planes, dtype=np.uint32)
+    lo = np.ascontiguousarray(lo, dtype=np.float32)
+    hi = np.ascontiguousarray(hi, dtype=np.float32)
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    plan_ = np.ascontiguousarray(plan_, dtype=np.uint8)
+    hkv, d, nbc = lo.shape
+    hq = q.shape[0]
+    out = np.zeros((hq, max(n, 1)), np.float32)
+    _check(_load().orc_scan_blocked(_ptr(planes), _ptr(lo), _ptr(hi), nbc, n, hkv, d, _ptr(q),
+                                    _ptr(plan_), hq, _ptr(out), out.shape[1]), "scan_blocked")
+    return out[:, :n]
+
+
+def scan_blocked_at(planes, lo, hi, n: int, q, plan_, keys):
+    planes = np.ascontiguousarray(planes, dtype=np.uint32)
+    lo = np.ascontiguousarray(lo, dtype=np.float32)
+    hi = np.ascontiguousarray(hi, dtype=np.float32)
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    plan_ = np.ascontiguousarray(plan_, dtype=np.uint8)
+    keys = np.ascontiguousarray(keys, dtype=np.int64)
+    hkv, d, nbc = lo.shape
+    hq = q.shape[0]
+    out = np.zeros((hq, keys.size), np.float32)
+    _check(_load().orc_scan_blocked_at(_ptr(planes), _ptr(lo), _ptr(hi), nbc, n, hkv, d,
+                                       _ptr(q), _ptr(plan_), hq, _ptr(keys), keys.size,
+                                       _ptr(out)), "scan_blocked_at")
+    return out
+
+
+def append_blocked(keys_new, n_old: int, planes, lo, hi):
+    """Append keys_new [m][hkv][d] as tokens n_old.. in place into planes
+    [hkv][d][4][W] and per-block ranges lo/hi [hkv][d][nbc] (reading R22);
+    returns the number of clamped values."""
+    k = np.ascontiguousarray(keys_new, dtype=np.float32)
+    m, hkv, d = k.shape
+    assert planes.flags.c_contiguous and planes.dtype == np.uint32
+    assert lo.flags.c_contiguous and hi.flags.c_contiguous
+    W = planes.shape[-1]
+    nbc = lo.shape[-1]
+    cnt = np.zeros(1, np.int64)
+    _check(_load().orc_append_blocked(_ptr(k), m, hkv, d, hkv * d, d, n_old, _ptr(planes), W,
+                                      _ptr(lo), _ptr(hi), nbc, _ptr(cnt)), "append_blocked")
+    return int(cnt[0])
