@@ -342,6 +342,73 @@ int32_t fathom_append(const void *keys, int32_t dtype, int64_t m, int32_t hkv,
                       const float *lo, const float *hi, uint32_t *clamped,
                       void *stream);
 
+/* ---- per-block ranges ------------------------------------------------------
+ * Explainer, deployment warnings item 3 (the bit planes ARE the stored 4-bit
+ * K: changing its quantisation must not force anything else to be rebuilt)
+ * and problem statement (long sessions that grow by one key per decode
+ * step).  The pages keep one range per channel; a session whose key ranges
+ * drift would then either clamp its later keys or re-quantise every stored
+ * code.  Reading taken here: the range of a channel is kept per block of
+ * FATHOM_RANGE_BLOCK = 2048 consecutive keys (one 64-word block of every
+ * plane row), so later blocks get ranges of their own and no stored code is
+ * ever re-quantised.  Planes keep the fathom_pack layout.
+ *
+ * lo, hi       device fp32[hkv][d][range_stride]: block b of channel c of kv
+ *              head h at [(h*d + c)*range_stride + b]; range_stride is a
+ *              capacity, fathom_range_blocks(n) <= range_stride <= 2^20.
+ *
+ * fathom_pack_blocked: each block's range is the min and max of its own keys
+ * (-0 stored as +0); its keys are coded with it exactly as fathom_pack codes
+ * a layer (delta_b = (hi_b - lo_b) * 1/16, code = min(15, floor((x - lo_b) /
+ * delta_b)), delta_b == 0 gives 0).  sigma2 (device fp32[hkv][d]) is the
+ * pooled within-block variance of the dequantised values:
+ *   sigma2 = fp32( sum over blocks in order of fp64(var_b * (n_b / n)) ),
+ *   var_b  = fp64((n_b*S2_b - S1_b^2) / n_b^2) * delta_b^2   (fp64 steps),
+ * with n_b the block's keys and S1_b, S2_b its code sums; a layer of one
+ * block gets fathom_pack's sigma2.  ws: fathom_pack_blocked_workspace_bytes.
+ * Other arguments as fathom_pack.  Outputs are bit-identical to the CPU
+ * definition.  Enqueues 3 kernels.
+ *
+ * fathom_append_blocked: as fathom_append, except that a block which holds no
+ * key before the call first takes the range of the block before it, widened
+ * to cover the keys the call puts in it (block 0: those keys' own min and
+ * max); a block that already holds keys keeps its range, and keys outside it
+ * are clamped and counted in `clamped`.  lo and hi are read and written.
+ * Enqueues 1 to 3 kernels (none when m == 0).
+ *
+ * fathom_scan_blocked: fathom_scan with key i reading lo_b, delta_b of its
+ * block b = i / 2048 in the reconstruction formula (no side stream);
+ * plane_words as fathom_session.plane_words (0: fathom_plane_words(n)).
+ * Accuracy |s - exact| <= 1e-5 * A_h, A_h = sum_c |q_c| * max over blocks of
+ * max(|lo_cb|, |hi_cb|).
+ *
+ * fathom_scan_topk_blocked: fathom_scan_topk over the per-block scan (same
+ * ranking, ties and padding; workspace from fathom_scan_topk_workspace_bytes).
+ */
+#define FATHOM_RANGE_BLOCK 2048
+int64_t fathom_range_blocks(int64_t n);
+int64_t fathom_pack_blocked_workspace_bytes(int64_t n, int32_t hkv, int32_t d);
+int32_t fathom_pack_blocked(const void *keys, int32_t dtype, int64_t n, int32_t hkv,
+                            int32_t d, int64_t stride_tok, int64_t stride_head,
+                            uint32_t *planes, float *lo, float *hi, int64_t range_stride,
+                            float *sigma2, void *ws, int64_t ws_bytes, void *stream);
+int32_t fathom_append_blocked(const void *keys, int32_t dtype, int64_t m, int32_t hkv,
+                              int32_t d, int64_t stride_tok, int64_t stride_head,
+                              int64_t n_old, uint32_t *planes, int64_t plane_words,
+                              float *lo, float *hi, int64_t range_stride,
+                              uint32_t *clamped, void *stream);
+int32_t fathom_scan_blocked(const uint32_t *planes, const float *lo, const float *hi,
+                            int64_t range_stride, int64_t n, int32_t hkv, int32_t d,
+                            const float *q, const uint8_t *plan, int32_t hq,
+                            int64_t plane_words, float *logits, int64_t ld_logits,
+                            void *stream);
+int32_t fathom_scan_topk_blocked(const uint32_t *planes, const float *lo, const float *hi,
+                                 int64_t range_stride, int64_t n, int32_t hkv, int32_t d,
+                                 const float *q, const uint8_t *plan, int32_t hq,
+                                 int64_t plane_words, int32_t group, int32_t k,
+                                 int32_t *idx, float *vals, void *ws, int64_t ws_bytes,
+                                 void *stream);
+
 /* ---- sparse attention over the selected keys -------------------------------
  * Explainer, problem statement: each generated token attends over the top k
  * of its n keys; the future-work list keeps V dense.  The pages do not lay

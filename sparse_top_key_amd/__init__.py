@@ -86,6 +86,16 @@ def lib():
             "fathom_scan_topk": (I32, [P, P, P, I64, I32, I32, P, P, I32, P, F, I32, I32, P, P,
                                        P, I64, P]),
             "fathom_scan_topk_batched": (I32, [P, I32, I32, I32, I32, I32, I32, P, I64, P]),
+            "fathom_range_blocks": (I64, [I64]),
+            "fathom_pack_blocked_workspace_bytes": (I64, [I64, I32, I32]),
+            "fathom_pack_blocked": (I32, [P, I32, I64, I32, I32, I64, I64, P, P, P, I64, P, P,
+                                          I64, P]),
+            "fathom_append_blocked": (I32, [P, I32, I64, I32, I32, I64, I64, I64, P, I64, P, P,
+                                            I64, P, P]),
+            "fathom_scan_blocked": (I32, [P, P, P, I64, I64, I32, I32, P, P, I32, I64, P, I64,
+                                          P]),
+            "fathom_scan_topk_blocked": (I32, [P, P, P, I64, I64, I32, I32, P, P, I32, I64, I32,
+                                               I32, P, P, P, I64, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -418,6 +428,106 @@ def append(keys: torch.Tensor, n_old: int, planes: torch.Tensor, lo: torch.Tenso
     _check(lib().fathom_append(_p(keys), dtype, m, hkv, d, keys.stride(0), keys.stride(1),
                                n_old, _p(planes), planes.shape[-1], _p(lo), _p(hi),
                                _p(clamped), _stream(lo.device)), "fathom_append")
+
+
+# ---- per-block ranges (one lo/hi per 2048-key block of a channel) ----------
+
+def range_blocks(n: int) -> int:
+    return int(lib().fathom_range_blocks(n))
+
+
+def pack_blocked(keys: torch.Tensor, capacity: Optional[int] = None,
+                 ws: Optional[torch.Tensor] = None) -> Packed:
+    """keys [n][hkv][d] -> Packed with lo, hi fp32 [hkv][d][R] (R = the range
+    blocks of `capacity` keys, default n) and planes [hkv][d][4][W] with room
+    for `capacity` keys (zeroed past n)."""
+    _require_gpu(keys)
+    n, hkv, d = keys.shape
+    if keys.stride(2) != 1:
+        raise FathomError("pack_blocked: channel stride must be 1")
+    dt = {torch.float16: F16, torch.float32: F32}.get(keys.dtype)
+    if dt is None:
+        raise FathomError("pack_blocked: keys must be fp16 or fp32")
+    dev = keys.device
+    cap = n if capacity is None else max(int(capacity), n)
+    R = max(range_blocks(cap), 1)
+    if cap == n:
+        planes = torch.empty((hkv, d, 4, plane_words(n)), dtype=torch.int32, device=dev)
+    else:
+        planes = torch.zeros((hkv, d, 4, plane_words(cap)), dtype=torch.int32, device=dev)
+    lo = torch.zeros((hkv, d, R), dtype=torch.float32, device=dev)
+    hi = torch.zeros_like(lo)
+    s2 = torch.empty((hkv, d), dtype=torch.float32, device=dev)
+    need = int(lib().fathom_pack_blocked_workspace_bytes(n, hkv, d)) if n > 0 else 0
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if cap == n:
+        _check(lib().fathom_pack_blocked(_p(keys), dt, n, hkv, d, keys.stride(0), keys.stride(1),
+                                         _p(planes), _p(lo), _p(hi), R, _p(s2), _p(ws),
+                                         ws.numel(), _stream(dev)), "fathom_pack_blocked")
+    else:
+        # pack into rows of plane_words(n), then place them in the capacity rows
+        tmp = torch.empty((hkv, d, 4, plane_words(n)), dtype=torch.int32, device=dev)
+        _check(lib().fathom_pack_blocked(_p(keys), dt, n, hkv, d, keys.stride(0), keys.stride(1),
+                                         _p(tmp), _p(lo), _p(hi), R, _p(s2), _p(ws),
+                                         ws.numel(), _stream(dev)), "fathom_pack_blocked")
+        planes[..., :tmp.shape[-1]] = tmp
+    return Packed(planes, lo, hi, s2, n)
+
+
+def append_blocked(keys: torch.Tensor, n_old: int, planes: torch.Tensor, lo: torch.Tensor,
+                   hi: torch.Tensor, clamped: Optional[torch.Tensor] = None) -> None:
+    """append() for per-block ranges: lo, hi [hkv][d][R] are read and written
+    (the blocks the call starts get their ranges first)."""
+    _require_gpu(keys, planes, lo)
+    m, hkv, d = keys.shape
+    if keys.stride(2) != 1:
+        raise FathomError("channel stride of keys must be 1")
+    dtype = {torch.float16: F16, torch.float32: F32}.get(keys.dtype)
+    if dtype is None:
+        raise FathomError("keys must be float16 or float32")
+    _check(lib().fathom_append_blocked(_p(keys), dtype, m, hkv, d, keys.stride(0),
+                                       keys.stride(1), n_old, _p(planes), planes.shape[-1],
+                                       _p(lo), _p(hi), lo.shape[-1], _p(clamped),
+                                       _stream(lo.device)), "fathom_append_blocked")
+
+
+def scan_blocked(planes: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor, n: int,
+                 q: torch.Tensor, plan_: torch.Tensor,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """scan() with per-block ranges lo, hi [hkv][d][R] -> logits [hq][n]."""
+    _require_gpu(planes, lo, q, plan_)
+    hkv, d, R = lo.shape
+    hq = q.shape[0]
+    if out is None:
+        out = torch.empty((hq, max(n, 1)), dtype=torch.float32, device=q.device)
+    _check(lib().fathom_scan_blocked(_p(planes), _p(lo), _p(hi), R, n, hkv, d, _p(q),
+                                     _p(plan_), hq, planes.shape[-1], _p(out), out.stride(0),
+                                     _stream(q.device)), "fathom_scan_blocked")
+    return out[:, :n]
+
+
+def scan_topk_blocked(planes: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor, n: int,
+                      q: torch.Tensor, plan_: torch.Tensor, k: int, group: int = 1,
+                      ws: Optional[torch.Tensor] = None, idx=None, vals=None):
+    """scan_topk() with per-block ranges lo, hi [hkv][d][R]."""
+    _require_gpu(planes, lo, q, plan_)
+    hkv, d, R = lo.shape
+    hq = q.shape[0]
+    ro = hq // group
+    dev = q.device
+    if idx is None:
+        idx = torch.empty((ro, k), dtype=torch.int32, device=dev)
+    if vals is None:
+        vals = torch.empty((ro, k), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(max(scan_topk_workspace_bytes([n], hkv, hq, group, k), 1),
+                         dtype=torch.uint8, device=dev)
+    _check(lib().fathom_scan_topk_blocked(_p(planes), _p(lo), _p(hi), R, n, hkv, d, _p(q),
+                                          _p(plan_), hq, planes.shape[-1], group, k, _p(idx),
+                                          _p(vals), _p(ws), ws.numel(), _stream(dev)),
+           "fathom_scan_topk_blocked")
+    return idx, vals
 
 
 def alloc_planes(capacity: int, hkv: int, d: int = D, device="cuda", pin_memory=False):

@@ -1,5 +1,6 @@
 // Exported C ABI of libfathom (declared in include/fathom.h): argument
 // validation on the host, then kernel launches on the caller's stream.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -91,8 +92,49 @@ int32_t fathom_pack(const void *keys, int32_t dtype, int64_t n, int32_t hkv, int
   REQUIRE(ws && ws_bytes >= need, FATHOM_ERR_WORKSPACE,
           "fathom_pack: workspace of %lld bytes needed (got %lld)", (long long)need,
           (long long)ws_bytes);
-  return launch_pack(keys, dtype, n, hkv, stride_tok, stride_head, planes, lo, hi, sigma2,
+  return launch_pack(keys, dtype, n, hkv, stride_tok, stride_head, planes, lo, hi, 0, sigma2,
                      ws, as_stream(stream));
+}
+
+int64_t fathom_range_blocks(int64_t n) {
+  return n < 0 ? 0 : (n + kBlockKeys - 1) / kBlockKeys;
+}
+
+int64_t fathom_pack_blocked_workspace_bytes(int64_t n, int32_t hkv, int32_t d) {
+  if (n < 1 || hkv < 1 || d != kD) return 0;
+  return pack_blocked_workspace_bytes(n, hkv);
+}
+
+// Range rows of per-block layers: at least the blocks of n keys, at most 2^20
+// (the blocks of 2^31 keys).
+static int32_t check_range_stride(int64_t rs, int64_t n, const char *who) {
+  REQUIRE(rs >= fathom_range_blocks(n) && rs >= 1 && rs <= ((int64_t)1 << 20),
+          FATHOM_ERR_INVALID_ARG, "%s: range_stride (%lld) must be in [%lld, 2^20]", who,
+          (long long)rs, (long long)std::max<int64_t>(1, fathom_range_blocks(n)));
+  return FATHOM_OK;
+}
+
+int32_t fathom_pack_blocked(const void *keys, int32_t dtype, int64_t n, int32_t hkv, int32_t d,
+                            int64_t stride_tok, int64_t stride_head, uint32_t *planes,
+                            float *lo, float *hi, int64_t range_stride, float *sigma2,
+                            void *ws, int64_t ws_bytes, void *stream) {
+  REQUIRE(keys && planes && lo && hi && sigma2, FATHOM_ERR_INVALID_ARG,
+          "fathom_pack_blocked: null pointer");
+  REQUIRE(dtype == FATHOM_F16 || dtype == FATHOM_F32, FATHOM_ERR_INVALID_ARG,
+          "fathom_pack_blocked: dtype must be FATHOM_F16 or FATHOM_F32 (got %d)", dtype);
+  REQUIRE(n >= 1 && n <= ((int64_t)1 << 31), FATHOM_ERR_INVALID_ARG,
+          "fathom_pack_blocked: n must be in [1, 2^31] (got %lld)", (long long)n);
+  REQUIRE(hkv >= 1, FATHOM_ERR_INVALID_ARG, "fathom_pack_blocked: hkv must be >= 1");
+  if (int32_t rc = check_d(d)) return rc;
+  REQUIRE(stride_tok >= 0 && stride_head >= 0, FATHOM_ERR_INVALID_ARG,
+          "fathom_pack_blocked: strides must be non-negative");
+  if (int32_t rc = check_range_stride(range_stride, n, "fathom_pack_blocked")) return rc;
+  const int64_t need = pack_blocked_workspace_bytes(n, hkv);
+  REQUIRE(ws && ws_bytes >= need, FATHOM_ERR_WORKSPACE,
+          "fathom_pack_blocked: workspace of %lld bytes needed (got %lld)", (long long)need,
+          (long long)ws_bytes);
+  return launch_pack(keys, dtype, n, hkv, stride_tok, stride_head, planes, lo, hi,
+                     range_stride, sigma2, ws, as_stream(stream));
 }
 
 int32_t fathom_plan(const float *q, int32_t hq, int32_t hkv, int32_t d,
@@ -156,7 +198,35 @@ int32_t fathom_append(const void *keys, int32_t dtype, int64_t m, int32_t hkv, i
           (long long)plane_words_, (long long)plane_words(n_old + m));
   if (m == 0) return FATHOM_OK;
   return launch_append(keys, dtype, m, hkv, stride_tok, stride_head, n_old, planes,
-                       plane_words_, lo, hi, clamped, as_stream(stream));
+                       plane_words_, const_cast<float *>(lo), const_cast<float *>(hi), 0,
+                       clamped, as_stream(stream));
+}
+
+int32_t fathom_append_blocked(const void *keys, int32_t dtype, int64_t m, int32_t hkv,
+                              int32_t d, int64_t stride_tok, int64_t stride_head,
+                              int64_t n_old, uint32_t *planes, int64_t plane_words_,
+                              float *lo, float *hi, int64_t range_stride, uint32_t *clamped,
+                              void *stream) {
+  REQUIRE(planes && lo && hi && (keys || m == 0), FATHOM_ERR_INVALID_ARG,
+          "fathom_append_blocked: null pointer");
+  REQUIRE(dtype == FATHOM_F16 || dtype == FATHOM_F32, FATHOM_ERR_INVALID_ARG,
+          "fathom_append_blocked: dtype must be FATHOM_F16 or FATHOM_F32 (got %d)", dtype);
+  REQUIRE(hkv >= 1, FATHOM_ERR_INVALID_ARG, "fathom_append_blocked: hkv must be >= 1");
+  if (int32_t rc = check_d(d)) return rc;
+  REQUIRE(m >= 0 && n_old >= 0 && n_old + m <= ((int64_t)1 << 31), FATHOM_ERR_INVALID_ARG,
+          "fathom_append_blocked: need m >= 0, n_old >= 0, n_old + m <= 2^31");
+  REQUIRE(stride_tok >= 0 && stride_head >= 0, FATHOM_ERR_INVALID_ARG,
+          "fathom_append_blocked: strides must be non-negative");
+  REQUIRE(plane_words_ >= plane_words(n_old + m) && plane_words_ % 64 == 0 &&
+              plane_words_ <= ((int64_t)1 << 26),
+          FATHOM_ERR_INVALID_ARG,
+          "fathom_append_blocked: plane_words (%lld) must be a multiple of 64 in [%lld, 2^26]",
+          (long long)plane_words_, (long long)plane_words(n_old + m));
+  if (int32_t rc = check_range_stride(range_stride, n_old + m, "fathom_append_blocked"))
+    return rc;
+  if (m == 0) return FATHOM_OK;
+  return launch_append(keys, dtype, m, hkv, stride_tok, stride_head, n_old, planes,
+                       plane_words_, lo, hi, range_stride, clamped, as_stream(stream));
 }
 
 int64_t fathom_attention_workspace_bytes(int32_t hq, int32_t k) {
@@ -328,6 +398,31 @@ int32_t fathom_scan(const uint32_t *planes, const float *lo, const float *hi, in
   return launch_scan(&ss, 1, hkv, hq, as_stream(stream));
 }
 
+int32_t fathom_scan_blocked(const uint32_t *planes, const float *lo, const float *hi,
+                            int64_t range_stride, int64_t n, int32_t hkv, int32_t d,
+                            const float *q, const uint8_t *plan, int32_t hq,
+                            int64_t plane_words_, float *logits, int64_t ld_logits,
+                            void *stream) {
+  if (int32_t rc = check_heads(hq, hkv)) return rc;
+  if (int32_t rc = check_d(d)) return rc;
+  fathom_session s{};
+  s.planes = planes;
+  s.lo = lo;
+  s.hi = hi;
+  s.n = n;
+  s.q = q;
+  s.plan = plan;
+  s.logits = logits;
+  s.ld_logits = ld_logits;
+  s.plane_words = plane_words_;
+  if (int32_t rc = check_scan_session(s, hq, "fathom_scan_blocked")) return rc;
+  if (int32_t rc = check_range_stride(range_stride, n, "fathom_scan_blocked")) return rc;
+  if (n == 0) return FATHOM_OK;
+  ScanSession ss = to_scan(s);
+  ss.rs = range_stride;
+  return launch_scan(&ss, 1, hkv, hq, as_stream(stream));
+}
+
 int32_t fathom_scan_batched(const fathom_session *sessions, int32_t n_sessions, int32_t hkv,
                             int32_t d, int32_t hq, void *stream) {
   REQUIRE(sessions, FATHOM_ERR_INVALID_ARG, "fathom_scan_batched: null sessions");
@@ -444,7 +539,8 @@ static int32_t check_scan_topk_session(const fathom_session &s, const char *who)
 
 static int32_t scan_topk_common(const fathom_session *sessions, int32_t n_sessions,
                                 int32_t hkv, int32_t d, int32_t hq, int32_t group, int32_t k,
-                                void *ws, int64_t ws_bytes, void *stream, const char *who) {
+                                void *ws, int64_t ws_bytes, void *stream, const char *who,
+                                int64_t rs = 0) {
   if (int32_t rc = check_heads(hq, hkv)) return rc;
   if (int32_t rc = check_d(d)) return rc;
   if (int32_t rc = check_topk_common(hq, group, k, who)) return rc;
@@ -463,6 +559,7 @@ static int32_t scan_topk_common(const fathom_session *sessions, int32_t n_sessio
     ss[i].cand = nullptr;
     ss[i].seg_cnt = nullptr;
     ss[i].redo = nullptr;
+    ss[i].rs = rs;
     idx[i] = sessions[i].idx;
     vals[i] = sessions[i].vals;
     ns[i] = sessions[i].n;
@@ -492,6 +589,26 @@ int32_t fathom_scan_topk(const uint32_t *planes, const float *lo, const float *h
   s.vals = vals;
   return scan_topk_common(&s, 1, hkv, d, hq, group, k, ws, ws_bytes, stream,
                           "fathom_scan_topk");
+}
+
+int32_t fathom_scan_topk_blocked(const uint32_t *planes, const float *lo, const float *hi,
+                                 int64_t range_stride, int64_t n, int32_t hkv, int32_t d,
+                                 const float *q, const uint8_t *plan, int32_t hq,
+                                 int64_t plane_words_, int32_t group, int32_t k, int32_t *idx,
+                                 float *vals, void *ws, int64_t ws_bytes, void *stream) {
+  if (int32_t rc = check_range_stride(range_stride, n, "fathom_scan_topk_blocked")) return rc;
+  fathom_session s{};
+  s.planes = planes;
+  s.lo = lo;
+  s.hi = hi;
+  s.n = n;
+  s.q = q;
+  s.plan = plan;
+  s.idx = idx;
+  s.vals = vals;
+  s.plane_words = plane_words_;
+  return scan_topk_common(&s, 1, hkv, d, hq, group, k, ws, ws_bytes, stream,
+                          "fathom_scan_topk_blocked", range_stride);
 }
 
 int32_t fathom_scan_topk_batched(const fathom_session *sessions, int32_t n_sessions,

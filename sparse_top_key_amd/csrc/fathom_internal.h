@@ -61,10 +61,13 @@ int64_t topk_ws_bytes(int64_t out_rows, int64_t redo_slots);
 TopkWs topk_ws_carve(void *ws, int64_t out_rows, int64_t redo_slots);
 
 // ---- pack -------------------------------------------------------------------
+// rs: 0 for one range per channel (lo, hi [hkv][d]); > 0 for one range per
+// 2048-key block (lo, hi [hkv][d][rs], rs >= the number of blocks).
 int64_t pack_workspace_bytes(int64_t n, int32_t hkv);
+int64_t pack_blocked_workspace_bytes(int64_t n, int32_t hkv);
 int32_t launch_pack(const void *keys, int32_t dtype, int64_t n, int32_t hkv,
                     int64_t stride_tok, int64_t stride_head, uint32_t *planes,
-                    float *lo, float *hi, float *sigma2, void *ws,
+                    float *lo, float *hi, int64_t rs, float *sigma2, void *ws,
                     hipStream_t s);
 
 // ---- plan -------------------------------------------------------------------
@@ -89,9 +92,10 @@ int32_t launch_plan_calibrated(const float *q, int32_t hq, int32_t hkv, const fl
                                hipStream_t s);
 
 // ---- append -------------------------------------------------------------------
+// rs > 0: per-block ranges; the blocks the call starts get theirs first.
 int32_t launch_append(const void *keys, int32_t dtype, int64_t m, int32_t hkv,
                       int64_t stride_tok, int64_t stride_head, int64_t n_old,
-                      uint32_t *planes, int64_t W, const float *lo, const float *hi,
+                      uint32_t *planes, int64_t W, float *lo, float *hi, int64_t rs,
                       uint32_t *clamped, hipStream_t s);
 
 // ---- sparse attention -------------------------------------------------------
@@ -124,6 +128,7 @@ struct ScanSession {
   int32_t table_mode;     // ScanTable: what the scan does with them
   int32_t residency;      // planes: 0 unknown (queried), 1 device, 2 pinned host
   int64_t W;              // plane row length in words; 0: plane_words(n)
+  int64_t rs;             // 0: lo, hi [hkv][d]; > 0: per 2048-key block, [hkv][d][rs]
 };
 inline int64_t sess_words(const ScanSession &s) { return s.W > 0 ? s.W : plane_words(s.n); }
 // Slot tables (matrix-core scan): built in each block (kTableNone), built and

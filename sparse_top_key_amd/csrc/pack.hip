@@ -14,6 +14,12 @@
 //
 // Keys whose rows are 16-byte aligned take the vector kernels (16-byte loads,
 // four key rows per wave instruction); other strides take the scalar ones.
+//
+// Per-block ranges (lo, hi kept per 2048-key block of a channel, for long
+// sessions whose key ranges drift; deployment warnings item 3 and the problem
+// statement): the min/max kernels run with one chunk per block and store the
+// block's range directly, the planes kernels quantise each block with its own
+// range, and pack_sigma_blocked pools the blocks' variances in block order.
 #include <hip/hip_fp16.h>
 
 #include "fathom_internal.h"
@@ -30,10 +36,25 @@ __device__ inline float load_key(const __half *p) { return __half2float(*p); }
 __device__ inline float load_key(const float *p) { return *p; }
 
 // Partial min/max of chunk blockIdx.x for kv head blockIdx.y.
+// Per-block ranges (rs > 0, chunk = one 2048-key block): the chunk's min and
+// max are block blockIdx.x's range, stored (+0 for a -0 end) into
+// blo/bhi[h][c][blockIdx.x] instead of part.
+__device__ __forceinline__ void store_minmax(float2 *part, float *blo, float *bhi, int64_t rs,
+                                             int hkv, int h, int c, float mn, float mx) {
+  if (rs == 0) {
+    part[((int64_t)blockIdx.x * hkv + h) * kD + c] = make_float2(mn, mx);
+  } else {
+    const int64_t o = ((int64_t)h * kD + c) * rs + blockIdx.x;
+    blo[o] = __fadd_rn(mn, 0.0f);
+    bhi[o] = __fadd_rn(mx, 0.0f);
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kMinmaxThreads) void pack_minmax_kernel(
     const T *__restrict__ keys, int64_t n, int64_t stride_tok,
-    int64_t stride_head, int64_t chunk, float2 *__restrict__ part) {
+    int64_t stride_head, int64_t chunk, float2 *__restrict__ part, float *__restrict__ blo,
+    float *__restrict__ bhi, int64_t rs) {
   const int h = blockIdx.y;
   const int hkv = gridDim.y;
   const int c = threadIdx.x % kD;
@@ -54,7 +75,7 @@ __global__ __launch_bounds__(kMinmaxThreads) void pack_minmax_kernel(
     float2 o = red[threadIdx.x + kD];
     mn = fminf(mn, o.x);
     mx = fmaxf(mx, o.y);
-    part[((int64_t)blockIdx.x * hkv + h) * kD + c] = make_float2(mn, mx);
+    store_minmax(part, blo, bhi, rs, hkv, h, c, mn, mx);
   }
 }
 
@@ -89,6 +110,12 @@ __global__ __launch_bounds__(kReduceThreads) void pack_range_kernel(
   }
 }
 
+// Range of channel c of kv head h for 2048-key block b: lo/hi are [hkv][d]
+// (rs == 0) or [hkv][d][rs] per block.
+__device__ __forceinline__ float range_at(const float *a, int h, int c, int64_t rs, int64_t b) {
+  return rs == 0 ? a[h * kD + c] : a[((int64_t)h * kD + c) * rs + b];
+}
+
 __device__ inline int quantise(float x, float lo, float delta) {
   if (delta == 0.0f) return 0;
   float y = __fdiv_rn(__fsub_rn(x, lo), delta);
@@ -104,7 +131,7 @@ template <typename T>
 __global__ __launch_bounds__(kPlaneThreads) void pack_planes_kernel(
     const T *__restrict__ keys, int64_t n, int64_t stride_tok,
     int64_t stride_head, int64_t W, const float *__restrict__ lo,
-    const float *__restrict__ hi, uint32_t *__restrict__ planes,
+    const float *__restrict__ hi, int64_t rs, uint32_t *__restrict__ planes,
     int2 *__restrict__ sums) {
   __shared__ float tile[kSubTile * kLdsPitch];
   const int h = blockIdx.y;
@@ -115,8 +142,9 @@ __global__ __launch_bounds__(kPlaneThreads) void pack_planes_kernel(
 
   // lane cc of this wave keeps channel (wave*32 + cc)'s range and sums
   const int my_c = wave * 32 + (lane & 31);
-  const float my_lo = lo[h * kD + my_c];
-  const float my_delta = __fmul_rn(__fsub_rn(hi[h * kD + my_c], my_lo), 0.0625f);
+  const float my_lo = range_at(lo, h, my_c, rs, blockIdx.x);
+  const float my_delta =
+      __fmul_rn(__fsub_rn(range_at(hi, h, my_c, rs, blockIdx.x), my_lo), 0.0625f);
   int my_s1 = 0, my_s2 = 0;
 
   for (int sub = 0; sub < kBlockKeys / kSubTile; ++sub) {
@@ -212,7 +240,8 @@ __device__ __forceinline__ void unpack_row8<float>(const uint4 (&v)[2], float (&
 template <typename T>
 __global__ __launch_bounds__(kVecThreads) void pack_minmax_vec_kernel(
     const T *__restrict__ keys, int64_t n, int64_t stride_tok, int64_t stride_head,
-    int64_t chunk, float2 *__restrict__ part) {
+    int64_t chunk, float2 *__restrict__ part, float *__restrict__ blo, float *__restrict__ bhi,
+    int64_t rs) {
   __shared__ float s_mn[kVecRows][kD + 1], s_mx[kVecRows][kD + 1];
   const int h = blockIdx.y, hkv = gridDim.y;
   const int r = threadIdx.x >> 4, j = threadIdx.x & 15;
@@ -267,7 +296,7 @@ __global__ __launch_bounds__(kVecThreads) void pack_minmax_vec_kernel(
       a = fminf(a, s_mn[q][c]);
       b = fmaxf(b, s_mx[q][c]);
     }
-    part[((int64_t)blockIdx.x * hkv + h) * kD + c] = make_float2(a, b);
+    store_minmax(part, blo, bhi, rs, hkv, h, c, a, b);
   }
 }
 
@@ -341,7 +370,7 @@ template <typename T>
 __global__ __launch_bounds__(kVecThreads) void pack_planes_vec_kernel(
     const T *__restrict__ keys, int64_t n, int64_t stride_tok, int64_t stride_head,
     int64_t W, int32_t hkv, const float *__restrict__ lo, const float *__restrict__ hi,
-    uint32_t *__restrict__ planes, int2 *__restrict__ sums) {
+    int64_t rs, uint32_t *__restrict__ planes, int2 *__restrict__ sums) {
   constexpr int kGroups = 4;                      // 8-channel groups per quarter
   constexpr int kRowsPerStep = kVecThreads / kGroups;  // 64
   constexpr int kSteps = kBlockKeys / kRowsPerStep;    // 32
@@ -368,12 +397,13 @@ __global__ __launch_bounds__(kVecThreads) void pack_planes_vec_kernel(
   const int cbase = 32 * Q + 8 * j;         // this thread's staging channels
   const T *base = keys + (int64_t)h * stride_head + cbase;
 
-  float clo[8], crec[8];
+  float clo[8], cdel[8], crec[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    const float l = lo[h * kD + cbase + c];
+    const float l = range_at(lo, h, cbase + c, rs, tile);
     clo[c] = l;
-    crec[c] = __fdiv_rn(1.0f, __fmul_rn(__fsub_rn(hi[h * kD + cbase + c], l), 0.0625f));
+    cdel[c] = __fmul_rn(__fsub_rn(range_at(hi, h, cbase + c, rs, tile), l), 0.0625f);
+    crec[c] = __fdiv_rn(1.0f, cdel[c]);
   }
 
   auto load_batch = [&](int bt, uint4 (&v)[kBatch][2]) {
@@ -409,10 +439,7 @@ __global__ __launch_bounds__(kVecThreads) void pack_planes_vec_kernel(
       if (exact) {
 #pragma unroll
         for (int c = 0; c < 8; ++c)
-          if (code[c] < 0) {
-            const float l = clo[c];
-            code[c] = quantise(x[c], l, __fmul_rn(__fsub_rn(hi[h * kD + cbase + c], l), 0.0625f));
-          }
+          if (code[c] < 0) code[c] = quantise(x[c], clo[c], cdel[c]);
       }
       const int key = (bt * kBatch + u) * kRowsPerStep + jr;
       uint32_t w = 0;
@@ -501,6 +528,31 @@ __global__ __launch_bounds__(kReduceThreads) void pack_sigma_kernel(
   sigma2[h * kD + c] = (float)__dmul_rn(var_code, dd);
 }
 
+// Per-block ranges: one thread per channel pools the blocks' variances in
+// block order, sigma2 = fp32(sum_b fp64(var_b * (n_b / n))), var_b =
+// Var(code) * delta_b^2 of block b from its exact integer code sums (the
+// expression of pack_sigma for one block).  Each step is one correctly
+// rounded fp64 operation, so the result is the CPU definition's bit for bit.
+__global__ __launch_bounds__(kD) void pack_sigma_blocked_kernel(
+    const int2 *__restrict__ sums, int32_t nblocks, int32_t hkv, int64_t n,
+    const float *__restrict__ lo, const float *__restrict__ hi, int64_t rs,
+    float *__restrict__ sigma2) {
+  const int h = blockIdx.x, c = threadIdx.x;
+  const float *lrow = lo + ((int64_t)h * kD + c) * rs;
+  const float *hrow = hi + ((int64_t)h * kD + c) * rs;
+  double acc = 0.0;
+  for (int32_t b = 0; b < nblocks; ++b) {
+    const int2 v = sums[((int64_t)b * hkv + h) * kD + c];
+    const int64_t nb = min((int64_t)kBlockKeys, n - (int64_t)b * kBlockKeys);
+    const float delta = __fmul_rn(__fsub_rn(hrow[b], lrow[b]), 0.0625f);
+    const int64_t num = nb * (int64_t)v.y - (int64_t)v.x * (int64_t)v.x;
+    const double var_code = __ddiv_rn((double)num, __dmul_rn((double)nb, (double)nb));
+    const double var = __dmul_rn(var_code, __dmul_rn((double)delta, (double)delta));
+    acc = __dadd_rn(acc, __dmul_rn(var, __ddiv_rn((double)nb, (double)n)));
+  }
+  sigma2[h * kD + c] = (float)acc;
+}
+
 struct PackLayout {
   int64_t chunk;
   int32_t nparts;
@@ -523,11 +575,22 @@ PackLayout pack_layout(int64_t n, int32_t hkv) {
   return L;
 }
 
+// Workspace of the per-block pack: the blocks' code sums only (the min/max
+// kernels store the ranges themselves).
+int64_t pack_blocked_ws(int64_t n, int32_t hkv) {
+  return plane_words(n) / 64 * hkv * kD * (int64_t)sizeof(int2);
+}
+
 template <typename T>
 int32_t launch_pack_t(const T *keys, int64_t n, int32_t hkv, int64_t stride_tok,
                       int64_t stride_head, uint32_t *planes, float *lo,
-                      float *hi, float *sigma2, void *ws, hipStream_t s) {
-  const PackLayout L = pack_layout(n, hkv);
+                      float *hi, int64_t rs, float *sigma2, void *ws, hipStream_t s) {
+  PackLayout L = pack_layout(n, hkv);
+  if (rs > 0) {  // one min/max chunk per 2048-key block, no partials
+    L.chunk = kBlockKeys;
+    L.nparts = L.nblocks;
+    L.part_bytes = 0;
+  }
   float2 *part = reinterpret_cast<float2 *>(ws);
   int2 *sums = reinterpret_cast<int2 *>(static_cast<char *>(ws) + L.part_bytes);
   const int64_t W = plane_words(n);
@@ -539,21 +602,26 @@ int32_t launch_pack_t(const T *keys, int64_t n, int32_t hkv, int64_t stride_tok,
                    stride_head % kAlign == 0 && W * 4 * kPlanes * kD <= INT32_MAX;
   if (vec)
     hipLaunchKernelGGL(pack_minmax_vec_kernel<T>, dim3(L.nparts, hkv), dim3(kVecThreads), 0, s,
-                       keys, n, stride_tok, stride_head, L.chunk, part);
+                       keys, n, stride_tok, stride_head, L.chunk, part, lo, hi, rs);
   else
     hipLaunchKernelGGL(pack_minmax_kernel<T>, dim3(L.nparts, hkv), dim3(kMinmaxThreads),
-                       0, s, keys, n, stride_tok, stride_head, L.chunk, part);
-  hipLaunchKernelGGL(pack_range_kernel, dim3(hkv), dim3(kReduceThreads), 0, s, part, L.nparts,
-                     hkv, lo, hi);
+                       0, s, keys, n, stride_tok, stride_head, L.chunk, part, lo, hi, rs);
+  if (rs == 0)
+    hipLaunchKernelGGL(pack_range_kernel, dim3(hkv), dim3(kReduceThreads), 0, s, part,
+                       L.nparts, hkv, lo, hi);
   if (vec)
     hipLaunchKernelGGL(pack_planes_vec_kernel<T>,
                        dim3((unsigned)(((int64_t)L.nblocks * hkv + 7) / 8 * 32)), dim3(kVecThreads),
-                       0, s, keys, n, stride_tok, stride_head, W, hkv, lo, hi, planes, sums);
+                       0, s, keys, n, stride_tok, stride_head, W, hkv, lo, hi, rs, planes, sums);
   else
     hipLaunchKernelGGL(pack_planes_kernel<T>, dim3(L.nblocks, hkv), dim3(kPlaneThreads),
-                       0, s, keys, n, stride_tok, stride_head, W, lo, hi, planes, sums);
-  hipLaunchKernelGGL(pack_sigma_kernel, dim3(hkv), dim3(kReduceThreads), 0, s, sums,
-                     L.nblocks, hkv, n, lo, hi, sigma2);
+                       0, s, keys, n, stride_tok, stride_head, W, lo, hi, rs, planes, sums);
+  if (rs == 0)
+    hipLaunchKernelGGL(pack_sigma_kernel, dim3(hkv), dim3(kReduceThreads), 0, s, sums,
+                       L.nblocks, hkv, n, lo, hi, sigma2);
+  else
+    hipLaunchKernelGGL(pack_sigma_blocked_kernel, dim3(hkv), dim3(kD), 0, s, sums, L.nblocks,
+                       hkv, n, lo, hi, rs, sigma2);
   return hip_fail(hipGetLastError(), "pack launch");
 }
 
@@ -564,14 +632,16 @@ int64_t pack_workspace_bytes(int64_t n, int32_t hkv) {
   return L.part_bytes + L.sums_bytes;
 }
 
+int64_t pack_blocked_workspace_bytes(int64_t n, int32_t hkv) { return pack_blocked_ws(n, hkv); }
+
 int32_t launch_pack(const void *keys, int32_t dtype, int64_t n, int32_t hkv,
                     int64_t stride_tok, int64_t stride_head, uint32_t *planes,
-                    float *lo, float *hi, float *sigma2, void *ws, hipStream_t s) {
+                    float *lo, float *hi, int64_t rs, float *sigma2, void *ws, hipStream_t s) {
   if (dtype == FATHOM_F16)
     return launch_pack_t(static_cast<const __half *>(keys), n, hkv, stride_tok,
-                         stride_head, planes, lo, hi, sigma2, ws, s);
+                         stride_head, planes, lo, hi, rs, sigma2, ws, s);
   return launch_pack_t(static_cast<const float *>(keys), n, hkv, stride_tok,
-                       stride_head, planes, lo, hi, sigma2, ws, s);
+                       stride_head, planes, lo, hi, rs, sigma2, ws, s);
 }
 
 }  // namespace fathom

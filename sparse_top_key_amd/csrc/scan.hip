@@ -31,6 +31,7 @@
 //    per channel read, so its rounding error is bounded by
 //    (terms + 1) * 2^-24 * sum|terms|, well inside 1e-5 * A_h.
 #include <climits>
+#include <type_traits>
 
 #include "fathom_internal.h"
 
@@ -68,6 +69,7 @@ struct ScanSess {
   int32_t seg_cap;         // candidate words per (row, block) segment
   uint8_t *table;          // slot records of the session, or null
   int32_t table_mode;      // ScanTable
+  int64_t rs;              // 0: lo, hi [hkv][d]; > 0: per 2048-key block, [hkv][d][rs]
 };
 
 struct ScanArgs {
@@ -220,7 +222,10 @@ __device__ __forceinline__ int memb_class(int memb) {
 // The slot table of one (session, kv head) and the GH query heads from
 // head_base.  Every step is parallel: per-channel terms in registers, C_h by
 // wave shuffles in a fixed fp64 order, slot ranks by counting ballots per
-// membership class, the per-head max |gamma| by LDS atomics.
+// membership class, the per-head max |gamma| by LDS atomics.  Per-block
+// ranges (S.rs > 0): the table is built with delta = 1 and lo = 0, so that
+// gam holds q_hc for the heads using the slot (each scan block then forms
+// its own gamma and C_h per 2048-key block).
 template <int GH>
 __device__ void build_slot_table(SlotTable<GH> &T, SlotScratch<GH> &X, KScanSess &S, int g,
                                  int head_base) {
@@ -228,8 +233,9 @@ __device__ void build_slot_table(SlotTable<GH> &T, SlotScratch<GH> &X, KScanSess
   const int lane = tid & 63;
   if (tid < kD) {
     const int c = tid;
-    const float lo = S.lo[g * kD + c];
-    const float hi = S.hi[g * kD + c];
+    const bool unit = S.rs > 0;
+    const float lo = unit ? 0.0f : S.lo[g * kD + c];
+    const float hi = unit ? 16.0f : S.hi[g * kD + c];
     int t[GH];
     float q[GH];
 #pragma unroll
@@ -372,7 +378,50 @@ __device__ __forceinline__ BlockWork block_work(const ScanArgs &) {
   return w;
 }
 
-template <int GH, int AUX>
+// Per-block ranges (BLK): a wave's 2048 keys are one range block b, and the
+// wave forms that block's weights gamma = q_hc * delta_cb for every slot and
+// C_h,b (the same fp64 butterfly as the slot table) before scanning it.
+template <int GH>
+struct BlockWeights {
+  float gam[kScanThreads / 64][kMaxSlots][GH];
+  float delta[kScanThreads / 64][kD];
+};
+
+template <int GH>
+__device__ __forceinline__ void block_weights(BlockWeights<GH> &Wt, const SlotTable<GH> &T,
+                                              const SlotScratch<GH> &X, KScanSess &S, int g,
+                                              int64_t b, int wave, int lane, float (&C)[GH]) {
+  const int64_t r0 = (int64_t)g * kD * S.rs + b;
+  const float l0 = S.lo[r0 + (int64_t)lane * S.rs], l1 = S.lo[r0 + (int64_t)(lane + 64) * S.rs];
+  const float d0 = __fmul_rn(__fsub_rn(S.hi[r0 + (int64_t)lane * S.rs], l0), 0.0625f);
+  const float d1 = __fmul_rn(__fsub_rn(S.hi[r0 + (int64_t)(lane + 64) * S.rs], l1), 0.0625f);
+  Wt.delta[wave][lane] = d0;
+  Wt.delta[wave][lane + 64] = d1;
+#pragma unroll
+  for (int j = 0; j < GH; ++j) {
+    const int t0 = X.t[j][lane], t1 = X.t[j][lane + 64];
+    double v0 = (double)X.q[j][lane] *
+                ((double)l0 + (double)d0 * (double)(1 << (4 - t0)) * 0.5);
+    double v1 = (double)X.q[j][lane + 64] *
+                ((double)l1 + (double)d1 * (double)(1 << (4 - t1)) * 0.5);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      v0 = __dadd_rn(v0, __shfl_xor(v0, off));
+      v1 = __dadd_rn(v1, __shfl_xor(v1, off));
+    }
+    C[j] = (float)__dadd_rn(v0, v1);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's deltas are stored
+  const int nslots8 = ((T.nslots + 7) >> 3) * 8;
+  for (int e = lane; e < nslots8; e += 64) {
+    const float dl = Wt.delta[wave][(T.desc[e] >> 3) & (kD - 1)];
+#pragma unroll
+    for (int j = 0; j < GH; ++j) Wt.gam[wave][e][j] = __fmul_rn(T.gam[e][j], dl);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's weights are stored
+}
+
+template <int GH, int AUX, bool BLK>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   const BlockWork bw = block_work(a);
   KScanSess &S = *bw.S;
@@ -380,6 +429,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   const int64_t n = S.n;
   __shared__ SlotTable<GH> T;
   __shared__ SlotScratch<GH> X;
+  __shared__ typename std::conditional<BLK, BlockWeights<GH>, char>::type Wt;
   build_slot_table<GH>(T, X, S, g, head_base);
   const int tid = threadIdx.x;
   const int ngroups = (T.nslots + 7) >> 3;
@@ -404,6 +454,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
     const int64_t word = wkey0 / 32 + lane;
     const int32_t wbase = (int32_t)(wkey0 / 32);
     const uint32_t voff = (uint32_t)lane * 4u;  // byte offset
+    if constexpr (BLK) block_weights<GH>(Wt, T, X, S, g, wkey0 / kBlockKeys, wave, lane, C);
 
     float acc[GH][KPL];
 #pragma unroll
@@ -425,7 +476,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int h = 0; h < GH; ++h) gv[h][j] = uniform_f(T.gam[grp * 8 + j][h]);
+        for (int h = 0; h < GH; ++h) {
+          if constexpr (BLK)
+            gv[h][j] = uniform_f(Wt.gam[wave][grp * 8 + j][h]);
+          else
+            gv[h][j] = uniform_f(T.gam[grp * 8 + j][h]);
+        }
       if (gm == (1 << GH) - 1) {
 #pragma unroll
         for (int k = 0; k < KPL; ++k) {
@@ -649,9 +705,23 @@ struct alignas(16) SlotRecord {
   int32_t limbs[kMaxPasses][64][4];
 };
 
+// Per-block ranges (BLK): gamma, C_h and the fixed-point exponent change with
+// every 2048-key tile.  The first producer task of each item (its pass's first
+// slot group) also loads the tile's lo and hi of the 128 channels with its
+// planes and, once its codes are stored, writes this header beside them: the
+// pass's A operands (int8 limbs of gamma_h,slot = q_hc * delta_c,tile at the
+// tile's own exponent E_h), C_h,tile, 2^(E_h - 30) and the candidate bound.
+// The consumers read it with the codes, after the same fill wait.
+struct alignas(16) ItemHeader {
+  int32_t limbs[64][4];  // A operands of the item's pass (layout of s_limbs)
+  float delta[kD];       // delta_c of the item's tile
+  float C[kMaxGH], scale[kMaxGH];
+  int32_t ht[kMaxGH];    // hi_bound of the head's row (one-pass candidate scans)
+};
+
 // META: the sessions carry a side stream (its bytes are prefetched with the
 // planes, which costs registers the other variants do not spend).
-template <int GH, int MODE, bool META>
+template <int GH, int MODE, bool META, bool BLK>
 __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   const BlockWork bw = block_work(a);
   KScanSess &S = *bw.S;
@@ -673,9 +743,16 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   // producer task), [2..3] releases (one per consumer wave and item); counts
   // only grow during a launch
   __shared__ uint32_t s_ring[4];
+  // per-block ranges: the items' headers; q_hc and t_hc of the block's heads
+  // live where the per-layer limbs would
+  __shared__ typename std::conditional<BLK, ItemHeader[2], char>::type s_hdr;
+  float(*const s_bq)[kD] = reinterpret_cast<float(*)[kD]>(&s_limbs[0][0][0]);
+  uint8_t(*const s_bt)[kD] =
+      reinterpret_cast<uint8_t(*)[kD]>(reinterpret_cast<char *>(&s_limbs[0][0][0]) +
+                                       sizeof(float) * kMaxGH * kD);
   const int tid = threadIdx.x;
   SlotRecord *rec = S.table ? reinterpret_cast<SlotRecord *>(S.table) + bw.rec : nullptr;
-  if (S.table_mode == kTableRead) {
+  if (!BLK && S.table_mode == kTableRead) {
     // the set-up an earlier scan of this call stored
     if (tid == 0) s_nslots = rec->nslots;
     if (tid < GH) {
@@ -695,8 +772,18 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
     const int nslots = T.nslots;
     const int ngroups = (nslots + 7) >> 3;
     const int npasses = max(1, (ngroups + kPassGroups - 1) / kPassGroups);
+    if constexpr (BLK) {
+      // slot order, q and t; the weights are formed per tile
+      if (tid == 0) s_nslots = nslots;
+      for (int e = tid; e < npasses * kPassGroups * 8; e += kMThreads)
+        s_desc[e] = e < nslots ? T.desc[e] : (int16_t)0;
+      for (int e = tid; e < GH * kD; e += kMThreads) {
+        s_bq[e / kD][e % kD] = U.X.q[e / kD][e % kD];
+        s_bt[e / kD][e % kD] = U.X.t[e / kD][e % kD];
+      }
+    }
     // fixed-point exponent per head
-    if (tid < GH) {
+    if (!BLK && tid < GH) {
       const float m = __uint_as_float(T.gmax[tid]);
       int e = 0;
       if (m > 0.0f) frexpf(m, &e);
@@ -704,15 +791,16 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
       s_scale[tid] = ldexpf(1.0f, e - 30);
       s_C[tid] = T.C[tid];
     }
-    if (tid == 0) s_nslots = nslots;
-    for (int e = tid; e < npasses * kPassGroups * 8; e += kMThreads)
-      s_desc[e] = e < nslots ? T.desc[e] : (int16_t)0;
+    if (!BLK && tid == 0) s_nslots = nslots;
+    if (!BLK)
+      for (int e = tid; e < npasses * kPassGroups * 8; e += kMThreads)
+        s_desc[e] = e < nslots ? T.desc[e] : (int16_t)0;
     __syncthreads();
     // A operands: lane l = row (head (l%16)/4, limb (l%16)%4), slot chunk l/16;
     // dword d, byte b <-> slot 64p + 16(l/16) + 8(d/2) + 2b + (d%2), the order
     // in which the code words are split into bytes below.
     uint8_t *limb_bytes = reinterpret_cast<uint8_t *>(&s_limbs[0][0][0]);
-    for (int idx = tid; idx < npasses * 64 * 16; idx += kMThreads) {
+    for (int idx = tid; idx < (BLK ? 0 : npasses * 64 * 16); idx += kMThreads) {
       const int p = idx >> 10, l = (idx >> 4) & 63, d = (idx >> 2) & 3, b = idx & 3;
       const int r = l & 15, h = r >> 2, limb = r & 3, j = l >> 4;
       const int slot = 64 * p + 16 * j + 8 * (d >> 1) + 2 * b + (d & 1);
@@ -734,16 +822,18 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
     // thresholds are read here, before any plane load is in flight
     if constexpr (MODE == kScanCand) {
       s_tf[tid] = key_threshold(S.thr[head_base + tid]);
-      s_ht[tid] = hi_bound(s_tf[tid], s_C[tid], s_scale[tid]);
+      if (!BLK) s_ht[tid] = hi_bound(s_tf[tid], s_C[tid], s_scale[tid]);
     }
     if constexpr (MODE == kScanCandGroup) s_tf[tid] = key_threshold(S.thr[g]);
   }
   __syncthreads();  // the code table is free from here on
   const int nslots = s_nslots;
-  const int ngroups = (nslots + 7) >> 3;
+  // per-block ranges: at least one slot group (padding slots read nothing),
+  // whose producer task writes each item's header
+  const int ngroups = max(BLK ? 1 : 0, (nslots + 7) >> 3);
   // at least one pass, so that a plan reading nothing still writes C_h
   const int npasses = max(1, (ngroups + kPassGroups - 1) / kPassGroups);
-  if (S.table_mode == kTableWrite && bw.tile0 == 0) {
+  if (!BLK && S.table_mode == kTableWrite && bw.tile0 == 0) {
     // for the later scans of this call (one block per kv head stores it)
     if (tid == 0) rec->nslots = nslots;
     if (tid < GH) {
@@ -764,8 +854,8 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   const int role = tid >> 9, wave = (tid >> 6) & 7, lane = tid & 63;
   const int quarter = lane >> 4, m16 = lane & 15;
   const int hh = lane >> 4;  // head of this lane's results (MFMA row block)
-  const float Ch = hh < GH ? s_C[hh] : 0.0f;
-  const float scale = hh < GH ? s_scale[hh] : 0.0f;
+  const float Ch = !BLK && hh < GH ? s_C[hh] : 0.0f;
+  const float scale = !BLK && hh < GH ? s_scale[hh] : 0.0f;
   const uint32_t *gplanes = S.planes + (int64_t)g * kD * kPlanes * W;
   const int64_t ld = S.ld;
   const uint8_t *meta = META && S.meta ? S.meta + (int64_t)g * n : nullptr;
@@ -784,6 +874,15 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   // quarter k loads code bit k, i.e. plane slot 3 - k, words 4*m16 .. +3
   const uint32_t plane_sl = 3u - (uint32_t)quarter;
   const uint32_t lane_part = plane_sl * row_bytes + (uint32_t)m16 * 16u;
+  // per-block ranges: this kv head's rows of lo and hi ([d][rs]; the launcher
+  // keeps them within 2 GiB), channel c of tile t at byte 4 (c rs + t)
+  const uint32_t rs32 = BLK ? (uint32_t)S.rs : 0u;
+  const __amdgpu_buffer_rsrc_t rsrc_lo = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(S.lo) + (int64_t)g * kD * rs32, (short)0, (int32_t)(kD * rs32 * 4u),
+      kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rsrc_hi = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(S.hi) + (int64_t)g * kD * rs32, (short)0, (int32_t)(kD * rs32 * 4u),
+      kRsrcWord3);
 
   // Work items = (tile, pass) of this block's tiles in order; item i goes
   // through code buffer i % 2.  Visited tile v of this block: all tiles, or
@@ -814,12 +913,22 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
     // offsets lie past the buffer: they read 0 and touch no memory), so that
     // the loads of the two tasks in flight always complete in issue order
     // and the wait for the older one leaves the newer one in flight.
-    auto issue = [&](int k, uint32_t(&x)[32]) {
+    auto issue = [&](int k, uint32_t(&x)[32], uint32_t(&rr)[4]) {
       const bool live = k < ntasks;  // wave-uniform
       const int ti = live ? k / ngroups : 0;
       const int grp = live ? k - ti * ngroups : 0;
-      const uint32_t tile_off =
-          live ? (uint32_t)real_tile(bw.tile0 + ti * bw.tile_step) * (kMTileKeys / 8) : 0u;
+      const uint32_t tile = live ? (uint32_t)real_tile(bw.tile0 + ti * bw.tile_step) : 0u;
+      const uint32_t tile_off = tile * (kMTileKeys / 8);
+      if constexpr (BLK) {
+        // the tile's lo and hi of channels lane and lane + 64 (header tasks)
+        const bool hdr = live && (grp & 7) == 0;
+        const uint32_t o0 = hdr ? ((uint32_t)lane * rs32 + tile) * 4u : kUnread;
+        const uint32_t o1 = hdr ? ((uint32_t)(lane + 64) * rs32 + tile) * 4u : kUnread;
+        rr[0] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_lo, (int32_t)o0, 0, 0);
+        rr[1] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_lo, (int32_t)o1, 0, 0);
+        rr[2] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_hi, (int32_t)o0, 0, 0);
+        rr[3] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_hi, (int32_t)o1, 0, 0);
+      }
       const uint4 dv = *reinterpret_cast<const uint4 *>(&s_desc[grp * 8]);
       const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
@@ -837,9 +946,84 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
         x[4 * i + 3] = (uint32_t)v[3];
       }
     };
+    // per-block ranges: the header of pass p of a tile from its lo, hi
+    // (channels lane and lane + 64 in rr); see ItemHeader
+    auto item_header = [&](int p, ItemHeader &H, const uint32_t(&rr)[4]) {
+      const float l0 = __uint_as_float(rr[0]), l1 = __uint_as_float(rr[1]);
+      const float d0 = __fmul_rn(__fsub_rn(__uint_as_float(rr[2]), l0), 0.0625f);
+      const float d1 = __fmul_rn(__fsub_rn(__uint_as_float(rr[3]), l1), 0.0625f);
+      H.delta[lane] = d0;
+      H.delta[lane + 64] = d1;
+      int e[GH];
+      float Cv[GH], sc[GH];
+#pragma unroll
+      for (int j = 0; j < GH; ++j) {
+        const int t0 = s_bt[j][lane], t1 = s_bt[j][lane + 64];
+        const float q0 = s_bq[j][lane], q1 = s_bq[j][lane + 64];
+        // max |gamma| over the channels the head reads (its slots' weights)
+        float m = fmaxf(t0 > 0 ? fabsf(__fmul_rn(q0, d0)) : 0.0f,
+                        t1 > 0 ? fabsf(__fmul_rn(q1, d1)) : 0.0f);
+        // C_h in the slot table's fp64 order
+        double v0 = (double)q0 * ((double)l0 + (double)d0 * (double)(1 << (4 - t0)) * 0.5);
+        double v1 = (double)q1 * ((double)l1 + (double)d1 * (double)(1 << (4 - t1)) * 0.5);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+          m = fmaxf(m, __shfl_xor(m, off));
+          v0 = __dadd_rn(v0, __shfl_xor(v0, off));
+          v1 = __dadd_rn(v1, __shfl_xor(v1, off));
+        }
+        e[j] = 0;
+        if (m > 0.0f) frexpf(m, &e[j]);
+        sc[j] = ldexpf(1.0f, e[j] - 30);
+        Cv[j] = (float)__dadd_rn(v0, v1);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile's deltas are stored
+      // A operands of pass p (the set-up's layout and limb split)
+      const int r = lane & 15, ha = r >> 2, limb = r & 3, ja = lane >> 4;
+      int ea = e[0];
+#pragma unroll
+      for (int j = 1; j < GH; ++j) ea = ha == j ? e[j] : ea;
+      const int nslots_ = s_nslots;
+      int32_t dw[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const int slot = 64 * p + 16 * ja + 8 * (d >> 1) + 2 * bb + (d & 1);
+          int v = 0;
+          if (ha < GH && slot < nslots_) {
+            const int desc = s_desc[slot];
+            const int c = (desc >> 3) & (kD - 1), dep = desc & 7;
+            if (s_bt[ha][c] >= dep) {
+              int G = (int)rintf(ldexpf(__fmul_rn(s_bq[ha][c], H.delta[c]), 30 - ea));
+              for (int i = 0; i < limb; ++i) {
+                const int dg = ((G + 128) & 255) - 128;
+                G = (G - dg) >> 8;
+              }
+              v = ((G + 128) & 255) - 128;
+            }
+          }
+          word |= (uint32_t)(uint8_t)(int8_t)v << (8 * bb);
+        }
+        dw[d] = (int32_t)word;
+      }
+      *reinterpret_cast<int4 *>(&H.limbs[lane][0]) = make_int4(dw[0], dw[1], dw[2], dw[3]);
+      if (lane < GH) {
+        float cl = Cv[0], sl = sc[0];
+#pragma unroll
+        for (int j = 1; j < GH; ++j) {
+          cl = lane == j ? Cv[j] : cl;
+          sl = lane == j ? sc[j] : sl;
+        }
+        H.C[lane] = cl;
+        H.scale[lane] = sl;
+        H.ht[lane] = MODE == kScanCand ? hi_bound(s_tf[lane], cl, sl) : 0;
+      }
+    };
     // regroup and transpose task k's words in place and store them in its
     // item's code buffer, once the consumers have released that buffer
-    auto produce = [&](int k, uint32_t(&x)[32]) {
+    auto produce = [&](int k, uint32_t(&x)[32], const uint32_t(&rr)[4]) {
       const int ti = k / ngroups, grp = k - ti * ngroups;
       const int item = ti * npasses + (grp >> 3);
       const int b = item & 1;
@@ -871,18 +1055,20 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
       uint32_t *dst = &s_codes[b][code_index(grp & 7, 32 * w)];
 #pragma unroll
       for (int t = 0; t < 32; ++t) dst[t] = x[t];
+      if constexpr (BLK)
+        if ((grp & 7) == 0) item_header(grp >> 3, s_hdr[b], rr);
       ring_signal(&s_ring[b]);  // one group of the buffer filled
     };
-    uint32_t x0[32], x1[32];
+    uint32_t x0[32], x1[32], r0[4] = {0u, 0u, 0u, 0u}, r1[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int r = 0; r < 32; ++r) x0[r] = x1[r] = 0;
-    issue(wave, x0);
-    issue(wave + 8, x1);
+    issue(wave, x0, r0);
+    issue(wave + 8, x1, r1);
     for (int k = wave; k < ntasks; k += 16) {
-      produce(k, x0);
-      issue(k + 16, x0);
-      if (k + 8 < ntasks) produce(k + 8, x1);
-      issue(k + 24, x1);
+      produce(k, x0, r0);
+      issue(k + 16, x0, r0);
+      if (k + 8 < ntasks) produce(k + 8, x1, r1);
+      issue(k + 24, x1, r1);
     }
   } else {
     // ==== consumers: wave v multiplies keys 256v .. 256v+255 of every item
@@ -911,13 +1097,27 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
           if (kb0 + 64 * beta + 4 <= n)
             mw[beta] = *reinterpret_cast<const uint32_t *>(meta + kb0 + 64 * beta);
       }
-      const int4 av = *reinterpret_cast<const int4 *>(&s_limbs[p][lane][0]);
+      int4 av;
+      if constexpr (!BLK) av = *reinterpret_cast<const int4 *>(&s_limbs[p][lane][0]);
+      ring_wait(&s_ring[b], fill_target[b]);  // every group of the item stored
+      // per-block ranges: this item's operands, C_h and scale from its header
+      float Cit = Ch, sit = scale;
+      int htit = INT_MAX;
+      if constexpr (BLK) {
+        av = *reinterpret_cast<const int4 *>(&s_hdr[b].limbs[lane][0]);
+        if (hh < GH) {
+          Cit = s_hdr[b].C[hh];
+          sit = s_hdr[b].scale[hh];
+          htit = s_hdr[b].ht[hh];
+        }
+      } else if (MODE == kScanCand && hh < GH) {
+        htit = s_ht[hh];
+      }
       const v4i A = v4i{av.x, av.y, av.z, av.w};
       if (p == 0) {
 #pragma unroll
-        for (int q = 0; q < 16; ++q) s[q] = Ch;
+        for (int q = 0; q < 16; ++q) s[q] = Cit;
       }
-      ring_wait(&s_ring[b], fill_target[b]);  // every group of the item stored
       const uint32_t *codes = s_codes[b];
       if (MODE == kScanCand && !META && npasses == 1) {
         // one pass, one row per head: the exact score of a key is formed
@@ -927,7 +1127,7 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
         const int64_t kb = tile_key0 + 256 * wave + 4 * nn;  // + 64*beta + e
         const int64_t rem = n - kb;
         const int lim = hh < GH ? (rem > 256 ? 256 : (int)rem) : 0;
-        const int ht = hh < GH ? s_ht[hh] : INT_MAX;
+        const int ht = htit;
         // all 16 products first; the buffer is released once they are issued
         v4i acc[16];
 #pragma unroll
@@ -952,7 +1152,7 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
           if (__ballot(maybe) != 0ull) {
             const int lo = acc[q][0] + acc[q][1] * 256;
             const float t = __fmaf_rn((float)hi, 65536.0f, (float)lo);
-            sv[q] = __fmaf_rn(t, scale, Ch);
+            sv[q] = __fmaf_rn(t, sit, Cit);
             mask |= (uint32_t)(maybe && sv[q] >= row_tf) << q;
           }
         }
@@ -989,7 +1189,7 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
           const int lo = acc[e][0] + acc[e][1] * 256;
           const int hi = acc[e][2] + acc[e][3] * 256;
           const float t = __fmaf_rn((float)hi, 65536.0f, (float)lo);
-          s[4 * beta + e] = __fmaf_rn(t, scale, s[4 * beta + e]);
+          s[4 * beta + e] = __fmaf_rn(t, sit, s[4 * beta + e]);
         }
       }
       ring_signal(&s_ring[2 + b]);  // buffer read (by this wave)
@@ -1153,55 +1353,58 @@ constexpr int kHostTileKeys = 32 * 64 * (kScanThreads / 64);
 
 using ScanFn = void (*)(ScanArgs);
 
-template <int AUX>
+template <int AUX, bool BLK>
 ScanFn pick(int GH) {
   switch (GH) {
-    case 1: return scan_kernel<1, AUX>;
-    case 2: return scan_kernel<2, AUX>;
-    case 3: return scan_kernel<3, AUX>;
-    default: return scan_kernel<4, AUX>;
+    case 1: return scan_kernel<1, AUX, BLK>;
+    case 2: return scan_kernel<2, AUX, BLK>;
+    case 3: return scan_kernel<3, AUX, BLK>;
+    default: return scan_kernel<4, AUX, BLK>;
   }
 }
 
-template <int MODE, bool META>
+template <int MODE, bool META, bool BLK>
 ScanFn pick_mfma_mode(int GH) {
   switch (GH) {
-    case 1: return scan_mfma_kernel<1, MODE, META>;
-    case 2: return scan_mfma_kernel<2, MODE, META>;
-    case 3: return scan_mfma_kernel<3, MODE, META>;
-    default: return scan_mfma_kernel<4, MODE, META>;
+    case 1: return scan_mfma_kernel<1, MODE, META, BLK>;
+    case 2: return scan_mfma_kernel<2, MODE, META, BLK>;
+    case 3: return scan_mfma_kernel<3, MODE, META, BLK>;
+    default: return scan_mfma_kernel<4, MODE, META, BLK>;
   }
 }
 
-template <bool META>
+template <bool META, bool BLK>
 ScanFn pick_mfma_meta(int GH, int mode) {
   switch (mode) {
-    case kScanSample: return pick_mfma_mode<kScanSample, META>(GH);
-    case kScanCand: return pick_mfma_mode<kScanCand, META>(GH);
-    case kScanCandGroup: return pick_mfma_mode<kScanCandGroup, META>(GH);
-    default: return pick_mfma_mode<kScanLogits, META>(GH);
+    case kScanSample: return pick_mfma_mode<kScanSample, META, BLK>(GH);
+    case kScanCand: return pick_mfma_mode<kScanCand, META, BLK>(GH);
+    case kScanCandGroup: return pick_mfma_mode<kScanCandGroup, META, BLK>(GH);
+    default: return pick_mfma_mode<kScanLogits, META, BLK>(GH);
   }
 }
 
-ScanFn pick_mfma(int GH, int mode, bool meta) {
-  return meta ? pick_mfma_meta<true>(GH, mode) : pick_mfma_meta<false>(GH, mode);
+// (per-block ranges come without a side stream: the launcher refuses both)
+ScanFn pick_mfma(int GH, int mode, bool meta, bool blk) {
+  if (blk) return pick_mfma_meta<false, true>(GH, mode);
+  return meta ? pick_mfma_meta<true, false>(GH, mode) : pick_mfma_meta<false, false>(GH, mode);
 }
 
 // Pinned-host planes: the link is the bound, the fp32 kernel with whole-word
 // lanes keeps 256-byte wave accesses.  HBM planes: the matrix-core kernel
 // (the fp32 kernel above 2^25 keys per session).
-ScanFn kernel_for(bool host, int GH, int mode, bool meta) {
-  return host ? pick<kHostAux>(GH) : pick_mfma(GH, mode, meta);
+ScanFn kernel_for(bool host, int GH, int mode, bool meta, bool blk) {
+  if (host) return blk ? pick<kHostAux, true>(GH) : pick<kHostAux, false>(GH);
+  return pick_mfma(GH, mode, meta, blk);
 }
 int threads_for(bool host) { return host ? kScanThreads : kMThreads; }
 
-int resident_blocks_per_cu(bool host, int GH, int mode, bool meta) {
-  static int cached[2][kMaxGH + 1][4][2] = {};
-  int &c = cached[host ? 1 : 0][GH][mode][meta ? 1 : 0];
+int resident_blocks_per_cu(bool host, int GH, int mode, bool meta, bool blk) {
+  static int cached[2][kMaxGH + 1][4][2][2] = {};
+  int &c = cached[host ? 1 : 0][GH][mode][meta ? 1 : 0][blk ? 1 : 0];
   if (c == 0) {
     int nb = 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &nb, kernel_for(host, GH, mode, meta), threads_for(host), 0);
+        &nb, kernel_for(host, GH, mode, meta, blk), threads_for(host), 0);
     c = (e == hipSuccess && nb > 0) ? nb : 1;
   }
   return c;
@@ -1293,6 +1496,21 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_
       set_error("scan: recompute flags need the matrix-core scan");
       return FATHOM_ERR_UNSUPPORTED;
     }
+  // per-block ranges: all sessions of a call or none, no side stream, and
+  // each kv head's lo / hi rows within 2 GiB (32-bit buffer offsets)
+  const bool blk = sess[0].rs > 0;
+  for (int32_t j = 0; j < n_sess; ++j) {
+    if ((sess[j].rs > 0) != blk || (blk && sess[j].meta)) {
+      set_error("scan: per-block ranges need every session blocked and no side stream");
+      return FATHOM_ERR_UNSUPPORTED;
+    }
+    if (blk && (sess[j].rs > ((int64_t)1 << 20) ||
+                sess[j].rs * kBlockKeys < sess[j].n)) {
+      set_error("scan: range stride %lld must cover the %lld keys' blocks, at most 2^20",
+                (long long)sess[j].rs, (long long)sess[j].n);
+      return FATHOM_ERR_INVALID_ARG;
+    }
+  }
   const bool cand = mode == kScanCand || mode == kScanCandGroup;
   const int64_t tile_keys =
       fp32_path ? (int64_t)kHostTileKeys : (int64_t)kMTileKeys;
@@ -1313,7 +1531,7 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_
     for (int j = 0; j < cnt; ++j) total_tiles += visited(sess[s0 + j].n) * hkv;
     const int64_t target_blocks =
         (int64_t)ncu *
-        resident_blocks_per_cu(fp32_path, std::min(kMaxGH, group), kernel_mode, any_meta);
+        resident_blocks_per_cu(fp32_path, std::min(kMaxGH, group), kernel_mode, any_meta, blk);
     int64_t tpb_s[kSessPerLaunch];
     for (int j = 0; j < cnt; ++j) {
       const int64_t tiles = visited(sess[s0 + j].n);
@@ -1354,8 +1572,10 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_
         o.ovf_cnt = in.ovf_cnt;
         o.ovf = in.ovf;
         o.redo = in.redo;
-        o.table = fp32_path ? nullptr : in.table;
-        o.table_mode = fp32_path || !in.table ? kTableNone : in.table_mode;
+        o.rs = in.rs;
+        // slot records hold per-layer weights: per-block scans build their own
+        o.table = fp32_path || blk ? nullptr : in.table;
+        o.table_mode = fp32_path || blk || !in.table ? kTableNone : in.table_mode;
         const int64_t tiles = visited(in.n);
         o.nvtiles = (int32_t)tiles;
         o.ntiles = (int32_t)((in.n + tile_keys - 1) / tile_keys);
@@ -1366,7 +1586,7 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_
         blocks += o.blocks_per_head * hkv;
       }
       if (blocks == 0) continue;
-      hipLaunchKernelGGL(kernel_for(fp32_path, GH, mode, any_meta), dim3(blocks),
+      hipLaunchKernelGGL(kernel_for(fp32_path, GH, mode, any_meta, blk), dim3(blocks),
                          dim3(threads_for(fp32_path)), 0, s, a);
       int32_t rc = hip_fail(hipGetLastError(), "scan launch");
       if (rc) return rc;

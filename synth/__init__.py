@@ -98,6 +98,22 @@ def keys(seed: int, layer: int, n: int, hkv: int, d: int, dtype, outliers: int,
     return z.to(dtype)
 
 
+def drifting_keys(seed: int, layer: int, n: int, hkv: int, d: int, dtype, outliers: int,
+                  drift: float = 3.0, device="cpu", session: int = 0) -> torch.Tensor:
+    """Keys of a long session whose ranges drift: keys() scaled per token by
+    1 + drift * i / n and shifted by drift * sigma_c * u_c * i / n, with u_c
+    ~ N(0, 1) per (kv head, channel).  The last token's range is about
+    (1 + drift) times the first's, and centred elsewhere."""
+    z = keys(seed, layer, n, hkv, d, torch.float32, outliers, device, session)
+    sig = channel_sigmas(seed * 131 + session, layer, hkv, d, outliers)
+    g = _cpu_gen(seed, layer, session, 8)
+    u = torch.randn((hkv, d), generator=g, dtype=torch.float64)
+    ramp = torch.arange(n, device=device, dtype=torch.float32) * (drift / max(n, 1))
+    shift = (sig * u).to(device=device, dtype=torch.float32)
+    z.mul_((1.0 + ramp)[:, None, None]).add_(ramp[:, None, None] * shift[None])
+    return z.to(dtype)
+
+
 def queries(seed: int, layer: int, hq: int, d: int, device="cpu",
             session: int = 0) -> torch.Tensor:
     g = _cpu_gen(seed, layer, session, 3)

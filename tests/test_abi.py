@@ -348,3 +348,83 @@ def test_calibrated_validation(L):
     assert L.fathom_plan_calibrated_group(A, 4, 2, 128, A, A, A, g, A, None) == 1
     assert "budget_bits[1] = 513" in err(L)
     assert L.fathom_plan_calibrated_group(A, 4, 3, 128, A, A, A, g, A, None) == 1
+
+
+def test_blocked_sizes(L):
+    for n, nb in ((0, 0), (1, 1), (2047, 1), (2048, 1), (2049, 2), (1 << 31, 1 << 20)):
+        assert L.fathom_range_blocks(n) == nb
+    assert L.fathom_pack_blocked_workspace_bytes(5000, 8, 128) == 3 * 8 * 128 * 8
+    assert L.fathom_pack_blocked_workspace_bytes(0, 8, 128) == 0
+    assert L.fathom_pack_blocked_workspace_bytes(10, 8, 64) == 0
+
+
+def test_pack_blocked_validation(L):
+    A = ctypes.c_void_p(0x10000)
+    ws = L.fathom_pack_blocked_workspace_bytes(5000, 8, 128)
+    # every case below fails validation, so nothing is ever enqueued
+    base = [A, 0, 5000, 8, 128, 1024, 128, A, A, A, 3, A, A, ws, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return L.fathom_pack_blocked(*a)
+    assert call(0, None) == 1                    # keys
+    assert call(8, None) == 1                    # lo
+    assert call(1, 5) == 1                       # dtype
+    assert call(2, 0) == 1                       # n
+    assert call(4, 96) == 2                      # d
+    assert call(10, 2) == 1 and "range_stride" in err(L)   # 5000 keys span 3 blocks
+    assert call(10, (1 << 20) + 1) == 1          # above 2^20
+    assert call(13, ws - 1) == 4                 # workspace
+    assert call(12, None) == 4
+
+
+def test_append_blocked_validation(L):
+    A = ctypes.c_void_p(0x10000)
+    base = [A, 0, 10, 8, 128, 1024, 128, 4090, A, 192, A, A, 3, None, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return L.fathom_append_blocked(*a)
+    assert call(0, None) == 1                    # keys
+    assert call(10, None) == 1                   # lo
+    assert call(4, 64) == 2                      # d
+    assert call(9, 64) == 1 and "plane_words" in err(L)
+    assert call(12, 1) == 1 and "range_stride" in err(L)   # 4100 keys span 3 blocks
+    assert call(12, 0) == 1
+    assert call(7, -1) == 1                      # n_old
+
+
+def test_scan_blocked_validation(L):
+    A = ctypes.c_void_p(0x10000)
+    base = [A, A, A, 3, 5000, 8, 128, A, A, 32, 0, A, 5000, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return L.fathom_scan_blocked(*a)
+    assert call(3, 2) == 1 and "range_stride" in err(L)
+    assert call(3, (1 << 20) + 1) == 1
+    assert call(9, 30) == 1                      # hq not a multiple of hkv
+    assert call(6, 256) == 2                     # d
+    assert call(12, 4999) == 1                   # ld < n
+    assert call(10, 100) == 1                    # plane_words
+    assert call(0, None) == 1
+
+
+def test_scan_topk_blocked_validation(L):
+    A = ctypes.c_void_p(0x10000)
+    ws = L.fathom_scan_topk_workspace_bytes((ctypes.c_int64 * 1)(5000), 1, 8, 32, 1, 64)
+    base = [A, A, A, 3, 5000, 8, 128, A, A, 32, 0, 1, 64, A, A, A, ws, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return L.fathom_scan_topk_blocked(*a)
+    assert call(3, 2) == 1 and "range_stride" in err(L)
+    assert call(12, 0) == 1                      # k
+    assert call(12, 4096) == 1
+    assert call(11, 3) == 1                      # group does not divide hq
+    assert call(16, ws - 1) == 4                 # workspace
+    assert call(13, None) == 1                   # idx
