@@ -480,6 +480,110 @@ def bench_clustered(dev, steps, warmup, iid_step_ms):
             "rows_recomputed": flagged, "rows_total": len(layers) * w.hq}
 
 
+def bench_blocked(dev, steps, warmup, n_layers=4):
+    """Per-block ranges (one lo/hi per 2048-key block of a channel) against
+    per-layer ranges on the same keys: 1M-key layers whose key ranges drift
+    along the sequence (synth.drifting_keys, drift 3), B = 92, k = 2048.  Fused
+    plan + scan + top-k step times with planes in HBM and in pinned host
+    memory, their ratios, the cost of pack and of a one-token append, and the
+    recall@2048 of each against the exact top-k of the fp64 logits q . k of
+    the fp16 keys (torch's matmul on the GPU, as in plan_quality)."""
+    w = synth.LAYER_1M
+    G = w.hq // w.hkv
+    layers = []
+    recall = {"per_layer": [], "per_block": []}
+    fws = torch.empty(fathom.scan_topk_workspace_bytes([w.n], w.hkv, w.hq, 1, w.k),
+                      dtype=torch.uint8, device=dev)
+    idx = torch.empty((w.hq, w.k), dtype=torch.int32, device=dev)
+    vals = torch.empty((w.hq, w.k), device=dev)
+    pack_ms = {"per_layer": [], "per_block": []}
+    for l in range(n_layers):
+        keys = synth.drifting_keys(w.seed, l, w.n, w.hkv, w.d, w.dtype, w.outliers, device=dev)
+        q = synth.queries(w.seed, l, w.hq, w.d, device=dev)
+        for name, fn in (("per_layer", fathom.pack), ("per_block", fathom.pack_blocked)):
+            fn(keys)
+            torch.cuda.synchronize()
+            a, b = _event_pair()
+            a.record()
+            p = fn(keys)
+            b.record()
+            torch.cuda.synchronize()
+            pack_ms[name].append(a.elapsed_time(b))
+            host = torch.empty(p.planes.shape, dtype=p.planes.dtype, pin_memory=True)
+            host.copy_(p.planes)
+            plan = torch.empty((w.hq, w.d), dtype=torch.uint8, device=dev)
+            layers.append((name, p, host, q, plan))
+        if l == 0:
+            exact = []
+            for g in range(w.hkv):
+                K = keys[:, g, :].double()
+                s = q[g * G:(g + 1) * G].double() @ K.T
+                exact.append(torch.topk(s, w.k, dim=1).indices)
+                del K, s
+            exact = torch.cat(exact).cpu().numpy()
+            for name, p, host, q_, plan in layers:
+                fathom.plan(q_, p.sigma2, w.budget, out=plan)
+                if name == "per_layer":
+                    fathom.scan_topk(p.planes, p.lo, p.hi, w.n, q_, plan, w.k, 1, ws=fws,
+                                     idx=idx, vals=vals)
+                else:
+                    fathom.scan_topk_blocked(p.planes, p.lo, p.hi, w.n, q_, plan, w.k, 1,
+                                             ws=fws, idx=idx, vals=vals)
+                got = idx.cpu().numpy()
+                recall[name] = float(np.mean([len(np.intersect1d(got[h], exact[h])) / w.k
+                                              for h in range(w.hq)]))
+        del keys
+    out = {"workload": ("1M-key layers (8 kv heads, fp16) with drifting key ranges, B=92, "
+                        "k=2048: per-block ranges against per-layer ranges on the same keys")}
+    for mode in ("hbm", "host"):
+        for kind in ("per_layer", "per_block"):
+            sel = [L for L in layers if L[0] == kind]
+
+            def step(i):
+                _, p, host, q, plan = sel[i % len(sel)]
+                planes = host if mode == "host" else p.planes
+                fathom.plan(q, p.sigma2, w.budget, out=plan)
+                if kind == "per_layer":
+                    fathom.scan_topk(planes, p.lo, p.hi, w.n, q, plan, w.k, 1, ws=fws,
+                                     idx=idx, vals=vals)
+                else:
+                    fathom.scan_topk_blocked(planes, p.lo, p.hi, w.n, q, plan, w.k, 1,
+                                             ws=fws, idx=idx, vals=vals)
+            for i in range(warmup):
+                step(i)
+            torch.cuda.synchronize()
+            a, b = _event_pair()
+            a.record()
+            for i in range(steps):
+                step(i)
+            b.record()
+            torch.cuda.synchronize()
+            out[f"{mode}_{kind}_fused_step_ms"] = round(a.elapsed_time(b) / steps, 4)
+        out[f"{mode}_time_ratio_block_to_layer"] = round(
+            out[f"{mode}_per_block_fused_step_ms"] / out[f"{mode}_per_layer_fused_step_ms"], 4)
+    out["pack_ms"] = {k: round(float(np.mean(v)), 3) for k, v in pack_ms.items()}
+    # one decode token appended to each layout (block 511 already holds keys)
+    _, pb, _, _, _ = [L for L in layers if L[0] == "per_block"][0]
+    _, pl, _, _, _ = [L for L in layers if L[0] == "per_layer"][0]
+    tok = synth.drifting_keys(w.seed, 99, 1, w.hkv, w.d, w.dtype, w.outliers, device=dev)
+    for kind, fn in (("per_layer", lambda: fathom.append(tok, w.n - 1, pl.planes, pl.lo, pl.hi)),
+                     ("per_block", lambda: fathom.append_blocked(tok, w.n - 1, pb.planes, pb.lo,
+                                                                 pb.hi))):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = _event_pair()
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        out[f"append_1_token_{kind}_us"] = round(a.elapsed_time(b) / steps * 1e3, 2)
+    out["recall_at_2048"] = {k: round(v, 4) for k, v in recall.items()}
+    del layers
+    return out
+
+
 def plan_quality(dev, layers_q=2):
     """Recall of each plan's top-k against the exact top-k of the fp64 logits
     q . k of the fp16 keys (not timed; torch's matmul on the GPU is the
@@ -1037,6 +1141,9 @@ def main():
             extra["clustered_1m_hbm"] = bench_clustered(dev, 30, 5, res["hbm_fused"]["step_ms"])
             log(f"clustered: {extra['clustered_1m_hbm']}")
             torch.cuda.empty_cache()
+        extra["blocked_ranges_1m"] = bench_blocked(dev, 30, 5)
+        log(f"blocked ranges: {extra['blocked_ranges_1m']}")
+        torch.cuda.empty_cache()
         extra["pack"] = bench_pack(dev)
         log(f"pack: {extra['pack']}")
         torch.cuda.empty_cache()

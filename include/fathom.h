@@ -288,8 +288,9 @@ int32_t fathom_topk_batched(const fathom_session *sessions, int32_t n_sessions,
  * those of fathom_scan followed by fathom_topk on the same inputs (same
  * scores, ranking, tie order and padding), but the logits of all keys are
  * not written unless needed.  With planes in device memory, n <= 2^25 and
- * group 1 or hq/hkv (<= 4), the call scores a sample of 16384 keys per row,
- * sets a per-row threshold from it, scans again keeping only the
+ * group 1 or hq/hkv (<= 4), the call scores a sample of 32 key tiles (2048
+ * keys each, the middle tiles of 32 equal stretches of the row; all tiles of
+ * shorter rows), sets a per-row threshold from it, scans again keeping only the
  * (score, index) pairs at or above the threshold, and ranks those; a row
  * whose candidate count falls outside [k, 8192] is recomputed from full
  * logits in the workspace.  Otherwise (pinned host planes, other groups,
@@ -353,9 +354,10 @@ int32_t fathom_append(const void *keys, int32_t dtype, int64_t m, int32_t hkv,
  * plane row), so later blocks get ranges of their own and no stored code is
  * ever re-quantised.  Planes keep the fathom_pack layout.
  *
- * lo, hi       device fp32[hkv][d][range_stride]: block b of channel c of kv
- *              head h at [(h*d + c)*range_stride + b]; range_stride is a
- *              capacity, fathom_range_blocks(n) <= range_stride <= 2^20.
+ * lo, hi       device fp32[hkv][range_stride][d]: block b of channel c of kv
+ *              head h at [(h*range_stride + b)*d + c] (one block's d ranges
+ *              are contiguous); range_stride is a capacity,
+ *              fathom_range_blocks(n) <= range_stride <= 2^20.
  *
  * fathom_pack_blocked: each block's range is the min and max of its own keys
  * (-0 stored as +0); its keys are coded with it exactly as fathom_pack codes

@@ -575,10 +575,16 @@ int orc_append(const float *keys, int64_t m, int hkv, int d, int64_t stride_tok,
  *           keys the call puts in it (block 0: those keys' own min and max);
  *           a block that already holds keys keeps its range, and keys outside
  *           it are clamped and counted as in orc_append.
- * lo, hi: [hkv][d][nbc] with nbc >= the number of blocks (a capacity).       */
+ * lo, hi: [hkv][nbc][d] (block-major: the d ranges of one block are
+ * contiguous), nbc >= the number of blocks (a capacity).                    */
 #define ORC_RB 2048
 
 int64_t orc_range_blocks(int64_t n) { return (n + ORC_RB - 1) / ORC_RB; }
+
+/* index of (kv head h, channel c, block b) in lo / hi */
+static int64_t orc_rix(int h, int c, int64_t b, int64_t nbc, int d) {
+  return ((int64_t)h * nbc + b) * d + c;
+}
 
 static int orc_quantise(float x, float l, float delta) {
   if (delta == 0.0f) return 0;
@@ -610,8 +616,8 @@ int orc_pack_blocked(const float *keys, int64_t n, int hkv, int d, int64_t strid
         mn = mn + 0.0f;
         mx = mx + 0.0f;
         const float delta = (mx - mn) * 0.0625f;
-        lo[((int64_t)h * d + c) * nbc + b] = mn;
-        hi[((int64_t)h * d + c) * nbc + b] = mx;
+        lo[orc_rix(h, c, b, nbc, d)] = mn;
+        hi[orc_rix(h, c, b, nbc, d)] = mx;
         int64_t s1 = 0, s2 = 0;
         for (int64_t i = i0; i < i1; ++i) {
           const int code = orc_quantise(col[i * stride_tok], mn, delta);
@@ -638,7 +644,7 @@ static double orc_score_blocked(const uint32_t *planes, int64_t W, const float *
   double s = 0.0;
   for (int c = 0; c < d; ++c) {
     const int t = ph[c];
-    const float l = lo[((int64_t)g * d + c) * nbc + b], u = hi[((int64_t)g * d + c) * nbc + b];
+    const float l = lo[orc_rix(g, c, b, nbc, d)], u = hi[orc_rix(g, c, b, nbc, d)];
     const float delta = (u - l) * 0.0625f;
     const int r = orc_prefix(orc_code_from_planes(planes, W, d, g, c, i), t);
     const double cell = (double)delta * (double)(1 << (4 - t));
@@ -691,14 +697,13 @@ int orc_append_blocked(const float *keys, int64_t m, int hkv, int d, int64_t str
   const int64_t nb_end = orc_range_blocks(n_old + m);
   for (int h = 0; h < hkv; ++h) {
     for (int c = 0; c < d; ++c) {
-      float *lrow = lo + ((int64_t)h * d + c) * nbc, *hrow = hi + ((int64_t)h * d + c) * nbc;
       /* ranges of the blocks this call starts, in block order */
       for (int64_t b = first_new; b < nb_end; ++b) {
         const int64_t i0 = b * ORC_RB, i1 = i0 + ORC_RB < n_old + m ? i0 + ORC_RB : n_old + m;
         float mn, mx;
         if (b > 0) {
-          mn = lrow[b - 1];
-          mx = hrow[b - 1];
+          mn = lo[orc_rix(h, c, b - 1, nbc, d)];
+          mx = hi[orc_rix(h, c, b - 1, nbc, d)];
         } else {
           mn = mx = keys[(i0 - n_old) * stride_tok + (int64_t)h * stride_head + c];
         }
@@ -707,13 +712,13 @@ int orc_append_blocked(const float *keys, int64_t m, int hkv, int d, int64_t str
           if (x < mn) mn = x;
           if (x > mx) mx = x;
         }
-        lrow[b] = mn + 0.0f;
-        hrow[b] = mx + 0.0f;
+        lo[orc_rix(h, c, b, nbc, d)] = mn + 0.0f;
+        hi[orc_rix(h, c, b, nbc, d)] = mx + 0.0f;
       }
       uint32_t *pl = planes + ((int64_t)h * d + c) * 4 * W;
       for (int64_t j = 0; j < m; ++j) {
         const int64_t i = n_old + j, b = i / ORC_RB;
-        const float l = lrow[b], u = hrow[b];
+        const float l = lo[orc_rix(h, c, b, nbc, d)], u = hi[orc_rix(h, c, b, nbc, d)];
         const float x = keys[j * stride_tok + (int64_t)h * stride_head + c];
         const int code = orc_quantise(x, l, (u - l) * 0.0625f);
         count += (x < l || x > u);

@@ -307,7 +307,7 @@ def range_blocks(n: int) -> int:
 
 
 def pack_blocked(keys: np.ndarray, nbc=None):
-    """keys [n][hkv][d] -> dict(planes [hkv][d][4][W] uint32, lo/hi [hkv][d][nbc]
+    """keys [n][hkv][d] -> dict(planes [hkv][d][4][W] uint32, lo/hi [hkv][nbc][d]
     fp32 per 2048-key block, sigma2 [hkv][d] fp32 (pooled within-block))."""
     k = np.ascontiguousarray(keys, dtype=np.float32)
     n, hkv, d = k.shape
@@ -315,8 +315,8 @@ def pack_blocked(keys: np.ndarray, nbc=None):
     nbc = nb if nbc is None else nbc
     W = plane_words(n)
     planes = np.zeros((hkv, d, 4, W), np.uint32)
-    lo = np.zeros((hkv, d, nbc), np.float32)
-    hi = np.zeros((hkv, d, nbc), np.float32)
+    lo = np.zeros((hkv, nbc, d), np.float32)
+    hi = np.zeros((hkv, nbc, d), np.float32)
     s2 = np.zeros((hkv, d), np.float32)
     _check(_load().orc_pack_blocked(_ptr(k), n, hkv, d, hkv * d, d, _ptr(planes), _ptr(lo),
                                     _ptr(hi), nbc, _ptr(s2)), "pack_blocked")
@@ -325,13 +325,13 @@ def pack_blocked(keys: np.ndarray, nbc=None):
 
 def scan_blocked(planes, lo, hi, n: int, q, plan_):
     """Logits [hq][n] fp32 of a layer packed with per-block ranges lo/hi
-    [hkv][d][nbc]."""
+    [hkv][nbc][d]."""
     planes = np.ascontiguousarray(planes, dtype=np.uint32)
     lo = np.ascontiguousarray(lo, dtype=np.float32)
     hi = np.ascontiguousarray(hi, dtype=np.float32)
     q = np.ascontiguousarray(q, dtype=np.float32)
     plan_ = np.ascontiguousarray(plan_, dtype=np.uint8)
-    hkv, d, nbc = lo.shape
+    hkv, nbc, d = lo.shape
     hq = q.shape[0]
     out = np.zeros((hq, max(n, 1)), np.float32)
     _check(_load().orc_scan_blocked(_ptr(planes), _ptr(lo), _ptr(hi), nbc, n, hkv, d, _ptr(q),
@@ -346,7 +346,7 @@ def scan_blocked_at(planes, lo, hi, n: int, q, plan_, keys):
     q = np.ascontiguousarray(q, dtype=np.float32)
     plan_ = np.ascontiguousarray(plan_, dtype=np.uint8)
     keys = np.ascontiguousarray(keys, dtype=np.int64)
-    hkv, d, nbc = lo.shape
+    hkv, nbc, d = lo.shape
     hq = q.shape[0]
     out = np.zeros((hq, keys.size), np.float32)
     _check(_load().orc_scan_blocked_at(_ptr(planes), _ptr(lo), _ptr(hi), nbc, n, hkv, d,
@@ -357,14 +357,14 @@ def scan_blocked_at(planes, lo, hi, n: int, q, plan_, keys):
 
 def append_blocked(keys_new, n_old: int, planes, lo, hi):
     """Append keys_new [m][hkv][d] as tokens n_old.. in place into planes
-    [hkv][d][4][W] and per-block ranges lo/hi [hkv][d][nbc] (reading R22);
+    [hkv][d][4][W] and per-block ranges lo/hi [hkv][nbc][d] (reading R22);
     returns the number of clamped values."""
     k = np.ascontiguousarray(keys_new, dtype=np.float32)
     m, hkv, d = k.shape
     assert planes.flags.c_contiguous and planes.dtype == np.uint32
     assert lo.flags.c_contiguous and hi.flags.c_contiguous
     W = planes.shape[-1]
-    nbc = lo.shape[-1]
+    nbc = lo.shape[1]
     cnt = np.zeros(1, np.int64)
     _check(_load().orc_append_blocked(_ptr(k), m, hkv, d, hkv * d, d, n_old, _ptr(planes), W,
                                       _ptr(lo), _ptr(hi), nbc, _ptr(cnt)), "append_blocked")

@@ -438,7 +438,7 @@ def range_blocks(n: int) -> int:
 
 def pack_blocked(keys: torch.Tensor, capacity: Optional[int] = None,
                  ws: Optional[torch.Tensor] = None) -> Packed:
-    """keys [n][hkv][d] -> Packed with lo, hi fp32 [hkv][d][R] (R = the range
+    """keys [n][hkv][d] -> Packed with lo, hi fp32 [hkv][R][d] (R = the range
     blocks of `capacity` keys, default n) and planes [hkv][d][4][W] with room
     for `capacity` keys (zeroed past n)."""
     _require_gpu(keys)
@@ -455,7 +455,7 @@ def pack_blocked(keys: torch.Tensor, capacity: Optional[int] = None,
         planes = torch.empty((hkv, d, 4, plane_words(n)), dtype=torch.int32, device=dev)
     else:
         planes = torch.zeros((hkv, d, 4, plane_words(cap)), dtype=torch.int32, device=dev)
-    lo = torch.zeros((hkv, d, R), dtype=torch.float32, device=dev)
+    lo = torch.zeros((hkv, R, d), dtype=torch.float32, device=dev)
     hi = torch.zeros_like(lo)
     s2 = torch.empty((hkv, d), dtype=torch.float32, device=dev)
     need = int(lib().fathom_pack_blocked_workspace_bytes(n, hkv, d)) if n > 0 else 0
@@ -477,7 +477,7 @@ def pack_blocked(keys: torch.Tensor, capacity: Optional[int] = None,
 
 def append_blocked(keys: torch.Tensor, n_old: int, planes: torch.Tensor, lo: torch.Tensor,
                    hi: torch.Tensor, clamped: Optional[torch.Tensor] = None) -> None:
-    """append() for per-block ranges: lo, hi [hkv][d][R] are read and written
+    """append() for per-block ranges: lo, hi [hkv][R][d] are read and written
     (the blocks the call starts get their ranges first)."""
     _require_gpu(keys, planes, lo)
     m, hkv, d = keys.shape
@@ -488,16 +488,16 @@ def append_blocked(keys: torch.Tensor, n_old: int, planes: torch.Tensor, lo: tor
         raise FathomError("keys must be float16 or float32")
     _check(lib().fathom_append_blocked(_p(keys), dtype, m, hkv, d, keys.stride(0),
                                        keys.stride(1), n_old, _p(planes), planes.shape[-1],
-                                       _p(lo), _p(hi), lo.shape[-1], _p(clamped),
+                                       _p(lo), _p(hi), lo.shape[1], _p(clamped),
                                        _stream(lo.device)), "fathom_append_blocked")
 
 
 def scan_blocked(planes: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor, n: int,
                  q: torch.Tensor, plan_: torch.Tensor,
                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """scan() with per-block ranges lo, hi [hkv][d][R] -> logits [hq][n]."""
+    """scan() with per-block ranges lo, hi [hkv][R][d] -> logits [hq][n]."""
     _require_gpu(planes, lo, q, plan_)
-    hkv, d, R = lo.shape
+    hkv, R, d = lo.shape
     hq = q.shape[0]
     if out is None:
         out = torch.empty((hq, max(n, 1)), dtype=torch.float32, device=q.device)
@@ -510,9 +510,9 @@ def scan_blocked(planes: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor, n: in
 def scan_topk_blocked(planes: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor, n: int,
                       q: torch.Tensor, plan_: torch.Tensor, k: int, group: int = 1,
                       ws: Optional[torch.Tensor] = None, idx=None, vals=None):
-    """scan_topk() with per-block ranges lo, hi [hkv][d][R]."""
+    """scan_topk() with per-block ranges lo, hi [hkv][R][d]."""
     _require_gpu(planes, lo, q, plan_)
-    hkv, d, R = lo.shape
+    hkv, R, d = lo.shape
     hq = q.shape[0]
     ro = hq // group
     dev = q.device

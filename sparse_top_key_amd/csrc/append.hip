@@ -40,7 +40,7 @@ __global__ __launch_bounds__(kD) void append_kernel(const T *__restrict__ keys, 
   const int64_t i0 = w * 32 > n_old ? w * 32 : n_old;
   const int64_t i1 = w * 32 + 32 < n_old + m ? w * 32 + 32 : n_old + m;
   // the 32 keys of word w lie in 2048-key block w / 64
-  const int64_t ro = rs == 0 ? (int64_t)h * kD + c : ((int64_t)h * kD + c) * rs + w / 64;
+  const int64_t ro = rs == 0 ? (int64_t)h * kD + c : ((int64_t)h * rs + w / 64) * kD + c;
   const float l = lo[ro], u = hi[ro];
   const float delta = __fmul_rn(__fsub_rn(u, l), 0.0625f);
   uint32_t bits[kPlanes] = {0u, 0u, 0u, 0u};
@@ -96,10 +96,10 @@ __global__ __launch_bounds__(kRangeThreads) void append_range_kernel(
   if (r != 0) return;
   mn = fminf(mn, red[c].x);
   mx = fmaxf(mx, red[c].y);
-  const int64_t o = ((int64_t)h * kD + c) * rs + b;
+  const int64_t o = ((int64_t)h * rs + b) * kD + c;
   if (fold && b > 0) {
-    mn = fminf(mn, lo[o - 1]);
-    mx = fmaxf(mx, hi[o - 1]);
+    mn = fminf(mn, lo[o - kD]);
+    mx = fmaxf(mx, hi[o - kD]);
   }
   lo[o] = __fadd_rn(mn, 0.0f);
   hi[o] = __fadd_rn(mx, 0.0f);
@@ -111,13 +111,14 @@ __global__ __launch_bounds__(kD) void append_widen_kernel(int64_t b0, int64_t b1
                                                           float *__restrict__ lo,
                                                           float *__restrict__ hi, int64_t rs) {
   const int c = threadIdx.x, h = blockIdx.x;
-  float *lrow = lo + ((int64_t)h * kD + c) * rs, *hrow = hi + ((int64_t)h * kD + c) * rs;
-  float mn = b0 > 0 ? lrow[b0 - 1] : INFINITY, mx = b0 > 0 ? hrow[b0 - 1] : -INFINITY;
+  float *lrow = lo + (int64_t)h * rs * kD + c, *hrow = hi + (int64_t)h * rs * kD + c;
+  float mn = b0 > 0 ? lrow[(b0 - 1) * kD] : INFINITY;
+  float mx = b0 > 0 ? hrow[(b0 - 1) * kD] : -INFINITY;
   for (int64_t b = b0; b < b1; ++b) {
-    mn = fminf(mn, lrow[b]);
-    mx = fmaxf(mx, hrow[b]);
-    lrow[b] = __fadd_rn(mn, 0.0f);
-    hrow[b] = __fadd_rn(mx, 0.0f);
+    mn = fminf(mn, lrow[b * kD]);
+    mx = fmaxf(mx, hrow[b * kD]);
+    lrow[b * kD] = __fadd_rn(mn, 0.0f);
+    hrow[b * kD] = __fadd_rn(mx, 0.0f);
   }
 }
 

@@ -15,8 +15,15 @@ constexpr int kBlockKeys = 2048;        // keys per 64-word plane block
 constexpr int kSessPerLaunch = 16;      // sessions carried in one kernarg set
 constexpr int kCandCap = 8192;          // top-k candidates kept per row
 constexpr int kSampleTarget = 16384;    // sampled scores per row (threshold)
-constexpr int kSampleTiles = 8;         // 2048-key tiles a fused call scores first
+constexpr int kSampleTiles = 32;        // 2048-key tiles a fused call scores first
 constexpr int kSampleKeys = kSampleTiles * kBlockKeys;
+// Sampled tile j of ns among nt (ns <= nt): the middle tile of the j-th of ns
+// equal strata of the row (all tiles when ns == nt).  Centres, not starts: in
+// a row whose score scale drifts along the sequence, a stratum's first tile
+// is its least (or most) extreme one, which biases the threshold estimate.
+__host__ __device__ inline int64_t sample_tile(int64_t j, int64_t ns, int64_t nt) {
+  return (2 * j + 1) * nt / (2 * ns);
+}
 constexpr int kCntStride = 32;          // candidate counters, one 128-byte line each
 // Candidate store of the fused call: per output row, one segment per scan
 // block of the row's kv head (at most kMaxSeg), kFusedCap words in all; a
@@ -62,7 +69,7 @@ TopkWs topk_ws_carve(void *ws, int64_t out_rows, int64_t redo_slots);
 
 // ---- pack -------------------------------------------------------------------
 // rs: 0 for one range per channel (lo, hi [hkv][d]); > 0 for one range per
-// 2048-key block (lo, hi [hkv][d][rs], rs >= the number of blocks).
+// 2048-key block (lo, hi [hkv][rs][d], rs >= the number of blocks).
 int64_t pack_workspace_bytes(int64_t n, int32_t hkv);
 int64_t pack_blocked_workspace_bytes(int64_t n, int32_t hkv);
 int32_t launch_pack(const void *keys, int32_t dtype, int64_t n, int32_t hkv,
@@ -128,7 +135,7 @@ struct ScanSession {
   int32_t table_mode;     // ScanTable: what the scan does with them
   int32_t residency;      // planes: 0 unknown (queried), 1 device, 2 pinned host
   int64_t W;              // plane row length in words; 0: plane_words(n)
-  int64_t rs;             // 0: lo, hi [hkv][d]; > 0: per 2048-key block, [hkv][d][rs]
+  int64_t rs;             // 0: lo, hi [hkv][d]; > 0: per 2048-key block, [hkv][rs][d]
 };
 inline int64_t sess_words(const ScanSession &s) { return s.W > 0 ? s.W : plane_words(s.n); }
 // Slot tables (matrix-core scan): built in each block (kTableNone), built and

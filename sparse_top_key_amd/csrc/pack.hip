@@ -38,13 +38,13 @@ __device__ inline float load_key(const float *p) { return *p; }
 // Partial min/max of chunk blockIdx.x for kv head blockIdx.y.
 // Per-block ranges (rs > 0, chunk = one 2048-key block): the chunk's min and
 // max are block blockIdx.x's range, stored (+0 for a -0 end) into
-// blo/bhi[h][c][blockIdx.x] instead of part.
+// blo/bhi[h][blockIdx.x][c] instead of part.
 __device__ __forceinline__ void store_minmax(float2 *part, float *blo, float *bhi, int64_t rs,
                                              int hkv, int h, int c, float mn, float mx) {
   if (rs == 0) {
     part[((int64_t)blockIdx.x * hkv + h) * kD + c] = make_float2(mn, mx);
   } else {
-    const int64_t o = ((int64_t)h * kD + c) * rs + blockIdx.x;
+    const int64_t o = ((int64_t)h * rs + blockIdx.x) * kD + c;
     blo[o] = __fadd_rn(mn, 0.0f);
     bhi[o] = __fadd_rn(mx, 0.0f);
   }
@@ -111,9 +111,9 @@ __global__ __launch_bounds__(kReduceThreads) void pack_range_kernel(
 }
 
 // Range of channel c of kv head h for 2048-key block b: lo/hi are [hkv][d]
-// (rs == 0) or [hkv][d][rs] per block.
+// (rs == 0) or [hkv][rs][d] per block.
 __device__ __forceinline__ float range_at(const float *a, int h, int c, int64_t rs, int64_t b) {
-  return rs == 0 ? a[h * kD + c] : a[((int64_t)h * kD + c) * rs + b];
+  return rs == 0 ? a[h * kD + c] : a[((int64_t)h * rs + b) * kD + c];
 }
 
 __device__ inline int quantise(float x, float lo, float delta) {
@@ -528,28 +528,34 @@ __global__ __launch_bounds__(kReduceThreads) void pack_sigma_kernel(
   sigma2[h * kD + c] = (float)__dmul_rn(var_code, dd);
 }
 
-// Per-block ranges: one thread per channel pools the blocks' variances in
-// block order, sigma2 = fp32(sum_b fp64(var_b * (n_b / n))), var_b =
+// Per-block ranges: sigma2 = fp32(sum_b fp64(var_b * (n_b / n))), var_b =
 // Var(code) * delta_b^2 of block b from its exact integer code sums (the
-// expression of pack_sigma for one block).  Each step is one correctly
-// rounded fp64 operation, so the result is the CPU definition's bit for bit.
-__global__ __launch_bounds__(kD) void pack_sigma_blocked_kernel(
-    const int2 *__restrict__ sums, int32_t nblocks, int32_t hkv, int64_t n,
+// expression of pack_sigma for one block).  One block of threads per kv head:
+// first every (block, channel) term in parallel, written over its own code
+// sums; then one thread per channel adds its terms in block order.  Each step
+// is one correctly rounded fp64 operation, so the result is the CPU
+// definition's bit for bit.
+__global__ __launch_bounds__(kReduceThreads) void pack_sigma_blocked_kernel(
+    int2 *__restrict__ sums, int32_t nblocks, int32_t hkv, int64_t n,
     const float *__restrict__ lo, const float *__restrict__ hi, int64_t rs,
     float *__restrict__ sigma2) {
-  const int h = blockIdx.x, c = threadIdx.x;
-  const float *lrow = lo + ((int64_t)h * kD + c) * rs;
-  const float *hrow = hi + ((int64_t)h * kD + c) * rs;
-  double acc = 0.0;
-  for (int32_t b = 0; b < nblocks; ++b) {
-    const int2 v = sums[((int64_t)b * hkv + h) * kD + c];
+  const int h = blockIdx.x, c = threadIdx.x % kD;
+  double *terms = reinterpret_cast<double *>(sums);  // same 8 bytes per (block, channel)
+  for (int32_t b = threadIdx.x / kD; b < nblocks; b += kReduceSlices) {
+    const int64_t e = ((int64_t)b * hkv + h) * kD + c;
+    const int2 v = sums[e];
     const int64_t nb = min((int64_t)kBlockKeys, n - (int64_t)b * kBlockKeys);
-    const float delta = __fmul_rn(__fsub_rn(hrow[b], lrow[b]), 0.0625f);
+    const int64_t r = ((int64_t)h * rs + b) * kD + c;
+    const float delta = __fmul_rn(__fsub_rn(hi[r], lo[r]), 0.0625f);
     const int64_t num = nb * (int64_t)v.y - (int64_t)v.x * (int64_t)v.x;
     const double var_code = __ddiv_rn((double)num, __dmul_rn((double)nb, (double)nb));
     const double var = __dmul_rn(var_code, __dmul_rn((double)delta, (double)delta));
-    acc = __dadd_rn(acc, __dmul_rn(var, __ddiv_rn((double)nb, (double)n)));
+    terms[e] = __dmul_rn(var, __ddiv_rn((double)nb, (double)n));
   }
+  __syncthreads();
+  if (threadIdx.x >= kD) return;
+  double acc = 0.0;
+  for (int32_t b = 0; b < nblocks; ++b) acc = __dadd_rn(acc, terms[((int64_t)b * hkv + h) * kD + c]);
   sigma2[h * kD + c] = (float)acc;
 }
 
@@ -620,8 +626,8 @@ int32_t launch_pack_t(const T *keys, int64_t n, int32_t hkv, int64_t stride_tok,
     hipLaunchKernelGGL(pack_sigma_kernel, dim3(hkv), dim3(kReduceThreads), 0, s, sums,
                        L.nblocks, hkv, n, lo, hi, sigma2);
   else
-    hipLaunchKernelGGL(pack_sigma_blocked_kernel, dim3(hkv), dim3(kD), 0, s, sums, L.nblocks,
-                       hkv, n, lo, hi, rs, sigma2);
+    hipLaunchKernelGGL(pack_sigma_blocked_kernel, dim3(hkv), dim3(kReduceThreads), 0, s, sums,
+                       L.nblocks, hkv, n, lo, hi, rs, sigma2);
   return hip_fail(hipGetLastError(), "pack launch");
 }
 

@@ -69,7 +69,7 @@ struct ScanSess {
   int32_t seg_cap;         // candidate words per (row, block) segment
   uint8_t *table;          // slot records of the session, or null
   int32_t table_mode;      // ScanTable
-  int64_t rs;              // 0: lo, hi [hkv][d]; > 0: per 2048-key block, [hkv][d][rs]
+  int64_t rs;              // 0: lo, hi [hkv][d]; > 0: per 2048-key block, [hkv][rs][d]
 };
 
 struct ScanArgs {
@@ -391,10 +391,10 @@ template <int GH>
 __device__ __forceinline__ void block_weights(BlockWeights<GH> &Wt, const SlotTable<GH> &T,
                                               const SlotScratch<GH> &X, KScanSess &S, int g,
                                               int64_t b, int wave, int lane, float (&C)[GH]) {
-  const int64_t r0 = (int64_t)g * kD * S.rs + b;
-  const float l0 = S.lo[r0 + (int64_t)lane * S.rs], l1 = S.lo[r0 + (int64_t)(lane + 64) * S.rs];
-  const float d0 = __fmul_rn(__fsub_rn(S.hi[r0 + (int64_t)lane * S.rs], l0), 0.0625f);
-  const float d1 = __fmul_rn(__fsub_rn(S.hi[r0 + (int64_t)(lane + 64) * S.rs], l1), 0.0625f);
+  const int64_t r0 = ((int64_t)g * S.rs + b) * kD;  // block b's row of the kv head's ranges
+  const float l0 = S.lo[r0 + lane], l1 = S.lo[r0 + lane + 64];
+  const float d0 = __fmul_rn(__fsub_rn(S.hi[r0 + lane], l0), 0.0625f);
+  const float d1 = __fmul_rn(__fsub_rn(S.hi[r0 + lane + 64], l1), 0.0625f);
   Wt.delta[wave][lane] = d0;
   Wt.delta[wave][lane + 64] = d1;
 #pragma unroll
@@ -705,18 +705,18 @@ struct alignas(16) SlotRecord {
   int32_t limbs[kMaxPasses][64][4];
 };
 
-// Per-block ranges (BLK): gamma, C_h and the fixed-point exponent change with
-// every 2048-key tile.  The first producer task of each item (its pass's first
-// slot group) also loads the tile's lo and hi of the 128 channels with its
-// planes and, once its codes are stored, writes this header beside them: the
-// pass's A operands (int8 limbs of gamma_h,slot = q_hc * delta_c,tile at the
-// tile's own exponent E_h), C_h,tile, 2^(E_h - 30) and the candidate bound.
-// The consumers read it with the codes, after the same fill wait.
-struct alignas(16) ItemHeader {
+// Per-block ranges (BLK): gamma and C_h change with every 2048-key tile.  The
+// block's set-up forms, for each of its tiles, delta_c,tile of every channel,
+// C_h,tile (in the slot table's fp64 order) and the candidate bound, and one
+// fixed-point exponent per head for all of its tiles, from the largest
+// |gamma| over them (quantisation error <= 2^-31 of that per weight, still
+// far inside the tolerance).  Every producer task, once its codes are
+// stored, writes the int8 limbs of its 8 slots' gamma = q_hc * delta_c,tile
+// beside them; consumers read those A operands with the codes, after the same
+// fill wait.
+constexpr int kBlkTiles = 16;  // tiles per block with per-block ranges (the launcher keeps to it)
+struct alignas(16) ItemLimbs {
   int32_t limbs[64][4];  // A operands of the item's pass (layout of s_limbs)
-  float delta[kD];       // delta_c of the item's tile
-  float C[kMaxGH], scale[kMaxGH];
-  int32_t ht[kMaxGH];    // hi_bound of the head's row (one-pass candidate scans)
 };
 
 // META: the sessions carry a side stream (its bytes are prefetched with the
@@ -743,16 +743,124 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   // producer task), [2..3] releases (one per consumer wave and item); counts
   // only grow during a launch
   __shared__ uint32_t s_ring[4];
-  // per-block ranges: the items' headers; q_hc and t_hc of the block's heads
-  // live where the per-layer limbs would
-  __shared__ typename std::conditional<BLK, ItemHeader[2], char>::type s_hdr;
-  float(*const s_bq)[kD] = reinterpret_cast<float(*)[kD]>(&s_limbs[0][0][0]);
-  uint8_t(*const s_bt)[kD] =
-      reinterpret_cast<uint8_t(*)[kD]>(reinterpret_cast<char *>(&s_limbs[0][0][0]) +
-                                       sizeof(float) * kMaxGH * kD);
+  // per-block ranges: the items' A operands, C_h and the candidate bound per
+  // tile
+  __shared__ typename std::conditional<BLK, ItemLimbs[2], char>::type s_hdr;
+  __shared__ typename std::conditional<BLK, float[kBlkTiles][kMaxGH], char>::type s_tC;
+  __shared__ typename std::conditional<BLK, float[kBlkTiles][kD], char>::type s_tD;
+  __shared__ typename std::conditional<BLK && MODE == kScanCand, int[kBlkTiles][kMaxGH],
+                                       char>::type s_tht;
+  __shared__ uint32_t s_gmax[kMaxGH];
+  // per-block ranges: q_hc of each slot's channel for the heads using the
+  // slot, else 0 (in place of the per-layer limbs)
+  float(*const s_gq)[kMaxGH] = reinterpret_cast<float(*)[kMaxGH]>(&s_limbs[0][0][0]);
+  static_assert(sizeof(float) * kMaxSlots * kMaxGH <= sizeof(s_limbs), "slot weights overlay");
   const int tid = threadIdx.x;
+  // Work items = (tile, pass) of this block's tiles in order; item i goes
+  // through code buffer i % 2.  Visited tile v of this block: all tiles, or
+  // (sample mode) nvtiles tiles spread evenly over the ntiles real ones.
+  const int tiles_per_block = S.tiles_per_block;
+  const int nvtiles = S.nvtiles, ntiles_real = S.ntiles;
+  auto real_tile = [&](int v) -> int {
+    return MODE == kScanSample ? (int)sample_tile(v, nvtiles, ntiles_real) : v;
+  };
+  int ntiles = 0;
+  while (ntiles < tiles_per_block && bw.tile0 + ntiles * bw.tile_step < nvtiles) ++ntiles;
+  // per-block ranges: wave w's first tile's lo and hi (channels lane, lane +
+  // 64), loaded before the set-up so that their latency overlaps it
+  float pf[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (BLK) {
+    const int wv = tid >> 6, ln = tid & 63;
+    if (wv < ntiles) {
+      const int64_t r0 = ((int64_t)g * S.rs + real_tile(bw.tile0 + wv * bw.tile_step)) * kD;
+      pf[0] = S.lo[r0 + ln];
+      pf[1] = S.lo[r0 + ln + 64];
+      pf[2] = S.hi[r0 + ln];
+      pf[3] = S.hi[r0 + ln + 64];
+    }
+  }
   SlotRecord *rec = S.table ? reinterpret_cast<SlotRecord *>(S.table) + bw.rec : nullptr;
-  if (!BLK && S.table_mode == kTableRead) {
+  if constexpr (BLK) {
+    // Slot order (from an earlier scan of the call, or built with unit
+    // weights), q and t of the block's heads, per-slot weights s_gq; then per
+    // tile delta_c, C_h and the heads' largest |gamma| (wave w takes tile w,
+    // lanes channels lane and lane + 64).
+    MfmaSetup<GH> &U = *reinterpret_cast<MfmaSetup<GH> *>(s_codes[0]);
+    if (S.table_mode == kTableRead) {
+      if (tid == 0) s_nslots = rec->nslots;
+      constexpr int kDescVec = sizeof(rec->desc) / 16;
+      if (tid < kDescVec)
+        reinterpret_cast<int4 *>(s_desc)[tid] = reinterpret_cast<const int4 *>(rec->desc)[tid];
+      for (int e = tid; e < GH * kD; e += kMThreads) {
+        U.X.q[e / kD][e % kD] = S.q[(int64_t)(head_base + e / kD) * kD + e % kD];
+        U.X.t[e / kD][e % kD] = S.plan[(int64_t)(head_base + e / kD) * kD + e % kD];
+      }
+    } else {
+      build_slot_table<GH>(U.T, U.X, S, g, head_base);
+      const int nslots = U.T.nslots;
+      if (tid == 0) s_nslots = nslots;
+      for (int e = tid; e < kMaxSlots; e += kMThreads)
+        s_desc[e] = e < nslots ? U.T.desc[e] : (int16_t)0;
+      if (S.table_mode == kTableWrite && bw.tile0 == 0) {
+        // for the later scans of this call (one block per kv head stores it)
+        if (tid == 0) rec->nslots = nslots;
+        for (int e = tid; e < kMaxSlots; e += kMThreads)
+          rec->desc[e] = e < nslots ? U.T.desc[e] : (int16_t)0;
+      }
+    }
+    if (tid < kMaxGH) s_gmax[tid] = 0u;
+    __syncthreads();
+    const int nslots = s_nslots;
+    for (int e = tid; e < kMaxSlots * GH; e += kMThreads) {
+      const int slot = e / GH, h = e % GH;
+      const int desc = s_desc[slot];
+      const int c = (desc >> 3) & (kD - 1), dep = desc & 7;
+      s_gq[slot][h] = slot < nslots && U.X.t[h][c] >= dep ? U.X.q[h][c] : 0.0f;
+    }
+    const int wv = tid >> 6, ln = tid & 63;
+    float m[GH];
+#pragma unroll
+    for (int j = 0; j < GH; ++j) m[j] = 0.0f;
+    static_assert(kBlkTiles <= kMThreads / 64, "one tile per wave");
+    if (wv < ntiles) {
+      const int ti = wv;
+      const float l0 = pf[0], l1 = pf[1];
+      const float d0 = __fmul_rn(__fsub_rn(pf[2], l0), 0.0625f);
+      const float d1 = __fmul_rn(__fsub_rn(pf[3], l1), 0.0625f);
+      s_tD[ti][ln] = d0;
+      s_tD[ti][ln + 64] = d1;
+#pragma unroll
+      for (int j = 0; j < GH; ++j) {
+        const int t0 = U.X.t[j][ln], t1 = U.X.t[j][ln + 64];
+        const float q0 = U.X.q[j][ln], q1 = U.X.q[j][ln + 64];
+        if (t0 > 0) m[j] = fmaxf(m[j], fabsf(__fmul_rn(q0, d0)));
+        if (t1 > 0) m[j] = fmaxf(m[j], fabsf(__fmul_rn(q1, d1)));
+        double v0 = (double)q0 * ((double)l0 + (double)d0 * (double)(1 << (4 - t0)) * 0.5);
+        double v1 = (double)q1 * ((double)l1 + (double)d1 * (double)(1 << (4 - t1)) * 0.5);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+          v0 = __dadd_rn(v0, __shfl_xor(v0, off));
+          v1 = __dadd_rn(v1, __shfl_xor(v1, off));
+        }
+        if (ln == 0) s_tC[ti][j] = (float)__dadd_rn(v0, v1);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < GH; ++j) {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m[j] = fmaxf(m[j], __shfl_xor(m[j], off));
+      if (ln == 0) atomicMax(&s_gmax[j], __float_as_uint(m[j]));
+    }
+    __syncthreads();
+    // one fixed-point exponent per head for the block's tiles
+    if (tid < GH) {
+      const float mx = __uint_as_float(s_gmax[tid]);
+      int e = 0;
+      if (mx > 0.0f) frexpf(mx, &e);
+      s_exp[tid] = e;
+      s_scale[tid] = ldexpf(1.0f, e - 30);
+    }
+  } else if (S.table_mode == kTableRead) {
     // the set-up an earlier scan of this call stored
     if (tid == 0) s_nslots = rec->nslots;
     if (tid < GH) {
@@ -772,18 +880,8 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
     const int nslots = T.nslots;
     const int ngroups = (nslots + 7) >> 3;
     const int npasses = max(1, (ngroups + kPassGroups - 1) / kPassGroups);
-    if constexpr (BLK) {
-      // slot order, q and t; the weights are formed per tile
-      if (tid == 0) s_nslots = nslots;
-      for (int e = tid; e < npasses * kPassGroups * 8; e += kMThreads)
-        s_desc[e] = e < nslots ? T.desc[e] : (int16_t)0;
-      for (int e = tid; e < GH * kD; e += kMThreads) {
-        s_bq[e / kD][e % kD] = U.X.q[e / kD][e % kD];
-        s_bt[e / kD][e % kD] = U.X.t[e / kD][e % kD];
-      }
-    }
     // fixed-point exponent per head
-    if (!BLK && tid < GH) {
+    if (tid < GH) {
       const float m = __uint_as_float(T.gmax[tid]);
       int e = 0;
       if (m > 0.0f) frexpf(m, &e);
@@ -791,16 +889,15 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
       s_scale[tid] = ldexpf(1.0f, e - 30);
       s_C[tid] = T.C[tid];
     }
-    if (!BLK && tid == 0) s_nslots = nslots;
-    if (!BLK)
-      for (int e = tid; e < npasses * kPassGroups * 8; e += kMThreads)
-        s_desc[e] = e < nslots ? T.desc[e] : (int16_t)0;
+    if (tid == 0) s_nslots = nslots;
+    for (int e = tid; e < npasses * kPassGroups * 8; e += kMThreads)
+      s_desc[e] = e < nslots ? T.desc[e] : (int16_t)0;
     __syncthreads();
     // A operands: lane l = row (head (l%16)/4, limb (l%16)%4), slot chunk l/16;
     // dword d, byte b <-> slot 64p + 16(l/16) + 8(d/2) + 2b + (d%2), the order
     // in which the code words are split into bytes below.
     uint8_t *limb_bytes = reinterpret_cast<uint8_t *>(&s_limbs[0][0][0]);
-    for (int idx = tid; idx < (BLK ? 0 : npasses * 64 * 16); idx += kMThreads) {
+    for (int idx = tid; idx < npasses * 64 * 16; idx += kMThreads) {
       const int p = idx >> 10, l = (idx >> 4) & 63, d = (idx >> 2) & 3, b = idx & 3;
       const int r = l & 15, h = r >> 2, limb = r & 3, j = l >> 4;
       const int slot = 64 * p + 16 * j + 8 * (d >> 1) + 2 * b + (d & 1);
@@ -827,6 +924,12 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
     if constexpr (MODE == kScanCandGroup) s_tf[tid] = key_threshold(S.thr[g]);
   }
   __syncthreads();  // the code table is free from here on
+  if constexpr (BLK && MODE == kScanCand) {
+    // integer candidate bound of each tile and head
+    for (int e = tid; e < ntiles * GH; e += kMThreads)
+      s_tht[e / GH][e % GH] = hi_bound(s_tf[e % GH], s_tC[e / GH][e % GH], s_scale[e % GH]);
+    __syncthreads();
+  }
   const int nslots = s_nslots;
   // per-block ranges: at least one slot group (padding slots read nothing),
   // whose producer task writes each item's header
@@ -855,14 +958,13 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   const int quarter = lane >> 4, m16 = lane & 15;
   const int hh = lane >> 4;  // head of this lane's results (MFMA row block)
   const float Ch = !BLK && hh < GH ? s_C[hh] : 0.0f;
-  const float scale = !BLK && hh < GH ? s_scale[hh] : 0.0f;
+  const float scale = hh < GH ? s_scale[hh] : 0.0f;
   const uint32_t *gplanes = S.planes + (int64_t)g * kD * kPlanes * W;
   const int64_t ld = S.ld;
   const uint8_t *meta = META && S.meta ? S.meta + (int64_t)g * n : nullptr;
   const float meta_scale = S.meta_scale;
   float *out_row = hh < GH ? S.logits + (int64_t)(head_base + hh) * ld : nullptr;
   const bool vec_out = S.vec_out != 0;
-  const int tiles_per_block = S.tiles_per_block;
   // One buffer resource over this kv head's planes (the launcher keeps them
   // within 2 GiB).  Plane slot s of channel c, word w sits at byte
   // c*chan_bytes + s*row_bytes + 4w; offsets at or past kUnread read 0 and
@@ -874,25 +976,7 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   // quarter k loads code bit k, i.e. plane slot 3 - k, words 4*m16 .. +3
   const uint32_t plane_sl = 3u - (uint32_t)quarter;
   const uint32_t lane_part = plane_sl * row_bytes + (uint32_t)m16 * 16u;
-  // per-block ranges: this kv head's rows of lo and hi ([d][rs]; the launcher
-  // keeps them within 2 GiB), channel c of tile t at byte 4 (c rs + t)
-  const uint32_t rs32 = BLK ? (uint32_t)S.rs : 0u;
-  const __amdgpu_buffer_rsrc_t rsrc_lo = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float *>(S.lo) + (int64_t)g * kD * rs32, (short)0, (int32_t)(kD * rs32 * 4u),
-      kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rsrc_hi = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float *>(S.hi) + (int64_t)g * kD * rs32, (short)0, (int32_t)(kD * rs32 * 4u),
-      kRsrcWord3);
 
-  // Work items = (tile, pass) of this block's tiles in order; item i goes
-  // through code buffer i % 2.  Visited tile v of this block: all tiles, or
-  // (sample mode) nvtiles tiles spread evenly over the ntiles real ones.
-  const int nvtiles = S.nvtiles, ntiles_real = S.ntiles;
-  auto real_tile = [&](int v) -> int {
-    return MODE == kScanSample ? (int)((int64_t)v * ntiles_real / nvtiles) : v;
-  };
-  int ntiles = 0;
-  while (ntiles < tiles_per_block && bw.tile0 + ntiles * bw.tile_step < nvtiles) ++ntiles;
   const int nitems = ntiles * npasses;
 
   // float threshold of this lane's output row (candidate modes)
@@ -919,18 +1003,16 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
       const int grp = live ? k - ti * ngroups : 0;
       const uint32_t tile = live ? (uint32_t)real_tile(bw.tile0 + ti * bw.tile_step) : 0u;
       const uint32_t tile_off = tile * (kMTileKeys / 8);
-      if constexpr (BLK) {
-        // the tile's lo and hi of channels lane and lane + 64 (header tasks)
-        const bool hdr = live && (grp & 7) == 0;
-        const uint32_t o0 = hdr ? ((uint32_t)lane * rs32 + tile) * 4u : kUnread;
-        const uint32_t o1 = hdr ? ((uint32_t)(lane + 64) * rs32 + tile) * 4u : kUnread;
-        rr[0] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_lo, (int32_t)o0, 0, 0);
-        rr[1] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_lo, (int32_t)o1, 0, 0);
-        rr[2] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_hi, (int32_t)o0, 0, 0);
-        rr[3] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_hi, (int32_t)o1, 0, 0);
-      }
       const uint4 dv = *reinterpret_cast<const uint4 *>(&s_desc[grp * 8]);
       const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
+      if constexpr (BLK) {
+        // the channels of this lane's two limb slots (slots 2 (lane / 16)
+        // and + 1 of the group; see item_limbs)
+        const uint32_t dl = (lane >> 4) == 0 ? dw[0] : (lane >> 4) == 1 ? dw[1]
+                          : (lane >> 4) == 2 ? dw[2] : dw[3];
+        rr[0] = (dl >> 3) & (kD - 1);
+        rr[1] = (dl >> 19) & (kD - 1);
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint32_t desc =
@@ -946,79 +1028,38 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
         x[4 * i + 3] = (uint32_t)v[3];
       }
     };
-    // per-block ranges: the header of pass p of a tile from its lo, hi
-    // (channels lane and lane + 64 in rr); see ItemHeader
-    auto item_header = [&](int p, ItemHeader &H, const uint32_t(&rr)[4]) {
-      const float l0 = __uint_as_float(rr[0]), l1 = __uint_as_float(rr[1]);
-      const float d0 = __fmul_rn(__fsub_rn(__uint_as_float(rr[2]), l0), 0.0625f);
-      const float d1 = __fmul_rn(__fsub_rn(__uint_as_float(rr[3]), l1), 0.0625f);
-      H.delta[lane] = d0;
-      H.delta[lane + 64] = d1;
-      int e[GH];
-      float Cv[GH], sc[GH];
+    // per-block ranges: the A-operand bytes of slot group gp (of the npg
+    // groups of pass p) for the block's tile ti.  Lane: row r = lane % 16
+    // (head r / 4, limb r % 4) of the group's slots 2 (lane / 16) and + 1,
+    // whose channels are rr[0], rr[1]; byte of (row, slot sl of the pass) in
+    // the operands: lane 16 (sl / 16) + row, dword 2 ((sl % 16) / 8) +
+    // sl % 2, byte (sl % 8) / 2.  The first group also clears the bytes of
+    // groups the pass lacks.
+    auto item_limbs = [&](int ti, int p, int gp, int npg, ItemLimbs &H, const uint32_t(&rr)[4]) {
+      if constexpr (BLK) {
+        const int r = lane & 15, ha = r >> 2, limb = r & 3;
+        const int ea = s_exp[ha < GH ? ha : 0];
+        uint8_t *lb = reinterpret_cast<uint8_t *>(&H.limbs[0][0]);
 #pragma unroll
-      for (int j = 0; j < GH; ++j) {
-        const int t0 = s_bt[j][lane], t1 = s_bt[j][lane + 64];
-        const float q0 = s_bq[j][lane], q1 = s_bq[j][lane + 64];
-        // max |gamma| over the channels the head reads (its slots' weights)
-        float m = fmaxf(t0 > 0 ? fabsf(__fmul_rn(q0, d0)) : 0.0f,
-                        t1 > 0 ? fabsf(__fmul_rn(q1, d1)) : 0.0f);
-        // C_h in the slot table's fp64 order
-        double v0 = (double)q0 * ((double)l0 + (double)d0 * (double)(1 << (4 - t0)) * 0.5);
-        double v1 = (double)q1 * ((double)l1 + (double)d1 * (double)(1 << (4 - t1)) * 0.5);
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-          m = fmaxf(m, __shfl_xor(m, off));
-          v0 = __dadd_rn(v0, __shfl_xor(v0, off));
-          v1 = __dadd_rn(v1, __shfl_xor(v1, off));
-        }
-        e[j] = 0;
-        if (m > 0.0f) frexpf(m, &e[j]);
-        sc[j] = ldexpf(1.0f, e[j] - 30);
-        Cv[j] = (float)__dadd_rn(v0, v1);
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile's deltas are stored
-      // A operands of pass p (the set-up's layout and limb split)
-      const int r = lane & 15, ha = r >> 2, limb = r & 3, ja = lane >> 4;
-      int ea = e[0];
-#pragma unroll
-      for (int j = 1; j < GH; ++j) ea = ha == j ? e[j] : ea;
-      const int nslots_ = s_nslots;
-      int32_t dw[4];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          const int slot = 64 * p + 16 * ja + 8 * (d >> 1) + 2 * bb + (d & 1);
+        for (int u = 0; u < 2; ++u) {
+          const int sl = 8 * gp + 2 * (lane >> 4) + u;
+          const int slot = 64 * p + sl;
+          const float gq = ha < GH ? s_gq[slot][ha] : 0.0f;  // 0: head does not use the slot
           int v = 0;
-          if (ha < GH && slot < nslots_) {
-            const int desc = s_desc[slot];
-            const int c = (desc >> 3) & (kD - 1), dep = desc & 7;
-            if (s_bt[ha][c] >= dep) {
-              int G = (int)rintf(ldexpf(__fmul_rn(s_bq[ha][c], H.delta[c]), 30 - ea));
-              for (int i = 0; i < limb; ++i) {
-                const int dg = ((G + 128) & 255) - 128;
-                G = (G - dg) >> 8;
-              }
-              v = ((G + 128) & 255) - 128;
+          if (gq != 0.0f) {
+            int G = (int)rintf(ldexpf(__fmul_rn(gq, s_tD[ti][rr[u]]), 30 - ea));
+            for (int i = 0; i < limb; ++i) {
+              const int dg = ((G + 128) & 255) - 128;
+              G = (G - dg) >> 8;
             }
+            v = ((G + 128) & 255) - 128;
           }
-          word |= (uint32_t)(uint8_t)(int8_t)v << (8 * bb);
+          lb[((16 * (sl >> 4) + r) * 4 + 2 * ((sl & 15) >> 3) + (sl & 1)) * 4 + ((sl & 7) >> 1)] =
+              (uint8_t)(int8_t)v;
         }
-        dw[d] = (int32_t)word;
-      }
-      *reinterpret_cast<int4 *>(&H.limbs[lane][0]) = make_int4(dw[0], dw[1], dw[2], dw[3]);
-      if (lane < GH) {
-        float cl = Cv[0], sl = sc[0];
-#pragma unroll
-        for (int j = 1; j < GH; ++j) {
-          cl = lane == j ? Cv[j] : cl;
-          sl = lane == j ? sc[j] : sl;
-        }
-        H.C[lane] = cl;
-        H.scale[lane] = sl;
-        H.ht[lane] = MODE == kScanCand ? hi_bound(s_tf[lane], cl, sl) : 0;
+        if (gp == 0)
+          for (int g2 = npg; g2 < kPassGroups; ++g2)
+            if (lane < 32) H.limbs[16 * (g2 >> 1) + (lane & 15)][2 * (g2 & 1) + (lane >> 4)] = 0;
       }
     };
     // regroup and transpose task k's words in place and store them in its
@@ -1056,7 +1097,7 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
 #pragma unroll
       for (int t = 0; t < 32; ++t) dst[t] = x[t];
       if constexpr (BLK)
-        if ((grp & 7) == 0) item_header(grp >> 3, s_hdr[b], rr);
+        item_limbs(ti, grp >> 3, grp & 7, min(kPassGroups, ngroups - (grp & ~7)), s_hdr[b], rr);
       ring_signal(&s_ring[b]);  // one group of the buffer filled
     };
     uint32_t x0[32], x1[32], r0[4] = {0u, 0u, 0u, 0u}, r1[4] = {0u, 0u, 0u, 0u};
@@ -1099,20 +1140,21 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
       }
       int4 av;
       if constexpr (!BLK) av = *reinterpret_cast<const int4 *>(&s_limbs[p][lane][0]);
-      ring_wait(&s_ring[b], fill_target[b]);  // every group of the item stored
-      // per-block ranges: this item's operands, C_h and scale from its header
-      float Cit = Ch, sit = scale;
+      // per-block ranges: the tile's C_h and bound (the item's operands are
+      // read after the fill wait, beside its codes)
+      float Cit = Ch;
+      const float sit = scale;
       int htit = INT_MAX;
       if constexpr (BLK) {
-        av = *reinterpret_cast<const int4 *>(&s_hdr[b].limbs[lane][0]);
         if (hh < GH) {
-          Cit = s_hdr[b].C[hh];
-          sit = s_hdr[b].scale[hh];
-          htit = s_hdr[b].ht[hh];
+          Cit = s_tC[ti][hh];
+          if constexpr (MODE == kScanCand) htit = s_tht[ti][hh];
         }
       } else if (MODE == kScanCand && hh < GH) {
         htit = s_ht[hh];
       }
+      ring_wait(&s_ring[b], fill_target[b]);  // every group of the item stored
+      if constexpr (BLK) av = *reinterpret_cast<const int4 *>(&s_hdr[b].limbs[lane][0]);
       const v4i A = v4i{av.x, av.y, av.z, av.w};
       if (p == 0) {
 #pragma unroll
@@ -1539,6 +1581,9 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_
       if (one_block_per_head) tpb = std::max<int64_t>(1, tiles);
       if (total_tiles > target_blocks) tpb = std::max(tpb, (total_tiles + target_blocks - 1) / target_blocks);
       if (cand) tpb = std::max(tpb, (tiles + kMaxSeg - 1) / kMaxSeg);  // segments per row
+      // per-block ranges: a block keeps C_h of each of its tiles in LDS (at
+      // most 2^25 keys: 16 tiles per segment, within the cap)
+      if (blk && !fp32_path) tpb = std::min<int64_t>(tpb, kBlkTiles);
       tpb_s[j] = std::max<int64_t>(1, std::min<int64_t>(tpb, tiles));
       if (nseg_out) nseg_out[s0 + j] = (int32_t)((tiles + tpb_s[j] - 1) / tpb_s[j]);
     }
@@ -1573,9 +1618,8 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_
         o.ovf = in.ovf;
         o.redo = in.redo;
         o.rs = in.rs;
-        // slot records hold per-layer weights: per-block scans build their own
-        o.table = fp32_path || blk ? nullptr : in.table;
-        o.table_mode = fp32_path || blk || !in.table ? kTableNone : in.table_mode;
+        o.table = fp32_path ? nullptr : in.table;
+        o.table_mode = fp32_path || !in.table ? kTableNone : in.table_mode;
         const int64_t tiles = visited(in.n);
         o.nvtiles = (int32_t)tiles;
         o.ntiles = (int32_t)((in.n + tile_keys - 1) / tile_keys);

@@ -4,7 +4,8 @@
 // written when a row needs them.
 //
 // With device-resident planes the steps are:
-//   1. sample scan    logits of 8 tiles (16384 keys) spread over each row,
+//   1. sample scan    logits of 32 tiles (65536 keys), the middle tiles of 32
+//                     equal strata of each row (one round of scan blocks),
 //   2. threshold      per output row, a key T expected to leave ~2.5k of the
 //                     row's n scores at or above it (all keys when n <= 8192),
 //   3. candidate scan every key scored again, the (score key, index) words of
@@ -43,7 +44,7 @@ int64_t sampled_keys(int64_t n) {
   const int64_t ns = std::min<int64_t>(nt, kSampleTiles);
   int64_t m = 0;
   for (int64_t j = 0; j < ns; ++j) {
-    const int64_t t = j * nt / ns;
+    const int64_t t = sample_tile(j, ns, nt);
     m += std::min<int64_t>(kBlockKeys, n - t * kBlockKeys);
   }
   return m;

@@ -51,7 +51,7 @@ def u32(t):
 
 def block_scale(q, lo, hi, group):
     """A_h with each channel's largest |lo_b|, |hi_b| over its blocks."""
-    m = np.maximum(np.abs(lo), np.abs(hi)).max(-1)
+    m = np.maximum(np.abs(lo), np.abs(hi)).max(1)
     return logit_scale(q, m, m, group)
 
 
@@ -82,10 +82,10 @@ def grow(F, orc, keys, n0, chunks, capacity):
     R = orc.range_blocks(capacity)
     W = F.plane_words(capacity)
     planes = torch.zeros((hkv, 128, 4, W), dtype=torch.int32, device=dev())
-    lo = torch.zeros((hkv, 128, R), dtype=torch.float32, device=dev())
+    lo = torch.zeros((hkv, R, 128), dtype=torch.float32, device=dev())
     hi = torch.zeros_like(lo)
     rp = np.zeros((hkv, 128, 4, W), np.uint32)
-    rlo = np.zeros((hkv, 128, R), np.float32)
+    rlo = np.zeros((hkv, R, 128), np.float32)
     rhi = np.zeros_like(rlo)
     kn = keys_np(keys)
     if n0 > 0:
@@ -183,8 +183,7 @@ def test_scan_blocked_mixed_depths(F, orc, pinned):
         planes.copy_(p.planes)
     L = F.scan_blocked(planes, p.lo, p.hi, n, q.to(dev()), torch.from_numpy(pn).to(dev()))
     torch.cuda.synchronize()
-    R = orc.scan_blocked(ref["planes"], ref["lo"][..., :orc.range_blocks(n)],
-                         ref["hi"][..., :orc.range_blocks(n)], n, q.numpy(), pn)
+    R = orc.scan_blocked(ref["planes"], ref["lo"], ref["hi"], n, q.numpy(), pn)
     assert_logits_close(L.cpu().numpy(), R, block_scale(q.numpy(), ref["lo"], ref["hi"], 4))
 
 
@@ -199,8 +198,8 @@ def test_scan_blocked_equals_per_layer_scan(F, pinned, n):
     p = F.pack(keys)
     plan = F.plan(q, p.sigma2, B)
     R = F.range_blocks(n)
-    lo = p.lo[..., None].expand(hkv, 128, R).contiguous()
-    hi = p.hi[..., None].expand(hkv, 128, R).contiguous()
+    lo = p.lo[:, None, :].expand(hkv, R, 128).contiguous()
+    hi = p.hi[:, None, :].expand(hkv, R, 128).contiguous()
     planes = p.planes
     if pinned:
         planes = torch.empty(p.planes.shape, dtype=torch.int32, pin_memory=True)
@@ -212,7 +211,7 @@ def test_scan_blocked_equals_per_layer_scan(F, pinned, n):
     assert torch.equal(a, b)
     if n <= RB:
         pb = F.pack_blocked(keys)
-        assert torch.equal(pb.lo[..., 0], p.lo) and torch.equal(pb.hi[..., 0], p.hi)
+        assert torch.equal(pb.lo[:, 0], p.lo) and torch.equal(pb.hi[:, 0], p.hi)
         assert torch.equal(pb.sigma2, p.sigma2) and torch.equal(pb.planes, p.planes)
 
 

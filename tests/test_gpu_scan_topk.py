@@ -124,13 +124,15 @@ def test_scan_topk_sample_misled_recomputes(F):
     """Keys of the sampled tiles made much larger in one channel: the sampled
     threshold is far from the rest of the row, so candidate counts fall
     outside [k, 8192] and rows are recomputed; results still match."""
-    n = 64 * 2048
+    n = 256 * 2048
     hkv, hq = 2, 8
-    keys = synth.keys(530, 0, n, hkv, 128, torch.float32, 0, device=dev())
+    keys = synth.keys(530, 0, n, hkv, 128, torch.float16, 0, device=dev())
     q = synth.queries(530, 0, hq, 128, device=dev())
     ntiles = n // 2048
-    for j in range(8):
-        t = j * ntiles // 8
+    # the sampled tiles: the middle tile of each of 32 equal stretches (an
+    # eighth of this row)
+    for j in range(32):
+        t = (2 * j + 1) * ntiles // 64
         keys[t * 2048:(t + 1) * 2048, :, 0] += 60.0
     p = F.pack(keys)
     # kv head 0's query heads weigh the planted channel up, kv head 1's down

@@ -50,8 +50,8 @@ def test_one_block_is_the_per_layer_pack(orc, n):
     a = orc.pack(k)
     b = orc.pack_blocked(k)
     np.testing.assert_array_equal(b["planes"], a["planes"])
-    np.testing.assert_array_equal(b["lo"][..., 0], a["lo"])
-    np.testing.assert_array_equal(b["hi"][..., 0], a["hi"])
+    np.testing.assert_array_equal(b["lo"][:, 0], a["lo"])
+    np.testing.assert_array_equal(b["hi"][:, 0], a["hi"])
     np.testing.assert_array_equal(b["sigma2"], a["sigma2"])
 
 
@@ -66,7 +66,7 @@ def test_block_codes_are_the_block_quantiser(orc, n):
             for blk in range(-(-n // RB)):
                 x = k[blk * RB:(blk + 1) * RB, h, c]
                 lo, hi = np.float32(x.min() + 0), np.float32(x.max() + 0)
-                assert b["lo"][h, c, blk] == lo and b["hi"][h, c, blk] == hi
+                assert b["lo"][h, blk, c] == lo and b["hi"][h, blk, c] == hi
                 np.testing.assert_array_equal(codes[h, c, blk * RB:(blk + 1) * RB],
                                               np_block_codes(x, lo, hi))
     # padding bits stay zero
@@ -84,7 +84,7 @@ def test_block_prefix_invariant(orc):
     for t in range(5):
         for blk in range(3):
             x = k[blk * RB:(blk + 1) * RB, 0, 3]
-            lo, hi = b["lo"][0, 3, blk], b["hi"][0, 3, blk]
+            lo, hi = b["lo"][0, blk, 3], b["hi"][0, blk, 3]
             want = t_bit_quantizer(x, lo, hi, t)
             got = codes[0, 3, blk * RB:(blk + 1) * RB] >> (4 - t)
             np.testing.assert_array_equal(got, want)
@@ -100,7 +100,7 @@ def test_sigma2_is_pooled_within_block_variance(orc):
         for c in range(d):
             tot = 0.0
             for blk in range(3):
-                lo, hi = np.float64(b["lo"][h, c, blk]), np.float64(b["hi"][h, c, blk])
+                lo, hi = np.float64(b["lo"][h, blk, c]), np.float64(b["hi"][h, blk, c])
                 delta = np.float64(np.float32(np.float32(hi - lo) * np.float32(0.0625)))
                 cb = codes[h, c, blk * RB:(blk + 1) * RB].astype(np.float64)
                 deq = lo + (cb + 0.5) * delta
@@ -120,8 +120,8 @@ def test_blocks_with_the_layer_range_equal_the_per_layer_layer(orc):
     b = orc.pack_blocked(k)
     np.testing.assert_array_equal(b["planes"], a["planes"])
     for blk in range(4):
-        np.testing.assert_array_equal(b["lo"][..., blk], a["lo"])
-        np.testing.assert_array_equal(b["hi"][..., blk], a["hi"])
+        np.testing.assert_array_equal(b["lo"][:, blk], a["lo"])
+        np.testing.assert_array_equal(b["hi"][:, blk], a["hi"])
     rng = np.random.default_rng(6)
     q = rng.standard_normal((4, 8)).astype(np.float32)
     plan = orc.plan(q, a["sigma2"], 14)
@@ -159,7 +159,7 @@ def test_blocked_scan_is_the_t_bit_reconstruction_of_the_raw_keys(orc, B):
             t = int(plan[h, c])
             for blk in range(3):
                 sl = slice(blk * RB, min((blk + 1) * RB, n))
-                lo, hi = b["lo"][g, c, blk], b["hi"][g, c, blk]
+                lo, hi = b["lo"][g, blk, c], b["hi"][g, blk, c]
                 delta = np.float64(np.float32(np.float32(hi - lo) * np.float32(0.0625)))
                 r = t_bit_quantizer(k[sl, g, c], lo, hi, t)     # from the raw keys
                 cell = delta * 2.0 ** (4 - t)
@@ -181,10 +181,10 @@ def fresh(orc, k, n0, n_cap):
     planes = np.zeros((hkv, d, 4, W), np.uint32)
     planes[..., :p["planes"].shape[-1]] = p["planes"]
     nbc = -(-n_cap // RB)
-    lo = np.zeros((hkv, d, nbc), np.float32)
-    hi = np.zeros((hkv, d, nbc), np.float32)
-    lo[..., :p["lo"].shape[-1]] = p["lo"]
-    hi[..., :p["hi"].shape[-1]] = p["hi"]
+    lo = np.zeros((hkv, nbc, d), np.float32)
+    hi = np.zeros((hkv, nbc, d), np.float32)
+    lo[:, :p["lo"].shape[1]] = p["lo"]
+    hi[:, :p["hi"].shape[1]] = p["hi"]
     return planes, lo, hi
 
 
@@ -217,8 +217,8 @@ def test_append_new_blocks_inherit_and_widen_the_previous_range(orc):
     for h in range(hkv):
         for c in range(d):
             # block 1 existed: its range is kept and its new keys clamp
-            l1, h1 = lo_before[h, c, 1], hi_before[h, c, 1]
-            assert lo[h, c, 1] == l1 and hi[h, c, 1] == h1
+            l1, h1 = lo_before[h, 1, c], hi_before[h, 1, c]
+            assert lo[h, 1, c] == l1 and hi[h, 1, c] == h1
             x = k[n0:2 * RB, h, c]
             want_clamped += int(((x < l1) | (x > h1)).sum())
             np.testing.assert_array_equal(codes[h, c, n0:2 * RB], np_block_codes(x, l1, h1))
@@ -228,7 +228,7 @@ def test_append_new_blocks_inherit_and_widen_the_previous_range(orc):
                 x = k[blk * RB:min((blk + 1) * RB, n), h, c]
                 nl = np.float32(min(pl, x.min()) + 0)
                 nh = np.float32(max(ph, x.max()) + 0)
-                assert lo[h, c, blk] == nl and hi[h, c, blk] == nh
+                assert lo[h, blk, c] == nl and hi[h, blk, c] == nh
                 np.testing.assert_array_equal(codes[h, c, blk * RB:blk * RB + x.size],
                                               np_block_codes(x, nl, nh))
                 pl, ph = nl, nh
@@ -240,8 +240,8 @@ def test_append_block_zero_takes_its_own_range(orc):
     k = keys_for(11, n)
     hkv, d = k.shape[1:]
     planes = np.zeros((hkv, d, 4, orc.plane_words(n)), np.uint32)
-    lo = np.zeros((hkv, d, 1), np.float32)
-    hi = np.zeros((hkv, d, 1), np.float32)
+    lo = np.zeros((hkv, 1, d), np.float32)
+    hi = np.zeros((hkv, 1, d), np.float32)
     assert orc.append_blocked(k, 0, planes, lo, hi) == 0
     full = orc.pack_blocked(k)
     np.testing.assert_array_equal(planes, full["planes"])
@@ -285,4 +285,4 @@ def test_blocked_rejects_bad_arguments(orc):
     q = np.ones((2, 8), np.float32)
     plan = np.zeros((2, 8), np.uint8)
     with pytest.raises(ValueError):
-        orc.scan_blocked(b["planes"], b["lo"][..., :1], b["hi"][..., :1], 3000, q, plan)
+        orc.scan_blocked(b["planes"], b["lo"][:, :1], b["hi"][:, :1], 3000, q, plan)
