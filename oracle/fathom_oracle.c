@@ -302,41 +302,85 @@ static int orc_code_from_planes(const uint32_t *planes, int64_t W, int d, int h,
  * planes of a channel are that channel's t-bit quantiser. */
 static int orc_prefix(int code, int t) { return t == 0 ? 0 : code >> (4 - t); }
 
-/* Scan.  [EXP] core method, read side: the query reads, per channel, only the
- * planes its plan gives that channel, and scores every key.  Reading R11: the
- * unread low bits sit at their midpoint, i.e. the t-bit prefix r is
+/* The side stream of the fixed-width baselines (R10), value of key i of kv
+ * head g: 8 bits: meta [hkv][n], one byte per key; 4 bits (the r = 16 form,
+ * whose metadata is r/4 bits per key): meta [hkv][ceil(n/2)], two keys per
+ * byte, key i in the low nibble of byte i/2 when i is even, the high nibble
+ * when it is odd. */
+static double orc_meta(const uint8_t *meta, int bits, int g, int64_t n, int64_t i) {
+  if (bits == 8) return (double)meta[(int64_t)g * n + i];
+  const uint8_t b = meta[(int64_t)g * ((n + 1) / 2) + i / 2];
+  return (double)((b >> (4 * (i & 1))) & 15);
+}
+
+/* Score of key i for query head h.  [EXP] core method, read side: the query
+ * reads, per channel, only the planes its plan gives that channel.  Reading
+ * R11: the unread low bits sit at their midpoint, i.e. the t-bit prefix r is
  * reconstructed at the centre of its cell of width delta*2^(4-t):
  *     deq_t = lo + (r + 1/2) * delta * 2^(4-t)       (t = 0: lo + 8*delta),
  *     s_i   = sum_c q_c * deq_{t_c}(code_ic)  [+ meta_scale * meta_i],
- * evaluated in fp64 and rounded once to fp32.  meta [hkv][n] is the optional
- * 8-bit per-key side stream of the fixed-width baseline (R10).
- * logits [hq][ld]. */
-int orc_scan(const uint32_t *planes, const float *lo, const float *hi, int64_t n,
-             int hkv, int d, const float *q, const uint8_t *plan, int hq,
-             const uint8_t *meta, float meta_scale, float *logits, int64_t ld) {
+ * evaluated in fp64 (rounded once to fp32 by the callers). */
+static double orc_score(const uint32_t *planes, int64_t W, const float *lo, const float *hi,
+                        int64_t n, int d, int g, const float *qh, const uint8_t *ph,
+                        const uint8_t *meta, int bits, float meta_scale, int64_t i) {
+  double s = 0.0;
+  for (int c = 0; c < d; ++c) {
+    int t = ph[c];
+    float l = lo[g * d + c], u = hi[g * d + c];
+    float delta = (u - l) * 0.0625f;
+    int r = orc_prefix(orc_code_from_planes(planes, W, d, g, c, i), t);
+    double cell = (double)delta * (double)(1 << (4 - t));
+    double deq = (double)l + ((double)r + 0.5) * cell;
+    s += (double)qh[c] * deq;
+  }
+  if (meta) s += (double)meta_scale * orc_meta(meta, bits, g, n, i);
+  return s;
+}
+
+static int orc_scan_bits(const uint32_t *planes, const float *lo, const float *hi, int64_t n,
+                         int hkv, int d, const float *q, const uint8_t *plan, int hq,
+                         const uint8_t *meta, int bits, float meta_scale, float *logits,
+                         int64_t ld) {
   if (!planes || !lo || !hi || !q || !plan || !logits || n < 0 || hkv < 1 ||
       hq % hkv || ld < n)
     return ORC_BAD;
   const int G = hq / hkv;
   const int64_t W = orc_plane_words(n);
-  for (int h = 0; h < hq; ++h) {
-    const int g = h / G;
-    for (int64_t i = 0; i < n; ++i) {
-      double s = 0.0;
-      for (int c = 0; c < d; ++c) {
-        int t = plan[(int64_t)h * d + c];
-        float l = lo[g * d + c], u = hi[g * d + c];
-        float delta = (u - l) * 0.0625f;
-        int r = orc_prefix(orc_code_from_planes(planes, W, d, g, c, i), t);
-        double cell = (double)delta * (double)(1 << (4 - t));
-        double deq = (double)l + ((double)r + 0.5) * cell;
-        s += (double)q[(int64_t)h * d + c] * deq;
-      }
-      if (meta) s += (double)meta_scale * (double)meta[(int64_t)g * n + i];
-      logits[(int64_t)h * ld + i] = (float)s;
-    }
-  }
+  for (int h = 0; h < hq; ++h)
+    for (int64_t i = 0; i < n; ++i)
+      logits[(int64_t)h * ld + i] =
+          (float)orc_score(planes, W, lo, hi, n, d, h / G, q + (int64_t)h * d,
+                           plan + (int64_t)h * d, meta, bits, meta_scale, i);
   return ORC_OK;
+}
+
+static int orc_scan_at_bits(const uint32_t *planes, const float *lo, const float *hi,
+                            int64_t n, int hkv, int d, const float *q, const uint8_t *plan,
+                            int hq, const uint8_t *meta, int bits, float meta_scale,
+                            const int64_t *keys, int64_t nk, float *out) {
+  if (!planes || !lo || !hi || !q || !plan || !keys || !out || hkv < 1 ||
+      hq % hkv)
+    return ORC_BAD;
+  const int G = hq / hkv;
+  const int64_t W = orc_plane_words(n);
+  for (int h = 0; h < hq; ++h)
+    for (int64_t j = 0; j < nk; ++j) {
+      const int64_t i = keys[j];
+      if (i < 0 || i >= n) return ORC_BAD;
+      out[(int64_t)h * nk + j] =
+          (float)orc_score(planes, W, lo, hi, n, d, h / G, q + (int64_t)h * d,
+                           plan + (int64_t)h * d, meta, bits, meta_scale, i);
+    }
+  return ORC_OK;
+}
+
+/* Scan: every key's score (orc_score) for every query head, logits [hq][ld];
+ * meta: the optional 8-bit side stream [hkv][n]. */
+int orc_scan(const uint32_t *planes, const float *lo, const float *hi, int64_t n,
+             int hkv, int d, const float *q, const uint8_t *plan, int hq,
+             const uint8_t *meta, float meta_scale, float *logits, int64_t ld) {
+  return orc_scan_bits(planes, lo, hi, n, hkv, d, q, plan, hq, meta, 8, meta_scale, logits,
+                       ld);
 }
 
 /* The same scores at chosen keys only: out[h][j] = s_{keys[j]} of head h
@@ -345,31 +389,25 @@ int orc_scan_at(const uint32_t *planes, const float *lo, const float *hi,
                 int64_t n, int hkv, int d, const float *q, const uint8_t *plan,
                 int hq, const uint8_t *meta, float meta_scale,
                 const int64_t *keys, int64_t nk, float *out) {
-  if (!planes || !lo || !hi || !q || !plan || !keys || !out || hkv < 1 ||
-      hq % hkv)
-    return ORC_BAD;
-  const int G = hq / hkv;
-  const int64_t W = orc_plane_words(n);
-  for (int h = 0; h < hq; ++h) {
-    const int g = h / G;
-    for (int64_t j = 0; j < nk; ++j) {
-      const int64_t i = keys[j];
-      if (i < 0 || i >= n) return ORC_BAD;
-      double s = 0.0;
-      for (int c = 0; c < d; ++c) {
-        int t = plan[(int64_t)h * d + c];
-        float l = lo[g * d + c], u = hi[g * d + c];
-        float delta = (u - l) * 0.0625f;
-        int r = orc_prefix(orc_code_from_planes(planes, W, d, g, c, i), t);
-        double cell = (double)delta * (double)(1 << (4 - t));
-        double deq = (double)l + ((double)r + 0.5) * cell;
-        s += (double)q[(int64_t)h * d + c] * deq;
-      }
-      if (meta) s += (double)meta_scale * (double)meta[(int64_t)g * n + i];
-      out[(int64_t)h * nk + j] = (float)s;
-    }
-  }
-  return ORC_OK;
+  return orc_scan_at_bits(planes, lo, hi, n, hkv, d, q, plan, hq, meta, 8, meta_scale, keys,
+                          nk, out);
+}
+
+/* orc_scan and orc_scan_at with the 4-bit side stream (meta [hkv][ceil(n/2)],
+ * see orc_meta). */
+int orc_scan_meta4(const uint32_t *planes, const float *lo, const float *hi, int64_t n,
+                   int hkv, int d, const float *q, const uint8_t *plan, int hq,
+                   const uint8_t *meta, float meta_scale, float *logits, int64_t ld) {
+  return orc_scan_bits(planes, lo, hi, n, hkv, d, q, plan, hq, meta, 4, meta_scale, logits,
+                       ld);
+}
+
+int orc_scan_at_meta4(const uint32_t *planes, const float *lo, const float *hi,
+                      int64_t n, int hkv, int d, const float *q, const uint8_t *plan,
+                      int hq, const uint8_t *meta, float meta_scale,
+                      const int64_t *keys, int64_t nk, float *out) {
+  return orc_scan_at_bits(planes, lo, hi, n, hkv, d, q, plan, hq, meta, 4, meta_scale, keys,
+                          nk, out);
 }
 
 /* The plane reads themselves: out[h][i][c] = t_c-bit prefix of code_ic. */

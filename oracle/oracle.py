@@ -51,6 +51,8 @@ def _load():
         lib.orc_plan_group.argtypes = [P, I, I, I, P, P, P]
         lib.orc_scan.argtypes = [P, P, P, L, I, I, P, P, I, P, F, P, L]
         lib.orc_scan_at.argtypes = [P, P, P, L, I, I, P, P, I, P, F, P, L, P]
+        lib.orc_scan_meta4.argtypes = [P, P, P, L, I, I, P, P, I, P, F, P, L]
+        lib.orc_scan_at_meta4.argtypes = [P, P, P, L, I, I, P, P, I, P, F, P, L, P]
         lib.orc_read_prefixes.argtypes = [P, L, I, I, P, I, P]
         lib.orc_topk.argtypes = [P, I, L, L, I, I, P, P]
         lib.orc_append.argtypes = [P, L, I, I, L, L, L, P, L, P, P, P]
@@ -66,7 +68,7 @@ def _load():
         lib.orc_plan_calibrated_group.argtypes = [P, I, I, I, P, P, P, P, P]
         lib.orc_sparse_attention.argtypes = [P, I, I, I, P, P, L, L, L, P, I, I, F, P, P]
         for f in ("orc_pack", "orc_plan", "orc_plan_fixed", "orc_plan_rd", "orc_plan_group",
-                  "orc_scan", "orc_scan_at",
+                  "orc_scan", "orc_scan_at", "orc_scan_meta4", "orc_scan_at_meta4",
                   "orc_read_prefixes", "orc_topk", "orc_sparse_attention", "orc_append", "orc_code_hist", "orc_depth_errors",
                   "orc_plan_calibrated", "orc_plan_calibrated_group", "orc_pack_blocked",
                   "orc_scan_blocked", "orc_scan_blocked_at", "orc_append_blocked"):
@@ -154,8 +156,11 @@ def plan_fixed(q: np.ndarray, r: int) -> np.ndarray:
     return out
 
 
-def scan(planes, lo, hi, n: int, q, plan_, meta=None, meta_scale: float = 0.0):
-    """-> logits [hq][n] fp32 (computed in fp64, rounded once)."""
+def scan(planes, lo, hi, n: int, q, plan_, meta=None, meta_scale: float = 0.0,
+         meta_bits: int = 8):
+    """-> logits [hq][n] fp32 (computed in fp64, rounded once).  meta: the
+    side stream, uint8 [hkv][n] (meta_bits 8) or packed nibbles uint8
+    [hkv][ceil(n/2)] (meta_bits 4, even keys in the low nibble)."""
     planes = np.ascontiguousarray(planes, dtype=np.uint32)
     lo = np.ascontiguousarray(lo, dtype=np.float32)
     hi = np.ascontiguousarray(hi, dtype=np.float32)
@@ -166,13 +171,14 @@ def scan(planes, lo, hi, n: int, q, plan_, meta=None, meta_scale: float = 0.0):
     if meta is not None:
         meta = np.ascontiguousarray(meta, dtype=np.uint8)
     out = np.empty((hq, max(n, 1)), np.float32)
-    _check(_load().orc_scan(_ptr(planes), _ptr(lo), _ptr(hi), n, hkv, d, _ptr(q),
-                            _ptr(plan_), hq, _ptr(meta), meta_scale, _ptr(out),
-                            max(n, 1)), "scan")
+    fn = _load().orc_scan if meta_bits == 8 else _load().orc_scan_meta4
+    _check(fn(_ptr(planes), _ptr(lo), _ptr(hi), n, hkv, d, _ptr(q), _ptr(plan_), hq,
+              _ptr(meta), meta_scale, _ptr(out), max(n, 1)), "scan")
     return out[:, :n]
 
 
-def scan_at(planes, lo, hi, n: int, q, plan_, keys, meta=None, meta_scale: float = 0.0):
+def scan_at(planes, lo, hi, n: int, q, plan_, keys, meta=None, meta_scale: float = 0.0,
+            meta_bits: int = 8):
     """Scores of the chosen key indices only -> [hq][len(keys)] fp32."""
     planes = np.ascontiguousarray(planes, dtype=np.uint32)
     lo = np.ascontiguousarray(lo, dtype=np.float32)
@@ -185,9 +191,9 @@ def scan_at(planes, lo, hi, n: int, q, plan_, keys, meta=None, meta_scale: float
     if meta is not None:
         meta = np.ascontiguousarray(meta, dtype=np.uint8)
     out = np.empty((hq, keys.size), np.float32)
-    _check(_load().orc_scan_at(_ptr(planes), _ptr(lo), _ptr(hi), n, hkv, d, _ptr(q),
-                               _ptr(plan_), hq, _ptr(meta), meta_scale, _ptr(keys),
-                               keys.size, _ptr(out)), "scan_at")
+    fn = _load().orc_scan_at if meta_bits == 8 else _load().orc_scan_at_meta4
+    _check(fn(_ptr(planes), _ptr(lo), _ptr(hi), n, hkv, d, _ptr(q), _ptr(plan_), hq,
+              _ptr(meta), meta_scale, _ptr(keys), keys.size, _ptr(out)), "scan_at")
     return out
 
 

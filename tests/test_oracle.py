@@ -568,6 +568,50 @@ def test_scan_side_stream_adds_scaled_byte(orc):
                                    atol=1e-6)
 
 
+def np_nibbles(packed, n):
+    """Independent unpacking of a 4-bit side stream: key i is the low nibble
+    of byte i // 2 when i is even, the high nibble when it is odd."""
+    lo = packed & 0x0F
+    hi = packed >> 4
+    return np.stack([lo, hi], -1).reshape(packed.shape[0], -1)[:, :n]
+
+
+def test_scan_meta4_nibble_order_worked_example(orc):
+    # bytes 0x21, 0x03 hold keys 0, 1, 2 = 1, 2, 3: the same scores as the
+    # byte stream [1, 2, 3]
+    keys, q = make_layer(21, n=3)
+    n, hkv, d = keys.shape
+    p = orc.pack(keys)
+    plan = orc.plan(q, p["sigma2"], 40)
+    packed = np.tile(np.array([[0x21, 0x03]], np.uint8), (hkv, 1))
+    bytes_ = np.tile(np.array([[1, 2, 3]], np.uint8), (hkv, 1))
+    a = orc.scan(p["planes"], p["lo"], p["hi"], n, q, plan, packed, 0.75, meta_bits=4)
+    b = orc.scan(p["planes"], p["lo"], p["hi"], n, q, plan, bytes_, 0.75)
+    np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("n", [100, 101, 2049])
+def test_scan_meta4_adds_scaled_nibble(orc, n):
+    keys, q = make_layer(22, n=n)
+    n, hkv, d = keys.shape
+    p = orc.pack(keys)
+    plan = orc.plan_fixed(q, 16)
+    packed = np.random.default_rng(3).integers(0, 256, (hkv, (n + 1) // 2)).astype(np.uint8)
+    vals = np_nibbles(packed, n)
+    s0 = orc.scan(p["planes"], p["lo"], p["hi"], n, q, plan)
+    s1 = orc.scan(p["planes"], p["lo"], p["hi"], n, q, plan, packed, 0.25, meta_bits=4)
+    G = q.shape[0] // hkv
+    for h in range(q.shape[0]):
+        np.testing.assert_allclose(s1[h], s0[h] + 0.25 * vals[h // G], rtol=1e-6, atol=1e-6)
+    # the nibbles as a byte stream give the same scores bit for bit
+    s8 = orc.scan(p["planes"], p["lo"], p["hi"], n, q, plan, vals.astype(np.uint8), 0.25)
+    np.testing.assert_array_equal(s1, s8)
+    pick = np.array([0, 1, n - 2, n - 1, n // 2])
+    part = orc.scan_at(p["planes"], p["lo"], p["hi"], n, q, plan, pick, packed, 0.25,
+                       meta_bits=4)
+    np.testing.assert_array_equal(part, s1[:, pick])
+
+
 def test_read_prefixes_are_shifted_codes(orc):
     keys, q = make_layer(8, n=90)
     n, hkv, d = keys.shape
