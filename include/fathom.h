@@ -317,6 +317,29 @@ int32_t fathom_scan_topk_batched(const fathom_session *sessions,
                                  int32_t hq, int32_t group, int32_t k, void *ws,
                                  int64_t ws_bytes, void *stream);
 
+/* ---- the 68-bit fixed-width baseline --------------------------------------
+ * Explainer, key-experiments section (关键实验与数据): Fathom is compared with
+ * the fixed r = 16 scan at 68 bits per key, and with fixed 136-bit scans at
+ * r = 32.  Both are 4.25 r bits: 4 bits of each of r channels plus r/4 bits
+ * of per-key metadata (a reading; the pages do not lay the metadata out).
+ * The 136-bit form's 8-bit stream is fathom_scan's `meta`; these calls carry
+ * the r = 16 form's 4-bit stream:
+ *   meta4  device or pinned-host uint8[hkv][ceil(n/2)], two keys per byte:
+ *          key i of kv head g is the low nibble of meta4[g][i/2] when i is
+ *          even, the high nibble when i is odd; it adds meta_scale * value.
+ * Otherwise as fathom_scan and fathom_scan_topk (typically with a plan from
+ * fathom_plan_fixed with r = 16).  meta4 may be NULL only when n == 0.     */
+int32_t fathom_scan_meta4(const uint32_t *planes, const float *lo, const float *hi,
+                          int64_t n, int32_t hkv, int32_t d, const float *q,
+                          const uint8_t *plan, int32_t hq, const uint8_t *meta4,
+                          float meta_scale, float *logits, int64_t ld_logits,
+                          void *stream);
+int32_t fathom_scan_topk_meta4(const uint32_t *planes, const float *lo, const float *hi,
+                               int64_t n, int32_t hkv, int32_t d, const float *q,
+                               const uint8_t *plan, int32_t hq, const uint8_t *meta4,
+                               float meta_scale, int32_t group, int32_t k, int32_t *idx,
+                               float *vals, void *ws, int64_t ws_bytes, void *stream);
+
 /* ---- append (decode-time growth) -------------------------------------------
  * Deployment warnings, item 3: the planes are the stored 4-bit K itself, so
  * nothing else is rebuilt when K changes; a decode step adds its new keys to

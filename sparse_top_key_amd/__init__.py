@@ -86,6 +86,9 @@ def lib():
             "fathom_scan_topk": (I32, [P, P, P, I64, I32, I32, P, P, I32, P, F, I32, I32, P, P,
                                        P, I64, P]),
             "fathom_scan_topk_batched": (I32, [P, I32, I32, I32, I32, I32, I32, P, I64, P]),
+            "fathom_scan_meta4": (I32, [P, P, P, I64, I32, I32, P, P, I32, P, F, P, I64, P]),
+            "fathom_scan_topk_meta4": (I32, [P, P, P, I64, I32, I32, P, P, I32, P, F, I32, I32,
+                                             P, P, P, I64, P]),
             "fathom_range_blocks": (I64, [I64]),
             "fathom_pack_blocked_workspace_bytes": (I64, [I64, I32, I32]),
             "fathom_pack_blocked": (I32, [P, I32, I64, I32, I32, I64, I64, P, P, P, I64, P, P,
@@ -277,13 +280,22 @@ def _has_capacity(planes: torch.Tensor, n: int) -> bool:
 
 def scan(planes: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor, n: int,
          q: torch.Tensor, plan_: torch.Tensor, meta: Optional[torch.Tensor] = None,
-         meta_scale: float = 0.0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """-> logits [hq][n] fp32.  planes may live in pinned host memory."""
+         meta_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+         meta_bits: int = 8) -> torch.Tensor:
+    """-> logits [hq][n] fp32.  planes may live in pinned host memory.  meta:
+    uint8 [hkv][n] (meta_bits 8) or packed nibbles [hkv][ceil(n/2)] (4)."""
     _require_gpu(planes, lo, q, plan_)
     hkv, d = lo.shape
     hq = q.shape[0]
     if out is None:
         out = torch.empty((hq, max(n, 1)), dtype=torch.float32, device=q.device)
+    if meta_bits == 4:
+        if _has_capacity(planes, n):
+            raise FathomError("scan: the 4-bit side stream takes compact planes")
+        _check(lib().fathom_scan_meta4(_p(planes), _p(lo), _p(hi), n, hkv, d, _p(q), _p(plan_),
+                                       hq, _p(meta), meta_scale, _p(out), out.stride(0),
+                                       _stream(q.device)), "fathom_scan_meta4")
+        return out[:, :n]
     if _has_capacity(planes, n):
         scan_batched([Session(planes, lo, hi, n, q, plan_, logits=out, meta=meta,
                               meta_scale=meta_scale)])
@@ -373,7 +385,7 @@ def scan_topk_workspace_bytes(ns: Sequence[int], hkv: int, hq: int, group: int, 
 def scan_topk(planes: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor, n: int,
               q: torch.Tensor, plan_: torch.Tensor, k: int, group: int = 1,
               meta: Optional[torch.Tensor] = None, meta_scale: float = 0.0,
-              ws: Optional[torch.Tensor] = None, idx=None, vals=None):
+              ws: Optional[torch.Tensor] = None, idx=None, vals=None, meta_bits: int = 8):
     """Scan + top-k in one call -> (idx int32 [hq/group][k], vals fp32 [hq/group][k]),
     the result of scan() followed by topk()."""
     _require_gpu(planes, lo, q, plan_)
@@ -388,6 +400,14 @@ def scan_topk(planes: torch.Tensor, lo: torch.Tensor, hi: torch.Tensor, n: int,
     if ws is None:
         ws = torch.empty(max(scan_topk_workspace_bytes([n], hkv, hq, group, k), 1),
                          dtype=torch.uint8, device=dev)
+    if meta_bits == 4:
+        if _has_capacity(planes, n):
+            raise FathomError("scan_topk: the 4-bit side stream takes compact planes")
+        _check(lib().fathom_scan_topk_meta4(_p(planes), _p(lo), _p(hi), n, hkv, d, _p(q),
+                                            _p(plan_), hq, _p(meta), meta_scale, group, k,
+                                            _p(idx), _p(vals), _p(ws), ws.numel(),
+                                            _stream(dev)), "fathom_scan_topk_meta4")
+        return idx, vals
     if _has_capacity(planes, n):
         scan_topk_batched([Session(planes, lo, hi, n, q, plan_, idx=idx, vals=vals, meta=meta,
                                    meta_scale=meta_scale)], k, group, ws)

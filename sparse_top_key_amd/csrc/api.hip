@@ -398,6 +398,31 @@ int32_t fathom_scan(const uint32_t *planes, const float *lo, const float *hi, in
   return launch_scan(&ss, 1, hkv, hq, as_stream(stream));
 }
 
+int32_t fathom_scan_meta4(const uint32_t *planes, const float *lo, const float *hi, int64_t n,
+                          int32_t hkv, int32_t d, const float *q, const uint8_t *plan,
+                          int32_t hq, const uint8_t *meta4, float meta_scale, float *logits,
+                          int64_t ld_logits, void *stream) {
+  REQUIRE(meta4 || n == 0, FATHOM_ERR_INVALID_ARG, "fathom_scan_meta4: null side stream");
+  if (int32_t rc = check_heads(hq, hkv)) return rc;
+  if (int32_t rc = check_d(d)) return rc;
+  fathom_session s{};
+  s.planes = planes;
+  s.lo = lo;
+  s.hi = hi;
+  s.n = n;
+  s.q = q;
+  s.plan = plan;
+  s.meta = meta4;
+  s.meta_scale = meta_scale;
+  s.logits = logits;
+  s.ld_logits = ld_logits;
+  if (int32_t rc = check_scan_session(s, hq, "fathom_scan_meta4")) return rc;
+  if (n == 0) return FATHOM_OK;
+  ScanSession ss = to_scan(s);
+  ss.meta_bits = 4;
+  return launch_scan(&ss, 1, hkv, hq, as_stream(stream));
+}
+
 int32_t fathom_scan_blocked(const uint32_t *planes, const float *lo, const float *hi,
                             int64_t range_stride, int64_t n, int32_t hkv, int32_t d,
                             const float *q, const uint8_t *plan, int32_t hq,
@@ -540,7 +565,7 @@ static int32_t check_scan_topk_session(const fathom_session &s, const char *who)
 static int32_t scan_topk_common(const fathom_session *sessions, int32_t n_sessions,
                                 int32_t hkv, int32_t d, int32_t hq, int32_t group, int32_t k,
                                 void *ws, int64_t ws_bytes, void *stream, const char *who,
-                                int64_t rs = 0) {
+                                int64_t rs = 0, int32_t meta_bits = 8) {
   if (int32_t rc = check_heads(hq, hkv)) return rc;
   if (int32_t rc = check_d(d)) return rc;
   if (int32_t rc = check_topk_common(hq, group, k, who)) return rc;
@@ -560,6 +585,7 @@ static int32_t scan_topk_common(const fathom_session *sessions, int32_t n_sessio
     ss[i].seg_cnt = nullptr;
     ss[i].redo = nullptr;
     ss[i].rs = rs;
+    ss[i].meta_bits = meta_bits;
     idx[i] = sessions[i].idx;
     vals[i] = sessions[i].vals;
     ns[i] = sessions[i].n;
@@ -589,6 +615,27 @@ int32_t fathom_scan_topk(const uint32_t *planes, const float *lo, const float *h
   s.vals = vals;
   return scan_topk_common(&s, 1, hkv, d, hq, group, k, ws, ws_bytes, stream,
                           "fathom_scan_topk");
+}
+
+int32_t fathom_scan_topk_meta4(const uint32_t *planes, const float *lo, const float *hi,
+                               int64_t n, int32_t hkv, int32_t d, const float *q,
+                               const uint8_t *plan, int32_t hq, const uint8_t *meta4,
+                               float meta_scale, int32_t group, int32_t k, int32_t *idx,
+                               float *vals, void *ws, int64_t ws_bytes, void *stream) {
+  REQUIRE(meta4 || n == 0, FATHOM_ERR_INVALID_ARG, "fathom_scan_topk_meta4: null side stream");
+  fathom_session s{};
+  s.planes = planes;
+  s.lo = lo;
+  s.hi = hi;
+  s.n = n;
+  s.q = q;
+  s.plan = plan;
+  s.meta = meta4;
+  s.meta_scale = meta_scale;
+  s.idx = idx;
+  s.vals = vals;
+  return scan_topk_common(&s, 1, hkv, d, hq, group, k, ws, ws_bytes, stream,
+                          "fathom_scan_topk_meta4", 0, 4);
 }
 
 int32_t fathom_scan_topk_blocked(const uint32_t *planes, const float *lo, const float *hi,

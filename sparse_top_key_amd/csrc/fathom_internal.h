@@ -121,6 +121,7 @@ struct ScanSession {
   const uint8_t *plan;
   const uint8_t *meta;
   float meta_scale;
+  int32_t meta_bits;      // side stream: 8 (uint8 [hkv][n]), 4 (nibbles [hkv][ceil(n/2)]); 0 = 8
   float *logits;
   int64_t ld;
   // fused scan + top-k (unused by plain scans)

@@ -48,6 +48,7 @@ struct ScanSess {
   const uint32_t *planes;
   const float *lo, *hi, *q;
   const uint8_t *plan, *meta;
+  int32_t meta_bits;       // side stream: 8 (a byte per key) or 4 (two keys per byte)
   float *logits;
   int64_t n, W, ld;
   float meta_scale;
@@ -516,13 +517,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
       }
     }
 
-    // ---- optional 8-bit side stream (fixed-width baseline) ----------------
+    // ---- optional side stream (fixed-width baselines): a byte per key, or
+    // (meta_bits 4) two keys per byte, the even key in the low nibble
     const int64_t key0 = word * 32;
     if (S.meta) {
-      const uint8_t *mp = S.meta + (int64_t)g * n + key0;
+      const bool nib = S.meta_bits == 4;
+      const uint8_t *mp = S.meta + (int64_t)g * (nib ? (n + 1) / 2 : n);
 #pragma unroll
       for (int k = 0; k < KPL; ++k) {
-        const float m = key0 + k < n ? (float)mp[k] : 0.0f;
+        const int64_t i = key0 + k;
+        const uint32_t v = i < n ? (nib ? (mp[i >> 1] >> (4 * (i & 1))) & 15u : mp[i]) : 0u;
+        const float m = (float)v;
 #pragma unroll
         for (int h = 0; h < GH; ++h) acc[h][k] = __fmaf_rn(S.meta_scale, m, acc[h][k]);
       }
@@ -961,7 +966,11 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   const float scale = hh < GH ? s_scale[hh] : 0.0f;
   const uint32_t *gplanes = S.planes + (int64_t)g * kD * kPlanes * W;
   const int64_t ld = S.ld;
-  const uint8_t *meta = META && S.meta ? S.meta + (int64_t)g * n : nullptr;
+  // side stream: a byte per key, or (meta_bits 4) two keys per byte, the
+  // even key in the low nibble
+  const bool meta_nib = META && S.meta_bits == 4;
+  const uint8_t *meta =
+      META && S.meta ? S.meta + (int64_t)g * (meta_nib ? (n + 1) / 2 : n) : nullptr;
   const float meta_scale = S.meta_scale;
   float *out_row = hh < GH ? S.logits + (int64_t)(head_base + hh) * ld : nullptr;
   const bool vec_out = S.vec_out != 0;
@@ -982,8 +991,11 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   // float threshold of this lane's output row (candidate modes)
   const float row_tf = (MODE == kScanCand || MODE == kScanCandGroup) && hh < GH ? s_tf[hh] : 0.0f;
   // side stream: 4 aligned bytes per beta when rows start on 4-byte bounds
-  const bool meta_words =
-      META && meta && ((reinterpret_cast<uintptr_t>(S.meta) & 3) == 0) && (n & 3) == 0;
+  // (4 keys per load: 4 bytes, or 2 bytes of nibbles)
+  const bool meta_words = META && meta &&
+                          ((reinterpret_cast<uintptr_t>(S.meta) & (meta_nib ? 1 : 3)) == 0) &&
+                          (n & 3) == 0;
+  const uint32_t meta_sh = meta_nib ? 4u : 8u, meta_mask = meta_nib ? 15u : 255u;
 
   if (role == 0) {
     // ==== producers.  A task is one slot group of one tile: 32 plane rows
@@ -1136,7 +1148,9 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
 #pragma unroll
         for (int beta = 0; beta < 4; ++beta)
           if (kb0 + 64 * beta + 4 <= n)
-            mw[beta] = *reinterpret_cast<const uint32_t *>(meta + kb0 + 64 * beta);
+            mw[beta] = meta_nib
+                           ? (uint32_t)*reinterpret_cast<const uint16_t *>(meta + (kb0 + 64 * beta) / 2)
+                           : *reinterpret_cast<const uint32_t *>(meta + kb0 + 64 * beta);
       }
       int4 av;
       if constexpr (!BLK) av = *reinterpret_cast<const int4 *>(&s_limbs[p][lane][0]);
@@ -1242,13 +1256,14 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
       if (META && meta_words && hh < GH) {
 #pragma unroll
         for (int q = 0; q < 16; ++q)
-          s[q] = __fmaf_rn(meta_scale, (float)((mw[q >> 2] >> (8 * (q & 3))) & 0xFFu), s[q]);
+          s[q] = __fmaf_rn(meta_scale, (float)((mw[q >> 2] >> (meta_sh * (q & 3))) & meta_mask),
+                           s[q]);
       } else if (META && meta && hh < GH) {
         uint32_t mb[16];
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int64_t key = kb + 64 * (q >> 2) + (q & 3);
-          mb[q] = key < n ? meta[key] : 0u;
+          mb[q] = key < n ? (meta_nib ? (meta[key >> 1] >> (4 * (key & 1))) & 15u : meta[key]) : 0u;
         }
 #pragma unroll
         for (int q = 0; q < 16; ++q) s[q] = __fmaf_rn(meta_scale, (float)mb[q], s[q]);
@@ -1609,6 +1624,7 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_
         o.W = sess_words(in);
         o.ld = in.ld;
         o.meta_scale = in.meta_scale;
+        o.meta_bits = in.meta_bits == 4 ? 4 : 8;
         o.vec_out = ((reinterpret_cast<uintptr_t>(in.logits) & 15) == 0) && (in.ld % 4 == 0);
         o.sample = in.sample;
         o.thr = in.thr;

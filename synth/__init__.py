@@ -128,6 +128,15 @@ def side_stream(seed: int, layer: int, hkv: int, n: int, device="cpu",
                          dtype=torch.int32).to(torch.uint8)
 
 
+def side_stream4(seed: int, layer: int, hkv: int, n: int, device="cpu",
+                 session: int = 0) -> torch.Tensor:
+    """The r = 16 baseline's 4-bit per-key metadata, packed two keys per byte
+    (even key in the low nibble): uint8 [hkv][ceil(n/2)], uniform bytes."""
+    g = _dev_gen(device, seed, layer, session, 9)
+    return torch.randint(0, 256, (hkv, (n + 1) // 2), generator=g, device=device,
+                         dtype=torch.int32).to(torch.uint8)
+
+
 def session_lengths(w: Workload):
     g = _cpu_gen(w.seed, 5)
     lo, hi = w.n_range

@@ -428,3 +428,27 @@ def test_scan_topk_blocked_validation(L):
     assert call(11, 3) == 1                      # group does not divide hq
     assert call(16, ws - 1) == 4                 # workspace
     assert call(13, None) == 1                   # idx
+
+
+def test_meta4_validation(L):
+    A = ctypes.c_void_p(0x10000)
+    base = [A, A, A, 5000, 8, 128, A, A, 32, A, 0.5, A, 5000, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return L.fathom_scan_meta4(*a)
+    assert call(9, None) == 1 and "side stream" in err(L)   # meta4 required
+    assert call(8, 30) == 1                      # hq not a multiple of hkv
+    assert call(5, 64) == 2                      # d
+    assert call(12, 4999) == 1                   # ld < n
+    ws = L.fathom_scan_topk_workspace_bytes((ctypes.c_int64 * 1)(5000), 1, 8, 32, 1, 64)
+    tbase = [A, A, A, 5000, 8, 128, A, A, 32, A, 0.5, 1, 64, A, A, A, ws, None]
+
+    def tcall(i, v):
+        a = list(tbase)
+        a[i] = v
+        return L.fathom_scan_topk_meta4(*a)
+    assert tcall(9, None) == 1
+    assert tcall(12, 0) == 1                     # k
+    assert tcall(16, ws - 1) == 4                # workspace
