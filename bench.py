@@ -61,6 +61,12 @@ class Layer:
         if host:
             self.meta_host = torch.empty(self.meta.shape, dtype=torch.uint8, pin_memory=True)
             self.meta_host.copy_(self.meta)
+        # the r = 16 baseline's 4-bit stream (two keys per byte)
+        self.meta4 = synth.side_stream4(w.seed, layer, w.hkv, w.n, device=dev)
+        self.meta4_host = None
+        if host:
+            self.meta4_host = torch.empty(self.meta4.shape, dtype=torch.uint8, pin_memory=True)
+            self.meta4_host.copy_(self.meta4)
         self.budget = [w.budget] * w.hq
         self.group_budget = [w.budget] * w.hkv
         self.group_budget176 = [176] * w.hkv     # about the per-head plans' union bits
@@ -82,13 +88,15 @@ def union_plane_bytes(plan, hkv, n):
 
 
 def run_steps(layers, w, ws, steps, mode, fixed=False, fused=False, per_call=True,
-              variant=None, with_meta=True):
+              variant=None, with_meta=True, meta_bits=8):
     """mode: 'host' or 'hbm'.  fused: fathom_scan_topk in place of fathom_scan
     then fathom_topk (ws must then be its workspace).  fixed: True (r = 32,
     the 136-bit baseline) or the baseline's channel count r.  variant: None (the
     fill-to-cap walk), 'rd' (rate-distortion plan) or 'group' (one plan per
     GQA group, budget B per kv head).  with_meta: the fixed baselines read
-    their 8-bit side stream (fixed-136); without it, r = 32 is fixed-128.  per_call: events around
+    their side stream (8-bit: fixed-136, or the r = 16 form at 72 bits; 4-bit,
+    meta_bits 4: the r = 16 form at 68 bits); without it, r = 32 is
+    fixed-128.  per_call: events around
     every call (for the per-call times); otherwise none, since an event
     recorded between two calls stalls the stream for a few microseconds.
     Returns the per-step event lists (empty lists when per_call is off)."""
@@ -98,7 +106,9 @@ def run_steps(layers, w, ws, steps, mode, fixed=False, fused=False, per_call=Tru
         L = layers[s % len(layers)]
         planes = L.host if mode == "host" else L.planes
         meta = None
-        if fixed and with_meta:
+        if fixed and with_meta and meta_bits == 4:
+            meta = L.meta4_host if mode == "host" else L.meta4
+        elif fixed and with_meta:
             meta = L.meta_host if mode == "host" else L.meta
         e = ev[s]
         if per_call:
@@ -120,11 +130,12 @@ def run_steps(layers, w, ws, steps, mode, fixed=False, fused=False, per_call=Tru
             e[1].record()
         if fused:
             fathom.scan_topk(planes, L.lo, L.hi, L.n, L.q, plan, w.k, 1, meta, 0.0, ws=ws,
-                             idx=L.idx, vals=L.vals)
+                             idx=L.idx, vals=L.vals, meta_bits=meta_bits)
             if per_call:
                 e[2].record()
         else:
-            fathom.scan(planes, L.lo, L.hi, L.n, L.q, plan, meta, 0.0, out=L.logits)
+            fathom.scan(planes, L.lo, L.hi, L.n, L.q, plan, meta, 0.0, out=L.logits,
+                        meta_bits=meta_bits)
             if per_call:
                 e[2].record()
             fathom.topk(L.logits, w.k, ws=ws, idx=L.idx, vals=L.vals)
@@ -145,11 +156,11 @@ def summarize(ev):
 
 
 def timed(layers, w, ws, steps, warmup, mode, fixed=False, fused=False, variant=None,
-          with_meta=True):
+          with_meta=True, meta_bits=8):
     """Throughput: K steps between one pair of events (and synchronisations);
     then the same K steps again with events around every call, for the
     per-call times (the scan's is the one the rooflines use)."""
-    kw = dict(variant=variant, with_meta=with_meta)
+    kw = dict(variant=variant, with_meta=with_meta, meta_bits=meta_bits)
     run_steps(layers, w, ws, warmup, mode, fixed, fused, per_call=False, **kw)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -988,17 +999,21 @@ def main():
                                       **{k: round(x, 4) for k, x in t.items()}}
                 log(f"{var} {mode}_fused: {t}")
             variants[var] = v
-        # the r = 16 analogue of the baseline (64 plane bits + the 8-bit side
-        # stream per query head): the pages compare Fathom with it at equal time
+        # the r = 16 analogue of the baseline: 64 plane bits per query head and
+        # a side stream of r/4 = 4 bits per key (68 bits, the pages' figure)
+        # or of 8 bits (72 bits); the pages compare Fathom with it
         fper16 = [union_plane_bytes(fathom.plan_fixed(L.q, 16), w.hkv, w.n) for L in layers]
-        v = {"union_plane_bytes": int(np.mean([x[0] for x in fper16])),
-             "meta_bytes": w.hkv * w.n, "union_bits_per_kv_head": fper16[0][1]}
-        for mode in res_modes(args):
-            t = timed(layers, w, fws, args.steps, args.warmup, mode, fixed=16, fused=True)
-            v[mode + "_fused"] = {"keys_per_s": round(w.n * w.hkv / (t["step_ms"] * 1e-3), 1),
-                                  **{k: round(x, 4) for k, x in t.items()}}
-            log(f"fixed r=16 {mode}_fused: {t}")
-        variants["fixed_r16"] = v
+        for name, mbits in (("fixed_r16", 8), ("fixed_r16_68bit", 4)):
+            v = {"union_plane_bytes": int(np.mean([x[0] for x in fper16])),
+                 "meta_bytes": w.hkv * w.n * mbits // 8, "meta_bits_per_key": mbits,
+                 "bits_per_key": 64 + mbits, "union_bits_per_kv_head": fper16[0][1]}
+            for mode in res_modes(args):
+                t = timed(layers, w, fws, args.steps, args.warmup, mode, fixed=16, fused=True,
+                          meta_bits=mbits)
+                v[mode + "_fused"] = {"keys_per_s": round(w.n * w.hkv / (t["step_ms"] * 1e-3), 1),
+                                      **{k: round(x, 4) for k, x in t.items()}}
+                log(f"{name} {mode}_fused: {t}")
+            variants[name] = v
         # fixed-128: the r = 32 plan without the side stream
         v = {"union_plane_bytes": fixed_plan_b}
         for mode in res_modes(args):
@@ -1122,13 +1137,16 @@ def main():
                             "whole GQA group reads 92 plane bits per key; group_calibrated: 176, "
                             "about the per-head plans' union); fixed_r16: top-16 |q| channels x 4 "
                             "bits + the 8-bit side stream; fused scan + top-k steps")
-        f16 = variants["fixed_r16"]
         fb = plane_b
-        variants["fathom_vs_fixed_r16"] = {
-            "byte_ratio": round(fb / (f16["union_plane_bytes"] + f16["meta_bytes"]), 4),
-            **{m + "_time_ratio": round(res[m + "_fused"]["step_ms"] /
-                                        f16[m + "_fused"]["step_ms"], 4)
-               for m in res_modes(args)}}
+        for name, key in (("fathom_vs_fixed_r16", "fixed_r16"),
+                          ("fathom_vs_fixed_r16_68bit", "fixed_r16_68bit")):
+            f16 = variants[key]
+            variants[name] = {
+                "baseline_bits_per_key": f16["bits_per_key"],
+                "byte_ratio": round(fb / (f16["union_plane_bytes"] + f16["meta_bytes"]), 4),
+                **{m + "_time_ratio": round(res[m + "_fused"]["step_ms"] /
+                                            f16[m + "_fused"]["step_ms"], 4)
+                   for m in res_modes(args)}}
         out["plan_variants"] = variants
     out["probe"] = probe
     if not args.no_cpu:

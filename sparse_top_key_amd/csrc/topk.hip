@@ -282,6 +282,8 @@ __global__ __launch_bounds__(kBig) void topk_sample_kernel(TopkArgs a) {
   __shared__ int wave_tot[16];
   __shared__ int s_res[2];
   __shared__ uint32_t red[48];
+  __shared__ int tile_cnt[kSampleTiles];   // fused threshold: per sampled tile
+  __shared__ bool tile_out[kSampleTiles];
   const int o = blockIdx.x;
   const RowRef R = row_ref(a, o);
   const int64_t n = R.s->n, ld = R.s->ld, n_full = R.s->n_full;
@@ -348,47 +350,89 @@ __global__ __launch_bounds__(kBig) void topk_sample_kernel(TopkArgs a) {
         if (j0 + u < kPer) v[j0 + u] = ((okm >> (j0 + u)) & 1) ? to_key((float)acc[u]) : 0u;
     }
   }
-  uint32_t mx = 0, mn = 0xFFFFFFFFu;
-  int cnt = __popc(okm);
+  // Fused threshold stage: the sample row holds whole 2048-key tiles, the
+  // middle tiles of equal stretches of the row.  A tile whose count of
+  // sampled keys at or above T exceeds 4x its larger neighbour's (+8) holds a
+  // local cluster of top keys (one stretch of the row, not a drift, which
+  // changes smoothly from tile to tile): the sample then overstates the
+  // cluster by the sampling ratio and T lands above almost all other keys.
+  // Such tiles are left out and T is taken again from the others (the
+  // cluster's own keys are still candidates: they lie above it).
+  const bool tiled = a.stage == kTopkThreshold;
+  const int ntl = tiled ? (int)((n + kBlockKeys - 1) / kBlockKeys) : 0;
+  uint32_t prefix = 0;
+  for (int round = 0; round < 2; ++round) {
+    uint32_t mx = 0, mn = 0xFFFFFFFFu;
+    int cnt = __popc(okm);
 #pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    if ((okm >> j) & 1) {
-      mx = max(mx, v[j]);
-      mn = min(mn, v[j]);
+    for (int j = 0; j < kPer; ++j)
+      if ((okm >> j) & 1) {
+        mx = max(mx, v[j]);
+        mn = min(mn, v[j]);
+      }
+    block_minmax_count(mx, mn, cnt, red);
+    if (cnt == 0) {
+      if (threadIdx.x == 0) a.thr[o] = 0;
+      return;
     }
-  block_minmax_count(mx, mn, cnt, red);
-  if (cnt == 0) {
-    if (threadIdx.x == 0) a.thr[o] = 0;
-    return;
-  }
-  // rank of the threshold inside the sample: ~2.5k of n_full at or above T
-  int64_t rs = ((int64_t)5 * a.k * cnt + 2 * n_full - 1) / (2 * n_full);
-  rs = rs < 1 ? 1 : (rs > cnt ? cnt : rs);
-  // Two 11-bit digits below the bits all sampled keys share: T = the rs-th
-  // largest key with its bits below the second digit cleared.
-  const uint32_t diff = mx ^ mn;
-  const int hb = diff ? 31 - __clz(diff) : 0;  // highest bit in which keys differ
-  int sh = hb > 10 ? hb - 10 : 0;
-  uint32_t prefix = sh + 11 >= 32 ? 0u : (mx >> (sh + 11)) << (sh + 11);
-  uint32_t pmask = sh + 11 >= 32 ? 0u : ~((1u << (sh + 11)) - 1u);
-  int rem = (int)rs;
-  for (int pass = 0; pass < 2; ++pass) {
-    for (int b = threadIdx.x; b < kHistBins; b += kBig) hist[b] = 0;
+    // rank of the threshold inside the sample: ~2.5k of n_full at or above T
+    int64_t rs = ((int64_t)5 * a.k * cnt + 2 * n_full - 1) / (2 * n_full);
+    rs = rs < 1 ? 1 : (rs > cnt ? cnt : rs);
+    // Two 11-bit digits below the bits all sampled keys share: T = the rs-th
+    // largest key with its bits below the second digit cleared.
+    const uint32_t diff = mx ^ mn;
+    const int hb = diff ? 31 - __clz(diff) : 0;  // highest bit in which keys differ
+    int sh = hb > 10 ? hb - 10 : 0;
+    prefix = sh + 11 >= 32 ? 0u : (mx >> (sh + 11)) << (sh + 11);
+    uint32_t pmask = sh + 11 >= 32 ? 0u : ~((1u << (sh + 11)) - 1u);
+    int rem = (int)rs;
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int b = threadIdx.x; b < kHistBins; b += kBig) hist[b] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (((okm >> j) & 1) && (v[j] & pmask) == prefix)
+          atomicAdd(&hist[(v[j] >> sh) & (kHistBins - 1)], 1);
+      __syncthreads();
+      int above = 0;
+      const int d = find_digit(hist, kHistBins, rem, &above, wave_tot, s_res);
+      rem -= above;
+      prefix |= (uint32_t)d << sh;
+      pmask |= (uint32_t)(kHistBins - 1) << sh;
+      if (sh == 0) break;
+      // next digit: the 11 bits below (when fewer remain, it also spans bits
+      // the matching keys share, which keeps its order)
+      sh = sh > 11 ? sh - 11 : 0;
+    }
+    if (round == 1 || ntl < 3) break;
+    // per-tile counts of sampled keys at or above T, then the outliers
+    for (int t = threadIdx.x; t < ntl; t += kBig) tile_cnt[t] = 0;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
-      if (((okm >> j) & 1) && (v[j] & pmask) == prefix)
-        atomicAdd(&hist[(v[j] >> sh) & (kHistBins - 1)], 1);
+      if (((okm >> j) & 1) && v[j] >= prefix) {
+        const int e = threadIdx.x + j * kBig;
+        const int64_t pos = (int64_t)(e / kRun) * stride + (e % kRun);
+        atomicAdd(&tile_cnt[pos / kBlockKeys], 1);
+      }
     __syncthreads();
-    int above = 0;
-    const int d = find_digit(hist, kHistBins, rem, &above, wave_tot, s_res);
-    rem -= above;
-    prefix |= (uint32_t)d << sh;
-    pmask |= (uint32_t)(kHistBins - 1) << sh;
-    if (sh == 0) break;
-    // next digit: the 11 bits below (when fewer remain, it also spans bits
-    // the matching keys share, which keeps its order)
-    sh = sh > 11 ? sh - 11 : 0;
+    if (threadIdx.x == 0) s_res[0] = 0;
+    __syncthreads();
+    for (int t = threadIdx.x; t < ntl; t += kBig) {
+      const int nb = max(t > 0 ? tile_cnt[t - 1] : 0, t + 1 < ntl ? tile_cnt[t + 1] : 0);
+      const bool outlier = tile_cnt[t] > 4 * nb + 8;
+      tile_out[t] = outlier;
+      if (outlier) s_res[0] = 1;
+    }
+    __syncthreads();
+    if (!s_res[0]) break;  // block-uniform
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = threadIdx.x + j * kBig;
+      const int64_t pos = (int64_t)(e / kRun) * stride + (e % kRun);
+      if (((okm >> j) & 1) && tile_out[pos / kBlockKeys]) okm &= ~(1u << j);
+    }
+    __syncthreads();
   }
   if (threadIdx.x == 0) a.thr[o] = prefix;
 }

@@ -264,15 +264,19 @@ def _planted_layer(F, w, keys, q, group, tile, m, head):
 
 
 @pytest.mark.parametrize("group", [1, 4])
-def test_layer_1m_clustered_top_keys(F, orc, layer_1m, group):
+@pytest.mark.parametrize("tile", [301, 392])
+def test_layer_1m_clustered_top_keys(F, orc, layer_1m, group, tile):
     """1,500 top-scoring keys inside one 2048-key tile of the 1M-key layer:
     one scan block finds more candidates than its even share of the row's
-    candidate store.  The fused call still equals scan then top-k, and its
-    rows hold the planted keys."""
+    candidate store.  Tile 392 is one the fused threshold samples (the middle
+    tiles of 32 equal stretches of 512 tiles are 8 (2j + 1)): the threshold
+    stage must leave its cluster out of the estimate; tile 301 is not
+    sampled.  The fused call still equals scan then top-k, no
+    row is recomputed, and its rows hold the planted keys."""
     w, keys, _, q = layer_1m
     n, G = w.n, w.hq // w.hkv
-    head, tile, m = 9, 301, 1500
-    print(f"1M clustered, group {group}", flush=True)
+    head, m = 9, 1500
+    print(f"1M clustered, group {group}, tile {tile}", flush=True)
     p = _planted_layer(F, w, keys, q, group, tile, m, head)
     plan = F.plan(q, p.sigma2, w.budget)
     logits = F.scan(p.planes, p.lo, p.hi, n, q, plan)
