@@ -1036,7 +1036,7 @@ def main():
                     "peak": PCIE_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / PCIE_PEAK_GBPS, 4),
                     "traffic": (traffic or {}).get("host_scan_fetch_bytes"),
-                    "kernel": "scan_kernel<4, 2> (planes in pinned host memory, fp32 FMA form)",
+                    "kernel": "scan_kernel<4, 2, false> (planes in pinned host memory, fp32 FMA form)",
                     "algorithmic_bytes": plane_b,
                     "frac_of_measured_link_peak": (round(achieved / probe["host_read_zero_copy_GBps"], 4)
                                                    if probe else None),
@@ -1072,7 +1072,7 @@ def main():
             "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBPS, 4),
             "traffic": (traffic or {}).get("hbm_scan_bytes"),
-            "kernel": "scan_mfma_kernel<4, 0, false> (planes in HBM, all logits written)",
+            "kernel": "scan_mfma_kernel<4, 0, false, false> (planes in HBM, all logits written)",
             "algorithmic_bytes": plane_b,
             "non_algorithmic_bytes": logits_b,
             "achieved_with_logits_GBps": round((plane_b + logits_b) / (h["scan_ms"] * 1e-3) / 1e9, 1),
