@@ -185,7 +185,7 @@ __device__ __forceinline__ void wave_sort128_desc(uint64_t (&v)[2]) {
 // length: thread t finds by binary search how many of the first 2t outputs
 // of its pair of runs come from the first run, and writes outputs 2t, 2t+1.
 // Returns the buffer holding the result.
-__device__ uint64_t *sort_winners_desc(uint64_t *w, uint64_t *tmp, int m) {
+__device__ __forceinline__ uint64_t *sort_winners_desc(uint64_t *w, uint64_t *tmp, int m) {
   int P = 128;
   while (P < m) P <<= 1;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
@@ -361,6 +361,10 @@ __global__ __launch_bounds__(kBig) void topk_sample_kernel(TopkArgs a) {
   const bool tiled = a.stage == kTopkThreshold;
   const int ntl = tiled ? (int)((n + kBlockKeys - 1) / kBlockKeys) : 0;
   uint32_t prefix = 0;
+  // (sample rows of the threshold stage hold at most kSampleKeys keys, so
+  // positions fit 32 bits)
+  const int stride32 = (int)stride;
+#pragma unroll 1
   for (int round = 0; round < 2; ++round) {
     uint32_t mx = 0, mn = 0xFFFFFFFFu;
     int cnt = __popc(okm);
@@ -412,8 +416,7 @@ __global__ __launch_bounds__(kBig) void topk_sample_kernel(TopkArgs a) {
     for (int j = 0; j < kPer; ++j)
       if (((okm >> j) & 1) && v[j] >= prefix) {
         const int e = threadIdx.x + j * kBig;
-        const int64_t pos = (int64_t)(e / kRun) * stride + (e % kRun);
-        atomicAdd(&tile_cnt[pos / kBlockKeys], 1);
+        atomicAdd(&tile_cnt[((e / kRun) * stride32 + (e % kRun)) / kBlockKeys], 1);
       }
     __syncthreads();
     if (threadIdx.x == 0) s_res[0] = 0;
@@ -429,8 +432,8 @@ __global__ __launch_bounds__(kBig) void topk_sample_kernel(TopkArgs a) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int e = threadIdx.x + j * kBig;
-      const int64_t pos = (int64_t)(e / kRun) * stride + (e % kRun);
-      if (((okm >> j) & 1) && tile_out[pos / kBlockKeys]) okm &= ~(1u << j);
+      if (((okm >> j) & 1) && tile_out[((e / kRun) * stride32 + (e % kRun)) / kBlockKeys])
+        okm &= ~(1u << j);
     }
     __syncthreads();
   }
@@ -581,16 +584,21 @@ __device__ uint64_t block_or64(uint64_t v, uint64_t *red) {
 // the 11 bits below their common prefix, the buckets at or above the one
 // holding the kk-th word are laid out in descending bucket order, and each
 // word's rank is its bucket's offset plus the number of larger words in its
-// bucket.  Returns false, having written nothing, when one of those buckets
-// holds more than kMaxBucket words (the caller then sorts).  Buckets grow
-// when the candidates span two binades, so that the binning window starts in
-// the exponent bits; a word's rank is a loop over its bucket, and even at 512
-// words that costs far less than the sort it avoids.
+// bucket.  Buckets grow when the candidates span two binades, so that the
+// binning window starts in the exponent bits; a word's rank is a loop over
+// its bucket, and even at 512 words that costs far less than a sort.  One
+// larger bucket strictly above the kk-th word's (top keys clustered in a
+// narrow score range: all of its words are winners, at most kk of them) is
+// sorted on its own in `sort_buf` (2 * FATHOM_MAX_K words), its words ranked
+// by position.  Returns false, having written nothing, for anything else
+// (the caller then selects and sorts).  buck holds kBuckCap words, above
+// kHistBins + 1 ints.
 constexpr int kMaxBucket = 512;
+constexpr int kBuckCap = FATHOM_MAX_K + kMaxBucket;
 
-__device__ bool bucket_rank_out(const uint64_t *src, int m, int kk, uint64_t *buck, int *hist,
+__device__ __forceinline__ bool bucket_rank_out(const uint64_t *src, int m, int kk, uint64_t *buck, int *hist,
                                 int *above, int *wave_tot, int *s_res, uint64_t *red,
-                                const TopkSess &S, int r, int k) {
+                                const TopkSess &S, int r, int k, uint64_t *sort_buf) {
   const int t = threadIdx.x;
   uint64_t diff = 0;
   const uint64_t w0 = src[0];
@@ -614,9 +622,22 @@ __device__ bool bucket_rank_out(const uint64_t *src, int m, int kk, uint64_t *bu
   if (excl + c1 < kk && kk <= incl) s_res[0] = d2;
   __syncthreads();
   const int db = s_res[0];  // digit holding the kk-th word
-  if ((d1 >= db && c1 > kMaxBucket) || (d2 >= db && c2 > kMaxBucket)) s_res[1] = 1;
+  // big buckets at or above db: one strictly above db (all of its words are
+  // winners) is sorted on its own; the kk-th word's bucket must stay small
+  const int big1 = d1 >= db && c1 > kMaxBucket, big2 = d2 >= db && c2 > kMaxBucket;
+  if ((big1 && d1 == db) || (big2 && d2 == db)) atomicAdd(&s_res[1], 2);
+  if (big1) {
+    atomicAdd(&s_res[1], 1);
+    above[kHistBins] = d1;
+  }
+  if (big2) {
+    atomicAdd(&s_res[1], 1);
+    above[kHistBins] = d2;
+  }
   __syncthreads();
-  if (s_res[1]) return false;
+  const int nbig = s_res[1];
+  if (nbig > 1) return false;
+  const int dbig = nbig == 1 ? above[kHistBins] : -1;
   // bucket order; above[d] becomes the end of bucket d
   for (int j = t; j < m; j += kBig) {
     const uint64_t w = src[j];
@@ -630,6 +651,7 @@ __device__ bool bucket_rank_out(const uint64_t *src, int m, int kk, uint64_t *bu
   for (int p = t; p < total; p += kBig) {
     const uint64_t w = buck[p];
     const int d = (int)((w >> sh) & (kHistBins - 1));
+    if (d == dbig) continue;
     const int c = hist[d];
     const int b0 = above[d] - c;
     int rank = b0;
@@ -637,6 +659,17 @@ __device__ bool bucket_rank_out(const uint64_t *src, int m, int kk, uint64_t *bu
     if (rank < kk) {
       idx[rank] = (int32_t)(~(uint32_t)w);
       vals[rank] = from_key((uint32_t)(w >> 32));
+    }
+  }
+  if (dbig >= 0) {
+    // the big bucket: copied out, sorted, written at its offset
+    const int c = hist[dbig], b0 = above[dbig] - c;
+    for (int j = t; j < c; j += kBig) sort_buf[j] = buck[b0 + j];
+    const uint64_t *sorted = sort_winners_desc(sort_buf, sort_buf + FATHOM_MAX_K, c);
+    for (int j = t; j < c; j += kBig) {
+      const uint64_t w = sorted[j];
+      idx[b0 + j] = (int32_t)(~(uint32_t)w);
+      vals[b0 + j] = from_key((uint32_t)(w >> 32));
     }
   }
   for (int j = kk + t; j < k; j += kBig) {
@@ -651,7 +684,7 @@ __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
   __shared__ uint64_t s[kCandCap];
   __shared__ uint64_t win[FATHOM_MAX_K + kMaxBucket];
   __shared__ int hist[kHistBins];
-  __shared__ int above[kHistBins];
+  __shared__ int above[kHistBins + 1];  // [kHistBins]: the big bucket (bucket_rank_out)
   __shared__ uint64_t red[kBig / 64];
   __shared__ int wave_tot[16];
   __shared__ int s_res[2];
@@ -734,7 +767,8 @@ __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
     }
     __syncthreads();
     if (kk > 0 &&
-        bucket_rank_out(s, m, kk, win, hist, above, wave_tot, s_res, red, S, r, k))
+        bucket_rank_out(s, m, kk, win, hist, above, wave_tot, s_res, red, S, r, k,
+                        s + kBuckCap))
       return;
     if (kk > 0) {
       const uint64_t T = m > kk ? select_kth(s, m, kk, hist, wave_tot, s_res) : 0ull;
@@ -794,7 +828,8 @@ __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
   __syncthreads();
   // win[0..kk) holds the winners
   if (!fast && kk > 0 &&
-      bucket_rank_out(win, kk, kk, s, hist, above, wave_tot, s_res, red, S, r, k))
+      bucket_rank_out(win, kk, kk, s, hist, above, wave_tot, s_res, red, S, r, k,
+                      s + kBuckCap))
     return;
   const uint64_t *sorted = sort_winners_desc(win, s, kk);
   write_out(S, r, k, sorted, kk);

@@ -68,6 +68,24 @@ def test_topk_bucket_overflow_sorts(F, orc):
     check(F, orc, S, 700)
 
 
+@pytest.mark.parametrize("n", [7000, 300000])
+def test_topk_cluster_bucket_above_kth(F, orc, n):
+    """1,500 distinct scores in a tiny range far above the rest (top keys
+    clustered in one stretch of the row): among the winners they fill one
+    bucket beyond the exact-ranking cap, strictly above the k-th word's
+    bucket, which is then sorted on its own; with ties inside the cluster,
+    per row and per GQA group."""
+    rng = np.random.default_rng(n)
+    S = rng.standard_normal((4, n)).astype(np.float32)
+    at = rng.integers(0, n - 1500, 4)
+    for r in range(4):
+        S[r, at[r]:at[r] + 1500] = (40.0 + rng.uniform(0, 1e-4, 1500)).astype(np.float32)
+    S[2, at[2] + 50:at[2] + 90] = S[2, at[2] + 7]     # ties inside the cluster
+    check(F, orc, S, 2048)
+    check(F, orc, S, 1800)
+    check(F, orc, S, 2048, group=2)
+
+
 def test_topk_all_equal_takes_lowest_indices(F, orc):
     S = np.full((2, 30000), 1.5, np.float32)            # forces the exact fallback
     check(F, orc, S, 2048)
