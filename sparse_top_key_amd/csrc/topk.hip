@@ -589,8 +589,8 @@ __device__ uint64_t block_or64(uint64_t v, uint64_t *red) {
 // its bucket, and even at 512 words that costs far less than a sort.  One
 // larger bucket strictly above the kk-th word's (top keys clustered in a
 // narrow score range: all of its words are winners, at most kk of them) is
-// sorted on its own in `sort_buf` (2 * FATHOM_MAX_K words), its words ranked
-// by position.  Returns false, having written nothing, for anything else
+// ranked on its own, binned again below its own words' common prefix, in
+// `sort_buf` (2 * FATHOM_MAX_K words; sorted there when that fails).  Returns false, having written nothing, for anything else
 // (the caller then selects and sorts).  buck holds kBuckCap words, above
 // kHistBins + 1 ints.
 constexpr int kMaxBucket = 512;
@@ -662,14 +662,51 @@ __device__ __forceinline__ bool bucket_rank_out(const uint64_t *src, int m, int 
     }
   }
   if (dbig >= 0) {
-    // the big bucket: copied out, sorted, written at its offset
+    // The big bucket (words buck[b0 .. b0+c), ranks b0 ..): binned again on
+    // the 11 bits below its own words' common prefix and ranked within those
+    // bins as above; should a bin still exceed the cap, the bucket is sorted.
     const int c = hist[dbig], b0 = above[dbig] - c;
-    for (int j = t; j < c; j += kBig) sort_buf[j] = buck[b0 + j];
-    const uint64_t *sorted = sort_winners_desc(sort_buf, sort_buf + FATHOM_MAX_K, c);
-    for (int j = t; j < c; j += kBig) {
-      const uint64_t w = sorted[j];
-      idx[b0 + j] = (int32_t)(~(uint32_t)w);
-      vals[b0 + j] = from_key((uint32_t)(w >> 32));
+    const uint64_t *bw = buck + b0;
+    uint64_t dif = 0;
+    for (int j = t; j < c; j += kBig) dif |= bw[j] ^ bw[0];
+    dif = block_or64(dif, red);  // (its barrier also ends the ranking loop above)
+    const int hb2 = dif ? 63 - __clzll(dif) : 0;
+    const int sh2 = hb2 > 10 ? hb2 - 10 : 0;
+    for (int b = t; b < kHistBins; b += kBig) hist[b] = 0;
+    if (t == 0) s_res[1] = 0;
+    __syncthreads();
+    for (int j = t; j < c; j += kBig) atomicAdd(&hist[(int)((bw[j] >> sh2) & (kHistBins - 1))], 1);
+    __syncthreads();
+    const int h1 = hist[d1], h2 = hist[d2];
+    const int inc2 = block_inclusive_scan(h1 + h2, wave_tot);
+    above[d1] = inc2 - h1 - h2;
+    above[d2] = inc2 - h2;
+    if (h1 > kMaxBucket || h2 > kMaxBucket) s_res[1] = 1;
+    __syncthreads();
+    if (!s_res[1]) {
+      for (int j = t; j < c; j += kBig) {
+        const uint64_t w = bw[j];
+        sort_buf[atomicAdd(&above[(int)((w >> sh2) & (kHistBins - 1))], 1)] = w;
+      }
+      __syncthreads();
+      for (int p = t; p < c; p += kBig) {
+        const uint64_t w = sort_buf[p];
+        const int d = (int)((w >> sh2) & (kHistBins - 1));
+        const int cnt = hist[d];
+        const int s0 = above[d] - cnt;
+        int rank = b0 + s0;
+        for (int q = s0; q < s0 + cnt; ++q) rank += sort_buf[q] > w;
+        idx[rank] = (int32_t)(~(uint32_t)w);
+        vals[rank] = from_key((uint32_t)(w >> 32));
+      }
+    } else {
+      for (int j = t; j < c; j += kBig) sort_buf[j] = bw[j];
+      const uint64_t *sorted = sort_winners_desc(sort_buf, sort_buf + FATHOM_MAX_K, c);
+      for (int j = t; j < c; j += kBig) {
+        const uint64_t w = sorted[j];
+        idx[b0 + j] = (int32_t)(~(uint32_t)w);
+        vals[b0 + j] = from_key((uint32_t)(w >> 32));
+      }
     }
   }
   for (int j = kk + t; j < k; j += kBig) {
