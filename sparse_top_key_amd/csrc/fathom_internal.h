@@ -25,6 +25,7 @@ __host__ __device__ inline int64_t sample_tile(int64_t j, int64_t ns, int64_t nt
   return (2 * j + 1) * nt / (2 * ns);
 }
 constexpr int kCntStride = 32;          // candidate counters, one 128-byte line each
+constexpr int kMaxGH = 4;               // query heads per scan launch chunk
 // Candidate store of the fused call: per output row, one segment per scan
 // block of the row's kv head (at most kMaxSeg), kFusedCap words in all; a
 // block whose candidates outgrow its segment puts the rest in the row's
@@ -61,8 +62,10 @@ __device__ __forceinline__ uint64_t compose(uint32_t key, int64_t i) {
 struct TopkWs {
   uint32_t *thr, *cnt, *flag, *redo;
   uint64_t *cand;
-  uint32_t *seg_cnt;  // fused final only: [rows][kMaxSeg]
-  uint64_t *fcand;    // fused final only: [rows][kFusedCap]
+  uint32_t *seg_cnt;    // fused final only: [rows][kMaxSeg]
+  uint64_t *fcand;      // fused final only: [rows][kFusedCap]
+  uint32_t *redo_done;  // fused threshold only: [session][hkv][redo_chunks], zeroed there
+  int32_t redo_chunks;  // head chunks per kv head
 };
 int64_t topk_ws_bytes(int64_t out_rows, int64_t redo_slots);
 TopkWs topk_ws_carve(void *ws, int64_t out_rows, int64_t redo_slots);
@@ -132,6 +135,14 @@ struct ScanSession {
   uint32_t *ovf_cnt;      // [rows] (stride kCntStride): candidates past their segment
   uint64_t *ovf;          // [rows][kCandCap] ... stored here, in arrival order
   const uint32_t *redo;   // [hkv]: recompute only the kv heads flagged here
+  // recompute scan of a fused call: the last block of each flagged (kv head,
+  // head chunk) ranks the chunk's flagged rows into the outputs
+  uint32_t *redo_done;    // [hkv][head chunks] blocks finished (zeroed earlier in the call)
+  const uint32_t *row_flag;  // [rows] rows to recompute
+  int32_t *out_idx;       // [rows][out_k]
+  float *out_vals;        // [rows][out_k]
+  int32_t out_k;
+  int32_t out_group;      // 1: a row per query head; hq / hkv: a row per kv head
   uint8_t *table;         // slot tables of the session's kv heads, or null
   int32_t table_mode;     // ScanTable: what the scan does with them
   int32_t residency;      // planes: 0 unknown (queried), 1 device, 2 pinned host
@@ -182,9 +193,9 @@ struct TopkSession {
 int64_t topk_workspace_bytes(int32_t out_rows);
 // Plain: sample -> compact -> final over the scores.  Fused: threshold from
 // scores holding only the sampled logits, then (after the candidate scan) a
-// final pass that flags rows whose candidate count is out of range.  Redo:
-// exact final over full scores for the flagged rows only.
-enum TopkStage { kTopkAll = 0, kTopkThreshold = 1, kTopkFusedFinal = 2, kTopkRedoFinal = 3 };
+// final pass that flags rows whose candidate count is out of range (the
+// recompute scan ranks those).
+enum TopkStage { kTopkAll = 0, kTopkThreshold = 1, kTopkFusedFinal = 2 };
 int32_t launch_topk(const TopkSession *sess, int32_t n_sess, int32_t rows_per_sess,
                     int32_t group, int32_t k, const TopkWs &w, hipStream_t s,
                     int32_t stage = kTopkAll, int32_t rows_per_kv = 1, int32_t hkv = 1);

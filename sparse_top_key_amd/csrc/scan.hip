@@ -34,6 +34,7 @@
 #include <type_traits>
 
 #include "fathom_internal.h"
+#include "select.h"
 
 namespace fathom {
 namespace {
@@ -42,7 +43,6 @@ constexpr int kScanThreads = 256;
 constexpr int kMinSetupThreads = 256;             // smallest block building a slot table
 constexpr int kMaxSlots = kD * kPlanes;           // (channel, depth) pairs
 constexpr int kMaxGroups = kMaxSlots / 8;
-constexpr int kMaxGH = 4;                          // heads per launch chunk
 
 struct ScanSess {
   const uint32_t *planes;
@@ -61,12 +61,17 @@ struct ScanSess {
   // fused scan + top-k
   float *sample;
   const uint32_t *thr;
-  uint32_t *cnt;
   uint64_t *cand;
   uint32_t *seg_cnt;
   uint32_t *ovf_cnt;
   uint64_t *ovf;
   const uint32_t *redo;
+  // recompute scan of a fused call (null otherwise): blocks finished per
+  // (kv head, head chunk), the rows to recompute and the outputs
+  uint32_t *redo_done;
+  const uint32_t *row_flag;
+  int32_t *out_idx;
+  float *out_vals;
   int32_t seg_cap;         // candidate words per (row, block) segment
   uint8_t *table;          // slot records of the session, or null
   int32_t table_mode;      // ScanTable
@@ -76,7 +81,9 @@ struct ScanSess {
 struct ScanArgs {
   ScanSess s[kSessPerLaunch];
   int32_t n_sess, hkv, group, head0;
+  int32_t out_k, out_group;  // recompute scan: outputs per row; query heads per row
 };
+static_assert(sizeof(ScanArgs) <= 4096, "kernel arguments");
 
 // The kernels read their descriptors in place from the kernel-argument
 // segment (address space 4): indexing them by session then needs no copy.
@@ -744,6 +751,7 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   __shared__ float s_tf[kMaxGH];       // float thresholds of the block's rows
   __shared__ int s_ht[kMaxGH];         // integer pre-check bounds (see hi_bound)
   __shared__ int s_nslots;
+  __shared__ int s_last;  // recompute scan: this block finished its (kv head, chunk) last
   // code-buffer ring: [0..1] groups stored in buffer 0/1 (one count per
   // producer task), [2..3] releases (one per consumer wave and item); counts
   // only grow during a launch
@@ -1375,6 +1383,51 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
       }
     }
   }
+  if constexpr (MODE == kScanLogits) {
+    // Recompute scan of a fused call: the block of a flagged (kv head, head
+    // chunk) that finishes last ranks the chunk's flagged rows from the
+    // logits every block of it wrote (a device-scope fence on each side of
+    // the count makes those stores visible to it), in the code buffers.
+    if (S.redo_done) {
+      __syncthreads();
+      if (tid == 0) {
+        __threadfence();
+        s_last = atomicAdd(&S.redo_done[bw.rec], 1u) == (uint32_t)(S.blocks_per_head - 1);
+      }
+      __syncthreads();
+      if (s_last) {
+        __threadfence();
+        constexpr int kSortWords = kBuckCap + 2 * FATHOM_MAX_K;
+        uint8_t *lds = reinterpret_cast<uint8_t *>(&s_codes[0][0]);
+        static_assert((kSortWords + kBuckCap) * 8 + (2 * kHistBins + 8) * 4 + 16 * 8 + 16 * 4 +
+                              16 <= sizeof(s_codes),
+                      "selection scratch");
+        SelScratch X;
+        X.s = reinterpret_cast<uint64_t *>(lds);
+        X.win = X.s + kSortWords;
+        X.red = X.win + kBuckCap;
+        X.hist = reinterpret_cast<int *>(X.red + 16);
+        X.above = X.hist + kHistBins;
+        X.wave_tot = X.above + kHistBins + 4;
+        X.s_res = X.wave_tot + 16;
+        X.s_count = X.s_res + 2;
+        const int k = a.out_k, G = a.out_group;
+        if (G > 1) {
+          // one row per kv head, scored by the sum of its G query heads
+          if (S.row_flag[g])
+            exact_row_topk(S.logits + (int64_t)head_base * S.ld, S.ld, G, n, k,
+                           S.out_idx + (int64_t)g * k, S.out_vals + (int64_t)g * k, X);
+        } else {
+          for (int j = 0; j < GH; ++j) {
+            const int o = head_base + j;
+            if (S.row_flag[o])
+              exact_row_topk(S.logits + (int64_t)o * S.ld, S.ld, 1, n, k,
+                             S.out_idx + (int64_t)o * k, S.out_vals + (int64_t)o * k, X);
+          }
+        }
+      }
+    }
+  }
   if constexpr (MODE == kScanCand || MODE == kScanCandGroup) {
     // every block reports its count (above seg_cap: the rest is in the
     // row's overflow list)
@@ -1609,6 +1662,8 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_
       a.hkv = hkv;
       a.group = group;
       a.head0 = head0;
+      a.out_k = sess[s0].out_k;
+      a.out_group = sess[s0].out_group > 0 ? sess[s0].out_group : 1;
       int32_t blocks = 0;
       for (int j = 0; j < cnt; ++j) {
         const ScanSession &in = sess[s0 + j];
@@ -1633,6 +1688,10 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_
         o.ovf_cnt = in.ovf_cnt;
         o.ovf = in.ovf;
         o.redo = in.redo;
+        o.redo_done = in.redo ? in.redo_done : nullptr;
+        o.row_flag = in.row_flag;
+        o.out_idx = in.out_idx;
+        o.out_vals = in.out_vals;
         o.rs = in.rs;
         o.table = fp32_path ? nullptr : in.table;
         o.table_mode = fp32_path || !in.table ? kTableNone : in.table_mode;

@@ -17,12 +17,13 @@
 //   4. final          the exact top k of each row whose candidate count lies
 //                     in [k, 8192], ranked and written; other rows flagged,
 //   5. redo scan      full logits of the flagged rows' kv heads, tiled like
-//                     any scan (blocks of unflagged kv heads return at once),
-//   6. redo final     exact top k of the flagged rows from those logits.
+//                     any scan (blocks of unflagged kv heads return at once);
+//                     the last block of each flagged kv head to finish then
+//                     ranks the exact top k of its flagged rows.
 // Every score >= T is a candidate, so a row with k..8192 candidates holds
-// its exact top k; the redo steps cover every other row (a sample that
-// misjudged the row, or more than 8192 scores tied at the threshold).  Steps
-// 5-6 cost one early-exiting launch each when no row is flagged.
+// its exact top k; step 5 covers every other row (a sample that misjudged
+// the row, or more than 8192 scores tied at the threshold) and costs one
+// early-exiting launch when no row is flagged.
 //
 // Planes in pinned host memory, sessions above 2^25 keys, or groups other
 // than 1 and hq/hkv <= 4: the logits go to the workspace and fathom_topk's
@@ -51,16 +52,21 @@ int64_t sampled_keys(int64_t n) {
 }
 
 struct Layout {
-  int64_t topk_off, seg_off, fcand_off, sample_off, table_off, table_bytes, logits_off, total;
+  int64_t topk_off, done_off, seg_off, fcand_off, sample_off, table_off, table_bytes, logits_off,
+      total;
   int64_t out_rows, redo_slots;
+  int32_t chunks;  // scan head chunks per kv head
 };
 
 Layout layout(const int64_t *n, int32_t n_sess, int32_t hkv, int32_t hq, int32_t group) {
   Layout L;
   L.out_rows = (int64_t)n_sess * (hq / group);
   L.redo_slots = std::max<int64_t>(L.out_rows, (int64_t)n_sess * hkv);
+  L.chunks = (hq / hkv + kMaxGH - 1) / kMaxGH;
   L.topk_off = 0;
-  L.seg_off = align256(topk_ws_bytes(L.out_rows, L.redo_slots));
+  L.done_off = align256(topk_ws_bytes(L.out_rows, L.redo_slots));
+  L.seg_off = L.done_off +
+              align256((int64_t)n_sess * hkv * L.chunks * (int64_t)sizeof(uint32_t));
   L.fcand_off = L.seg_off + align256(L.out_rows * kMaxSeg * (int64_t)sizeof(uint32_t));
   L.sample_off = L.fcand_off + align256(L.out_rows * kFusedCap * (int64_t)sizeof(uint64_t));
   L.table_off =
@@ -91,6 +97,8 @@ int32_t launch_scan_topk(const ScanSession *in, int32_t *const *idx, float *cons
   TopkWs tw = topk_ws_carve(w + L.topk_off, L.out_rows, L.redo_slots);
   tw.seg_cnt = reinterpret_cast<uint32_t *>(w + L.seg_off);
   tw.fcand = reinterpret_cast<uint64_t *>(w + L.fcand_off);
+  tw.redo_done = reinterpret_cast<uint32_t *>(w + L.done_off);
+  tw.redo_chunks = L.chunks;
   const int32_t rows_per_sess = hq / group;
   const int32_t rows_per_kv = std::max(1, rows_per_sess / hkv);
 
@@ -121,8 +129,15 @@ int32_t launch_scan_topk(const ScanSession *in, int32_t *const *idx, float *cons
     thr[j] = TopkSession{c.sample, sampled_keys(in[j].n), kSampleKeys, idx[j], vals[j],
                          in[j].n, 0};
     if (in[j].n > 0) {
+      // the recompute scan's view (the other scans clear these)
       sc[m] = c;
-      sc[m].redo = tw.redo + (int64_t)j * hkv;  // used by the redo scan only
+      sc[m].redo = tw.redo + (int64_t)j * hkv;
+      sc[m].redo_done = tw.redo_done + (int64_t)j * hkv * L.chunks;
+      sc[m].row_flag = tw.flag + row0;
+      sc[m].out_idx = idx[j];
+      sc[m].out_vals = vals[j];
+      sc[m].out_k = k;
+      sc[m].out_group = group;
       ++m;
     }
   }
@@ -132,6 +147,7 @@ int32_t launch_scan_topk(const ScanSession *in, int32_t *const *idx, float *cons
   for (int32_t j = 0; j < m; ++j) {
     plain[j] = sc[j];
     plain[j].redo = nullptr;
+    plain[j].redo_done = nullptr;
     first[j] = plain[j];
     first[j].table_mode = kTableWrite;
   }
@@ -160,10 +176,8 @@ int32_t launch_scan_topk(const ScanSession *in, int32_t *const *idx, float *cons
   if (int32_t rc = launch_topk(fin, n_sess, rows_per_sess, group, k, tw, s, kTopkFusedFinal,
                                rows_per_kv, hkv))
     return rc;
-  if (m > 0)
-    if (int32_t rc = launch_scan(sc, m, hkv, hq, s, kScanLogits)) return rc;
-  return launch_topk(fin, n_sess, rows_per_sess, group, k, tw, s, kTopkRedoFinal, rows_per_kv,
-                     hkv);
+  if (m > 0) return launch_scan(sc, m, hkv, hq, s, kScanLogits);
+  return FATHOM_OK;
 }
 
 }  // namespace fathom

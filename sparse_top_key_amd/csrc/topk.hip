@@ -31,15 +31,15 @@
 // +0); a GQA group's score is its rows' fp32 scores added in fp64, in row
 // order, rounded once.
 #include "fathom_internal.h"
+#include "select.h"
 
 namespace fathom {
 namespace {
 
-constexpr int kBig = 1024;            // threads of the per-row kernels
+constexpr int kBig = kSelThreads;     // threads of the per-row kernels
 constexpr int kCompactThreads = 256;
 constexpr int kCompactChunk = 16384;  // scores per compact block
 constexpr int kRun = 64;              // contiguous scores per sample run
-constexpr int kHistBins = 2048;
 constexpr int kStage = 2048;           // candidates staged per compact block
 
 struct TopkSess {
@@ -64,15 +64,9 @@ struct TopkArgs {
   uint64_t *cand;
   uint32_t *seg_cnt;    // fused final: [rows][kMaxSeg]
   uint64_t *fcand;      // fused final: [rows][kFusedCap]
+  uint32_t *redo_done;  // fused threshold: [session][hkv][redo_chunks] (zeroed)
+  int32_t redo_chunks;
 };
-
-__device__ __forceinline__ float group_score(const float *__restrict__ row, int64_t ld,
-                                             int group, int64_t i) {
-  if (group == 1) return row[i];
-  double acc = 0.0;
-  for (int j = 0; j < group; ++j) acc = __dadd_rn(acc, (double)row[(int64_t)j * ld + i]);
-  return (float)acc;
-}
 
 struct RowRef {
   const TopkSess *s;
@@ -88,159 +82,6 @@ __device__ __forceinline__ RowRef row_ref(const TopkArgs &a, int o) {
   return ref;
 }
 
-// Inclusive scan over the 1024 threads of a block (thread order).
-__device__ int block_inclusive_scan(int v, int *wave_tot) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int u = __shfl_up(v, off);
-    if (lane >= off) v += u;
-  }
-  if (lane == 63) wave_tot[wave] = v;
-  __syncthreads();
-  if (wave == 0) {
-    int t = lane < kBig / 64 ? wave_tot[lane] : 0;
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      const int u = __shfl_up(t, off);
-      if (lane >= off) t += u;
-    }
-    if (lane < kBig / 64) wave_tot[lane] = t;
-  }
-  __syncthreads();
-  const int r = v + (wave > 0 ? wave_tot[wave - 1] : 0);
-  __syncthreads();
-  return r;
-}
-
-// Given hist[nbins] of the digits still in play, find digit d such that
-// (#digits > d) < rem <= (#digits >= d).  Returns d; *above = #digits > d.
-__device__ int find_digit(const int *hist, int nbins, int rem, int *above,
-                          int *wave_tot, int *s_res) {
-  // thread t owns digits hi = nbins-1-2t and hi-1 (descending order)
-  const int t = threadIdx.x;
-  const int d1 = nbins - 1 - 2 * t, d2 = d1 - 1;
-  const int c1 = d1 >= 0 ? hist[d1] : 0;
-  const int c2 = d2 >= 0 ? hist[d2] : 0;
-  const int incl = block_inclusive_scan(c1 + c2, wave_tot);
-  const int excl = incl - c1 - c2;
-  if (excl < rem && rem <= incl) {
-    if (excl + c1 >= rem) {
-      s_res[0] = d1;
-      s_res[1] = excl;
-    } else {
-      s_res[0] = d2;
-      s_res[1] = excl + c1;
-    }
-  }
-  __syncthreads();
-  const int d = s_res[0];
-  *above = s_res[1];
-  __syncthreads();
-  return d;
-}
-
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// In-wave bitonic sort of 128 words, descending: lane l holds elements 2l and
-// 2l+1.  Stride 1 is a register compare; strides 2..64 exchange with the
-// partner lane (distance stride/2).
-__device__ __forceinline__ void wave_sort128_desc(uint64_t (&v)[2]) {
-  const int l = threadIdx.x & 63;
-#pragma unroll
-  for (int size = 2; size <= 128; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride == 1) {
-        const bool desc = ((2 * l) & size) == 0;
-        if (desc ? (v[0] < v[1]) : (v[0] > v[1])) {
-          const uint64_t x = v[0];
-          v[0] = v[1];
-          v[1] = x;
-        }
-        continue;
-      }
-      const int pt = stride >> 1;
-      const uint64_t o0 = shfl_xor64(v[0], pt), o1 = shfl_xor64(v[1], pt);
-      const uint64_t o[2] = {o0, o1};
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int e = 2 * l + r;
-        const bool lo = (e & stride) == 0;
-        const bool desc = ((lo ? e : (e ^ stride)) & size) == 0;
-        const bool keep_max = (lo == desc);
-        const uint64_t mx = v[r] > o[r] ? v[r] : o[r], mn = v[r] > o[r] ? o[r] : v[r];
-        v[r] = keep_max ? mx : mn;
-      }
-    }
-  }
-}
-
-// Sort the m <= FATHOM_MAX_K = 2048 unique words w[0..m) descending, with
-// entries past m read as 0; tmp is scratch of the same size.  Each wave
-// sorts a run of 128 in registers, then merge-path rounds double the run
-// length: thread t finds by binary search how many of the first 2t outputs
-// of its pair of runs come from the first run, and writes outputs 2t, 2t+1.
-// Returns the buffer holding the result.
-__device__ __forceinline__ uint64_t *sort_winners_desc(uint64_t *w, uint64_t *tmp, int m) {
-  int P = 128;
-  while (P < m) P <<= 1;
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  __syncthreads();
-  if (wave < P / 128) {
-    const int e0 = 128 * wave + 2 * lane;
-    uint64_t v[2] = {e0 < m ? w[e0] : 0ull, e0 + 1 < m ? w[e0 + 1] : 0ull};
-    wave_sort128_desc(v);
-    w[e0] = v[0];
-    w[e0 + 1] = v[1];
-  }
-  uint64_t *src = w, *dst = tmp;
-  for (int L = 128; L < P; L <<= 1) {
-    __syncthreads();
-    if (t < P / 2) {
-      const int base = (2 * t) / (2 * L) * (2 * L);
-      const int d = 2 * t - base;
-      const uint64_t *A = src + base, *B = src + base + L;
-      int lo = d > L ? d - L : 0, hi = d < L ? d : L;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (A[mid] > B[d - 1 - mid])
-          lo = mid + 1;
-        else
-          hi = mid;
-      }
-      int ia = lo, ib = d - lo;
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const bool takeA = ib >= L || (ia < L && A[ia] > B[ib]);
-        dst[base + d + r] = takeA ? A[ia++] : B[ib++];
-      }
-    }
-    uint64_t *x = src;
-    src = dst;
-    dst = x;
-  }
-  __syncthreads();
-  return src;
-}
-
-__device__ void write_out(const TopkSess &S, int r, int k, const uint64_t *s, int m) {
-  int32_t *idx = S.idx + (int64_t)r * k;
-  float *vals = S.vals + (int64_t)r * k;
-  for (int j = threadIdx.x; j < k; j += kBig) {
-    if (j < m) {
-      const uint64_t c = s[j];
-      idx[j] = (int32_t)(~(uint32_t)c);
-      vals[j] = from_key((uint32_t)(c >> 32));
-    } else {
-      idx[j] = -1;
-      vals[j] = -INFINITY;
-    }
-  }
-}
 
 // ---- sample -> threshold -----------------------------------------------------
 // Max, min and sum over the block (16 waves).
@@ -288,9 +129,15 @@ __global__ __launch_bounds__(kBig) void topk_sample_kernel(TopkArgs a) {
   const RowRef R = row_ref(a, o);
   const int64_t n = R.s->n, ld = R.s->ld, n_full = R.s->n_full;
   if (threadIdx.x == 0) {
+    const int r = o % a.rows_per_sess, si = o / a.rows_per_sess;
     a.cnt[(int64_t)o * kCntStride] = 0;
     a.flag[o] = 0;
-    a.redo[(o / a.rows_per_sess) * a.hkv + (o % a.rows_per_sess) / a.rows_per_kv] = 0;
+    a.redo[si * a.hkv + r / a.rows_per_kv] = 0;
+    // the recompute scan's count of finished blocks of this row's (kv head,
+    // head chunk)
+    if (a.redo_done)
+      a.redo_done[((int64_t)si * a.hkv + r / a.rows_per_kv) * a.redo_chunks +
+                  (r % a.rows_per_kv) / kMaxGH] = 0;
   }
   if (n_full <= kCandCap) {
     if (threadIdx.x == 0) a.thr[o] = 0;
@@ -566,155 +413,6 @@ __device__ uint64_t select_kth(const uint64_t *s, int m, int kk, int *hist, int 
   return prefix;
 }
 
-// OR of v over the block.
-__device__ uint64_t block_or64(uint64_t v, uint64_t *red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v |= shfl_xor64(v, off);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  uint64_t r = 0;
-#pragma unroll
-  for (int w = 0; w < kBig / 64; ++w) r |= red[w];
-  __syncthreads();
-  return r;
-}
-
-// Writes the kk largest of the unique words src[0..m) (1 <= kk <= m) to
-// output row r in descending order, without sorting: words are bucketed by
-// the 11 bits below their common prefix, the buckets at or above the one
-// holding the kk-th word are laid out in descending bucket order, and each
-// word's rank is its bucket's offset plus the number of larger words in its
-// bucket.  Buckets grow when the candidates span two binades, so that the
-// binning window starts in the exponent bits; a word's rank is a loop over
-// its bucket, and even at 512 words that costs far less than a sort.  One
-// larger bucket strictly above the kk-th word's (top keys clustered in a
-// narrow score range: all of its words are winners, at most kk of them) is
-// ranked on its own, binned again below its own words' common prefix, in
-// `sort_buf` (2 * FATHOM_MAX_K words; sorted there when that fails).  Returns false, having written nothing, for anything else
-// (the caller then selects and sorts).  buck holds kBuckCap words, above
-// kHistBins + 1 ints.
-constexpr int kMaxBucket = 512;
-constexpr int kBuckCap = FATHOM_MAX_K + kMaxBucket;
-
-__device__ __forceinline__ bool bucket_rank_out(const uint64_t *src, int m, int kk, uint64_t *buck, int *hist,
-                                int *above, int *wave_tot, int *s_res, uint64_t *red,
-                                const TopkSess &S, int r, int k, uint64_t *sort_buf) {
-  const int t = threadIdx.x;
-  uint64_t diff = 0;
-  const uint64_t w0 = src[0];
-  for (int j = t; j < m; j += kBig) diff |= src[j] ^ w0;
-  diff = block_or64(diff, red);
-  const int hb = diff ? 63 - __clzll(diff) : 0;  // highest bit in which words differ
-  const int sh = hb > 10 ? hb - 10 : 0;
-  for (int b = t; b < kHistBins; b += kBig) hist[b] = 0;
-  if (t == 0) s_res[1] = 0;
-  __syncthreads();
-  for (int j = t; j < m; j += kBig) atomicAdd(&hist[(int)((src[j] >> sh) & (kHistBins - 1))], 1);
-  __syncthreads();
-  // above[d] = words in digits > d; thread t owns digits 2047-2t and 2046-2t
-  const int d1 = kHistBins - 1 - 2 * t, d2 = d1 - 1;
-  const int c1 = hist[d1], c2 = hist[d2];
-  const int incl = block_inclusive_scan(c1 + c2, wave_tot);
-  const int excl = incl - c1 - c2;
-  above[d1] = excl;
-  above[d2] = excl + c1;
-  if (excl < kk && kk <= excl + c1) s_res[0] = d1;
-  if (excl + c1 < kk && kk <= incl) s_res[0] = d2;
-  __syncthreads();
-  const int db = s_res[0];  // digit holding the kk-th word
-  // big buckets at or above db: one strictly above db (all of its words are
-  // winners) is sorted on its own; the kk-th word's bucket must stay small
-  const int big1 = d1 >= db && c1 > kMaxBucket, big2 = d2 >= db && c2 > kMaxBucket;
-  if ((big1 && d1 == db) || (big2 && d2 == db)) atomicAdd(&s_res[1], 2);
-  if (big1) {
-    atomicAdd(&s_res[1], 1);
-    above[kHistBins] = d1;
-  }
-  if (big2) {
-    atomicAdd(&s_res[1], 1);
-    above[kHistBins] = d2;
-  }
-  __syncthreads();
-  const int nbig = s_res[1];
-  if (nbig > 1) return false;
-  const int dbig = nbig == 1 ? above[kHistBins] : -1;
-  // bucket order; above[d] becomes the end of bucket d
-  for (int j = t; j < m; j += kBig) {
-    const uint64_t w = src[j];
-    const int d = (int)((w >> sh) & (kHistBins - 1));
-    if (d >= db) buck[atomicAdd(&above[d], 1)] = w;
-  }
-  __syncthreads();
-  const int total = above[db];
-  int32_t *idx = S.idx + (int64_t)r * k;
-  float *vals = S.vals + (int64_t)r * k;
-  for (int p = t; p < total; p += kBig) {
-    const uint64_t w = buck[p];
-    const int d = (int)((w >> sh) & (kHistBins - 1));
-    if (d == dbig) continue;
-    const int c = hist[d];
-    const int b0 = above[d] - c;
-    int rank = b0;
-    for (int q = b0; q < b0 + c; ++q) rank += buck[q] > w;
-    if (rank < kk) {
-      idx[rank] = (int32_t)(~(uint32_t)w);
-      vals[rank] = from_key((uint32_t)(w >> 32));
-    }
-  }
-  if (dbig >= 0) {
-    // The big bucket (words buck[b0 .. b0+c), ranks b0 ..): binned again on
-    // the 11 bits below its own words' common prefix and ranked within those
-    // bins as above; should a bin still exceed the cap, the bucket is sorted.
-    const int c = hist[dbig], b0 = above[dbig] - c;
-    const uint64_t *bw = buck + b0;
-    uint64_t dif = 0;
-    for (int j = t; j < c; j += kBig) dif |= bw[j] ^ bw[0];
-    dif = block_or64(dif, red);  // (its barrier also ends the ranking loop above)
-    const int hb2 = dif ? 63 - __clzll(dif) : 0;
-    const int sh2 = hb2 > 10 ? hb2 - 10 : 0;
-    for (int b = t; b < kHistBins; b += kBig) hist[b] = 0;
-    if (t == 0) s_res[1] = 0;
-    __syncthreads();
-    for (int j = t; j < c; j += kBig) atomicAdd(&hist[(int)((bw[j] >> sh2) & (kHistBins - 1))], 1);
-    __syncthreads();
-    const int h1 = hist[d1], h2 = hist[d2];
-    const int inc2 = block_inclusive_scan(h1 + h2, wave_tot);
-    above[d1] = inc2 - h1 - h2;
-    above[d2] = inc2 - h2;
-    if (h1 > kMaxBucket || h2 > kMaxBucket) s_res[1] = 1;
-    __syncthreads();
-    if (!s_res[1]) {
-      for (int j = t; j < c; j += kBig) {
-        const uint64_t w = bw[j];
-        sort_buf[atomicAdd(&above[(int)((w >> sh2) & (kHistBins - 1))], 1)] = w;
-      }
-      __syncthreads();
-      for (int p = t; p < c; p += kBig) {
-        const uint64_t w = sort_buf[p];
-        const int d = (int)((w >> sh2) & (kHistBins - 1));
-        const int cnt = hist[d];
-        const int s0 = above[d] - cnt;
-        int rank = b0 + s0;
-        for (int q = s0; q < s0 + cnt; ++q) rank += sort_buf[q] > w;
-        idx[rank] = (int32_t)(~(uint32_t)w);
-        vals[rank] = from_key((uint32_t)(w >> 32));
-      }
-    } else {
-      for (int j = t; j < c; j += kBig) sort_buf[j] = bw[j];
-      const uint64_t *sorted = sort_winners_desc(sort_buf, sort_buf + FATHOM_MAX_K, c);
-      for (int j = t; j < c; j += kBig) {
-        const uint64_t w = sorted[j];
-        idx[b0 + j] = (int32_t)(~(uint32_t)w);
-        vals[b0 + j] = from_key((uint32_t)(w >> 32));
-      }
-    }
-  }
-  for (int j = kk + t; j < k; j += kBig) {
-    idx[j] = -1;
-    vals[j] = -INFINITY;
-  }
-  return true;
-}
 
 // ---- exact selection of each row's top k -------------------------------------
 __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
@@ -754,122 +452,72 @@ __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
   } else {
     cnt = a.cnt[(int64_t)o * kCntStride];
   }
-  bool fast = (n <= kCandCap) || (cnt >= (uint32_t)k && cnt <= (uint32_t)kCandCap);
-  if (a.stage == kTopkRedoFinal) {
-    if (!a.flag[o]) return;  // this row was answered from its candidates
-    fast = false;
-  } else if (a.stage == kTopkFusedFinal && !fast) {
-    // too few or too many candidates: the row is recomputed from full logits
-    if (threadIdx.x == 0) {
-      a.flag[o] = 1;
-      a.redo[(o / a.rows_per_sess) * a.hkv + r / a.rows_per_kv] = 1;
+  const bool fast = (n <= kCandCap) || (cnt >= (uint32_t)k && cnt <= (uint32_t)kCandCap);
+  int32_t *idx = S.idx + (int64_t)r * k;
+  float *vals = S.vals + (int64_t)r * k;
+  if (!fast) {
+    if (a.stage == kTopkFusedFinal) {
+      // too few or too many candidates: the row is recomputed from full
+      // logits (by the last block of the recompute scan of its kv head)
+      if (threadIdx.x == 0) {
+        a.flag[o] = 1;
+        a.redo[(o / a.rows_per_sess) * a.hkv + r / a.rows_per_kv] = 1;
+      }
+      return;
     }
+    // exact recomputation over the whole row
+    const SelScratch X{win, s, hist, above, wave_tot, s_res, &s_count, red};
+    exact_row_topk(R.row, ld, a.group, n, k, idx, vals, X);
     return;
   }
   if (threadIdx.x == 0) s_count = 0;
-  if (fast) {
-    const int m = (int)cnt;
-    if (a.stage == kTopkFusedFinal) {
-      const int nseg = S.nseg, seg_cap = kFusedCap / (nseg > 0 ? nseg : 1);
-      const uint64_t *fc = a.fcand + (int64_t)o * kFusedCap;
-      // kBig / nseg threads per segment; each has 8 loads in flight before it
-      // stores (segments hold at most seg_cap words: no overflow here)
-      const int tps = kBig / (nseg > 0 ? nseg : 1);
-      const int sg = threadIdx.x / tps, sub = threadIdx.x % tps;
-      if (sg < nseg) {
-        const int c = (sg + 1 < nseg ? s_off[sg + 1] : s_off[kMaxSeg]) - s_off[sg];
-        const uint64_t *src = fc + (int64_t)sg * seg_cap;
-        uint64_t *dst = s + s_off[sg];
-        for (int b0 = sub; b0 < c; b0 += 8 * tps) {
-          uint64_t v[8];
+  const int m = (int)cnt;
+  if (a.stage == kTopkFusedFinal) {
+    const int nseg = S.nseg, seg_cap = kFusedCap / (nseg > 0 ? nseg : 1);
+    const uint64_t *fc = a.fcand + (int64_t)o * kFusedCap;
+    // kBig / nseg threads per segment; each has 8 loads in flight before it
+    // stores (segments hold at most seg_cap words: no overflow here)
+    const int tps = kBig / (nseg > 0 ? nseg : 1);
+    const int sg = threadIdx.x / tps, sub = threadIdx.x % tps;
+    if (sg < nseg) {
+      const int c = (sg + 1 < nseg ? s_off[sg + 1] : s_off[kMaxSeg]) - s_off[sg];
+      const uint64_t *src = fc + (int64_t)sg * seg_cap;
+      uint64_t *dst = s + s_off[sg];
+      for (int b0 = sub; b0 < c; b0 += 8 * tps) {
+        uint64_t v[8];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int i = b0 + u * tps;
-            v[u] = src[i < c ? i : c - 1];
-          }
+        for (int u = 0; u < 8; ++u) {
+          const int i = b0 + u * tps;
+          v[u] = src[i < c ? i : c - 1];
+        }
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int i = b0 + u * tps;
-            if (i < c) dst[i] = v[u];
-          }
+        for (int u = 0; u < 8; ++u) {
+          const int i = b0 + u * tps;
+          if (i < c) dst[i] = v[u];
         }
       }
-      // then the overflow list (m <= kCandCap words in all)
-      const int stored = s_off[kMaxSeg];
-      const uint64_t *ov = a.cand + (int64_t)o * kCandCap;
-      for (int j = threadIdx.x; j < m - stored; j += kBig) s[stored + j] = ov[j];
-    } else {
-      const uint64_t *cand = a.cand + (int64_t)o * kCandCap;
-      for (int j = threadIdx.x; j < m; j += kBig) s[j] = cand[j];
     }
-    __syncthreads();
-    if (kk > 0 &&
-        bucket_rank_out(s, m, kk, win, hist, above, wave_tot, s_res, red, S, r, k,
-                        s + kBuckCap))
-      return;
-    if (kk > 0) {
-      const uint64_t T = m > kk ? select_kth(s, m, kk, hist, wave_tot, s_res) : 0ull;
-      for (int j = threadIdx.x; j < m; j += kBig)
-        if (s[j] >= T) win[atomicAdd(&s_count, 1)] = s[j];
-    }
+    // then the overflow list (m <= kCandCap words in all)
+    const int stored = s_off[kMaxSeg];
+    const uint64_t *ov = a.cand + (int64_t)o * kCandCap;
+    for (int j = threadIdx.x; j < m - stored; j += kBig) s[stored + j] = ov[j];
   } else {
-    // exact recomputation over the whole row
-    int rem = kk;
-    uint32_t prefix = 0, pmask = 0;
-    const int shifts[3] = {21, 10, 0};
-    const int bits[3] = {11, 11, 10};
-    for (int pass = 0; pass < 3; ++pass) {
-      const int sh = shifts[pass], nb = 1 << bits[pass];
-      for (int b = threadIdx.x; b < kHistBins; b += kBig) hist[b] = 0;
-      __syncthreads();
-      for (int64_t i = threadIdx.x; i < n; i += kBig) {
-        const uint32_t v = to_key(group_score(R.row, ld, a.group, i));
-        if ((v & pmask) == prefix) atomicAdd(&hist[(v >> sh) & (nb - 1)], 1);
-      }
-      __syncthreads();
-      int above = 0;
-      const int d = find_digit(hist, nb, rem, &above, wave_tot, s_res);
-      rem -= above;
-      prefix |= (uint32_t)d << sh;
-      pmask |= (uint32_t)(nb - 1) << sh;
-    }
-    const uint32_t kth = prefix;  // key of the kk-th largest score
-    const int need_eq = rem;      // how many scores equal to it are kept
-    int eq_seen = 0;
-    for (int64_t b0 = 0; b0 < n; b0 += (int64_t)kBig * 4) {
-      uint32_t key[4];
-      int eqc = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t i = b0 + threadIdx.x * 4 + e;
-        key[e] = i < n ? to_key(group_score(R.row, ld, a.group, i)) : 0u;
-        eqc += (i < n && key[e] == kth);
-      }
-      const int incl = block_inclusive_scan(eqc, wave_tot);
-      int rank = eq_seen + incl - eqc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t i = b0 + threadIdx.x * 4 + e;
-        if (i >= n) continue;
-        bool take = key[e] > kth;
-        if (key[e] == kth) {
-          take = rank < need_eq;
-          ++rank;
-        }
-        if (take) win[atomicAdd(&s_count, 1)] = compose(key[e], i);
-      }
-      eq_seen += wave_tot[kBig / 64 - 1];
-      __syncthreads();
-    }
+    const uint64_t *cand = a.cand + (int64_t)o * kCandCap;
+    for (int j = threadIdx.x; j < m; j += kBig) s[j] = cand[j];
+  }
+  __syncthreads();
+  if (kk > 0 && bucket_rank_out(s, m, kk, win, hist, above, wave_tot, s_res, red, idx, vals, k,
+                                s + kBuckCap))
+    return;
+  if (kk > 0) {
+    const uint64_t T = m > kk ? select_kth(s, m, kk, hist, wave_tot, s_res) : 0ull;
+    for (int j = threadIdx.x; j < m; j += kBig)
+      if (s[j] >= T) win[atomicAdd(&s_count, 1)] = s[j];
   }
   __syncthreads();
   // win[0..kk) holds the winners
-  if (!fast && kk > 0 &&
-      bucket_rank_out(win, kk, kk, s, hist, above, wave_tot, s_res, red, S, r, k,
-                      s + kBuckCap))
-    return;
   const uint64_t *sorted = sort_winners_desc(win, s, kk);
-  write_out(S, r, k, sorted, kk);
+  write_out(idx, vals, k, sorted, kk);
 }
 
 }  // namespace
@@ -896,6 +544,8 @@ TopkWs topk_ws_carve(void *ws, int64_t out_rows, int64_t redo_slots) {
   t.cand = reinterpret_cast<uint64_t *>(w + small + out_rows * kCntStride * sizeof(uint32_t));
   t.seg_cnt = nullptr;
   t.fcand = nullptr;
+  t.redo_done = nullptr;
+  t.redo_chunks = 1;
   return t;
 }
 
@@ -926,6 +576,10 @@ int32_t launch_topk(const TopkSession *sess, int32_t n_sess, int32_t rows_per_se
     a.cand = w.cand + rows_before * kCandCap;
     a.seg_cnt = w.seg_cnt ? w.seg_cnt + rows_before * kMaxSeg : nullptr;
     a.fcand = w.fcand ? w.fcand + rows_before * kFusedCap : nullptr;
+    a.redo_done = stage == kTopkThreshold && w.redo_done
+                      ? w.redo_done + (int64_t)s0 * hkv * w.redo_chunks
+                      : nullptr;
+    a.redo_chunks = w.redo_chunks;
     int64_t max_n = 0;
     for (int j = 0; j < cnt; ++j) {
       const TopkSession &in = sess[s0 + j];
