@@ -440,10 +440,13 @@ int32_t fathom_scan_topk_blocked(const uint32_t *planes, const float *lo, const 
  * this step out.  Here the selected keys' full-precision K and V rows are
  * gathered (token-major, in HBM or pinned host memory) and, per query head h
  * with kv head g = h / (hq / hkv), over the entries of its index row:
- *   s_i = scale * sum_c q_hc K_igc   (fp32 products and sums, channel order)
+ *   s_i = scale * sum_c q_hc K_igc   (fp32 products and sums: runs of 8
+ *                                     (fp16) or 4 (fp32) channels in order,
+ *                                     their sums by a butterfly)
  *   m = max s_i, p_i = exp(s_i - m), out_h = sum_i p_i V_ig / sum_i p_i,
  *   lse_h = m + log(sum_i p_i)       (natural log)
- * in fp32 (per 64 entries a partial (m, sum p, sum p V), merged by maxima).
+ * in fp32 (partials (m, sum p, sum p V) over at most 64 entries each,
+ * merged by maxima).
  *
  * q        device fp32[hq][d]
  * k_cache, v_cache  device or pinned-host rows of `dtype` (FATHOM_F16 or

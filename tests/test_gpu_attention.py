@@ -3,8 +3,10 @@ over the listed keys): fp16 and fp32 caches, groups 1/2/4/8, ragged and padded
 index rows, strided and pinned-host caches, entries out of range, empty rows,
 and the decode step's own indices from fathom_scan_topk at the 1M-key size.
 
-Tolerance, derived from the fp32 arithmetic: a score is a chain of d fused
-multiply-adds and one scaling, so |s_gpu - s| <= eps_s with
+Tolerance, derived from the fp32 arithmetic: a score is a sum of d fp32
+products along which every term meets at most d + 1 roundings (fused
+multiply-adds over runs of channels, a butterfly over the runs, one
+scaling), so |s_gpu - s| <= eps_s with
 eps_s = scale * (d + 2) * 2^-24 * max_i sum_c |q_c K_ic|.  Score errors move
 each softmax weight by a relative 2 eps_s at most (first order), and a
 convex combination of V rows then moves by <= 2 eps_s max|V|; the fp32 sums
@@ -83,11 +85,21 @@ def rand_idx(seed, rows, k, n, pad=0):
     return torch.from_numpy(idx)
 
 
-@pytest.mark.parametrize("k", [1, 63, 64, 65, 255, 256, 257, 1000, 2048])
+@pytest.mark.parametrize("k", [1, 63, 64, 65, 255, 256, 257, 1000, 2048, 2500])
 def test_attention_per_head_fp16(F, orc, k):
     K, V = caches(k, 5000, 2, torch.float16)
     q = torch.randn((8, 128), generator=torch.Generator().manual_seed(k))
     check(F, orc, q, K, V, rand_idx(k, 8, k, 5000), 1)
+
+
+@pytest.mark.parametrize("k,group,dtype", [(9000, 1, torch.float16), (12345, 2, torch.float32)])
+def test_attention_long_rows(F, orc, k, group, dtype):
+    """Rows above 8192 entries: 64 entries per wave, more than one batch of
+    block partials to merge."""
+    n = 20000
+    K, V = caches(k, n, 2, dtype)
+    q = torch.randn((4, 128), generator=torch.Generator().manual_seed(k))
+    check(F, orc, q, K, V, rand_idx(k, 4 // group, k, n, pad=100), group)
 
 
 @pytest.mark.parametrize("group,hq,hkv", [(2, 8, 2), (4, 8, 2), (8, 16, 2), (4, 32, 8)])
