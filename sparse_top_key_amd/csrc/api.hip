@@ -486,7 +486,7 @@ int32_t fathom_topk(const float *scores, int32_t rows, int64_t n, int64_t ld, in
   REQUIRE(ws && ws_bytes >= need, FATHOM_ERR_WORKSPACE,
           "fathom_topk: workspace of %lld bytes needed (got %lld)", (long long)need,
           (long long)ws_bytes);
-  TopkSession t{scores, n, ld, idx, vals, n};
+  TopkSession t{scores, nullptr, n, ld, idx, vals, n};
   const TopkWs w = topk_ws_carve(ws, rows / group, rows / group);
   return launch_topk(&t, 1, rows / group, group, k, w, as_stream(stream));
 }
@@ -510,7 +510,7 @@ int32_t fathom_topk_noalloc(const float *scores, int32_t rows, int64_t n, int64_
           (long long)noalloc_scratch_bytes());
   void *ws = nullptr;
   if (int32_t rc = noalloc_scratch(&ws)) return rc;
-  TopkSession t{scores, n, ld, idx, vals, n};
+  TopkSession t{scores, nullptr, n, ld, idx, vals, n};
   const TopkWs w = topk_ws_carve(ws, out_rows, out_rows);
   return launch_topk(&t, 1, out_rows, group, k, w, as_stream(stream));
 }
@@ -530,7 +530,7 @@ int32_t fathom_topk_batched(const fathom_session *sessions, int32_t n_sessions, 
             "fathom_topk_batched: n must be in [0, 2^31)");
     REQUIRE(s.n == 0 || s.logits, FATHOM_ERR_INVALID_ARG, "fathom_topk_batched: null logits");
     REQUIRE(s.ld_logits >= s.n, FATHOM_ERR_INVALID_ARG, "fathom_topk_batched: ld < n");
-    ts[i] = TopkSession{s.logits, s.n, s.ld_logits, s.idx, s.vals, s.n};
+    ts[i] = TopkSession{s.logits, nullptr, s.n, s.ld_logits, s.idx, s.vals, s.n};
   }
   const int32_t out_rows = n_sessions * (hq / group);
   const int64_t need = topk_workspace_bytes(out_rows);

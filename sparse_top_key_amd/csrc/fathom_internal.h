@@ -16,7 +16,11 @@ constexpr int kSessPerLaunch = 16;      // sessions carried in one kernarg set
 constexpr int kCandCap = 8192;          // top-k candidates kept per row
 constexpr int kSampleTarget = 16384;    // sampled scores per row (threshold)
 constexpr int kSampleTiles = 32;        // 2048-key tiles a fused call scores first
-constexpr int kSampleKeys = kSampleTiles * kBlockKeys;
+// The threshold's subsample of a sampled tile: the first 64 of every 256 keys
+// (512 per tile, 16384 per row at 32 tiles), each as the top 16 bits of its
+// order-preserving score key (0 marks a key past the end of the row).
+constexpr int kSampleSub = 512;
+constexpr int kSubKeys = kSampleTiles * kSampleSub;
 // Sampled tile j of ns among nt (ns <= nt): the middle tile of the j-th of ns
 // equal strata of the row (all tiles when ns == nt).  Centres, not starts: in
 // a row whose score scale drifts along the sequence, a stratum's first tile
@@ -128,7 +132,7 @@ struct ScanSession {
   float *logits;
   int64_t ld;
   // fused scan + top-k (unused by plain scans)
-  float *sample;          // [hq][kSampleKeys] logits of the sampled tiles
+  uint16_t *sample;       // [rows][kSubKeys] the sampled tiles' subsample (16-bit keys)
   const uint32_t *thr;    // [rows] threshold keys of the session's output rows
   uint64_t *cand;         // [rows][kFusedCap] candidate segments
   uint32_t *seg_cnt;      // [rows][kMaxSeg] candidates found by each block
@@ -184,6 +188,7 @@ int32_t launch_read_prefixes(const uint32_t *planes, int64_t n, int32_t hkv,
 // ---- top-k ------------------------------------------------------------------
 struct TopkSession {
   const float *scores;  // first input row of the session
+  const uint16_t *sub;  // threshold stage: first subsample row (kSubKeys apart), else null
   int64_t n, ld;
   int32_t *idx;
   float *vals;

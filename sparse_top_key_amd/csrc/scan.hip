@@ -59,7 +59,7 @@ struct ScanSess {
   // tiles this launch visits (all, or the sampled ones) and real tiles
   int32_t nvtiles, ntiles;
   // fused scan + top-k
-  float *sample;
+  uint16_t *sample;
   const uint32_t *thr;
   uint64_t *cand;
   uint32_t *seg_cnt;
@@ -1294,19 +1294,39 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
           }
         }
       } else if constexpr (MODE == kScanSample) {
-        // sampled tile vt lands at vt * 2048 of the head's sample row; keys
-        // past n read as -inf
-        if (hh < GH) {
-          float *op = S.sample + (int64_t)(head_base + hh) * kSampleKeys +
-                      (int64_t)vt * kMTileKeys + 256 * wave + 4 * nn;
+        // The threshold's subsample: this wave's keys 256 wave + 4 nn + e
+        // (beta = 0: the first 64 of every 256 keys) as the top 16 bits of
+        // their score keys, 0 past the end of the row, at vt * 512 of the
+        // output row's subsample.  A group call (a row per kv head) stores
+        // the group score: its heads' logits added in fp64 in head order,
+        // rounded once (lanes of head 0 gather the others by lane-row swaps).
+        const int G = a.out_group;
+        float sv[4] = {s[0], s[1], s[2], s[3]};
+        int orow = head_base + hh;
+        bool writer = hh < GH;
+        if (G > 1) {
 #pragma unroll
-          for (int beta = 0; beta < 4; ++beta) {
-            float v4[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              v4[e] = kb + 64 * beta + e < n ? s[4 * beta + e] : -INFINITY;
-            *reinterpret_cast<float4 *>(op + 64 * beta) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t v = __float_as_uint(s[e]);
+            const auto p16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+            const auto p32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+            const auto p48 = __builtin_amdgcn_permlane16_swap(p32[1], p32[1], false, false);
+            double acc = (double)s[e];
+            if (G > 1) acc = __dadd_rn(acc, (double)__uint_as_float(p16[1]));
+            if (G > 2) acc = __dadd_rn(acc, (double)__uint_as_float(p32[1]));
+            if (G > 3) acc = __dadd_rn(acc, (double)__uint_as_float(p48[1]));
+            sv[e] = (float)acc;
           }
+          orow = g;
+          writer = hh == 0;
+        }
+        if (writer) {
+          uint32_t k16[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) k16[e] = kb + e < n ? to_key(sv[e]) >> 16 : 0u;
+          uint16_t *op = S.sample + (int64_t)orow * kSubKeys + (int64_t)vt * kSampleSub +
+                         64 * wave + 4 * nn;
+          *reinterpret_cast<uint2 *>(op) = make_uint2(k16[0] | (k16[1] << 16), k16[2] | (k16[3] << 16));
         }
       } else {
         // candidates: score key at or above the row's threshold

@@ -4,10 +4,13 @@
 // written when a row needs them.
 //
 // With device-resident planes the steps are:
-//   1. sample scan    logits of 32 tiles (65536 keys), the middle tiles of 32
-//                     equal strata of each row (one round of scan blocks),
-//   2. threshold      per output row, a key T expected to leave ~2.5k of the
-//                     row's n scores at or above it (all keys when n <= 8192),
+//   1. sample scan    scores of 32 tiles, the middle tiles of 32 equal strata
+//                     of each row (one round of scan blocks); a quarter of
+//                     each tile's keys (the first 64 of every 256) is stored
+//                     as 16-bit score keys, per output row,
+//   2. threshold      per output row, from those 16384 keys, a key T
+//                     expected to leave ~2.5k of the row's n scores at or
+//                     above it (all keys when n <= 8192),
 //   3. candidate scan every key scored again, the (score key, index) words of
 //                     those >= T stored in the row's candidate segment of the
 //                     scan block (block-local counters in LDS); a block that
@@ -38,17 +41,11 @@ namespace {
 int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
 int64_t ld_pad(int64_t n) { return std::max<int64_t>(64, (n + 63) / 64 * 64); }
 
-// Valid keys among the sampled tiles of a row of n keys (only the last
-// sampled tile can be partial).
-int64_t sampled_keys(int64_t n) {
+// Subsample entries of a row of n keys: kSampleSub per sampled tile (those
+// past the end of the row hold key 0, which the threshold stage skips).
+int64_t subsample_entries(int64_t n) {
   const int64_t nt = (n + kBlockKeys - 1) / kBlockKeys;
-  const int64_t ns = std::min<int64_t>(nt, kSampleTiles);
-  int64_t m = 0;
-  for (int64_t j = 0; j < ns; ++j) {
-    const int64_t t = sample_tile(j, ns, nt);
-    m += std::min<int64_t>(kBlockKeys, n - t * kBlockKeys);
-  }
-  return m;
+  return std::min<int64_t>(nt, kSampleTiles) * kSampleSub;
 }
 
 struct Layout {
@@ -70,7 +67,7 @@ Layout layout(const int64_t *n, int32_t n_sess, int32_t hkv, int32_t hq, int32_t
   L.fcand_off = L.seg_off + align256(L.out_rows * kMaxSeg * (int64_t)sizeof(uint32_t));
   L.sample_off = L.fcand_off + align256(L.out_rows * kFusedCap * (int64_t)sizeof(uint64_t));
   L.table_off =
-      L.sample_off + align256((int64_t)n_sess * hq * kSampleKeys * (int64_t)sizeof(float));
+      L.sample_off + align256((int64_t)n_sess * hq * kSubKeys * (int64_t)sizeof(uint16_t));
   L.table_bytes = align256(scan_table_bytes(hkv, hq));
   L.logits_off = L.table_off + (int64_t)n_sess * L.table_bytes;
   int64_t logits = 0;
@@ -112,7 +109,7 @@ int32_t launch_scan_topk(const ScanSession *in, int32_t *const *idx, float *cons
     c.ld = ld_pad(in[j].n);
     c.logits = reinterpret_cast<float *>(w + logits_off);
     logits_off += align256((int64_t)hq * c.ld * (int64_t)sizeof(float));
-    c.sample = reinterpret_cast<float *>(w + L.sample_off) + (int64_t)j * hq * kSampleKeys;
+    c.sample = reinterpret_cast<uint16_t *>(w + L.sample_off) + (int64_t)j * hq * kSubKeys;
     const int64_t row0 = (int64_t)j * rows_per_sess;
     c.thr = tw.thr + row0;
     c.cand = tw.fcand + row0 * kFusedCap;
@@ -125,9 +122,9 @@ int32_t launch_scan_topk(const ScanSession *in, int32_t *const *idx, float *cons
     c.redo = nullptr;
     c.table = reinterpret_cast<uint8_t *>(w + L.table_off + (int64_t)j * L.table_bytes);
     c.table_mode = kTableRead;
-    fin[j] = TopkSession{c.logits, in[j].n, c.ld, idx[j], vals[j], in[j].n, 0};
-    thr[j] = TopkSession{c.sample, sampled_keys(in[j].n), kSampleKeys, idx[j], vals[j],
-                         in[j].n, 0};
+    fin[j] = TopkSession{c.logits, nullptr, in[j].n, c.ld, idx[j], vals[j], in[j].n, 0};
+    thr[j] = TopkSession{nullptr, c.sample, subsample_entries(in[j].n), kSubKeys, idx[j],
+                         vals[j], in[j].n, 0};
     if (in[j].n > 0) {
       // the recompute scan's view (the other scans clear these)
       sc[m] = c;
@@ -164,7 +161,8 @@ int32_t launch_scan_topk(const ScanSession *in, int32_t *const *idx, float *cons
   }
   if (m > 0)
     if (int32_t rc = launch_scan(first, m, hkv, hq, s, kScanSample)) return rc;
-  if (int32_t rc = launch_topk(thr, n_sess, rows_per_sess, group, k, tw, s, kTopkThreshold,
+  // (each output row has its own subsample row, group scores included)
+  if (int32_t rc = launch_topk(thr, n_sess, rows_per_sess, 1, k, tw, s, kTopkThreshold,
                                rows_per_kv, hkv))
     return rc;
   int32_t nseg[FATHOM_MAX_SESSIONS];

@@ -44,6 +44,7 @@ constexpr int kStage = 2048;           // candidates staged per compact block
 
 struct TopkSess {
   const float *scores;
+  const uint16_t *sub;  // threshold stage: subsample rows (kSubKeys apart)
   int64_t n, ld;
   int32_t *idx;
   float *vals;
@@ -112,13 +113,16 @@ __device__ void block_minmax_count(uint32_t &mx, uint32_t &mn, int &cnt, uint32_
 }
 
 // One block per output row: from a sample of the row (runs of 64 scores
-// spread evenly, about 16K in all; or all of a row of sampled logits), a
-// threshold key T expected to leave about 2.5k of the row's n_full scores at
-// or above it: the sample's keys are histogrammed on the 11 bits below their
-// common prefix and T is the lower edge of the bin holding the rs-th
-// largest.  Rows of at most 8192 scores take T = 0 (all).
+// spread evenly, about 16K in all; or, in the fused threshold stage, the
+// row's subsample of 16-bit keys), a threshold key T expected to leave about
+// 2.5k of the row's n_full scores at or above it: the sample's keys are
+// histogrammed on the 11 bits below their common prefix and T is the lower
+// edge of the bin holding the rs-th largest.  Rows of at most 8192 scores
+// take T = 0 (all).
 __global__ __launch_bounds__(kBig) void topk_sample_kernel(TopkArgs a) {
   constexpr int kPer = (kSampleTarget + kRun + kBig - 1) / kBig;
+  constexpr int kSubPer = kSubKeys / kBig;  // subsample keys per thread (fused stage)
+  static_assert(kSubPer <= kPer && kSubPer == 16 && kSampleSub % kSubPer == 0, "subsample");
   __shared__ int hist[kHistBins];
   __shared__ int wave_tot[16];
   __shared__ int s_res[2];
@@ -143,6 +147,7 @@ __global__ __launch_bounds__(kBig) void topk_sample_kernel(TopkArgs a) {
     if (threadIdx.x == 0) a.thr[o] = 0;
     return;
   }
+  const bool tiled = a.stage == kTopkThreshold;
   int64_t stride = (n * kRun + kSampleTarget - 1) / kSampleTarget;
   stride = (stride + kRun - 1) / kRun * kRun;
   if (stride < kRun) stride = kRun;
@@ -152,13 +157,34 @@ __global__ __launch_bounds__(kBig) void topk_sample_kernel(TopkArgs a) {
   // keys after)
   uint32_t v[kPer];
   uint32_t okm = 0;
+  if (tiled) {
+    // 16 consecutive subsample keys per thread, all of one sampled tile (two
+    // 16-byte loads); key 0 marks an entry past the end of the row, and the
+    // key's low 16 bits are taken as 0 (T is then the lower edge of its
+    // 16-bit bin)
+    const uint16_t *sub = R.s->sub + (int64_t)(o % a.rows_per_sess) * kSubKeys;
+    const int e0 = threadIdx.x * kSubPer;
+    uint4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
+    if (e0 < n) {
+      w0 = reinterpret_cast<const uint4 *>(sub + e0)[0];
+      w1 = reinterpret_cast<const uint4 *>(sub + e0)[1];
+    }
+    const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int e = threadIdx.x + j * kBig;
-    const int64_t pos = (int64_t)(e / kRun) * stride + (e % kRun);
-    okm |= (uint32_t)(e < m && pos < n) << j;
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t k16 = j < kSubPer ? (wd[j >> 1] >> (16 * (j & 1))) & 0xFFFFu : 0u;
+      v[j] = k16 << 16;
+      okm |= (uint32_t)(k16 != 0u) << j;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = threadIdx.x + j * kBig;
+      const int64_t pos = (int64_t)(e / kRun) * stride + (e % kRun);
+      okm |= (uint32_t)(e < m && pos < n) << j;
+    }
   }
-  if (a.group == 1) {
+  if (!tiled && a.group == 1) {
     // unconditional loads (positions out of the sample read element 0, which
     // exists: n >= 1 here), so that all of them are issued before any wait
     float f[kPer];
@@ -170,7 +196,7 @@ __global__ __launch_bounds__(kBig) void topk_sample_kernel(TopkArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < kPer; ++j) v[j] = ((okm >> j) & 1) ? to_key(f[j]) : 0u;
-  } else {
+  } else if (!tiled) {
     // group scores: rows added in fp64 in row order (as group_score does);
     // per row and half of the samples, every load is issued before the adds
     constexpr int kHalf = (kPer + 1) / 2;
@@ -197,20 +223,17 @@ __global__ __launch_bounds__(kBig) void topk_sample_kernel(TopkArgs a) {
         if (j0 + u < kPer) v[j0 + u] = ((okm >> (j0 + u)) & 1) ? to_key((float)acc[u]) : 0u;
     }
   }
-  // Fused threshold stage: the sample row holds whole 2048-key tiles, the
-  // middle tiles of equal stretches of the row.  A tile whose count of
-  // sampled keys at or above T exceeds 4x its larger neighbour's (+8) holds a
+  // Fused threshold stage: the subsample row holds 512 keys of each sampled
+  // tile, the middle tiles of equal stretches of the row.  A tile whose count
+  // of sampled keys at or above T exceeds 4x its larger neighbour's (+8) holds a
   // local cluster of top keys (one stretch of the row, not a drift, which
   // changes smoothly from tile to tile): the sample then overstates the
   // cluster by the sampling ratio and T lands above almost all other keys.
   // Such tiles are left out and T is taken again from the others (the
   // cluster's own keys are still candidates: they lie above it).
-  const bool tiled = a.stage == kTopkThreshold;
-  const int ntl = tiled ? (int)((n + kBlockKeys - 1) / kBlockKeys) : 0;
+  const int ntl = tiled ? (int)(n / kSampleSub) : 0;
+  const int my_tile = threadIdx.x * kSubPer / kSampleSub;  // (tiled)
   uint32_t prefix = 0;
-  // (sample rows of the threshold stage hold at most kSampleKeys keys, so
-  // positions fit 32 bits)
-  const int stride32 = (int)stride;
 #pragma unroll 1
   for (int round = 0; round < 2; ++round) {
     uint32_t mx = 0, mn = 0xFFFFFFFFu;
@@ -259,12 +282,10 @@ __global__ __launch_bounds__(kBig) void topk_sample_kernel(TopkArgs a) {
     // per-tile counts of sampled keys at or above T, then the outliers
     for (int t = threadIdx.x; t < ntl; t += kBig) tile_cnt[t] = 0;
     __syncthreads();
+    int mine = 0;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      if (((okm >> j) & 1) && v[j] >= prefix) {
-        const int e = threadIdx.x + j * kBig;
-        atomicAdd(&tile_cnt[((e / kRun) * stride32 + (e % kRun)) / kBlockKeys], 1);
-      }
+    for (int j = 0; j < kPer; ++j) mine += ((okm >> j) & 1) && v[j] >= prefix;
+    if (mine) atomicAdd(&tile_cnt[my_tile], mine);
     __syncthreads();
     if (threadIdx.x == 0) s_res[0] = 0;
     __syncthreads();
@@ -276,12 +297,7 @@ __global__ __launch_bounds__(kBig) void topk_sample_kernel(TopkArgs a) {
     }
     __syncthreads();
     if (!s_res[0]) break;  // block-uniform
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int e = threadIdx.x + j * kBig;
-      if (((okm >> j) & 1) && tile_out[((e / kRun) * stride32 + (e % kRun)) / kBlockKeys])
-        okm &= ~(1u << j);
-    }
+    if (tile_out[my_tile]) okm = 0;
     __syncthreads();
   }
   if (threadIdx.x == 0) a.thr[o] = prefix;
@@ -584,6 +600,7 @@ int32_t launch_topk(const TopkSession *sess, int32_t n_sess, int32_t rows_per_se
     for (int j = 0; j < cnt; ++j) {
       const TopkSession &in = sess[s0 + j];
       a.s[j].scores = in.scores;
+      a.s[j].sub = in.sub;
       a.s[j].n = in.n;
       a.s[j].ld = in.ld;
       a.s[j].idx = in.idx;
