@@ -1419,7 +1419,7 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
         __threadfence();
         constexpr int kSortWords = kBuckCap + 2 * FATHOM_MAX_K;
         uint8_t *lds = reinterpret_cast<uint8_t *>(&s_codes[0][0]);
-        static_assert((kSortWords + kBuckCap) * 8 + (2 * kHistBins + 8) * 4 + 16 * 8 + 16 * 4 +
+        static_assert((kSortWords + kBuckCap) * 8 + 16 * 8 + (2 * kRankBins + 8) * 4 + 16 * 4 +
                               16 <= sizeof(s_codes),
                       "selection scratch");
         SelScratch X;
@@ -1427,8 +1427,8 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
         X.win = X.s + kSortWords;
         X.red = X.win + kBuckCap;
         X.hist = reinterpret_cast<int *>(X.red + 16);
-        X.above = X.hist + kHistBins;
-        X.wave_tot = X.above + kHistBins + 4;
+        X.above = X.hist + kRankBins;
+        X.wave_tot = X.above + kRankBins + 4;
         X.s_res = X.wave_tot + 16;
         X.s_count = X.s_res + 2;
         const int k = a.out_k, G = a.out_group;

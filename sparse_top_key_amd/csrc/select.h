@@ -14,7 +14,8 @@ namespace fathom {
 namespace {
 
 constexpr int kSelThreads = 1024;  // threads of a selecting block
-constexpr int kHistBins = 2048;
+constexpr int kHistBins = 2048;    // radix digits of 11 bits
+constexpr int kRankBins = 4096;    // ranking buckets (12 bits)
 
 __device__ __forceinline__ float group_score(const float *__restrict__ row, int64_t ld,
                                              int group, int64_t i) {
@@ -192,81 +193,105 @@ __device__ uint64_t block_or64(uint64_t v, uint64_t *red) {
 }
 
 // Writes the kk largest of the unique words src[0..m) (1 <= kk <= m) to
-// output row (idx, vals) in descending order, without sorting: words are bucketed by
-// the 11 bits below their common prefix, the buckets at or above the one
-// holding the kk-th word are laid out in descending bucket order, and each
-// word's rank is its bucket's offset plus the number of larger words in its
-// bucket.  Buckets grow when the candidates span two binades, so that the
+// output row (idx, vals) in descending order, without sorting: words are
+// bucketed by the 12 bits below their common prefix, the buckets at or above
+// the one holding the kk-th word are laid out in descending bucket order, and
+// each word's rank is its bucket's offset plus the number of larger words in
+// its bucket.  Buckets grow when the candidates span two binades, so that the
 // binning window starts in the exponent bits; a word's rank is a loop over
 // its bucket, and even at 512 words that costs far less than a sort.  One
 // larger bucket strictly above the kk-th word's (top keys clustered in a
 // narrow score range: all of its words are winners, at most kk of them) is
-// ranked on its own, binned again below its own words' common prefix, in
-// `sort_buf` (2 * FATHOM_MAX_K words; sorted there when that fails).
-// Returns false, having written nothing, for anything else (the caller then
-// selects and sorts).  buck holds kBuckCap words, above
-// kHistBins + 1 ints.
+// ranked on its own, binned again on the 11 bits below its own words' common
+// prefix, in `sort_buf` (2 * FATHOM_MAX_K words; sorted there when that
+// fails).  Returns false, having written nothing, for anything else (the
+// caller then selects and sorts).  buck holds kBuckCap words, hist
+// kRankBins ints, above kRankBins + 1.
+// Words of b[b0 .. e) larger than w: 8 independent LDS reads per step (the
+// last step's indices clamped to e - 1 and masked), so that a long bucket
+// costs its reads' issue time rather than one LDS latency per word.
+__device__ __forceinline__ int count_larger(const uint64_t *b, int b0, int e, uint64_t w) {
+  int r = 0;
+  for (int q = b0; q < e; q += 8) {
+    uint64_t x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = b[q + u < e ? q + u : e - 1];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) r += (q + u < e) & (x[u] > w);
+  }
+  return r;
+}
+
 constexpr int kMaxBucket = 512;
 constexpr int kBuckCap = FATHOM_MAX_K + kMaxBucket;
 
-__device__ __forceinline__ bool bucket_rank_out(const uint64_t *src, int m, int kk, uint64_t *buck, int *hist,
-                                int *above, int *wave_tot, int *s_res, uint64_t *red,
-                                int32_t *idx, float *vals, int k, uint64_t *sort_buf) {
+__device__ __forceinline__ bool bucket_rank_out(const uint64_t *src, int m, int kk, uint64_t *buck,
+                                                int *hist, int *above,
+                                                int *wave_tot, int *s_res, uint64_t *red,
+                                                int32_t *idx, float *vals, int k,
+                                                uint64_t *sort_buf) {
   const int t = threadIdx.x;
   uint64_t diff = 0;
   const uint64_t w0 = src[0];
   for (int j = t; j < m; j += kSelThreads) diff |= src[j] ^ w0;
   diff = block_or64(diff, red);
   const int hb = diff ? 63 - __clzll(diff) : 0;  // highest bit in which words differ
-  const int sh = hb > 10 ? hb - 10 : 0;
-  for (int b = t; b < kHistBins; b += kSelThreads) hist[b] = 0;
+  const int sh = hb > 11 ? hb - 11 : 0;
+  for (int b = t; b < kRankBins; b += kSelThreads) hist[b] = 0;
   if (t == 0) s_res[1] = 0;
   __syncthreads();
-  for (int j = t; j < m; j += kSelThreads) atomicAdd(&hist[(int)((src[j] >> sh) & (kHistBins - 1))], 1);
+  for (int j = t; j < m; j += kSelThreads)
+    atomicAdd(&hist[(int)((src[j] >> sh) & (kRankBins - 1))], 1);
   __syncthreads();
-  // above[d] = words in digits > d; thread t owns digits 2047-2t and 2046-2t
-  const int d1 = kHistBins - 1 - 2 * t, d2 = d1 - 1;
-  const int c1 = hist[d1], c2 = hist[d2];
-  const int incl = block_inclusive_scan(c1 + c2, wave_tot);
-  const int excl = incl - c1 - c2;
-  above[d1] = excl;
-  above[d2] = excl + c1;
-  if (excl < kk && kk <= excl + c1) s_res[0] = d1;
-  if (excl + c1 < kk && kk <= incl) s_res[0] = d2;
+  // above[d] = words in digits > d; thread t owns digits kRankBins-1-4t ..
+  // kRankBins-4-4t (descending)
+  constexpr int kOwn = kRankBins / kSelThreads;
+  int cown[kOwn], sum = 0;
+#pragma unroll
+  for (int i = 0; i < kOwn; ++i) {
+    cown[i] = hist[kRankBins - 1 - kOwn * t - i];
+    sum += cown[i];
+  }
+  const int incl = block_inclusive_scan(sum, wave_tot);
+  int run = incl - sum;
+#pragma unroll
+  for (int i = 0; i < kOwn; ++i) {
+    const int d = kRankBins - 1 - kOwn * t - i;
+    above[d] = run;
+    if (run < kk && kk <= run + cown[i]) s_res[0] = d;
+    run += cown[i];
+  }
   __syncthreads();
   const int db = s_res[0];  // digit holding the kk-th word
   // big buckets at or above db: one strictly above db (all of its words are
-  // winners) is sorted on its own; the kk-th word's bucket must stay small
-  const int big1 = d1 >= db && c1 > kMaxBucket, big2 = d2 >= db && c2 > kMaxBucket;
-  if ((big1 && d1 == db) || (big2 && d2 == db)) atomicAdd(&s_res[1], 2);
-  if (big1) {
-    atomicAdd(&s_res[1], 1);
-    above[kHistBins] = d1;
-  }
-  if (big2) {
-    atomicAdd(&s_res[1], 1);
-    above[kHistBins] = d2;
+  // winners) is ranked on its own; the kk-th word's bucket must stay small
+#pragma unroll
+  for (int i = 0; i < kOwn; ++i) {
+    const int d = kRankBins - 1 - kOwn * t - i;
+    if (d >= db && cown[i] > kMaxBucket) {
+      atomicAdd(&s_res[1], d == db ? 2 : 1);
+      if (d != db) above[kRankBins] = d;
+    }
   }
   __syncthreads();
   const int nbig = s_res[1];
   if (nbig > 1) return false;
-  const int dbig = nbig == 1 ? above[kHistBins] : -1;
+  const int dbig = nbig == 1 ? above[kRankBins] : -1;
   // bucket order; above[d] becomes the end of bucket d
   for (int j = t; j < m; j += kSelThreads) {
     const uint64_t w = src[j];
-    const int d = (int)((w >> sh) & (kHistBins - 1));
+    const int d = (int)((w >> sh) & (kRankBins - 1));
     if (d >= db) buck[atomicAdd(&above[d], 1)] = w;
   }
   __syncthreads();
   const int total = above[db];
   for (int p = t; p < total; p += kSelThreads) {
     const uint64_t w = buck[p];
-    const int d = (int)((w >> sh) & (kHistBins - 1));
+    const int d = (int)((w >> sh) & (kRankBins - 1));
     if (d == dbig) continue;
     const int c = hist[d];
     const int b0 = above[d] - c;
-    int rank = b0;
-    for (int q = b0; q < b0 + c; ++q) rank += buck[q] > w;
+    const int rank = b0 + count_larger(buck, b0, b0 + c, w);
     if (rank < kk) {
       idx[rank] = (int32_t)(~(uint32_t)w);
       vals[rank] = from_key((uint32_t)(w >> 32));
@@ -278,6 +303,7 @@ __device__ __forceinline__ bool bucket_rank_out(const uint64_t *src, int m, int 
     // bins as above; should a bin still exceed the cap, the bucket is sorted.
     const int c = hist[dbig], b0 = above[dbig] - c;
     const uint64_t *bw = buck + b0;
+    const int d1 = kHistBins - 1 - 2 * t, d2 = d1 - 1;  // digits of thread t (descending)
     uint64_t dif = 0;
     for (int j = t; j < c; j += kSelThreads) dif |= bw[j] ^ bw[0];
     dif = block_or64(dif, red);  // (its barrier also ends the ranking loop above)
@@ -305,8 +331,7 @@ __device__ __forceinline__ bool bucket_rank_out(const uint64_t *src, int m, int 
         const int d = (int)((w >> sh2) & (kHistBins - 1));
         const int cnt = hist[d];
         const int s0 = above[d] - cnt;
-        int rank = b0 + s0;
-        for (int q = s0; q < s0 + cnt; ++q) rank += sort_buf[q] > w;
+        const int rank = b0 + s0 + count_larger(sort_buf, s0, s0 + cnt, w);
         idx[rank] = (int32_t)(~(uint32_t)w);
         vals[rank] = from_key((uint32_t)(w >> 32));
       }
@@ -331,8 +356,8 @@ __device__ __forceinline__ bool bucket_rank_out(const uint64_t *src, int m, int 
 struct SelScratch {
   uint64_t *win;   // kBuckCap words: the winners
   uint64_t *s;     // kBuckCap + 2 * FATHOM_MAX_K words: buckets, sort space
-  int *hist;       // kHistBins
-  int *above;      // kHistBins + 1
+  int *hist;       // kRankBins
+  int *above;      // kRankBins + 1
   int *wave_tot;   // 16
   int *s_res;      // 2
   int *s_count;    // 1

@@ -433,9 +433,9 @@ __device__ uint64_t select_kth(const uint64_t *s, int m, int kk, int *hist, int 
 // ---- exact selection of each row's top k -------------------------------------
 __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
   __shared__ uint64_t s[kCandCap];
-  __shared__ uint64_t win[FATHOM_MAX_K + kMaxBucket];
-  __shared__ int hist[kHistBins];
-  __shared__ int above[kHistBins + 1];  // [kHistBins]: the big bucket (bucket_rank_out)
+  __shared__ uint64_t win[kBuckCap];
+  __shared__ int hist[kRankBins];
+  __shared__ int above[kRankBins + 1];  // [kRankBins]: the big bucket (bucket_rank_out)
   __shared__ uint64_t red[kBig / 64];
   __shared__ int wave_tot[16];
   __shared__ int s_res[2];
