@@ -793,6 +793,13 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
     }
   }
   SlotRecord *rec = S.table ? reinterpret_cast<SlotRecord *>(S.table) + bw.rec : nullptr;
+  // candidate modes: the rows' threshold keys, loaded now so that their
+  // latency overlaps the set-up's own loads
+  uint32_t thr_key = 0;
+  if constexpr (MODE == kScanCand)
+    if (tid < GH) thr_key = S.thr[head_base + tid];
+  if constexpr (MODE == kScanCandGroup)
+    if (tid < GH) thr_key = S.thr[g];
   if constexpr (BLK) {
     // Slot order (from an earlier scan of the call, or built with unit
     // weights), q and t of the block's heads, per-slot weights s_gq; then per
@@ -929,12 +936,11 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   if (tid < 4) s_ring[tid] = 0u;
   if (tid < GH) {
     s_segc[tid] = 0;
-    // thresholds are read here, before any plane load is in flight
     if constexpr (MODE == kScanCand) {
-      s_tf[tid] = key_threshold(S.thr[head_base + tid]);
+      s_tf[tid] = key_threshold(thr_key);
       if (!BLK) s_ht[tid] = hi_bound(s_tf[tid], s_C[tid], s_scale[tid]);
     }
-    if constexpr (MODE == kScanCandGroup) s_tf[tid] = key_threshold(S.thr[g]);
+    if constexpr (MODE == kScanCandGroup) s_tf[tid] = key_threshold(thr_key);
   }
   __syncthreads();  // the code table is free from here on
   if constexpr (BLK && MODE == kScanCand) {

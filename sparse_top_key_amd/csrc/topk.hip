@@ -449,11 +449,29 @@ __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
   const int k = a.k;
   const int kk = (int)(n < k ? n : k);
   uint32_t cnt = 0;
+  // fused final: kBig / nseg threads per candidate segment; each loads the
+  // first kSpec of its words before the segment counts are known, so that
+  // both reads share one memory latency (words past a segment's count are
+  // dropped; segments hold at most seg_cap words)
+  constexpr int kSpec = 8;
+  const int nseg = S.nseg, seg_cap = kFusedCap / (nseg > 0 ? nseg : 1);
+  const int tps = kBig / (nseg > 0 ? nseg : 1);
+  const int sg = threadIdx.x / tps, sub = threadIdx.x % tps;
+  const uint64_t *fseg = a.stage == kTopkFusedFinal
+                             ? a.fcand + (int64_t)o * kFusedCap + (int64_t)sg * seg_cap
+                             : nullptr;
+  uint64_t spec[kSpec];
+  if (a.stage == kTopkFusedFinal && sg < nseg) {
+#pragma unroll
+    for (int u = 0; u < kSpec; ++u) {
+      const int i = sub + u * tps;
+      spec[u] = fseg[i < seg_cap ? i : seg_cap - 1];
+    }
+  }
   if (a.stage == kTopkFusedFinal) {
     // the row's candidates: min(c, seg_cap) words in each scan block's
     // segment, the rest of each block's count in the row's overflow list
     // (which then holds sum_b max(0, c_b - seg_cap) words)
-    const int nseg = S.nseg, seg_cap = kFusedCap / (nseg > 0 ? nseg : 1);
     const int c = threadIdx.x < nseg ? (int)a.seg_cnt[(int64_t)o * kMaxSeg + threadIdx.x] : 0;
     const int kept = c < seg_cap ? c : seg_cap;
     const int incl = block_inclusive_scan(kept, wave_tot);
@@ -489,17 +507,18 @@ __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
   if (threadIdx.x == 0) s_count = 0;
   const int m = (int)cnt;
   if (a.stage == kTopkFusedFinal) {
-    const int nseg = S.nseg, seg_cap = kFusedCap / (nseg > 0 ? nseg : 1);
-    const uint64_t *fc = a.fcand + (int64_t)o * kFusedCap;
-    // kBig / nseg threads per segment; each has 8 loads in flight before it
-    // stores (segments hold at most seg_cap words: no overflow here)
-    const int tps = kBig / (nseg > 0 ? nseg : 1);
-    const int sg = threadIdx.x / tps, sub = threadIdx.x % tps;
+    // the words loaded ahead, then the rest of each segment with 8 loads in
+    // flight per thread before it stores
     if (sg < nseg) {
       const int c = (sg + 1 < nseg ? s_off[sg + 1] : s_off[kMaxSeg]) - s_off[sg];
-      const uint64_t *src = fc + (int64_t)sg * seg_cap;
+      const uint64_t *src = fseg;
       uint64_t *dst = s + s_off[sg];
-      for (int b0 = sub; b0 < c; b0 += 8 * tps) {
+#pragma unroll
+      for (int u = 0; u < kSpec; ++u) {
+        const int i = sub + u * tps;
+        if (i < c) dst[i] = spec[u];
+      }
+      for (int b0 = sub + kSpec * tps; b0 < c; b0 += 8 * tps) {
         uint64_t v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
