@@ -252,15 +252,40 @@ __global__ __launch_bounds__(kBig) void topk_sample_kernel(TopkArgs a) {
     // rank of the threshold inside the sample: ~2.5k of n_full at or above T
     int64_t rs = ((int64_t)5 * a.k * cnt + 2 * n_full - 1) / (2 * n_full);
     rs = rs < 1 ? 1 : (rs > cnt ? cnt : rs);
-    // Two 11-bit digits below the bits all sampled keys share: T = the rs-th
-    // largest key with its bits below the second digit cleared.
+    int rem = (int)rs;
+    // Fused stage with a positive largest score (in binade e >= 2): the keys
+    // from the start of binade e - 2 up span three binades, which bins of
+    // 2^14 key units split into 1536 (finer than the 16-bit keys); when at
+    // least rs keys lie there, one histogram of them gives T = the rs-th
+    // largest key (far fewer LDS atomics than a pass over every key).
+    bool found = false;
+    if (tiled && mx >= 0x80000000u + (2u << 23)) {
+      const uint32_t lo = 0x80000000u | ((((mx >> 23) & 0xFFu) - 2u) << 23);
+      constexpr int kWinShift = 14;
+      for (int b = threadIdx.x; b < kHistBins; b += kBig) hist[b] = 0;
+      if (threadIdx.x == 0) s_res[0] = -1;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (((okm >> j) & 1) && v[j] >= lo) atomicAdd(&hist[(v[j] - lo) >> kWinShift], 1);
+      __syncthreads();
+      int above = 0;
+      const int d = find_digit(hist, kHistBins, rem, &above, wave_tot, s_res);
+      if (d >= 0) {  // block-uniform
+        prefix = lo + ((uint32_t)d << kWinShift);
+        found = true;
+      }
+    }
+    // Otherwise two 11-bit digits below the bits all sampled keys share: T =
+    // the rs-th largest key with its bits below the second digit cleared.
     const uint32_t diff = mx ^ mn;
     const int hb = diff ? 31 - __clz(diff) : 0;  // highest bit in which keys differ
     int sh = hb > 10 ? hb - 10 : 0;
-    prefix = sh + 11 >= 32 ? 0u : (mx >> (sh + 11)) << (sh + 11);
+    if (!found) {
+      prefix = sh + 11 >= 32 ? 0u : (mx >> (sh + 11)) << (sh + 11);
+    }
     uint32_t pmask = sh + 11 >= 32 ? 0u : ~((1u << (sh + 11)) - 1u);
-    int rem = (int)rs;
-    for (int pass = 0; pass < 2; ++pass) {
+    for (int pass = 0; pass < 2 && !found; ++pass) {
       for (int b = threadIdx.x; b < kHistBins; b += kBig) hist[b] = 0;
       __syncthreads();
 #pragma unroll
