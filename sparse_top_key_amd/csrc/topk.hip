@@ -4,29 +4,31 @@
 //
 // Three launches per call (MI355X-first design; the pages give none):
 //   topk_sample   one block per output row: reads a sample of the row
-//                 (64-score runs spread evenly, about 16K scores; or a row of
-//                 sampled logits) and picks a threshold key T expected to
-//                 leave about 2.5k scores at or above it, by two 11-bit
-//                 radix digits below the bits all sampled keys share.  Rows
-//                 of at most 8192 scores take T = 0 (all).
+//                 (64-score runs spread evenly, about 16K scores; or, in the
+//                 fused call, the row's subsample of 16-bit score keys) and
+//                 picks a threshold key T expected to leave about 2.5k
+//                 scores at or above it, by two 11-bit radix digits below
+//                 the bits all sampled keys share (fused call: one histogram
+//                 of the three binades below the largest key when that
+//                 suffices).  Rows of at most 8192 scores take T = 0 (all).
 //   topk_compact  the whole grid streams every row once and appends the
 //                 (score key, index) words >= T to the row's candidate list
 //                 (staged in LDS, one global atomic per block).
 //   topk_final    one block per output row: if the candidates hold at least k
 //                 and at most 8192 words they contain the exact top k (every
 //                 score >= T is present).  The winners are ranked without a
-//                 sort: words are bucketed on the 11 bits below their common
+//                 sort: words are bucketed on the 12 bits below their common
 //                 prefix and each takes its bucket's offset plus the number of
 //                 larger words in its bucket (a radix select plus a merge sort
 //                 of in-wave bitonic runs when a bucket is too large).  Other
 //                 rows are recomputed exactly: a 3-pass radix select over the
 //                 whole row finds the k-th key, an index-ordered pass gathers
 //                 the winners (ties at the k-th key by lowest index), and the
-//                 same ranking orders them.
+//                 same ranking orders them (select.h holds these steps).
 // The fused scan + top-k call reuses these kernels in stages: the threshold
-// from sampled logits, a final over the candidate segments the scan wrote
-// (rows out of range are flagged instead of recomputed), and an exact final
-// for the flagged rows once their logits exist.
+// from the sampled subsample, and a final over the candidate segments the
+// scan wrote (rows out of range are flagged instead of recomputed; the
+// recompute scan ranks them once their logits exist).
 // Scores map to order-preserving uint32 keys after adding +0 (so -0 ranks as
 // +0); a GQA group's score is its rows' fp32 scores added in fp64, in row
 // order, rounded once.
