@@ -209,3 +209,31 @@ def test_scan_topk_against_oracle(F, orc):
     ridx, _ = orc.topk(ref_logits.astype(np.float32), k, 1)
     A = logit_scale(q.cpu().numpy(), p.lo.cpu().numpy(), p.hi.cpu().numpy(), hq // hkv)
     assert_topk_tie_tolerant(idx.cpu().numpy(), ridx, ref_logits, A, n, k)
+
+
+def test_scan_topk_threshold_negative_and_outlier_rows(F):
+    """The fused threshold's two ways to its key: one histogram of the three
+    binades below the largest sampled score (a positive one with enough keys
+    there), else two radix digits over every sampled key.  Rows whose scores
+    are all negative, and rows whose largest sampled score is one outlier far
+    above the rest, take the second way; both still equal scan then top-k."""
+    n, hkv, hq = 200000, 2, 8
+    keys = synth.keys(540, 0, n, hkv, 128, torch.float16, 0, device=dev())
+    keys[:, :, 0] = 8.0                      # a constant channel every head weighs
+    ntiles = (n + 2047) // 2048
+    t0 = ntiles // 64 * 2048                 # first sampled tile (the middle of stretch 0)
+    keys[t0, 1, 1] = 2000.0                  # one key of kv head 1, in the subsample
+    p = F.pack(keys)
+    q = synth.queries(540, 0, hq, 128, device=dev())
+    q[:hq // 2, 0] = -20.0                   # kv head 0: every score negative
+    q[hq // 2:, 0] = 0.0
+    q[hq // 2:, 1] = 10.0                    # kv head 1: one outlier key on top
+    plan = F.plan(q, p.sigma2, 92)
+    torch.cuda.synchronize()
+    print("scan_topk negative rows and outlier rows", flush=True)
+    for group in (1, 4):
+        got, ref, logits = both(F, p, n, q, plan, 512, group)
+        assert_same(got, ref)
+        if group == 1:
+            assert float(logits[: hq // 2, :n].max()) < 0.0
+            assert int(got[0][hq // 2, 0]) == t0
