@@ -290,16 +290,18 @@ int32_t fathom_topk_batched(const fathom_session *sessions, int32_t n_sessions,
  * not written unless needed.  With planes in device memory, n <= 2^25 and
  * group 1 or hq/hkv (<= 4), the call scores a sample of 32 key tiles (2048
  * keys each, the middle tiles of 32 equal stretches of the row; all tiles of
- * shorter rows), sets a per-row threshold from it, scans again keeping only the
- * (score, index) pairs at or above the threshold, and ranks those; a row
- * whose candidate count falls outside [k, 8192] is recomputed from full
- * logits in the workspace.  Otherwise (pinned host planes, other groups,
- * longer sessions) the full logits go to the workspace and are ranked there.
+ * shorter rows), sets a per-row threshold from a quarter of their keys,
+ * scans again keeping only the (score, index) pairs at or above the
+ * threshold, and ranks those; a row whose candidate count falls outside
+ * [k, 8192] is recomputed from full logits in the workspace (by the last
+ * block of its kv head's recompute scan).  Otherwise (pinned host planes,
+ * other groups, longer sessions) the full logits go to the workspace and are
+ * ranked there.
  *
  * Arguments as for fathom_scan and fathom_topk (group over the hq rows);
  * idx, vals  device outputs int32/fp32[hq/group][k].
  * ws         device workspace of fathom_scan_topk_workspace_bytes bytes.
- * Enqueues 6 or fewer kernel launches; nothing synchronises.               */
+ * Enqueues 5 or fewer kernel launches; nothing synchronises.               */
 int64_t fathom_scan_topk_workspace_bytes(const int64_t *n_host, int32_t n_sessions,
                                          int32_t hkv, int32_t hq, int32_t group,
                                          int32_t k);
