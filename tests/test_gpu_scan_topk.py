@@ -196,6 +196,36 @@ def test_scan_topk_batched_sessions(F):
                 assert torch.equal(s.idx, r[0]) and torch.equal(s.vals, r[1])
 
 
+def test_scan_topk_batched_recompute_in_some_sessions(F):
+    """Sessions of one batched call where some rows are recomputed (budget 0:
+    every logit of a row ties, so its candidates overflow) beside sessions
+    answered from their candidates: each recompute scan block counts into
+    its own session's per-kv-head counters and the last one ranks that
+    session's flagged rows; every session equals scan then top-k."""
+    lengths = [60000, 90000, 40000, 70000]
+    budgets = [0, 92, 92, 0]
+    hkv, hq, k = 8, 32, 512
+    for group in (1, 4):
+        sess, refs = [], []
+        for s, (n, B) in enumerate(zip(lengths, budgets)):
+            print(f"batched recompute session n={n} B={B} group={group}", flush=True)
+            keys = synth.keys(560, 0, n, hkv, 128, torch.float16, 4, device=dev(), session=s)
+            q = synth.queries(560, 0, hq, 128, device=dev(), session=s)
+            p = F.pack(keys)
+            plan = F.plan(q, p.sigma2, B)
+            idx = torch.empty((hq // group, k), dtype=torch.int32, device=dev())
+            vals = torch.empty((hq // group, k), device=dev())
+            sess.append(F.Session(p.planes, p.lo, p.hi, n, q, plan, None, idx, vals))
+            refs.append(F.topk(F.scan(p.planes, p.lo, p.hi, n, q, plan), k, group))
+        for rep in range(2):   # the counters must be back at a clean state for the second call
+            for s in sess:
+                s.idx.fill_(-7)
+            F.scan_topk_batched(sess, k, group)
+            torch.cuda.synchronize()
+            for s, r in zip(sess, refs):
+                assert torch.equal(s.idx, r[0]) and torch.equal(s.vals, r[1])
+
+
 def test_scan_topk_against_oracle(F, orc):
     """Oracle logits (fp64 from the planes) ranked by the oracle's top-k: the
     fused result agrees up to ties within the logit tolerance."""
