@@ -138,11 +138,15 @@ struct ScanSession {
   uint32_t *seg_cnt;      // [rows][kMaxSeg] candidates found by each block
   uint32_t *ovf_cnt;      // [rows] (stride kCntStride): candidates past their segment
   uint64_t *ovf;          // [rows][kCandCap] ... stored here, in arrival order
-  const uint32_t *redo;   // [hkv]: recompute only the kv heads flagged here
-  // recompute scan of a fused call: the last block of each flagged (kv head,
-  // head chunk) ranks the chunk's flagged rows into the outputs
+  // recompute scan of a fused call (redo_done set): only (kv head, head
+  // chunk)s with a row whose candidate count (over its nseg segments) lies
+  // outside [out_k, kCandCap] are scanned, and the last block of each ranks
+  // those rows into the outputs
   uint32_t *redo_done;    // [hkv][head chunks] blocks finished (zeroed earlier in the call)
-  const uint32_t *row_flag;  // [rows] rows to recompute
+  int32_t nseg;           // candidate segments per row (the candidate scan's blocks per kv head)
+  // set by the fused final's blocks (launch_scan's final_rows) for such rows
+  uint32_t *redo;         // [hkv] kv heads with a recomputed row
+  uint32_t *row_flag;     // [rows] recomputed rows
   int32_t *out_idx;       // [rows][out_k]
   float *out_vals;        // [rows][out_k]
   int32_t out_k;
@@ -160,8 +164,8 @@ inline int64_t sess_words(const ScanSession &s) { return s.W > 0 ? s.W : plane_w
 enum ScanTable { kTableNone = 0, kTableWrite = 1, kTableRead = 2 };
 // Bytes of the slot tables of one session (all its kv heads and head chunks).
 int64_t scan_table_bytes(int32_t hkv, int32_t hq);
-// What a scan writes: every logit (into logits; only the flagged kv heads when
-// redo is set), the logits of the sampled tiles (into sample), or the
+// What a scan writes: every logit (into logits; in a fused call's recompute
+// scan, only those of kv heads with a row to recompute), the logits of the sampled tiles (into sample), or the
 // (score key, index) words of the keys whose score key reaches the row's
 // threshold (into cand): kScanCand with one output row per query head,
 // kScanCandGroup with one row per kv head scored by the sum of its
@@ -170,10 +174,14 @@ enum ScanMode { kScanLogits = 0, kScanSample = 1, kScanCand = 2, kScanCandGroup 
 // nseg_out (candidate mode, optional): per session, the blocks per kv head,
 // i.e. the candidate segments of each row.  one_block_per_head: a single
 // block per (session, kv head) takes all its tiles (a grid of hkv blocks per
-// session, for recomputations that are usually skipped).
+// session, for recomputations that are usually skipped).  final_rows
+// (recompute scan of a fused call): the launch also runs the fused final of
+// the sessions' final_rows output rows each, one block per row ahead of the
+// scan blocks (the sessions' cand, seg_cnt, ovf, out_* and flags).
 int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv,
                     int32_t hq, hipStream_t s, int32_t mode = kScanLogits,
-                    int32_t *nseg_out = nullptr, bool one_block_per_head = false);
+                    int32_t *nseg_out = nullptr, bool one_block_per_head = false,
+                    int32_t final_rows = 0);
 // Whether launch_scan can run the sample and candidate modes on these
 // sessions (planes in device memory, at most 2^25 keys each).
 bool scan_can_fuse(const ScanSession *sess, int32_t n_sess);

@@ -65,14 +65,16 @@ struct ScanSess {
   uint32_t *seg_cnt;
   uint32_t *ovf_cnt;
   uint64_t *ovf;
-  const uint32_t *redo;
   // recompute scan of a fused call (null otherwise): blocks finished per
-  // (kv head, head chunk), the rows to recompute and the outputs
+  // (kv head, head chunk), the outputs, and the records of recomputed rows
+  // and kv heads that the final blocks set
   uint32_t *redo_done;
-  const uint32_t *row_flag;
+  uint32_t *redo;
+  uint32_t *row_flag;
   int32_t *out_idx;
   float *out_vals;
   int32_t seg_cap;         // candidate words per (row, block) segment
+  int32_t nseg;            // recompute scan: the candidate scan's segments per row
   uint8_t *table;          // slot records of the session, or null
   int32_t table_mode;      // ScanTable
   int64_t rs;              // 0: lo, hi [hkv][d]; > 0: per 2048-key block, [hkv][rs][d]
@@ -82,6 +84,9 @@ struct ScanArgs {
   ScanSess s[kSessPerLaunch];
   int32_t n_sess, hkv, group, head0;
   int32_t out_k, out_group;  // recompute scan: outputs per row; query heads per row
+  // recompute scan: blocks 0 .. n_final-1 are the fused final's, one per
+  // output row (final_rows per session) ahead of the scan blocks
+  int32_t n_final, final_rows;
 };
 static_assert(sizeof(ScanArgs) <= 4096, "kernel arguments");
 
@@ -731,6 +736,35 @@ struct alignas(16) ItemLimbs {
   int32_t limbs[64][4];  // A operands of the item's pass (layout of s_limbs)
 };
 
+// A fused final block inside the recompute scan's launch: output row
+// blockIdx.x (final_rows per session) is ranked from its candidates, with
+// the code buffers as its LDS; a row whose candidate count is out of range
+// is recorded (row and kv head) and left to the scan blocks of its kv head,
+// which apply the same rule to the same counts.
+__device__ __forceinline__ void scan_final_block(KScanArgs &a, uint8_t *lds) {
+  const int o = blockIdx.x;
+  const int si = o / a.final_rows, r = o % a.final_rows;
+  KScanSess &S = a.s[si];
+  FinalScratch X;
+  X.s = reinterpret_cast<uint64_t *>(lds);
+  X.win = X.s + kCandCap;
+  X.red = X.win + kBuckCap;
+  X.hist = reinterpret_cast<int *>(X.red + kSelThreads / 64);
+  X.above = X.hist + kRankBins;
+  X.wave_tot = X.above + kRankBins + 1;
+  X.s_res = X.wave_tot + 16;
+  X.s_count = X.s_res + 2;
+  X.s_off = X.s_count + 1;
+  const int k = a.out_k;
+  if (!fused_final_row(S.cand + (int64_t)r * kFusedCap, S.seg_cnt + (int64_t)r * kMaxSeg,
+                       S.nseg, S.ovf + (int64_t)r * kCandCap, S.n, k,
+                       S.out_idx + (int64_t)r * k, S.out_vals + (int64_t)r * k, X) &&
+      threadIdx.x == 0) {
+    S.row_flag[r] = 1;
+    S.redo[r / max(1, a.final_rows / a.hkv)] = 1;
+  }
+}
+
 // META: the sessions carry a side stream (its bytes are prefetched with the
 // planes, which costs registers the other variants do not spend).
 template <int GH, int MODE, bool META, bool BLK>
@@ -738,11 +772,11 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   const BlockWork bw = block_work(a);
   KScanSess &S = *bw.S;
   const int g = bw.g, head_base = bw.head_base;
-  if (MODE == kScanLogits && S.redo && S.redo[g] == 0) return;  // kv head not flagged
   const int64_t n = S.n;
   const int64_t W = S.W;
   __shared__ __align__(16) uint32_t s_codes[2][kPassGroups * kGroupPitch + 4];  // the ring's buffers
   static_assert(sizeof(MfmaSetup<GH>) <= sizeof(s_codes[0]), "set-up overlay");
+  static_assert(kFinalScratchBytes <= sizeof(s_codes), "fused final overlay");
   __shared__ __align__(16) int32_t s_limbs[kMaxPasses][64][4];
   __shared__ __align__(16) int16_t s_desc[kMaxSlots];
   __shared__ float s_scale[kMaxGH], s_C[kMaxGH];
@@ -752,6 +786,7 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   __shared__ int s_ht[kMaxGH];         // integer pre-check bounds (see hi_bound)
   __shared__ int s_nslots;
   __shared__ int s_last;  // recompute scan: this block finished its (kv head, chunk) last
+  __shared__ uint32_t s_redo_rows;  // recompute scan: bit j = row j of the block's rows
   // code-buffer ring: [0..1] groups stored in buffer 0/1 (one count per
   // producer task), [2..3] releases (one per consumer wave and item); counts
   // only grow during a launch
@@ -769,6 +804,33 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   float(*const s_gq)[kMaxGH] = reinterpret_cast<float(*)[kMaxGH]>(&s_limbs[0][0][0]);
   static_assert(sizeof(float) * kMaxSlots * kMaxGH <= sizeof(s_limbs), "slot weights overlay");
   const int tid = threadIdx.x;
+  if constexpr (MODE == kScanLogits) {
+    // recompute scan of a fused call: the fused final's blocks come first
+    KScanArgs &ka = *(KScanArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+    if ((int)blockIdx.x < ka.n_final) {
+      scan_final_block(ka, reinterpret_cast<uint8_t *>(&s_codes[0][0]));
+      return;
+    }
+    if (S.redo_done) {
+      // The block's rows whose candidate count lies outside [k, kCandCap]
+      // (the rows the final blocks leave unanswered, by the same rule); a
+      // block with none returns at once.
+      if (tid == 0) s_redo_rows = 0;
+      __syncthreads();
+      const int wv = tid >> 6, ln = tid & 63;
+      if (wv < (a.out_group > 1 ? 1 : GH) && n > kCandCap) {
+        const int row = a.out_group > 1 ? g : head_base + wv;
+        uint32_t c = 0;
+        for (int b = ln; b < S.nseg; b += 64) c += S.seg_cnt[(int64_t)row * kMaxSeg + b];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) c += (uint32_t)__shfl_xor((int)c, off);
+        if (ln == 0 && (c < (uint32_t)a.out_k || c > (uint32_t)kCandCap))
+          atomicOr(&s_redo_rows, 1u << wv);
+      }
+      __syncthreads();
+      if (s_redo_rows == 0) return;
+    }
+  }
   // Work items = (tile, pass) of this block's tiles in order; item i goes
   // through code buffer i % 2.  Visited tile v of this block: all tiles, or
   // (sample mode) nvtiles tiles spread evenly over the ntiles real ones.
@@ -1440,13 +1502,13 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
         const int k = a.out_k, G = a.out_group;
         if (G > 1) {
           // one row per kv head, scored by the sum of its G query heads
-          if (S.row_flag[g])
+          if (s_redo_rows & 1u)
             exact_row_topk(S.logits + (int64_t)head_base * S.ld, S.ld, G, n, k,
                            S.out_idx + (int64_t)g * k, S.out_vals + (int64_t)g * k, X);
         } else {
           for (int j = 0; j < GH; ++j) {
             const int o = head_base + j;
-            if (S.row_flag[o])
+            if ((s_redo_rows >> j) & 1u)
               exact_row_topk(S.logits + (int64_t)o * S.ld, S.ld, 1, n, k,
                              S.out_idx + (int64_t)o * k, S.out_vals + (int64_t)o * k, X);
           }
@@ -1611,7 +1673,8 @@ bool scan_can_fuse(const ScanSession *sess, int32_t n_sess) {
 }
 
 int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_t hq,
-                    hipStream_t s, int32_t mode, int32_t *nseg_out, bool one_block_per_head) {
+                    hipStream_t s, int32_t mode, int32_t *nseg_out, bool one_block_per_head,
+                    int32_t final_rows) {
   const int32_t group = hq / hkv;
   const int ncu = device_cus();
   bool any_host = false;
@@ -1628,7 +1691,7 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_
     return FATHOM_ERR_UNSUPPORTED;
   }
   for (int32_t j = 0; j < n_sess; ++j)
-    if (fp32_path && sess[j].redo) {
+    if (fp32_path && (sess[j].redo_done || final_rows > 0)) {
       set_error("scan: recompute flags need the matrix-core scan");
       return FATHOM_ERR_UNSUPPORTED;
     }
@@ -1690,7 +1753,10 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_
       a.head0 = head0;
       a.out_k = sess[s0].out_k;
       a.out_group = sess[s0].out_group > 0 ? sess[s0].out_group : 1;
-      int32_t blocks = 0;
+      // the fused final's blocks (first launch of the sessions only)
+      a.final_rows = final_rows;
+      a.n_final = mode == kScanLogits && head0 == 0 ? cnt * final_rows : 0;
+      int32_t blocks = a.n_final;
       for (int j = 0; j < cnt; ++j) {
         const ScanSession &in = sess[s0 + j];
         ScanSess &o = a.s[j];
@@ -1714,8 +1780,9 @@ int32_t launch_scan(const ScanSession *sess, int32_t n_sess, int32_t hkv, int32_
         o.ovf_cnt = in.ovf_cnt;
         o.ovf = in.ovf;
         o.redo = in.redo;
-        o.redo_done = in.redo ? in.redo_done : nullptr;
+        o.redo_done = in.redo_done;
         o.row_flag = in.row_flag;
+        o.nseg = in.nseg;
         o.out_idx = in.out_idx;
         o.out_vals = in.out_vals;
         o.rs = in.rs;

@@ -19,14 +19,17 @@
 //                     overflow list (one global counter per row),
 //   4. final          the exact top k of each row whose candidate count lies
 //                     in [k, 8192], ranked and written; other rows flagged,
-//   5. redo scan      full logits of the flagged rows' kv heads, tiled like
-//                     any scan (blocks of unflagged kv heads return at once);
-//                     the last block of each flagged kv head to finish then
-//                     ranks the exact top k of its flagged rows.
+//   5. redo scan      full logits of the kv heads of rows whose count lies
+//                     outside that range, tiled like any scan (blocks of other
+//                     kv heads return at once); the last block of each such
+//                     kv head to finish then ranks the exact top k of those
+//                     rows.
+// Steps 4 and 5 share one launch (the final's blocks first) when every
+// session has keys: both read only the candidate counts and lists.
 // Every score >= T is a candidate, so a row with k..8192 candidates holds
 // its exact top k; step 5 covers every other row (a sample that misjudged
-// the row, or more than 8192 scores tied at the threshold) and costs one
-// early-exiting launch when no row is flagged.
+// the row, or more than 8192 scores tied at the threshold) and costs only
+// early-exiting blocks when there is none.
 //
 // Planes in pinned host memory, sessions above 2^25 keys, or groups other
 // than 1 and hq/hkv <= 4: the logits go to the workspace and fathom_topk's
@@ -171,6 +174,10 @@ int32_t launch_scan_topk(const ScanSession *in, int32_t *const *idx, float *cons
                                  nseg))
       return rc;
   for (int32_t j = 0, i = 0; j < n_sess; ++j) fin[j].nseg = in[j].n > 0 ? nseg[i++] : 0;
+  for (int32_t j = 0; j < m; ++j) sc[j].nseg = nseg[j];
+  // every session has keys: the final's blocks run in the recompute scan's
+  // launch (neither waits for the other)
+  if (m == n_sess) return launch_scan(sc, m, hkv, hq, s, kScanLogits, nullptr, false, rows_per_sess);
   if (int32_t rc = launch_topk(fin, n_sess, rows_per_sess, group, k, tw, s, kTopkFusedFinal,
                                rows_per_kv, hkv))
     return rc;

@@ -353,6 +353,38 @@ __device__ __forceinline__ bool bucket_rank_out(const uint64_t *src, int m, int 
 }
 
 // LDS the exact row selection works in.
+// Exact kk-th largest of the unique 64-bit words s[0..m) by 11-bit radix
+// passes from the top bit; stops early once a whole digit bin is taken.
+// Returns T such that exactly kk words are >= T.
+__device__ uint64_t select_kth(const uint64_t *s, int m, int kk, int *hist, int *wave_tot,
+                               int *s_res) {
+  uint64_t prefix = 0, pmask = 0;
+  int rem = kk;
+  int hi = 64;
+  while (hi > 0) {
+    const int bits = hi >= 11 ? 11 : hi;
+    const int sh = hi - bits;
+    const int nb = 1 << bits;
+    for (int b = threadIdx.x; b < kHistBins; b += kSelThreads) hist[b] = 0;
+    __syncthreads();
+    for (int j = threadIdx.x; j < m; j += kSelThreads) {
+      const uint64_t v = s[j];
+      if ((v & pmask) == prefix) atomicAdd(&hist[(int)((v >> sh) & (uint64_t)(nb - 1))], 1);
+    }
+    __syncthreads();
+    int above = 0;
+    const int d = find_digit(hist, nb, rem, &above, wave_tot, s_res);
+    const int in_bin = hist[d];
+    __syncthreads();
+    rem -= above;
+    prefix |= (uint64_t)d << sh;
+    pmask |= (uint64_t)(nb - 1) << sh;
+    hi = sh;
+    if (in_bin == rem) break;  // the whole bin is kept: T = prefix, low bits 0
+  }
+  return prefix;
+}
+
 struct SelScratch {
   uint64_t *win;   // kBuckCap words: the winners
   uint64_t *s;     // kBuckCap + 2 * FATHOM_MAX_K words: buckets, sort space
@@ -369,7 +401,7 @@ struct SelScratch {
 // row finds the kk-th key, an index-ordered pass gathers the winners (ties at
 // the kk-th key by lowest index), and they are ranked as above (sorted when
 // that fails).
-__device__ void exact_row_topk(const float *row, int64_t ld, int group, int64_t n, int k,
+__device__ __forceinline__ void exact_row_topk(const float *row, int64_t ld, int group, int64_t n, int k,
                                int32_t *idx, float *vals, const SelScratch &X) {
   const int kk = (int)(n < k ? n : k);
   __syncthreads();  // the scratch may still be read by an earlier call
@@ -428,6 +460,112 @@ __device__ void exact_row_topk(const float *row, int64_t ld, int group, int64_t 
     return;
   const uint64_t *sorted = sort_winners_desc(X.win, X.s, kk);
   write_out(idx, vals, k, sorted, kk);
+}
+
+// LDS of the fused final (fused_final_row): the row's candidate words (the
+// ranking also uses their upper part as sort space), the winners, ranking
+// bins, reduction slots and the segments' offsets.
+struct FinalScratch {
+  uint64_t *s;      // kCandCap
+  uint64_t *win;    // kBuckCap
+  int *hist;        // kRankBins
+  int *above;       // kRankBins + 1
+  uint64_t *red;    // kSelThreads / 64
+  int *wave_tot;    // 16
+  int *s_res;       // 2
+  int *s_count;     // 1
+  int *s_off;       // kMaxSeg + 1
+};
+constexpr int64_t kFinalScratchBytes =
+    (int64_t)(kCandCap + kBuckCap + kSelThreads / 64) * 8 +
+    (int64_t)(2 * kRankBins + 1 + 16 + 2 + 1 + kMaxSeg + 1) * 4;
+
+// Exact top k of one output row of a fused scan + top-k call, from the
+// candidate words the candidate scan stored: min(c_b, seg_cap) words in each
+// of the nseg segments of frow (seg_cap = kFusedCap / nseg words apart), the
+// rest of every block's count c_b in the overflow list ov.  Every score at
+// or above the row's threshold is a candidate, so when the row holds k to
+// kCandCap of them (or n <= kCandCap: all keys) they contain its top k,
+// which are ranked and written; otherwise nothing is written and false is
+// returned (the row needs its full logits).
+__device__ __forceinline__ bool fused_final_row(const uint64_t *frow, const uint32_t *segc, int nseg,
+                                                const uint64_t *ov, int64_t n, int k, int32_t *idx,
+                                                float *vals, const FinalScratch &X) {
+  const int kk = (int)(n < k ? n : k);
+  // kSelThreads / nseg threads per segment; each loads the first kSpec of its
+  // words before the segment counts are known, so that both reads share one
+  // memory latency (words past a segment's count are dropped; segments hold
+  // at most seg_cap words)
+  constexpr int kSpec = 8;
+  const int seg_cap = kFusedCap / (nseg > 0 ? nseg : 1);
+  const int tps = kSelThreads / (nseg > 0 ? nseg : 1);
+  const int sg = threadIdx.x / tps, sub = threadIdx.x % tps;
+  const uint64_t *fseg = frow + (int64_t)sg * seg_cap;
+  uint64_t spec[kSpec];
+  if (sg < nseg) {
+#pragma unroll
+    for (int u = 0; u < kSpec; ++u) {
+      const int i = sub + u * tps;
+      spec[u] = fseg[i < seg_cap ? i : seg_cap - 1];
+    }
+  }
+  // the row's count: min(c, seg_cap) words in each segment, the rest of each
+  // block's count in the overflow list
+  const int c = threadIdx.x < nseg ? (int)segc[threadIdx.x] : 0;
+  const int kept = c < seg_cap ? c : seg_cap;
+  const int incl = block_inclusive_scan(kept, X.wave_tot);
+  X.s_off[threadIdx.x] = incl - kept;
+  if (threadIdx.x == kSelThreads - 1) X.s_off[kMaxSeg] = incl;
+  if (threadIdx.x == 0) X.s_res[1] = 0;
+  __syncthreads();
+  if (c > 0) atomicAdd(&X.s_res[1], c);
+  __syncthreads();
+  const uint32_t cnt = (uint32_t)X.s_res[1];
+  __syncthreads();
+  if (!(n <= kCandCap || (cnt >= (uint32_t)k && cnt <= (uint32_t)kCandCap))) return false;
+  if (threadIdx.x == 0) *X.s_count = 0;
+  const int m = (int)cnt;
+  // the words loaded ahead, then the rest of each segment with 8 loads in
+  // flight per thread before it stores
+  if (sg < nseg) {
+    const int cs = (sg + 1 < nseg ? X.s_off[sg + 1] : X.s_off[kMaxSeg]) - X.s_off[sg];
+    uint64_t *dst = X.s + X.s_off[sg];
+#pragma unroll
+    for (int u = 0; u < kSpec; ++u) {
+      const int i = sub + u * tps;
+      if (i < cs) dst[i] = spec[u];
+    }
+    for (int b0 = sub + kSpec * tps; b0 < cs; b0 += 8 * tps) {
+      uint64_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = b0 + u * tps;
+        v[u] = fseg[i < cs ? i : cs - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = b0 + u * tps;
+        if (i < cs) dst[i] = v[u];
+      }
+    }
+  }
+  // then the overflow list (m <= kCandCap words in all)
+  const int stored = X.s_off[kMaxSeg];
+  for (int j = threadIdx.x; j < m - stored; j += kSelThreads) X.s[stored + j] = ov[j];
+  __syncthreads();
+  if (kk > 0 && bucket_rank_out(X.s, m, kk, X.win, X.hist, X.above, X.wave_tot, X.s_res, X.red,
+                                idx, vals, k, X.s + kBuckCap))
+    return true;
+  if (kk > 0) {
+    const uint64_t T = m > kk ? select_kth(X.s, m, kk, X.hist, X.wave_tot, X.s_res) : 0ull;
+    for (int j = threadIdx.x; j < m; j += kSelThreads)
+      if (X.s[j] >= T) X.win[atomicAdd(X.s_count, 1)] = X.s[j];
+  }
+  __syncthreads();
+  // win[0..kk) holds the winners
+  const uint64_t *sorted = sort_winners_desc(X.win, X.s, kk);
+  write_out(idx, vals, k, sorted, kk);
+  return true;
 }
 
 }  // namespace

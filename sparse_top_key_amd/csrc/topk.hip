@@ -424,39 +424,6 @@ __global__ __launch_bounds__(kCompactThreads) void topk_compact_kernel(TopkArgs 
     if (b + j < (uint32_t)kCandCap) cand[b + j] = stage[j];
 }
 
-// Exact kk-th largest of the unique 64-bit words s[0..m) by 11-bit radix
-// passes from the top bit; stops early once a whole digit bin is taken.
-// Returns T such that exactly kk words are >= T.
-__device__ uint64_t select_kth(const uint64_t *s, int m, int kk, int *hist, int *wave_tot,
-                               int *s_res) {
-  uint64_t prefix = 0, pmask = 0;
-  int rem = kk;
-  int hi = 64;
-  while (hi > 0) {
-    const int bits = hi >= 11 ? 11 : hi;
-    const int sh = hi - bits;
-    const int nb = 1 << bits;
-    for (int b = threadIdx.x; b < kHistBins; b += kBig) hist[b] = 0;
-    __syncthreads();
-    for (int j = threadIdx.x; j < m; j += kBig) {
-      const uint64_t v = s[j];
-      if ((v & pmask) == prefix) atomicAdd(&hist[(int)((v >> sh) & (uint64_t)(nb - 1))], 1);
-    }
-    __syncthreads();
-    int above = 0;
-    const int d = find_digit(hist, nb, rem, &above, wave_tot, s_res);
-    const int in_bin = hist[d];
-    __syncthreads();
-    rem -= above;
-    prefix |= (uint64_t)d << sh;
-    pmask |= (uint64_t)(nb - 1) << sh;
-    hi = sh;
-    if (in_bin == rem) break;  // the whole bin is kept: T = prefix, low bits 0
-  }
-  return prefix;
-}
-
-
 // ---- exact selection of each row's top k -------------------------------------
 __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
   __shared__ uint64_t s[kCandCap];
@@ -475,57 +442,23 @@ __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
   const int64_t n = S.n, ld = S.ld;
   const int k = a.k;
   const int kk = (int)(n < k ? n : k);
-  uint32_t cnt = 0;
-  // fused final: kBig / nseg threads per candidate segment; each loads the
-  // first kSpec of its words before the segment counts are known, so that
-  // both reads share one memory latency (words past a segment's count are
-  // dropped; segments hold at most seg_cap words)
-  constexpr int kSpec = 8;
-  const int nseg = S.nseg, seg_cap = kFusedCap / (nseg > 0 ? nseg : 1);
-  const int tps = kBig / (nseg > 0 ? nseg : 1);
-  const int sg = threadIdx.x / tps, sub = threadIdx.x % tps;
-  const uint64_t *fseg = a.stage == kTopkFusedFinal
-                             ? a.fcand + (int64_t)o * kFusedCap + (int64_t)sg * seg_cap
-                             : nullptr;
-  uint64_t spec[kSpec];
-  if (a.stage == kTopkFusedFinal && sg < nseg) {
-#pragma unroll
-    for (int u = 0; u < kSpec; ++u) {
-      const int i = sub + u * tps;
-      spec[u] = fseg[i < seg_cap ? i : seg_cap - 1];
-    }
-  }
-  if (a.stage == kTopkFusedFinal) {
-    // the row's candidates: min(c, seg_cap) words in each scan block's
-    // segment, the rest of each block's count in the row's overflow list
-    // (which then holds sum_b max(0, c_b - seg_cap) words)
-    const int c = threadIdx.x < nseg ? (int)a.seg_cnt[(int64_t)o * kMaxSeg + threadIdx.x] : 0;
-    const int kept = c < seg_cap ? c : seg_cap;
-    const int incl = block_inclusive_scan(kept, wave_tot);
-    s_off[threadIdx.x] = incl - kept;
-    if (threadIdx.x == kBig - 1) s_off[kMaxSeg] = incl;
-    if (threadIdx.x == 0) s_res[1] = 0;
-    __syncthreads();
-    if (c > 0) atomicAdd(&s_res[1], c);
-    __syncthreads();
-    cnt = (uint32_t)s_res[1];
-    __syncthreads();
-  } else {
-    cnt = a.cnt[(int64_t)o * kCntStride];
-  }
-  const bool fast = (n <= kCandCap) || (cnt >= (uint32_t)k && cnt <= (uint32_t)kCandCap);
   int32_t *idx = S.idx + (int64_t)r * k;
   float *vals = S.vals + (int64_t)r * k;
-  if (!fast) {
-    if (a.stage == kTopkFusedFinal) {
-      // too few or too many candidates: the row is recomputed from full
-      // logits (by the last block of the recompute scan of its kv head)
-      if (threadIdx.x == 0) {
-        a.flag[o] = 1;
-        a.redo[(o / a.rows_per_sess) * a.hkv + r / a.rows_per_kv] = 1;
-      }
-      return;
+  if (a.stage == kTopkFusedFinal) {
+    // too few or too many candidates: the row is flagged and recomputed from
+    // full logits (by the last block of the recompute scan of its kv head)
+    const FinalScratch X{s, win, hist, above, red, wave_tot, s_res, &s_count, s_off};
+    if (!fused_final_row(a.fcand + (int64_t)o * kFusedCap, a.seg_cnt + (int64_t)o * kMaxSeg,
+                         S.nseg, a.cand + (int64_t)o * kCandCap, n, k, idx, vals, X) &&
+        threadIdx.x == 0) {
+      a.flag[o] = 1;
+      a.redo[(o / a.rows_per_sess) * a.hkv + r / a.rows_per_kv] = 1;
     }
+    return;
+  }
+  const uint32_t cnt = a.cnt[(int64_t)o * kCntStride];
+  const bool fast = (n <= kCandCap) || (cnt >= (uint32_t)k && cnt <= (uint32_t)kCandCap);
+  if (!fast) {
     // exact recomputation over the whole row
     const SelScratch X{win, s, hist, above, wave_tot, s_res, &s_count, red};
     exact_row_topk(R.row, ld, a.group, n, k, idx, vals, X);
@@ -533,40 +466,8 @@ __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
   }
   if (threadIdx.x == 0) s_count = 0;
   const int m = (int)cnt;
-  if (a.stage == kTopkFusedFinal) {
-    // the words loaded ahead, then the rest of each segment with 8 loads in
-    // flight per thread before it stores
-    if (sg < nseg) {
-      const int c = (sg + 1 < nseg ? s_off[sg + 1] : s_off[kMaxSeg]) - s_off[sg];
-      const uint64_t *src = fseg;
-      uint64_t *dst = s + s_off[sg];
-#pragma unroll
-      for (int u = 0; u < kSpec; ++u) {
-        const int i = sub + u * tps;
-        if (i < c) dst[i] = spec[u];
-      }
-      for (int b0 = sub + kSpec * tps; b0 < c; b0 += 8 * tps) {
-        uint64_t v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int i = b0 + u * tps;
-          v[u] = src[i < c ? i : c - 1];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int i = b0 + u * tps;
-          if (i < c) dst[i] = v[u];
-        }
-      }
-    }
-    // then the overflow list (m <= kCandCap words in all)
-    const int stored = s_off[kMaxSeg];
-    const uint64_t *ov = a.cand + (int64_t)o * kCandCap;
-    for (int j = threadIdx.x; j < m - stored; j += kBig) s[stored + j] = ov[j];
-  } else {
-    const uint64_t *cand = a.cand + (int64_t)o * kCandCap;
-    for (int j = threadIdx.x; j < m; j += kBig) s[j] = cand[j];
-  }
+  const uint64_t *cand = a.cand + (int64_t)o * kCandCap;
+  for (int j = threadIdx.x; j < m; j += kBig) s[j] = cand[j];
   __syncthreads();
   if (kk > 0 && bucket_rank_out(s, m, kk, win, hist, above, wave_tot, s_res, red, idx, vals, k,
                                 s + kBuckCap))
