@@ -196,34 +196,51 @@ def test_scan_topk_batched_sessions(F):
                 assert torch.equal(s.idx, r[0]) and torch.equal(s.vals, r[1])
 
 
-def test_scan_topk_batched_recompute_in_some_sessions(F):
+@pytest.mark.parametrize("with_empty", [False, True])
+def test_scan_topk_batched_recompute_in_some_sessions(F, with_empty):
     """Sessions of one batched call where some rows are recomputed (budget 0:
     every logit of a row ties, so its candidates overflow) beside sessions
     answered from their candidates: each recompute scan block counts into
     its own session's per-kv-head counters and the last one ranks that
-    session's flagged rows; every session equals scan then top-k."""
+    session's rows; every session equals scan then top-k.  Without an empty
+    session the final's blocks share the recompute scan's launch; with one,
+    the final runs as a launch of its own before it."""
     lengths = [60000, 90000, 40000, 70000]
     budgets = [0, 92, 92, 0]
+    if with_empty:
+        lengths.insert(2, 0)
+        budgets.insert(2, 92)
     hkv, hq, k = 8, 32, 512
     for group in (1, 4):
         sess, refs = [], []
         for s, (n, B) in enumerate(zip(lengths, budgets)):
-            print(f"batched recompute session n={n} B={B} group={group}", flush=True)
-            keys = synth.keys(560, 0, n, hkv, 128, torch.float16, 4, device=dev(), session=s)
+            print(f"batched recompute session n={n} B={B} group={group} "
+                  f"with_empty={with_empty}", flush=True)
             q = synth.queries(560, 0, hq, 128, device=dev(), session=s)
-            p = F.pack(keys)
-            plan = F.plan(q, p.sigma2, B)
+            if n > 0:
+                keys = synth.keys(560, 0, n, hkv, 128, torch.float16, 4, device=dev(), session=s)
+                p = F.pack(keys)
+                planes, lo, hi, s2 = p.planes, p.lo, p.hi, p.sigma2
+            else:
+                planes = torch.zeros((hkv, 128, 4, 0), dtype=torch.int32, device=dev())
+                lo = torch.zeros((hkv, 128), device=dev())
+                hi = torch.ones((hkv, 128), device=dev())
+                s2 = torch.ones((hkv, 128), device=dev())
+            plan = F.plan(q, s2, B)
             idx = torch.empty((hq // group, k), dtype=torch.int32, device=dev())
             vals = torch.empty((hq // group, k), device=dev())
-            sess.append(F.Session(p.planes, p.lo, p.hi, n, q, plan, None, idx, vals))
-            refs.append(F.topk(F.scan(p.planes, p.lo, p.hi, n, q, plan), k, group))
+            sess.append(F.Session(planes, lo, hi, n, q, plan, None, idx, vals))
+            refs.append(F.topk(F.scan(planes, lo, hi, n, q, plan), k, group) if n > 0 else None)
         for rep in range(2):   # the counters must be back at a clean state for the second call
             for s in sess:
                 s.idx.fill_(-7)
             F.scan_topk_batched(sess, k, group)
             torch.cuda.synchronize()
             for s, r in zip(sess, refs):
-                assert torch.equal(s.idx, r[0]) and torch.equal(s.vals, r[1])
+                if r is None:
+                    assert torch.all(s.idx == -1) and torch.all(torch.isinf(s.vals))
+                else:
+                    assert torch.equal(s.idx, r[0]) and torch.equal(s.vals, r[1])
 
 
 def test_scan_topk_against_oracle(F, orc):
