@@ -757,8 +757,8 @@ __device__ __forceinline__ void scan_final_block(KScanArgs &a, uint8_t *lds) {
   X.s_off = X.s_count + 1;
   const int k = a.out_k;
   if (!fused_final_row(S.cand + (int64_t)r * kFusedCap, S.seg_cnt + (int64_t)r * kMaxSeg,
-                       S.nseg, S.ovf + (int64_t)r * kCandCap, S.n, k,
-                       S.out_idx + (int64_t)r * k, S.out_vals + (int64_t)r * k, X) &&
+                       S.nseg, S.ovf + (int64_t)r * kCandCap, S.ovf_cnt + (int64_t)r * kCntStride,
+                       S.n, k, S.out_idx + (int64_t)r * k, S.out_vals + (int64_t)r * k, X) &&
       threadIdx.x == 0) {
     S.row_flag[r] = 1;
     S.redo[r / max(1, a.final_rows / a.hkv)] = 1;

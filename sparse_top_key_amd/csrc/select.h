@@ -225,21 +225,28 @@ __device__ __forceinline__ int count_larger(const uint64_t *b, int b0, int e, ui
 constexpr int kMaxBucket = 512;
 constexpr int kBuckCap = FATHOM_MAX_K + kMaxBucket;
 
+// PRE: the caller passes the bits in which the words differ (pre_diff) and
+// has zeroed hist behind at least one block barrier.
+template <bool PRE = false>
 __device__ __forceinline__ bool bucket_rank_out(const uint64_t *src, int m, int kk, uint64_t *buck,
                                                 int *hist, int *above,
                                                 int *wave_tot, int *s_res, uint64_t *red,
                                                 int32_t *idx, float *vals, int k,
-                                                uint64_t *sort_buf) {
+                                                uint64_t *sort_buf, uint64_t pre_diff = 0) {
   const int t = threadIdx.x;
-  uint64_t diff = 0;
-  const uint64_t w0 = src[0];
-  for (int j = t; j < m; j += kSelThreads) diff |= src[j] ^ w0;
-  diff = block_or64(diff, red);
+  uint64_t diff = pre_diff;
+  if constexpr (!PRE) {
+    const uint64_t w0 = src[0];
+    for (int j = t; j < m; j += kSelThreads) diff |= src[j] ^ w0;
+    diff = block_or64(diff, red);
+  }
   const int hb = diff ? 63 - __clzll(diff) : 0;  // highest bit in which words differ
   const int sh = hb > 11 ? hb - 11 : 0;
-  for (int b = t; b < kRankBins; b += kSelThreads) hist[b] = 0;
   if (t == 0) s_res[1] = 0;
-  __syncthreads();
+  if constexpr (!PRE) {
+    for (int b = t; b < kRankBins; b += kSelThreads) hist[b] = 0;
+    __syncthreads();
+  }
   for (int j = t; j < m; j += kSelThreads)
     atomicAdd(&hist[(int)((src[j] >> sh) & (kRankBins - 1))], 1);
   __syncthreads();
@@ -483,15 +490,18 @@ constexpr int64_t kFinalScratchBytes =
 // Exact top k of one output row of a fused scan + top-k call, from the
 // candidate words the candidate scan stored: min(c_b, seg_cap) words in each
 // of the nseg segments of frow (seg_cap = kFusedCap / nseg words apart), the
-// rest of every block's count c_b in the overflow list ov.  Every score at
+// rest of every block's count c_b in the overflow list ov (*ov_cnt words).  Every score at
 // or above the row's threshold is a candidate, so when the row holds k to
 // kCandCap of them (or n <= kCandCap: all keys) they contain its top k,
 // which are ranked and written; otherwise nothing is written and false is
 // returned (the row needs its full logits).
 __device__ __forceinline__ bool fused_final_row(const uint64_t *frow, const uint32_t *segc, int nseg,
-                                                const uint64_t *ov, int64_t n, int k, int32_t *idx,
-                                                float *vals, const FinalScratch &X) {
+                                                const uint64_t *ov, const uint32_t *ov_cnt, int64_t n,
+                                                int k, int32_t *idx, float *vals,
+                                                const FinalScratch &X) {
   const int kk = (int)(n < k ? n : k);
+  // the ranking histogram is cleared while the loads below are in flight
+  for (int b = threadIdx.x; b < kRankBins; b += kSelThreads) X.hist[b] = 0;
   // kSelThreads / nseg threads per segment; each loads the first kSpec of its
   // words before the segment counts are known, so that both reads share one
   // memory latency (words past a segment's count are dropped; segments hold
@@ -509,31 +519,35 @@ __device__ __forceinline__ bool fused_final_row(const uint64_t *frow, const uint
       spec[u] = fseg[i < seg_cap ? i : seg_cap - 1];
     }
   }
-  // the row's count: min(c, seg_cap) words in each segment, the rest of each
-  // block's count in the overflow list
+  // the row's count: min(c, seg_cap) words in each segment, plus the
+  // overflow list's count (the rest of every block's count)
   const int c = threadIdx.x < nseg ? (int)segc[threadIdx.x] : 0;
+  const uint32_t ovf = *ov_cnt;
   const int kept = c < seg_cap ? c : seg_cap;
   const int incl = block_inclusive_scan(kept, X.wave_tot);
   X.s_off[threadIdx.x] = incl - kept;
   if (threadIdx.x == kSelThreads - 1) X.s_off[kMaxSeg] = incl;
-  if (threadIdx.x == 0) X.s_res[1] = 0;
-  __syncthreads();
-  if (c > 0) atomicAdd(&X.s_res[1], c);
-  __syncthreads();
-  const uint32_t cnt = (uint32_t)X.s_res[1];
-  __syncthreads();
-  if (!(n <= kCandCap || (cnt >= (uint32_t)k && cnt <= (uint32_t)kCandCap))) return false;
   if (threadIdx.x == 0) *X.s_count = 0;
+  __syncthreads();
+  const int stored = X.s_off[kMaxSeg];
+  const uint32_t cnt = (uint32_t)stored + ovf;
+  if (!(n <= kCandCap || (cnt >= (uint32_t)k && cnt <= (uint32_t)kCandCap))) return false;
   const int m = (int)cnt;
   // the words loaded ahead, then the rest of each segment with 8 loads in
-  // flight per thread before it stores
+  // flight per thread before it stores; each thread keeps the OR and the AND
+  // of the words it stores (the bits in which the row's words differ)
+  uint64_t w_or = 0, w_and = ~0ull;
   if (sg < nseg) {
     const int cs = (sg + 1 < nseg ? X.s_off[sg + 1] : X.s_off[kMaxSeg]) - X.s_off[sg];
     uint64_t *dst = X.s + X.s_off[sg];
 #pragma unroll
     for (int u = 0; u < kSpec; ++u) {
       const int i = sub + u * tps;
-      if (i < cs) dst[i] = spec[u];
+      if (i < cs) {
+        dst[i] = spec[u];
+        w_or |= spec[u];
+        w_and &= spec[u];
+      }
     }
     for (int b0 = sub + kSpec * tps; b0 < cs; b0 += 8 * tps) {
       uint64_t v[8];
@@ -545,16 +559,43 @@ __device__ __forceinline__ bool fused_final_row(const uint64_t *frow, const uint
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int i = b0 + u * tps;
-        if (i < cs) dst[i] = v[u];
+        if (i < cs) {
+          dst[i] = v[u];
+          w_or |= v[u];
+          w_and &= v[u];
+        }
       }
     }
   }
   // then the overflow list (m <= kCandCap words in all)
-  const int stored = X.s_off[kMaxSeg];
-  for (int j = threadIdx.x; j < m - stored; j += kSelThreads) X.s[stored + j] = ov[j];
+  for (int j = threadIdx.x; j < m - stored; j += kSelThreads) {
+    const uint64_t w = ov[j];
+    X.s[stored + j] = w;
+    w_or |= w;
+    w_and &= w;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    w_or |= shfl_xor64(w_or, off);
+    w_and &= shfl_xor64(w_and, off);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    X.red[threadIdx.x >> 6] = w_or;
+    X.win[threadIdx.x >> 6] = w_and;  // (win is free until the ranking places words)
+  }
   __syncthreads();
-  if (kk > 0 && bucket_rank_out(X.s, m, kk, X.win, X.hist, X.above, X.wave_tot, X.s_res, X.red,
-                                idx, vals, k, X.s + kBuckCap))
+  uint64_t diff = 0;
+  if (kk > 0) {
+    uint64_t o = 0, a = ~0ull;
+#pragma unroll
+    for (int w = 0; w < kSelThreads / 64; ++w) {
+      o |= X.red[w];
+      a &= X.win[w];
+    }
+    diff = o & ~a;
+  }
+  if (kk > 0 && bucket_rank_out<true>(X.s, m, kk, X.win, X.hist, X.above, X.wave_tot, X.s_res,
+                                      X.red, idx, vals, k, X.s + kBuckCap, diff))
     return true;
   if (kk > 0) {
     const uint64_t T = m > kk ? select_kth(X.s, m, kk, X.hist, X.wave_tot, X.s_res) : 0ull;

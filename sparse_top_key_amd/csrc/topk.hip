@@ -449,7 +449,8 @@ __global__ __launch_bounds__(kBig) void topk_final_kernel(TopkArgs a) {
     // full logits (by the last block of the recompute scan of its kv head)
     const FinalScratch X{s, win, hist, above, red, wave_tot, s_res, &s_count, s_off};
     if (!fused_final_row(a.fcand + (int64_t)o * kFusedCap, a.seg_cnt + (int64_t)o * kMaxSeg,
-                         S.nseg, a.cand + (int64_t)o * kCandCap, n, k, idx, vals, X) &&
+                         S.nseg, a.cand + (int64_t)o * kCandCap, a.cnt + (int64_t)o * kCntStride,
+                         n, k, idx, vals, X) &&
         threadIdx.x == 0) {
       a.flag[o] = 1;
       a.redo[(o / a.rows_per_sess) * a.hkv + r / a.rows_per_kv] = 1;
