@@ -670,6 +670,30 @@ __device__ __forceinline__ int hi_bound(float tf, float C, float scale) {
   return (int)h;
 }
 
+// Group pre-check of a one-pass group candidate scan (one output row per kv
+// head, scored by the fp32 logits of its GH query heads added in fp64 and
+// rounded once).  The group score is linear in the codes: with Gamma_slot =
+// sum_h gamma_h,slot in fixed point (scale 2^(EG-30), integer limbs as for
+// the heads), every head's exact value C_h + scale_h * X_h adds up to
+// sum_h C_h + gscale * XG plus at most gmarg, which covers the weights'
+// rounding to the two fixed points (15 codes x nslots x half a unit of
+// each) and every fp32 / fp64 rounding of the logits and of their sum
+// (2^-20 of sum_h B_h, B_h = |C_h| + 15 nslots max|gamma_h|, plus 8 units of
+// each scale).  A key whose group score reaches tf therefore has
+// gscale * XG >= tf - sum C_h - gmarg; its high limb pair hiG = XG >> 16
+// (|low part| < 2^26) is then at least group_bound.  Keys below it are no
+// candidates.
+__device__ __forceinline__ int group_bound(float tf, double sumC, double marg, float gscale) {
+  if (tf == -INFINITY) return INT_MIN;
+  if (tf == INFINITY) return INT_MAX;
+  double x = ((double)tf - sumC - marg) / (double)gscale;
+  x -= 134217728.0;  // 2^27: the low limb pair and slack
+  const double h = floor(x / 65536.0) - 1.0;
+  if (h <= (double)INT_MIN) return INT_MIN;
+  if (h >= (double)INT_MAX) return INT_MAX;
+  return (int)h;
+}
+
 // Where the candidate words of one lane go: positions pos, pos+1, ... of the
 // scan block's segment of output row `row`, and past its end the row's
 // overflow list, whose slots the lane takes with one global add for all of
@@ -716,10 +740,14 @@ struct MfmaSetup {
 // What the main loop of the matrix-core scan needs from its set-up, as one
 // scan of a fused call stores it for the later ones.
 struct alignas(16) SlotRecord {
-  int32_t nslots, pad[3];
+  int32_t nslots, gvalid, pad[2];
   float C[kMaxGH], scale[kMaxGH];
   int16_t desc[kMaxSlots];
   int32_t limbs[kMaxPasses][64][4];
+  // group pre-check (GroupCheck), when gvalid
+  int32_t glimbs[64][4];
+  double gsumC, gmarg;
+  float gscale, gpad[3];
 };
 
 // Per-block ranges (BLK): gamma and C_h change with every 2048-key tile.  The
@@ -785,6 +813,14 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   __shared__ float s_tf[kMaxGH];       // float thresholds of the block's rows
   __shared__ int s_ht[kMaxGH];         // integer pre-check bounds (see hi_bound)
   __shared__ int s_nslots;
+  // group pre-check: A operands of the group weights' limbs, its integer
+  // bound, whether the block has it, and (set-up) the weights' exponent and
+  // the record's constants
+  __shared__ __align__(16) typename std::conditional<!BLK && GH == kMaxGH, int32_t[64][4],
+                                                      char>::type s_glimbs;
+  __shared__ int s_gvalid, s_ght, s_gexp;
+  __shared__ double s_gsumC, s_gmarg;
+  __shared__ float s_gscale;
   __shared__ int s_last;  // recompute scan: this block finished its (kv head, chunk) last
   __shared__ uint32_t s_redo_rows;  // recompute scan: bit j = row j of the block's rows
   // code-buffer ring: [0..1] groups stored in buffer 0/1 (one count per
@@ -955,6 +991,17 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
     for (int e = tid; e < kLimbVec; e += kMThreads)
       reinterpret_cast<int4 *>(&s_limbs[0][0][0])[e] =
           reinterpret_cast<const int4 *>(&rec->limbs[0][0][0])[e];
+    if constexpr (!BLK && GH == kMaxGH) {
+      if (tid == 0) {
+        s_gvalid = rec->gvalid;
+        s_gsumC = rec->gsumC;
+        s_gmarg = rec->gmarg;
+        s_gscale = rec->gscale;
+      }
+      if (tid < 64)
+        reinterpret_cast<int4 *>(&s_glimbs[0][0])[tid] =
+            reinterpret_cast<const int4 *>(&rec->glimbs[0][0])[tid];
+    }
   } else {
     MfmaSetup<GH> &U = *reinterpret_cast<MfmaSetup<GH> *>(s_codes[0]);
     SlotTable<GH> &T = U.T;
@@ -994,6 +1041,64 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
       }
       limb_bytes[idx] = (uint8_t)(int8_t)v;
     }
+    if constexpr (!BLK && GH == kMaxGH) {
+      // Group pre-check of a one-pass call scored per GQA group: Gamma_slot =
+      // sum_h gamma_h,slot (fp64, exact) in fixed point below 2^30, its limbs
+      // in the A layout above (every row block holds them), and the margin.
+      const bool gbuild = a.out_group > 1 && npasses == 1;  // block-uniform
+      if (tid == 0) s_gvalid = gbuild ? 1 : 0;
+      if (gbuild) {
+        if (tid < 64) {
+          double gs = 0.0;
+          if (tid < nslots)
+#pragma unroll
+            for (int h = 0; h < GH; ++h) gs = __dadd_rn(gs, (double)T.gam[tid][h]);
+          double m = fabs(gs);
+#pragma unroll
+          for (int off = 32; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off));
+          if (tid == 0) {
+            int e = 0;
+            if (m > 0.0) frexp(m, &e);
+            s_gexp = e;
+          }
+        }
+        __syncthreads();
+        const int eg = s_gexp;
+        uint8_t *gl = reinterpret_cast<uint8_t *>(&s_glimbs[0][0]);
+        for (int idx = tid; idx < 64 * 16; idx += kMThreads) {
+          const int l = idx >> 4, d = (idx >> 2) & 3, b = idx & 3;
+          const int limb = (l & 15) & 3, j = l >> 4;
+          const int slot = 16 * j + 8 * (d >> 1) + 2 * b + (d & 1);
+          int v = 0;
+          if (slot < nslots) {
+            double gs = 0.0;
+#pragma unroll
+            for (int h = 0; h < GH; ++h) gs = __dadd_rn(gs, (double)T.gam[slot][h]);
+            int G = (int)rint(ldexp(gs, 30 - eg));
+            for (int i = 0; i < limb; ++i) {
+              const int dg = ((G + 128) & 255) - 128;
+              G = (G - dg) >> 8;
+            }
+            v = ((G + 128) & 255) - 128;
+          }
+          gl[idx] = (uint8_t)(int8_t)v;
+        }
+        if (tid == 0) {
+          double sumC = 0.0, sumB = 0.0, sumS = 0.0, half = ldexp(1.0, eg - 31);
+#pragma unroll
+          for (int h = 0; h < GH; ++h) {
+            const double ch = (double)s_C[h];
+            sumC += ch;
+            sumB += fabs(ch) + 15.0 * nslots * (double)__uint_as_float(T.gmax[h]);
+            sumS += (double)s_scale[h];
+            half += ldexp(1.0, s_exp[h] - 31);
+          }
+          s_gsumC = sumC;
+          s_gmarg = 9.5367431640625e-07 * sumB + 8.0 * sumS + 15.0 * nslots * half;
+          s_gscale = ldexpf(1.0f, eg - 30);
+        }
+      }
+    }
   }
   if (tid < 4) s_ring[tid] = 0u;
   if (tid < GH) {
@@ -1004,6 +1109,9 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
     }
     if constexpr (MODE == kScanCandGroup) s_tf[tid] = key_threshold(thr_key);
   }
+  if constexpr (MODE == kScanCandGroup && !BLK && GH == kMaxGH)
+    if (tid == 0 && s_gvalid)
+      s_ght = group_bound(key_threshold(thr_key), s_gsumC, s_gmarg, s_gscale);
   __syncthreads();  // the code table is free from here on
   if constexpr (BLK && MODE == kScanCand) {
     // integer candidate bound of each tile and head
@@ -1030,6 +1138,19 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
     for (int e = tid; e < npasses * 64; e += kMThreads)
       reinterpret_cast<int4 *>(&rec->limbs[0][0][0])[e] =
           reinterpret_cast<const int4 *>(&s_limbs[0][0][0])[e];
+    if constexpr (GH == kMaxGH && !BLK) {
+      if (tid == 0) {
+        rec->gvalid = s_gvalid;
+        rec->gsumC = s_gsumC;
+        rec->gmarg = s_gmarg;
+        rec->gscale = s_gscale;
+      }
+      if (tid < 64)
+        reinterpret_cast<int4 *>(&rec->glimbs[0][0])[tid] =
+            reinterpret_cast<const int4 *>(&s_glimbs[0][0])[tid];
+    } else {
+      if (tid == 0) rec->gvalid = 0;
+    }
   }
 
   // role 0: producer waves (load, regroup, transpose into a code buffer);
@@ -1208,6 +1329,18 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
     // the consumers, whose matrix and epilogue phases set the pace, win
     // issue arbitration over the producers (whose loads run well ahead)
     __builtin_amdgcn_s_setprio(1);
+    // group pre-check operands (one-pass group calls)
+    v4i AG = v4i{0, 0, 0, 0};
+    int ght = INT_MAX;
+    bool gcheck = false;
+    if constexpr (MODE == kScanCandGroup && !META && !BLK && GH == kMaxGH) {
+      gcheck = s_gvalid != 0;
+      if (gcheck) {
+        const int4 ag = *reinterpret_cast<const int4 *>(&s_glimbs[lane][0]);
+        AG = v4i{ag.x, ag.y, ag.z, ag.w};
+        ght = s_ght;
+      }
+    }
     float s[16];
     uint32_t fill_target[2] = {0u, 0u};  // groups stored in each buffer so far
     for (int it = 0; it < nitems; ++it) {
@@ -1251,6 +1384,74 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
         for (int q = 0; q < 16; ++q) s[q] = Cit;
       }
       const uint32_t *codes = s_codes[b];
+      if constexpr (MODE == kScanCandGroup && !META && !BLK && GH == kMaxGH) {
+        if (npasses == 1 && gcheck) {
+          // one pass, one row per kv head: the products of the group weights
+          // first; a key's heads' products and its group score are formed only
+          // where some lane's group high limb pair reaches the row's bound
+          // (group_bound), which no candidate misses, and then exactly as in
+          // the general path below (fp32 sum, fp64 near the threshold).  The
+          // buffer is released after the tests (they may read it again).
+          const int64_t kb = tile_key0 + 256 * wave + 4 * nn;  // + 64*beta + e
+          const int64_t rem = n - kb;
+          const int lim = rem > 256 ? 256 : (int)rem;
+          auto operand = [&](int q) -> v4i {
+            const int key = 256 * wave + 64 * (q >> 2) + 4 * nn + (q & 3);
+            const uint32_t w0 = codes[code_index(2 * j, key)];
+            const uint32_t w1 = codes[code_index(2 * j + 1, key)];
+            return v4i{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu),
+                       (int)(w1 & 0x0F0F0F0Fu), (int)((w1 >> 4) & 0x0F0F0F0Fu)};
+          };
+          v4i accg[16];
+#pragma unroll
+          for (int q = 0; q < 16; ++q)
+            accg[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(AG, operand(q), v4i{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int hig = accg[q][2] + accg[q][3] * 256;
+            const bool maybe = hh == 0 && 64 * (q >> 2) + (q & 3) < lim && hig >= ght;
+            if (__ballot(maybe) != 0ull) {
+              // this lane's head's logit of the key, as the logits scan forms it
+              const v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, operand(q), v4i{0, 0, 0, 0},
+                                                                    0, 0, 0);
+              const int lo = acc[0] + acc[1] * 256;
+              const int hi = acc[2] + acc[3] * 256;
+              const float t = __fmaf_rn((float)hi, 65536.0f, (float)lo);
+              const float sh = __fmaf_rn(t, sit, Cit);
+              const uint32_t v = __float_as_uint(sh);
+              const auto p16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+              const auto p32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+              const auto p48 = __builtin_amdgcn_permlane16_swap(p32[1], p32[1], false, false);
+              const float s1 = __uint_as_float(p16[1]);
+              const float s2 = __uint_as_float(p32[1]);
+              const float s3 = __uint_as_float(p48[1]);
+              float approx = sh, mag = fabsf(sh);
+              if (GH > 1) { approx = __fadd_rn(approx, s1); mag = __fadd_rn(mag, fabsf(s1)); }
+              if (GH > 2) { approx = __fadd_rn(approx, s2); mag = __fadd_rn(mag, fabsf(s2)); }
+              if (GH > 3) { approx = __fadd_rn(approx, s3); mag = __fadd_rn(mag, fabsf(s3)); }
+              const float margin = __fmaf_rn(mag, 4.76837158203125e-07f /* 2^-21 */,
+                                             1.1754943508222875e-38f /* 2^-126 */);
+              const bool near = maybe && __fadd_rn(approx, margin) >= row_tf;
+              float gs = approx;
+              if (__ballot(near) != 0ull) {
+                double dacc = (double)sh;
+                if (GH > 1) dacc = __dadd_rn(dacc, (double)s1);
+                if (GH > 2) dacc = __dadd_rn(dacc, (double)s2);
+                if (GH > 3) dacc = __dadd_rn(dacc, (double)s3);
+                gs = (float)dacc;
+              }
+              if (maybe && gs >= row_tf) {
+                // a candidate: the next place in this block's segment of the
+                // kv head's row (few keys get here, one LDS add each)
+                CandSink sink = cand_sink(S, g, bw.tile0, atomicAdd(&s_segc[0], 1u), 1u);
+                cand_put(sink, compose(to_key(gs), kb + 64 * (q >> 2) + (q & 3)));
+              }
+            }
+          }
+          ring_signal(&s_ring[2 + b]);  // buffer read (by this wave)
+          continue;
+        }
+      }
       if (MODE == kScanCand && !META && npasses == 1) {
         // one pass, one row per head: the exact score of a key is formed
         // only where some lane's high limb pair reaches the row's integer

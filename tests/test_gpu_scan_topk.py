@@ -284,3 +284,27 @@ def test_scan_topk_threshold_negative_and_outlier_rows(F):
         if group == 1:
             assert float(logits[: hq // 2, :n].max()) < 0.0
             assert int(got[0][hq // 2, 0]) == t0
+
+
+@pytest.mark.parametrize("n,k", [(150000, 1024), (1 << 20, 2048)])
+def test_scan_topk_group_cancelling_heads(F, n, k):
+    """Rows per GQA group of four whose heads' weights cancel: in every group
+    head 1 is head 0 negated (their plans agree, so the group weight of
+    every slot they share is that of heads 2 and 3 alone), and in kv head 0
+    heads 2 and 3 cancel as well (every group weight 0, the scores only
+    rounding noise around the constant).  The integer pre-check of a key's
+    group score against the row's bound must miss no candidate: fused equals
+    scan then top-k bit for bit."""
+    hkv, hq = 8, 32
+    keys = synth.keys(570, 0, n, hkv, 128, torch.float16, 4, device=dev())
+    q = synth.queries(570, 0, hq, 128, device=dev()).view(hkv, 4, 128)
+    q[:, 1] = -q[:, 0]
+    q[0, 3] = -q[0, 2]
+    q = q.reshape(hq, 128).contiguous()
+    p = F.pack(keys)
+    del keys
+    plan = F.plan(q, p.sigma2, 92)
+    torch.cuda.synchronize()
+    print(f"scan_topk cancelling heads n={n} k={k}", flush=True)
+    got, ref, _ = both(F, p, n, q, plan, k, 4)
+    assert_same(got, ref)
