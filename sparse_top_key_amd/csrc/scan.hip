@@ -814,11 +814,10 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
   __shared__ int s_ht[kMaxGH];         // integer pre-check bounds (see hi_bound)
   __shared__ int s_nslots;
   // group pre-check: A operands of the group weights' limbs, its integer
-  // bound, whether the block has it, and (set-up) the weights' exponent and
-  // the record's constants
+  // bound, whether the block has it, and (set-up) the record's constants
   __shared__ __align__(16) typename std::conditional<!BLK && GH == kMaxGH, int32_t[64][4],
                                                       char>::type s_glimbs;
-  __shared__ int s_gvalid, s_ght, s_gexp;
+  __shared__ int s_gvalid, s_ght;
   __shared__ double s_gsumC, s_gmarg;
   __shared__ float s_gscale;
   __shared__ int s_last;  // recompute scan: this block finished its (kv head, chunk) last
@@ -1048,22 +1047,14 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
       const bool gbuild = a.out_group > 1 && npasses == 1;  // block-uniform
       if (tid == 0) s_gvalid = gbuild ? 1 : 0;
       if (gbuild) {
-        if (tid < 64) {
-          double gs = 0.0;
-          if (tid < nslots)
+        // |Gamma_slot| <= sum_h max |gamma_h| < 2^eg: the exponent needs no
+        // pass over the slots
+        double gsum = 0.0;
 #pragma unroll
-            for (int h = 0; h < GH; ++h) gs = __dadd_rn(gs, (double)T.gam[tid][h]);
-          double m = fabs(gs);
-#pragma unroll
-          for (int off = 32; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off));
-          if (tid == 0) {
-            int e = 0;
-            if (m > 0.0) frexp(m, &e);
-            s_gexp = e;
-          }
-        }
-        __syncthreads();
-        const int eg = s_gexp;
+        for (int h = 0; h < GH; ++h) gsum += (double)__uint_as_float(T.gmax[h]);
+        int eg = 0;
+        if (gsum > 0.0) frexp(gsum * (1.0 + 1.0e-12), &eg);  // (rounded up past the sum)
+        const double to_fixed = __longlong_as_double((long long)(30 - eg + 1023) << 52);
         uint8_t *gl = reinterpret_cast<uint8_t *>(&s_glimbs[0][0]);
         for (int idx = tid; idx < 64 * 16; idx += kMThreads) {
           const int l = idx >> 4, d = (idx >> 2) & 3, b = idx & 3;
@@ -1074,7 +1065,7 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
             double gs = 0.0;
 #pragma unroll
             for (int h = 0; h < GH; ++h) gs = __dadd_rn(gs, (double)T.gam[slot][h]);
-            int G = (int)rint(ldexp(gs, 30 - eg));
+            int G = (int)rint(gs * to_fixed);
             for (int i = 0; i < limb; ++i) {
               const int dg = ((G + 128) & 255) - 128;
               G = (G - dg) >> 8;
@@ -1084,14 +1075,16 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
           gl[idx] = (uint8_t)(int8_t)v;
         }
         if (tid == 0) {
-          double sumC = 0.0, sumB = 0.0, sumS = 0.0, half = ldexp(1.0, eg - 31);
+          // half a fixed-point unit of every head and of Gamma: 2^(e - 31)
+          double sumC = 0.0, sumB = 0.0, sumS = 0.0;
+          double half = __longlong_as_double((long long)(eg - 31 + 1023) << 52);
 #pragma unroll
           for (int h = 0; h < GH; ++h) {
             const double ch = (double)s_C[h];
             sumC += ch;
             sumB += fabs(ch) + 15.0 * nslots * (double)__uint_as_float(T.gmax[h]);
             sumS += (double)s_scale[h];
-            half += ldexp(1.0, s_exp[h] - 31);
+            half += __longlong_as_double((long long)(s_exp[h] - 31 + 1023) << 52);
           }
           s_gsumC = sumC;
           s_gmarg = 9.5367431640625e-07 * sumB + 8.0 * sumS + 15.0 * nslots * half;
