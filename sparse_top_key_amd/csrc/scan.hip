@@ -990,7 +990,7 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
     for (int e = tid; e < kLimbVec; e += kMThreads)
       reinterpret_cast<int4 *>(&s_limbs[0][0][0])[e] =
           reinterpret_cast<const int4 *>(&rec->limbs[0][0][0])[e];
-    if constexpr (!BLK && GH == kMaxGH) {
+    if constexpr (MODE == kScanCandGroup && !BLK && GH == kMaxGH) {
       if (tid == 0) {
         s_gvalid = rec->gvalid;
         s_gsumC = rec->gsumC;
@@ -1138,7 +1138,7 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a) {
         rec->gmarg = s_gmarg;
         rec->gscale = s_gscale;
       }
-      if (tid < 64)
+      if (tid < 64 && s_gvalid)
         reinterpret_cast<int4 *>(&rec->glimbs[0][0])[tid] =
             reinterpret_cast<const int4 *>(&s_glimbs[0][0])[tid];
     } else {
