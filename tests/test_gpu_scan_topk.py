@@ -308,3 +308,43 @@ def test_scan_topk_group_cancelling_heads(F, n, k):
     print(f"scan_topk cancelling heads n={n} k={k}", flush=True)
     got, ref, _ = both(F, p, n, q, plan, k, 4)
     assert_same(got, ref)
+
+
+@pytest.mark.parametrize("case", ["rd_two_passes", "group_plan", "side_stream"])
+def test_scan_topk_group4_other_paths(F, case):
+    """Rows per GQA group of four that keep the general candidate path (more
+    than 64 slots, i.e. two matrix-core passes, from a rate-distortion plan
+    with a large budget; a side stream) or take the group pre-check with a
+    plan shared by the group: fused equals scan then top-k bit for bit."""
+    n, hkv, hq, k = 120000, 8, 32, 1024
+    keys = synth.keys(580, 0, n, hkv, 128, torch.float16, 4, device=dev())
+    q = synth.queries(580, 0, hq, 128, device=dev())
+    p = F.pack(keys)
+    del keys
+    meta, scale = None, 0.0
+    if case == "rd_two_passes":
+        plan = F.plan_rd(q, p.sigma2, 300)
+    elif case == "group_plan":
+        plan = F.plan_group(q, p.sigma2, 176)
+    else:
+        plan = F.plan_fixed(q, 32)
+        meta, scale = synth.side_stream(580, 0, hkv, n, device=dev()), 0.25
+    torch.cuda.synchronize()
+    print(f"scan_topk group 4 other paths case={case}", flush=True)
+    got, ref, _ = both(F, p, n, q, plan, k, 4, meta, scale)
+    assert_same(got, ref)
+
+
+def test_scan_topk_recompute_two_head_chunks(F):
+    """Eight query heads per kv head (two head chunks of four, two launches of
+    the recompute scan) with every logit tied (budget 0): the final's blocks
+    in the first launch flag every row, the scan blocks of both chunks
+    recompute theirs; equals scan then top-k."""
+    n, hkv, hq, k = 60000, 2, 16, 256
+    _, q, p, plan = layer(F, 590, n, hkv, hq, budget=0)
+    print("scan_topk recompute two head chunks", flush=True)
+    flags = redo_flags(F, n, hkv, hq, 1, k, lambda ws: F.scan_topk(
+        p.planes, p.lo, p.hi, n, q, plan, k, 1, ws=ws))
+    assert int(flags.sum()) == hq
+    got, ref, _ = both(F, p, n, q, plan, k, 1)
+    assert_same(got, ref)
