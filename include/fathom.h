@@ -294,14 +294,18 @@ int32_t fathom_topk_batched(const fathom_session *sessions, int32_t n_sessions,
  * scans again keeping only the (score, index) pairs at or above the
  * threshold, and ranks those; a row whose candidate count falls outside
  * [k, 8192] is recomputed from full logits in the workspace (by the last
- * block of its kv head's recompute scan).  Otherwise (pinned host planes,
- * other groups, longer sessions) the full logits go to the workspace and are
+ * block of its kv head's recompute scan, whose launch also holds the
+ * ranking blocks of the other rows).  Otherwise (pinned host planes, other
+ * groups, longer sessions) the full logits go to the workspace and are
  * ranked there.
  *
  * Arguments as for fathom_scan and fathom_topk (group over the hq rows);
  * idx, vals  device outputs int32/fp32[hq/group][k].
  * ws         device workspace of fathom_scan_topk_workspace_bytes bytes.
- * Enqueues 5 or fewer kernel launches; nothing synchronises.               */
+ * Enqueues four kernel launches (sample scan, threshold, candidate scan,
+ * ranking + recompute scan; the scans once more per further 4 query heads
+ * of a kv head or 16 sessions, and the ranking as a launch of its own when
+ * a session has no keys); nothing synchronises.                            */
 int64_t fathom_scan_topk_workspace_bytes(const int64_t *n_host, int32_t n_sessions,
                                          int32_t hkv, int32_t hq, int32_t group,
                                          int32_t k);
