@@ -272,11 +272,12 @@ int orc_plan_group(const float *q, int hq, int hkv, int d, const float *sigma2,
       order[c].c = c;
     }
     qsort(order, d, sizeof(orc_wc), orc_cmp_w_desc);
-    int remaining = B;
+    /* fill to the 4-bit cap in that order, as orc_plan: B / 4 channels in
+       full, the next one B % 4 bits, the rest none; one plan for all heads */
+    const int full = B / 4, part = B % 4;
     for (int j = 0; j < d; ++j) {
-      int take = remaining <= 0 ? 0 : (remaining < 4 ? remaining : 4);
-      for (int k = 0; k < G; ++k) plan[(int64_t)(g * G + k) * d + order[j].c] = (uint8_t)take;
-      remaining -= take;
+      const uint8_t t = j < full ? 4 : (j == full ? (uint8_t)part : 0);
+      for (int k = 0; k < G; ++k) plan[(int64_t)(g * G + k) * d + order[j].c] = t;
     }
   }
   free(order);
