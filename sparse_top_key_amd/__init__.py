@@ -128,8 +128,19 @@ def _check(rc: int, name: str):
         raise FathomError(f"{name}: {_ERRORS.get(rc, rc)}: {msg}")
 
 
+# The current stream's raw handle straight from torch's C layer (about 0.1 us
+# per call against about 2 us for building a Stream object), where it exists.
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device=None):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    if _RAW_STREAM is None:
+        return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    if device is None or device.index is None:
+        index = torch.cuda.current_device()
+    else:
+        index = device.index
+    return ctypes.c_void_p(_RAW_STREAM(index))
 
 
 def _p(t: Optional[torch.Tensor]):
