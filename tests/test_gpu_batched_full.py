@@ -173,3 +173,41 @@ def test_step_36_layers_spot_parity(F, orc, layer):
         ridx, rvals = orc.topk(L[r:r + 1], w.k)
         np.testing.assert_array_equal(idx[r:r + 1].cpu().numpy(), ridx)
         np.testing.assert_array_equal(vals[r:r + 1].cpu().numpy(), rvals)
+
+
+@pytest.mark.parametrize("layer", [5, 30])
+def test_step_36_layers_spot_parity_host_resident(F, orc, layer):
+    """The 36-layer step's host leg: the same layer's planes in pinned host
+    memory (read zero-copy by the scan): sampled logits within tolerance of
+    the oracle, scan_topk bit-identical to scan then top-k on those planes,
+    and two rows' top-k bit-exact against the oracle's sort of the GPU
+    logits."""
+    w = synth.STEP_36L_1M
+    n = w.n
+    print(f"36-layer step, host-resident layer {layer}", flush=True)
+    keys = synth.keys(w.seed, layer, n, w.hkv, 128, w.dtype, w.outliers, device=dev())
+    q = synth.queries(w.seed, layer, w.hq, 128, device=dev())
+    p = F.pack(keys)
+    del keys
+    hplanes = torch.empty(p.planes.shape, dtype=p.planes.dtype, pin_memory=True)
+    hplanes.copy_(p.planes)
+    plan = F.plan(q, p.sigma2, w.budget)
+    logits = F.scan(hplanes, p.lo, p.hi, n, q, plan)
+    idx, vals = F.topk(logits, w.k)
+    fidx, fvals = F.scan_topk(hplanes, p.lo, p.hi, n, q, plan, w.k, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(fidx, idx) and torch.equal(fvals, vals)
+    planes_np = hplanes.numpy().view(np.uint32)
+    lo, hi = p.lo.cpu().numpy(), p.hi.cpu().numpy()
+    qn, pn = q.cpu().numpy(), plan.cpu().numpy()
+    np.testing.assert_array_equal(pn, orc.plan(qn, p.sigma2.cpu().numpy(), w.budget))
+    rng = np.random.default_rng(100 + layer)
+    pick = np.unique(np.concatenate([rng.integers(0, n, 1000), np.arange(n - 20, n)]))
+    ref = orc.scan_at(planes_np, lo, hi, n, qn, pn, pick)
+    A = logit_scale(qn, lo, hi, 4)
+    L = logits.cpu().numpy()
+    assert_logits_close(L[:, pick], ref, A)
+    for r in (layer % 32, 31 - layer % 32):
+        ridx, rvals = orc.topk(L[r:r + 1], w.k)
+        np.testing.assert_array_equal(idx[r:r + 1].cpu().numpy(), ridx)
+        np.testing.assert_array_equal(vals[r:r + 1].cpu().numpy(), rvals)
